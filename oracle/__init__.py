@@ -1,0 +1,24 @@
+"""fp64 CPU oracle for paged-KV attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package.  The product path (the HIP library
+and its Python binding) never imports, calls or links it, and shares no code
+with it: the only code both sides use is the seeded input generator in
+``workloads``.
+
+Pins (what fixes each function to something other than itself) are listed in
+``oracle/attention.py``'s header; every function is pinned, none is
+"parity unpinned".
+"""
+
+from .attention import (  # noqa: F401
+    stored_to_f64,
+    gather_rows,
+    attend,
+    lse_merge,
+    paged_attention,
+    decode,
+    prefix_cascade,
+    mixed_chunk,
+    check_block_tables,
+)
