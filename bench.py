@@ -1,0 +1,195 @@
+"""Benchmark: paged decode attention at the Llama-3-8B shape on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pa_decode call (split-KV kernel + LSE merge) over the whole
+batch, with inputs resident in HBM.  Prints ONE JSON line:
+value = algorithmic bytes per step / measured step time (GB/s), plus decode
+tokens/s for a 32-layer model (attention only), a roofline object for the
+dominant (split-KV) kernel timed with HIP events on its own stream, and the
+fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama8b_decode")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--split-pages", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(lay, q, k, v, budget_s):
+    """Time the fp64 oracle, single-threaded, on whole sequences of the same
+    batch until about budget_s seconds of CPU work are spent."""
+    import torch
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    import oracle
+    from paged_kv_decode_02_amd import roofline
+
+    def host(t):
+        if lay.dtype == "bf16":
+            return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.float().cpu().numpy()
+
+    order = np.random.default_rng(123).permutation(lay.num_seqs)
+    done, spent, nbytes = [], 0.0, 0
+    limit = threadpool_limits(1) if threadpool_limits else None
+    try:
+        while spent < budget_s and len(done) < lay.num_seqs:
+            s = int(order[len(done)])
+            n = (int(lay.context_lens[s]) + 15) // 16
+            idx = torch.from_numpy(lay.block_tables[s, :n].astype(np.int64)).to(k.device)
+            ks, vs = host(k.index_select(0, idx)), host(v.index_select(0, idx))
+            qs = host(q[s : s + 1])
+            bt = np.arange(n, dtype=np.int32)[None, :]  # the gathered pages, relabelled 0..n-1
+            ctx = lay.context_lens[s : s + 1]
+            t0 = time.perf_counter()
+            oracle.decode(qs, ks, vs, bt, ctx, lay.scale, lay.num_kv_heads, 16, lay.dtype)
+            spent += time.perf_counter() - t0
+            done.append(s)
+            nbytes += roofline.decode_bytes(ctx, lay.num_q_heads, lay.num_kv_heads, lay.head_dim,
+                                            lay.elem_bytes)["total"]
+    finally:
+        if limit is not None:
+            limit.unregister()
+    return {
+        "value": nbytes / spent / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{len(done)} of {lay.num_seqs} sequences ({nbytes / 1e6:.1f} MB algorithmic), "
+                  f"{spent:.1f} s, fp64 numpy, BLAS limited to 1 thread",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); this path does not shard across GPUs.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from paged_kv_decode_02_amd import pa, roofline
+    from workloads import values_torch, workload
+
+    lay = workload(args.workload, seed=args.seed)
+    if lay.q_lens.max() != 1 or lay.group_seq_offsets is not None:
+        print(f"{args.workload} is not a plain decode batch", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] workload {args.workload} seed {args.seed}: drawing inputs on the device", file=sys.stderr,
+          flush=True)
+    q, k, v = values_torch(lay, dev)
+    bt = torch.from_numpy(lay.block_tables).to(dev)
+    ctx = torch.from_numpy(lay.context_lens).to(dev)
+    out = torch.empty_like(q)
+    S, Hq, D = q.shape
+    total_pages = int(((lay.context_lens + 15) // 16).sum())
+    ws = torch.empty(pa.decode_workspace_size(S, lay.num_kv_heads, lay.gqa_ratio, D, total_pages, args.split_pages),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        pa.decode(out, q, k, v, bt, ctx, lay.context_lens, lay.scale, ws, split_pages=args.split_pages,
+                  stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+
+    # Dominant kernel alone: HIP events the library records around the
+    # split-KV launch on the same stream.
+    pa.profile_enable(args.steps)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kern_ms = pa.profile_collect(args.steps)
+    pa.profile_enable(0)
+    kern_avg = float(np.mean(kern_ms))
+
+    nb = roofline.decode_bytes(lay.context_lens, lay.num_q_heads, lay.num_kv_heads, D, lay.elem_bytes)
+    gbs = nb["total"] / (ms_per_step * 1e-3) / 1e9
+    achieved = nb["total"] / (kern_avg * 1e-3) / 1e9
+    result = {
+        "metric": "paged decode attn KV GB/s (% of HBM peak) + decode tokens/s, Llama-8B shape",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": lay.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "num_seqs": int(S),
+            "q_heads": lay.num_q_heads,
+            "kv_heads": lay.num_kv_heads,
+            "head_dim": int(D),
+            "block_size": 16,
+            "kv_tokens": int(lay.context_lens.sum()),
+            "seed": args.seed,
+            "parallelism": "single GPU",
+        },
+        "hbm_frac": round(gbs / roofline.HBM_PEAK_GBS, 4),
+        "decode_tokens_per_s_32_layers": round(S / (roofline.LLAMA8B_LAYERS * ms_per_step * 1e-3), 1),
+        "algorithmic_bytes_per_step": nb["total"],
+        "wall_s": round(wall, 3),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "split_decode_kernel",
+            "achieved": round(achieved, 1),
+            "peak": roofline.HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / roofline.HBM_PEAK_GBS, 4),
+            "kernel_ms": round(kern_avg, 5),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(lay, q, k, v, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,149 @@
+/*
+ * pa.h -- attention over a paged KV cache on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libpa.so.  Every pointer is a raw address; the header says for
+ * each one whether it is device memory (HBM) or host memory.  No call
+ * allocates memory: the caller owns q, the pools, the tables, the outputs
+ * and the workspace.  Kernels are launched asynchronously on the HIP stream
+ * passed as `stream` (a hipStream_t, NULL = the default stream); device
+ * buffers must stay alive until the stream reaches the call.  Host arrays
+ * (the `*_host` twins) are read synchronously before the call returns, so
+ * planning never waits for the device.
+ *
+ * The problem statement these calls follow:
+ *  - KV cache split into fixed-size blocks (pages); a sequence's rows are
+ *    found through its block table; blocks of a shared prefix may be named
+ *    by many tables (SwiftLLM page, section 3.1 "PagedAttention and KV
+ *    cache management").
+ *  - The attention layer is handed the block tables and per-sequence
+ *    context lengths (SwiftLLM page, section 5.1).
+ *  - Split-KV decode: each split writes a partial output and its
+ *    log-sum-exp to a workspace, and a second pass reduces the partials by
+ *    their LSE (TokenSpeed deep-dive, sections 7 and 7.1).
+ *  - Page size is a property of the kernel, passed explicitly, never
+ *    derived (TokenSpeed deep-dive, section 4.3); no argument has a
+ *    default and an idle step passes zero-length arrays (section 8.2).
+ *
+ * Layouts (all row-major, C order):
+ *  q          [T, Hq, D]   dtype        T = number of query tokens
+ *  out        [T, Hq, D]   dtype
+ *  lse_out    [T, Hq]      float32, natural log (may be NULL)
+ *  k_pool     [num_pages, Hkv, block_size, D]   dtype
+ *  v_pool     [num_pages, Hkv, block_size, D]   dtype
+ *  block_tables [num_seqs, max_blocks_per_seq] int32; entry j of row s is
+ *             the physical page holding rows [16j, 16j+16) of sequence s.
+ *  context_lens [num_seqs] int32: rows of sequence s in the pool,
+ *             including this step's own tokens.
+ * Hq = num_kv_heads * gqa_ratio; q-head h reads kv-head h / gqa_ratio.
+ *
+ * Semantics: query token i of a sequence with L rows and n query tokens
+ * sees rows [0, L - n + i] (decode: n = 1, all L rows):
+ *     out = sum_t softmax_t(scale * <q, k_t>) v_t,
+ *     lse = ln sum_t exp(scale * <q, k_t>).
+ * Arithmetic is float32 (bf16 products are exact in float32); bf16
+ * outputs are rounded to nearest even.
+ *
+ * Errors: every call returns PA_OK or a negative code, never throws, and
+ * on error launches nothing; pa_last_error() then holds a message.
+ * Table *contents* in device memory are not checked on the hot call
+ * (pa_check_block_tables does that on host copies); kernels clamp every
+ * page id into [0, num_pages), so a bad table gives wrong numbers, never an
+ * out-of-bounds access.  `context_lens` and `context_lens_host` must hold
+ * the same values; if they do not, results are undefined but every access
+ * still stays inside the buffers passed.
+ *
+ * Thread safety: calls are reentrant.  Two calls that share a workspace
+ * must be ordered on one stream.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+enum {
+  PA_OK = 0,
+  PA_EINVAL = -1,       /* bad argument (null pointer, size, length) */
+  PA_EUNSUPPORTED = -2, /* valid but not built: head_dim, block_size, gqa_ratio, dtype */
+  PA_EWORKSPACE = -3,   /* workspace too small for this call's plan */
+  PA_EHIP = -4          /* a HIP runtime call failed */
+};
+
+/* Supported shapes: block_size 16; head_dim 64 or 128 (bf16) and 64
+ * (float32); gqa_ratio 1, 2, 4, 8 or 16 for decode. */
+
+/* ---------------------------------------------------------------------------
+ * Decode: one query token per sequence (T = num_seqs).
+ *
+ * Each (sequence, kv-head) is cut into splits of `split_pages` pages
+ * (0 = chosen from the batch); each split computes the G = gqa_ratio
+ * q-heads that share its kv-head from one pass over its K/V pages, then the
+ * partials of sequences with more than one split are merged by their LSE.
+ *
+ * workspace: device memory of at least pa_decode_workspace_size(...) bytes
+ *   for the largest batch it will serve; 256-byte aligned.  Its contents
+ *   need no initialisation and are scratch between calls.
+ * Returns PA_OK; PA_EINVAL for null pointers (lse_out may be NULL), sizes
+ *   < 1 (num_seqs == 0 is a no-op returning PA_OK), a context length < 1
+ *   or > max_blocks_per_seq * block_size, or split_pages < 0;
+ *   PA_EUNSUPPORTED for shapes not built; PA_EWORKSPACE if the plan needs
+ *   more workspace than workspace_bytes; PA_EHIP if a launch fails.
+ * ------------------------------------------------------------------------- */
+size_t pa_decode_workspace_size(int32_t max_num_seqs, int32_t num_kv_heads, int32_t gqa_ratio,
+                                int32_t head_dim, int64_t max_total_pages, int32_t split_pages);
+
+int pa_decode(void* out,                      /* device [S, Hq, D] dtype */
+              float* lse_out,                 /* device [S, Hq] or NULL */
+              const void* q,                  /* device [S, Hq, D] dtype */
+              const void* k_pool,             /* device [NP, Hkv, BS, D] dtype */
+              const void* v_pool,             /* device [NP, Hkv, BS, D] dtype */
+              const int32_t* block_tables,    /* device [S, max_blocks_per_seq] */
+              int32_t max_blocks_per_seq,
+              const int32_t* context_lens,    /* device [S] */
+              const int32_t* context_lens_host, /* host [S], same values */
+              int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_ratio, int32_t head_dim,
+              int32_t block_size, int64_t num_pages, float scale, pa_dtype dtype,
+              int32_t split_pages,            /* pages per split; 0 = automatic */
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Host-side table check (host copies only, no device access).
+ * Every sequence needs ceil(L/block_size) entries in [0, num_pages); a page
+ * may appear in more than one table only as a declared shared prefix: for
+ * each group g, sequences [group_seq_offsets[g], group_seq_offsets[g+1])
+ * must all start with the same prefix_lens[g] / block_size pages, and
+ * prefix_lens[g] must be a multiple of block_size and shorter than every
+ * member's context.  num_groups = 0 (offsets/prefix NULL) means no sharing.
+ * Returns PA_OK or PA_EINVAL with the first problem in pa_last_error().
+ * ------------------------------------------------------------------------- */
+int pa_check_block_tables(const int32_t* block_tables_host, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens_host, int32_t num_seqs, int32_t block_size,
+                          int64_t num_pages, int32_t num_groups, const int32_t* group_seq_offsets_host,
+                          const int32_t* prefix_lens_host);
+
+/* Message for the last non-OK return on this thread ("" if none). */
+const char* pa_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Profiling hook (measurement only; changes no result).
+ * pa_profile_enable(n) creates n pairs of HIP timing events on this thread;
+ * every later call records one pair around its dominant kernel (the split
+ * stage of pa_decode) on its stream.  pa_profile_collect() waits for those
+ * events, writes up to `cap` durations in milliseconds to `ms_out`, returns
+ * how many it wrote and rewinds the ring.  pa_profile_enable(0) frees the
+ * events and stops recording.  Returns a negative code on error.
+ * ------------------------------------------------------------------------- */
+int pa_profile_enable(int32_t num_pairs);
+int pa_profile_collect(float* ms_out, int32_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,144 @@
+// Device helpers shared by the paged-attention kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// bf16 pair packed in one dword: element 0 in the low half.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// a.lo*b.lo + a.hi*b.hi + c with bf16 pairs (products exact in float32).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Splits of C pages that sequence s needs over pages [begin, pages).
+__device__ __forceinline__ int nsplit_of(int L, int begin_pages, int max_blocks, int C) {
+  const int64_t pg = (static_cast<int64_t>(L) + 15) >> 4;
+  const int pages = static_cast<int>(pg < max_blocks ? pg : max_blocks);
+  const int n = pages - begin_pages;
+  return n > 0 ? (n + C - 1) / C : 0;
+}
+
+struct ItemLoc {
+  int s;     // sequence
+  int j;     // split index within the sequence
+  int ns;    // splits of the sequence
+  int base;  // index of the sequence's first item
+  int total; // items over all sequences
+};
+
+// Work item x -> (sequence, split).  Items are numbered sequence by
+// sequence; every wave derives the numbering itself from the device copy
+// of the context lengths (one pass over S values, then one over the
+// S/64 values of the lane that holds x), so no plan buffer is needed.
+// `begin_pages` (nullable) gives pages each sequence skips.
+__device__ __forceinline__ bool locate_item(const int32_t* __restrict__ ctx, const int32_t* __restrict__ begin_pages,
+                                            int S, int max_blocks, int C, int x, ItemLoc& loc) {
+  const int lane = lane_id();
+  const int per = (S + 63) >> 6;
+  int tot = 0;
+  // Unrolled with clamped indices so that eight independent loads are in
+  // flight at once instead of one load-use chain per sequence.
+#pragma unroll 8
+  for (int i = 0; i < per; ++i) {
+    const int s = lane * per + i;
+    const int sc = s < S ? s : S - 1;
+    const int n = nsplit_of(ctx[sc], begin_pages ? begin_pages[sc] : 0, max_blocks, C);
+    tot += s < S ? n : 0;
+  }
+  const int incl = wave_inclusive_scan(tot);
+  const int excl = incl - tot;
+  loc.total = __shfl(incl, 63, 64);
+  const unsigned long long b = __ballot(x >= excl && x < incl);
+  if (b == 0ull) return false;
+  const int l = __ffsll(b) - 1;
+  int base = __shfl(excl, l, 64);
+  const int first = l * per;
+  for (int r0 = 0; r0 < per; r0 += 64) {
+    const int i = r0 + lane;
+    const int s = first + i;
+    const int ns = (i < per && s < S) ? nsplit_of(ctx[s], begin_pages ? begin_pages[s] : 0, max_blocks, C) : 0;
+    const int inc2 = wave_inclusive_scan(ns);
+    const int ex2 = inc2 - ns;
+    const unsigned long long b2 = __ballot(ns > 0 && x >= base + ex2 && x < base + inc2);
+    if (b2 != 0ull) {
+      const int l2 = __ffsll(b2) - 1;
+      loc.s = first + r0 + l2;
+      loc.ns = __shfl(ns, l2, 64);
+      loc.base = base + __shfl(ex2, l2, 64);
+      loc.j = x - loc.base;
+      return true;
+    }
+    base += __shfl(inc2, 63, 64);
+  }
+  return false;
+}
+
+// First item index and split count of sequence s.
+__device__ __forceinline__ void sequence_items(const int32_t* __restrict__ ctx, const int32_t* __restrict__ begin_pages,
+                                               int S, int max_blocks, int C, int s, int& base, int& ns) {
+  const int lane = lane_id();
+  const int per = (S + 63) >> 6;
+  int tot = 0;
+#pragma unroll 8
+  for (int i = 0; i < per; ++i) {
+    const int s2 = lane * per + i;
+    const int sc = s2 < S ? s2 : S - 1;
+    const int n = nsplit_of(ctx[sc], begin_pages ? begin_pages[sc] : 0, max_blocks, C);
+    tot += s2 < s ? n : 0;
+  }
+  base = wave_sum_int(tot);
+  ns = nsplit_of(ctx[s], begin_pages ? begin_pages[s] : 0, max_blocks, C);
+}
+
+}  // namespace pa

@@ -1,0 +1,115 @@
+// Host-side pieces of libpa: error state, split planning, workspace layout
+// and the block-table checker.  Plain C++ (no HIP), so it can also be built
+// with g++ and host sanitizers.
+#include <algorithm>
+#include <cstring>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+int32_t auto_split_pages(int64_t total_pages, int32_t num_kv_heads) {
+  // Aim at about kTargetWaves (sequence, split, kv-head) waves so 256 CUs
+  // see several rounds of work and a long sequence is cut into many splits;
+  // never below kMinSplitPages, and a whole number of 4-page batches.
+  int64_t want = (total_pages * num_kv_heads + kTargetWaves - 1) / kTargetWaves;
+  want = std::max<int64_t>(want, kMinSplitPages);
+  want = (want + kBatchPages - 1) / kBatchPages * kBatchPages;
+  return static_cast<int32_t>(std::min<int64_t>(want, 1 << 24));
+}
+
+PartialLayout partial_layout(int64_t items, int32_t num_kv_heads, int32_t gqa, int32_t head_dim) {
+  PartialLayout l;
+  const size_t rows = static_cast<size_t>(items) * num_kv_heads * gqa;
+  l.o_offset = 0;
+  l.lse_offset = align_up(rows * head_dim * sizeof(float));
+  l.bytes = l.lse_offset + align_up(rows * sizeof(float));
+  return l;
+}
+
+int64_t capacity_items(size_t bytes, int32_t num_kv_heads, int32_t gqa, int32_t head_dim) {
+  const size_t per = static_cast<size_t>(num_kv_heads) * gqa * (head_dim + 1) * sizeof(float);
+  int64_t cap = static_cast<int64_t>(bytes / per);
+  while (cap > 0 && partial_layout(cap, num_kv_heads, gqa, head_dim).bytes > bytes) --cap;
+  return std::min<int64_t>(cap, (int64_t(1) << 31) - 1);
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" int pa_check_block_tables(const int32_t* bt, int32_t max_blocks, const int32_t* ctx, int32_t num_seqs,
+                                     int32_t block_size, int64_t num_pages, int32_t num_groups,
+                                     const int32_t* group_offsets, const int32_t* prefix_lens) {
+  clear_error();
+  if (num_seqs < 0 || max_blocks < 0 || block_size < 1 || num_pages < 0 || num_groups < 0)
+    return fail(PA_EINVAL, "pa_check_block_tables: negative size");
+  if (num_seqs == 0) return PA_OK;
+  if (!bt || !ctx) return fail(PA_EINVAL, "pa_check_block_tables: null table or lengths");
+  if (num_groups > 0 && (!group_offsets || !prefix_lens))
+    return fail(PA_EINVAL, "pa_check_block_tables: groups given without offsets/prefix lengths");
+  std::vector<int64_t> prefix_pages(num_seqs, 0);
+  // page -> owner: >= 0 sequence id, < 0 encodes -(group + 1)
+  std::unordered_map<int64_t, int64_t> owner;
+  if (num_groups > 0) {
+    if (group_offsets[0] < 0 || group_offsets[num_groups] > num_seqs)
+      return fail(PA_EINVAL, "group offsets outside [0, num_seqs]");
+    for (int32_t g = 0; g < num_groups; ++g) {
+      const int32_t a = group_offsets[g], b = group_offsets[g + 1];
+      if (b < a) return fail(PA_EINVAL, "group " + std::to_string(g) + ": offsets decrease");
+      const int32_t P = prefix_lens[g];
+      if (P < 0 || P % block_size)
+        return fail(PA_EINVAL, "group " + std::to_string(g) + ": prefix length not a whole number of pages");
+      const int64_t np = P / block_size;
+      if (np > max_blocks) return fail(PA_EINVAL, "group " + std::to_string(g) + ": prefix longer than the table");
+      for (int32_t s = a; s < b; ++s) {
+        if (P >= ctx[s])
+          return fail(PA_EINVAL, "group " + std::to_string(g) + ": prefix not shorter than sequence " +
+                                     std::to_string(s));
+        if (std::memcmp(bt + static_cast<int64_t>(s) * max_blocks, bt + static_cast<int64_t>(a) * max_blocks,
+                        np * sizeof(int32_t)) != 0)
+          return fail(PA_EINVAL, "group " + std::to_string(g) + ": sequence " + std::to_string(s) +
+                                     " does not share the prefix pages");
+        prefix_pages[s] = np;
+      }
+      for (int64_t j = 0; j < np && b > a; ++j) {
+        const int64_t p = bt[static_cast<int64_t>(a) * max_blocks + j];
+        if (p < 0 || p >= num_pages)
+          return fail(PA_EINVAL, "group " + std::to_string(g) + ": prefix entry out of range");
+        if (!owner.emplace(p, -(g + 1)).second)
+          return fail(PA_EINVAL, "page " + std::to_string(p) + " named by two groups' prefixes");
+      }
+    }
+  }
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t L = ctx[s];
+    if (L < 1) return fail(PA_EINVAL, "sequence " + std::to_string(s) + ": empty context");
+    const int64_t n = (L + block_size - 1) / block_size;
+    if (n > max_blocks) return fail(PA_EINVAL, "sequence " + std::to_string(s) + ": table too short");
+    for (int64_t j = prefix_pages[s]; j < n; ++j) {
+      const int64_t p = bt[static_cast<int64_t>(s) * max_blocks + j];
+      if (p < 0 || p >= num_pages)
+        return fail(PA_EINVAL, "sequence " + std::to_string(s) + ": entry " + std::to_string(j) + " out of range");
+      if (!owner.emplace(p, s).second)
+        return fail(PA_EINVAL, "sequence " + std::to_string(s) + ": page " + std::to_string(p) +
+                                   " is also named elsewhere");
+    }
+  }
+  return PA_OK;
+}

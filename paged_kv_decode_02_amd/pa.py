@@ -1,0 +1,191 @@
+"""ctypes binding for libpa.so (the HIP paged-attention library).
+
+Argument marshalling only: this module checks that tensor shapes agree with
+each other (so the sizes handed to the C ABI describe the buffers passed),
+converts tensors to raw pointers and forwards to the library.  Every step of
+the computation runs in the library's kernels; there is no fallback path.
+If the built library is missing, :func:`load` raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpa.so")
+
+PA_F32 = 0
+PA_BF16 = 1
+PA_OK = 0
+PA_EINVAL = -1
+PA_EUNSUPPORTED = -2
+PA_EWORKSPACE = -3
+PA_EHIP = -4
+
+# every symbol include/pa.h declares
+EXPORTS = (
+    "pa_decode_workspace_size",
+    "pa_decode",
+    "pa_check_block_tables",
+    "pa_last_error",
+    "pa_profile_enable",
+    "pa_profile_collect",
+)
+
+_lib = None
+
+c_i32 = ctypes.c_int32
+c_i64 = ctypes.c_int64
+c_vp = ctypes.c_void_p
+c_sz = ctypes.c_size_t
+
+
+class PAError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libpa error {code}: {msg}")
+        self.code = code
+
+
+def load(path: Optional[str] = None):
+    """Load libpa.so (built in-tree by ``paged_kv_decode_02_amd.build``)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m paged_kv_decode_02_amd.build`")
+    lib = ctypes.CDLL(p)
+    lib.pa_decode_workspace_size.restype = c_sz
+    lib.pa_decode_workspace_size.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i64, c_i32]
+    lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
+                              c_i32, c_i64, ctypes.c_float, ctypes.c_int, c_i32, c_vp, c_sz, c_vp]
+    lib.pa_check_block_tables.restype = ctypes.c_int
+    lib.pa_check_block_tables.argtypes = [c_vp, c_i32, c_vp, c_i32, c_i32, c_i64, c_i32, c_vp, c_vp]
+    lib.pa_last_error.restype = ctypes.c_char_p
+    lib.pa_last_error.argtypes = []
+    lib.pa_profile_enable.restype = ctypes.c_int
+    lib.pa_profile_enable.argtypes = [c_i32]
+    lib.pa_profile_collect.restype = ctypes.c_int
+    lib.pa_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_float), c_i32]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().pa_last_error().decode()
+
+
+def _check(rc: int) -> int:
+    if rc < 0:
+        raise PAError(rc, last_error())
+    return rc
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t, name, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _host_i32(a, name):
+    arr = np.ascontiguousarray(a.numpy() if hasattr(a, "numpy") else a, dtype=np.int32)
+    return arr
+
+
+def _stream_ptr(stream):
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def decode_workspace_size(max_num_seqs, num_kv_heads, gqa_ratio, head_dim, max_total_pages, split_pages=0) -> int:
+    return int(load().pa_decode_workspace_size(max_num_seqs, num_kv_heads, gqa_ratio, head_dim, max_total_pages,
+                                               split_pages))
+
+
+def decode(out, q, k_pool, v_pool, block_tables, context_lens, context_lens_host, scale, workspace,
+           lse_out=None, split_pages=0, stream=None):
+    """pa_decode on torch tensors.
+
+    q, out: [S, Hq, D]; k_pool, v_pool: [NP, Hkv, 16, D]; block_tables
+    [S, MB] int32; context_lens [S] int32 (device) and context_lens_host
+    (numpy or CPU tensor, same values); workspace: uint8 device tensor.
+    """
+    import torch
+
+    S, Hq, D = q.shape
+    NP, Hkv, BS, D2 = k_pool.shape
+    if tuple(out.shape) != (S, Hq, D) or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if tuple(v_pool.shape) != tuple(k_pool.shape) or k_pool.dtype != q.dtype or v_pool.dtype != q.dtype:
+        raise ValueError("k_pool and v_pool must match each other and q's dtype")
+    if D2 != D or Hq % Hkv:
+        raise ValueError("head_dim mismatch or q heads not a multiple of kv heads")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_tables / context_lens must have one row per sequence")
+    ch = _host_i32(context_lens_host, "context_lens_host")
+    if ch.size != S:
+        raise ValueError("context_lens_host must have one entry per sequence")
+    if lse_out is not None and tuple(lse_out.shape) != (S, Hq):
+        raise ValueError("lse_out must be [S, Hq]")
+    rc = load().pa_decode(
+        _dev(out, "out"),
+        _dev(lse_out, "lse_out", torch.float32) if lse_out is not None else None,
+        _dev(q, "q"),
+        _dev(k_pool, "k_pool"),
+        _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32),
+        ch.ctypes.data,
+        S, Hkv, Hq // Hkv, D, BS, NP, float(scale), _dtype_code(q), int(split_pages),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream_ptr(stream),
+    )
+    return _check(rc)
+
+
+def check_block_tables(block_tables, context_lens, num_pages, block_size=16, group_seq_offsets=None,
+                       prefix_lens=None) -> int:
+    bt = _host_i32(block_tables, "block_tables")
+    ctx = _host_i32(context_lens, "context_lens")
+    ng = 0
+    go = pl = None
+    if group_seq_offsets is not None:
+        go = _host_i32(group_seq_offsets, "group_seq_offsets")
+        pl = _host_i32(prefix_lens, "prefix_lens")
+        ng = go.size - 1
+    rc = load().pa_check_block_tables(
+        bt.ctypes.data, bt.shape[1] if bt.ndim == 2 else 0, ctx.ctypes.data, ctx.size, block_size, num_pages, ng,
+        go.ctypes.data if go is not None else None, pl.ctypes.data if pl is not None else None)
+    return _check(rc)
+
+
+def profile_enable(num_pairs: int) -> None:
+    _check(load().pa_profile_enable(num_pairs))
+
+
+def profile_collect(cap: int = 1 << 16):
+    buf = (ctypes.c_float * cap)()
+    n = _check(load().pa_profile_collect(buf, cap))
+    return [buf[i] for i in range(n)]

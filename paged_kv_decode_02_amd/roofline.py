@@ -1,0 +1,37 @@
+"""Algorithmic work of one call, for throughput and roofline figures.
+
+Bytes count what the method must move at least once: every K and V row a
+query sees, read once per kv-head (GQA heads share it), plus q, the output,
+the block-table entries walked and the context lengths.  Workspace traffic
+(split partials) is implementation overhead and is not counted.
+
+The per-token KV size is the uncompressed MHA/GQA formula the tokenspeed
+deep-dive (fiv.co.kr) gives in section 7-2: 2 x layers x kv_heads x head_dim
+x tokens x bytes per element, here for one layer.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+LLAMA8B_LAYERS = 32
+
+
+def kv_cache_bytes(layers: int, kv_heads: int, head_dim: int, tokens: int, elem_bytes: int) -> int:
+    """Size of an uncompressed K+V cache."""
+    return 2 * layers * kv_heads * head_dim * tokens * elem_bytes
+
+
+def decode_bytes(context_lens, num_q_heads, num_kv_heads, head_dim, elem_bytes, block_size=16) -> dict:
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    S = ctx.size
+    kv = kv_cache_bytes(1, num_kv_heads, head_dim, int(ctx.sum()), elem_bytes)
+    qo = 2 * S * num_q_heads * head_dim * elem_bytes
+    tables = 4 * int(((ctx + block_size - 1) // block_size).sum()) + 4 * S
+    return {"kv": kv, "q_out": qo, "tables": tables, "total": kv + qo + tables}
+
+
+def decode_flops(context_lens, num_q_heads, head_dim) -> int:
+    """2*D for q.k plus 2*D for p.v per (q-head, visible key)."""
+    return int(4 * head_dim * num_q_heads * np.asarray(context_lens, dtype=np.int64).sum())

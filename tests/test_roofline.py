@@ -1,0 +1,27 @@
+"""Byte accounting used by the benchmark, pinned to the worked example the
+tokenspeed deep-dive prints (section 7-2)."""
+
+import json
+import os
+
+import numpy as np
+
+from paged_kv_decode_02_amd import roofline
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def test_kv_bytes_worked_example():
+    g = json.load(open(os.path.join(HERE, "golden", "kv_bytes_llama8b.json")))
+    got = roofline.kv_cache_bytes(g["layers"], g["kv_heads"], g["head_dim"], g["tokens"], g["bytes_per_element"])
+    assert got == g["kv_bytes"] == 512 * 2**20
+
+
+def test_decode_bytes_counts_kv_once_per_kv_head():
+    b = roofline.decode_bytes([4096], num_q_heads=32, num_kv_heads=8, head_dim=128, elem_bytes=2)
+    assert b["kv"] * 32 == 536870912  # one layer of the worked example
+    b4 = roofline.decode_bytes([4096], num_q_heads=8, num_kv_heads=8, head_dim=128, elem_bytes=2)
+    assert b4["kv"] == b["kv"]  # GQA does not multiply KV traffic
+    assert b["tables"] == 4 * 256 + 4
+    assert b["q_out"] == 2 * 32 * 128 * 2
+    assert roofline.decode_flops(np.array([10, 20]), 32, 128) == 4 * 128 * 32 * 30
