@@ -32,11 +32,8 @@ extern "C" size_t pa_decode_workspace_size(int32_t max_num_seqs, int32_t num_kv_
   if (max_num_seqs < 0 || num_kv_heads < 1 || gqa_ratio < 1 || head_dim < 1 || max_total_pages < 0 ||
       split_pages < 0)
     return 0;
-  // Items = sum over sequences of ceil(pages / C) <= S + pages / C, with C
-  // at least the smallest split the planner may pick.
-  const int64_t c = split_pages > 0 ? split_pages : kMinSplitPages;
-  const int64_t items = static_cast<int64_t>(max_num_seqs) + max_total_pages / c;
-  return partial_layout(items, num_kv_heads, gqa_ratio, head_dim).bytes;
+  const int64_t waves = max_waves_per_head(max_total_pages, num_kv_heads, split_pages);
+  return partial_layout(waves, max_num_seqs, num_kv_heads, gqa_ratio, head_dim).bytes;
 }
 
 extern "C" int pa_decode(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,
@@ -65,24 +62,14 @@ extern "C" int pa_decode(void* out, float* lse_out, const void* q, const void* k
       return fail(PA_EINVAL, "pa_decode: context_lens[" + std::to_string(s) + "] exceeds the block table");
     total_pages += (L + block_size - 1) / block_size;
   }
-  const int32_t C = split_pages > 0 ? split_pages : auto_split_pages(total_pages, num_kv_heads);
-  int64_t items = 0;
-  bool any_multi = false;
-  for (int32_t s = 0; s < num_seqs; ++s) {
-    const int64_t n = splits_for((context_lens_host[s] + block_size - 1) / block_size, 0, C);
-    items += n;
-    any_multi |= n > 1;
-  }
-  if (items > (int64_t(1) << 31) - 1) return fail(PA_EUNSUPPORTED, "pa_decode: too many work items");
-  const PartialLayout need = partial_layout(items, num_kv_heads, gqa_ratio, head_dim);
-  if (any_multi && need.bytes > workspace_bytes)
-    return fail(PA_EWORKSPACE, "pa_decode: workspace holds " + std::to_string(workspace_bytes) + " bytes, plan needs " +
-                                   std::to_string(need.bytes));
-  // The kernels bound every partial write by the capacity of the workspace
-  // actually passed, so a device-side length that disagrees with the host
-  // copy cannot write past it.
-  const int64_t cap = capacity_items(workspace_bytes, num_kv_heads, gqa_ratio, head_dim);
-  const PartialLayout pl = partial_layout(cap, num_kv_heads, gqa_ratio, head_dim);
+  if (total_pages > (int64_t(1) << 31) - 1) return fail(PA_EUNSUPPORTED, "pa_decode: more than 2^31-1 pages");
+  // The workspace must hold the largest plan this batch could get, so that
+  // a call never depends on the occupancy the device reports.
+  const PartialLayout worst = partial_layout(max_waves_per_head(total_pages, num_kv_heads, split_pages), num_seqs,
+                                             num_kv_heads, gqa_ratio, head_dim);
+  if (worst.bytes > workspace_bytes)
+    return fail(PA_EWORKSPACE, "pa_decode: workspace holds " + std::to_string(workspace_bytes) + " bytes, needs " +
+                                   std::to_string(worst.bytes));
   DecodeLaunch a;
   a.out = out;
   a.lse_out = lse_out;
@@ -99,12 +86,10 @@ extern "C" int pa_decode(void* out, float* lse_out, const void* q, const void* k
   a.num_pages = num_pages;
   a.scale = scale;
   a.dtype = dtype;
-  a.split_pages = C;
-  a.items = items;
-  a.capacity = cap;
-  a.any_multi = any_multi;
-  a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.o_offset);
-  a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.lse_offset);
+  a.split_pages = split_pages;
+  a.total_pages = total_pages;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
   a.stream = stream;
   return launch_decode(a);
 }

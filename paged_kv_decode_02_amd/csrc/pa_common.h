@@ -33,16 +33,50 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// Cross-lane steps without LDS: DPP inside rows of 16 lanes, and gfx950's
+// v_permlane16_swap / v_permlane32_swap across rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppRor4 = 0x124;  // row_ror:4
+constexpr int kDppRor8 = 0x128;  // row_ror:8
+
+// a[l] + a[l ^ 16] in every lane l.
+__device__ __forceinline__ float add_xor16(float a) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// a[l] + a[l ^ 32] in every lane l.
+__device__ __forceinline__ float add_xor32(float a) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float a) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float a) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  v = fmaxf(v, dpp<kDppXor2>(v));
+  v = fmaxf(v, dpp<kDppRor4>(v));
+  v = fmaxf(v, dpp<kDppRor8>(v));
+  return max_xor32(max_xor16(v));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppRor4>(v);
+  v += dpp<kDppRor8>(v);
+  return add_xor32(add_xor16(v));
 }
 
 __device__ __forceinline__ int wave_sum_int(int v) {

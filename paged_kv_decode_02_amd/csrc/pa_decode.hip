@@ -1,33 +1,44 @@
-// Split-KV paged decode attention for gfx950 (MI355X).
+// Paged decode attention for gfx950 (MI355X): stream-K split-KV kernel and
+// log-sum-exp merge.
 //
-// Work item = (sequence s, split j, kv-head g): one wave walks the pages
-// [j*C, min((j+1)*C, pages_s)) of sequence s through its block table and
-// computes, for the G q-heads that share kv-head g, the split's softmax
-// partial (normalised output + log2-sum-exp).  A sequence with a single
-// split writes its final output directly; otherwise a second kernel merges
-// the partials by their log-sum-exp (TokenSpeed deep-dive, sections 7 and
-// 7.1: split-KV partial output + LSE into a workspace, reduced by a second
-// kernel).  Page walk, GQA head packing (one K/V pass serves all G heads
-// of a kv-head, the analog of fold_sq_factor in section 7.2) and the
-// per-step gather follow the PagedAttention cache of the SwiftLLM page,
-// section 3.1.
+// Work split.  For each kv-head, the pages of all sequences are laid end to
+// end (sequence 0's pages, then sequence 1's, ...) and cut into W equal runs
+// of `per` pages; wave w of kv-head g streams run w.  A run can end inside a
+// sequence, so a long sequence is shared by several waves and a wave can
+// cover many short sequences: every wave gets the same number of bytes to
+// read whatever the length mix.  A sequence that one wave covers entirely is
+// written out directly; a sequence shared by several waves leaves one
+// partial (normalised output + log2-sum-exp) per wave, and the merge kernel
+// reduces those by their log-sum-exp.  This is the split-KV / second-pass
+// reduction the TokenSpeed deep-dive describes (sections 7 and 7.1), with
+// the splits placed by byte count instead of a fixed split count.
 //
-// Per iteration a wave consumes one batch of 4 pages = 64 rows:
-//  * K: the 4 (page, kv-head) tiles are read with coalesced 16-byte loads
-//    (each instruction covers 1 KB contiguous), written to LDS with an XOR
-//    swizzle, and read back transposed so that lane t holds row t.  Scores
-//    are then lane-local dot products (bf16 pairs: v_dot2_f32_bf16) against
-//    q, which is wave-uniform and read through the scalar cache.
-//  * V: row-per-instruction dword loads (256 B contiguous per instruction
-//    at D=128 bf16), so lane l holds columns (2l, 2l+1) of every row and
-//    P.V needs no cross-lane reduction; the 64 probabilities of each head
-//    are broadcast through LDS.
-//  * Online softmax per head in the exp2 domain; masked rows are selected
-//    out (never multiplied by zero) so NaN poison in unused rows cannot
-//    leak.
+// Inside a wave: batches of 4 pages (64 rows) of one sequence.
+//  * K: the 4 (page, kv-head) tiles go straight from HBM into LDS with
+//    16-byte global_load_lds (1 KB contiguous per instruction), XOR-swizzled
+//    so that the transposed read (lane t takes row t) is conflict-free; the
+//    next batch's K is fetched while this batch finishes softmax and P.V.
+//  * V: 1 KB contiguous per instruction into registers: lane (grp, chk)
+//    holds 16-byte chunk chk of rows grp, grp+RPI, ...; the next batch's V
+//    is fetched while the next batch's scores are computed.
+//  * Scores: lane = row; q is wave-uniform and read through the scalar
+//    cache as the scalar operand of v_dot2_f32_bf16 (bf16) / v_fma (fp32).
+//    The G q-heads sharing a kv-head all use one pass over K and V (the
+//    analog of fold_sq_factor, TokenSpeed deep-dive section 7.2).
+//  * Online softmax per head in the exp2 domain; rows past the end are
+//    masked by select (never by multiplying by zero) so NaN poison in
+//    unused rows cannot leak.
+//  * P.V: probabilities go through LDS; for bf16 they are rounded to bf16
+//    (round to nearest even) and paired across rows for v_dot2_f32_bf16,
+//    while the normaliser and the log-sum-exp use the float32 values;
+//    fp32 uses v_fma.
+// The page walk follows the block table of the PagedAttention cache
+// (SwiftLLM page, section 3.1); physical page ids are clamped into the pool.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <string>
 #include <vector>
 
 #include "pa_common.h"
@@ -36,333 +47,559 @@
 namespace pa {
 namespace {
 
+// LDS pointer types (DMA destination; opaque q reads).
+typedef __attribute__((address_space(3))) void* LdsPtr;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const u32x4 LdsU4;
+
 template <typename T, int D>
 struct Geom {
-  static constexpr int EB = sizeof(T);              // element bytes
-  static constexpr int RD = D * EB / 4;             // dwords per row
-  static constexpr int NCH = RD / 4;                // 16-byte chunks per row
-  static constexpr int TILE = 16 * RD * 4;          // bytes of one (page, kv-head) tile
-  static constexpr int NKI = 4 * TILE / 1024;       // 1 KB staging loads per batch
-  static constexpr int VH = 64 / RD;                // row halves the V loads split into
-  static constexpr int VT = 64 / VH;                // V rows each lane holds per batch
-  static constexpr int EPD = 4 / EB;                // elements per dword
+  static constexpr int EB = sizeof(T);        // element bytes
+  static constexpr int RD = D * EB / 4;       // dwords per row
+  static constexpr int NCH = RD / 4;          // 16-byte chunks per row
+  static constexpr int TILE = 16 * RD * 4;    // bytes of one (page, kv-head) tile
+  static constexpr int NI = 4 * TILE / 1024;  // 1 KB loads per 4-page batch (K and V each)
+  static constexpr int RPI = 64 / NCH;        // rows one 1 KB load covers
+  static constexpr int EPC = 16 / EB;         // elements per 16-byte chunk
   static_assert(RD == 32 || RD == 64, "row must be 128 or 256 bytes");
+  static_assert(NI * RPI == 64, "a batch is 64 rows");
 };
 
-// Pointer into the constant address space: loads through it are scalar.
-typedef __attribute__((address_space(4))) const uint32_t ConstU32;
-typedef __attribute__((address_space(3))) void* LdsPtr;
+// One batch: rows [16*pb, 16*pb + 64) of sequence s, pages clamped to the
+// segment [.., seg_hi) this wave covers.
+struct Batch {
+  int s;       // sequence
+  int L;       // its context length
+  int P;       // its page count
+  int pb;      // first page of the batch
+  int seg_lo;  // first page of the sequence this wave covers
+  int seg_hi;  // one past the last page this wave covers
+  int cs;      // flattened index of the sequence's first page
+  int pid[4];  // physical pages (entries past seg_hi repeat the last one)
+};
 
-template <int EPD>
-__device__ __forceinline__ void unpack(uint32_t w, float (&v)[EPD]) {
-  if constexpr (EPD == 2) {
-    v[0] = bf16_lo(w);
-    v[1] = bf16_hi(w);
+__device__ __forceinline__ int pages_of_len(int L, int max_blocks) {
+  const int64_t pg = (static_cast<int64_t>(L) + 15) >> 4;
+  return static_cast<int>(pg < max_blocks ? (pg > 0 ? pg : 0) : max_blocks);
+}
+
+__device__ __forceinline__ void load_pids(const int32_t* __restrict__ block_tables, int max_blocks, int num_pages,
+                                          Batch& b) {
+  const int32_t* bt = block_tables + static_cast<int64_t>(b.s) * max_blocks;
+  if (b.pb + 4 <= b.seg_hi) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b.pid[i] = bt[b.pb + i];
   } else {
-    v[0] = __uint_as_float(w);
+    b.pid[0] = bt[b.pb];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) b.pid[i] = (b.pb + i < b.seg_hi) ? bt[b.pb + i] : b.pid[i - 1];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b.pid[i] = min(max(b.pid[i], 0), num_pages - 1);
+}
+
+template <int EPC>
+__device__ __forceinline__ void unpack_chunk(const uint4& c, float (&v)[EPC]) {
+  if constexpr (EPC == 8) {
+    v[0] = bf16_lo(c.x); v[1] = bf16_hi(c.x);
+    v[2] = bf16_lo(c.y); v[3] = bf16_hi(c.y);
+    v[4] = bf16_lo(c.z); v[5] = bf16_hi(c.z);
+    v[6] = bf16_lo(c.w); v[7] = bf16_hi(c.w);
+  } else {
+    v[0] = __uint_as_float(c.x); v[1] = __uint_as_float(c.y);
+    v[2] = __uint_as_float(c.z); v[3] = __uint_as_float(c.w);
   }
 }
 
-// Physical page ids of table entries [pb, pb+4), clamped into the pool;
-// entries at or past p_hi repeat the last valid one (its tile is then
-// re-read from cache and its rows are masked out).
-__device__ __forceinline__ void load_page_ids(const int32_t* __restrict__ bt, int pb, int p_hi, int num_pages,
-                                              int (&pid)[4]) {
-  if (pb + 4 <= p_hi) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pid[i] = bt[pb + i];
+template <typename T>
+__device__ __forceinline__ float dot_chunk(const uint4& k, uint32_t q0, uint32_t q1, uint32_t q2, uint32_t q3,
+                                           float acc) {
+  if constexpr (sizeof(T) == 2) {
+    acc = dot2_bf16(k.x, q0, acc);
+    acc = dot2_bf16(k.y, q1, acc);
+    acc = dot2_bf16(k.z, q2, acc);
+    acc = dot2_bf16(k.w, q3, acc);
   } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pid[i] = bt[min(pb + i, p_hi - 1)];
+    acc = fmaf(__uint_as_float(k.x), __uint_as_float(q0), acc);
+    acc = fmaf(__uint_as_float(k.y), __uint_as_float(q1), acc);
+    acc = fmaf(__uint_as_float(k.z), __uint_as_float(q2), acc);
+    acc = fmaf(__uint_as_float(k.w), __uint_as_float(q3), acc);
   }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) pid[i] = min(max(pid[i], 0), num_pages - 1);
+  return acc;
 }
+
+// Pair two rows' bf16 values column by column: (lo: row a, hi: row b).
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(64) void split_decode_kernel(
+__global__ __launch_bounds__(64) void stream_decode_kernel(
     T* __restrict__ out, float* __restrict__ lse_out, const T* __restrict__ q, const T* __restrict__ k_pool,
     const T* __restrict__ v_pool, const int32_t* __restrict__ block_tables, const int32_t* __restrict__ ctx,
-    int max_blocks, int S, int Hkv, int num_pages, float scale_log2, int C, int cap, float* __restrict__ part_o,
-    float* __restrict__ part_lse) {
+    int max_blocks, int S, int Hkv, int num_pages, float scale_log2, int per, int total_pages,
+    int32_t* __restrict__ seq_info, float* __restrict__ part_o, float* __restrict__ part_lse) {
   using Gm = Geom<T, D>;
-  constexpr int RD = Gm::RD, NCH = Gm::NCH, TILE = Gm::TILE, NKI = Gm::NKI, VH = Gm::VH, VT = Gm::VT,
-                EPD = Gm::EPD;
+  constexpr int RD = Gm::RD, NCH = Gm::NCH, TILE = Gm::TILE, NI = Gm::NI, RPI = Gm::RPI, EPC = Gm::EPC;
+  constexpr bool BF16 = sizeof(T) == 2;
+  constexpr int per_tile = TILE / 1024;  // 1 KB loads per page tile
+  constexpr int CG = (8 / G) < 1 ? 1 : ((8 / G) > 4 ? 4 : (8 / G));  // K chunks per QK step
+  static_assert(NCH % CG == 0, "chunk groups must tile the row");
+  constexpr int QU4 = G * NCH;               // 16-byte chunks of the G q rows
+  constexpr int QPL = (QU4 + 63) / 64;        // of them per lane when loading
   __shared__ uint4 k_lds[64 * NCH];
-  __shared__ __align__(16) float p_lds[G * 64];
+  __shared__ uint4 q_lds[QU4];
+  __shared__ __align__(16) uint32_t p_lds[G * 64];  // fp32 bits, or bf16 in the first half
 
   const int lane = lane_id();
+  const int grp = lane / NCH;  // V layout: row group of this lane
+  const int chk = lane % NCH;  // V layout: 16-byte column chunk of this lane
+  const int w = blockIdx.x;
   const int kvh = blockIdx.y;
   const int Hq = Hkv * G;
   const char* kbytes = reinterpret_cast<const char*>(k_pool);
   const char* vbytes = reinterpret_cast<const char*>(v_pool);
 
-  // Normally the grid has one wave per item; if the device lengths imply
-  // more items than the host planned, waves take the extra ones in turn.
-  for (int x = blockIdx.x, total = 0x7fffffff; x < total; x += gridDim.x) {
-    ItemLoc loc;
-    if (!locate_item(ctx, nullptr, S, max_blocks, C, x, loc)) return;
-    // The lookup is wave-uniform; say so, so that everything derived from it
-    // lives in scalar registers and branches on it are scalar branches.
-    total = __builtin_amdgcn_readfirstlane(loc.total);
-    const int s = __builtin_amdgcn_readfirstlane(loc.s);
-    const int split_j = __builtin_amdgcn_readfirstlane(loc.j);
-    const int split_n = __builtin_amdgcn_readfirstlane(loc.ns);
-    const int L = ctx[s];
-    const int64_t pg = (static_cast<int64_t>(L) + 15) >> 4;
-    const int pages = static_cast<int>(pg < max_blocks ? pg : max_blocks);
-    const int p_lo = split_j * C;
-    const int p_hi = min(p_lo + C, pages);
-    const int t_hi = min(p_hi * 16, L);
-    const int32_t* bt = block_tables + static_cast<int64_t>(s) * max_blocks;
-    const uint4* qh = reinterpret_cast<const uint4*>(q + (static_cast<int64_t>(s) * Hq + kvh * G) * D);
+  const int run_a = w * per;
+  const int run_b = min(run_a + per, total_pages);
+  if (run_a >= run_b) return;
 
-    float m[G], l[G], acc[G][EPD];
+  // Per-lane offsets inside a page tile.  K: instruction i of a tile fills
+  // LDS slots 64i..64i+63 of that tile's rows; slot -> (row, chunk) with the
+  // chunk XOR-swizzled by the row.  V: lane = (row group, chunk).
+  uint32_t koff[per_tile];
+#pragma unroll
+  for (int r = 0; r < per_tile; ++r) {
+    const int slot = r * 64 + lane;
+    const int row = slot / NCH;
+    const int ch = (slot % NCH) ^ (row % NCH);
+    koff[r] = row * (RD * 4) + ch * 16;
+  }
+  const uint32_t voff = grp * (RD * 4) + chk * 16;
+  // p slot of the row this lane scores: the rows a V row group holds are
+  // contiguous, so its P.V read is one run.
+  const int pslot = (lane % RPI) * NI + lane / RPI;
+
+  // Where the run starts: sequence s0 and its first flattened page.
+  ItemLoc loc;
+  if (!locate_item(ctx, nullptr, S, max_blocks, 1, run_a, loc)) return;
+  const int s0 = __builtin_amdgcn_readfirstlane(loc.s);
+
+  Batch cur;
+  cur.s = s0;
+  cur.L = ctx[s0];
+  cur.P = pages_of_len(cur.L, max_blocks);
+  cur.cs = __builtin_amdgcn_readfirstlane(loc.base);
+  cur.seg_lo = run_a - cur.cs;
+  cur.seg_hi = min(cur.P, run_b - cur.cs);
+  cur.pb = cur.seg_lo;
+  load_pids(block_tables, max_blocks, num_pages, cur);
+
+  uint4 vr[NI];
+  auto issue_k = [&](const Batch& b) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const char* tile = kbytes + (static_cast<int64_t>(b.pid[i / per_tile]) * Hkv + kvh) * TILE;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(tile + koff[i % per_tile]),
+                                       (LdsPtr)(&k_lds[i * 64]), 16, 0, 0);
+    }
+  };
+  // `dep` is a value computed after the last use of vr: routing the offset
+  // through an opaque asm that reads it keeps the compiler from hoisting
+  // the next batch's V loads above this batch's P.V (which would need a
+  // second set of 4*NI registers).
+  auto issue_v = [&](const Batch& b, float dep) {
+    uint32_t vo = voff;
+    asm volatile("" : "+v"(vo) : "v"(dep));
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row0 = i * RPI;
+      const char* tile = vbytes + (static_cast<int64_t>(b.pid[row0 / 16]) * Hkv + kvh) * TILE;
+      vr[i] = *reinterpret_cast<const uint4*>(tile + (row0 % 16) * (RD * 4) + vo);
+    }
+  };
+
+  // The G q rows of sequence s for this kv-head, into registers; written
+  // to LDS when that sequence's first batch is scored.
+  uint4 qreg[QPL];
+  auto load_q = [&](int s) {
+    const uint4* src = reinterpret_cast<const uint4*>(q + (static_cast<int64_t>(s) * Hq + kvh * G) * D);
+#pragma unroll
+    for (int i = 0; i < QPL; ++i) {
+      const int u = i * 64 + lane;
+      qreg[i] = src[u < QU4 ? u : QU4 - 1];
+    }
+  };
+  auto store_q = [&]() {
+#pragma unroll
+    for (int i = 0; i < QPL; ++i) {
+      const int u = i * 64 + lane;
+      if (u < QU4) q_lds[u] = qreg[i];
+    }
+  };
+
+  float m[G], l[G], acc[G][EPC];
+  auto reset = [&]() {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       m[h] = -INFINITY;
       l[h] = 0.f;
 #pragma unroll
-      for (int e = 0; e < EPD; ++e) acc[h][e] = 0.f;
+      for (int e = 0; e < EPC; ++e) acc[h][e] = 0.f;
+    }
+  };
+  reset();
+
+  load_q(cur.s);
+  bool q_pending = true;  // qreg holds q of cur.s, not yet in LDS
+  issue_k(cur);
+  issue_v(cur, 0.f);
+
+  while (true) {
+    // Coordinates of the next batch (same sequence, or the next one).
+    Batch nxt = cur;
+    bool has_next = true;
+    if (cur.pb + 4 < cur.seg_hi) {
+      nxt.pb = cur.pb + 4;
+    } else if (cur.cs + cur.P < run_b && cur.s + 1 < S) {
+      nxt.s = cur.s + 1;
+      nxt.cs = cur.cs + cur.P;
+      nxt.L = ctx[nxt.s];
+      nxt.P = pages_of_len(nxt.L, max_blocks);
+      nxt.seg_lo = 0;
+      nxt.seg_hi = min(nxt.P, run_b - nxt.cs);
+      nxt.pb = 0;
+      has_next = nxt.seg_hi > 0;
+    } else {
+      has_next = false;
+    }
+    if (has_next) load_pids(block_tables, max_blocks, num_pages, nxt);
+
+    // K of this batch (and q, loaded before it) is in LDS / registers once
+    // only V (NI loads) may be outstanding.
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI) : "memory");
+    if (q_pending) {
+      store_q();
+      q_pending = false;
+    }
+    __syncthreads();
+    const bool next_seq = has_next && nxt.s != cur.s;
+    if (next_seq) {
+      load_q(nxt.s);
+      q_pending = true;
     }
 
-    // Page ids of the first batch; later batches' ids are fetched one batch
-    // ahead, while the current batch computes.
-    int pid[4];
-    load_page_ids(bt, p_lo, p_hi, num_pages, pid);
-    // Per-lane byte offsets of the K loads inside a page tile: instruction i
-    // covers rows 4(i%per_tile)..+3 of tile i/per_tile (see below).
-    constexpr int per_tile = TILE / 1024;
-    uint32_t koff[per_tile];
+    // Scores, lane = row: K row chunks and q chunks (one address for the
+    // whole wave, a broadcast read) from LDS, CG chunks at a time.
+    const int nvalid = min(cur.seg_hi * 16, cur.L) - cur.pb * 16;  // rows of this batch (1..64)
+    float sc[G];
 #pragma unroll
-    for (int r = 0; r < per_tile; ++r) {
-      const int slot = r * 64 + lane;   // slot inside the tile's rows
-      const int row = slot / NCH;       // row inside the tile (0..15)
-      const int ch = (slot % NCH) ^ (row % NCH);
-      koff[r] = row * (RD * 4) + ch * 16;
-    }
-    const uint32_t voff = ((VH == 2) ? (lane >> 5) * 32 * (RD * 4) : 0) + (lane % RD) * 4;
-
-    for (int pb = p_lo; pb < p_hi; pb += 4) {
-      const char* ktile[4];
-      const char* vtile[4];
+    for (int h = 0; h < G; ++h) sc[h] = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t t = (static_cast<int64_t>(pid[i]) * Hkv + kvh) * TILE;
-        ktile[i] = kbytes + t;
-        vtile[i] = vbytes + t;
-      }
-      // K: straight from HBM into LDS with 16-byte loads (global_load_lds),
-      // each instruction covering 1 KB contiguous of one page tile.  Lane l
-      // of instruction i fills LDS slot 64*i + l with the chunk the XOR
-      // swizzle assigns to that slot, so the transposed read below (lane t
-      // takes row t) is free of bank conflicts.
+    for (int c0 = 0; c0 < NCH; c0 += CG) {
+      // K and q are read through pointers made opaque per chunk group and
+      // tied to the previous group's result, so each group's reads are
+      // issued after the previous group's math: only CG chunks of K and
+      // G*CG chunks of q are in registers at a time.
+      LdsU4* qp = (LdsU4*)(&q_lds[0]);
+      LdsU4* kp = (LdsU4*)(&k_lds[lane * NCH]);
 #pragma unroll
-      for (int i = 0; i < NKI; ++i) {
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(ktile[i / per_tile] + koff[i % per_tile]),
-                                         (LdsPtr)(&k_lds[i * 64]), 16, 0, 0);
-      }
-      // V: one row (or two half-rows) per instruction, one dword per lane.
-      uint32_t vr[VT];
+      for (int h = 0; h < G; ++h) asm volatile("" : "+v"(qp), "+v"(kp) : "v"(sc[h]));
+      u32x4 kr[CG];
 #pragma unroll
-      for (int t = 0; t < VT; ++t) {
-        // VH == 2: lanes 32..63 read row t + 32, which lives two pages on.
-        const char* base = (VH == 2) ? ((lane >> 5) ? vtile[(t / 16 + 2) & 3] - 32 * (RD * 4) : vtile[t / 16])
-                                     : vtile[t / 16];
-        vr[t] = *reinterpret_cast<const uint32_t*>(base + voff + (t % 16) * (RD * 4));
-      }
-      // Next batch's page ids (scalar loads) while this batch is in flight.
-      int pid_next[4];
-      if (pb + 4 < p_hi) load_page_ids(bt, pb + 4, p_hi, num_pages, pid_next);
-      // Keep every load of the batch ahead of any use, so the whole batch is
-      // in flight at once.
-      __builtin_amdgcn_sched_barrier(0);
-      const int nvalid = t_hi - pb * 16;  // rows of this batch that exist (1..64)
-      if (nvalid < 64) {
-#pragma unroll
-        for (int t = 0; t < VT; ++t) {
-          const int row = (VH == 2) ? t + (lane >> 5) * 32 : t;
-          if (row >= nvalid) vr[t] = 0u;
-        }
-      }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      uint4 kr[NCH];
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) kr[c] = k_lds[lane * NCH + (c ^ (lane % NCH))];
-
-      // Scores: lane = row.  q is wave-uniform: it is re-read from the
-      // scalar cache each batch, one head at a time (the empty asm keeps the
-      // compiler from hoisting all G*D values into scalar registers, which
-      // would spill), and used as the scalar operand of v_dot2.
-      float sc[G];
+      for (int c = 0; c < CG; ++c) kr[c] = kp[(c0 + c) ^ (lane % NCH)];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        sc[h] = 0.f;
-        ConstU32* qrow = (ConstU32*)(uintptr_t)(qh + h * NCH);
-        asm volatile("" : "+s"(qrow));
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-          uint4 qv;
-          qv.x = qrow[4 * c];
-          qv.y = qrow[4 * c + 1];
-          qv.z = qrow[4 * c + 2];
-          qv.w = qrow[4 * c + 3];
-          if constexpr (EPD == 2) {
-            sc[h] = dot2_bf16(kr[c].x, qv.x, sc[h]);
-            sc[h] = dot2_bf16(kr[c].y, qv.y, sc[h]);
-            sc[h] = dot2_bf16(kr[c].z, qv.z, sc[h]);
-            sc[h] = dot2_bf16(kr[c].w, qv.w, sc[h]);
-          } else {
-            sc[h] = fmaf(__uint_as_float(kr[c].x), __uint_as_float(qv.x), sc[h]);
-            sc[h] = fmaf(__uint_as_float(kr[c].y), __uint_as_float(qv.y), sc[h]);
-            sc[h] = fmaf(__uint_as_float(kr[c].z), __uint_as_float(qv.z), sc[h]);
-            sc[h] = fmaf(__uint_as_float(kr[c].w), __uint_as_float(qv.w), sc[h]);
+        for (int c = 0; c < CG; ++c) {
+          const u32x4 qv = qp[h * NCH + c0 + c];
+          sc[h] = dot_chunk<T>(make_uint4(kr[c].x, kr[c].y, kr[c].z, kr[c].w), qv.x, qv.y, qv.z, qv.w, sc[h]);
+        }
+      }
+      asm volatile("" ::: "memory");
+    }
+    // All LDS reads of this batch's K are done: the next K may land.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (has_next) issue_k(nxt);
+
+    // Online softmax; probabilities to LDS.
+    const bool valid = lane < nvalid;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float s2 = valid ? sc[h] * scale_log2 : -INFINITY;
+      const float mn = fmaxf(m[h], wave_max(s2));
+      const float alpha = fast_exp2(m[h] - mn);
+      const float p = fast_exp2(s2 - mn);
+      // The normaliser sums the float32 probabilities; for bf16 the P.V
+      // product uses them rounded to bf16 (unbiased, round to nearest even).
+      const uint32_t pbits = BF16 ? bf16_bits_rne(p) : __float_as_uint(p);
+      l[h] = l[h] * alpha + p;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[h][e] *= alpha;
+      m[h] = mn;
+      if constexpr (BF16)
+        reinterpret_cast<uint16_t*>(p_lds)[h * 64 + pslot] = static_cast<uint16_t>(pbits);
+      else
+        p_lds[h * 64 + pslot] = pbits;
+    }
+    // V of this batch: the next K (NI loads) may still be outstanding.
+    if (has_next)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (nvalid < 64) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        if (i * RPI + grp >= nvalid) vr[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+
+    // P.V: lane (grp, chk) accumulates its NI rows into its EPC columns.
+    if constexpr (BF16) {
+      // Probabilities of rows (2k, 2k+1) of the group against V pairs.
+#pragma unroll
+      for (int i8 = 0; i8 < NI; i8 += 8) {
+        uint4 pp[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+          pp[h] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p_lds) + h * 64 + grp * NI + i8);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint4 va = vr[i8 + 2 * u], vb = vr[i8 + 2 * u + 1];
+          const uint32_t vp[8] = {pair_lo(va.x, vb.x), pair_hi(va.x, vb.x), pair_lo(va.y, vb.y), pair_hi(va.y, vb.y),
+                                  pair_lo(va.z, vb.z), pair_hi(va.z, vb.z), pair_lo(va.w, vb.w), pair_hi(va.w, vb.w)};
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const uint32_t pw = u == 0 ? pp[h].x : u == 1 ? pp[h].y : u == 2 ? pp[h].z : pp[h].w;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] = dot2_bf16(vp[e], pw, acc[h][e]);
           }
         }
       }
-      const bool valid = lane < nvalid;
+    } else {
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float s2 = valid ? sc[h] * scale_log2 : -INFINITY;
-        const float mn = fmaxf(m[h], wave_max(s2));
-        const float alpha = fast_exp2(m[h] - mn);
-        const float p = fast_exp2(s2 - mn);
-        l[h] = l[h] * alpha + p;
-#pragma unroll
-        for (int e = 0; e < EPD; ++e) acc[h][e] *= alpha;
-        m[h] = mn;
-        p_lds[h * 64 + lane] = p;
-      }
-      __syncthreads();
-      // P.V: lane owns one dword column of V; rows are uniform per step.
-      const int rbase = (VH == 2) ? (lane >> 5) * 32 : 0;
-#pragma unroll
-      for (int t4 = 0; t4 < VT / 4; ++t4) {
+      for (int i4 = 0; i4 < NI; i4 += 4) {
         float4 p4[G];
 #pragma unroll
-        for (int h = 0; h < G; ++h) p4[h] = *reinterpret_cast<const float4*>(&p_lds[h * 64 + rbase + t4 * 4]);
+        for (int h = 0; h < G; ++h) p4[h] = *reinterpret_cast<const float4*>(&p_lds[h * 64 + grp * NI + i4]);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          float v[EPD];
-          unpack<EPD>(vr[t4 * 4 + u], v);
+          float v[EPC];
+          unpack_chunk<EPC>(vr[i4 + u], v);
 #pragma unroll
           for (int h = 0; h < G; ++h) {
             const float p = u == 0 ? p4[h].x : u == 1 ? p4[h].y : u == 2 ? p4[h].z : p4[h].w;
 #pragma unroll
-            for (int e = 0; e < EPD; ++e) acc[h][e] = fmaf(p, v[e], acc[h][e]);
+            for (int e = 0; e < EPC; ++e) acc[h][e] = fmaf(p, v[e], acc[h][e]);
           }
         }
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pid[i] = pid_next[i];
     }
+    const bool seg_end = cur.pb + 4 >= cur.seg_hi;
+    if (has_next && !seg_end) issue_v(nxt, acc[G - 1][EPC - 1]);
 
-    // Finish the split.
-    const int dw = lane % RD;
-    const bool writer = (VH == 1) || (lane < 32);
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float lt = wave_sum(l[h]);
-      const float inv = 1.0f / lt;
-      float o[EPD];
-#pragma unroll
-      for (int e = 0; e < EPD; ++e) {
-        float a = acc[h][e];
-        if constexpr (VH == 2) a += __shfl_xor(a, 32, 64);
-        o[e] = a * inv;
+    if (seg_end) {
+      // End of this wave's part of sequence cur.s: sum the row groups,
+      // normalise, write the output (whole sequence) or a partial.
+      const int s = cur.s;
+      const bool whole = cur.seg_lo == 0 && cur.seg_hi == cur.P;
+      const int slot = (s == s0) ? 0 : 1;
+      if (cur.seg_lo == 0 && kvh == 0 && lane == 0) {
+        seq_info[4 * s + 0] = w;
+        seq_info[4 * s + 1] = (cur.cs + cur.P - 1) / per;  // last wave on the sequence
+        seq_info[4 * s + 2] = slot;
+        seq_info[4 * s + 3] = 0;
       }
-      const float lse2 = m[h] + fast_log2(lt);
-      const int hq = kvh * G + h;
-      if (split_n == 1) {
-        const int64_t row = static_cast<int64_t>(s) * Hq + hq;
-        if (writer) {
-          if constexpr (EPD == 2) {
-            const uint32_t packed = bf16_bits_rne(o[0]) | (bf16_bits_rne(o[1]) << 16);
-            reinterpret_cast<uint32_t*>(out)[row * RD + dw] = packed;
-          } else {
-            reinterpret_cast<float*>(out)[row * D + dw] = o[0];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          float a = acc[h][e];
+          if constexpr (NCH == 8) a += dpp<kDppRor8>(a);  // rows 8 apart share a row of 16
+          acc[h][e] = add_xor32(add_xor16(a));
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float lt = wave_sum(l[h]);
+        const float inv = 1.0f / lt;
+        const float lse2 = m[h] + fast_log2(lt);
+        const bool mine = (h % RPI) == grp;  // one row group writes each head
+        if (whole) {
+          const int64_t row = static_cast<int64_t>(s) * Hq + kvh * G + h;
+          if (mine) {
+            if constexpr (EPC == 8) {
+              uint4 o;
+              o.x = bf16_bits_rne(acc[h][0] * inv) | (bf16_bits_rne(acc[h][1] * inv) << 16);
+              o.y = bf16_bits_rne(acc[h][2] * inv) | (bf16_bits_rne(acc[h][3] * inv) << 16);
+              o.z = bf16_bits_rne(acc[h][4] * inv) | (bf16_bits_rne(acc[h][5] * inv) << 16);
+              o.w = bf16_bits_rne(acc[h][6] * inv) | (bf16_bits_rne(acc[h][7] * inv) << 16);
+              reinterpret_cast<uint4*>(out)[row * NCH + chk] = o;
+            } else {
+              reinterpret_cast<float4*>(out)[row * NCH + chk] =
+                  make_float4(acc[h][0] * inv, acc[h][1] * inv, acc[h][2] * inv, acc[h][3] * inv);
+            }
           }
-        }
-        if (lse_out && lane == 0) lse_out[row] = lse2 * kLn2;
-      } else if (x < cap) {
-        const int64_t r = (static_cast<int64_t>(x) * Hkv + kvh) * G + h;
-        if (writer) {
+          if (lse_out && lane == 0) lse_out[row] = lse2 * kLn2;
+        } else {
+          const int64_t r = ((static_cast<int64_t>(w) * Hkv + kvh) * 2 + slot) * G + h;
+          if (mine) {
+            float4* dst = reinterpret_cast<float4*>(part_o + r * D + chk * EPC);
 #pragma unroll
-          for (int e = 0; e < EPD; ++e) part_o[r * D + dw * EPD + e] = o[e];
+            for (int e = 0; e < EPC; e += 4)
+              dst[e / 4] = make_float4(acc[h][e] * inv, acc[h][e + 1] * inv, acc[h][e + 2] * inv, acc[h][e + 3] * inv);
+          }
+          if (lane == 0) part_lse[r] = lse2;
         }
-        if (lane == 0) part_lse[r] = lse2;
       }
+      // The next V is fetched only now, so the finalisation above does not
+      // hold a second batch of V in registers.
+      if (has_next) issue_v(nxt, m[G - 1]);
+      reset();
     }
+    if (!has_next) break;
+    cur = nxt;
   }
 }
 
-// Merge the split partials of one (sequence, kv-head): out = sum_j a_j o_j /
-// sum_j a_j with a_j = 2^(lse_j - max lse), lse = max + log2(sum a_j).
+// Merge the partials of one (sequence, kv-head): the waves w0..w1 that
+// shared the sequence each left (o_w, lse_w) per head; out = sum_w a_w o_w /
+// sum_w a_w with a_w = 2^(lse_w - max lse), lse = max + log2(sum a_w).  Lane
+// j holds wave j's weights; lane d holds output columns; four waves'
+// partial rows are loaded together.
 template <typename T, int D, int G>
-__global__ __launch_bounds__(64) void merge_kernel(T* __restrict__ out, float* __restrict__ lse_out,
-                                                   const int32_t* __restrict__ ctx, int max_blocks, int S, int Hkv,
-                                                   int C, int cap, const float* __restrict__ part_o,
+__global__ __launch_bounds__(64) void merge_kernel(T* __restrict__ out, float* __restrict__ lse_out, int Hkv, int W,
+                                                   const int32_t* __restrict__ seq_info,
+                                                   const float* __restrict__ part_o,
                                                    const float* __restrict__ part_lse) {
   constexpr int EPL = D / 64;  // output elements per lane
   const int lane = lane_id();
   const int s = blockIdx.x;
   const int kvh = blockIdx.y;
   const int Hq = Hkv * G;
-  int base, ns;
-  sequence_items(ctx, nullptr, S, max_blocks, C, s, base, ns);
-  if (ns <= 1 || base + ns > cap) return;
+  const int w0 = seq_info[4 * s + 0];
+  const int w1 = seq_info[4 * s + 1];
+  const int slot0 = seq_info[4 * s + 2];
+  if (w1 <= w0 || w0 < 0 || w1 >= W || slot0 < 0 || slot0 > 1) return;
+  const int n = w1 - w0 + 1;
+  // Partial row of (wave w0 + j, head h).
+  auto prow = [&](int j, int h) -> int64_t {
+    const int slot = j == 0 ? slot0 : 0;
+    return ((static_cast<int64_t>(w0 + j) * Hkv + kvh) * 2 + slot) * G + h;
+  };
+  float M[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) M[h] = -INFINITY;
+  for (int j = lane; j < n; j += 64) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) M[h] = fmaxf(M[h], part_lse[prow(j, h)]);
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) M[h] = wave_max(M[h]);
+  float acc[G][EPL], wsum[G];
+#pragma unroll
   for (int h = 0; h < G; ++h) {
-    const int64_t r0 = (static_cast<int64_t>(base) * Hkv + kvh) * G + h;
-    const int64_t stride = static_cast<int64_t>(Hkv) * G;
-    float M = -INFINITY;
-    for (int j = lane; j < ns; j += 64) M = fmaxf(M, part_lse[r0 + j * stride]);
-    M = wave_max(M);
-    float o[EPL];
+    wsum[h] = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-    float wsum = 0.f;
-    for (int j = 0; j < ns; ++j) {
-      const int64_t r = r0 + j * stride;
-      const float a = fast_exp2(part_lse[r] - M);
-      wsum += a;
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
+  for (int j0 = 0; j0 < n; j0 += 64) {
+    const int j = j0 + lane;
+    float wt[G];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) o[e] = fmaf(a, part_o[r * D + lane * EPL + e], o[e]);
+    for (int h = 0; h < G; ++h) {
+      wt[h] = j < n ? fast_exp2(part_lse[prow(min(j, n - 1), h)] - M[h]) : 0.f;
+      wsum[h] += wt[h];
     }
-    const float inv = 1.0f / wsum;
+    const int cnt = min(64, n - j0);
+    for (int jj = 0; jj < cnt; jj += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int jx = min(jj + u, cnt - 1);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float* src = part_o + prow(j0 + jx, h) * D + lane * EPL;
+          const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt[h]), jx));
+          const float a = (jj + u < cnt) ? wj : 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(a, src[e], acc[h][e]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float ws = wave_sum(wsum[h]);
+    const float inv = 1.0f / ws;
     const int64_t row = static_cast<int64_t>(s) * Hq + kvh * G + h;
     if constexpr (sizeof(T) == 2) {
       if constexpr (EPL == 2) {
         reinterpret_cast<uint32_t*>(out)[row * (D / 2) + lane] =
-            bf16_bits_rne(o[0] * inv) | (bf16_bits_rne(o[1] * inv) << 16);
+            bf16_bits_rne(acc[h][0] * inv) | (bf16_bits_rne(acc[h][1] * inv) << 16);
       } else {
-        reinterpret_cast<uint16_t*>(out)[row * D + lane] = static_cast<uint16_t>(bf16_bits_rne(o[0] * inv));
+        reinterpret_cast<uint16_t*>(out)[row * D + lane] = static_cast<uint16_t>(bf16_bits_rne(acc[h][0] * inv));
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) reinterpret_cast<float*>(out)[row * D + lane * EPL + e] = o[e] * inv;
+      for (int e = 0; e < EPL; ++e) reinterpret_cast<float*>(out)[row * D + lane * EPL + e] = acc[h][e] * inv;
     }
-    if (lse_out && lane == 0) lse_out[row] = (M + fast_log2(wsum)) * kLn2;
+    if (lse_out && lane == 0) lse_out[row] = (M[h] + fast_log2(ws)) * kLn2;
   }
+}
+
+// Resident waves of one kernel on the current device (cached per device).
+template <typename KernelFn>
+int resident_waves(KernelFn fn, std::atomic<int>* cache) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0, blocks = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, 64, 0) != hipSuccess) return 0;
+  v = std::max(1, cus * blocks);
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
 }
 
 template <typename T, int D, int G>
 int launch_typed(const DecodeLaunch& a) {
+  static std::atomic<int> occ_cache[64];
+  auto kern = stream_decode_kernel<T, D, G>;
+  int64_t per = a.split_pages;
+  if (per <= 0) {
+    // Fill the GPU once: as many waves as can be resident, spread over the
+    // kv-heads, each streaming the same number of pages.
+    const int res = resident_waves(kern, occ_cache);
+    if (res <= 0) return fail(PA_EHIP, "pa_decode: occupancy query failed");
+    const int64_t per_head = std::max<int64_t>(1, std::min<int64_t>(res, kMaxResidentWaves) / a.num_kv_heads);
+    per = std::max<int64_t>(kMinPagesPerWave, (a.total_pages + per_head - 1) / per_head);
+  }
+  const int64_t W = (a.total_pages + per - 1) / per;
+  if (W > 0x7fffffff) return fail(PA_EUNSUPPORTED, "pa_decode: too many waves");
+  const PartialLayout pl = partial_layout(W, a.num_seqs, a.num_kv_heads, a.gqa, a.head_dim);
+  if (pl.bytes > a.workspace_bytes)
+    return fail(PA_EWORKSPACE, "pa_decode: workspace holds " + std::to_string(a.workspace_bytes) +
+                                   " bytes, this batch needs " + std::to_string(pl.bytes));
+  char* ws = static_cast<char*>(a.workspace);
+  int32_t* seq_info = reinterpret_cast<int32_t*>(ws + pl.info_offset);
+  float* part_lse = reinterpret_cast<float*>(ws + pl.lse_offset);
+  float* part_o = reinterpret_cast<float*>(ws + pl.o_offset);
   hipStream_t st = static_cast<hipStream_t>(a.stream);
   const float scale_log2 = a.scale * kLog2e;
-  const int gx = static_cast<int>(std::min<int64_t>(a.items, 0x7fffffff));
   profile_before(a.stream);
-  hipLaunchKernelGGL((split_decode_kernel<T, D, G>), dim3(gx, a.num_kv_heads), dim3(64), 0, st,
-                     static_cast<T*>(a.out), a.lse_out, static_cast<const T*>(a.q), static_cast<const T*>(a.k_pool),
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(W), a.num_kv_heads), dim3(64), 0, st, static_cast<T*>(a.out),
+                     a.lse_out, static_cast<const T*>(a.q), static_cast<const T*>(a.k_pool),
                      static_cast<const T*>(a.v_pool), a.block_tables, a.context_lens, a.max_blocks, a.num_seqs,
-                     a.num_kv_heads, static_cast<int>(a.num_pages), scale_log2, a.split_pages,
-                     static_cast<int>(a.capacity), a.part_o, a.part_lse);
+                     a.num_kv_heads, static_cast<int>(a.num_pages), scale_log2, static_cast<int>(per),
+                     static_cast<int>(a.total_pages), seq_info, part_o, part_lse);
   profile_after(a.stream);
-  if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_decode: split kernel launch failed");
-  if (a.any_multi) {
+  if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_decode: stream kernel launch failed");
+  // Unless one wave covers everything, some sequence may be shared; the
+  // merge kernel skips the sequences one wave covered.
+  if (W > 1) {
     hipLaunchKernelGGL((merge_kernel<T, D, G>), dim3(a.num_seqs, a.num_kv_heads), dim3(64), 0, st,
-                       static_cast<T*>(a.out), a.lse_out, a.context_lens, a.max_blocks, a.num_seqs, a.num_kv_heads,
-                       a.split_pages, static_cast<int>(a.capacity), a.part_o, a.part_lse);
+                       static_cast<T*>(a.out), a.lse_out, a.num_kv_heads, static_cast<int>(W), seq_info, part_o,
+                       part_lse);
     if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_decode: merge kernel launch failed");
   }
   return PA_OK;

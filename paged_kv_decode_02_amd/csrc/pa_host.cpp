@@ -22,30 +22,21 @@ int fail(int code, const std::string& msg) {
 
 void clear_error() { g_last_error.clear(); }
 
-int32_t auto_split_pages(int64_t total_pages, int32_t num_kv_heads) {
-  // Aim at about kTargetWaves (sequence, split, kv-head) waves so 256 CUs
-  // see several rounds of work and a long sequence is cut into many splits;
-  // never below kMinSplitPages, and a whole number of 4-page batches.
-  int64_t want = (total_pages * num_kv_heads + kTargetWaves - 1) / kTargetWaves;
-  want = std::max<int64_t>(want, kMinSplitPages);
-  want = (want + kBatchPages - 1) / kBatchPages * kBatchPages;
-  return static_cast<int32_t>(std::min<int64_t>(want, 1 << 24));
-}
-
-PartialLayout partial_layout(int64_t items, int32_t num_kv_heads, int32_t gqa, int32_t head_dim) {
+PartialLayout partial_layout(int64_t waves, int64_t num_seqs, int32_t num_kv_heads, int32_t gqa, int32_t head_dim) {
   PartialLayout l;
-  const size_t rows = static_cast<size_t>(items) * num_kv_heads * gqa;
-  l.o_offset = 0;
-  l.lse_offset = align_up(rows * head_dim * sizeof(float));
-  l.bytes = l.lse_offset + align_up(rows * sizeof(float));
+  const size_t rows = static_cast<size_t>(waves) * num_kv_heads * 2 * gqa;
+  l.info_offset = 0;
+  l.lse_offset = align_up(static_cast<size_t>(num_seqs) * 4 * sizeof(int32_t));
+  l.o_offset = l.lse_offset + align_up(rows * sizeof(float));
+  l.bytes = l.o_offset + align_up(rows * head_dim * sizeof(float));
   return l;
 }
 
-int64_t capacity_items(size_t bytes, int32_t num_kv_heads, int32_t gqa, int32_t head_dim) {
-  const size_t per = static_cast<size_t>(num_kv_heads) * gqa * (head_dim + 1) * sizeof(float);
-  int64_t cap = static_cast<int64_t>(bytes / per);
-  while (cap > 0 && partial_layout(cap, num_kv_heads, gqa, head_dim).bytes > bytes) --cap;
-  return std::min<int64_t>(cap, (int64_t(1) << 31) - 1);
+int64_t max_waves_per_head(int64_t total_pages, int32_t num_kv_heads, int32_t split_pages) {
+  if (split_pages > 0) return (total_pages + split_pages - 1) / split_pages;
+  const int64_t by_gpu = (kMaxResidentWaves + num_kv_heads - 1) / num_kv_heads;
+  const int64_t by_pages = (total_pages + kMinPagesPerWave - 1) / kMinPagesPerWave;
+  return std::max<int64_t>(1, std::min(by_gpu, by_pages));
 }
 
 }  // namespace pa

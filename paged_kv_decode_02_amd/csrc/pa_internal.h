@@ -11,10 +11,9 @@
 
 namespace pa {
 
-constexpr int kBlockSize = 16;      // rows per page: the only page size built
-constexpr int kBatchPages = 4;      // pages one wave consumes per iteration (64 rows)
-constexpr int kMinSplitPages = 8;   // smallest automatic split, in pages
-constexpr int kTargetWaves = 4096;  // automatic splits aim at about this many waves
+constexpr int kBlockSize = 16;            // rows per page: the only page size built
+constexpr int kMinPagesPerWave = 4;       // automatic runs are at least one 4-page batch
+constexpr int kMaxResidentWaves = 16384;  // bound on waves resident on one GPU (sizes workspace)
 constexpr size_t kAlign = 256;
 
 // Error reporting: thread-local message + code.
@@ -23,22 +22,18 @@ void clear_error();
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Number of splits sequence s needs, from its page count after `begin_pages`.
-inline int64_t splits_for(int64_t pages, int64_t begin_pages, int64_t split_pages) {
-  const int64_t n = pages - begin_pages;
-  return n > 0 ? (n + split_pages - 1) / split_pages : 0;
-}
-
-// Split size chosen from the batch when the caller passes 0.
-int32_t auto_split_pages(int64_t total_pages, int32_t num_kv_heads);
-
-// Workspace carve-up for the split-KV partials.
+// Workspace carve-up: per-sequence records (first wave, last wave, slot of
+// the first wave) written by the stream kernel for the merge kernel, then
+// two partial slots per (wave, kv-head): log2-sum-exp and output rows.
 struct PartialLayout {
-  size_t o_offset, lse_offset, bytes;
+  size_t info_offset, lse_offset, o_offset, bytes;
 };
-PartialLayout partial_layout(int64_t items, int32_t num_kv_heads, int32_t gqa, int32_t head_dim);
-// Largest item count whose partials fit in `bytes`.
-int64_t capacity_items(size_t bytes, int32_t num_kv_heads, int32_t gqa, int32_t head_dim);
+PartialLayout partial_layout(int64_t waves, int64_t num_seqs, int32_t num_kv_heads, int32_t gqa, int32_t head_dim);
+
+// Waves per kv-head the decode planner may use for a batch of total_pages
+// pages: split_pages > 0 fixes the run length, 0 lets the launcher size runs
+// so the resident waves of the GPU are filled once.
+int64_t max_waves_per_head(int64_t total_pages, int32_t num_kv_heads, int32_t split_pages);
 
 // Everything the decode launcher needs; all pointers already validated.
 struct DecodeLaunch {
@@ -57,12 +52,10 @@ struct DecodeLaunch {
   int64_t num_pages;
   float scale;
   pa_dtype dtype;
-  int32_t split_pages;
-  int64_t items;      // total (sequence, split) work items, from the host copy
-  int64_t capacity;   // partial slots the workspace holds (items index them)
-  bool any_multi;     // some sequence has more than one split
-  float* part_o;      // workspace partial outputs [items, Hkv, G, D]
-  float* part_lse;    // workspace partial log2-sum-exp [items, Hkv, G]
+  int32_t split_pages;  // pages per wave run; 0 = automatic
+  int64_t total_pages;  // sum over sequences of ceil(L / 16), from the host copy
+  void* workspace;
+  size_t workspace_bytes;
   void* stream;
 };
 

@@ -98,10 +98,11 @@ def test_zero_sequences_is_a_no_op():
 def test_workspace_size_covers_plans():
     for S, P in [(1, 1), (64, 9216), (256, 90000), (1024, 20000)]:
         for G in [1, 4, 8]:
-            ws = pa.decode_workspace_size(S, 8, G, 128, P, 0)
-            items = S + P // 8
-            assert ws >= items * 8 * G * 129 * 4
-            assert pa.decode_workspace_size(S, 8, G, 128, P, 1) >= ws
+            auto = pa.decode_workspace_size(S, 8, G, 128, P, 0)
+            assert auto >= 16 * S + 8 * 2 * G * 129 * 4  # per-sequence records + at least one wave
+            fine = pa.decode_workspace_size(S, 8, G, 128, P, 1)
+            assert fine >= P * 8 * 2 * G * 129 * 4  # one wave per page
+            assert pa.decode_workspace_size(S, 8, G, 128, P, 16) <= fine
     assert pa.decode_workspace_size(-1, 8, 4, 128, 10, 0) == 0
 
 
