@@ -34,7 +34,47 @@ def parse():
     ap.add_argument("--split-pages", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES (calibrates HBM traffic counters)")
     return ap.parse_args()
+
+
+KERNEL_SOURCES = ["paged_kv_decode_02_amd/csrc/pa_decode.hip", "paged_kv_decode_02_amd/csrc/pa_common.h"]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel, from the PMC summary
+    committed under profiles/ -- or None when there is none for this
+    workload or the kernel source changed since the counters were taken."""
+    import glob
+    import hashlib
+    import re
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    digest = h.hexdigest()[:16]
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*.md")):
+        for m in re.finditer(r"<!-- traffic: (.*?) -->", open(path).read()):
+            kv = dict(x.split("=", 1) for x in m.group(1).split())
+            if kv.get("workload") == workload and kv.get("source_sha256") == digest:
+                return int(float(kv["fetch_kib"]) * float(kv["fetch_scale"]) * 1024 +
+                           float(kv["write_kib"]) * float(kv["write_scale"]) * 1024)
+    return None
+
+
+def copy_probe(nbytes: int) -> None:
+    """A plain copy of known size: under rocprofv3 --pmc its FETCH_SIZE and
+    WRITE_SIZE give the counters' scale (KiB per byte moved)."""
+    import torch
+
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "copies": 3}), flush=True)
 
 
 def cpu_baseline(lay, q, k, v, budget_s):
@@ -87,6 +127,9 @@ def cpu_baseline(lay, q, k, v, budget_s):
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); this path does not shard across GPUs.",
               file=sys.stderr)
@@ -182,7 +225,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / roofline.HBM_PEAK_GBS, 4),
             "kernel_ms": round(kern_avg, 5),
-            "traffic": None,
+            "traffic": measured_traffic(args.workload),
         },
     }
     if not args.no_cpu_baseline:
