@@ -81,10 +81,12 @@ enum {
 /* ---------------------------------------------------------------------------
  * Decode: one query token per sequence (T = num_seqs).
  *
- * Each (sequence, kv-head) is cut into splits of `split_pages` pages
- * (0 = chosen from the batch); each split computes the G = gqa_ratio
- * q-heads that share its kv-head from one pass over its K/V pages, then the
- * partials of sequences with more than one split are merged by their LSE.
+ * For each kv-head the pages of all sequences are laid end to end and cut
+ * into runs of `split_pages` pages (0 = sized so the GPU's resident waves
+ * are filled once); each wave streams one run and computes the G =
+ * gqa_ratio q-heads that share the kv-head from one pass over K and V.  A
+ * sequence covered by one run is written directly; the partials of a
+ * sequence shared by several runs are merged by their LSE.
  *
  * workspace: device memory of at least pa_decode_workspace_size(...) bytes
  *   for the largest batch it will serve; 256-byte aligned.  Its contents
@@ -113,6 +115,44 @@ int pa_decode(void* out,                      /* device [S, Hq, D] dtype */
               void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Shared-prefix (cascade) decode: one query token per sequence, sequences in
+ * groups whose block tables start with the same prefix pages (shared blocks,
+ * SwiftLLM page section 3.1); the result equals pa_decode on the same
+ * inputs.  The prefix is attended once per group with MFMA -- the group's
+ * (member, q-head) rows against the prefix keys form one dense product
+ * (Tokasaurus page, "dynamic prefix identification": Hydragen / cascade
+ * attention) -- each member's suffix is decoded as in pa_decode, and the two
+ * are merged by log-sum-exp.
+ *
+ * Groups: sequences [group_seq_offsets[g], group_seq_offsets[g+1]) for
+ * g < num_groups, covering 0 .. num_seqs-1 in order; prefix_lens[g] is a
+ * multiple of block_size (0 allowed), shorter than every member's context,
+ * and every member's first prefix_lens[g]/block_size table entries are the
+ * same pages (not checked on this call; see pa_check_block_tables).  Device
+ * arrays and their host twins must hold the same values.
+ * Built for bf16, head_dim 128, gqa_ratio 1, 2, 4, 8, 16.
+ * Errors as pa_decode, plus PA_EINVAL for malformed groups.
+ * ------------------------------------------------------------------------- */
+size_t pa_prefix_cascade_workspace_size(int32_t max_num_seqs, int32_t num_kv_heads, int32_t gqa_ratio,
+                                        int32_t head_dim, int64_t max_total_pages);
+
+int pa_prefix_cascade(void* out,                       /* device [S, Hq, D] */
+                      float* lse_out,                  /* device [S, Hq] or NULL */
+                      const void* q,                   /* device [S, Hq, D] */
+                      const void* k_pool, const void* v_pool, /* device [NP, Hkv, BS, D] */
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens,      /* device [S] */
+                      const int32_t* context_lens_host, /* host [S] */
+                      int32_t num_seqs, int32_t num_groups,
+                      const int32_t* group_seq_offsets,      /* device [G+1] */
+                      const int32_t* group_seq_offsets_host, /* host [G+1] */
+                      const int32_t* prefix_lens,            /* device [G] */
+                      const int32_t* prefix_lens_host,       /* host [G] */
+                      int32_t num_kv_heads, int32_t gqa_ratio, int32_t head_dim, int32_t block_size,
+                      int64_t num_pages, float scale, pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* ---------------------------------------------------------------------------
  * Host-side table check (host copies only, no device access).
  * Every sequence needs ceil(L/block_size) entries in [0, num_pages); a page
  * may appear in more than one table only as a declared shared prefix: for
@@ -133,8 +173,9 @@ const char* pa_last_error(void);
 /* ---------------------------------------------------------------------------
  * Profiling hook (measurement only; changes no result).
  * pa_profile_enable(n) creates n pairs of HIP timing events on this thread;
- * every later call records one pair around its dominant kernel (the split
- * stage of pa_decode) on its stream.  pa_profile_collect() waits for those
+ * every later call records one pair around its dominant kernel (the stream
+ * kernel of pa_decode, the prefix kernel of pa_prefix_cascade) on its
+ * stream.  pa_profile_collect() waits for those
  * events, writes up to `cap` durations in milliseconds to `ms_out`, returns
  * how many it wrote and rewinds the ring.  pa_profile_enable(0) frees the
  * events and stops recording.  Returns a negative code on error.

@@ -1,5 +1,6 @@
 // C-ABI entry points: argument validation and split planning on the host,
 // then the launch.  Nothing here touches device memory.
+#include <algorithm>
 #include <string>
 
 #include "pa_internal.h"
@@ -92,4 +93,112 @@ extern "C" int pa_decode(void* out, float* lse_out, const void* q, const void* k
   a.workspace_bytes = workspace_bytes;
   a.stream = stream;
   return launch_decode(a);
+}
+
+extern "C" size_t pa_prefix_cascade_workspace_size(int32_t max_num_seqs, int32_t num_kv_heads, int32_t gqa_ratio,
+                                                   int32_t head_dim, int64_t max_total_pages) {
+  if (max_num_seqs < 0 || num_kv_heads < 1 || gqa_ratio < 1 || head_dim < 1 || max_total_pages < 0) return 0;
+  const int64_t waves = max_waves_per_head(max_total_pages, num_kv_heads, 0);
+  const size_t stream = partial_layout(waves, max_num_seqs, num_kv_heads, gqa_ratio, head_dim).bytes;
+  return cascade_layout(max_num_seqs, num_kv_heads, gqa_ratio, head_dim, kMaxPrefixSplits, stream).bytes;
+}
+
+extern "C" int pa_prefix_cascade(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                                 const int32_t* context_lens_host, int32_t num_seqs, int32_t num_groups,
+                                 const int32_t* group_seq_offsets, const int32_t* group_seq_offsets_host,
+                                 const int32_t* prefix_lens, const int32_t* prefix_lens_host, int32_t num_kv_heads,
+                                 int32_t gqa_ratio, int32_t head_dim, int32_t block_size, int64_t num_pages,
+                                 float scale, pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  clear_error();
+  if (num_seqs < 0 || num_groups < 0) return fail(PA_EINVAL, "pa_prefix_cascade: negative count");
+  if (num_seqs == 0) return PA_OK;
+  int rc = check_common(out, q, k_pool, v_pool, block_tables, max_blocks, context_lens, context_lens_host,
+                        num_kv_heads, gqa_ratio, head_dim, block_size, num_pages, scale, dtype, workspace,
+                        "pa_prefix_cascade");
+  if (rc) return rc;
+  if (num_groups < 1 || !group_seq_offsets || !group_seq_offsets_host || !prefix_lens || !prefix_lens_host)
+    return fail(PA_EINVAL, "pa_prefix_cascade: groups must be given (device and host copies)");
+  if (!cascade_supported(dtype, head_dim, gqa_ratio))
+    return fail(PA_EUNSUPPORTED, "pa_prefix_cascade: built for bf16, head_dim 128, gqa_ratio 1/2/4/8/16");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(PA_EINVAL, "pa_prefix_cascade: workspace not 256B aligned");
+  if (group_seq_offsets_host[0] != 0 || group_seq_offsets_host[num_groups] != num_seqs)
+    return fail(PA_EINVAL, "pa_prefix_cascade: groups must cover sequences 0 .. num_seqs-1 in order");
+  int64_t suffix_pages = 0;
+  int64_t max_rows = 0;
+  int32_t max_prefix = 0;
+  for (int32_t g = 0; g < num_groups; ++g) {
+    const int32_t a = group_seq_offsets_host[g], b = group_seq_offsets_host[g + 1];
+    if (b < a) return fail(PA_EINVAL, "pa_prefix_cascade: group offsets decrease");
+    const int32_t P = prefix_lens_host[g];
+    if (P < 0 || P % block_size)
+      return fail(PA_EINVAL, "pa_prefix_cascade: prefix_lens[" + std::to_string(g) + "] not a whole number of pages");
+    max_prefix = std::max(max_prefix, P);
+    max_rows = std::max<int64_t>(max_rows, static_cast<int64_t>(b - a) * gqa_ratio);
+    for (int32_t s = a; s < b; ++s) {
+      const int64_t L = context_lens_host[s];
+      if (L < 1) return fail(PA_EINVAL, "pa_prefix_cascade: context_lens[" + std::to_string(s) + "] < 1");
+      if (L > static_cast<int64_t>(max_blocks) * block_size)
+        return fail(PA_EINVAL, "pa_prefix_cascade: context_lens[" + std::to_string(s) + "] exceeds the block table");
+      if (P >= L)
+        return fail(PA_EINVAL, "pa_prefix_cascade: prefix of group " + std::to_string(g) +
+                                   " is not shorter than sequence " + std::to_string(s));
+      suffix_pages += (L + block_size - 1) / block_size - P / block_size;
+    }
+  }
+  if (suffix_pages > (int64_t(1) << 31) - 1) return fail(PA_EUNSUPPORTED, "pa_prefix_cascade: too many pages");
+  // Prefix plan: about 512 workgroups, each a 64-key multiple of the prefix.
+  const int32_t row_chunks =
+      static_cast<int32_t>(std::max<int64_t>(1, (max_rows + kPrefixRowsPerBlock - 1) / kPrefixRowsPerBlock));
+  const int64_t units = static_cast<int64_t>(num_groups) * row_chunks * num_kv_heads;
+  int32_t nks = static_cast<int32_t>(std::min<int64_t>(kMaxPrefixSplits, std::max<int64_t>(1, (512 + units - 1) / units)));
+  int32_t kps = 64;
+  if (max_prefix > 0) {
+    kps = (max_prefix + nks - 1) / nks;
+    kps = (kps + 63) / 64 * 64;
+    nks = (max_prefix + kps - 1) / kps;
+  } else {
+    nks = 1;
+  }
+  const int64_t waves = max_waves_per_head(suffix_pages, num_kv_heads, 0);
+  const size_t stream_bytes = partial_layout(waves, num_seqs, num_kv_heads, gqa_ratio, head_dim).bytes;
+  const CascadeLayout lay = cascade_layout(num_seqs, num_kv_heads, gqa_ratio, head_dim, nks, stream_bytes);
+  if (lay.bytes > workspace_bytes)
+    return fail(PA_EWORKSPACE, "pa_prefix_cascade: workspace holds " + std::to_string(workspace_bytes) +
+                                   " bytes, needs " + std::to_string(lay.bytes));
+  CascadeLaunch c;
+  DecodeLaunch& a = c.base;
+  a.out = out;
+  a.lse_out = lse_out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.max_blocks = max_blocks;
+  a.num_seqs = num_seqs;
+  a.num_kv_heads = num_kv_heads;
+  a.gqa = gqa_ratio;
+  a.head_dim = head_dim;
+  a.num_pages = num_pages;
+  a.scale = scale;
+  a.dtype = dtype;
+  a.split_pages = 0;
+  a.total_pages = suffix_pages;
+  a.workspace = nullptr;
+  a.workspace_bytes = 0;
+  a.stream = stream;
+  c.group_offsets = group_seq_offsets;
+  c.prefix_lens = prefix_lens;
+  c.num_groups = num_groups;
+  c.row_chunks = row_chunks;
+  c.nks = nks;
+  c.kps = kps;
+  c.suffix_pages = suffix_pages;
+  c.layout = lay;
+  c.workspace = workspace;
+  c.workspace_bytes = workspace_bytes;
+  return launch_cascade(c);
 }

@@ -72,6 +72,7 @@ struct Batch {
   int L;       // its context length
   int P;       // its page count
   int pb;      // first page of the batch
+  int B;       // first page of the sequence the walk covers at all (cascade: after the shared prefix)
   int seg_lo;  // first page of the sequence this wave covers
   int seg_hi;  // one past the last page this wave covers
   int cs;      // flattened index of the sequence's first page
@@ -137,7 +138,8 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
     T* __restrict__ out, float* __restrict__ lse_out, const T* __restrict__ q, const T* __restrict__ k_pool,
     const T* __restrict__ v_pool, const int32_t* __restrict__ block_tables, const int32_t* __restrict__ ctx,
     int max_blocks, int S, int Hkv, int num_pages, float scale_log2, int per, int total_pages,
-    int32_t* __restrict__ seq_info, float* __restrict__ part_o, float* __restrict__ part_lse) {
+    int32_t* __restrict__ seq_info, float* __restrict__ part_o, float* __restrict__ part_lse,
+    const int32_t* __restrict__ begin_pages, float* __restrict__ seq_part) {
   using Gm = Geom<T, D>;
   constexpr int RD = Gm::RD, NCH = Gm::NCH, TILE = Gm::TILE, NI = Gm::NI, RPI = Gm::RPI, EPC = Gm::EPC;
   constexpr bool BF16 = sizeof(T) == 2;
@@ -181,16 +183,19 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
 
   // Where the run starts: sequence s0 and its first flattened page.
   ItemLoc loc;
-  if (!locate_item(ctx, nullptr, S, max_blocks, 1, run_a, loc)) return;
+  // (Cascade suffix: only pages from begin_pages[s] on are laid end to end.)
+  if (!locate_item(ctx, begin_pages, S, max_blocks, 1, run_a, loc)) return;
   const int s0 = __builtin_amdgcn_readfirstlane(loc.s);
+  auto first_page = [&](int s, int P) { return begin_pages ? min(max(begin_pages[s], 0), P) : 0; };
 
   Batch cur;
   cur.s = s0;
   cur.L = ctx[s0];
   cur.P = pages_of_len(cur.L, max_blocks);
+  cur.B = first_page(s0, cur.P);
   cur.cs = __builtin_amdgcn_readfirstlane(loc.base);
-  cur.seg_lo = run_a - cur.cs;
-  cur.seg_hi = min(cur.P, run_b - cur.cs);
+  cur.seg_lo = cur.B + (run_a - cur.cs);
+  cur.seg_hi = min(cur.P, cur.B + (run_b - cur.cs));
   cur.pb = cur.seg_lo;
   load_pids(block_tables, max_blocks, num_pages, cur);
 
@@ -260,15 +265,16 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
     bool has_next = true;
     if (cur.pb + 4 < cur.seg_hi) {
       nxt.pb = cur.pb + 4;
-    } else if (cur.cs + cur.P < run_b && cur.s + 1 < S) {
+    } else if (cur.cs + (cur.P - cur.B) < run_b && cur.s + 1 < S) {
       nxt.s = cur.s + 1;
-      nxt.cs = cur.cs + cur.P;
+      nxt.cs = cur.cs + (cur.P - cur.B);
       nxt.L = ctx[nxt.s];
       nxt.P = pages_of_len(nxt.L, max_blocks);
-      nxt.seg_lo = 0;
-      nxt.seg_hi = min(nxt.P, run_b - nxt.cs);
-      nxt.pb = 0;
-      has_next = nxt.seg_hi > 0;
+      nxt.B = first_page(nxt.s, nxt.P);
+      nxt.seg_lo = nxt.B;
+      nxt.seg_hi = min(nxt.P, nxt.B + (run_b - nxt.cs));
+      nxt.pb = nxt.B;
+      has_next = nxt.seg_hi > nxt.seg_lo;
     } else {
       has_next = false;
     }
@@ -401,11 +407,11 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
       // End of this wave's part of sequence cur.s: sum the row groups,
       // normalise, write the output (whole sequence) or a partial.
       const int s = cur.s;
-      const bool whole = cur.seg_lo == 0 && cur.seg_hi == cur.P;
+      const bool whole = cur.seg_lo == cur.B && cur.seg_hi == cur.P;
       const int slot = (s == s0) ? 0 : 1;
-      if (cur.seg_lo == 0 && kvh == 0 && lane == 0) {
+      if (cur.seg_lo == cur.B && kvh == 0 && lane == 0) {
         seq_info[4 * s + 0] = w;
-        seq_info[4 * s + 1] = (cur.cs + cur.P - 1) / per;  // last wave on the sequence
+        seq_info[4 * s + 1] = (cur.cs + (cur.P - cur.B) - 1) / per;  // last wave on the sequence
         seq_info[4 * s + 2] = slot;
         seq_info[4 * s + 3] = 0;
       }
@@ -424,7 +430,19 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
         const float inv = 1.0f / lt;
         const float lse2 = m[h] + fast_log2(lt);
         const bool mine = (h % RPI) == grp;  // one row group writes each head
-        if (whole) {
+        if (whole && seq_part) {
+          // Cascade: the suffix of a sequence one wave covered is still a
+          // partial, to be merged with the shared prefix's.
+          // seq_part: outputs [S][Hq][D], then log2-sum-exp [S][Hq].
+          const int64_t r = static_cast<int64_t>(s) * Hq + kvh * G + h;
+          if (mine) {
+            float4* dst = reinterpret_cast<float4*>(seq_part + r * D + chk * EPC);
+#pragma unroll
+            for (int e = 0; e < EPC; e += 4)
+              dst[e / 4] = make_float4(acc[h][e] * inv, acc[h][e + 1] * inv, acc[h][e + 2] * inv, acc[h][e + 3] * inv);
+          }
+          if (lane == 0) seq_part[static_cast<int64_t>(S) * Hq * D + r] = lse2;
+        } else if (whole) {
           const int64_t row = static_cast<int64_t>(s) * Hq + kvh * G + h;
           if (mine) {
             if constexpr (EPC == 8) {
@@ -562,7 +580,7 @@ int resident_waves(KernelFn fn, std::atomic<int>* cache) {
 }
 
 template <typename T, int D, int G>
-int launch_typed(const DecodeLaunch& a) {
+int launch_typed(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_part, bool merge, StreamPlan* plan) {
   static std::atomic<int> occ_cache[64];
   auto kern = stream_decode_kernel<T, D, G>;
   int64_t per = a.split_pages;
@@ -574,29 +592,34 @@ int launch_typed(const DecodeLaunch& a) {
     const int64_t per_head = std::max<int64_t>(1, std::min<int64_t>(res, kMaxResidentWaves) / a.num_kv_heads);
     per = std::max<int64_t>(kMinPagesPerWave, (a.total_pages + per_head - 1) / per_head);
   }
-  const int64_t W = (a.total_pages + per - 1) / per;
+  const int64_t W = std::max<int64_t>(1, (a.total_pages + per - 1) / per);
   if (W > 0x7fffffff) return fail(PA_EUNSUPPORTED, "pa_decode: too many waves");
   const PartialLayout pl = partial_layout(W, a.num_seqs, a.num_kv_heads, a.gqa, a.head_dim);
   if (pl.bytes > a.workspace_bytes)
     return fail(PA_EWORKSPACE, "pa_decode: workspace holds " + std::to_string(a.workspace_bytes) +
                                    " bytes, this batch needs " + std::to_string(pl.bytes));
+  if (plan) {
+    plan->waves = W;
+    plan->per = static_cast<int32_t>(per);
+    plan->layout = pl;
+  }
   char* ws = static_cast<char*>(a.workspace);
   int32_t* seq_info = reinterpret_cast<int32_t*>(ws + pl.info_offset);
   float* part_lse = reinterpret_cast<float*>(ws + pl.lse_offset);
   float* part_o = reinterpret_cast<float*>(ws + pl.o_offset);
   hipStream_t st = static_cast<hipStream_t>(a.stream);
   const float scale_log2 = a.scale * kLog2e;
-  profile_before(a.stream);
+  if (!begin_pages) profile_before(a.stream);
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(W), a.num_kv_heads), dim3(64), 0, st, static_cast<T*>(a.out),
                      a.lse_out, static_cast<const T*>(a.q), static_cast<const T*>(a.k_pool),
                      static_cast<const T*>(a.v_pool), a.block_tables, a.context_lens, a.max_blocks, a.num_seqs,
                      a.num_kv_heads, static_cast<int>(a.num_pages), scale_log2, static_cast<int>(per),
-                     static_cast<int>(a.total_pages), seq_info, part_o, part_lse);
-  profile_after(a.stream);
+                     static_cast<int>(a.total_pages), seq_info, part_o, part_lse, begin_pages, seq_part);
+  if (!begin_pages) profile_after(a.stream);
   if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_decode: stream kernel launch failed");
   // Unless one wave covers everything, some sequence may be shared; the
   // merge kernel skips the sequences one wave covered.
-  if (W > 1) {
+  if (merge && W > 1) {
     hipLaunchKernelGGL((merge_kernel<T, D, G>), dim3(a.num_seqs, a.num_kv_heads), dim3(64), 0, st,
                        static_cast<T*>(a.out), a.lse_out, a.num_kv_heads, static_cast<int>(W), seq_info, part_o,
                        part_lse);
@@ -606,13 +629,13 @@ int launch_typed(const DecodeLaunch& a) {
 }
 
 template <typename T, int D>
-int launch_g(const DecodeLaunch& a) {
+int launch_g(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_part, bool merge, StreamPlan* plan) {
   switch (a.gqa) {
-    case 1: return launch_typed<T, D, 1>(a);
-    case 2: return launch_typed<T, D, 2>(a);
-    case 4: return launch_typed<T, D, 4>(a);
-    case 8: return launch_typed<T, D, 8>(a);
-    case 16: return launch_typed<T, D, 16>(a);
+    case 1: return launch_typed<T, D, 1>(a, begin_pages, seq_part, merge, plan);
+    case 2: return launch_typed<T, D, 2>(a, begin_pages, seq_part, merge, plan);
+    case 4: return launch_typed<T, D, 4>(a, begin_pages, seq_part, merge, plan);
+    case 8: return launch_typed<T, D, 8>(a, begin_pages, seq_part, merge, plan);
+    case 16: return launch_typed<T, D, 16>(a, begin_pages, seq_part, merge, plan);
   }
   return fail(PA_EUNSUPPORTED, "pa_decode: gqa_ratio not built");
 }
@@ -634,15 +657,17 @@ bool decode_supported(pa_dtype dtype, int32_t head_dim, int32_t gqa) {
   return false;
 }
 
-int launch_decode(const DecodeLaunch& a) {
+int launch_stream(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_part, bool merge, StreamPlan* plan) {
   if (a.dtype == PA_BF16) {
-    if (a.head_dim == 128) return launch_g<uint16_t, 128>(a);
-    if (a.head_dim == 64) return launch_g<uint16_t, 64>(a);
+    if (a.head_dim == 128) return launch_g<uint16_t, 128>(a, begin_pages, seq_part, merge, plan);
+    if (a.head_dim == 64) return launch_g<uint16_t, 64>(a, begin_pages, seq_part, merge, plan);
   } else if (a.dtype == PA_F32) {
-    if (a.head_dim == 64) return launch_g<float, 64>(a);
+    if (a.head_dim == 64) return launch_g<float, 64>(a, begin_pages, seq_part, merge, plan);
   }
   return fail(PA_EUNSUPPORTED, "pa_decode: shape not built");
 }
+
+int launch_decode(const DecodeLaunch& a) { return launch_stream(a, nullptr, nullptr, true, nullptr); }
 
 void profile_before(void* stream) {
   if (g_prof.ev.empty() || g_prof.next + 2 > g_prof.ev.size()) return;

@@ -39,6 +39,19 @@ int64_t max_waves_per_head(int64_t total_pages, int32_t num_kv_heads, int32_t sp
   return std::max<int64_t>(1, std::min(by_gpu, by_pages));
 }
 
+CascadeLayout cascade_layout(int64_t num_seqs, int32_t num_kv_heads, int32_t gqa, int32_t head_dim, int32_t nks,
+                             int64_t stream_bytes) {
+  CascadeLayout l;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_kv_heads * gqa;  // (sequence, q-head)
+  l.begin_offset = 0;
+  l.seq_part_offset = align_up(static_cast<size_t>(num_seqs) * sizeof(int32_t));
+  l.pre_o_offset = l.seq_part_offset + align_up(rows * (head_dim + 1) * sizeof(float));
+  l.pre_lse_offset = l.pre_o_offset + align_up(rows * nks * head_dim * sizeof(float));
+  l.stream_offset = l.pre_lse_offset + align_up(rows * nks * sizeof(float));
+  l.bytes = l.stream_offset + align_up(static_cast<size_t>(stream_bytes));
+  return l;
+}
+
 }  // namespace pa
 
 using namespace pa;

@@ -14,6 +14,8 @@ namespace pa {
 constexpr int kBlockSize = 16;            // rows per page: the only page size built
 constexpr int kMinPagesPerWave = 4;       // automatic runs are at least one 4-page batch
 constexpr int kMaxResidentWaves = 16384;  // bound on waves resident on one GPU (sizes workspace)
+constexpr int kMaxPrefixSplits = 8;       // key splits of a shared prefix (sizes workspace)
+constexpr int kPrefixRowsPerBlock = 256;  // query rows one prefix workgroup takes
 constexpr size_t kAlign = 256;
 
 // Error reporting: thread-local message + code.
@@ -61,6 +63,39 @@ struct DecodeLaunch {
 
 bool decode_supported(pa_dtype dtype, int32_t head_dim, int32_t gqa);
 int launch_decode(const DecodeLaunch& a);
+
+// The stream kernel alone (plus, if `merge`, its merge kernel).  With
+// begin_pages (device, per sequence) only pages from there on are walked;
+// with seq_part, sequences one wave covers are written there as partials
+// instead of to `out`.  The plan actually used comes back in *plan.
+struct StreamPlan {
+  int64_t waves;
+  int32_t per;
+  PartialLayout layout;  // inside a.workspace
+};
+int launch_stream(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_part, bool merge, StreamPlan* plan);
+
+// Shared-prefix (cascade) decode.
+struct CascadeLayout {
+  size_t begin_offset, seq_part_offset, pre_o_offset, pre_lse_offset, stream_offset, bytes;
+};
+CascadeLayout cascade_layout(int64_t num_seqs, int32_t num_kv_heads, int32_t gqa, int32_t head_dim, int32_t nks,
+                             int64_t stream_bytes);
+struct CascadeLaunch {
+  DecodeLaunch base;             // out, q, pools, tables, lengths, shapes, stream
+  const int32_t* group_offsets;  // device [NG+1]
+  const int32_t* prefix_lens;    // device [NG]
+  int32_t num_groups;
+  int32_t row_chunks;  // ceil(max group rows / kPrefixRowsPerBlock)
+  int32_t nks;         // key splits per prefix
+  int32_t kps;         // keys per split (multiple of 64)
+  int64_t suffix_pages;
+  CascadeLayout layout;
+  void* workspace;
+  size_t workspace_bytes;
+};
+bool cascade_supported(pa_dtype dtype, int32_t head_dim, int32_t gqa);
+int launch_cascade(const CascadeLaunch& c);
 
 // Profiling hook: bracket the dominant kernel of a call.
 void profile_before(void* stream);

@@ -30,6 +30,8 @@ PA_EHIP = -4
 EXPORTS = (
     "pa_decode_workspace_size",
     "pa_decode",
+    "pa_prefix_cascade_workspace_size",
+    "pa_prefix_cascade",
     "pa_check_block_tables",
     "pa_last_error",
     "pa_profile_enable",
@@ -64,6 +66,12 @@ def load(path: Optional[str] = None):
     lib.pa_decode.restype = ctypes.c_int
     lib.pa_decode.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                               c_i32, c_i64, ctypes.c_float, ctypes.c_int, c_i32, c_vp, c_sz, c_vp]
+    lib.pa_prefix_cascade_workspace_size.restype = c_sz
+    lib.pa_prefix_cascade_workspace_size.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i64]
+    lib.pa_prefix_cascade.restype = ctypes.c_int
+    lib.pa_prefix_cascade.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_vp, c_vp,
+                                      c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i64, ctypes.c_float, ctypes.c_int,
+                                      c_vp, c_sz, c_vp]
     lib.pa_check_block_tables.restype = ctypes.c_int
     lib.pa_check_block_tables.argtypes = [c_vp, c_i32, c_vp, c_i32, c_i32, c_i64, c_i32, c_vp, c_vp]
     lib.pa_last_error.restype = ctypes.c_char_p
@@ -160,6 +168,51 @@ def decode(out, q, k_pool, v_pool, block_tables, context_lens, context_lens_host
         _dev(context_lens, "context_lens", torch.int32),
         ch.ctypes.data,
         S, Hkv, Hq // Hkv, D, BS, NP, float(scale), _dtype_code(q), int(split_pages),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream_ptr(stream),
+    )
+    return _check(rc)
+
+
+def prefix_cascade_workspace_size(max_num_seqs, num_kv_heads, gqa_ratio, head_dim, max_total_pages) -> int:
+    return int(load().pa_prefix_cascade_workspace_size(max_num_seqs, num_kv_heads, gqa_ratio, head_dim,
+                                                       max_total_pages))
+
+
+def prefix_cascade(out, q, k_pool, v_pool, block_tables, context_lens, context_lens_host, group_seq_offsets,
+                   group_seq_offsets_host, prefix_lens, prefix_lens_host, scale, workspace, lse_out=None,
+                   stream=None):
+    """pa_prefix_cascade on torch tensors (shapes as :func:`decode`);
+    group_seq_offsets [NG+1] / prefix_lens [NG] int32 on the device plus
+    host twins with the same values."""
+    import torch
+
+    S, Hq, D = q.shape
+    NP, Hkv, BS, D2 = k_pool.shape
+    if tuple(out.shape) != (S, Hq, D) or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if tuple(v_pool.shape) != tuple(k_pool.shape) or k_pool.dtype != q.dtype or v_pool.dtype != q.dtype:
+        raise ValueError("k_pool and v_pool must match each other and q's dtype")
+    if D2 != D or Hq % Hkv:
+        raise ValueError("head_dim mismatch or q heads not a multiple of kv heads")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_tables / context_lens must have one row per sequence")
+    ch = _host_i32(context_lens_host, "context_lens_host")
+    goh = _host_i32(group_seq_offsets_host, "group_seq_offsets_host")
+    plh = _host_i32(prefix_lens_host, "prefix_lens_host")
+    NG = plh.size
+    if ch.size != S or goh.size != NG + 1 or group_seq_offsets.numel() != NG + 1 or prefix_lens.numel() != NG:
+        raise ValueError("group arrays must be [NG+1] offsets and [NG] prefix lengths")
+    if lse_out is not None and tuple(lse_out.shape) != (S, Hq):
+        raise ValueError("lse_out must be [S, Hq]")
+    rc = load().pa_prefix_cascade(
+        _dev(out, "out"),
+        _dev(lse_out, "lse_out", torch.float32) if lse_out is not None else None,
+        _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), ch.ctypes.data, S, NG,
+        _dev(group_seq_offsets, "group_seq_offsets", torch.int32), goh.ctypes.data,
+        _dev(prefix_lens, "prefix_lens", torch.int32), plh.ctypes.data,
+        Hkv, Hq // Hkv, D, BS, NP, float(scale), _dtype_code(q),
         _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream_ptr(stream),
     )
     return _check(rc)
