@@ -140,8 +140,9 @@ def main():
     from workloads import values_torch, workload
 
     lay = workload(args.workload, seed=args.seed)
-    if lay.q_lens.max() != 1 or lay.group_seq_offsets is not None:
-        print(f"{args.workload} is not a plain decode batch", file=sys.stderr)
+    cascade = lay.group_seq_offsets is not None
+    if lay.q_lens.max() != 1:
+        print(f"{args.workload} is not a decode batch", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -153,31 +154,44 @@ def main():
     out = torch.empty_like(q)
     S, Hq, D = q.shape
     total_pages = int(((lay.context_lens + 15) // 16).sum())
-    ws = torch.empty(pa.decode_workspace_size(S, lay.num_kv_heads, lay.gqa_ratio, D, total_pages, args.split_pages),
-                     dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    if cascade:
+        go = torch.from_numpy(lay.group_seq_offsets).to(dev)
+        pl = torch.from_numpy(lay.prefix_lens).to(dev)
+        ws = torch.empty(pa.prefix_cascade_workspace_size(S, lay.num_kv_heads, lay.gqa_ratio, D, total_pages),
+                         dtype=torch.uint8, device=dev)
 
-    def step():
-        pa.decode(out, q, k, v, bt, ctx, lay.context_lens, lay.scale, ws, split_pages=args.split_pages,
-                  stream=stream)
+        def step():
+            pa.prefix_cascade(out, q, k, v, bt, ctx, lay.context_lens, go, lay.group_seq_offsets, pl,
+                              lay.prefix_lens, lay.scale, ws, stream=stream)
+    else:
+        ws = torch.empty(pa.decode_workspace_size(S, lay.num_kv_heads, lay.gqa_ratio, D, total_pages,
+                                                  args.split_pages), dtype=torch.uint8, device=dev)
+
+        def step():
+            pa.decode(out, q, k, v, bt, ctx, lay.context_lens, lay.scale, ws, split_pages=args.split_pages,
+                      stream=stream)
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
+    ms_per_step = timed(step, args.steps)
     wall = time.perf_counter() - t0
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
 
-    # Dominant kernel alone: HIP events the library records around the
-    # split-KV launch on the same stream.
+    # Dominant kernel alone: HIP events the library records around it on
+    # the same stream (decode: the stream kernel; cascade: the prefix kernel).
     pa.profile_enable(args.steps)
     for _ in range(args.steps):
         step()
@@ -186,9 +200,41 @@ def main():
     pa.profile_enable(0)
     kern_avg = float(np.mean(kern_ms))
 
-    nb = roofline.decode_bytes(lay.context_lens, lay.num_q_heads, lay.num_kv_heads, D, lay.elem_bytes)
+    if cascade:
+        nb = roofline.cascade_bytes(lay.context_lens, lay.group_seq_offsets, lay.prefix_lens, lay.num_q_heads,
+                                    lay.num_kv_heads, D, lay.elem_bytes)
+        flops = roofline.prefix_flops(lay.group_seq_offsets, lay.prefix_lens, lay.num_q_heads, D)
+        tflops = flops / (kern_avg * 1e-3) / 1e12
+        roof = {
+            "bound": "mfma",
+            "kernel": "prefix_kernel",
+            "achieved": round(tflops, 1),
+            "peak": roofline.MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / roofline.MFMA_BF16_PEAK_TFLOPS, 4),
+            "kernel_ms": round(kern_avg, 5),
+            "traffic": None,
+        }
+        # the same batch through plain decode, for the cascade's speed-up
+        dws = torch.empty(pa.decode_workspace_size(S, lay.num_kv_heads, lay.gqa_ratio, D, total_pages, 0),
+                          dtype=torch.uint8, device=dev)
+        dout = torch.empty_like(q)
+        dec_ms = timed(lambda: pa.decode(dout, q, k, v, bt, ctx, lay.context_lens, lay.scale, dws, stream=stream),
+                       args.steps)
+    else:
+        nb = roofline.decode_bytes(lay.context_lens, lay.num_q_heads, lay.num_kv_heads, D, lay.elem_bytes)
+        achieved = nb["total"] / (kern_avg * 1e-3) / 1e9
+        roof = {
+            "bound": "hbm",
+            "kernel": "stream_decode_kernel",
+            "achieved": round(achieved, 1),
+            "peak": roofline.HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / roofline.HBM_PEAK_GBS, 4),
+            "kernel_ms": round(kern_avg, 5),
+            "traffic": measured_traffic(args.workload),
+        }
     gbs = nb["total"] / (ms_per_step * 1e-3) / 1e9
-    achieved = nb["total"] / (kern_avg * 1e-3) / 1e9
     result = {
         "metric": "paged decode attn KV GB/s (% of HBM peak) + decode tokens/s, Llama-8B shape",
         "value": round(gbs, 1),
@@ -217,17 +263,12 @@ def main():
         "decode_tokens_per_s_32_layers": round(S / (roofline.LLAMA8B_LAYERS * ms_per_step * 1e-3), 1),
         "algorithmic_bytes_per_step": nb["total"],
         "wall_s": round(wall, 3),
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "split_decode_kernel",
-            "achieved": round(achieved, 1),
-            "peak": roofline.HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / roofline.HBM_PEAK_GBS, 4),
-            "kernel_ms": round(kern_avg, 5),
-            "traffic": measured_traffic(args.workload),
-        },
+        "roofline": roof,
     }
+    if cascade:
+        result["prefix_gflop"] = round(flops / 1e9, 3)
+        result["decode_same_batch_ms"] = round(dec_ms, 5)
+        result["cascade_speedup_vs_decode"] = round(dec_ms / ms_per_step, 3)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(lay, q, k, v, args.cpu_seconds)

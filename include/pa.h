@@ -153,6 +153,45 @@ int pa_prefix_cascade(void* out,                       /* device [S, Hq, D] */
                       void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Mixed batch: prefill chunks and decode tokens in one call (decode tokens
+ * of many sequences piggybacked on prefill chunks: SOSP tutorial page,
+ * section 3.3 "SARATHI"; prefill admitted in bounded chunks, each attending
+ * to the cached prefix plus itself: TokenSpeed deep-dive section 5.1, with
+ * the per-segment lengths passed as device + host copies and no defaults,
+ * section 8.2).
+ *
+ * Segment s has q_len = cu_q_lens[s+1] - cu_q_lens[s] >= 1 query tokens at
+ * rows cu_q_lens[s] .. cu_q_lens[s+1]-1 of q / out / lse_out (T =
+ * cu_q_lens[num_segments] rows), and context_lens[s] >= q_len rows in the
+ * pool, its own new rows included (they are written to the pool before the
+ * call).  Its token i sees rows [0, context_lens[s] - q_len + i]: causal
+ * inside the chunk; q_len = 1 is a decode token and sees every row.
+ * Chunks (q_len > 1) run as MFMA tiles of (token, q-head) rows against the
+ * segment's keys, split along the keys and merged by log-sum-exp; decode
+ * tokens run through pa_decode's kernels, so their rows equal pa_decode's.
+ * Chunks are built for bf16, head_dim 128, gqa_ratio 1, 2, 4, 8, 16; a
+ * batch without chunks takes every pa_decode shape.
+ * Returns as pa_decode, plus PA_EINVAL for cu_q_lens[0] != 0, a segment
+ * with no query token or with context_lens[s] < q_len.
+ * ------------------------------------------------------------------------- */
+size_t pa_mixed_chunk_workspace_size(int32_t max_num_tokens, int32_t max_num_segments, int32_t num_kv_heads,
+                                     int32_t gqa_ratio, int32_t head_dim, int64_t max_total_pages);
+
+int pa_mixed_chunk(void* out,                      /* device [T, Hq, D] dtype */
+                   float* lse_out,                 /* device [T, Hq] or NULL */
+                   const void* q,                  /* device [T, Hq, D] dtype */
+                   const void* k_pool, const void* v_pool, /* device [NP, Hkv, BS, D] */
+                   const int32_t* block_tables,    /* device [S, max_blocks_per_seq] */
+                   int32_t max_blocks_per_seq,
+                   const int32_t* cu_q_lens,       /* device [S+1] */
+                   const int32_t* cu_q_lens_host,  /* host [S+1], same values */
+                   const int32_t* context_lens,    /* device [S] */
+                   const int32_t* context_lens_host, /* host [S], same values */
+                   int32_t num_segments, int32_t num_kv_heads, int32_t gqa_ratio, int32_t head_dim,
+                   int32_t block_size, int64_t num_pages, float scale, pa_dtype dtype, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Host-side table check (host copies only, no device access).
  * Every sequence needs ceil(L/block_size) entries in [0, num_pages); a page
  * may appear in more than one table only as a declared shared prefix: for
@@ -173,9 +212,10 @@ const char* pa_last_error(void);
 /* ---------------------------------------------------------------------------
  * Profiling hook (measurement only; changes no result).
  * pa_profile_enable(n) creates n pairs of HIP timing events on this thread;
- * every later call records one pair around its dominant kernel (the stream
- * kernel of pa_decode, the prefix kernel of pa_prefix_cascade) on its
- * stream.  pa_profile_collect() waits for those
+ * every later call records one pair around each of its dominant kernels on
+ * its stream: the stream kernel of pa_decode; the prefix kernel of
+ * pa_prefix_cascade; for pa_mixed_chunk, the chunk kernel(s) (if the batch
+ * has chunks) and then the decode stream kernel (if it has decode tokens).  pa_profile_collect() waits for those
  * events, writes up to `cap` durations in milliseconds to `ms_out`, returns
  * how many it wrote and rewinds the ring.  pa_profile_enable(0) frees the
  * events and stops recording.  Returns a negative code on error.

@@ -2,6 +2,7 @@
 // then the launch.  Nothing here touches device memory.
 #include <algorithm>
 #include <string>
+#include <vector>
 
 #include "pa_internal.h"
 
@@ -201,4 +202,113 @@ extern "C" int pa_prefix_cascade(void* out, float* lse_out, const void* q, const
   c.workspace = workspace;
   c.workspace_bytes = workspace_bytes;
   return launch_cascade(c);
+}
+
+extern "C" size_t pa_mixed_chunk_workspace_size(int32_t max_num_tokens, int32_t max_num_segments,
+                                                int32_t num_kv_heads, int32_t gqa_ratio, int32_t head_dim,
+                                                int64_t max_total_pages) {
+  if (max_num_tokens < 0 || max_num_segments < 0 || num_kv_heads < 1 || gqa_ratio < 1 || head_dim < 1 ||
+      max_total_pages < 0)
+    return 0;
+  const int64_t waves = max_waves_per_head(max_total_pages, num_kv_heads, 0);
+  const size_t stream = partial_layout(waves, max_num_segments, num_kv_heads, gqa_ratio, head_dim).bytes;
+  return mixed_layout(max_num_segments, max_num_tokens, num_kv_heads, gqa_ratio, head_dim, kMaxChunkSplits, stream)
+      .bytes;
+}
+
+extern "C" int pa_mixed_chunk(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, int32_t max_blocks, const int32_t* cu_q_lens,
+                              const int32_t* cu_q_lens_host, const int32_t* context_lens,
+                              const int32_t* context_lens_host, int32_t num_segments, int32_t num_kv_heads,
+                              int32_t gqa_ratio, int32_t head_dim, int32_t block_size, int64_t num_pages, float scale,
+                              pa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  if (num_segments < 0) return fail(PA_EINVAL, "pa_mixed_chunk: num_segments < 0");
+  if (num_segments == 0) return PA_OK;
+  int rc = check_common(out, q, k_pool, v_pool, block_tables, max_blocks, context_lens, context_lens_host,
+                        num_kv_heads, gqa_ratio, head_dim, block_size, num_pages, scale, dtype, workspace,
+                        "pa_mixed_chunk");
+  if (rc) return rc;
+  if (!cu_q_lens || !cu_q_lens_host) return fail(PA_EINVAL, "pa_mixed_chunk: cu_q_lens must be given (device and host)");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(PA_EINVAL, "pa_mixed_chunk: workspace not 256B aligned");
+  if (cu_q_lens_host[0] != 0) return fail(PA_EINVAL, "pa_mixed_chunk: cu_q_lens[0] != 0");
+  std::vector<int32_t> chunk_seg, chunk_tok{0};
+  int64_t decode_pages = 0;
+  int64_t max_rows = 0;
+  int64_t max_keys = 0;
+  for (int32_t s = 0; s < num_segments; ++s) {
+    const int64_t n = static_cast<int64_t>(cu_q_lens_host[s + 1]) - cu_q_lens_host[s];
+    const int64_t L = context_lens_host[s];
+    const std::string at = "[" + std::to_string(s) + "]";
+    if (n < 1) return fail(PA_EINVAL, "pa_mixed_chunk: segment" + at + " has no query token");
+    if (L < n) return fail(PA_EINVAL, "pa_mixed_chunk: context_lens" + at + " is shorter than its query tokens");
+    if (L > static_cast<int64_t>(max_blocks) * block_size)
+      return fail(PA_EINVAL, "pa_mixed_chunk: context_lens" + at + " exceeds the block table");
+    if (n == 1) {
+      decode_pages += (L + block_size - 1) / block_size;
+    } else {
+      chunk_seg.push_back(s);
+      chunk_tok.push_back(chunk_tok.back() + static_cast<int32_t>(n));
+      max_rows = std::max(max_rows, n * gqa_ratio);
+      max_keys = std::max(max_keys, L);
+    }
+  }
+  if (decode_pages > (int64_t(1) << 31) - 1) return fail(PA_EUNSUPPORTED, "pa_mixed_chunk: too many pages");
+  const int32_t num_chunks = static_cast<int32_t>(chunk_seg.size());
+  if (num_chunks > 0 ? !mixed_supported(dtype, head_dim, gqa_ratio) : !decode_supported(dtype, head_dim, gqa_ratio))
+    return fail(PA_EUNSUPPORTED, "pa_mixed_chunk: prefill chunks are built for bf16, head_dim 128, gqa_ratio "
+                                 "1/2/4/8/16");
+  // Chunk plan: row blocks of kPrefixRowsPerBlock (token, q-head) rows;
+  // keys cut into at most kMaxChunkSplits splits of >= kMinChunkSplitKeys.
+  const int32_t row_chunks =
+      static_cast<int32_t>(std::max<int64_t>(1, (max_rows + kPrefixRowsPerBlock - 1) / kPrefixRowsPerBlock));
+  int32_t kps = kMinChunkSplitKeys;
+  int32_t nks = 1;
+  if (num_chunks > 0) {
+    kps = static_cast<int32_t>(std::max<int64_t>(kMinChunkSplitKeys, (max_keys + kMaxChunkSplits - 1) / kMaxChunkSplits));
+    kps = (kps + 63) / 64 * 64;
+    nks = static_cast<int32_t>((max_keys + kps - 1) / kps);
+  }
+  const int64_t waves = max_waves_per_head(decode_pages, num_kv_heads, 0);
+  const size_t stream_bytes = partial_layout(waves, num_segments, num_kv_heads, gqa_ratio, head_dim).bytes;
+  const MixedLayout lay =
+      mixed_layout(num_segments, chunk_tok.back(), num_kv_heads, gqa_ratio, head_dim, nks, stream_bytes);
+  if (lay.bytes > workspace_bytes)
+    return fail(PA_EWORKSPACE, "pa_mixed_chunk: workspace holds " + std::to_string(workspace_bytes) +
+                                   " bytes, needs " + std::to_string(lay.bytes));
+  MixedLaunch m;
+  DecodeLaunch& a = m.base;
+  a.out = out;
+  a.lse_out = lse_out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.max_blocks = max_blocks;
+  a.num_seqs = num_segments;
+  a.num_kv_heads = num_kv_heads;
+  a.gqa = gqa_ratio;
+  a.head_dim = head_dim;
+  a.num_pages = num_pages;
+  a.scale = scale;
+  a.dtype = dtype;
+  a.split_pages = 0;
+  a.total_pages = decode_pages;
+  a.workspace = nullptr;
+  a.workspace_bytes = 0;
+  a.stream = stream;
+  m.cu_q_lens = cu_q_lens;
+  m.chunk_seg = chunk_seg.data();
+  m.chunk_tok = chunk_tok.data();
+  m.num_chunks = num_chunks;
+  m.row_chunks = row_chunks;
+  m.nks = nks;
+  m.kps = kps;
+  m.decode_pages = decode_pages;
+  m.layout = lay;
+  m.workspace = workspace;
+  m.workspace_bytes = workspace_bytes;
+  return launch_mixed(m);
 }

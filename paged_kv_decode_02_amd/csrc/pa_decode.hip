@@ -139,7 +139,7 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
     const T* __restrict__ v_pool, const int32_t* __restrict__ block_tables, const int32_t* __restrict__ ctx,
     int max_blocks, int S, int Hkv, int num_pages, float scale_log2, int per, int total_pages,
     int32_t* __restrict__ seq_info, float* __restrict__ part_o, float* __restrict__ part_lse,
-    const int32_t* __restrict__ begin_pages, float* __restrict__ seq_part) {
+    const int32_t* __restrict__ begin_pages, float* __restrict__ seq_part, const int32_t* __restrict__ q_rows) {
   using Gm = Geom<T, D>;
   constexpr int RD = Gm::RD, NCH = Gm::NCH, TILE = Gm::TILE, NI = Gm::NI, RPI = Gm::RPI, EPC = Gm::EPC;
   constexpr bool BF16 = sizeof(T) == 2;
@@ -226,8 +226,10 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
   // The G q rows of sequence s for this kv-head, into registers; written
   // to LDS when that sequence's first batch is scored.
   uint4 qreg[QPL];
+  // Row of q / out / lse of sequence s (mixed batches: its one token).
+  auto qrow = [&](int s) -> int64_t { return q_rows ? q_rows[s] : s; };
   auto load_q = [&](int s) {
-    const uint4* src = reinterpret_cast<const uint4*>(q + (static_cast<int64_t>(s) * Hq + kvh * G) * D);
+    const uint4* src = reinterpret_cast<const uint4*>(q + (qrow(s) * Hq + kvh * G) * D);
 #pragma unroll
     for (int i = 0; i < QPL; ++i) {
       const int u = i * 64 + lane;
@@ -271,6 +273,15 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
       nxt.L = ctx[nxt.s];
       nxt.P = pages_of_len(nxt.L, max_blocks);
       nxt.B = first_page(nxt.s, nxt.P);
+      // Sequences with nothing after begin_pages (the prefill chunks of a
+      // mixed batch) hold no pages of the walk: step over them.  Pages of
+      // this run remain, so a sequence that holds some follows.
+      while (nxt.B >= nxt.P && nxt.s + 1 < S) {
+        nxt.s += 1;
+        nxt.L = ctx[nxt.s];
+        nxt.P = pages_of_len(nxt.L, max_blocks);
+        nxt.B = first_page(nxt.s, nxt.P);
+      }
       nxt.seg_lo = nxt.B;
       nxt.seg_hi = min(nxt.P, nxt.B + (run_b - nxt.cs));
       nxt.pb = nxt.B;
@@ -443,7 +454,7 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
           }
           if (lane == 0) seq_part[static_cast<int64_t>(S) * Hq * D + r] = lse2;
         } else if (whole) {
-          const int64_t row = static_cast<int64_t>(s) * Hq + kvh * G + h;
+          const int64_t row = qrow(s) * Hq + kvh * G + h;
           if (mine) {
             if constexpr (EPC == 8) {
               uint4 o;
@@ -488,7 +499,8 @@ template <typename T, int D, int G>
 __global__ __launch_bounds__(64) void merge_kernel(T* __restrict__ out, float* __restrict__ lse_out, int Hkv, int W,
                                                    const int32_t* __restrict__ seq_info,
                                                    const float* __restrict__ part_o,
-                                                   const float* __restrict__ part_lse) {
+                                                   const float* __restrict__ part_lse,
+                                                   const int32_t* __restrict__ q_rows) {
   constexpr int EPL = D / 64;  // output elements per lane
   const int lane = lane_id();
   const int s = blockIdx.x;
@@ -548,7 +560,7 @@ __global__ __launch_bounds__(64) void merge_kernel(T* __restrict__ out, float* _
   for (int h = 0; h < G; ++h) {
     const float ws = wave_sum(wsum[h]);
     const float inv = 1.0f / ws;
-    const int64_t row = static_cast<int64_t>(s) * Hq + kvh * G + h;
+    const int64_t row = (q_rows ? q_rows[s] : s) * static_cast<int64_t>(Hq) + kvh * G + h;
     if constexpr (sizeof(T) == 2) {
       if constexpr (EPL == 2) {
         reinterpret_cast<uint32_t*>(out)[row * (D / 2) + lane] =
@@ -580,7 +592,8 @@ int resident_waves(KernelFn fn, std::atomic<int>* cache) {
 }
 
 template <typename T, int D, int G>
-int launch_typed(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_part, bool merge, StreamPlan* plan) {
+int launch_typed(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_part, const int32_t* q_rows, bool merge,
+                 StreamPlan* plan) {
   static std::atomic<int> occ_cache[64];
   auto kern = stream_decode_kernel<T, D, G>;
   int64_t per = a.split_pages;
@@ -609,33 +622,34 @@ int launch_typed(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_p
   float* part_o = reinterpret_cast<float*>(ws + pl.o_offset);
   hipStream_t st = static_cast<hipStream_t>(a.stream);
   const float scale_log2 = a.scale * kLog2e;
-  if (!begin_pages) profile_before(a.stream);
+  if (a.timed) profile_before(a.stream);
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(W), a.num_kv_heads), dim3(64), 0, st, static_cast<T*>(a.out),
                      a.lse_out, static_cast<const T*>(a.q), static_cast<const T*>(a.k_pool),
                      static_cast<const T*>(a.v_pool), a.block_tables, a.context_lens, a.max_blocks, a.num_seqs,
                      a.num_kv_heads, static_cast<int>(a.num_pages), scale_log2, static_cast<int>(per),
-                     static_cast<int>(a.total_pages), seq_info, part_o, part_lse, begin_pages, seq_part);
-  if (!begin_pages) profile_after(a.stream);
+                     static_cast<int>(a.total_pages), seq_info, part_o, part_lse, begin_pages, seq_part, q_rows);
+  if (a.timed) profile_after(a.stream);
   if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_decode: stream kernel launch failed");
   // Unless one wave covers everything, some sequence may be shared; the
   // merge kernel skips the sequences one wave covered.
   if (merge && W > 1) {
     hipLaunchKernelGGL((merge_kernel<T, D, G>), dim3(a.num_seqs, a.num_kv_heads), dim3(64), 0, st,
                        static_cast<T*>(a.out), a.lse_out, a.num_kv_heads, static_cast<int>(W), seq_info, part_o,
-                       part_lse);
+                       part_lse, q_rows);
     if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_decode: merge kernel launch failed");
   }
   return PA_OK;
 }
 
 template <typename T, int D>
-int launch_g(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_part, bool merge, StreamPlan* plan) {
+int launch_g(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_part, const int32_t* q_rows, bool merge,
+             StreamPlan* plan) {
   switch (a.gqa) {
-    case 1: return launch_typed<T, D, 1>(a, begin_pages, seq_part, merge, plan);
-    case 2: return launch_typed<T, D, 2>(a, begin_pages, seq_part, merge, plan);
-    case 4: return launch_typed<T, D, 4>(a, begin_pages, seq_part, merge, plan);
-    case 8: return launch_typed<T, D, 8>(a, begin_pages, seq_part, merge, plan);
-    case 16: return launch_typed<T, D, 16>(a, begin_pages, seq_part, merge, plan);
+    case 1: return launch_typed<T, D, 1>(a, begin_pages, seq_part, q_rows, merge, plan);
+    case 2: return launch_typed<T, D, 2>(a, begin_pages, seq_part, q_rows, merge, plan);
+    case 4: return launch_typed<T, D, 4>(a, begin_pages, seq_part, q_rows, merge, plan);
+    case 8: return launch_typed<T, D, 8>(a, begin_pages, seq_part, q_rows, merge, plan);
+    case 16: return launch_typed<T, D, 16>(a, begin_pages, seq_part, q_rows, merge, plan);
   }
   return fail(PA_EUNSUPPORTED, "pa_decode: gqa_ratio not built");
 }
@@ -657,17 +671,18 @@ bool decode_supported(pa_dtype dtype, int32_t head_dim, int32_t gqa) {
   return false;
 }
 
-int launch_stream(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_part, bool merge, StreamPlan* plan) {
+int launch_stream(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_part, const int32_t* q_rows, bool merge,
+                  StreamPlan* plan) {
   if (a.dtype == PA_BF16) {
-    if (a.head_dim == 128) return launch_g<uint16_t, 128>(a, begin_pages, seq_part, merge, plan);
-    if (a.head_dim == 64) return launch_g<uint16_t, 64>(a, begin_pages, seq_part, merge, plan);
+    if (a.head_dim == 128) return launch_g<uint16_t, 128>(a, begin_pages, seq_part, q_rows, merge, plan);
+    if (a.head_dim == 64) return launch_g<uint16_t, 64>(a, begin_pages, seq_part, q_rows, merge, plan);
   } else if (a.dtype == PA_F32) {
-    if (a.head_dim == 64) return launch_g<float, 64>(a, begin_pages, seq_part, merge, plan);
+    if (a.head_dim == 64) return launch_g<float, 64>(a, begin_pages, seq_part, q_rows, merge, plan);
   }
   return fail(PA_EUNSUPPORTED, "pa_decode: shape not built");
 }
 
-int launch_decode(const DecodeLaunch& a) { return launch_stream(a, nullptr, nullptr, true, nullptr); }
+int launch_decode(const DecodeLaunch& a) { return launch_stream(a, nullptr, nullptr, nullptr, true, nullptr); }
 
 void profile_before(void* stream) {
   if (g_prof.ev.empty() || g_prof.next + 2 > g_prof.ev.size()) return;

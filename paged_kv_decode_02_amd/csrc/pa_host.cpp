@@ -52,6 +52,18 @@ CascadeLayout cascade_layout(int64_t num_seqs, int32_t num_kv_heads, int32_t gqa
   return l;
 }
 
+MixedLayout mixed_layout(int64_t num_seqs, int64_t chunk_tokens, int32_t num_kv_heads, int32_t gqa, int32_t head_dim,
+                         int32_t nks, int64_t stream_bytes) {
+  MixedLayout l;
+  const size_t rows = static_cast<size_t>(chunk_tokens) * num_kv_heads * gqa;  // (chunk token, q-head)
+  l.begin_offset = 0;
+  l.pre_o_offset = align_up(static_cast<size_t>(num_seqs) * sizeof(int32_t));
+  l.pre_lse_offset = l.pre_o_offset + align_up(rows * nks * head_dim * sizeof(float));
+  l.stream_offset = l.pre_lse_offset + align_up(rows * nks * sizeof(float));
+  l.bytes = l.stream_offset + align_up(static_cast<size_t>(stream_bytes));
+  return l;
+}
+
 }  // namespace pa
 
 using namespace pa;

@@ -59,6 +59,7 @@ struct DecodeLaunch {
   void* workspace;
   size_t workspace_bytes;
   void* stream;
+  bool timed = true;  // record profiling events around the stream kernel
 };
 
 bool decode_supported(pa_dtype dtype, int32_t head_dim, int32_t gqa);
@@ -73,7 +74,18 @@ struct StreamPlan {
   int32_t per;
   PartialLayout layout;  // inside a.workspace
 };
-int launch_stream(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_part, bool merge, StreamPlan* plan);
+// q_rows (device, per sequence, nullable) gives the q / out / lse row of
+// each sequence when the batch holds more than one token per sequence.
+int launch_stream(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_part, const int32_t* q_rows,
+                  bool merge, StreamPlan* plan);
+
+// Prefill chunks of a mixed batch, passed by value to the MFMA tile kernel.
+constexpr int kMaxChunkSegments = 64;
+struct ChunkList {
+  int32_t n;                                // chunk segments (q_len > 1)
+  int32_t seg[kMaxChunkSegments];           // their segment indices
+  int32_t tok_off[kMaxChunkSegments + 1];   // first chunk-token index of each
+};
 
 // Shared-prefix (cascade) decode.
 struct CascadeLayout {
@@ -96,6 +108,32 @@ struct CascadeLaunch {
 };
 bool cascade_supported(pa_dtype dtype, int32_t head_dim, int32_t gqa);
 int launch_cascade(const CascadeLaunch& c);
+
+// Mixed batch: prefill chunks (q_len > 1, causal inside the chunk) and
+// decode tokens (q_len = 1) of many sequences in one call.
+constexpr int32_t kMaxChunkSplits = 8;  // key splits of one chunk row block (sizes workspace)
+constexpr int32_t kMinChunkSplitKeys = 1024;
+struct MixedLayout {
+  size_t begin_offset, pre_o_offset, pre_lse_offset, stream_offset, bytes;
+};
+MixedLayout mixed_layout(int64_t num_seqs, int64_t chunk_tokens, int32_t num_kv_heads, int32_t gqa, int32_t head_dim,
+                         int32_t nks, int64_t stream_bytes);
+struct MixedLaunch {
+  DecodeLaunch base;         // num_seqs = segments; out / q rows are tokens
+  const int32_t* cu_q_lens;  // device [S+1]
+  const int32_t* chunk_seg;  // host [num_chunks]: segments with q_len > 1
+  const int32_t* chunk_tok;  // host [num_chunks+1]: first chunk-token index of each
+  int32_t num_chunks;
+  int32_t row_chunks;  // ceil(max chunk rows / kPrefixRowsPerBlock)
+  int32_t nks;         // key splits per chunk row block
+  int32_t kps;         // keys per split (multiple of 64)
+  int64_t decode_pages;
+  MixedLayout layout;
+  void* workspace;
+  size_t workspace_bytes;
+};
+bool mixed_supported(pa_dtype dtype, int32_t head_dim, int32_t gqa);
+int launch_mixed(const MixedLaunch& m);
 
 // Profiling hook: bracket the dominant kernel of a call.
 void profile_before(void* stream);

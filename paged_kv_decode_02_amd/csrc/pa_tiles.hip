@@ -1,0 +1,553 @@
+// MFMA tile kernels for gfx950 (MI355X): the dense parts of paged attention.
+//
+// Shared-prefix (cascade / Hydragen) decode.  A group is a contiguous range
+// of sequences whose block tables start with the same prefix pages (shared
+// blocks, SwiftLLM page section 3.1).  The Tokasaurus page ("dynamic prefix
+// identification") describes attending to the shared prefix once for the
+// whole group: the group's queries against the prefix keys form one dense
+// product.  Attention over prefix + suffix is then the log-sum-exp merge of
+// attention over each part.  Three launches on the caller's stream:
+//  1. tile_kernel<G, false> (MFMA): per (group, row chunk, key split,
+//     kv-head) a workgroup of 8 waves takes up to 256 query rows --
+//     (member, q-head) pairs of the kv-head, folded into one tile dimension
+//     the way TokenSpeed's fold_sq_factor folds query tokens (TokenSpeed
+//     deep-dive section 7.2) -- against one split of the prefix keys,
+//     FlashAttention style: S^T = K Q^T and O^T += V^T P^T on
+//     v_mfma_f32_16x16x32_bf16, online softmax in between.  Writes one
+//     partial (o, log2-sum-exp) per (member, head, split) and each member's
+//     first suffix page.
+//  2. stream_decode_kernel over the suffix pages only.
+//  3. cascade_merge_kernel: per (sequence, kv-head), the prefix splits and
+//     the suffix partial(s) merged by log-sum-exp.
+//
+// Mixed batch (SARATHI-style piggybacking, SOSP tutorial page section 3.3;
+// chunked prefill, TokenSpeed deep-dive section 5.1): prefill chunks (n > 1
+// new tokens, causal inside the chunk) and decode tokens in one call.
+//  1. tile_kernel<G, true>: per (chunk, row chunk, key split, kv-head) the
+//     chunk's (token, q-head) rows against its own keys, causal mask by
+//     select; marks the chunks as "no decode pages" for step 2.
+//  2. stream_decode_kernel (+ its merge) over the decode segments.
+//  3. chunk_merge_kernel: per (chunk token, kv-head), the key splits.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <string>
+
+#include "pa_common.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef __attribute__((address_space(3))) void* LdsPtr;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kPrefixRows = kPrefixRowsPerBlock;  // query rows per workgroup (8 waves x 32)
+constexpr int kKeyTile = 64;       // keys per LDS tile (4 pages)
+constexpr int kVtStride = 72;      // bf16 per row of the transposed V tile (64 + 8 pad)
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
+// MFMA 16x16x32 operand layout (wave64): A (16 x 32): lane l holds row l%16,
+// k = 8*(l/16) .. +8; B (32 x 16): lane l holds column l%16, the same k;
+// C (16 x 16): lane l holds column l%16, rows 4*(l/16) .. +4.
+//
+// One workgroup = 8 waves = up to 256 query rows of one kv-head against the
+// keys [k_lo, k_hi) of one block-table row, in tiles of 64 keys.
+//  PREFIX: unit = a group; rows are (member, q-head) pairs; keys are the
+//          shared prefix, read through the first member's table; every row
+//          sees every key.
+//  CHUNK:  unit = a prefill chunk (segment with more than one query token);
+//          rows are (token, q-head) pairs; keys are the segment's own rows;
+//          token i sees keys t <= L - n + i (causal inside the chunk).
+// Output: one partial (normalised o, log2-sum-exp) per (row, key split);
+// a row that sees no key of the split gets o = 0, lse = -inf.
+template <int G, bool CHUNK>
+__global__ __launch_bounds__(512) void tile_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool,
+    const int32_t* __restrict__ block_tables, int max_blocks, const int32_t* __restrict__ ctx,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ group_off, const int32_t* __restrict__ prefix_lens,
+    ChunkList chunks, int S, int RC, int nks, int kps, int Hkv, int num_pages, float scale_log2,
+    int32_t* __restrict__ begin_pages, int32_t* __restrict__ seq_info, float* __restrict__ pre_o,
+    float* __restrict__ pre_lse) {
+  constexpr int D = 128;
+  constexpr int TILE = 16 * D * 2;  // bytes of one (page, kv-head) tile
+  __shared__ uint4 k_lds[kKeyTile * 16];       // [key][16 chunks], chunk XOR-swizzled by key
+  __shared__ uint16_t vt_lds[D * kVtStride];  // V^T: [d][key]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  int bx = blockIdx.x;
+  const int ks = bx % nks;
+  bx /= nks;
+  const int rc = bx % RC;
+  const int u = bx / RC;
+  const int kvh = blockIdx.y;
+  const int Hq = Hkv * G;
+
+  // Per-sequence set-up for the launches that follow (first suffix page;
+  // for mixed batches also the "not shared" record the decode merge reads).
+  int seg, n_rows, k_lo, k_hi, L = 0, n_tok = 1, q_base, part_base;
+  if constexpr (CHUNK) {
+    if (blockIdx.x == 0 && blockIdx.y == 0) {
+      for (int s = tid; s < S; s += 512) {
+        const bool chunk = cu_q[s + 1] - cu_q[s] > 1;
+        const int64_t pg = (static_cast<int64_t>(ctx[s]) + 15) >> 4;
+        begin_pages[s] = chunk ? static_cast<int>(pg < max_blocks ? pg : max_blocks) : 0;
+        if (chunk) {
+          seq_info[4 * s + 0] = 0;
+          seq_info[4 * s + 1] = 0;
+          seq_info[4 * s + 2] = 0;
+          seq_info[4 * s + 3] = 0;
+        }
+      }
+    }
+    if (u >= chunks.n) return;
+    seg = chunks.seg[u];
+    n_tok = cu_q[seg + 1] - cu_q[seg];
+    L = ctx[seg];
+    n_rows = n_tok * G;
+    q_base = cu_q[seg];
+    part_base = chunks.tok_off[u];
+    const int r_end = min(n_rows, (rc + 1) * kPrefixRows);
+    const int i_max = (r_end - 1) / G;
+    const int k_end = min(L, L - n_tok + i_max + 1);
+    k_lo = ks * kps;
+    k_hi = min(k_end, k_lo + kps);
+  } else {
+    const int off0 = group_off[u];
+    const int n_g = group_off[u + 1] - off0;
+    const int P = prefix_lens[u];  // prefix tokens (whole pages)
+    if (kvh == 0 && rc == 0 && ks == 0)
+      for (int i = tid; i < n_g; i += 512) begin_pages[off0 + i] = P / 16;
+    seg = off0;
+    n_rows = n_g * G;
+    q_base = off0;
+    part_base = off0;
+    k_lo = ks * kps;
+    k_hi = min(P, k_lo + kps);
+  }
+  if (k_lo >= k_hi || rc * kPrefixRows >= n_rows) return;  // uniform over the workgroup
+
+  const int row0 = rc * kPrefixRows + wv * 32;  // first of this wave's 32 query rows
+  const int col = lane & 15;
+  const int lg = lane >> 4;
+  // Q^T operand (B of S^T = K Q^T): row r = row0 + 16 rb + col, d = 32 c + 8 lg.
+  u32x4 qb[2][4];
+  int vis[2];  // CHUNK: last visible key of the lane's query row
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int r = row0 + rb * 16 + col;
+    vis[rb] = CHUNK ? L - n_tok + min(r, n_rows - 1) / G : 0x7fffffff;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (r < n_rows) {
+        const int64_t qi = (static_cast<int64_t>(q_base + r / G) * Hq + kvh * G + r % G) * D + c * 32 + lg * 8;
+        qb[rb][c] = *reinterpret_cast<const u32x4*>(q + qi);
+      } else {
+        qb[rb][c] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+  const int32_t* bt = block_tables + static_cast<int64_t>(seg) * max_blocks;
+  const char* kbytes = reinterpret_cast<const char*>(k_pool);
+  const char* vbytes = reinterpret_cast<const char*>(v_pool);
+
+  f32x4 o[8][2];
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) o[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY};
+  float lsum[2] = {0.f, 0.f};
+
+  for (int kt = k_lo; kt < k_hi; kt += kKeyTile) {
+    const int nk = min(kKeyTile, k_hi - kt);  // keys of this tile that exist
+    const int npg = (nk + 15) / 16;
+    int pid[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pid[j] = min(max(bt[kt / 16 + min(j, npg - 1)], 0), num_pages - 1);
+    // K tile -> LDS: slot (i*8 + wave)*64 + lane holds key slot/16, chunk
+    // (slot%16) ^ (key%16).
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int slot = (i * 8 + wv) * 64 + lane;
+      const int key = slot >> 4;
+      const int ch = (slot & 15) ^ (key & 15);
+      const char* src = kbytes + (static_cast<int64_t>(pid[key >> 4]) * Hkv + kvh) * TILE + (key & 15) * (D * 2) + ch * 16;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), (LdsPtr)(&k_lds[(i * 8 + wv) * 64]), 16,
+                                       0, 0);
+    }
+    // V tile -> registers -> transposed into LDS; rows past the tile's keys
+    // (tail rows of a last page hold NaN) become zeros.
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int uu = i * 512 + tid;
+      const int key = uu >> 4;
+      const int dc = uu & 15;
+      const char* src = vbytes + (static_cast<int64_t>(pid[key >> 4]) * Hkv + kvh) * TILE + (key & 15) * (D * 2) + dc * 16;
+      u32x4 v = *reinterpret_cast<const u32x4*>(src);
+      if (key >= nk) v = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vt_lds[(dc * 8 + 2 * e) * kVtStride + key] = static_cast<uint16_t>(v[e] & 0xffffu);
+        vt_lds[(dc * 8 + 2 * e + 1) * kVtStride + key] = static_cast<uint16_t>(v[e] >> 16);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    // S^T = K Q^T: s[kb][rb] holds keys 16 kb + 4 lg + i, query row 16 rb + col.
+    f32x4 s[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int key = kb * 16 + col;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) s[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int cc = c * 4 + lg;
+        const u32x4 a = *reinterpret_cast<const u32x4*>(&k_lds[key * 16 + (cc ^ (key & 15))]);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) s[kb][rb] = mfma16x16x32(a, qb[rb][c], s[kb][rb]);
+      }
+    }
+    // Online softmax per query row (column of S^T); the 64 keys of a row are
+    // spread over this lane's 16 values and the lanes l^16, l^32, l^48.
+    u32x4 pb[2][2];  // P^T operand: [rb][key half]
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kb * 16 + lg * 4 + i;
+          const bool ok = key < nk && (!CHUNK || kt + key <= vis[rb]);
+          const float x = ok ? s[kb][rb][i] * scale_log2 : -INFINITY;
+          s[kb][rb][i] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = max_xor32(max_xor16(mx));
+      const float mn = fmaxf(m[rb], mx);
+      // A row with no visible key so far keeps m = -inf; use 0 as its
+      // reference so no -inf - -inf appears (its p are all 0).
+      const float ref = mn == -INFINITY ? 0.f : mn;
+      const float alpha = fast_exp2(m[rb] - ref);
+      m[rb] = mn;
+      float ps = 0.f;
+      uint32_t pw[4][2];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[i] = fast_exp2(s[kb][rb][i] - ref);
+          ps += p[i];
+        }
+        pw[kb][0] = bf16_bits_rne(p[0]) | (bf16_bits_rne(p[1]) << 16);
+        pw[kb][1] = bf16_bits_rne(p[2]) | (bf16_bits_rne(p[3]) << 16);
+      }
+      lsum[rb] = lsum[rb] * alpha + ps;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) o[db][rb] *= alpha;
+      // k slots 8 lg .. 8 lg + 7 of key half hf = keys 32 hf + 4 lg + [0, 4)
+      // and 32 hf + 16 + 4 lg + [0, 4): the same order the V^T operand uses.
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        pb[rb][hf] = u32x4{pw[2 * hf][0], pw[2 * hf][1], pw[2 * hf + 1][0], pw[2 * hf + 1][1]};
+    }
+    // O^T += V^T P^T.
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const int d = db * 16 + col;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(&vt_lds[d * kVtStride + hf * 32 + lg * 4]);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(&vt_lds[d * kVtStride + hf * 32 + 16 + lg * 4]);
+        const u32x4 a = u32x4{lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) o[db][rb] = mfma16x16x32(a, pb[rb][hf], o[db][rb]);
+      }
+    }
+    __syncthreads();
+  }
+
+  // Partials: o / l per query row, log2-sum-exp.
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const float lt = add_xor32(add_xor16(lsum[rb]));
+    const int r = row0 + rb * 16 + col;
+    if (r < n_rows) {
+      const int64_t pr = ((static_cast<int64_t>(part_base + r / G) * Hkv + kvh) * nks + ks) * G + r % G;
+      const bool any = lt > 0.f;
+      const float inv = any ? 1.0f / lt : 0.f;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const f32x4 v = o[db][rb] * inv;
+        *reinterpret_cast<f32x4*>(pre_o + pr * D + db * 16 + lg * 4) = v;
+      }
+      if (lg == 0) pre_lse[pr] = any ? m[rb] + fast_log2(lt) : -INFINITY;
+    }
+  }
+}
+
+// Merge the key splits of one chunk token (all G heads of a kv-head) and
+// write its output row.
+template <int G>
+__global__ __launch_bounds__(64) void chunk_merge_kernel(uint16_t* __restrict__ out, float* __restrict__ lse_out,
+                                                         const int32_t* __restrict__ ctx,
+                                                         const int32_t* __restrict__ cu_q, ChunkList chunks, int Hkv,
+                                                         int nks, int kps, const float* __restrict__ pre_o,
+                                                         const float* __restrict__ pre_lse) {
+  constexpr int D = 128;
+  const int lane = lane_id();
+  const int ct = chunks.tok_off[0] + static_cast<int>(blockIdx.x);  // chunk token
+  const int kvh = blockIdx.y;
+  const int Hq = Hkv * G;
+  int u = 0;
+  while (u + 1 < chunks.n && chunks.tok_off[u + 1] <= ct) ++u;
+  const int i = ct - chunks.tok_off[u];
+  const int s = chunks.seg[u];
+  const int n_tok = cu_q[s + 1] - cu_q[s];
+  if (i >= n_tok) return;
+  const int L = ctx[s];
+  // The key splits tile_kernel wrote for this token's row chunk.
+  const int n_rows = n_tok * G;
+  const int rc = (i * G) / kPrefixRows;
+  const int i_max = (min(n_rows, (rc + 1) * kPrefixRows) - 1) / G;
+  const int k_end = min(L, L - n_tok + i_max + 1);
+  const int nsp = min(nks, (k_end + kps - 1) / kps);
+#pragma unroll 1
+  for (int h = 0; h < G; ++h) {
+    const int64_t p0 = ((static_cast<int64_t>(ct) * Hkv + kvh) * nks) * G + h;
+    float M = -INFINITY;
+    for (int j = lane; j < nsp; j += 64) M = fmaxf(M, pre_lse[p0 + static_cast<int64_t>(j) * G]);
+    M = wave_max(M);
+    float acc0 = 0.f, acc1 = 0.f, wsum = 0.f;
+    for (int j = 0; j < nsp; ++j) {
+      const int64_t pr = p0 + static_cast<int64_t>(j) * G;
+      const float a = fast_exp2(pre_lse[pr] - M);  // -inf (no visible key) -> 0
+      wsum += a;
+      acc0 = fmaf(a, pre_o[pr * D + 2 * lane], acc0);
+      acc1 = fmaf(a, pre_o[pr * D + 2 * lane + 1], acc1);
+    }
+    const float inv = 1.0f / wsum;
+    const int64_t row = static_cast<int64_t>(cu_q[s] + i) * Hq + kvh * G + h;
+    reinterpret_cast<uint32_t*>(out)[row * (D / 2) + lane] = bf16_bits_rne(acc0 * inv) | (bf16_bits_rne(acc1 * inv) << 16);
+    if (lse_out && lane == 0) lse_out[row] = (M + fast_log2(wsum)) * kLn2;
+  }
+}
+
+// Final merge per (sequence, kv-head): the prefix splits of the sequence's
+// group (from begin_pages: the prefix length) and its suffix, which is one
+// partial (seq_part) when a single wave covered it and one partial per wave
+// otherwise.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(64) void cascade_merge_kernel(
+    T* __restrict__ out, float* __restrict__ lse_out, int S, int Hkv, int W, int nks, int kps,
+    const int32_t* __restrict__ begin_pages, const float* __restrict__ pre_o, const float* __restrict__ pre_lse,
+    const float* __restrict__ seq_part, const int32_t* __restrict__ seq_info, const float* __restrict__ part_o,
+    const float* __restrict__ part_lse) {
+  constexpr int EPL = D / 64;
+  const int lane = lane_id();
+  const int s = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int Hq = Hkv * G;
+  const int np = min(nks, (begin_pages[s] * 16 + kps - 1) / kps);  // prefix splits with keys
+  const int w0 = seq_info[4 * s + 0];
+  const int w1 = seq_info[4 * s + 1];
+  const int slot0 = seq_info[4 * s + 2];
+  const bool shared = w1 > w0;
+  if (shared && (w0 < 0 || w1 >= W || slot0 < 0 || slot0 > 1)) return;
+  const int ns = shared ? (w1 - w0 + 1) : 1;
+  const int n = np + ns;
+  // Partial j: prefix split j < np, else suffix part j - np.
+  auto lse_at = [&](int j, int h) -> float {
+    if (j < np) return pre_lse[((static_cast<int64_t>(s) * Hkv + kvh) * nks + j) * G + h];
+    const int k = j - np;
+    if (!shared) return seq_part[static_cast<int64_t>(S) * Hq * D + static_cast<int64_t>(s) * Hq + kvh * G + h];
+    return part_lse[((static_cast<int64_t>(w0 + k) * Hkv + kvh) * 2 + (k == 0 ? slot0 : 0)) * G + h];
+  };
+  auto o_at = [&](int j, int h) -> const float* {
+    if (j < np) return pre_o + (((static_cast<int64_t>(s) * Hkv + kvh) * nks + j) * G + h) * D;
+    const int k = j - np;
+    if (!shared) return seq_part + (static_cast<int64_t>(s) * Hq + kvh * G + h) * D;
+    return part_o + (((static_cast<int64_t>(w0 + k) * Hkv + kvh) * 2 + (k == 0 ? slot0 : 0)) * G + h) * D;
+  };
+#pragma unroll 1
+  for (int h = 0; h < G; ++h) {
+    float M = -INFINITY;
+    for (int j = lane; j < n; j += 64) M = fmaxf(M, lse_at(j, h));
+    M = wave_max(M);
+    float acc[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+    float wsum = 0.f;
+    for (int j = 0; j < n; ++j) {
+      const float a = fast_exp2(lse_at(j, h) - M);
+      wsum += a;
+      const float* src = o_at(j, h) + lane * EPL;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(a, src[e], acc[e]);
+    }
+    const float inv = 1.0f / wsum;
+    const int64_t row = static_cast<int64_t>(s) * Hq + kvh * G + h;
+    if constexpr (sizeof(T) == 2) {
+      if constexpr (EPL == 2) {
+        reinterpret_cast<uint32_t*>(out)[row * (D / 2) + lane] =
+            bf16_bits_rne(acc[0] * inv) | (bf16_bits_rne(acc[1] * inv) << 16);
+      } else {
+        reinterpret_cast<uint16_t*>(out)[row * D + lane] = static_cast<uint16_t>(bf16_bits_rne(acc[0] * inv));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) reinterpret_cast<float*>(out)[row * D + lane * EPL + e] = acc[e] * inv;
+    }
+    if (lse_out && lane == 0) lse_out[row] = (M + fast_log2(wsum)) * kLn2;
+  }
+}
+
+template <int G>
+int launch_cascade_g(const CascadeLaunch& c) {
+  const DecodeLaunch& a = c.base;
+  hipStream_t st = static_cast<hipStream_t>(a.stream);
+  char* ws = static_cast<char*>(c.workspace);
+  const CascadeLayout& L = c.layout;
+  int32_t* begin_pages = reinterpret_cast<int32_t*>(ws + L.begin_offset);
+  float* seq_part = reinterpret_cast<float*>(ws + L.seq_part_offset);
+  float* pre_o = reinterpret_cast<float*>(ws + L.pre_o_offset);
+  float* pre_lse = reinterpret_cast<float*>(ws + L.pre_lse_offset);
+  const float scale_log2 = a.scale * kLog2e;
+  profile_before(a.stream);
+  ChunkList none;
+  none.n = 0;
+  hipLaunchKernelGGL((tile_kernel<G, false>), dim3(c.num_groups * c.row_chunks * c.nks, a.num_kv_heads), dim3(512), 0,
+                     st, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
+                     static_cast<const uint16_t*>(a.v_pool), a.block_tables, a.max_blocks, a.context_lens, nullptr,
+                     c.group_offsets, c.prefix_lens, none, a.num_seqs, c.row_chunks, c.nks, c.kps, a.num_kv_heads,
+                     static_cast<int>(a.num_pages), scale_log2, begin_pages, nullptr, pre_o, pre_lse);
+  profile_after(a.stream);
+  if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_prefix_cascade: prefix kernel launch failed");
+  // Suffix: the stream decode kernel over the pages after each prefix.
+  DecodeLaunch sfx = a;
+  sfx.workspace = ws + L.stream_offset;
+  sfx.workspace_bytes = c.workspace_bytes - L.stream_offset;
+  sfx.total_pages = c.suffix_pages;
+  sfx.timed = false;
+  StreamPlan plan;
+  int rc = launch_stream(sfx, begin_pages, seq_part, nullptr, /*merge=*/false, &plan);
+  if (rc) return rc;
+  char* sws = static_cast<char*>(sfx.workspace);
+  hipLaunchKernelGGL((cascade_merge_kernel<uint16_t, 128, G>), dim3(a.num_seqs, a.num_kv_heads), dim3(64), 0, st,
+                     static_cast<uint16_t*>(a.out), a.lse_out, a.num_seqs, a.num_kv_heads,
+                     static_cast<int>(plan.waves), c.nks, c.kps, begin_pages, pre_o, pre_lse, seq_part,
+                     reinterpret_cast<const int32_t*>(sws + plan.layout.info_offset),
+                     reinterpret_cast<const float*>(sws + plan.layout.o_offset),
+                     reinterpret_cast<const float*>(sws + plan.layout.lse_offset));
+  if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_prefix_cascade: merge kernel launch failed");
+  return PA_OK;
+}
+
+template <int G>
+int launch_mixed_g(const MixedLaunch& mx) {
+  const DecodeLaunch& a = mx.base;
+  hipStream_t st = static_cast<hipStream_t>(a.stream);
+  char* ws = static_cast<char*>(mx.workspace);
+  const MixedLayout& L = mx.layout;
+  int32_t* begin_pages = reinterpret_cast<int32_t*>(ws + L.begin_offset);
+  float* pre_o = reinterpret_cast<float*>(ws + L.pre_o_offset);
+  float* pre_lse = reinterpret_cast<float*>(ws + L.pre_lse_offset);
+  char* sws = ws + L.stream_offset;
+  // The stream kernel's per-sequence records start its workspace.
+  int32_t* seq_info = reinterpret_cast<int32_t*>(sws + partial_layout(1, a.num_seqs, a.num_kv_heads, a.gqa,
+                                                                      a.head_dim).info_offset);
+  const float scale_log2 = a.scale * kLog2e;
+  auto chunk_list = [&](int b0) {
+    ChunkList cl;
+    cl.n = std::min(kMaxChunkSegments, mx.num_chunks - b0);
+    for (int i = 0; i < cl.n; ++i) {
+      cl.seg[i] = mx.chunk_seg[b0 + i];
+      cl.tok_off[i] = mx.chunk_tok[b0 + i];
+    }
+    cl.tok_off[cl.n] = mx.chunk_tok[b0 + cl.n];
+    return cl;
+  };
+  if (mx.num_chunks > 0) {
+    profile_before(a.stream);
+    for (int b0 = 0; b0 < mx.num_chunks; b0 += kMaxChunkSegments) {
+      const ChunkList cl = chunk_list(b0);
+      hipLaunchKernelGGL((tile_kernel<G, true>), dim3(cl.n * mx.row_chunks * mx.nks, a.num_kv_heads), dim3(512), 0,
+                         st, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
+                         static_cast<const uint16_t*>(a.v_pool), a.block_tables, a.max_blocks, a.context_lens,
+                         mx.cu_q_lens, nullptr, nullptr, cl, a.num_seqs, mx.row_chunks, mx.nks, mx.kps,
+                         a.num_kv_heads, static_cast<int>(a.num_pages), scale_log2, begin_pages, seq_info, pre_o,
+                         pre_lse);
+      if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_mixed_chunk: chunk kernel launch failed");
+    }
+    profile_after(a.stream);
+  }
+  if (mx.decode_pages > 0) {
+    DecodeLaunch dec = a;
+    dec.workspace = sws;
+    dec.workspace_bytes = mx.workspace_bytes - L.stream_offset;
+    dec.total_pages = mx.decode_pages;
+    const int rc = launch_stream(dec, mx.num_chunks > 0 ? begin_pages : nullptr, nullptr, mx.cu_q_lens,
+                                 /*merge=*/true, nullptr);
+    if (rc) return rc;
+  }
+  for (int b0 = 0; b0 < mx.num_chunks; b0 += kMaxChunkSegments) {
+    const ChunkList cl = chunk_list(b0);
+    hipLaunchKernelGGL((chunk_merge_kernel<G>), dim3(cl.tok_off[cl.n] - cl.tok_off[0], a.num_kv_heads), dim3(64), 0,
+                       st, static_cast<uint16_t*>(a.out), a.lse_out, a.context_lens, mx.cu_q_lens, cl, a.num_kv_heads,
+                       mx.nks, mx.kps, pre_o, pre_lse);
+    if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_mixed_chunk: chunk merge launch failed");
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
+bool mixed_supported(pa_dtype dtype, int32_t head_dim, int32_t gqa) { return cascade_supported(dtype, head_dim, gqa); }
+
+int launch_mixed(const MixedLaunch& m) {
+  if (m.num_chunks == 0) {
+    DecodeLaunch dec = m.base;
+    dec.workspace = static_cast<char*>(m.workspace) + m.layout.stream_offset;
+    dec.workspace_bytes = m.workspace_bytes - m.layout.stream_offset;
+    dec.total_pages = m.decode_pages;
+    return launch_stream(dec, nullptr, nullptr, m.cu_q_lens, /*merge=*/true, nullptr);
+  }
+  switch (m.base.gqa) {
+    case 1: return launch_mixed_g<1>(m);
+    case 2: return launch_mixed_g<2>(m);
+    case 4: return launch_mixed_g<4>(m);
+    case 8: return launch_mixed_g<8>(m);
+    case 16: return launch_mixed_g<16>(m);
+  }
+  return fail(PA_EUNSUPPORTED, "pa_mixed_chunk: gqa_ratio not built");
+}
+
+bool cascade_supported(pa_dtype dtype, int32_t head_dim, int32_t gqa) {
+  return dtype == PA_BF16 && head_dim == 128 && (gqa == 1 || gqa == 2 || gqa == 4 || gqa == 8 || gqa == 16);
+}
+
+int launch_cascade(const CascadeLaunch& c) {
+  switch (c.base.gqa) {
+    case 1: return launch_cascade_g<1>(c);
+    case 2: return launch_cascade_g<2>(c);
+    case 4: return launch_cascade_g<4>(c);
+    case 8: return launch_cascade_g<8>(c);
+    case 16: return launch_cascade_g<16>(c);
+  }
+  return fail(PA_EUNSUPPORTED, "pa_prefix_cascade: gqa_ratio not built");
+}
+
+}  // namespace pa

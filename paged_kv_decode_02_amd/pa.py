@@ -32,6 +32,8 @@ EXPORTS = (
     "pa_decode",
     "pa_prefix_cascade_workspace_size",
     "pa_prefix_cascade",
+    "pa_mixed_chunk_workspace_size",
+    "pa_mixed_chunk",
     "pa_check_block_tables",
     "pa_last_error",
     "pa_profile_enable",
@@ -72,6 +74,11 @@ def load(path: Optional[str] = None):
     lib.pa_prefix_cascade.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_vp, c_vp,
                                       c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i64, ctypes.c_float, ctypes.c_int,
                                       c_vp, c_sz, c_vp]
+    lib.pa_mixed_chunk_workspace_size.restype = c_sz
+    lib.pa_mixed_chunk_workspace_size.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32, c_i64]
+    lib.pa_mixed_chunk.restype = ctypes.c_int
+    lib.pa_mixed_chunk.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32,
+                                   c_i32, c_i32, c_i32, c_i64, ctypes.c_float, ctypes.c_int, c_vp, c_sz, c_vp]
     lib.pa_check_block_tables.restype = ctypes.c_int
     lib.pa_check_block_tables.argtypes = [c_vp, c_i32, c_vp, c_i32, c_i32, c_i64, c_i32, c_vp, c_vp]
     lib.pa_last_error.restype = ctypes.c_char_p
@@ -213,6 +220,54 @@ def prefix_cascade(out, q, k_pool, v_pool, block_tables, context_lens, context_l
         _dev(group_seq_offsets, "group_seq_offsets", torch.int32), goh.ctypes.data,
         _dev(prefix_lens, "prefix_lens", torch.int32), plh.ctypes.data,
         Hkv, Hq // Hkv, D, BS, NP, float(scale), _dtype_code(q),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream_ptr(stream),
+    )
+    return _check(rc)
+
+
+def mixed_chunk_workspace_size(max_num_tokens, max_num_segments, num_kv_heads, gqa_ratio, head_dim,
+                               max_total_pages) -> int:
+    return int(load().pa_mixed_chunk_workspace_size(max_num_tokens, max_num_segments, num_kv_heads, gqa_ratio,
+                                                    head_dim, max_total_pages))
+
+
+def mixed_chunk(out, q, k_pool, v_pool, block_tables, cu_q_lens, cu_q_lens_host, context_lens, context_lens_host,
+                scale, workspace, lse_out=None, stream=None):
+    """pa_mixed_chunk on torch tensors.
+
+    q, out: [T, Hq, D] (T = cu_q_lens[-1]); k_pool, v_pool: [NP, Hkv, 16, D];
+    block_tables [S, MB] int32; cu_q_lens [S+1] / context_lens [S] int32 on
+    the device plus host twins with the same values.
+    """
+    import torch
+
+    T, Hq, D = q.shape
+    NP, Hkv, BS, D2 = k_pool.shape
+    if tuple(out.shape) != (T, Hq, D) or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if tuple(v_pool.shape) != tuple(k_pool.shape) or k_pool.dtype != q.dtype or v_pool.dtype != q.dtype:
+        raise ValueError("k_pool and v_pool must match each other and q's dtype")
+    if D2 != D or Hq % Hkv:
+        raise ValueError("head_dim mismatch or q heads not a multiple of kv heads")
+    cq = _host_i32(cu_q_lens_host, "cu_q_lens_host")
+    ch = _host_i32(context_lens_host, "context_lens_host")
+    S = ch.size
+    if cq.size != S + 1 or cu_q_lens.numel() != S + 1 or context_lens.numel() != S:
+        raise ValueError("cu_q_lens must have one entry more than context_lens")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must have one row per segment")
+    if S and int(cq[-1]) != T:
+        raise ValueError("q must have cu_q_lens[-1] rows")
+    if lse_out is not None and tuple(lse_out.shape) != (T, Hq):
+        raise ValueError("lse_out must be [T, Hq]")
+    rc = load().pa_mixed_chunk(
+        _dev(out, "out"),
+        _dev(lse_out, "lse_out", torch.float32) if lse_out is not None else None,
+        _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(cu_q_lens, "cu_q_lens", torch.int32), cq.ctypes.data,
+        _dev(context_lens, "context_lens", torch.int32), ch.ctypes.data,
+        S, Hkv, Hq // Hkv, D, BS, NP, float(scale), _dtype_code(q),
         _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream_ptr(stream),
     )
     return _check(rc)

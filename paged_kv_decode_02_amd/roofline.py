@@ -15,6 +15,7 @@ from __future__ import annotations
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
 LLAMA8B_LAYERS = 32
 
 
@@ -35,3 +36,28 @@ def decode_bytes(context_lens, num_q_heads, num_kv_heads, head_dim, elem_bytes, 
 def decode_flops(context_lens, num_q_heads, head_dim) -> int:
     """2*D for q.k plus 2*D for p.v per (q-head, visible key)."""
     return int(4 * head_dim * num_q_heads * np.asarray(context_lens, dtype=np.int64).sum())
+
+
+def cascade_bytes(context_lens, group_seq_offsets, prefix_lens, num_q_heads, num_kv_heads, head_dim, elem_bytes,
+                  block_size=16) -> dict:
+    """Shared-prefix decode: each group's prefix K/V read once, every
+    member's suffix once, plus q, out and table entries."""
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    offs = np.asarray(group_seq_offsets, dtype=np.int64)
+    pl = np.asarray(prefix_lens, dtype=np.int64)
+    per_seq_prefix = np.repeat(pl, np.diff(offs))
+    prefix_tokens = int(pl.sum())
+    suffix_tokens = int((ctx - per_seq_prefix).sum())
+    kv = kv_cache_bytes(1, num_kv_heads, head_dim, prefix_tokens + suffix_tokens, elem_bytes)
+    S = ctx.size
+    qo = 2 * S * num_q_heads * head_dim * elem_bytes
+    tables = 4 * int(((ctx + block_size - 1) // block_size).sum()) + 4 * S
+    return {"kv": kv, "q_out": qo, "tables": tables, "total": kv + qo + tables,
+            "prefix_kv": kv_cache_bytes(1, num_kv_heads, head_dim, prefix_tokens, elem_bytes)}
+
+
+def prefix_flops(group_seq_offsets, prefix_lens, num_q_heads, head_dim) -> int:
+    """q.k and p.v over the shared prefixes: 4*D per (member q-head, prefix key)."""
+    offs = np.asarray(group_seq_offsets, dtype=np.int64)
+    pl = np.asarray(prefix_lens, dtype=np.int64)
+    return int(4 * head_dim * num_q_heads * (np.diff(offs) * pl).sum())

@@ -137,3 +137,53 @@ def test_host_table_checker_agrees_with_the_oracle_on_broken_tables():
         assert want, trial
         with pytest.raises(pa.PAError):
             pa.check_block_tables(bt, ctx, lay.num_pages, 16, go, pl)
+
+
+def call_mixed(lib, **kw):
+    args = dict(out=FAKE, lse=None, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, mb=4, cu=FAKE, cu_host=None, ctx=FAKE,
+                ctx_host=None, S=2, Hkv=2, G=4, D=128, BS=16, NP=10, scale=0.1, dtype=pa.PA_BF16,
+                ws=ctypes.c_void_p(0x100000), ws_bytes=1 << 20, stream=None)
+    args.update(kw)
+    cu = args["cu_host"] if args["cu_host"] is not None else np.array([0, 5, 6], dtype=np.int32)
+    ch = args["ctx_host"] if args["ctx_host"] is not None else np.array([20, 40], dtype=np.int32)
+    return lib.pa_mixed_chunk(args["out"], args["lse"], args["q"], args["k"], args["v"], args["bt"], args["mb"],
+                              args["cu"], cu.ctypes.data, args["ctx"], ch.ctypes.data, args["S"], args["Hkv"],
+                              args["G"], args["D"], args["BS"], args["NP"], args["scale"], args["dtype"], args["ws"],
+                              args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(q=None), pa.PA_EINVAL),
+        (dict(cu=None), pa.PA_EINVAL),
+        (dict(cu_host=np.array([1, 5, 6], dtype=np.int32)), pa.PA_EINVAL),  # does not start at 0
+        (dict(cu_host=np.array([0, 5, 5], dtype=np.int32)), pa.PA_EINVAL),  # a segment with no token
+        (dict(cu_host=np.array([0, 21, 22], dtype=np.int32)), pa.PA_EINVAL),  # more tokens than rows
+        (dict(ctx_host=np.array([20, 65], dtype=np.int32)), pa.PA_EINVAL),  # 65 > 4 pages * 16
+        (dict(ws=ctypes.c_void_p(0x100010)), pa.PA_EINVAL),
+        (dict(ws_bytes=64), pa.PA_EWORKSPACE),
+        (dict(D=64), pa.PA_EUNSUPPORTED),  # chunks: head_dim 128 only
+        (dict(dtype=pa.PA_F32, D=64), pa.PA_EUNSUPPORTED),
+        (dict(G=3), pa.PA_EUNSUPPORTED),
+        (dict(BS=8), pa.PA_EUNSUPPORTED),
+        (dict(S=-1), pa.PA_EINVAL),
+    ],
+)
+def test_mixed_rejects_bad_arguments(kw, code):
+    lib = pa.load()
+    assert call_mixed(lib, **kw) == code
+    assert lib.pa_last_error().decode() != ""
+
+
+def test_mixed_zero_segments_is_a_no_op():
+    lib = pa.load()
+    assert call_mixed(lib, S=0, q=None, out=None) == pa.PA_OK
+
+
+def test_mixed_workspace_size_covers_chunk_partials():
+    # 2,048 chunk tokens + 256 decode segments, Llama-8B heads.
+    ws = pa.mixed_chunk_workspace_size(2304, 260, 8, 4, 128, 80000)
+    assert ws >= 2304 * 32 * 8 * 129 * 4  # every chunk row may need eight key splits
+    assert ws >= pa.decode_workspace_size(260, 8, 4, 128, 80000, 0)
+    assert pa.mixed_chunk_workspace_size(-1, 1, 8, 4, 128, 1) == 0

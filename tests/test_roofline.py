@@ -25,3 +25,15 @@ def test_decode_bytes_counts_kv_once_per_kv_head():
     assert b["tables"] == 4 * 256 + 4
     assert b["q_out"] == 2 * 32 * 128 * 2
     assert roofline.decode_flops(np.array([10, 20]), 32, 128) == 4 * 128 * 32 * 30
+
+
+def test_cascade_accounting_on_the_shared_prefix_workload():
+    from workloads import workload
+
+    lay = workload("shared_prefix")
+    f = roofline.prefix_flops(lay.group_seq_offsets, lay.prefix_lens, lay.num_q_heads, lay.head_dim)
+    assert f == 4 * 128 * 32 * 64 * 2048 * 16  # 34.36 GFLOP
+    b = roofline.cascade_bytes(lay.context_lens, lay.group_seq_offsets, lay.prefix_lens, 32, 8, 128, 2)
+    assert b["prefix_kv"] == 16 * 2048 * 4096
+    naive = roofline.decode_bytes(lay.context_lens, 32, 8, 128, 2)
+    assert naive["kv"] - b["kv"] == 63 * 16 * 2048 * 4096  # the prefix is read once per group, not per member
