@@ -2,12 +2,13 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-A step is one pa_decode call (split-KV kernel + LSE merge) over the whole
-batch, with inputs resident in HBM.  Prints ONE JSON line:
-value = algorithmic bytes per step / measured step time (GB/s), plus decode
-tokens/s for a 32-layer model (attention only), a roofline object for the
-dominant (split-KV) kernel timed with HIP events on its own stream, and the
-fp64 CPU oracle timed on a bounded sample of the same workload.
+A step is one library call over the whole batch (pa_decode for decode
+batches, pa_prefix_cascade for shared-prefix groups, pa_mixed_chunk for
+prefill chunks + decode tokens), with inputs resident in HBM.  Prints ONE
+JSON line: value = algorithmic bytes per step / measured step time (GB/s),
+plus decode tokens/s for a 32-layer model (attention only), a roofline object
+for the dominant kernel timed with HIP events on its own stream, and the fp64
+CPU oracle timed on a bounded sample of the same workload.
 """
 
 from __future__ import annotations
@@ -77,9 +78,20 @@ def copy_probe(nbytes: int) -> None:
     print(json.dumps({"copy_probe_bytes": nbytes, "copies": 3}), flush=True)
 
 
-def cpu_baseline(lay, q, k, v, budget_s):
-    """Time the fp64 oracle, single-threaded, on whole sequences of the same
-    batch until about budget_s seconds of CPU work are spent."""
+def visible_pairs(lay, segs):
+    """(token, key) pairs the given segments' queries see (per q-head)."""
+    tot = 0
+    for s in segs:
+        L, n = int(lay.context_lens[s]), int(lay.q_lens[s])
+        tot += n * (L - n) + n * (n + 1) // 2
+    return tot
+
+
+def cpu_baseline(lay, q, k, v, total_bytes, budget_s):
+    """Time the fp64 oracle, single-threaded, on whole segments of the same
+    batch (random order) until about budget_s seconds of CPU work are spent,
+    then scale to the whole batch by the (token, key) pairs attended and
+    report the batch's algorithmic bytes over that time."""
     import torch
 
     try:
@@ -87,15 +99,15 @@ def cpu_baseline(lay, q, k, v, budget_s):
     except ImportError:  # pragma: no cover
         threadpool_limits = None
     import oracle
-    from paged_kv_decode_02_amd import roofline
 
     def host(t):
         if lay.dtype == "bf16":
             return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
         return t.float().cpu().numpy()
 
+    cu = lay.cu_q_lens
     order = np.random.default_rng(123).permutation(lay.num_seqs)
-    done, spent, nbytes = [], 0.0, 0
+    done, spent = [], 0.0
     limit = threadpool_limits(1) if threadpool_limits else None
     try:
         while spent < budget_s and len(done) < lay.num_seqs:
@@ -103,25 +115,25 @@ def cpu_baseline(lay, q, k, v, budget_s):
             n = (int(lay.context_lens[s]) + 15) // 16
             idx = torch.from_numpy(lay.block_tables[s, :n].astype(np.int64)).to(k.device)
             ks, vs = host(k.index_select(0, idx)), host(v.index_select(0, idx))
-            qs = host(q[s : s + 1])
+            qs = host(q[int(cu[s]) : int(cu[s + 1])])
             bt = np.arange(n, dtype=np.int32)[None, :]  # the gathered pages, relabelled 0..n-1
-            ctx = lay.context_lens[s : s + 1]
             t0 = time.perf_counter()
-            oracle.decode(qs, ks, vs, bt, ctx, lay.scale, lay.num_kv_heads, 16, lay.dtype)
+            oracle.paged_attention(qs, ks, vs, bt, lay.context_lens[s : s + 1], lay.q_lens[s : s + 1], lay.scale,
+                                   lay.num_kv_heads, 16, lay.dtype)
             spent += time.perf_counter() - t0
             done.append(s)
-            nbytes += roofline.decode_bytes(ctx, lay.num_q_heads, lay.num_kv_heads, lay.head_dim,
-                                            lay.elem_bytes)["total"]
     finally:
         if limit is not None:
             limit.unregister()
+    frac = visible_pairs(lay, done) / visible_pairs(lay, range(lay.num_seqs))
+    est = spent / frac
     return {
-        "value": nbytes / spent / 1e9,
+        "value": round(total_bytes / est / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{len(done)} of {lay.num_seqs} sequences ({nbytes / 1e6:.1f} MB algorithmic), "
-                  f"{spent:.1f} s, fp64 numpy, BLAS limited to 1 thread",
+        "sample": f"{len(done)} of {lay.num_seqs} segments ({100 * frac:.1f}% of the batch's (token, key) pairs), "
+                  f"{spent:.1f} s, fp64 numpy, BLAS limited to 1 thread; whole-batch time scaled by pairs",
     }
 
 
@@ -141,9 +153,7 @@ def main():
 
     lay = workload(args.workload, seed=args.seed)
     cascade = lay.group_seq_offsets is not None
-    if lay.q_lens.max() != 1:
-        print(f"{args.workload} is not a decode batch", file=sys.stderr)
-        sys.exit(2)
+    mixed = lay.q_lens.max() > 1
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] workload {args.workload} seed {args.seed}: drawing inputs on the device", file=sys.stderr,
@@ -152,7 +162,8 @@ def main():
     bt = torch.from_numpy(lay.block_tables).to(dev)
     ctx = torch.from_numpy(lay.context_lens).to(dev)
     out = torch.empty_like(q)
-    S, Hq, D = q.shape
+    T, Hq, D = q.shape
+    S = lay.num_seqs
     total_pages = int(((lay.context_lens + 15) // 16).sum())
     stream = torch.cuda.current_stream()
     if cascade:
@@ -164,6 +175,13 @@ def main():
         def step():
             pa.prefix_cascade(out, q, k, v, bt, ctx, lay.context_lens, go, lay.group_seq_offsets, pl,
                               lay.prefix_lens, lay.scale, ws, stream=stream)
+    elif mixed:
+        cu = torch.from_numpy(lay.cu_q_lens.astype(np.int32)).to(dev)
+        ws = torch.empty(pa.mixed_chunk_workspace_size(T, S, lay.num_kv_heads, lay.gqa_ratio, D, total_pages),
+                         dtype=torch.uint8, device=dev)
+
+        def step():
+            pa.mixed_chunk(out, q, k, v, bt, cu, lay.cu_q_lens, ctx, lay.context_lens, lay.scale, ws, stream=stream)
     else:
         ws = torch.empty(pa.decode_workspace_size(S, lay.num_kv_heads, lay.gqa_ratio, D, total_pages,
                                                   args.split_pages), dtype=torch.uint8, device=dev)
@@ -190,50 +208,61 @@ def main():
     ms_per_step = timed(step, args.steps)
     wall = time.perf_counter() - t0
 
-    # Dominant kernel alone: HIP events the library records around it on
-    # the same stream (decode: the stream kernel; cascade: the prefix kernel).
-    pa.profile_enable(args.steps)
+    # Dominant kernel(s) alone: HIP events the library records around them
+    # on the same stream (decode: the stream kernel; cascade: the prefix
+    # kernel; mixed: the chunk kernel, then the decode stream kernel).
+    pairs = 2 if mixed else 1
+    pa.profile_enable(args.steps * pairs)
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
-    kern_ms = pa.profile_collect(args.steps)
+    kern_ms = np.array(pa.profile_collect(args.steps * pairs)).reshape(args.steps, pairs)
     pa.profile_enable(0)
-    kern_avg = float(np.mean(kern_ms))
+    kern_avg = [float(x) for x in kern_ms.mean(axis=0)]
 
+    def hbm_roof(kernel, nbytes, ms, traffic):
+        achieved = nbytes / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": roofline.HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / roofline.HBM_PEAK_GBS, 4), "kernel_ms": round(ms, 5),
+                "traffic": traffic}
+
+    def mfma_roof(kernel, flops, ms):
+        tflops = flops / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "kernel": kernel, "achieved": round(tflops, 1),
+                "peak": roofline.MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / roofline.MFMA_BF16_PEAK_TFLOPS, 4), "kernel_ms": round(ms, 5),
+                "traffic": None}
+
+    extra = {}
     if cascade:
         nb = roofline.cascade_bytes(lay.context_lens, lay.group_seq_offsets, lay.prefix_lens, lay.num_q_heads,
                                     lay.num_kv_heads, D, lay.elem_bytes)
         flops = roofline.prefix_flops(lay.group_seq_offsets, lay.prefix_lens, lay.num_q_heads, D)
-        tflops = flops / (kern_avg * 1e-3) / 1e12
-        roof = {
-            "bound": "mfma",
-            "kernel": "prefix_kernel",
-            "achieved": round(tflops, 1),
-            "peak": roofline.MFMA_BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(tflops / roofline.MFMA_BF16_PEAK_TFLOPS, 4),
-            "kernel_ms": round(kern_avg, 5),
-            "traffic": None,
-        }
+        roof = mfma_roof("tile_kernel (shared prefix)", flops, kern_avg[0])
         # the same batch through plain decode, for the cascade's speed-up
         dws = torch.empty(pa.decode_workspace_size(S, lay.num_kv_heads, lay.gqa_ratio, D, total_pages, 0),
                           dtype=torch.uint8, device=dev)
         dout = torch.empty_like(q)
         dec_ms = timed(lambda: pa.decode(dout, q, k, v, bt, ctx, lay.context_lens, lay.scale, dws, stream=stream),
                        args.steps)
+        extra = {"prefix_gflop": round(flops / 1e9, 3), "decode_same_batch_ms": round(dec_ms, 5),
+                 "cascade_speedup_vs_decode": round(dec_ms / ms_per_step, 3)}
+    elif mixed:
+        nb = roofline.mixed_bytes(lay.context_lens, lay.q_lens, lay.num_q_heads, lay.num_kv_heads, D,
+                                  lay.elem_bytes)
+        flops = roofline.chunk_flops(lay.context_lens, lay.q_lens, lay.num_q_heads, D)
+        chunk_roof = mfma_roof("tile_kernel (prefill chunks)", flops, kern_avg[0])
+        dec = lay.q_lens == 1
+        dbytes = roofline.decode_bytes(lay.context_lens[dec], lay.num_q_heads, lay.num_kv_heads, D,
+                                       lay.elem_bytes)["total"]
+        dec_roof = hbm_roof("stream_decode_kernel (decode tokens)", dbytes, kern_avg[1], None)
+        # the dominant kernel is the one that takes longer
+        roof, other = (chunk_roof, dec_roof) if kern_avg[0] >= kern_avg[1] else (dec_roof, chunk_roof)
+        extra = {"chunk_gflop": round(flops / 1e9, 3), "other_kernel_roofline": other,
+                 "tokens_per_step": int(T)}
     else:
         nb = roofline.decode_bytes(lay.context_lens, lay.num_q_heads, lay.num_kv_heads, D, lay.elem_bytes)
-        achieved = nb["total"] / (kern_avg * 1e-3) / 1e9
-        roof = {
-            "bound": "hbm",
-            "kernel": "stream_decode_kernel",
-            "achieved": round(achieved, 1),
-            "peak": roofline.HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / roofline.HBM_PEAK_GBS, 4),
-            "kernel_ms": round(kern_avg, 5),
-            "traffic": measured_traffic(args.workload),
-        }
+        roof = hbm_roof("stream_decode_kernel", nb["total"], kern_avg[0], measured_traffic(args.workload))
     gbs = nb["total"] / (ms_per_step * 1e-3) / 1e9
     result = {
         "metric": "paged decode attn KV GB/s (% of HBM peak) + decode tokens/s, Llama-8B shape",
@@ -251,6 +280,7 @@ def main():
         "config": {
             "workload": args.workload,
             "num_seqs": int(S),
+            "num_tokens": int(T),
             "q_heads": lay.num_q_heads,
             "kv_heads": lay.num_kv_heads,
             "head_dim": int(D),
@@ -260,18 +290,16 @@ def main():
             "parallelism": "single GPU",
         },
         "hbm_frac": round(gbs / roofline.HBM_PEAK_GBS, 4),
-        "decode_tokens_per_s_32_layers": round(S / (roofline.LLAMA8B_LAYERS * ms_per_step * 1e-3), 1),
+        "decode_tokens_per_s_32_layers": round(int((lay.q_lens == 1).sum()) /
+                                               (roofline.LLAMA8B_LAYERS * ms_per_step * 1e-3), 1),
         "algorithmic_bytes_per_step": nb["total"],
         "wall_s": round(wall, 3),
         "roofline": roof,
     }
-    if cascade:
-        result["prefix_gflop"] = round(flops / 1e9, 3)
-        result["decode_same_batch_ms"] = round(dec_ms, 5)
-        result["cascade_speedup_vs_decode"] = round(dec_ms / ms_per_step, 3)
+    result.update(extra)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(lay, q, k, v, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(lay, q, k, v, nb["total"], args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

@@ -15,13 +15,13 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// float32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two float32 -> a packed bf16 pair (a in the low half), round to nearest
+// even, NaN stays NaN: one v_cvt_pk_bf16_f32 on gfx950, no branches.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
 }
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) { return bf16x2_rne(f, 0.f) & 0xffffu; }
 
 // a.lo*b.lo + a.hi*b.hi + c with bf16 pairs (products exact in float32).
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {

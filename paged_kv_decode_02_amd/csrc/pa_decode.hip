@@ -458,10 +458,10 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
           if (mine) {
             if constexpr (EPC == 8) {
               uint4 o;
-              o.x = bf16_bits_rne(acc[h][0] * inv) | (bf16_bits_rne(acc[h][1] * inv) << 16);
-              o.y = bf16_bits_rne(acc[h][2] * inv) | (bf16_bits_rne(acc[h][3] * inv) << 16);
-              o.z = bf16_bits_rne(acc[h][4] * inv) | (bf16_bits_rne(acc[h][5] * inv) << 16);
-              o.w = bf16_bits_rne(acc[h][6] * inv) | (bf16_bits_rne(acc[h][7] * inv) << 16);
+              o.x = bf16x2_rne(acc[h][0] * inv, acc[h][1] * inv);
+              o.y = bf16x2_rne(acc[h][2] * inv, acc[h][3] * inv);
+              o.z = bf16x2_rne(acc[h][4] * inv, acc[h][5] * inv);
+              o.w = bf16x2_rne(acc[h][6] * inv, acc[h][7] * inv);
               reinterpret_cast<uint4*>(out)[row * NCH + chk] = o;
             } else {
               reinterpret_cast<float4*>(out)[row * NCH + chk] =
@@ -564,7 +564,7 @@ __global__ __launch_bounds__(64) void merge_kernel(T* __restrict__ out, float* _
     if constexpr (sizeof(T) == 2) {
       if constexpr (EPL == 2) {
         reinterpret_cast<uint32_t*>(out)[row * (D / 2) + lane] =
-            bf16_bits_rne(acc[h][0] * inv) | (bf16_bits_rne(acc[h][1] * inv) << 16);
+            bf16x2_rne(acc[h][0] * inv, acc[h][1] * inv);
       } else {
         reinterpret_cast<uint16_t*>(out)[row * D + lane] = static_cast<uint16_t>(bf16_bits_rne(acc[h][0] * inv));
       }

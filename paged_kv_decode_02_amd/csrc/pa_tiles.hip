@@ -47,7 +47,19 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kPrefixRows = kPrefixRowsPerBlock;  // query rows per workgroup (8 waves x 32)
 constexpr int kKeyTile = 64;       // keys per LDS tile (4 pages)
-constexpr int kVtStride = 72;      // bf16 per row of the transposed V tile (64 + 8 pad)
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 LdsI16x4;
+typedef __attribute__((address_space(3))) const u32x4 LdsU4;
+
+// ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, lane j of
+// the group passes the address of 4 consecutive 16-bit elements, row j/4 and
+// columns 4(j%4) .. +3 of a 4 x 16 block; lane j receives column j of that
+// block, rows 0..3.  Returned as two packed 32-bit words.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* lds) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsI16x4*)(lds));
+  return __builtin_bit_cast(u32x2, r);
+}
 
 __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
@@ -78,8 +90,16 @@ __global__ __launch_bounds__(512) void tile_kernel(
     float* __restrict__ pre_lse) {
   constexpr int D = 128;
   constexpr int TILE = 16 * D * 2;  // bytes of one (page, kv-head) tile
-  __shared__ uint4 k_lds[kKeyTile * 16];       // [key][16 chunks], chunk XOR-swizzled by key
-  __shared__ uint16_t vt_lds[D * kVtStride];  // V^T: [d][key]
+  // Two buffers each of K and V tiles: [key][16 chunks of 16 bytes], the
+  // chunk index XOR-swizzled by key % 16 so that column reads spread over
+  // the banks.  Tile t+1 lands in one buffer while tile t is used.
+  // (Four separate arrays, and a loop unrolled by two, so that every LDS
+  // access names its buffer statically: the compiler then sees that reads
+  // of one buffer do not depend on the DMA into the other.)
+  __shared__ uint4 k_lds0[kKeyTile * 16];
+  __shared__ uint4 k_lds1[kKeyTile * 16];
+  __shared__ uint4 v_lds0[kKeyTile * 16];
+  __shared__ uint4 v_lds1[kKeyTile * 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -142,6 +162,8 @@ __global__ __launch_bounds__(512) void tile_kernel(
   // Q^T operand (B of S^T = K Q^T): row r = row0 + 16 rb + col, d = 32 c + 8 lg.
   u32x4 qb[2][4];
   int vis[2];  // CHUNK: last visible key of the lane's query row
+  // CHUNK: last key every row of this wave sees (uniform).
+  const int vis_lo = CHUNK ? L - n_tok + min(row0, n_rows - 1) / G : 0x7fffffff;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const int r = row0 + rb * 16 + col;
@@ -168,41 +190,52 @@ __global__ __launch_bounds__(512) void tile_kernel(
   float m[2] = {-INFINITY, -INFINITY};
   float lsum[2] = {0.f, 0.f};
 
-  for (int kt = k_lo; kt < k_hi; kt += kKeyTile) {
-    const int nk = min(kKeyTile, k_hi - kt);  // keys of this tile that exist
-    const int npg = (nk + 15) / 16;
-    int pid[4];
+  // Page ids of the tile at key kt (uniform: scalar loads).
+  auto tile_pids = [&](int kt, int* pid) {
+    const int npg = (min(kKeyTile, k_hi - kt) + 15) / 16;
 #pragma unroll
     for (int j = 0; j < 4; ++j) pid[j] = min(max(bt[kt / 16 + min(j, npg - 1)], 0), num_pages - 1);
-    // K tile -> LDS: slot (i*8 + wave)*64 + lane holds key slot/16, chunk
-    // (slot%16) ^ (key%16).
+  };
+  // K and V of the tile at kt -> LDS buffer b, by DMA: slot (i*8 + wave)*64
+  // + lane of a buffer holds key slot/16, chunk (slot%16) ^ (key%16).  Keys
+  // past the tile's end (past the split or the sequence) load the last
+  // valid key's row: finite values whose probability is 0.
+  auto issue_tile = [&](int kt, const int* pid, uint4* kw, uint4* vw) {
+    const int nk = min(kKeyTile, k_hi - kt);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int slot = (i * 8 + wv) * 64 + lane;
       const int key = slot >> 4;
       const int ch = (slot & 15) ^ (key & 15);
-      const char* src = kbytes + (static_cast<int64_t>(pid[key >> 4]) * Hkv + kvh) * TILE + (key & 15) * (D * 2) + ch * 16;
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), (LdsPtr)(&k_lds[(i * 8 + wv) * 64]), 16,
-                                       0, 0);
+      const int kc = min(key, nk - 1);
+      const int64_t off = (static_cast<int64_t>(pid[kc >> 4]) * Hkv + kvh) * TILE + (kc & 15) * (D * 2) + ch * 16;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(kbytes + off),
+                                       (LdsPtr)(&kw[(i * 8 + wv) * 64]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vbytes + off),
+                                       (LdsPtr)(&vw[(i * 8 + wv) * 64]), 16, 0, 0);
     }
-    // V tile -> registers -> transposed into LDS; rows past the tile's keys
-    // (tail rows of a last page hold NaN) become zeros.
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int uu = i * 512 + tid;
-      const int key = uu >> 4;
-      const int dc = uu & 15;
-      const char* src = vbytes + (static_cast<int64_t>(pid[key >> 4]) * Hkv + kvh) * TILE + (key & 15) * (D * 2) + dc * 16;
-      u32x4 v = *reinterpret_cast<const u32x4*>(src);
-      if (key >= nk) v = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vt_lds[(dc * 8 + 2 * e) * kVtStride + key] = static_cast<uint16_t>(v[e] & 0xffffu);
-        vt_lds[(dc * 8 + 2 * e + 1) * kVtStride + key] = static_cast<uint16_t>(v[e] >> 16);
-      }
-    }
+  };
+  // Per-lane byte offsets of the transposed V reads inside a buffer: lane
+  // (group lg, j) reads row key0 + j/4, columns d0 + 4(j%4) .. +3, with
+  // key0 = 4 lg (+16, +32, +48) and d0 = 16 db.
+  const int tr_r = col >> 2;
+  const int tr_c = col & 3;
+
+  int pid[4];
+  tile_pids(k_lo, pid);
+  issue_tile(k_lo, pid, k_lds0, v_lds0);
+  // One tile: wait for its DMA, start the next tile's into the other
+  // buffers, compute.  Returns whether another tile follows.
+  auto tile = [&](int kt, const uint4* kb_lds, const uint4* vb_lds4, uint4* k_next, uint4* v_next) -> bool {
+    const int nk = min(kKeyTile, k_hi - kt);  // keys of this tile that exist
+    const bool more = kt + kKeyTile < k_hi;
+    if (more) tile_pids(kt + kKeyTile, pid);
+    // This tile's DMA (issued one tile ago) has landed for every wave, and
+    // every wave is done with the other buffers.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (more) issue_tile(kt + kKeyTile, pid, k_next, v_next);
+    const char* vb_lds = reinterpret_cast<const char*>(vb_lds4);
 
     // S^T = K Q^T: s[kb][rb] holds keys 16 kb + 4 lg + i, query row 16 rb + col.
     f32x4 s[4][2];
@@ -214,34 +247,60 @@ __global__ __launch_bounds__(512) void tile_kernel(
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int cc = c * 4 + lg;
-        const u32x4 a = *reinterpret_cast<const u32x4*>(&k_lds[key * 16 + (cc ^ (key & 15))]);
+        const u32x4 a = *(LdsU4*)(&kb_lds[key * 16 + (cc ^ (key & 15))]);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) s[kb][rb] = mfma16x16x32(a, qb[rb][c], s[kb][rb]);
       }
     }
     // Online softmax per query row (column of S^T); the 64 keys of a row are
     // spread over this lane's 16 values and the lanes l^16, l^32, l^48.
-    u32x4 pb[2][2];  // P^T operand: [rb][key half]
+    // Keys are masked (by select) only in tiles that need it: the last,
+    // partial tile of a split, and chunk tiles that cross the causal
+    // diagonal of this wave's rows.
+    const bool need_mask = nk < kKeyTile || (CHUNK && kt + kKeyTile - 1 > vis_lo);
+    if (need_mask) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kb * 16 + lg * 4 + i;
+            const bool ok = key < nk && (!CHUNK || kt + key <= vis[rb]);
+            s[kb][rb][i] = ok ? s[kb][rb][i] : -INFINITY;
+          }
+    }
+    float mx[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      float mx = -INFINITY;
+      float x = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kb * 16 + lg * 4 + i;
-          const bool ok = key < nk && (!CHUNK || kt + key <= vis[rb]);
-          const float x = ok ? s[kb][rb][i] * scale_log2 : -INFINITY;
-          s[kb][rb][i] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = max_xor32(max_xor16(mx));
-      const float mn = fmaxf(m[rb], mx);
-      // A row with no visible key so far keeps m = -inf; use 0 as its
-      // reference so no -inf - -inf appears (its p are all 0).
-      const float ref = mn == -INFINITY ? 0.f : mn;
-      const float alpha = fast_exp2(m[rb] - ref);
-      m[rb] = mn;
+        for (int i = 0; i < 4; ++i) x = fmaxf(x, s[kb][rb][i]);
+      mx[rb] = max_xor32(max_xor16(x)) * scale_log2;  // scale > 0 keeps the order
+    }
+    // Lazy rescaling: probabilities are taken against the running reference
+    // m, which moves (and o, l are rescaled) only when a row's maximum
+    // exceeds it by more than 2^8 -- so p <= 256, and the rescale, a wave-wide
+    // branch, is rare after the first tiles.
+    if (__ballot(mx[0] > m[0] + 8.f || mx[1] > m[1] + 8.f) != 0ull) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const float mn = fmaxf(m[rb], mx[rb]);
+        // m = -inf (nothing visible yet): o and l are 0, any factor will do
+        const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m[rb] - mn);
+        m[rb] = mn;
+        lsum[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) o[db][rb] *= alpha;
+      }
+    }
+    u32x4 pb[2][2];  // P^T operand: [rb][key half]
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      // A row with no visible key so far keeps m = -inf: its p are all 0.
+      const float nref = m[rb] == -INFINITY ? 0.f : -m[rb];
       float ps = 0.f;
       uint32_t pw[4][2];
 #pragma unroll
@@ -249,35 +308,42 @@ __global__ __launch_bounds__(512) void tile_kernel(
         float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[i] = fast_exp2(s[kb][rb][i] - ref);
+          p[i] = fast_exp2(fmaf(s[kb][rb][i], scale_log2, nref));
           ps += p[i];
         }
-        pw[kb][0] = bf16_bits_rne(p[0]) | (bf16_bits_rne(p[1]) << 16);
-        pw[kb][1] = bf16_bits_rne(p[2]) | (bf16_bits_rne(p[3]) << 16);
+        pw[kb][0] = bf16x2_rne(p[0], p[1]);
+        pw[kb][1] = bf16x2_rne(p[2], p[3]);
       }
-      lsum[rb] = lsum[rb] * alpha + ps;
-#pragma unroll
-      for (int db = 0; db < 8; ++db) o[db][rb] *= alpha;
+      lsum[rb] += ps;
       // k slots 8 lg .. 8 lg + 7 of key half hf = keys 32 hf + 4 lg + [0, 4)
       // and 32 hf + 16 + 4 lg + [0, 4): the same order the V^T operand uses.
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
         pb[rb][hf] = u32x4{pw[2 * hf][0], pw[2 * hf][1], pw[2 * hf + 1][0], pw[2 * hf + 1][1]};
     }
-    // O^T += V^T P^T.
+    // O^T += V^T P^T; the V^T operand (d = 16 db + col, keys as above) comes
+    // from two transposed reads of 4 keys each.
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      const int d = db * 16 + col;
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(&vt_lds[d * kVtStride + hf * 32 + lg * 4]);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(&vt_lds[d * kVtStride + hf * 32 + 16 + lg * 4]);
-        const u32x4 a = u32x4{lo.x, lo.y, hi.x, hi.y};
+        u32x2 part[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int row = hf * 32 + e * 16 + lg * 4 + tr_r;
+          const int ch = (db * 2 + (tr_c >> 1)) ^ (row & 15);
+          part[e] = lds_read_tr16(vb_lds + row * (D * 2) + ch * 16 + (tr_c & 1) * 8);
+        }
+        const u32x4 a = u32x4{part[0].x, part[0].y, part[1].x, part[1].y};
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) o[db][rb] = mfma16x16x32(a, pb[rb][hf], o[db][rb]);
       }
     }
-    __syncthreads();
+    return more;
+  };
+  for (int kt = k_lo;; kt += 2 * kKeyTile) {
+    if (!tile(kt, k_lds0, v_lds0, k_lds1, v_lds1)) break;
+    if (!tile(kt + kKeyTile, k_lds1, v_lds1, k_lds0, v_lds0)) break;
   }
 
   // Partials: o / l per query row, log2-sum-exp.
@@ -341,7 +407,7 @@ __global__ __launch_bounds__(64) void chunk_merge_kernel(uint16_t* __restrict__ 
     }
     const float inv = 1.0f / wsum;
     const int64_t row = static_cast<int64_t>(cu_q[s] + i) * Hq + kvh * G + h;
-    reinterpret_cast<uint32_t*>(out)[row * (D / 2) + lane] = bf16_bits_rne(acc0 * inv) | (bf16_bits_rne(acc1 * inv) << 16);
+    reinterpret_cast<uint32_t*>(out)[row * (D / 2) + lane] = bf16x2_rne(acc0 * inv, acc1 * inv);
     if (lse_out && lane == 0) lse_out[row] = (M + fast_log2(wsum)) * kLn2;
   }
 }
@@ -403,7 +469,7 @@ __global__ __launch_bounds__(64) void cascade_merge_kernel(
     if constexpr (sizeof(T) == 2) {
       if constexpr (EPL == 2) {
         reinterpret_cast<uint32_t*>(out)[row * (D / 2) + lane] =
-            bf16_bits_rne(acc[0] * inv) | (bf16_bits_rne(acc[1] * inv) << 16);
+            bf16x2_rne(acc[0] * inv, acc[1] * inv);
       } else {
         reinterpret_cast<uint16_t*>(out)[row * D + lane] = static_cast<uint16_t>(bf16_bits_rne(acc[0] * inv));
       }

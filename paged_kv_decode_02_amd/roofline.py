@@ -61,3 +61,27 @@ def prefix_flops(group_seq_offsets, prefix_lens, num_q_heads, head_dim) -> int:
     offs = np.asarray(group_seq_offsets, dtype=np.int64)
     pl = np.asarray(prefix_lens, dtype=np.int64)
     return int(4 * head_dim * num_q_heads * (np.diff(offs) * pl).sum())
+
+
+def mixed_bytes(context_lens, q_lens, num_q_heads, num_kv_heads, head_dim, elem_bytes, block_size=16) -> dict:
+    """Mixed batch: every segment's visible K/V read once per kv-head (a
+    chunk's rows once for all its tokens), plus q and out for every token
+    and the table entries walked."""
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    ql = np.asarray(q_lens, dtype=np.int64)
+    kv = kv_cache_bytes(1, num_kv_heads, head_dim, int(ctx.sum()), elem_bytes)
+    qo = 2 * int(ql.sum()) * num_q_heads * head_dim * elem_bytes
+    tables = 4 * int(((ctx + block_size - 1) // block_size).sum()) + 4 * (2 * ctx.size + 1)
+    dec = ql == 1
+    return {"kv": kv, "q_out": qo, "tables": tables, "total": kv + qo + tables,
+            "decode_kv": kv_cache_bytes(1, num_kv_heads, head_dim, int(ctx[dec].sum()), elem_bytes)}
+
+
+def chunk_flops(context_lens, q_lens, num_q_heads, head_dim) -> int:
+    """q.k and p.v of the prefill chunks (q_len > 1) under the causal mask:
+    token i of a segment with L rows and n tokens sees L - n + i + 1 keys."""
+    total = 0
+    for L, n in zip(np.asarray(context_lens, dtype=np.int64), np.asarray(q_lens, dtype=np.int64)):
+        if n > 1:
+            total += int(n * (L - n) + n * (n + 1) // 2)
+    return int(4 * head_dim * num_q_heads * total)

@@ -37,3 +37,21 @@ def test_cascade_accounting_on_the_shared_prefix_workload():
     assert b["prefix_kv"] == 16 * 2048 * 4096
     naive = roofline.decode_bytes(lay.context_lens, 32, 8, 128, 2)
     assert naive["kv"] - b["kv"] == 63 * 16 * 2048 * 4096  # the prefix is read once per group, not per member
+
+
+def test_mixed_accounting_on_the_chunked_piggyback_workload():
+    from workloads import workload
+
+    lay = workload("chunked_piggyback")
+    f = roofline.chunk_flops(lay.context_lens, lay.q_lens, 32, 128)
+    # token i of a 512-token chunk after prefix p sees p + i + 1 keys
+    want = 4 * 128 * 32 * sum(512 * p + 512 * 513 // 2 for p in (0, 1024, 4096, 8192))
+    assert f == want  # 120.27 GFLOP
+    assert abs(f / 1e9 - 120.27) < 0.01
+    # brute-force the causal count on one small segment
+    assert roofline.chunk_flops([7], [3], 1, 1) == 4 * (5 + 6 + 7)
+    assert roofline.chunk_flops([9], [1], 1, 1) == 0  # decode tokens are not chunk work
+    b = roofline.mixed_bytes(lay.context_lens, lay.q_lens, 32, 8, 128, 2)
+    assert b["kv"] == 2 * 8 * 128 * 2 * int(lay.context_lens.sum())
+    assert b["decode_kv"] == 2 * 8 * 128 * 2 * int(lay.context_lens[4:].sum())
+    assert b["q_out"] == 2 * 2304 * 32 * 128 * 2
