@@ -150,11 +150,13 @@ extern "C" int pa_prefix_cascade(void* out, float* lse_out, const void* q, const
     }
   }
   if (suffix_pages > (int64_t(1) << 31) - 1) return fail(PA_EUNSUPPORTED, "pa_prefix_cascade: too many pages");
-  // Prefix plan: about 512 workgroups, each a 64-key multiple of the prefix.
+  // Prefix plan: one workgroup per CU holds 128 KB of LDS, so aim at about
+  // 256 workgroups (row blocks x key splits), each a 64-key multiple of the
+  // prefix; key splits only when the row blocks alone leave CUs idle.
   const int32_t row_chunks =
       static_cast<int32_t>(std::max<int64_t>(1, (max_rows + kPrefixRowsPerBlock - 1) / kPrefixRowsPerBlock));
   const int64_t units = static_cast<int64_t>(num_groups) * row_chunks * num_kv_heads;
-  int32_t nks = static_cast<int32_t>(std::min<int64_t>(kMaxPrefixSplits, std::max<int64_t>(1, (512 + units - 1) / units)));
+  int32_t nks = static_cast<int32_t>(std::min<int64_t>(kMaxPrefixSplits, std::max<int64_t>(1, (256 + units - 1) / units)));
   int32_t kps = 64;
   if (max_prefix > 0) {
     kps = (max_prefix + nks - 1) / nks;

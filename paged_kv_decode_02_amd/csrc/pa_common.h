@@ -33,6 +33,31 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// LDS byte offset of a pointer into a __shared__ object.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<size_t>((__attribute__((address_space(3))) const void*)(p)));
+}
+
+// 16 bytes per lane from global memory straight into LDS, lane i's bytes at
+// lds_base + 16 i (global_load_lds_dwordx4; M0 holds the wave's LDS base).
+// Issued through inline assembly so that the compiler does not track it: a
+// tracked LDS DMA makes the compiler put a wait for *all* outstanding vector
+// memory accesses (vmcnt(0)) in front of every later LDS read, which would
+// drain every prefetch.  Callers wait for these loads with explicit
+// s_waitcnt vmcnt, and order them against LDS reads of the same bytes.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds_base) : "memory");
+}
+// The same from a wave-uniform base (SGPRs) plus a per-lane 32-bit byte
+// offset: the address arithmetic that depends on the page stays scalar.
+__device__ __forceinline__ void dma16_sbase(const void* sbase, uint32_t voffset, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voffset), "s"(sbase), "{m0}"(lds_base) : "memory");
+}
+// The same with 4 bytes per lane (lane i's dword at lds_base + 4 i).
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(gptr), "{m0}"(lds_base) : "memory");
+}
+
 // Cross-lane steps without LDS: DPP inside rows of 16 lanes, and gfx950's
 // v_permlane16_swap / v_permlane32_swap across rows.
 template <int CTRL>

@@ -48,7 +48,6 @@ namespace pa {
 namespace {
 
 // LDS pointer types (DMA destination; opaque q reads).
-typedef __attribute__((address_space(3))) void* LdsPtr;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) const u32x4 LdsU4;
 
@@ -129,6 +128,16 @@ __device__ __forceinline__ float dot_chunk(const uint4& k, uint32_t q0, uint32_t
   return acc;
 }
 
+// The workgroup is one wave, whose LDS accesses execute in order: sharing
+// values between lanes through LDS needs no barrier, only that the compiler
+// keep the accesses in program order.  (__syncthreads() would also wait for
+// every outstanding global load, draining the K/V prefetch.)  LDS DMA
+// (global_load_lds) is waited for by vmcnt explicitly.
+__device__ __forceinline__ void lds_order() {
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Pair two rows' bf16 values column by column: (lo: row a, hi: row b).
 __device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
 __device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
@@ -149,7 +158,8 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
   constexpr int QU4 = G * NCH;               // 16-byte chunks of the G q rows
   constexpr int QPL = (QU4 + 63) / 64;        // of them per lane when loading
   __shared__ uint4 k_lds[64 * NCH];
-  __shared__ uint4 q_lds[QU4];
+  __shared__ uint4 v_lds[64 * NCH];
+  __shared__ uint4 q_lds[2][QPL * 64];              // two sequences' q rows (current, next)
   __shared__ __align__(16) uint32_t p_lds[G * 64];  // fp32 bits, or bf16 in the first half
 
   const int lane = lane_id();
@@ -199,48 +209,37 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
   cur.pb = cur.seg_lo;
   load_pids(block_tables, max_blocks, num_pages, cur);
 
-  uint4 vr[NI];
+  // K and V of a batch go to LDS by DMA, NI loads of 1 KB each: K with the
+  // swizzled layout above; V as it is in the pool (instruction i: rows
+  // i*RPI .. +RPI, lane (grp, chk) = its row grp, chunk chk).
+  const uint32_t k_base = lds_offset(k_lds);
+  const uint32_t v_base = lds_offset(v_lds);
   auto issue_k = [&](const Batch& b) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const char* tile = kbytes + (static_cast<int64_t>(b.pid[i / per_tile]) * Hkv + kvh) * TILE;
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(tile + koff[i % per_tile]),
-                                       (LdsPtr)(&k_lds[i * 64]), 16, 0, 0);
+      dma16(tile + koff[i % per_tile], k_base + i * 1024);
     }
   };
-  // `dep` is a value computed after the last use of vr: routing the offset
-  // through an opaque asm that reads it keeps the compiler from hoisting
-  // the next batch's V loads above this batch's P.V (which would need a
-  // second set of 4*NI registers).
-  auto issue_v = [&](const Batch& b, float dep) {
-    uint32_t vo = voff;
-    asm volatile("" : "+v"(vo) : "v"(dep));
+  auto issue_v = [&](const Batch& b) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int row0 = i * RPI;
       const char* tile = vbytes + (static_cast<int64_t>(b.pid[row0 / 16]) * Hkv + kvh) * TILE;
-      vr[i] = *reinterpret_cast<const uint4*>(tile + (row0 % 16) * (RD * 4) + vo);
+      dma16(tile + (row0 % 16) * (RD * 4) + voff, v_base + i * 1024);
     }
   };
 
-  // The G q rows of sequence s for this kv-head, into registers; written
-  // to LDS when that sequence's first batch is scored.
-  uint4 qreg[QPL];
+  // The G q rows of sequence s for this kv-head, by DMA into q buffer qb
+  // (lanes past the rows repeat the last chunk into the buffer's tail).
   // Row of q / out / lse of sequence s (mixed batches: its one token).
   auto qrow = [&](int s) -> int64_t { return q_rows ? q_rows[s] : s; };
-  auto load_q = [&](int s) {
+  auto load_q = [&](int s, int qb) {
     const uint4* src = reinterpret_cast<const uint4*>(q + (qrow(s) * Hq + kvh * G) * D);
 #pragma unroll
     for (int i = 0; i < QPL; ++i) {
       const int u = i * 64 + lane;
-      qreg[i] = src[u < QU4 ? u : QU4 - 1];
-    }
-  };
-  auto store_q = [&]() {
-#pragma unroll
-    for (int i = 0; i < QPL; ++i) {
-      const int u = i * 64 + lane;
-      if (u < QU4) q_lds[u] = qreg[i];
+      dma16(src + (u < QU4 ? u : QU4 - 1), lds_offset(&q_lds[qb][i * 64]));
     }
   };
 
@@ -256,10 +255,10 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
   };
   reset();
 
-  load_q(cur.s);
-  bool q_pending = true;  // qreg holds q of cur.s, not yet in LDS
+  int qcur = 0;  // q buffer of sequence cur.s
+  load_q(cur.s, qcur);
   issue_k(cur);
-  issue_v(cur, 0.f);
+  issue_v(cur);
 
   while (true) {
     // Coordinates of the next batch (same sequence, or the next one).
@@ -291,19 +290,14 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
     }
     if (has_next) load_pids(block_tables, max_blocks, num_pages, nxt);
 
-    // K of this batch (and q, loaded before it) is in LDS / registers once
-    // only V (NI loads) may be outstanding.
+    // K of this batch (and q, loaded before it) is in LDS once only this
+    // batch's V (NI loads) may be outstanding.
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI) : "memory");
-    if (q_pending) {
-      store_q();
-      q_pending = false;
-    }
-    __syncthreads();
+    lds_order();
+    // The next sequence's q goes to the other q buffer (last read two
+    // sequences ago).
     const bool next_seq = has_next && nxt.s != cur.s;
-    if (next_seq) {
-      load_q(nxt.s);
-      q_pending = true;
-    }
+    if (next_seq) load_q(nxt.s, qcur ^ 1);
 
     // Scores, lane = row: K row chunks and q chunks (one address for the
     // whole wave, a broadcast read) from LDS, CG chunks at a time.
@@ -317,7 +311,7 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
       // tied to the previous group's result, so each group's reads are
       // issued after the previous group's math: only CG chunks of K and
       // G*CG chunks of q are in registers at a time.
-      LdsU4* qp = (LdsU4*)(&q_lds[0]);
+      LdsU4* qp = (LdsU4*)(&q_lds[qcur][0]);
       LdsU4* kp = (LdsU4*)(&k_lds[lane * NCH]);
 #pragma unroll
       for (int h = 0; h < G; ++h) asm volatile("" : "+v"(qp), "+v"(kp) : "v"(sc[h]));
@@ -363,7 +357,15 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    lds_order();
+    // This batch's V rows to registers; once read, the buffer takes the
+    // next batch's V, which then streams in during this batch's P.V and
+    // the next batch's scores.
+    uint4 vr[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) vr[i] = v_lds[i * 64 + lane];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (has_next) issue_v(nxt);
     if (nvalid < 64) {
 #pragma unroll
       for (int i = 0; i < NI; ++i)
@@ -412,7 +414,6 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
       }
     }
     const bool seg_end = cur.pb + 4 >= cur.seg_hi;
-    if (has_next && !seg_end) issue_v(nxt, acc[G - 1][EPC - 1]);
 
     if (seg_end) {
       // End of this wave's part of sequence cur.s: sum the row groups,
@@ -480,12 +481,10 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
           if (lane == 0) part_lse[r] = lse2;
         }
       }
-      // The next V is fetched only now, so the finalisation above does not
-      // hold a second batch of V in registers.
-      if (has_next) issue_v(nxt, m[G - 1]);
       reset();
     }
     if (!has_next) break;
+    if (next_seq) qcur ^= 1;
     cur = nxt;
   }
 }

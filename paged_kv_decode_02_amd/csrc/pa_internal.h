@@ -15,7 +15,7 @@ constexpr int kBlockSize = 16;            // rows per page: the only page size b
 constexpr int kMinPagesPerWave = 4;       // automatic runs are at least one 4-page batch
 constexpr int kMaxResidentWaves = 16384;  // bound on waves resident on one GPU (sizes workspace)
 constexpr int kMaxPrefixSplits = 8;       // key splits of a shared prefix (sizes workspace)
-constexpr int kPrefixRowsPerBlock = 256;  // query rows one prefix workgroup takes
+constexpr int kPrefixRowsPerBlock = 128;  // query rows one MFMA tile workgroup takes
 constexpr size_t kAlign = 256;
 
 // Error reporting: thread-local message + code.

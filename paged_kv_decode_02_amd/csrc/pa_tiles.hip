@@ -39,14 +39,14 @@
 namespace pa {
 namespace {
 
-typedef __attribute__((address_space(3))) void* LdsPtr;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kPrefixRows = kPrefixRowsPerBlock;  // query rows per workgroup (8 waves x 32)
-constexpr int kKeyTile = 64;       // keys per LDS tile (4 pages)
+constexpr int kRows = kPrefixRowsPerBlock;  // query rows per workgroup: 4 row groups of 32
+constexpr int kKeyTile = 64;                  // keys per LDS tile (4 pages); each wave takes 32 of them
+constexpr int kPidWindow = 256;               // page ids per LDS window (64 tiles)
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 LdsI16x4;
@@ -66,18 +66,41 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, co
                                                  0, 0);
 }
 
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier that leaves global loads in flight: __syncthreads()
+// also waits for every outstanding vector memory access (vmcnt(0)), which
+// would drain the tile prefetch at each barrier.  LDS accesses are waited
+// for (lgkmcnt(0)); the DMA'd tiles are waited for explicitly by vmcnt.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // MFMA 16x16x32 operand layout (wave64): A (16 x 32): lane l holds row l%16,
 // k = 8*(l/16) .. +8; B (32 x 16): lane l holds column l%16, the same k;
 // C (16 x 16): lane l holds column l%16, rows 4*(l/16) .. +4.
 //
-// One workgroup = 8 waves = up to 256 query rows of one kv-head against the
-// keys [k_lo, k_hi) of one block-table row, in tiles of 64 keys.
+// One workgroup = 8 waves = up to 128 query rows of one kv-head against the
+// keys [k_lo, k_hi) of one block-table row, in tiles of 64 keys that stream
+// through four LDS buffers (three tiles in flight while one is used).  Wave
+// (row group rg, key half kh) takes query rows 32 rg .. +32 against keys
+// 32 kh .. +32 of every tile, so two waves share each SIMD and every K/V byte
+// in LDS is read by four waves; at the end the two key halves of a row group
+// are merged through LDS.
 //  PREFIX: unit = a group; rows are (member, q-head) pairs; keys are the
 //          shared prefix, read through the first member's table; every row
 //          sees every key.
 //  CHUNK:  unit = a prefill chunk (segment with more than one query token);
 //          rows are (token, q-head) pairs; keys are the segment's own rows;
 //          token i sees keys t <= L - n + i (causal inside the chunk).
+// Work items (unit, kv-head, key split) are numbered w; the row blocks of
+// one item sit on consecutive slots of one XCD (workgroup i runs on XCD
+// i % 8), so they fetch the same K/V tiles through the same L2.
 // Output: one partial (normalised o, log2-sum-exp) per (row, key split);
 // a row that sees no key of the split gets o = 0, lse = -inf.
 template <int G, bool CHUNK>
@@ -85,38 +108,35 @@ __global__ __launch_bounds__(512) void tile_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool,
     const int32_t* __restrict__ block_tables, int max_blocks, const int32_t* __restrict__ ctx,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ group_off, const int32_t* __restrict__ prefix_lens,
-    ChunkList chunks, int S, int RC, int nks, int kps, int Hkv, int num_pages, float scale_log2,
+    ChunkList chunks, int S, int RC, int nks, int kps, int Hkv, int n_items, int num_pages, float scale_log2,
     int32_t* __restrict__ begin_pages, int32_t* __restrict__ seq_info, float* __restrict__ pre_o,
     float* __restrict__ pre_lse) {
   constexpr int D = 128;
   constexpr int TILE = 16 * D * 2;  // bytes of one (page, kv-head) tile
-  // Two buffers each of K and V tiles: [key][16 chunks of 16 bytes], the
-  // chunk index XOR-swizzled by key % 16 so that column reads spread over
-  // the banks.  Tile t+1 lands in one buffer while tile t is used.
-  // (Four separate arrays, and a loop unrolled by two, so that every LDS
-  // access names its buffer statically: the compiler then sees that reads
-  // of one buffer do not depend on the DMA into the other.)
-  __shared__ uint4 k_lds0[kKeyTile * 16];
-  __shared__ uint4 k_lds1[kKeyTile * 16];
-  __shared__ uint4 v_lds0[kKeyTile * 16];
-  __shared__ uint4 v_lds1[kKeyTile * 16];
+  // Four buffers each of K and V: [key][16 chunks of 16 bytes], the chunk
+  // index XOR-swizzled by key % 16 so that column reads spread over the
+  // banks.  The tiles arrive by DMA (dma16), waited for explicitly.
+  // (Four arrays each, named statically in a loop unrolled by four.)
+  __shared__ uint4 k_lds0[kKeyTile * 16], k_lds1[kKeyTile * 16], k_lds2[kKeyTile * 16], k_lds3[kKeyTile * 16];
+  __shared__ uint4 v_lds0[kKeyTile * 16], v_lds1[kKeyTile * 16], v_lds2[kKeyTile * 16], v_lds3[kKeyTile * 16];
+  // Page ids of the key range, in windows of kPidWindow pages (64 tiles),
+  // two windows resident: reading an id from LDS is one short broadcast
+  // read, where a scalar load from the table would put a cache round trip
+  // in front of every tile's DMA.
+  __shared__ int32_t pid_lds[2][kPidWindow];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
-  int bx = blockIdx.x;
-  const int ks = bx % nks;
-  bx /= nks;
-  const int rc = bx % RC;
-  const int u = bx / RC;
-  const int kvh = blockIdx.y;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // (wave-uniform: scalar from here on)
+  const int rg = wv & 3;   // row group
+  const int kh = wv >> 2;  // key half
   const int Hq = Hkv * G;
 
-  // Per-sequence set-up for the launches that follow (first suffix page;
-  // for mixed batches also the "not shared" record the decode merge reads).
-  int seg, n_rows, k_lo, k_hi, L = 0, n_tok = 1, q_base, part_base;
+  // Per-sequence set-up for the launches that follow (mixed batches: each
+  // chunk's "no decode pages" mark and the "not shared" record the decode
+  // merge reads).
   if constexpr (CHUNK) {
-    if (blockIdx.x == 0 && blockIdx.y == 0) {
+    if (blockIdx.x == 0) {
       for (int s = tid; s < S; s += 512) {
         const bool chunk = cu_q[s + 1] - cu_q[s] > 1;
         const int64_t pg = (static_cast<int64_t>(ctx[s]) + 15) >> 4;
@@ -129,6 +149,21 @@ __global__ __launch_bounds__(512) void tile_kernel(
         }
       }
     }
+  }
+
+  // Workgroup -> (item w, row block rc): slot j of XCD x holds row block
+  // j % RC of item (j / RC) * 8 + x.
+  const int xcd = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  const int w = (slot / RC) * 8 + xcd;
+  const int rc = slot % RC;
+  if (w >= n_items) return;
+  const int ks = w % nks;
+  const int kvh = (w / nks) % Hkv;
+  const int u = w / (nks * Hkv);
+
+  int seg, n_rows, k_lo, k_hi, L = 0, n_tok = 1, q_base, part_base;
+  if constexpr (CHUNK) {
     if (u >= chunks.n) return;
     seg = chunks.seg[u];
     n_tok = cu_q[seg + 1] - cu_q[seg];
@@ -136,7 +171,7 @@ __global__ __launch_bounds__(512) void tile_kernel(
     n_rows = n_tok * G;
     q_base = cu_q[seg];
     part_base = chunks.tok_off[u];
-    const int r_end = min(n_rows, (rc + 1) * kPrefixRows);
+    const int r_end = min(n_rows, (rc + 1) * kRows);
     const int i_max = (r_end - 1) / G;
     const int k_end = min(L, L - n_tok + i_max + 1);
     k_lo = ks * kps;
@@ -154,9 +189,9 @@ __global__ __launch_bounds__(512) void tile_kernel(
     k_lo = ks * kps;
     k_hi = min(P, k_lo + kps);
   }
-  if (k_lo >= k_hi || rc * kPrefixRows >= n_rows) return;  // uniform over the workgroup
+  if (k_lo >= k_hi || rc * kRows >= n_rows) return;  // uniform over the workgroup
 
-  const int row0 = rc * kPrefixRows + wv * 32;  // first of this wave's 32 query rows
+  const int row0 = rc * kRows + rg * 32;  // first of this wave's 32 query rows
   const int col = lane & 15;
   const int lg = lane >> 4;
   // Q^T operand (B of S^T = K Q^T): row r = row0 + 16 rb + col, d = 32 c + 8 lg.
@@ -178,70 +213,140 @@ __global__ __launch_bounds__(512) void tile_kernel(
       }
     }
   }
+  // Wait for the q rows here, before any tile DMA is in flight: the
+  // compiler does not see the (inline-assembly) DMAs, and left to itself it
+  // would wait for q -- with vmcnt(0), draining the tile pipeline -- at the
+  // first MFMA of every tile.
+  asm volatile("" ::"v"(qb[0][0]), "v"(qb[0][1]), "v"(qb[0][2]), "v"(qb[0][3]), "v"(qb[1][0]), "v"(qb[1][1]),
+               "v"(qb[1][2]), "v"(qb[1][3]));
   const int32_t* bt = block_tables + static_cast<int64_t>(seg) * max_blocks;
   const char* kbytes = reinterpret_cast<const char*>(k_pool);
   const char* vbytes = reinterpret_cast<const char*>(v_pool);
 
+  // O^T accumulators, and the row sums of P (as bf16, the values P.V
+  // uses) from one more MFMA per row block against an all-ones A operand:
+  // every element of osum[rb] is the sum over this wave's keys of its row.
   f32x4 o[8][2];
+  f32x4 osum[2];
 #pragma unroll
-  for (int db = 0; db < 8; ++db)
+  for (int rb = 0; rb < 2; ++rb) {
+    osum[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) o[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < 8; ++db) o[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   float m[2] = {-INFINITY, -INFINITY};
-  float lsum[2] = {0.f, 0.f};
+  const u32x4 ones = u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0 pairs
 
-  // Page ids of the tile at key kt (uniform: scalar loads).
-  auto tile_pids = [&](int kt, int* pid) {
-    const int npg = (min(kKeyTile, k_hi - kt) + 15) / 16;
+  // K or V of tile t (keys k_lo + 64 t ..) -> an LDS buffer, by DMA: slot
+  // (i*8 + wave)*64 + lane of a buffer holds key slot/16, chunk
+  // (slot%16) ^ (key%16).  Keys past the tile's end (past the split or the
+  // sequence) load the last valid key's row: finite values whose
+  // probability is 0.
+  const int nt = (k_hi - k_lo + kKeyTile - 1) / kKeyTile;
+  // Lane offsets of a whole tile's DMA inside its page tile: slot
+  // (i*8 + wave)*64 + lane -> key row % 16 and the swizzled chunk.
+  uint32_t dma_off[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) pid[j] = min(max(bt[kt / 16 + min(j, npg - 1)], 0), num_pages - 1);
+  for (int i = 0; i < 2; ++i) {
+    const int sl = (i * 8 + wv) * 64 + lane;
+    const int key = sl >> 4;
+    dma_off[i] = (key & 15) * (D * 2) + ((sl & 15) ^ (key & 15)) * 16;
+  }
+  // Window w of page ids: pages k_lo/16 + 256 w .. +256 of the table row
+  // (entries past the row read its last entry), one dword DMA per wave
+  // from waves 0..3.
+  const int pg0 = k_lo / 16;
+  auto issue_pids = [&](int w) {
+    if (wv < 4) {
+      const int p = min(pg0 + w * kPidWindow + wv * 64 + lane, max_blocks - 1);
+      dma4(bt + p, lds_offset(&pid_lds[w & 1][wv * 64]));
+    }
   };
-  // K and V of the tile at kt -> LDS buffer b, by DMA: slot (i*8 + wave)*64
-  // + lane of a buffer holds key slot/16, chunk (slot%16) ^ (key%16).  Keys
-  // past the tile's end (past the split or the sequence) load the last
-  // valid key's row: finite values whose probability is 0.
-  auto issue_tile = [&](int kt, const int* pid, uint4* kw, uint4* vw) {
+  // Two DMA loads per wave: this wave's share of tile t of the pool at
+  // `pool` into buffer `dst`.  Page ids come from the LDS window (uniform).
+  auto issue_half = [&](int t, const char* pool, uint4* dst) {
+    const int kt = k_lo + t * kKeyTile;
     const int nk = min(kKeyTile, k_hi - kt);
+    const int npg = (nk + 15) / 16;
+    const int32_t* pw = &pid_lds[(t / (kPidWindow / 4)) & 1][(t * 4) % kPidWindow];
+    int pid[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int slot = (i * 8 + wv) * 64 + lane;
-      const int key = slot >> 4;
-      const int ch = (slot & 15) ^ (key & 15);
-      const int kc = min(key, nk - 1);
-      const int64_t off = (static_cast<int64_t>(pid[kc >> 4]) * Hkv + kvh) * TILE + (kc & 15) * (D * 2) + ch * 16;
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(kbytes + off),
-                                       (LdsPtr)(&kw[(i * 8 + wv) * 64]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vbytes + off),
-                                       (LdsPtr)(&vw[(i * 8 + wv) * 64]), 16, 0, 0);
+    for (int j = 0; j < 4; ++j)
+      pid[j] = __builtin_amdgcn_readfirstlane(min(max(pw[min(j, npg - 1)], 0), num_pages - 1));
+    if (nk == kKeyTile) {
+      // Whole tile: DMA instruction i of this wave covers keys
+      // 4 (8 i + wave) .. +4, all in page 2 i + wave / 4; the page's tile
+      // base is scalar, the lane's row and chunk a fixed offset.
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int64_t tb = (static_cast<int64_t>(pid[2 * i + wv / 4]) * Hkv + kvh) * TILE;
+        dma16_sbase(pool + tb, dma_off[i], lds_offset(&dst[(i * 8 + wv) * 64]));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int sl = (i * 8 + wv) * 64 + lane;
+        const int key = sl >> 4;
+        const int ch = (sl & 15) ^ (key & 15);
+        const int kc = min(key, nk - 1);
+        const int64_t off = (static_cast<int64_t>(pid[kc >> 4]) * Hkv + kvh) * TILE + (kc & 15) * (D * 2) + ch * 16;
+        dma16(pool + off, lds_offset(&dst[(i * 8 + wv) * 64]));
+      }
     }
   };
   // Per-lane byte offsets of the transposed V reads inside a buffer: lane
   // (group lg, j) reads row key0 + j/4, columns d0 + 4(j%4) .. +3, with
-  // key0 = 4 lg (+16, +32, +48) and d0 = 16 db.
+  // key0 = 32 kh + 4 lg (+16) and d0 = 16 db.
   const int tr_r = col >> 2;
   const int tr_c = col & 3;
 
-  int pid[4];
-  tile_pids(k_lo, pid);
-  issue_tile(k_lo, pid, k_lds0, v_lds0);
-  // One tile: wait for its DMA, start the next tile's into the other
-  // buffers, compute.  Returns whether another tile follows.
-  auto tile = [&](int kt, const uint4* kb_lds, const uint4* vb_lds4, uint4* k_next, uint4* v_next) -> bool {
+  // Tile t's K and V into buffers kw, vw.
+  auto issue_tile = [&](int t, uint4* kw, uint4* vw) {
+    issue_half(t, kbytes, kw);
+    issue_half(t, vbytes, vw);
+  };
+
+  // The first page-id window, then tiles 0..2 in flight before the first
+  // is used.
+  issue_pids(0);
+  wait_vmcnt<0>();
+  lds_barrier();
+  if (nt > kPidWindow / 4) issue_pids(1);
+  issue_tile(0, k_lds0, v_lds0);
+  if (nt > 1) issue_tile(1, k_lds1, v_lds1);
+  if (nt > 2) issue_tile(2, k_lds2, v_lds2);
+
+  // One tile: wait for its DMA (each wave issued 4 loads per tile; tiles
+  // t+1 and t+2 may stay in flight), start tile t+3 into the buffer freed by
+  // tile t-1, compute.  Returns whether another tile follows.
+  auto tile = [&](int t, const uint4* kb_lds, const uint4* vb_lds4, uint4* k_next, uint4* v_next) -> bool {
+    const int kt = k_lo + t * kKeyTile;
     const int nk = min(kKeyTile, k_hi - kt);  // keys of this tile that exist
-    const bool more = kt + kKeyTile < k_hi;
-    if (more) tile_pids(kt + kKeyTile, pid);
-    // This tile's DMA (issued one tile ago) has landed for every wave, and
-    // every wave is done with the other buffers.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (more) issue_tile(kt + kKeyTile, pid, k_next, v_next);
+    const int ahead = min(2, nt - 1 - t);
+    if (ahead >= 2)
+      wait_vmcnt<8>();
+    else if (ahead == 1)
+      wait_vmcnt<4>();
+    else
+      wait_vmcnt<0>();
+    // Every wave's part of this tile has landed, and every wave is done
+    // with the buffer tile t-1 used.
+    lds_barrier();
+    if (t + 3 < nt) issue_tile(t + 3, k_next, v_next);
+    // Page-id window w + 1 into the buffer window w - 1 used: its last
+    // tile's DMA went out three tiles before window w began.  (Its loads,
+    // issued after this tile's, are waited for by the tile waits that
+    // follow, long before the first of its ids is read.)
+    if (t % (kPidWindow / 4) == 0 && t > 0 && (t / (kPidWindow / 4) + 1) * (kPidWindow / 4) < nt)
+      issue_pids(t / (kPidWindow / 4) + 1);
     const char* vb_lds = reinterpret_cast<const char*>(vb_lds4);
 
-    // S^T = K Q^T: s[kb][rb] holds keys 16 kb + 4 lg + i, query row 16 rb + col.
-    f32x4 s[4][2];
+    // S^T = K Q^T: s[kb][rb] holds keys 32 kh + 16 kb + 4 lg + i, query
+    // row 16 rb + col.
+    f32x4 s[2][2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int key = kb * 16 + col;
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = kh * 32 + kb * 16 + col;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) s[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -252,20 +357,20 @@ __global__ __launch_bounds__(512) void tile_kernel(
         for (int rb = 0; rb < 2; ++rb) s[kb][rb] = mfma16x16x32(a, qb[rb][c], s[kb][rb]);
       }
     }
-    // Online softmax per query row (column of S^T); the 64 keys of a row are
-    // spread over this lane's 16 values and the lanes l^16, l^32, l^48.
-    // Keys are masked (by select) only in tiles that need it: the last,
-    // partial tile of a split, and chunk tiles that cross the causal
-    // diagonal of this wave's rows.
-    const bool need_mask = nk < kKeyTile || (CHUNK && kt + kKeyTile - 1 > vis_lo);
+    // Online softmax per query row (column of S^T); the 32 keys of a row in
+    // this wave's half are spread over this lane's 8 values and the lanes
+    // l^16, l^32, l^48.  Keys are masked (by select) only in tiles that need
+    // it: the last, partial tile of a split, and chunk tiles that cross the
+    // causal diagonal of this wave's rows.
+    const bool need_mask = nk < kh * 32 + 32 || (CHUNK && kt + kh * 32 + 31 > vis_lo);
     if (need_mask) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int key = kb * 16 + lg * 4 + i;
+            const int key = kh * 32 + kb * 16 + lg * 4 + i;
             const bool ok = key < nk && (!CHUNK || kt + key <= vis[rb]);
             s[kb][rb][i] = ok ? s[kb][rb][i] : -INFINITY;
           }
@@ -275,93 +380,117 @@ __global__ __launch_bounds__(512) void tile_kernel(
     for (int rb = 0; rb < 2; ++rb) {
       float x = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) x = fmaxf(x, s[kb][rb][i]);
       mx[rb] = max_xor32(max_xor16(x)) * scale_log2;  // scale > 0 keeps the order
     }
     // Lazy rescaling: probabilities are taken against the running reference
-    // m, which moves (and o, l are rescaled) only when a row's maximum
-    // exceeds it by more than 2^8 -- so p <= 256, and the rescale, a wave-wide
-    // branch, is rare after the first tiles.
+    // m, which moves (and o, the row sums are rescaled) only when a row's
+    // maximum exceeds it by more than 2^8 -- so p <= 256, and the rescale, a
+    // wave-wide branch, is rare after the first tiles.
     if (__ballot(mx[0] > m[0] + 8.f || mx[1] > m[1] + 8.f) != 0ull) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         const float mn = fmaxf(m[rb], mx[rb]);
-        // m = -inf (nothing visible yet): o and l are 0, any factor will do
+        // m = -inf (nothing visible yet): o and the sums are 0, any factor will do
         const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m[rb] - mn);
         m[rb] = mn;
-        lsum[rb] *= alpha;
+        osum[rb] *= alpha;
 #pragma unroll
         for (int db = 0; db < 8; ++db) o[db][rb] *= alpha;
       }
     }
-    u32x4 pb[2][2];  // P^T operand: [rb][key half]
+    u32x4 pb[2];  // P^T operand per row block
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       // A row with no visible key so far keeps m = -inf: its p are all 0.
       const float nref = m[rb] == -INFINITY ? 0.f : -m[rb];
-      float ps = 0.f;
-      uint32_t pw[4][2];
+      uint32_t pw[2][2];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = 0; kb < 2; ++kb) {
         float p[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[i] = fast_exp2(fmaf(s[kb][rb][i], scale_log2, nref));
-          ps += p[i];
-        }
+        for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(s[kb][rb][i], scale_log2, nref));
         pw[kb][0] = bf16x2_rne(p[0], p[1]);
         pw[kb][1] = bf16x2_rne(p[2], p[3]);
       }
-      lsum[rb] += ps;
-      // k slots 8 lg .. 8 lg + 7 of key half hf = keys 32 hf + 4 lg + [0, 4)
-      // and 32 hf + 16 + 4 lg + [0, 4): the same order the V^T operand uses.
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-        pb[rb][hf] = u32x4{pw[2 * hf][0], pw[2 * hf][1], pw[2 * hf + 1][0], pw[2 * hf + 1][1]};
+      // k slots 8 lg .. 8 lg + 7 = keys 32 kh + 4 lg + [0, 4) and
+      // 32 kh + 16 + 4 lg + [0, 4): the same order the V^T operand uses.
+      pb[rb] = u32x4{pw[0][0], pw[0][1], pw[1][0], pw[1][1]};
     }
     // O^T += V^T P^T; the V^T operand (d = 16 db + col, keys as above) comes
-    // from two transposed reads of 4 keys each.
+    // from two transposed reads of 4 keys each; the row sums come from the
+    // all-ones operand.
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
+      u32x2 part[2];
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        u32x2 part[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int row = hf * 32 + e * 16 + lg * 4 + tr_r;
-          const int ch = (db * 2 + (tr_c >> 1)) ^ (row & 15);
-          part[e] = lds_read_tr16(vb_lds + row * (D * 2) + ch * 16 + (tr_c & 1) * 8);
-        }
-        const u32x4 a = u32x4{part[0].x, part[0].y, part[1].x, part[1].y};
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) o[db][rb] = mfma16x16x32(a, pb[rb][hf], o[db][rb]);
+      for (int e = 0; e < 2; ++e) {
+        const int row = kh * 32 + e * 16 + lg * 4 + tr_r;
+        const int ch = (db * 2 + (tr_c >> 1)) ^ (row & 15);
+        part[e] = lds_read_tr16(vb_lds + row * (D * 2) + ch * 16 + (tr_c & 1) * 8);
       }
+      const u32x4 a = u32x4{part[0].x, part[0].y, part[1].x, part[1].y};
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) o[db][rb] = mfma16x16x32(a, pb[rb], o[db][rb]);
     }
-    return more;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) osum[rb] = mfma16x16x32(ones, pb[rb], osum[rb]);
+    return t + 1 < nt;
   };
-  for (int kt = k_lo;; kt += 2 * kKeyTile) {
-    if (!tile(kt, k_lds0, v_lds0, k_lds1, v_lds1)) break;
-    if (!tile(kt + kKeyTile, k_lds1, v_lds1, k_lds0, v_lds0)) break;
+  for (int t = 0;; t += 4) {
+    if (!tile(t, k_lds0, v_lds0, k_lds3, v_lds3)) break;
+    if (!tile(t + 1, k_lds1, v_lds1, k_lds0, v_lds0)) break;
+    if (!tile(t + 2, k_lds2, v_lds2, k_lds1, v_lds1)) break;
+    if (!tile(t + 3, k_lds3, v_lds3, k_lds2, v_lds2)) break;
   }
 
-  // Partials: o / l per query row, log2-sum-exp.
+  // Merge the two key halves of each row group through LDS (the buffers are
+  // free once every wave is past its last tile): wave (rg, kh) hands its
+  // state for row block 1 - kh to its partner and merges the partner's state
+  // for row block kh into its own.  Record (rg, kh): o as [8 db][64 lanes]
+  // f32x4 in K buffer rg at 8 KB * kh; m and the row sum per lane in V
+  // buffer 0 at 128 floats * (2 rg + kh).
+  __syncthreads();
+  uint4* kbuf = rg == 0 ? k_lds0 : rg == 1 ? k_lds1 : rg == 2 ? k_lds2 : k_lds3;
+  float* xm = reinterpret_cast<float*>(v_lds0);
+  // (Row block selected by value, not by a run-time index, so that o stays
+  // in registers.)
+  {
+    f32x4* xo = reinterpret_cast<f32x4*>(kbuf) + kh * 512;
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const float lt = add_xor32(add_xor16(lsum[rb]));
-    const int r = row0 + rb * 16 + col;
-    if (r < n_rows) {
-      const int64_t pr = ((static_cast<int64_t>(part_base + r / G) * Hkv + kvh) * nks + ks) * G + r % G;
-      const bool any = lt > 0.f;
-      const float inv = any ? 1.0f / lt : 0.f;
+    for (int db = 0; db < 8; ++db) xo[db * 64 + lane] = kh ? o[db][0] : o[db][1];
+    xm[(2 * rg + kh) * 128 + lane] = kh ? m[0] : m[1];
+    xm[(2 * rg + kh) * 128 + 64 + lane] = kh ? osum[0][0] : osum[1][0];
+  }
+  __syncthreads();
+  const int rb = kh;
+  f32x4 om[8];
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const f32x4 v = o[db][rb] * inv;
-        *reinterpret_cast<f32x4*>(pre_o + pr * D + db * 16 + lg * 4) = v;
-      }
-      if (lg == 0) pre_lse[pr] = any ? m[rb] + fast_log2(lt) : -INFINITY;
+  for (int db = 0; db < 8; ++db) om[db] = kh ? o[db][1] : o[db][0];
+  const float mm = kh ? m[1] : m[0];
+  const float lm = kh ? osum[1][0] : osum[0][0];
+  const f32x4* po = reinterpret_cast<const f32x4*>(kbuf) + (1 - kh) * 512;
+  const float* pm = xm + (2 * rg + 1 - kh) * 128;
+  const float m2 = pm[lane];
+  const float l2 = pm[64 + lane];
+  const float mn = fmaxf(mm, m2);
+  // A half that saw no visible key keeps m = -inf and o = l = 0.
+  const float a1 = mm == -INFINITY ? 0.f : fast_exp2(mm - mn);
+  const float a2 = m2 == -INFINITY ? 0.f : fast_exp2(m2 - mn);
+  const float lt = lm * a1 + l2 * a2;
+  const int r = row0 + rb * 16 + col;
+  if (r < n_rows) {
+    const int64_t pr = ((static_cast<int64_t>(part_base + r / G) * Hkv + kvh) * nks + ks) * G + r % G;
+    const bool any = lt > 0.f;
+    const float inv = any ? 1.0f / lt : 0.f;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const f32x4 v = (om[db] * a1 + po[db * 64 + lane] * a2) * inv;
+      *reinterpret_cast<f32x4*>(pre_o + pr * D + db * 16 + lg * 4) = v;
     }
+    if (lg == 0) pre_lse[pr] = any ? mn + fast_log2(lt) : -INFINITY;
   }
 }
 
@@ -387,8 +516,8 @@ __global__ __launch_bounds__(64) void chunk_merge_kernel(uint16_t* __restrict__ 
   const int L = ctx[s];
   // The key splits tile_kernel wrote for this token's row chunk.
   const int n_rows = n_tok * G;
-  const int rc = (i * G) / kPrefixRows;
-  const int i_max = (min(n_rows, (rc + 1) * kPrefixRows) - 1) / G;
+  const int rc = (i * G) / kRows;
+  const int i_max = (min(n_rows, (rc + 1) * kRows) - 1) / G;
   const int k_end = min(L, L - n_tok + i_max + 1);
   const int nsp = min(nks, (k_end + kps - 1) / kps);
 #pragma unroll 1
@@ -495,11 +624,13 @@ int launch_cascade_g(const CascadeLaunch& c) {
   profile_before(a.stream);
   ChunkList none;
   none.n = 0;
-  hipLaunchKernelGGL((tile_kernel<G, false>), dim3(c.num_groups * c.row_chunks * c.nks, a.num_kv_heads), dim3(512), 0,
-                     st, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
-                     static_cast<const uint16_t*>(a.v_pool), a.block_tables, a.max_blocks, a.context_lens, nullptr,
-                     c.group_offsets, c.prefix_lens, none, a.num_seqs, c.row_chunks, c.nks, c.kps, a.num_kv_heads,
-                     static_cast<int>(a.num_pages), scale_log2, begin_pages, nullptr, pre_o, pre_lse);
+  const int n_items = c.num_groups * a.num_kv_heads * c.nks;
+  const unsigned blocks = static_cast<unsigned>((n_items + 7) / 8 * 8 * c.row_chunks);
+  hipLaunchKernelGGL((tile_kernel<G, false>), dim3(blocks), dim3(512), 0, st, static_cast<const uint16_t*>(a.q),
+                     static_cast<const uint16_t*>(a.k_pool), static_cast<const uint16_t*>(a.v_pool),
+                     a.block_tables, a.max_blocks, a.context_lens, nullptr, c.group_offsets, c.prefix_lens, none,
+                     a.num_seqs, c.row_chunks, c.nks, c.kps, a.num_kv_heads, n_items, static_cast<int>(a.num_pages),
+                     scale_log2, begin_pages, nullptr, pre_o, pre_lse);
   profile_after(a.stream);
   if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_prefix_cascade: prefix kernel launch failed");
   // Suffix: the stream decode kernel over the pages after each prefix.
@@ -550,12 +681,13 @@ int launch_mixed_g(const MixedLaunch& mx) {
     profile_before(a.stream);
     for (int b0 = 0; b0 < mx.num_chunks; b0 += kMaxChunkSegments) {
       const ChunkList cl = chunk_list(b0);
-      hipLaunchKernelGGL((tile_kernel<G, true>), dim3(cl.n * mx.row_chunks * mx.nks, a.num_kv_heads), dim3(512), 0,
-                         st, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
-                         static_cast<const uint16_t*>(a.v_pool), a.block_tables, a.max_blocks, a.context_lens,
-                         mx.cu_q_lens, nullptr, nullptr, cl, a.num_seqs, mx.row_chunks, mx.nks, mx.kps,
-                         a.num_kv_heads, static_cast<int>(a.num_pages), scale_log2, begin_pages, seq_info, pre_o,
-                         pre_lse);
+      const int n_items = cl.n * a.num_kv_heads * mx.nks;
+      const unsigned blocks = static_cast<unsigned>((n_items + 7) / 8 * 8 * mx.row_chunks);
+      hipLaunchKernelGGL((tile_kernel<G, true>), dim3(blocks), dim3(512), 0, st, static_cast<const uint16_t*>(a.q),
+                         static_cast<const uint16_t*>(a.k_pool), static_cast<const uint16_t*>(a.v_pool),
+                         a.block_tables, a.max_blocks, a.context_lens, mx.cu_q_lens, nullptr, nullptr, cl,
+                         a.num_seqs, mx.row_chunks, mx.nks, mx.kps, a.num_kv_heads, n_items,
+                         static_cast<int>(a.num_pages), scale_log2, begin_pages, seq_info, pre_o, pre_lse);
       if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_mixed_chunk: chunk kernel launch failed");
     }
     profile_after(a.stream);

@@ -85,3 +85,13 @@ def assert_close(lay: Layout, got, ref, what=""):
 
 def out_to_f64(t):
     return t.float().cpu().numpy().astype(np.float64)
+
+
+# Log-sum-exp bound where MFMA tiles attend (shared prefixes, prefill
+# chunks): their P.V contraction takes P rounded to bf16 on the bf16 MFMA,
+# and the normaliser is summed from the same rounded P (so the weights of
+# every output row sum to one).  Rounding to nearest even moves each p by at
+# most 2^-9 of itself, so the sum, and exp(lse), by at most 2^-9 relative:
+# lse within 2^-9 ~ 1.95e-3.  (The decode kernels sum the float32 p and
+# meet 1e-3.)
+LSE_TOL_MFMA_BF16 = 2.0e-3
