@@ -1,6 +1,7 @@
 // C-ABI entry points: argument validation and split planning on the host,
 // then the launch.  Nothing here touches device memory.
 #include <algorithm>
+#include <climits>
 #include <string>
 #include <vector>
 
@@ -235,10 +236,9 @@ extern "C" int pa_mixed_chunk(void* out, float* lse_out, const void* q, const vo
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
     return fail(PA_EINVAL, "pa_mixed_chunk: workspace not 256B aligned");
   if (cu_q_lens_host[0] != 0) return fail(PA_EINVAL, "pa_mixed_chunk: cu_q_lens[0] != 0");
-  std::vector<int32_t> chunk_seg, chunk_tok{0};
+  std::vector<int32_t> chunk_seg, chunk_tok{0}, chunk_n, chunk_keys;
   int64_t decode_pages = 0;
   int64_t max_rows = 0;
-  int64_t max_keys = 0;
   for (int32_t s = 0; s < num_segments; ++s) {
     const int64_t n = static_cast<int64_t>(cu_q_lens_host[s + 1]) - cu_q_lens_host[s];
     const int64_t L = context_lens_host[s];
@@ -252,8 +252,9 @@ extern "C" int pa_mixed_chunk(void* out, float* lse_out, const void* q, const vo
     } else {
       chunk_seg.push_back(s);
       chunk_tok.push_back(chunk_tok.back() + static_cast<int32_t>(n));
+      chunk_n.push_back(static_cast<int32_t>(n));
+      chunk_keys.push_back(static_cast<int32_t>(L));
       max_rows = std::max(max_rows, n * gqa_ratio);
-      max_keys = std::max(max_keys, L);
     }
   }
   if (decode_pages > (int64_t(1) << 31) - 1) return fail(PA_EUNSUPPORTED, "pa_mixed_chunk: too many pages");
@@ -261,21 +262,23 @@ extern "C" int pa_mixed_chunk(void* out, float* lse_out, const void* q, const vo
   if (num_chunks > 0 ? !mixed_supported(dtype, head_dim, gqa_ratio) : !decode_supported(dtype, head_dim, gqa_ratio))
     return fail(PA_EUNSUPPORTED, "pa_mixed_chunk: prefill chunks are built for bf16, head_dim 128, gqa_ratio "
                                  "1/2/4/8/16");
-  // Chunk plan: row blocks of kPrefixRowsPerBlock (token, q-head) rows;
-  // keys cut into at most kMaxChunkSplits splits of >= kMinChunkSplitKeys.
+  // Chunk plan: row blocks of kPrefixRowsPerBlock (token, q-head) rows,
+  // each chunk's keys cut into splits of about equal work per workgroup.
   const int32_t row_chunks =
       static_cast<int32_t>(std::max<int64_t>(1, (max_rows + kPrefixRowsPerBlock - 1) / kPrefixRowsPerBlock));
-  int32_t kps = kMinChunkSplitKeys;
-  int32_t nks = 1;
+  ChunkPlan plan;
   if (num_chunks > 0) {
-    kps = static_cast<int32_t>(std::max<int64_t>(kMinChunkSplitKeys, (max_keys + kMaxChunkSplits - 1) / kMaxChunkSplits));
-    kps = (kps + 63) / 64 * 64;
-    nks = static_cast<int32_t>((max_keys + kps - 1) / kps);
+    // (The CU count only shapes the splits, never the results; should the
+    // query fail, the launch below reports the device error.)
+    const int cus = device_cu_count();
+    plan = plan_chunks(chunk_n, chunk_keys, gqa_ratio, num_kv_heads, cus > 0 ? cus : 256);
+    if (plan.records > INT32_MAX) return fail(PA_EUNSUPPORTED, "pa_mixed_chunk: too many chunk tokens");
   }
   const int64_t waves = max_waves_per_head(decode_pages, num_kv_heads, 0);
   const size_t stream_bytes = partial_layout(waves, num_segments, num_kv_heads, gqa_ratio, head_dim).bytes;
-  const MixedLayout lay =
-      mixed_layout(num_segments, chunk_tok.back(), num_kv_heads, gqa_ratio, head_dim, nks, stream_bytes);
+  // (Partial records per kv-head: sum over chunks of tokens x splits.)
+  const MixedLayout lay = mixed_layout(num_segments, plan.records / num_kv_heads, num_kv_heads, gqa_ratio, head_dim,
+                                       1, stream_bytes);
   if (lay.bytes > workspace_bytes)
     return fail(PA_EWORKSPACE, "pa_mixed_chunk: workspace holds " + std::to_string(workspace_bytes) +
                                    " bytes, needs " + std::to_string(lay.bytes));
@@ -306,8 +309,7 @@ extern "C" int pa_mixed_chunk(void* out, float* lse_out, const void* q, const vo
   m.chunk_tok = chunk_tok.data();
   m.num_chunks = num_chunks;
   m.row_chunks = row_chunks;
-  m.nks = nks;
-  m.kps = kps;
+  m.plan = &plan;
   m.decode_pages = decode_pages;
   m.layout = lay;
   m.workspace = workspace;

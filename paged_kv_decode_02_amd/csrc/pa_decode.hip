@@ -662,6 +662,17 @@ thread_local ProfileRing g_prof;
 
 }  // namespace
 
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) return 0;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
 bool decode_supported(pa_dtype dtype, int32_t head_dim, int32_t gqa) {
   const bool g_ok = gqa == 1 || gqa == 2 || gqa == 4 || gqa == 8 || gqa == 16;
   if (!g_ok) return false;

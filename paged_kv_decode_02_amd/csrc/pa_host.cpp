@@ -2,6 +2,7 @@
 // and the block-table checker.  Plain C++ (no HIP), so it can also be built
 // with g++ and host sanitizers.
 #include <algorithm>
+#include <climits>
 #include <cstring>
 #include <string>
 #include <unordered_map>
@@ -62,6 +63,44 @@ MixedLayout mixed_layout(int64_t num_seqs, int64_t chunk_tokens, int32_t num_kv_
   l.stream_offset = l.pre_lse_offset + align_up(rows * nks * sizeof(float));
   l.bytes = l.stream_offset + align_up(static_cast<size_t>(stream_bytes));
   return l;
+}
+
+ChunkPlan plan_chunks(const std::vector<int32_t>& n_tok, const std::vector<int32_t>& keys, int32_t gqa,
+                      int32_t num_kv_heads, int32_t cus) {
+  const size_t n = n_tok.size();
+  // Tiles of 64 keys the chunks' row blocks stream in all: the last token
+  // of a row block bounds the keys it sees (causal inside the chunk).
+  int64_t total = 0;
+  for (size_t u = 0; u < n; ++u) {
+    const int64_t rows = static_cast<int64_t>(n_tok[u]) * gqa;
+    const int64_t L = keys[u];
+    for (int64_t r0 = 0; r0 < rows; r0 += kPrefixRowsPerBlock) {
+      const int64_t i_max = (std::min<int64_t>(rows, r0 + kPrefixRowsPerBlock) - 1) / gqa;
+      const int64_t k_end = std::min<int64_t>(L, L - n_tok[u] + i_max + 1);
+      total += (k_end + 63) / 64;
+    }
+  }
+  total *= num_kv_heads;
+  const int64_t slots = static_cast<int64_t>(std::max(cus, 1)) * kChunkWorkgroupsPerCU;
+  const int64_t per_wg = std::max<int64_t>(kMinChunkSplitKeys / 64, (total + slots - 1) / slots);
+  ChunkPlan p;
+  p.nks.resize(n);
+  p.kps.resize(n);
+  p.rec.resize(n);
+  p.tiles.resize(n);
+  for (size_t u = 0; u < n; ++u) {
+    const int64_t L = keys[u];
+    const int64_t kt = (L + 63) / 64;
+    int64_t nks = std::min<int64_t>(kMaxChunkSplits, std::max<int64_t>(1, (kt + per_wg - 1) / per_wg));
+    const int64_t kps = ((L + nks - 1) / nks + 63) / 64 * 64;
+    nks = (L + kps - 1) / kps;
+    p.nks[u] = static_cast<int32_t>(nks);
+    p.kps[u] = static_cast<int32_t>(kps);
+    p.tiles[u] = static_cast<int32_t>((std::min<int64_t>(kps, L) + 63) / 64);
+    p.rec[u] = static_cast<int32_t>(std::min<int64_t>(p.records, INT32_MAX));
+    p.records += static_cast<int64_t>(n_tok[u]) * num_kv_heads * nks;
+  }
+  return p;
 }
 
 }  // namespace pa

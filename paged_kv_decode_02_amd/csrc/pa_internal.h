@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <string>
+#include <vector>
 
 #include "pa.h"
 
@@ -80,12 +81,37 @@ int launch_stream(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_
                   bool merge, StreamPlan* plan);
 
 // Prefill chunks of a mixed batch, passed by value to the MFMA tile kernel.
+constexpr int32_t kMaxChunkSplits = 8;  // key splits of one chunk (sizes workspace)
+constexpr int32_t kMinChunkSplitKeys = 1024;
 constexpr int kMaxChunkSegments = 64;
 struct ChunkList {
   int32_t n;                                // chunk segments (q_len > 1)
   int32_t seg[kMaxChunkSegments];           // their segment indices
   int32_t tok_off[kMaxChunkSegments + 1];   // first chunk-token index of each
+  int32_t nks[kMaxChunkSegments];           // key splits of each
+  int32_t kps[kMaxChunkSegments];           // keys per split (a multiple of 64)
+  int32_t rec[kMaxChunkSegments];           // first partial record (token, kv-head, split) of each
+  int32_t ord[kMaxChunkSegments];           // launch order: ord[j] is the j-th chunk launched
+  int32_t item_end[kMaxChunkSegments];      // work items (kv-head, split) of launch-order chunks 0..j
 };
+
+// Key splits of the prefill chunks: each chunk's keys are cut into splits
+// so that one workgroup (a row block against one split) streams about
+// total tiles / (CUs * kChunkWorkgroupsPerCU) tiles of 64 keys, and no
+// fewer than kMinChunkSplitKeys keys; at most kMaxChunkSplits splits.
+#ifndef PA_CHUNK_WG_PER_CU
+#define PA_CHUNK_WG_PER_CU 2
+#endif
+constexpr int kChunkWorkgroupsPerCU = PA_CHUNK_WG_PER_CU;
+struct ChunkPlan {
+  std::vector<int32_t> nks, kps, rec;
+  std::vector<int32_t> tiles;  // tiles of 64 keys per work item (launch order: most first)
+  int64_t records = 0;         // partial records (token, kv-head, split) of all chunks
+};
+ChunkPlan plan_chunks(const std::vector<int32_t>& n_tok, const std::vector<int32_t>& keys, int32_t gqa,
+                      int32_t num_kv_heads, int32_t cus);
+// Compute units of the current device (0 if the query fails).
+int device_cu_count();
 
 // Shared-prefix (cascade) decode.
 struct CascadeLayout {
@@ -111,8 +137,6 @@ int launch_cascade(const CascadeLaunch& c);
 
 // Mixed batch: prefill chunks (q_len > 1, causal inside the chunk) and
 // decode tokens (q_len = 1) of many sequences in one call.
-constexpr int32_t kMaxChunkSplits = 8;  // key splits of one chunk row block (sizes workspace)
-constexpr int32_t kMinChunkSplitKeys = 1024;
 struct MixedLayout {
   size_t begin_offset, pre_o_offset, pre_lse_offset, stream_offset, bytes;
 };
@@ -125,8 +149,7 @@ struct MixedLaunch {
   const int32_t* chunk_tok;  // host [num_chunks+1]: first chunk-token index of each
   int32_t num_chunks;
   int32_t row_chunks;  // ceil(max chunk rows / kPrefixRowsPerBlock)
-  int32_t nks;         // key splits per chunk row block
-  int32_t kps;         // keys per split (multiple of 64)
+  const ChunkPlan* plan;  // key splits of each chunk
   int64_t decode_pages;
   MixedLayout layout;
   void* workspace;

@@ -158,24 +158,44 @@ __global__ __launch_bounds__(512) void tile_kernel(
   const int w = (slot / RC) * 8 + xcd;
   const int rc = slot % RC;
   if (w >= n_items) return;
-  const int ks = w % nks;
-  const int kvh = (w / nks) % Hkv;
-  const int u = w / (nks * Hkv);
-
-  int seg, n_rows, k_lo, k_hi, L = 0, n_tok = 1, q_base, part_base;
+  // Item w -> (unit u, kv-head, key split ks of nsplit, kpsplit keys each).
+  // Chunks: items are numbered chunk by chunk in launch order (the chunks
+  // with the longest splits first), each chunk's (kv-head, split) pairs
+  // together; prefix groups: (group, kv-head, split) in order.
+  int u, kvh, ks, nsplit, kpsplit;
   if constexpr (CHUNK) {
-    if (u >= chunks.n) return;
+    int j = 0;
+    while (chunks.item_end[j] <= w) ++j;  // w < n_items = item_end[n - 1]
+    u = chunks.ord[j];
+    const int local = w - (j > 0 ? chunks.item_end[j - 1] : 0);
+    nsplit = chunks.nks[u];
+    kpsplit = chunks.kps[u];
+    ks = local % nsplit;
+    kvh = local / nsplit;
+  } else {
+    nsplit = nks;
+    kpsplit = kps;
+    ks = w % nks;
+    kvh = (w / nks) % Hkv;
+    u = w / (nks * Hkv);
+  }
+
+  // rec_base: partial record (token or member, kv-head, split) of the
+  // unit's first row.
+  int seg, n_rows, k_lo, k_hi, L = 0, n_tok = 1, q_base;
+  int64_t rec_base;
+  if constexpr (CHUNK) {
     seg = chunks.seg[u];
     n_tok = cu_q[seg + 1] - cu_q[seg];
     L = ctx[seg];
     n_rows = n_tok * G;
     q_base = cu_q[seg];
-    part_base = chunks.tok_off[u];
+    rec_base = chunks.rec[u];
     const int r_end = min(n_rows, (rc + 1) * kRows);
     const int i_max = (r_end - 1) / G;
     const int k_end = min(L, L - n_tok + i_max + 1);
-    k_lo = ks * kps;
-    k_hi = min(k_end, k_lo + kps);
+    k_lo = ks * kpsplit;
+    k_hi = min(k_end, k_lo + kpsplit);
   } else {
     const int off0 = group_off[u];
     const int n_g = group_off[u + 1] - off0;
@@ -185,7 +205,7 @@ __global__ __launch_bounds__(512) void tile_kernel(
     seg = off0;
     n_rows = n_g * G;
     q_base = off0;
-    part_base = off0;
+    rec_base = static_cast<int64_t>(off0) * Hkv * nks;
     k_lo = ks * kps;
     k_hi = min(P, k_lo + kps);
   }
@@ -482,7 +502,7 @@ __global__ __launch_bounds__(512) void tile_kernel(
   const float lt = lm * a1 + l2 * a2;
   const int r = row0 + rb * 16 + col;
   if (r < n_rows) {
-    const int64_t pr = ((static_cast<int64_t>(part_base + r / G) * Hkv + kvh) * nks + ks) * G + r % G;
+    const int64_t pr = (rec_base + (static_cast<int64_t>(r / G) * Hkv + kvh) * nsplit + ks) * G + r % G;
     const bool any = lt > 0.f;
     const float inv = any ? 1.0f / lt : 0.f;
 #pragma unroll
@@ -500,7 +520,7 @@ template <int G>
 __global__ __launch_bounds__(64) void chunk_merge_kernel(uint16_t* __restrict__ out, float* __restrict__ lse_out,
                                                          const int32_t* __restrict__ ctx,
                                                          const int32_t* __restrict__ cu_q, ChunkList chunks, int Hkv,
-                                                         int nks, int kps, const float* __restrict__ pre_o,
+                                                         const float* __restrict__ pre_o,
                                                          const float* __restrict__ pre_lse) {
   constexpr int D = 128;
   const int lane = lane_id();
@@ -519,10 +539,12 @@ __global__ __launch_bounds__(64) void chunk_merge_kernel(uint16_t* __restrict__ 
   const int rc = (i * G) / kRows;
   const int i_max = (min(n_rows, (rc + 1) * kRows) - 1) / G;
   const int k_end = min(L, L - n_tok + i_max + 1);
+  const int nks = chunks.nks[u];
+  const int kps = chunks.kps[u];
   const int nsp = min(nks, (k_end + kps - 1) / kps);
 #pragma unroll 1
   for (int h = 0; h < G; ++h) {
-    const int64_t p0 = ((static_cast<int64_t>(ct) * Hkv + kvh) * nks) * G + h;
+    const int64_t p0 = (chunks.rec[u] + (static_cast<int64_t>(i) * Hkv + kvh) * nks) * G + h;
     float M = -INFINITY;
     for (int j = lane; j < nsp; j += 64) M = fmaxf(M, pre_lse[p0 + static_cast<int64_t>(j) * G]);
     M = wave_max(M);
@@ -667,26 +689,39 @@ int launch_mixed_g(const MixedLaunch& mx) {
   int32_t* seq_info = reinterpret_cast<int32_t*>(sws + partial_layout(1, a.num_seqs, a.num_kv_heads, a.gqa,
                                                                       a.head_dim).info_offset);
   const float scale_log2 = a.scale * kLog2e;
+  const ChunkPlan& plan = *mx.plan;
   auto chunk_list = [&](int b0) {
     ChunkList cl;
     cl.n = std::min(kMaxChunkSegments, mx.num_chunks - b0);
     for (int i = 0; i < cl.n; ++i) {
       cl.seg[i] = mx.chunk_seg[b0 + i];
       cl.tok_off[i] = mx.chunk_tok[b0 + i];
+      cl.nks[i] = plan.nks[b0 + i];
+      cl.kps[i] = plan.kps[b0 + i];
+      cl.rec[i] = plan.rec[b0 + i];
+      cl.ord[i] = i;
     }
     cl.tok_off[cl.n] = mx.chunk_tok[b0 + cl.n];
+    // Longest work items first, so that the short ones fill in at the end.
+    std::stable_sort(cl.ord, cl.ord + cl.n,
+                     [&](int x, int y) { return plan.tiles[b0 + x] > plan.tiles[b0 + y]; });
+    int items = 0;
+    for (int j = 0; j < cl.n; ++j) {
+      items += a.num_kv_heads * cl.nks[cl.ord[j]];
+      cl.item_end[j] = items;
+    }
     return cl;
   };
   if (mx.num_chunks > 0) {
     profile_before(a.stream);
     for (int b0 = 0; b0 < mx.num_chunks; b0 += kMaxChunkSegments) {
       const ChunkList cl = chunk_list(b0);
-      const int n_items = cl.n * a.num_kv_heads * mx.nks;
+      const int n_items = cl.item_end[cl.n - 1];
       const unsigned blocks = static_cast<unsigned>((n_items + 7) / 8 * 8 * mx.row_chunks);
       hipLaunchKernelGGL((tile_kernel<G, true>), dim3(blocks), dim3(512), 0, st, static_cast<const uint16_t*>(a.q),
                          static_cast<const uint16_t*>(a.k_pool), static_cast<const uint16_t*>(a.v_pool),
                          a.block_tables, a.max_blocks, a.context_lens, mx.cu_q_lens, nullptr, nullptr, cl,
-                         a.num_seqs, mx.row_chunks, mx.nks, mx.kps, a.num_kv_heads, n_items,
+                         a.num_seqs, mx.row_chunks, 0, 0, a.num_kv_heads, n_items,
                          static_cast<int>(a.num_pages), scale_log2, begin_pages, seq_info, pre_o, pre_lse);
       if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_mixed_chunk: chunk kernel launch failed");
     }
@@ -705,7 +740,7 @@ int launch_mixed_g(const MixedLaunch& mx) {
     const ChunkList cl = chunk_list(b0);
     hipLaunchKernelGGL((chunk_merge_kernel<G>), dim3(cl.tok_off[cl.n] - cl.tok_off[0], a.num_kv_heads), dim3(64), 0,
                        st, static_cast<uint16_t*>(a.out), a.lse_out, a.context_lens, mx.cu_q_lens, cl, a.num_kv_heads,
-                       mx.nks, mx.kps, pre_o, pre_lse);
+                       pre_o, pre_lse);
     if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_mixed_chunk: chunk merge launch failed");
   }
   return PA_OK;
