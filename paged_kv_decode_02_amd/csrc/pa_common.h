@@ -104,12 +104,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return add_xor32(add_xor16(v));
 }
 
-__device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
   const int lane = lane_id();
 #pragma unroll
@@ -181,23 +175,6 @@ __device__ __forceinline__ bool locate_item(const int32_t* __restrict__ ctx, con
     base += __shfl(inc2, 63, 64);
   }
   return false;
-}
-
-// First item index and split count of sequence s.
-__device__ __forceinline__ void sequence_items(const int32_t* __restrict__ ctx, const int32_t* __restrict__ begin_pages,
-                                               int S, int max_blocks, int C, int s, int& base, int& ns) {
-  const int lane = lane_id();
-  const int per = (S + 63) >> 6;
-  int tot = 0;
-#pragma unroll 8
-  for (int i = 0; i < per; ++i) {
-    const int s2 = lane * per + i;
-    const int sc = s2 < S ? s2 : S - 1;
-    const int n = nsplit_of(ctx[sc], begin_pages ? begin_pages[sc] : 0, max_blocks, C);
-    tot += s2 < s ? n : 0;
-  }
-  base = wave_sum_int(tot);
-  ns = nsplit_of(ctx[s], begin_pages ? begin_pages[s] : 0, max_blocks, C);
 }
 
 }  // namespace pa
