@@ -7,8 +7,8 @@ with it: the only code both sides use is the seeded input generator in
 ``workloads``.
 
 Pins (what fixes each function to something other than itself) are listed in
-``oracle/attention.py``'s header; every function is pinned, none is
-"parity unpinned".
+the headers of ``oracle/attention.py`` and ``oracle/kv_append.py``; every
+function is pinned, none is "parity unpinned".
 """
 
 from .attention import (  # noqa: F401
@@ -22,3 +22,4 @@ from .attention import (  # noqa: F401
     mixed_chunk,
     check_block_tables,
 )
+from .kv_append import kv_append  # noqa: F401
