@@ -192,6 +192,44 @@ int pa_mixed_chunk(void* out,                      /* device [T, Hq, D] dtype */
                    size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * KV append: write this step's new K/V rows into the paged cache, the step
+ * that runs before attention each decode or prefill step.  The block table
+ * names where a sequence's rows live, its blocks being handed out as the
+ * sequence grows (SwiftLLM page, section 3.1); the segments and lengths are
+ * those of pa_mixed_chunk (device + host copies, no defaults: TokenSpeed
+ * deep-dive section 8.2).
+ *
+ * Segment s adds n = cu_q_lens[s+1] - cu_q_lens[s] >= 0 tokens, rows
+ * cu_q_lens[s] .. cu_q_lens[s+1]-1 of k_new / v_new, and holds
+ * context_lens[s] >= n rows counting them.  Its new token i is row
+ * pos = context_lens[s] - n + i: for every kv-head g,
+ *   k_pool[block_tables[s][pos / block_size]][g][pos % block_size][:] =
+ *       k_new[cu_q_lens[s] + i][g][:]
+ * and the same for V; values are copied bit for bit, every other pool row
+ * is left as it is.  A table entry outside [0, num_pages) is not written
+ * through (device-side tables are not checked on this path; see
+ * pa_check_block_tables).  Segments must not map two tokens to one row.
+ * k_pool / v_pool are written in place; k_new / v_new are read only; the
+ * launch is asynchronous on `stream`; nothing is allocated.
+ * head_dim * element size must be a multiple of 16 bytes and at most 512;
+ * block_size 16; dtype PA_F32 or PA_BF16.
+ * Returns PA_OK (num_segments == 0 or no new token: no launch), PA_EINVAL
+ * (null pointer, non-positive sizes, cu_q_lens[0] != 0, n < 0,
+ * context_lens[s] < n or > max_blocks_per_seq * block_size),
+ * PA_EUNSUPPORTED (shape or dtype), PA_EHIP (launch).
+ * ------------------------------------------------------------------------- */
+int pa_kv_append(void* k_pool, void* v_pool,        /* device [NP, Hkv, BS, D] dtype, updated in place */
+                 const void* k_new, const void* v_new, /* device [T, Hkv, D] dtype */
+                 const int32_t* block_tables,       /* device [S, max_blocks_per_seq] */
+                 int32_t max_blocks_per_seq,
+                 const int32_t* cu_q_lens,          /* device [S+1] */
+                 const int32_t* cu_q_lens_host,     /* host [S+1], same values */
+                 const int32_t* context_lens,       /* device [S] */
+                 const int32_t* context_lens_host,  /* host [S], same values */
+                 int32_t num_segments, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                 int64_t num_pages, pa_dtype dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Host-side table check (host copies only, no device access).
  * Every sequence needs ceil(L/block_size) entries in [0, num_pages); a page
  * may appear in more than one table only as a declared shared prefix: for

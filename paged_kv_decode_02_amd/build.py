@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpa.so")
-SOURCES = ["pa_host.cpp", "pa_api.cpp", "pa_decode.hip", "pa_tiles.hip"]
+SOURCES = ["pa_host.cpp", "pa_api.cpp", "pa_decode.hip", "pa_tiles.hip", "pa_append.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -316,3 +316,53 @@ extern "C" int pa_mixed_chunk(void* out, float* lse_out, const void* q, const vo
   m.workspace_bytes = workspace_bytes;
   return launch_mixed(m);
 }
+
+extern "C" int pa_kv_append(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                            const int32_t* block_tables, int32_t max_blocks, const int32_t* cu_q_lens,
+                            const int32_t* cu_q_lens_host, const int32_t* context_lens,
+                            const int32_t* context_lens_host, int32_t num_segments, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int64_t num_pages, pa_dtype dtype, void* stream) {
+  clear_error();
+  if (num_segments < 0) return fail(PA_EINVAL, "pa_kv_append: num_segments < 0");
+  if (num_segments == 0) return PA_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !block_tables || !cu_q_lens || !cu_q_lens_host || !context_lens ||
+      !context_lens_host)
+    return fail(PA_EINVAL, "pa_kv_append: null pointer argument");
+  if (max_blocks < 1 || num_kv_heads < 1 || head_dim < 1 || num_pages < 1)
+    return fail(PA_EINVAL, "pa_kv_append: sizes must be >= 1");
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_EUNSUPPORTED, "pa_kv_append: unknown dtype");
+  if (block_size != kBlockSize) return fail(PA_EUNSUPPORTED, "pa_kv_append: only block_size 16 is built");
+  const int64_t row_bytes = static_cast<int64_t>(head_dim) * (dtype == PA_F32 ? 4 : 2);
+  if (row_bytes % 16 || row_bytes > kMaxAppendRowBytes)
+    return fail(PA_EUNSUPPORTED, "pa_kv_append: head_dim * element size must be a multiple of 16 bytes, at most " +
+                                     std::to_string(kMaxAppendRowBytes));
+  if (num_pages > (int64_t(1) << 31) - 1) return fail(PA_EUNSUPPORTED, "pa_kv_append: num_pages above 2^31-1");
+  if (cu_q_lens_host[0] != 0) return fail(PA_EINVAL, "pa_kv_append: cu_q_lens[0] != 0");
+  for (int32_t s = 0; s < num_segments; ++s) {
+    const int64_t n = static_cast<int64_t>(cu_q_lens_host[s + 1]) - cu_q_lens_host[s];
+    const int64_t L = context_lens_host[s];
+    const std::string at = "[" + std::to_string(s) + "]";
+    if (n < 0) return fail(PA_EINVAL, "pa_kv_append: cu_q_lens decreases at segment" + at);
+    if (L < n) return fail(PA_EINVAL, "pa_kv_append: context_lens" + at + " is shorter than its new tokens");
+    if (L > static_cast<int64_t>(max_blocks) * block_size)
+      return fail(PA_EINVAL, "pa_kv_append: context_lens" + at + " exceeds the block table");
+  }
+  const int64_t tokens = cu_q_lens_host[num_segments];
+  if (tokens == 0) return PA_OK;
+  AppendLaunch a;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.block_tables = block_tables;
+  a.max_blocks = max_blocks;
+  a.cu_q_lens = cu_q_lens;
+  a.context_lens = context_lens;
+  a.num_segments = num_segments;
+  a.num_tokens = tokens;
+  a.num_kv_heads = num_kv_heads;
+  a.row_bytes = static_cast<int32_t>(row_bytes);
+  a.num_pages = num_pages;
+  a.stream = stream;
+  return launch_append(a);
+}

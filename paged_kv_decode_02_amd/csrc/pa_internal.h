@@ -158,6 +158,26 @@ struct MixedLaunch {
 bool mixed_supported(pa_dtype dtype, int32_t head_dim, int32_t gqa);
 int launch_mixed(const MixedLaunch& m);
 
+// KV append.
+constexpr int64_t kMaxAppendRowBytes = 512;  // head_dim * element size
+struct AppendLaunch {
+  void* k_pool;
+  void* v_pool;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* block_tables;
+  int32_t max_blocks;
+  const int32_t* cu_q_lens;     // device [S+1]
+  const int32_t* context_lens;  // device [S]
+  int32_t num_segments;
+  int64_t num_tokens;
+  int32_t num_kv_heads;
+  int32_t row_bytes;  // head_dim * element size, a multiple of 16
+  int64_t num_pages;
+  void* stream;
+};
+int launch_append(const AppendLaunch& a);
+
 // Profiling hook: bracket the dominant kernel of a call.
 void profile_before(void* stream);
 void profile_after(void* stream);

@@ -34,6 +34,7 @@ EXPORTS = (
     "pa_prefix_cascade",
     "pa_mixed_chunk_workspace_size",
     "pa_mixed_chunk",
+    "pa_kv_append",
     "pa_check_block_tables",
     "pa_last_error",
     "pa_profile_enable",
@@ -79,6 +80,9 @@ def load(path: Optional[str] = None):
     lib.pa_mixed_chunk.restype = ctypes.c_int
     lib.pa_mixed_chunk.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32,
                                    c_i32, c_i32, c_i32, c_i64, ctypes.c_float, ctypes.c_int, c_vp, c_sz, c_vp]
+    lib.pa_kv_append.restype = ctypes.c_int
+    lib.pa_kv_append.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32,
+                                 c_i32, c_i64, ctypes.c_int, c_vp]
     lib.pa_check_block_tables.restype = ctypes.c_int
     lib.pa_check_block_tables.argtypes = [c_vp, c_i32, c_vp, c_i32, c_i32, c_i64, c_i32, c_vp, c_vp]
     lib.pa_last_error.restype = ctypes.c_char_p
@@ -269,6 +273,43 @@ def mixed_chunk(out, q, k_pool, v_pool, block_tables, cu_q_lens, cu_q_lens_host,
         _dev(context_lens, "context_lens", torch.int32), ch.ctypes.data,
         S, Hkv, Hq // Hkv, D, BS, NP, float(scale), _dtype_code(q),
         _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream_ptr(stream),
+    )
+    return _check(rc)
+
+
+def kv_append(k_pool, v_pool, k_new, v_new, block_tables, cu_q_lens, cu_q_lens_host, context_lens,
+              context_lens_host, stream=None):
+    """pa_kv_append on torch tensors: the new rows into the pools, in place.
+
+    k_pool, v_pool: [NP, Hkv, 16, D]; k_new, v_new: [T, Hkv, D] of the same
+    dtype (T = cu_q_lens[-1]); block_tables [S, MB] int32; cu_q_lens [S+1] /
+    context_lens [S] int32 on the device plus host twins with the same values.
+    """
+    import torch
+
+    NP, Hkv, BS, D = k_pool.shape
+    T = k_new.shape[0]
+    if tuple(v_pool.shape) != tuple(k_pool.shape) or v_pool.dtype != k_pool.dtype:
+        raise ValueError("k_pool and v_pool must match")
+    if tuple(k_new.shape) != (T, Hkv, D) or tuple(v_new.shape) != (T, Hkv, D):
+        raise ValueError("k_new and v_new must be [T, Hkv, D] with the pools' Hkv and D")
+    if k_new.dtype != k_pool.dtype or v_new.dtype != k_pool.dtype:
+        raise ValueError("new rows must have the pools' dtype")
+    cq = _host_i32(cu_q_lens_host, "cu_q_lens_host")
+    ch = _host_i32(context_lens_host, "context_lens_host")
+    S = ch.size
+    if cq.size != S + 1 or cu_q_lens.numel() != S + 1 or context_lens.numel() != S:
+        raise ValueError("cu_q_lens must have one entry more than context_lens")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must have one row per segment")
+    if S and int(cq[-1]) != T:
+        raise ValueError("k_new must have cu_q_lens[-1] rows")
+    rc = load().pa_kv_append(
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(cu_q_lens, "cu_q_lens", torch.int32), cq.ctypes.data,
+        _dev(context_lens, "context_lens", torch.int32), ch.ctypes.data,
+        S, Hkv, D, BS, NP, _dtype_code(k_pool), _stream_ptr(stream),
     )
     return _check(rc)
 

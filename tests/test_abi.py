@@ -187,3 +187,46 @@ def test_mixed_workspace_size_covers_chunk_partials():
     assert ws >= 2304 * 32 * 8 * 129 * 4  # every chunk row may need eight key splits
     assert ws >= pa.decode_workspace_size(260, 8, 4, 128, 80000, 0)
     assert pa.mixed_chunk_workspace_size(-1, 1, 8, 4, 128, 1) == 0
+
+
+def call_append(lib, **kw):
+    args = dict(k=FAKE, v=FAKE, kn=FAKE, vn=FAKE, bt=FAKE, mb=4, cu=FAKE, cu_host=None, ctx=FAKE, ctx_host=None,
+                S=2, Hkv=2, D=128, BS=16, NP=10, dtype=pa.PA_BF16, stream=None)
+    args.update(kw)
+    cu = args["cu_host"] if args["cu_host"] is not None else np.array([0, 5, 6], dtype=np.int32)
+    ch = args["ctx_host"] if args["ctx_host"] is not None else np.array([20, 40], dtype=np.int32)
+    return lib.pa_kv_append(args["k"], args["v"], args["kn"], args["vn"], args["bt"], args["mb"], args["cu"],
+                            cu.ctypes.data, args["ctx"], ch.ctypes.data, args["S"], args["Hkv"], args["D"],
+                            args["BS"], args["NP"], args["dtype"], args["stream"])
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(k=None), pa.PA_EINVAL),
+        (dict(vn=None), pa.PA_EINVAL),
+        (dict(cu=None), pa.PA_EINVAL),
+        (dict(cu_host=np.array([1, 5, 6], dtype=np.int32)), pa.PA_EINVAL),  # does not start at 0
+        (dict(cu_host=np.array([0, 5, 4], dtype=np.int32)), pa.PA_EINVAL),  # decreasing offsets
+        (dict(cu_host=np.array([0, 21, 22], dtype=np.int32)), pa.PA_EINVAL),  # more new tokens than rows
+        (dict(ctx_host=np.array([20, 65], dtype=np.int32)), pa.PA_EINVAL),  # 65 > 4 pages * 16
+        (dict(Hkv=0), pa.PA_EINVAL),
+        (dict(NP=0), pa.PA_EINVAL),
+        (dict(D=100), pa.PA_EUNSUPPORTED),  # 200-byte rows: not a multiple of 16 bytes
+        (dict(D=512), pa.PA_EUNSUPPORTED),  # 1 KB rows
+        (dict(dtype=7), pa.PA_EUNSUPPORTED),
+        (dict(BS=8), pa.PA_EUNSUPPORTED),
+        (dict(S=-1), pa.PA_EINVAL),
+    ],
+)
+def test_append_rejects_bad_arguments(kw, code):
+    lib = pa.load()
+    assert call_append(lib, **kw) == code
+    assert lib.pa_last_error().decode() != ""
+
+
+def test_append_with_nothing_to_write_is_a_no_op():
+    lib = pa.load()
+    assert call_append(lib, S=0, k=None, kn=None) == pa.PA_OK
+    # segments that add no token: validated, then no launch
+    assert call_append(lib, cu_host=np.array([0, 0, 0], dtype=np.int32)) == pa.PA_OK

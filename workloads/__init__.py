@@ -15,5 +15,7 @@ from .gen import (  # noqa: F401
     workload,
     values_numpy,
     values_torch,
+    new_rows_numpy,
+    new_rows_torch,
     pages_of,
 )

@@ -449,3 +449,30 @@ def values_torch(lay: Layout, device, seed: Optional[int] = None, chunk_pages: i
     for pool in pools:
         pool.masked_fill_(bad[:, None, :, None], float("nan"))
     return q, pools[0], pools[1]
+
+
+def new_rows_numpy(lay: Layout, seed: Optional[int] = None):
+    """This step's new K/V rows, ``[T, Hkv, D]`` each (T = sum of q_lens), on
+    the host, in the layout's stored form (float32, or bf16 bit patterns),
+    drawn N(0, value_std^2) from their own seeded streams."""
+    seed = lay.seed if seed is None else seed
+    shape = (lay.num_tokens, lay.num_kv_heads, lay.head_dim)
+    out = []
+    for i in range(2):
+        x = _rng(seed, 20 + i).standard_normal(size=shape, dtype=np.float32)
+        if lay.value_std != 1.0:
+            x *= np.float32(lay.value_std)
+        out.append(bf16_bits_from_f32(x) if lay.dtype == "bf16" else x)
+    return out[0], out[1]
+
+
+def new_rows_torch(lay: Layout, device, seed: Optional[int] = None):
+    """As :func:`new_rows_numpy`, drawn on ``device`` with torch's generator."""
+    import torch
+
+    seed = lay.seed if seed is None else seed
+    tdt = torch.float32 if lay.dtype == "f32" else torch.bfloat16
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed) * 1000003 + 29)
+    shape = (lay.num_tokens, lay.num_kv_heads, lay.head_dim)
+    return tuple((torch.randn(shape, generator=gen, device=device) * lay.value_std).to(tdt) for _ in range(2))
