@@ -42,8 +42,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+def build(verbose: bool = False, defines: tuple = (), out: str = LIB) -> str:
+    """Compile every source and link libpa.so at `out`; `defines` are extra
+    -D options (tuning constants such as PA_TAIL_PERMILLE=150)."""
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC] + [f"-D{d}" for d in defines]
     with tempfile.TemporaryDirectory(prefix="pa_build_") as tmp:
         objs = []
         for src in SOURCES:
@@ -67,8 +69,9 @@ def build(verbose: bool = False) -> str:
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"linking libpa.so failed:\n{r.stdout}{r.stderr}")
-        shutil.move(tmp_lib, LIB)
-    return LIB
+        os.makedirs(os.path.dirname(os.path.abspath(out)), exist_ok=True)
+        shutil.move(tmp_lib, out)
+    return out
 
 
 if __name__ == "__main__":
