@@ -7,7 +7,8 @@ with it: the only code both sides use is the seeded input generator in
 ``workloads``.
 
 Pins (what fixes each function to something other than itself) are listed in
-the headers of ``oracle/attention.py`` and ``oracle/kv_append.py``; every
+the headers of ``oracle/attention.py``, ``oracle/kv_append.py`` and
+``oracle/fp8.py``; every
 function is pinned, none is "parity unpinned".
 """
 
@@ -23,3 +24,4 @@ from .attention import (  # noqa: F401
     check_block_tables,
 )
 from .kv_append import kv_append  # noqa: F401
+from .fp8 import decode_fp8, dequantize, e4m3_to_f64, quantize_rows  # noqa: F401

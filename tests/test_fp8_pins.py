@@ -1,0 +1,274 @@
+"""Pins for the fp8 (e4m3fn) cache oracle: the code table and the quantiser
+against torch's own float8_e4m3fn conversion (a library routine) and closed
+forms; attention over an fp8 cache against the pinned bf16 attention oracle
+and against brute force.
+
+Each ``pin_*`` helper returns a list of failure strings, so the planted-
+mistake tests at the bottom can run every pin against a broken oracle and
+require that some pin notices.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import fp8 as f8
+from workloads import bf16_bits_from_f32, decode_layout
+
+# ---------------------------------------------------------------------------
+# helpers (test-owned)
+# ---------------------------------------------------------------------------
+
+
+def torch_code_values():
+    """float32 value of each of the 256 codes, by torch's float8_e4m3fn."""
+    return torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+
+
+def torch_quantize(x):
+    """The token-group recipe written with torch ops: float32 scale, divide,
+    clamp, float8_e4m3fn cast."""
+    t = torch.from_numpy(np.asarray(x, dtype=np.float32))
+    s = t.abs().amax(dim=-1).clamp_min(1e-10) / 448.0
+    codes = (t / s[..., None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, s.numpy()
+
+
+def finite_codes(rng, shape):
+    """Random e4m3fn codes avoiding the two NaN codes."""
+    c = rng.integers(0, 256, size=shape).astype(np.uint8)
+    nan = (c & 0x7F) == 0x7F
+    c[nan] = c[nan] ^ 0x01  # 0x7F -> 0x7E, 0xFF -> 0xFE
+    return c
+
+
+def fp8_cache(rng, ctx, hkv, d, block_size, pow2_scales):
+    """A paged fp8 cache: every table a random run of free pages, unused
+    pages and tail rows NaN (code 0x7F, scale NaN)."""
+    lay = decode_layout(ctx, num_q_heads=hkv * 2, num_kv_heads=hkv, head_dim=d, dtype="bf16",
+                        block_size=block_size, pool_factor=1.5, seed=int(rng.integers(1 << 30)))
+    npg = lay.num_pages
+    kc = np.full((npg, hkv, block_size, d), 0x7F, dtype=np.uint8)
+    vc = kc.copy()
+    ks = np.full((npg, hkv, block_size), np.nan, dtype=np.float32)
+    vs = ks.copy()
+    for s, L in enumerate(ctx):
+        for t in range(L):
+            p, r = lay.block_tables[s, t // block_size], t % block_size
+            kc[p, :, r] = finite_codes(rng, (hkv, d))
+            vc[p, :, r] = finite_codes(rng, (hkv, d))
+            if pow2_scales:
+                ks[p, :, r] = 2.0 ** rng.integers(-9, -3, size=hkv)
+                vs[p, :, r] = 2.0 ** rng.integers(-9, -3, size=hkv)
+            else:
+                ks[p, :, r] = rng.uniform(0.5, 2.0, size=hkv).astype(np.float32) / 256
+                vs[p, :, r] = rng.uniform(0.5, 2.0, size=hkv).astype(np.float32) / 256
+    q = bf16_bits_from_f32(rng.standard_normal((len(ctx), hkv * 2, d)).astype(np.float32))
+    return lay, q, kc, ks, vc, vs
+
+
+# ---------------------------------------------------------------------------
+# pins
+# ---------------------------------------------------------------------------
+
+
+def pin_code_table():
+    ref = torch_code_values()
+    got = f8.e4m3_to_f64(np.arange(256, dtype=np.uint8))
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    return [f"code {c:#04x}: {got[c]} vs torch {ref[c]}" for c in np.nonzero(~same)[0][:5]]
+
+
+def pin_closed_forms():
+    fails = []
+    v = f8.e4m3_to_f64
+    want = {0x38: 1.0, 0x40: 2.0, 0x7E: 448.0, 0xFE: -448.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9,
+            0x08: 2.0 ** -6, 0x30: 0.5, 0xB8: -1.0}
+    for c, x in want.items():
+        if v(np.uint8(c)) != x:
+            fails.append(f"code {c:#04x} is {v(np.uint8(c))}, want {x}")
+    if not (v(np.uint8(0)) == 0 and not np.signbit(v(np.uint8(0)))):
+        fails.append("0x00 is not +0")
+    if not (v(np.uint8(0x80)) == 0 and np.signbit(v(np.uint8(0x80)))):
+        fails.append("0x80 is not -0")
+    for c in (0x7F, 0xFF):
+        if not math.isnan(v(np.uint8(c))):
+            fails.append(f"code {c:#04x} is not NaN")
+    return fails
+
+
+def quantizer_rows():
+    rng = np.random.default_rng(7)
+    rows = [rng.standard_normal(128) * 0.5, rng.standard_normal(128) * 1e-3, rng.standard_normal(128) * 300,
+            np.zeros(128), rng.uniform(-1, 1, 128) ** 9]
+    ties = np.zeros(128)
+    ties[0] = 448.0  # scale exactly 1: x / scale = x
+    ties[1:8] = [1.0625, 1.1875, -1.0625, 2.0 ** -10, 3 * 2.0 ** -10, 104.0, 0.0]  # halfway cases
+    rows.append(ties)
+    return np.array(rows, dtype=np.float32)
+
+
+def pin_quantizer_vs_torch():
+    x = quantizer_rows()
+    codes, scales = f8.quantize_rows(x)
+    rc, rs = torch_quantize(x)
+    fails = []
+    if not np.array_equal(scales, rs):
+        fails.append("scales differ from torch's recipe")
+    bad = np.argwhere(codes != rc)
+    fails += [f"row {r} col {c}: code {codes[r, c]:#04x} vs torch {rc[r, c]:#04x}" for r, c in bad[:5]]
+    return fails
+
+
+def pin_quantizer_properties():
+    x = quantizer_rows()
+    codes, scales = f8.quantize_rows(x)
+    deq = f8.dequantize(codes, scales)
+    fails = []
+    for r in range(x.shape[0]):
+        amax = float(np.max(np.abs(x[r])))
+        if amax == 0:
+            if np.any(codes[r] & 0x7F):
+                fails.append(f"row {r}: zero row has nonzero codes")
+            if scales[r] != np.float32(np.float32(1e-10) / np.float32(448)):
+                fails.append(f"row {r}: zero-row scale {scales[r]}")
+            continue
+        j = int(np.argmax(np.abs(x[r])))
+        if abs(f8.e4m3_to_f64(codes[r, j])) != 448.0:
+            fails.append(f"row {r}: largest element does not map to +-448")
+        # round to nearest: the error is at most half a code step at that
+        # magnitude (step 2^(e-3) for normals, 2^-9 for subnormals), scaled
+        y = np.abs(x[r].astype(np.float64) / float(scales[r]))
+        e = np.floor(np.log2(np.maximum(y, 2.0 ** -6)))
+        step = 2.0 ** (e - 3)
+        # float32 division may round y itself: allow its half-ulp too
+        bound = (step / 2 + y * 2.0 ** -24) * float(scales[r])
+        if np.any(np.abs(deq[r] - x[r]) > bound * (1 + 1e-12)):
+            fails.append(f"row {r}: read-back error above half a code step")
+    neg_codes, _ = f8.quantize_rows(-x)
+    nz = (codes & 0x7F) != 0
+    if not np.array_equal(neg_codes[nz], codes[nz] ^ 0x80):
+        fails.append("quantising -x does not flip the sign bit")
+    return fails
+
+
+def pin_attention_vs_bf16_oracle():
+    """Power-of-two scales make every read-back value an exact bf16 value;
+    attention over the fp8 cache then equals the bf16 oracle over those
+    values, bit for bit (same float64 values, same arithmetic)."""
+    rng = np.random.default_rng(11)
+    ctx = [1, 15, 16, 17, 40]
+    lay, q, kc, ks, vc, vs = fp8_cache(rng, ctx, hkv=2, d=16, block_size=16, pow2_scales=True)
+    out, lse = f8.decode_fp8(q, kc, ks, vc, vs, lay.block_tables, lay.context_lens, 0.25, 2, 16)
+    kd = f8.dequantize(kc, ks)
+    vd = f8.dequantize(vc, vs)
+    kb = bf16_bits_from_f32(np.nan_to_num(kd).astype(np.float32))
+    vb = bf16_bits_from_f32(np.nan_to_num(vd).astype(np.float32))
+    fails = []
+    used = np.isfinite(kd)
+    if not np.array_equal(oracle.stored_to_f64(kb, "bf16")[used], kd[used]):
+        fails.append("power-of-two read-back values are not exact bf16 values")
+    ro, rl = oracle.decode(q, kb, vb, lay.block_tables, lay.context_lens, 0.25, 2, 16, "bf16")
+    if not (np.array_equal(out, ro) and np.array_equal(lse, rl)):
+        fails.append(f"fp8 attention differs from bf16 attention: {np.nanmax(np.abs(out - ro)):.3e}")
+    return fails
+
+
+def pin_bruteforce():
+    """Tiny inputs: codes read through torch's float8 conversion, dense K/V
+    assembled with Python loops, softmax with math.exp."""
+    rng = np.random.default_rng(5)
+    ctx = [3, 18, 33]
+    hkv, d, bs = 2, 8, 16
+    lay, q, kc, ks, vc, vs = fp8_cache(rng, ctx, hkv=hkv, d=d, block_size=bs, pow2_scales=False)
+    out, lse = f8.decode_fp8(q, kc, ks, vc, vs, lay.block_tables, lay.context_lens, 0.3, hkv, bs)
+    cv = torch_code_values()
+    qf = oracle.stored_to_f64(q, "bf16")
+    sc = float(np.float32(0.3))
+    fails = []
+    for s, L in enumerate(ctx):
+        for h in range(hkv * 2):
+            g = h // 2
+            xs, vrows = [], []
+            for t in range(L):
+                p, r = int(lay.block_tables[s, t // bs]), t % bs
+                k = [cv[kc[p, g, r, j]] * float(ks[p, g, r]) for j in range(d)]
+                vrows.append([cv[vc[p, g, r, j]] * float(vs[p, g, r]) for j in range(d)])
+                xs.append(sc * sum(qf[s, h, j] * k[j] for j in range(d)))
+            m = max(xs)
+            w = [math.exp(x - m) for x in xs]
+            z = sum(w)
+            o = [sum(w[t] * vrows[t][j] for t in range(L)) / z for j in range(d)]
+            if np.max(np.abs(np.array(o) - out[s, h])) > 1e-12 or abs(m + math.log(z) - lse[s, h]) > 1e-12:
+                fails.append(f"seq {s} head {h} differs from brute force")
+    return fails
+
+
+ALL_PINS = [pin_code_table, pin_closed_forms, pin_quantizer_vs_torch, pin_quantizer_properties,
+            pin_attention_vs_bf16_oracle, pin_bruteforce]
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
+def test_pin(pin):
+    fails = pin()
+    assert not fails, fails
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each must be caught by at least one pin
+# ---------------------------------------------------------------------------
+
+
+def _fnuz_table():
+    t = np.array([0.0] * 256)
+    for c in range(256):
+        e, m, sgn = (c >> 3) & 0xF, c & 7, -1.0 if c & 0x80 else 1.0
+        t[c] = sgn * (m / 8 * 2.0 ** -7 if e == 0 else (1 + m / 8) * 2.0 ** (e - 8))
+    t[0x80] = math.nan
+    return t
+
+
+def _ignore_scale(codes, scales):
+    return f8.e4m3_to_f64(codes) * np.where(np.isnan(np.asarray(scales, dtype=np.float64)), np.nan, 1.0)[..., None]
+
+
+def _round_ties_away(y):
+    y = np.asarray(y, dtype=np.float64)
+    codes = np.array([c for c in range(256) if not math.isnan(f8.E4M3_TABLE[c])])
+    vals = f8.E4M3_TABLE[codes]
+    flat = y.reshape(-1)
+    d = np.abs(vals[None, :] - flat[:, None])
+    cand = (d == d.min(axis=1, keepdims=True)) & (np.signbit(vals)[None, :] == np.signbit(flat)[:, None])
+    mag = np.where(cand, np.abs(vals)[None, :], -1.0)
+    return codes[np.argmax(mag, axis=1)].astype(np.uint8).reshape(y.shape)
+
+
+PLANTED = {
+    "fnuz_bias_8": ("E4M3_TABLE", _fnuz_table()),
+    "scale_ignored": ("dequantize", _ignore_scale),
+    "ties_away_from_zero": ("round_to_e4m3", _round_ties_away),
+}
+
+
+def _run_pins():
+    return [p.__name__ for p in ALL_PINS if p()]
+
+
+@pytest.mark.parametrize("name", sorted(PLANTED))
+def test_planted_mistake_is_caught(monkeypatch, name):
+    attr, bad = PLANTED[name]
+    monkeypatch.setattr(f8, attr, bad)
+    assert _run_pins(), f"no pin noticed {name}"
+
+
+def test_planted_v_scale_swap_is_caught(monkeypatch):
+    orig = f8.decode_fp8
+
+    def swapped(q, kc, ks, vc, vs, *a, **kw):
+        return orig(q, kc, ks, vc, ks, *a, **kw)
+
+    monkeypatch.setattr(f8, "decode_fp8", swapped)
+    assert _run_pins(), "no pin noticed the K scale used for V"
