@@ -87,7 +87,7 @@ def visible_pairs(lay, segs):
     return tot
 
 
-def cpu_baseline(lay, q, k, v, total_bytes, budget_s):
+def cpu_baseline(lay, q, k, v, total_bytes, budget_s, k_scales=None, v_scales=None):
     """Time the fp64 oracle, single-threaded, on whole segments of the same
     batch (random order) until about budget_s seconds of CPU work are spent,
     then scale to the whole batch by the (token, key) pairs attended and
@@ -101,7 +101,7 @@ def cpu_baseline(lay, q, k, v, total_bytes, budget_s):
     import oracle
 
     def host(t):
-        if lay.dtype == "bf16":
+        if t.dtype == torch.bfloat16:
             return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
         return t.float().cpu().numpy()
 
@@ -114,12 +114,19 @@ def cpu_baseline(lay, q, k, v, total_bytes, budget_s):
             s = int(order[len(done)])
             n = (int(lay.context_lens[s]) + 15) // 16
             idx = torch.from_numpy(lay.block_tables[s, :n].astype(np.int64)).to(k.device)
-            ks, vs = host(k.index_select(0, idx)), host(v.index_select(0, idx))
             qs = host(q[int(cu[s]) : int(cu[s + 1])])
             bt = np.arange(n, dtype=np.int32)[None, :]  # the gathered pages, relabelled 0..n-1
-            t0 = time.perf_counter()
-            oracle.paged_attention(qs, ks, vs, bt, lay.context_lens[s : s + 1], lay.q_lens[s : s + 1], lay.scale,
-                                   lay.num_kv_heads, 16, lay.dtype)
+            if k_scales is not None:
+                kc, vc = k.index_select(0, idx).cpu().numpy(), v.index_select(0, idx).cpu().numpy()
+                ksc, vsc = k_scales.index_select(0, idx).cpu().numpy(), v_scales.index_select(0, idx).cpu().numpy()
+                t0 = time.perf_counter()
+                oracle.decode_fp8(qs, kc, ksc, vc, vsc, bt, lay.context_lens[s : s + 1], lay.scale,
+                                  lay.num_kv_heads, 16, "bf16")
+            else:
+                ks, vs = host(k.index_select(0, idx)), host(v.index_select(0, idx))
+                t0 = time.perf_counter()
+                oracle.paged_attention(qs, ks, vs, bt, lay.context_lens[s : s + 1], lay.q_lens[s : s + 1],
+                                       lay.scale, lay.num_kv_heads, 16, lay.dtype)
             spent += time.perf_counter() - t0
             done.append(s)
     finally:
@@ -149,7 +156,7 @@ def main():
     import torch
 
     from paged_kv_decode_02_amd import pa, roofline
-    from workloads import values_torch, workload
+    from workloads import fp8_values_torch, values_torch, workload
 
     lay = workload(args.workload, seed=args.seed)
     cascade = lay.group_seq_offsets is not None
@@ -158,7 +165,11 @@ def main():
     torch.cuda.set_device(dev)
     print(f"[bench] workload {args.workload} seed {args.seed}: drawing inputs on the device", file=sys.stderr,
           flush=True)
-    q, k, v = values_torch(lay, dev)
+    fp8 = lay.kv_dtype == "fp8"
+    if fp8:
+        q, k, ks, v, vs = fp8_values_torch(lay, dev)
+    else:
+        q, k, v = values_torch(lay, dev)
     bt = torch.from_numpy(lay.block_tables).to(dev)
     ctx = torch.from_numpy(lay.context_lens).to(dev)
     out = torch.empty_like(q)
@@ -187,8 +198,12 @@ def main():
                                                   args.split_pages), dtype=torch.uint8, device=dev)
 
         def step():
-            pa.decode(out, q, k, v, bt, ctx, lay.context_lens, lay.scale, ws, split_pages=args.split_pages,
-                      stream=stream)
+            if fp8:
+                pa.decode_fp8(out, q, k, v, ks, vs, bt, ctx, lay.context_lens, lay.scale, ws,
+                              split_pages=args.split_pages, stream=stream)
+            else:
+                pa.decode(out, q, k, v, bt, ctx, lay.context_lens, lay.scale, ws, split_pages=args.split_pages,
+                          stream=stream)
 
     def timed(fn, n):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -260,6 +275,10 @@ def main():
         roof, other = (chunk_roof, dec_roof) if kern_avg[0] >= kern_avg[1] else (dec_roof, chunk_roof)
         extra = {"chunk_gflop": round(flops / 1e9, 3), "other_kernel_roofline": other,
                  "tokens_per_step": int(T)}
+    elif fp8:
+        nb = roofline.decode_fp8_bytes(lay.context_lens, lay.num_q_heads, lay.num_kv_heads, D)
+        roof = hbm_roof("stream_decode_kernel (fp8 pools)", nb["total"], kern_avg[0],
+                        measured_traffic(args.workload))
     else:
         nb = roofline.decode_bytes(lay.context_lens, lay.num_q_heads, lay.num_kv_heads, D, lay.elem_bytes)
         roof = hbm_roof("stream_decode_kernel", nb["total"], kern_avg[0], measured_traffic(args.workload))
@@ -275,7 +294,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": lay.dtype,
+        "dtype": "bf16 q/out, fp8 e4m3fn K/V" if fp8 else lay.dtype,
         "data": "synthetic",
         "config": {
             "workload": args.workload,
@@ -299,7 +318,8 @@ def main():
     result.update(extra)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(lay, q, k, v, nb["total"], args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(lay, q, k, v, nb["total"], args.cpu_seconds,
+                                              ks if fp8 else None, vs if fp8 else None)
     print(json.dumps(result), flush=True)
 
 

@@ -115,6 +115,36 @@ int pa_decode(void* out,                      /* device [S, Hq, D] dtype */
               void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Decode over an fp8 KV cache: pa_decode with K and V stored as OCP e4m3fn
+ * codes (one byte each: 4 exponent bits with bias 7, 3 mantissa bits,
+ * subnormals, NaN = 0x7f/0xff, largest finite value 448) and one float32
+ * scale per (page, kv-head, slot) for K and one for V.  A stored row reads
+ * back as code value * scale -- the token-group FP8 recipe of the tokenspeed
+ * 딥다이브 page (section 6-4), with a group = one kv-head's row of one
+ * token.  q and out are bf16; scores use the K scale of each row, P.V the
+ * V scale folded into the probability (rounded to bf16 for P.V, like the
+ * bf16 path); lse_out, split planning and the workspace (the same size as
+ * pa_decode_workspace_size gives) are as for pa_decode.
+ *
+ *  k_pool, v_pool   [NP, Hkv, 16, D] uint8 codes (device)
+ *  k_scales, v_scales [NP, Hkv, 16] float32 (device)
+ * Built for head_dim 128 and gqa_ratio 1, 2, 4, 8.  Errors as pa_decode;
+ * PA_EINVAL also for a NULL scale pointer.
+ * ------------------------------------------------------------------------- */
+int pa_decode_fp8(void* out,                  /* device [S, Hq, D] bf16 */
+                  float* lse_out,             /* device [S, Hq] or NULL */
+                  const void* q,              /* device [S, Hq, D] bf16 */
+                  const void* k_pool,         /* device [NP, Hkv, BS, D] e4m3fn codes */
+                  const void* v_pool,         /* device [NP, Hkv, BS, D] e4m3fn codes */
+                  const float* k_scales,      /* device [NP, Hkv, BS] */
+                  const float* v_scales,      /* device [NP, Hkv, BS] */
+                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                  const int32_t* context_lens, const int32_t* context_lens_host,
+                  int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_ratio, int32_t head_dim,
+                  int32_t block_size, int64_t num_pages, float scale, int32_t split_pages,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Shared-prefix (cascade) decode: one query token per sequence, sequences in
  * groups whose block tables start with the same prefix pages (shared blocks,
  * SwiftLLM page section 3.1); the result equals pa_decode on the same

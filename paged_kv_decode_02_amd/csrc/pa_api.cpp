@@ -39,39 +39,43 @@ extern "C" size_t pa_decode_workspace_size(int32_t max_num_seqs, int32_t num_kv_
   return partial_layout(waves, max_num_seqs, num_kv_heads, gqa_ratio, head_dim).bytes;
 }
 
-extern "C" int pa_decode(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,
-                         const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
-                         const int32_t* context_lens_host, int32_t num_seqs, int32_t num_kv_heads,
-                         int32_t gqa_ratio, int32_t head_dim, int32_t block_size, int64_t num_pages, float scale,
-                         pa_dtype dtype, int32_t split_pages, void* workspace, size_t workspace_bytes,
-                         void* stream) {
-  clear_error();
-  if (num_seqs < 0) return fail(PA_EINVAL, "pa_decode: num_seqs < 0");
+namespace {
+
+// pa_decode and pa_decode_fp8: validation, page count, workspace check, launch.
+int decode_call(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,
+                const float* k_scales, const float* v_scales, bool kv_fp8, const int32_t* block_tables,
+                int32_t max_blocks, const int32_t* context_lens, const int32_t* context_lens_host, int32_t num_seqs,
+                int32_t num_kv_heads, int32_t gqa_ratio, int32_t head_dim, int32_t block_size, int64_t num_pages,
+                float scale, pa_dtype dtype, int32_t split_pages, void* workspace, size_t workspace_bytes,
+                void* stream, const char* who) {
+  const std::string w(who);
+  if (num_seqs < 0) return fail(PA_EINVAL, w + ": num_seqs < 0");
   if (num_seqs == 0) return PA_OK;
   int rc = check_common(out, q, k_pool, v_pool, block_tables, max_blocks, context_lens, context_lens_host,
-                        num_kv_heads, gqa_ratio, head_dim, block_size, num_pages, scale, dtype, workspace,
-                        "pa_decode");
+                        num_kv_heads, gqa_ratio, head_dim, block_size, num_pages, scale, dtype, workspace, who);
   if (rc) return rc;
-  if (split_pages < 0) return fail(PA_EINVAL, "pa_decode: split_pages < 0");
-  if (!decode_supported(dtype, head_dim, gqa_ratio))
-    return fail(PA_EUNSUPPORTED, "pa_decode: no kernel for dtype/head_dim " + std::to_string(head_dim) +
-                                     "/gqa_ratio " + std::to_string(gqa_ratio));
-  if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return fail(PA_EINVAL, "pa_decode: workspace not 256B aligned");
+  if (kv_fp8 && (!k_scales || !v_scales)) return fail(PA_EINVAL, w + ": null scale pointer");
+  if (split_pages < 0) return fail(PA_EINVAL, w + ": split_pages < 0");
+  const bool built = kv_fp8 ? decode_fp8_supported(head_dim, gqa_ratio) : decode_supported(dtype, head_dim, gqa_ratio);
+  if (!built)
+    return fail(PA_EUNSUPPORTED, w + ": no kernel for head_dim " + std::to_string(head_dim) + "/gqa_ratio " +
+                                     std::to_string(gqa_ratio));
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return fail(PA_EINVAL, w + ": workspace not 256B aligned");
   int64_t total_pages = 0;
   for (int32_t s = 0; s < num_seqs; ++s) {
     const int64_t L = context_lens_host[s];
-    if (L < 1) return fail(PA_EINVAL, "pa_decode: context_lens[" + std::to_string(s) + "] < 1");
+    if (L < 1) return fail(PA_EINVAL, w + ": context_lens[" + std::to_string(s) + "] < 1");
     if (L > static_cast<int64_t>(max_blocks) * block_size)
-      return fail(PA_EINVAL, "pa_decode: context_lens[" + std::to_string(s) + "] exceeds the block table");
+      return fail(PA_EINVAL, w + ": context_lens[" + std::to_string(s) + "] exceeds the block table");
     total_pages += (L + block_size - 1) / block_size;
   }
-  if (total_pages > (int64_t(1) << 31) - 1) return fail(PA_EUNSUPPORTED, "pa_decode: more than 2^31-1 pages");
+  if (total_pages > (int64_t(1) << 31) - 1) return fail(PA_EUNSUPPORTED, w + ": more than 2^31-1 pages");
   // The workspace must hold the largest plan this batch could get, so that
   // a call never depends on the occupancy the device reports.
   const PartialLayout worst = partial_layout(max_waves_per_head(total_pages, num_kv_heads, split_pages), num_seqs,
                                              num_kv_heads, gqa_ratio, head_dim);
   if (worst.bytes > workspace_bytes)
-    return fail(PA_EWORKSPACE, "pa_decode: workspace holds " + std::to_string(workspace_bytes) + " bytes, needs " +
+    return fail(PA_EWORKSPACE, w + ": workspace holds " + std::to_string(workspace_bytes) + " bytes, needs " +
                                    std::to_string(worst.bytes));
   DecodeLaunch a;
   a.out = out;
@@ -94,7 +98,36 @@ extern "C" int pa_decode(void* out, float* lse_out, const void* q, const void* k
   a.workspace = workspace;
   a.workspace_bytes = workspace_bytes;
   a.stream = stream;
+  a.kv_fp8 = kv_fp8;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
   return launch_decode(a);
+}
+
+}  // namespace
+
+extern "C" int pa_decode(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                         const int32_t* context_lens_host, int32_t num_seqs, int32_t num_kv_heads,
+                         int32_t gqa_ratio, int32_t head_dim, int32_t block_size, int64_t num_pages, float scale,
+                         pa_dtype dtype, int32_t split_pages, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  clear_error();
+  return decode_call(out, lse_out, q, k_pool, v_pool, nullptr, nullptr, false, block_tables, max_blocks, context_lens,
+                     context_lens_host, num_seqs, num_kv_heads, gqa_ratio, head_dim, block_size, num_pages, scale,
+                     dtype, split_pages, workspace, workspace_bytes, stream, "pa_decode");
+}
+
+extern "C" int pa_decode_fp8(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,
+                             const float* k_scales, const float* v_scales, const int32_t* block_tables,
+                             int32_t max_blocks, const int32_t* context_lens, const int32_t* context_lens_host,
+                             int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_ratio, int32_t head_dim,
+                             int32_t block_size, int64_t num_pages, float scale, int32_t split_pages,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  return decode_call(out, lse_out, q, k_pool, v_pool, k_scales, v_scales, true, block_tables, max_blocks,
+                     context_lens, context_lens_host, num_seqs, num_kv_heads, gqa_ratio, head_dim, block_size,
+                     num_pages, scale, PA_BF16, split_pages, workspace, workspace_bytes, stream, "pa_decode_fp8");
 }
 
 extern "C" size_t pa_prefix_cascade_workspace_size(int32_t max_num_seqs, int32_t num_kv_heads, int32_t gqa_ratio,

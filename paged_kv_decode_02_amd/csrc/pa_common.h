@@ -28,6 +28,28 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// Two e4m3fn codes (bytes 0,1 of w, or bytes 2,3 if HI) -> a packed bf16
+// pair, first code in the low half: one v_cvt_scalef32_pk_bf16_fp8 with
+// scale 1.  Every e4m3fn value (subnormals, signed zero, NaN) is a bf16
+// value, so the conversion is exact.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+// 16 codes (a 16-byte chunk, element 0 in the low byte of x) -> 8 bf16
+// pairs in element order.
+template <typename U4>
+__device__ __forceinline__ void fp8x16_to_bf16x2(const U4& c, uint32_t (&o)[8]) {
+  o[0] = fp8x2_to_bf16x2<false>(c.x);
+  o[1] = fp8x2_to_bf16x2<true>(c.x);
+  o[2] = fp8x2_to_bf16x2<false>(c.y);
+  o[3] = fp8x2_to_bf16x2<true>(c.y);
+  o[4] = fp8x2_to_bf16x2<false>(c.z);
+  o[5] = fp8x2_to_bf16x2<true>(c.z);
+  o[6] = fp8x2_to_bf16x2<false>(c.w);
+  o[7] = fp8x2_to_bf16x2<true>(c.w);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -62,6 +62,12 @@ struct Geom {
   static constexpr int EPC = 16 / EB;         // elements per 16-byte chunk
   static_assert(RD == 32 || RD == 64, "row must be 128 or 256 bytes");
   static_assert(NI * RPI == 64, "a batch is 64 rows");
+  // XOR applied to the chunk index of row r in the K buffer, so that the
+  // transposed read (lane r takes row r) of the 16 lanes the 64-bank LDS
+  // serves at once touches 16 different 16-byte bank groups: rows of 256
+  // bytes use r mod 16; rows of 128 bytes pair up rows r, r+1 (they sit 8
+  // groups apart) and use (r / 2) mod 8.
+  static __device__ __forceinline__ int swz(int r) { return NCH == 16 ? (r & 15) : ((r >> 1) & 7); }
 };
 
 // One batch: rows [16*pb, 16*pb + 64) of sequence s, pages clamped to the
@@ -75,6 +81,7 @@ struct Batch {
   int seg_lo;  // first page of the sequence this wave covers
   int seg_hi;  // one past the last page this wave covers
   int cs;      // flattened index of the sequence's first page
+  int qb;      // q buffer holding the sequence's q rows
   int pid[4];  // physical pages (entries past seg_hi repeat the last one)
 };
 
@@ -142,25 +149,39 @@ __device__ __forceinline__ void lds_order() {
 __device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
 __device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 
-template <typename T, int D, int G>
+// T: q and out elements (uint16_t = bf16 bits, or float).  TKV: pool
+// elements, T itself or uint8_t for e4m3fn codes, whose rows come with one
+// float32 scale each in k_scales / v_scales ([page][kv-head][slot]).
+template <typename T, typename TKV, int D, int G>
 __global__ __launch_bounds__(64) void stream_decode_kernel(
-    T* __restrict__ out, float* __restrict__ lse_out, const T* __restrict__ q, const T* __restrict__ k_pool,
-    const T* __restrict__ v_pool, const int32_t* __restrict__ block_tables, const int32_t* __restrict__ ctx,
+    T* __restrict__ out, float* __restrict__ lse_out, const T* __restrict__ q, const TKV* __restrict__ k_pool,
+    const TKV* __restrict__ v_pool, const float* __restrict__ k_scales, const float* __restrict__ v_scales,
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ ctx,
     int max_blocks, int S, int Hkv, int num_pages, float scale_log2, int per, int total_pages,
     int32_t* __restrict__ seq_info, float* __restrict__ part_o, float* __restrict__ part_lse,
     const int32_t* __restrict__ begin_pages, float* __restrict__ seq_part, const int32_t* __restrict__ q_rows) {
-  using Gm = Geom<T, D>;
+  using Gm = Geom<TKV, D>;
   constexpr int RD = Gm::RD, NCH = Gm::NCH, TILE = Gm::TILE, NI = Gm::NI, RPI = Gm::RPI, EPC = Gm::EPC;
-  constexpr bool BF16 = sizeof(T) == 2;
+  constexpr bool FP8 = sizeof(TKV) == 1;
+  constexpr bool BF16 = sizeof(T) == 2;  // bf16 q/out; P.V on bf16 pairs (also for fp8 pools)
+  static_assert(!FP8 || BF16, "fp8 pools come with bf16 q and out");
+  constexpr int NK = NI + (FP8 ? 2 : 0);  // loads one issue_k makes (K rows, + the K and V scales)
+  constexpr int NV = NI;                  // loads one issue_v makes
+  constexpr int QNCH = D * sizeof(T) / 16;  // 16-byte chunks of one q row
+  constexpr int QPC = FP8 ? 2 : 1;          // q chunks per K chunk
   constexpr int per_tile = TILE / 1024;  // 1 KB loads per page tile
   constexpr int CG = (8 / G) < 1 ? 1 : ((8 / G) > 4 ? 4 : (8 / G));  // K chunks per QK step
   static_assert(NCH % CG == 0, "chunk groups must tile the row");
-  constexpr int QU4 = G * NCH;               // 16-byte chunks of the G q rows
+  static_assert(QNCH == NCH * QPC, "q chunks must line up with K chunks");
+  constexpr int QU4 = G * QNCH;              // 16-byte chunks of the G q rows
   constexpr int QPL = (QU4 + 63) / 64;        // of them per lane when loading
+  static_assert(NV + NK <= 63, "vmcnt counts at most 63 loads");
   __shared__ uint4 k_lds[64 * NCH];
   __shared__ uint4 v_lds[64 * NCH];
   __shared__ uint4 q_lds[2][QPL * 64];              // two sequences' q rows (current, next)
   __shared__ __align__(16) uint32_t p_lds[G * 64];  // fp32 bits, or bf16 in the first half
+  __shared__ float ks_lds[FP8 ? 64 : 1];            // fp8: scale of each K row of the batch
+  __shared__ float vs_lds[FP8 ? 64 : 1];            // fp8: scale of each V row of the batch
 
   const int lane = lane_id();
   const int grp = lane / NCH;  // V layout: row group of this lane
@@ -183,7 +204,7 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
   for (int r = 0; r < per_tile; ++r) {
     const int slot = r * 64 + lane;
     const int row = slot / NCH;
-    const int ch = (slot % NCH) ^ (row % NCH);
+    const int ch = (slot % NCH) ^ Gm::swz(row);
     koff[r] = row * (RD * 4) + ch * 16;
   }
   const uint32_t voff = grp * (RD * 4) + chk * 16;
@@ -198,27 +219,42 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
   const int s0 = __builtin_amdgcn_readfirstlane(loc.s);
   auto first_page = [&](int s, int P) { return begin_pages ? min(max(begin_pages[s], 0), P) : 0; };
 
-  Batch cur;
-  cur.s = s0;
-  cur.L = ctx[s0];
-  cur.P = pages_of_len(cur.L, max_blocks);
-  cur.B = first_page(s0, cur.P);
-  cur.cs = __builtin_amdgcn_readfirstlane(loc.base);
-  cur.seg_lo = cur.B + (run_a - cur.cs);
-  cur.seg_hi = min(cur.P, cur.B + (run_b - cur.cs));
-  cur.pb = cur.seg_lo;
-  load_pids(block_tables, max_blocks, num_pages, cur);
+  Batch first;
+  first.s = s0;
+  first.L = ctx[s0];
+  first.P = pages_of_len(first.L, max_blocks);
+  first.B = first_page(s0, first.P);
+  first.cs = __builtin_amdgcn_readfirstlane(loc.base);
+  first.seg_lo = first.B + (run_a - first.cs);
+  first.seg_hi = min(first.P, first.B + (run_b - first.cs));
+  first.pb = first.seg_lo;
+  first.qb = 0;
+  load_pids(block_tables, max_blocks, num_pages, first);
 
   // K and V of a batch go to LDS by DMA, NI loads of 1 KB each: K with the
   // swizzled layout above; V as it is in the pool (instruction i: rows
   // i*RPI .. +RPI, lane (grp, chk) = its row grp, chunk chk).
   const uint32_t k_base = lds_offset(k_lds);
   const uint32_t v_base = lds_offset(v_lds);
+  // fp8: lane r fetches the scale of batch row r (page r / 16, slot r % 16).
+  auto scale_src = [&](const float* pool, const Batch& b) {
+    // (values first: a conditional over the array elements themselves would
+    // load through a selected address and keep the batch in scratch memory)
+    const int p0 = b.pid[0], p1 = b.pid[1], p2 = b.pid[2], p3 = b.pid[3];
+    const int pl = lane < 32 ? (lane < 16 ? p0 : p1) : (lane < 48 ? p2 : p3);
+    return pool + (static_cast<int64_t>(pl) * Hkv + kvh) * 16 + (lane & 15);
+  };
   auto issue_k = [&](const Batch& b) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const char* tile = kbytes + (static_cast<int64_t>(b.pid[i / per_tile]) * Hkv + kvh) * TILE;
       dma16(tile + koff[i % per_tile], k_base + i * 1024);
+    }
+    // fp8: both scale runs of the batch travel with its K, so that they
+    // have landed when the batch's scores start.
+    if constexpr (FP8) {
+      dma4(scale_src(k_scales, b), lds_offset(ks_lds));
+      dma4(scale_src(v_scales, b), lds_offset(vs_lds));
     }
   };
   auto issue_v = [&](const Batch& b) {
@@ -255,53 +291,66 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
   };
   reset();
 
-  int qcur = 0;  // q buffer of sequence cur.s
-  load_q(cur.s, qcur);
+  // The batch after x (same sequence, or the next one holding pages of
+  // this run); false if the run ends with x.
+  auto advance = [&](const Batch& x, Batch& y) -> bool {
+    y = x;
+    if (x.pb + 4 < x.seg_hi) {
+      y.pb = x.pb + 4;
+    } else if (x.cs + (x.P - x.B) < run_b && x.s + 1 < S) {
+      y.s = x.s + 1;
+      y.cs = x.cs + (x.P - x.B);
+      y.L = ctx[y.s];
+      y.P = pages_of_len(y.L, max_blocks);
+      y.B = first_page(y.s, y.P);
+      // Sequences with nothing after begin_pages (the prefill chunks of a
+      // mixed batch) hold no pages of the walk: step over them.  Pages of
+      // this run remain, so a sequence that holds some follows.
+      while (y.B >= y.P && y.s + 1 < S) {
+        y.s += 1;
+        y.L = ctx[y.s];
+        y.P = pages_of_len(y.L, max_blocks);
+        y.B = first_page(y.s, y.P);
+      }
+      y.seg_lo = y.B;
+      y.seg_hi = min(y.P, y.B + (run_b - y.cs));
+      y.pb = y.B;
+      y.qb = x.qb ^ 1;
+      if (y.seg_hi <= y.seg_lo) return false;
+    } else {
+      return false;
+    }
+    load_pids(block_tables, max_blocks, num_pages, y);
+    return true;
+  };
+
+  // cur is the batch being computed, nxt the one after it, whose K and V
+  // are issued during cur's math (q of a new sequence is loaded right
+  // before the K of its first batch).
+  Batch cur = first, nxt;
+  load_q(cur.s, cur.qb);
   issue_k(cur);
   issue_v(cur);
 
   while (true) {
-    // Coordinates of the next batch (same sequence, or the next one).
-    Batch nxt = cur;
-    bool has_next = true;
-    if (cur.pb + 4 < cur.seg_hi) {
-      nxt.pb = cur.pb + 4;
-    } else if (cur.cs + (cur.P - cur.B) < run_b && cur.s + 1 < S) {
-      nxt.s = cur.s + 1;
-      nxt.cs = cur.cs + (cur.P - cur.B);
-      nxt.L = ctx[nxt.s];
-      nxt.P = pages_of_len(nxt.L, max_blocks);
-      nxt.B = first_page(nxt.s, nxt.P);
-      // Sequences with nothing after begin_pages (the prefill chunks of a
-      // mixed batch) hold no pages of the walk: step over them.  Pages of
-      // this run remain, so a sequence that holds some follows.
-      while (nxt.B >= nxt.P && nxt.s + 1 < S) {
-        nxt.s += 1;
-        nxt.L = ctx[nxt.s];
-        nxt.P = pages_of_len(nxt.L, max_blocks);
-        nxt.B = first_page(nxt.s, nxt.P);
-      }
-      nxt.seg_lo = nxt.B;
-      nxt.seg_hi = min(nxt.P, nxt.B + (run_b - nxt.cs));
-      nxt.pb = nxt.B;
-      has_next = nxt.seg_hi > nxt.seg_lo;
-    } else {
-      has_next = false;
-    }
-    if (has_next) load_pids(block_tables, max_blocks, num_pages, nxt);
+    const bool has_next = advance(cur, nxt);
 
-    // K of this batch (and q, loaded before it) is in LDS once only this
-    // batch's V (NI loads) may be outstanding.
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI) : "memory");
+    // K of this batch (and its scales, and q, loaded before it) is in LDS
+    // once only this batch's V may be outstanding.
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NV) : "memory");
     lds_order();
     // The next sequence's q goes to the other q buffer (last read two
     // sequences ago).
-    const bool next_seq = has_next && nxt.s != cur.s;
-    if (next_seq) load_q(nxt.s, qcur ^ 1);
+    if (has_next && nxt.s != cur.s) load_q(nxt.s, nxt.qb);
+    const int qcur = cur.qb;
 
     // Scores, lane = row: K row chunks and q chunks (one address for the
     // whole wave, a broadcast read) from LDS, CG chunks at a time.
     const int nvalid = min(cur.seg_hi * 16, cur.L) - cur.pb * 16;  // rows of this batch (1..64)
+    // fp8: this row's K and V scales, read before the next batch's K (and
+    // scales) may be issued into the same LDS.
+    const float k_row_scale = FP8 ? ks_lds[FP8 ? lane : 0] : 1.0f;
+    const float v_row_scale = FP8 ? vs_lds[FP8 ? lane : 0] : 1.0f;
     float sc[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) sc[h] = 0.f;
@@ -317,13 +366,37 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
       for (int h = 0; h < G; ++h) asm volatile("" : "+v"(qp), "+v"(kp) : "v"(sc[h]));
       u32x4 kr[CG];
 #pragma unroll
-      for (int c = 0; c < CG; ++c) kr[c] = kp[(c0 + c) ^ (lane % NCH)];
+      for (int c = 0; c < CG; ++c) kr[c] = kp[(c0 + c) ^ Gm::swz(lane)];
+      if constexpr (FP8) {
+        // 16 codes per chunk -> 8 bf16 pairs (exact), once for all G heads.
+        uint32_t kb[CG][8];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
+        for (int c = 0; c < CG; ++c) fp8x16_to_bf16x2(kr[c], kb[c]);
 #pragma unroll
-        for (int c = 0; c < CG; ++c) {
-          const u32x4 qv = qp[h * NCH + c0 + c];
-          sc[h] = dot_chunk<T>(make_uint4(kr[c].x, kr[c].y, kr[c].z, kr[c].w), qv.x, qv.y, qv.z, qv.w, sc[h]);
+        for (int h = 0; h < G; ++h) {
+#pragma unroll
+          for (int c = 0; c < CG; ++c) {
+            const u32x4 q0 = qp[h * QNCH + 2 * (c0 + c)];
+            const u32x4 q1 = qp[h * QNCH + 2 * (c0 + c) + 1];
+            float a = sc[h];
+            a = dot2_bf16(kb[c][0], q0.x, a);
+            a = dot2_bf16(kb[c][1], q0.y, a);
+            a = dot2_bf16(kb[c][2], q0.z, a);
+            a = dot2_bf16(kb[c][3], q0.w, a);
+            a = dot2_bf16(kb[c][4], q1.x, a);
+            a = dot2_bf16(kb[c][5], q1.y, a);
+            a = dot2_bf16(kb[c][6], q1.z, a);
+            sc[h] = dot2_bf16(kb[c][7], q1.w, a);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+#pragma unroll
+          for (int c = 0; c < CG; ++c) {
+            const u32x4 qv = qp[h * QNCH + c0 + c];
+            sc[h] = dot_chunk<T>(make_uint4(kr[c].x, kr[c].y, kr[c].z, kr[c].w), qv.x, qv.y, qv.z, qv.w, sc[h]);
+          }
         }
       }
       asm volatile("" ::: "memory");
@@ -334,15 +407,20 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
 
     // Online softmax; probabilities to LDS.
     const bool valid = lane < nvalid;
+    // fp8: the row's K scale multiplies its scores; its V scale is folded
+    // into the probability that P.V uses (the normaliser sums the plain
+    // probabilities).  Rows past the end select 0 / -inf, never multiply.
+    const float kscale = FP8 ? k_row_scale * scale_log2 : scale_log2;
+    const float vscale = v_row_scale;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float s2 = valid ? sc[h] * scale_log2 : -INFINITY;
+      const float s2 = valid ? sc[h] * kscale : -INFINITY;
       const float mn = fmaxf(m[h], wave_max(s2));
       const float alpha = fast_exp2(m[h] - mn);
       const float p = fast_exp2(s2 - mn);
       // The normaliser sums the float32 probabilities; for bf16 the P.V
       // product uses them rounded to bf16 (unbiased, round to nearest even).
-      const uint32_t pbits = BF16 ? bf16_bits_rne(p) : __float_as_uint(p);
+      const uint32_t pbits = BF16 ? bf16_bits_rne(FP8 ? (valid ? p * vscale : 0.f) : p) : __float_as_uint(p);
       l[h] = l[h] * alpha + p;
 #pragma unroll
       for (int e = 0; e < EPC; ++e) acc[h][e] *= alpha;
@@ -352,9 +430,10 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
       else
         p_lds[h * 64 + pslot] = pbits;
     }
-    // V of this batch: the next K (NI loads) may still be outstanding.
+    // V of this batch: the next K (NK loads, and before it the next q)
+    // may still be outstanding.
     if (has_next)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NK) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_order();
@@ -373,7 +452,36 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
     }
 
     // P.V: lane (grp, chk) accumulates its NI rows into its EPC columns.
-    if constexpr (BF16) {
+    if constexpr (FP8) {
+      // Rows (2u, 2u+1) of the group: their codes interleaved byte by byte
+      // and widened to bf16 pairs (row 2u low, row 2u+1 high), one pair per
+      // column, against the pair of their scaled probabilities.
+#pragma unroll
+      for (int i8 = 0; i8 < NI; i8 += 8) {
+        uint4 pp[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+          pp[h] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p_lds) + h * 64 + grp * NI + i8);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint4 va = vr[i8 + 2 * u], vb = vr[i8 + 2 * u + 1];
+          const uint32_t a4[4] = {va.x, va.y, va.z, va.w}, b4[4] = {vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+          for (int d4 = 0; d4 < 4; ++d4) {
+            const uint32_t x0 = __builtin_amdgcn_perm(b4[d4], a4[d4], 0x05010400u);  // a0 b0 a1 b1
+            const uint32_t x1 = __builtin_amdgcn_perm(b4[d4], a4[d4], 0x07030602u);  // a2 b2 a3 b3
+            const uint32_t vp[4] = {fp8x2_to_bf16x2<false>(x0), fp8x2_to_bf16x2<true>(x0),
+                                    fp8x2_to_bf16x2<false>(x1), fp8x2_to_bf16x2<true>(x1)};
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+              const uint32_t pw = u == 0 ? pp[h].x : u == 1 ? pp[h].y : u == 2 ? pp[h].z : pp[h].w;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[h][4 * d4 + e] = dot2_bf16(vp[e], pw, acc[h][4 * d4 + e]);
+            }
+          }
+        }
+      }
+    } else if constexpr (BF16) {
       // Probabilities of rows (2k, 2k+1) of the group against V pairs.
 #pragma unroll
       for (int i8 = 0; i8 < NI; i8 += 8) {
@@ -457,16 +565,23 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
         } else if (whole) {
           const int64_t row = qrow(s) * Hq + kvh * G + h;
           if (mine) {
-            if constexpr (EPC == 8) {
-              uint4 o;
-              o.x = bf16x2_rne(acc[h][0] * inv, acc[h][1] * inv);
-              o.y = bf16x2_rne(acc[h][2] * inv, acc[h][3] * inv);
-              o.z = bf16x2_rne(acc[h][4] * inv, acc[h][5] * inv);
-              o.w = bf16x2_rne(acc[h][6] * inv, acc[h][7] * inv);
-              reinterpret_cast<uint4*>(out)[row * NCH + chk] = o;
+            // columns chk*EPC .. +EPC of the output row
+            if constexpr (BF16) {
+#pragma unroll
+              for (int j = 0; j < EPC / 8; ++j) {
+                uint4 o;
+                o.x = bf16x2_rne(acc[h][8 * j + 0] * inv, acc[h][8 * j + 1] * inv);
+                o.y = bf16x2_rne(acc[h][8 * j + 2] * inv, acc[h][8 * j + 3] * inv);
+                o.z = bf16x2_rne(acc[h][8 * j + 4] * inv, acc[h][8 * j + 5] * inv);
+                o.w = bf16x2_rne(acc[h][8 * j + 6] * inv, acc[h][8 * j + 7] * inv);
+                reinterpret_cast<uint4*>(out)[(row * D + chk * EPC) / 8 + j] = o;
+              }
             } else {
-              reinterpret_cast<float4*>(out)[row * NCH + chk] =
-                  make_float4(acc[h][0] * inv, acc[h][1] * inv, acc[h][2] * inv, acc[h][3] * inv);
+#pragma unroll
+              for (int j = 0; j < EPC / 4; ++j)
+                reinterpret_cast<float4*>(out)[(row * D + chk * EPC) / 4 + j] =
+                    make_float4(acc[h][4 * j] * inv, acc[h][4 * j + 1] * inv, acc[h][4 * j + 2] * inv,
+                                acc[h][4 * j + 3] * inv);
             }
           }
           if (lse_out && lane == 0) lse_out[row] = lse2 * kLn2;
@@ -484,7 +599,6 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
       reset();
     }
     if (!has_next) break;
-    if (next_seq) qcur ^= 1;
     cur = nxt;
   }
 }
@@ -590,11 +704,11 @@ int resident_waves(KernelFn fn, std::atomic<int>* cache) {
   return v;
 }
 
-template <typename T, int D, int G>
+template <typename T, typename TKV, int D, int G>
 int launch_typed(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_part, const int32_t* q_rows, bool merge,
                  StreamPlan* plan) {
   static std::atomic<int> occ_cache[64];
-  auto kern = stream_decode_kernel<T, D, G>;
+  auto kern = stream_decode_kernel<T, TKV, D, G>;
   int64_t per = a.split_pages;
   if (per <= 0) {
     // Fill the GPU once: as many waves as can be resident, spread over the
@@ -623,8 +737,9 @@ int launch_typed(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_p
   const float scale_log2 = a.scale * kLog2e;
   if (a.timed) profile_before(a.stream);
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(W), a.num_kv_heads), dim3(64), 0, st, static_cast<T*>(a.out),
-                     a.lse_out, static_cast<const T*>(a.q), static_cast<const T*>(a.k_pool),
-                     static_cast<const T*>(a.v_pool), a.block_tables, a.context_lens, a.max_blocks, a.num_seqs,
+                     a.lse_out, static_cast<const T*>(a.q), static_cast<const TKV*>(a.k_pool),
+                     static_cast<const TKV*>(a.v_pool), a.k_scales, a.v_scales, a.block_tables, a.context_lens,
+                     a.max_blocks, a.num_seqs,
                      a.num_kv_heads, static_cast<int>(a.num_pages), scale_log2, static_cast<int>(per),
                      static_cast<int>(a.total_pages), seq_info, part_o, part_lse, begin_pages, seq_part, q_rows);
   if (a.timed) profile_after(a.stream);
@@ -640,15 +755,17 @@ int launch_typed(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_p
   return PA_OK;
 }
 
-template <typename T, int D>
+template <typename T, typename TKV, int D>
 int launch_g(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_part, const int32_t* q_rows, bool merge,
              StreamPlan* plan) {
   switch (a.gqa) {
-    case 1: return launch_typed<T, D, 1>(a, begin_pages, seq_part, q_rows, merge, plan);
-    case 2: return launch_typed<T, D, 2>(a, begin_pages, seq_part, q_rows, merge, plan);
-    case 4: return launch_typed<T, D, 4>(a, begin_pages, seq_part, q_rows, merge, plan);
-    case 8: return launch_typed<T, D, 8>(a, begin_pages, seq_part, q_rows, merge, plan);
-    case 16: return launch_typed<T, D, 16>(a, begin_pages, seq_part, q_rows, merge, plan);
+    case 1: return launch_typed<T, TKV, D, 1>(a, begin_pages, seq_part, q_rows, merge, plan);
+    case 2: return launch_typed<T, TKV, D, 2>(a, begin_pages, seq_part, q_rows, merge, plan);
+    case 4: return launch_typed<T, TKV, D, 4>(a, begin_pages, seq_part, q_rows, merge, plan);
+    case 8: return launch_typed<T, TKV, D, 8>(a, begin_pages, seq_part, q_rows, merge, plan);
+    case 16:
+      if constexpr (sizeof(TKV) > 1) return launch_typed<T, TKV, D, 16>(a, begin_pages, seq_part, q_rows, merge, plan);
+      break;
   }
   return fail(PA_EUNSUPPORTED, "pa_decode: gqa_ratio not built");
 }
@@ -673,6 +790,10 @@ int device_cu_count() {
   return v;
 }
 
+bool decode_fp8_supported(int32_t head_dim, int32_t gqa) {
+  return head_dim == 128 && (gqa == 1 || gqa == 2 || gqa == 4 || gqa == 8);
+}
+
 bool decode_supported(pa_dtype dtype, int32_t head_dim, int32_t gqa) {
   const bool g_ok = gqa == 1 || gqa == 2 || gqa == 4 || gqa == 8 || gqa == 16;
   if (!g_ok) return false;
@@ -683,11 +804,14 @@ bool decode_supported(pa_dtype dtype, int32_t head_dim, int32_t gqa) {
 
 int launch_stream(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_part, const int32_t* q_rows, bool merge,
                   StreamPlan* plan) {
-  if (a.dtype == PA_BF16) {
-    if (a.head_dim == 128) return launch_g<uint16_t, 128>(a, begin_pages, seq_part, q_rows, merge, plan);
-    if (a.head_dim == 64) return launch_g<uint16_t, 64>(a, begin_pages, seq_part, q_rows, merge, plan);
+  if (a.kv_fp8) {
+    if (a.dtype == PA_BF16 && a.head_dim == 128)
+      return launch_g<uint16_t, uint8_t, 128>(a, begin_pages, seq_part, q_rows, merge, plan);
+  } else if (a.dtype == PA_BF16) {
+    if (a.head_dim == 128) return launch_g<uint16_t, uint16_t, 128>(a, begin_pages, seq_part, q_rows, merge, plan);
+    if (a.head_dim == 64) return launch_g<uint16_t, uint16_t, 64>(a, begin_pages, seq_part, q_rows, merge, plan);
   } else if (a.dtype == PA_F32) {
-    if (a.head_dim == 64) return launch_g<float, 64>(a, begin_pages, seq_part, q_rows, merge, plan);
+    if (a.head_dim == 64) return launch_g<float, float, 64>(a, begin_pages, seq_part, q_rows, merge, plan);
   }
   return fail(PA_EUNSUPPORTED, "pa_decode: shape not built");
 }

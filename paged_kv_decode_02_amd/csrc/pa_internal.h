@@ -61,9 +61,15 @@ struct DecodeLaunch {
   size_t workspace_bytes;
   void* stream;
   bool timed = true;  // record profiling events around the stream kernel
+  // fp8 pools: e4m3fn codes with one float32 scale per (page, kv-head,
+  // slot); q and out are then bf16 (dtype == PA_BF16)
+  bool kv_fp8 = false;
+  const float* k_scales = nullptr;
+  const float* v_scales = nullptr;
 };
 
 bool decode_supported(pa_dtype dtype, int32_t head_dim, int32_t gqa);
+bool decode_fp8_supported(int32_t head_dim, int32_t gqa);
 int launch_decode(const DecodeLaunch& a);
 
 // The stream kernel alone (plus, if `merge`, its merge kernel).  With

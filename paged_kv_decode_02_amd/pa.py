@@ -30,6 +30,7 @@ PA_EHIP = -4
 EXPORTS = (
     "pa_decode_workspace_size",
     "pa_decode",
+    "pa_decode_fp8",
     "pa_prefix_cascade_workspace_size",
     "pa_prefix_cascade",
     "pa_mixed_chunk_workspace_size",
@@ -69,6 +70,9 @@ def load(path: Optional[str] = None):
     lib.pa_decode.restype = ctypes.c_int
     lib.pa_decode.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                               c_i32, c_i64, ctypes.c_float, ctypes.c_int, c_i32, c_vp, c_sz, c_vp]
+    lib.pa_decode_fp8.restype = ctypes.c_int
+    lib.pa_decode_fp8.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32,
+                                  c_i32, c_i32, c_i32, c_i64, ctypes.c_float, c_i32, c_vp, c_sz, c_vp]
     lib.pa_prefix_cascade_workspace_size.restype = c_sz
     lib.pa_prefix_cascade_workspace_size.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i64]
     lib.pa_prefix_cascade.restype = ctypes.c_int
@@ -141,6 +145,53 @@ def _stream_ptr(stream):
 def decode_workspace_size(max_num_seqs, num_kv_heads, gqa_ratio, head_dim, max_total_pages, split_pages=0) -> int:
     return int(load().pa_decode_workspace_size(max_num_seqs, num_kv_heads, gqa_ratio, head_dim, max_total_pages,
                                                split_pages))
+
+
+def decode_fp8(out, q, k_pool, v_pool, k_scales, v_scales, block_tables, context_lens, context_lens_host, scale,
+               workspace, lse_out=None, split_pages=0, stream=None):
+    """pa_decode_fp8 on torch tensors.
+
+    q, out: [S, Hq, D] bfloat16; k_pool, v_pool: [NP, Hkv, 16, D] uint8
+    e4m3fn codes (or torch.float8_e4m3fn); k_scales, v_scales: [NP, Hkv, 16]
+    float32; the rest as :func:`decode`.
+    """
+    import torch
+
+    S, Hq, D = q.shape
+    NP, Hkv, BS, D2 = k_pool.shape
+    if q.dtype != torch.bfloat16 or tuple(out.shape) != (S, Hq, D) or out.dtype != torch.bfloat16:
+        raise ValueError("q and out must be bfloat16 [S, Hq, D]")
+    codes = (torch.uint8, torch.float8_e4m3fn)
+    if tuple(v_pool.shape) != tuple(k_pool.shape) or k_pool.dtype not in codes or v_pool.dtype not in codes:
+        raise ValueError("k_pool and v_pool must be [NP, Hkv, BS, D] uint8 / float8_e4m3fn")
+    for t, nm in ((k_scales, "k_scales"), (v_scales, "v_scales")):
+        if tuple(t.shape) != (NP, Hkv, BS) or t.dtype != torch.float32:
+            raise ValueError(f"{nm} must be float32 [NP, Hkv, BS]")
+    if D2 != D or Hq % Hkv:
+        raise ValueError("head_dim mismatch or q heads not a multiple of kv heads")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_tables / context_lens must have one row per sequence")
+    ch = _host_i32(context_lens_host, "context_lens_host")
+    if ch.size != S:
+        raise ValueError("context_lens_host must have one entry per sequence")
+    if lse_out is not None and tuple(lse_out.shape) != (S, Hq):
+        raise ValueError("lse_out must be [S, Hq]")
+    rc = load().pa_decode_fp8(
+        _dev(out, "out"),
+        _dev(lse_out, "lse_out", torch.float32) if lse_out is not None else None,
+        _dev(q, "q"),
+        _dev(k_pool, "k_pool"),
+        _dev(v_pool, "v_pool"),
+        _dev(k_scales, "k_scales", torch.float32),
+        _dev(v_scales, "v_scales", torch.float32),
+        _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32),
+        ch.ctypes.data,
+        S, Hkv, Hq // Hkv, D, BS, NP, float(scale), int(split_pages),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream_ptr(stream),
+    )
+    return _check(rc)
 
 
 def decode(out, q, k_pool, v_pool, block_tables, context_lens, context_lens_host, scale, workspace,

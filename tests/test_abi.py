@@ -95,6 +95,45 @@ def test_zero_sequences_is_a_no_op():
     assert call_decode(lib, S=0, q=None, out=None) == pa.PA_OK
 
 
+def call_decode_fp8(lib, **kw):
+    args = dict(out=FAKE, lse=None, q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, bt=FAKE, mb=4, ctx=FAKE, ctx_host=None,
+                S=2, Hkv=2, G=4, D=128, BS=16, NP=10, scale=0.1, split=0, ws=ctypes.c_void_p(0x100000),
+                ws_bytes=1 << 20, stream=None)
+    args.update(kw)
+    ch = args["ctx_host"]
+    if ch is None:
+        ch = np.array([20, 40], dtype=np.int32)
+    return lib.pa_decode_fp8(args["out"], args["lse"], args["q"], args["k"], args["v"], args["ks"], args["vs"],
+                             args["bt"], args["mb"], args["ctx"], ch.ctypes.data, args["S"], args["Hkv"], args["G"],
+                             args["D"], args["BS"], args["NP"], args["scale"], args["split"], args["ws"],
+                             args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(ks=None), pa.PA_EINVAL),
+        (dict(vs=None), pa.PA_EINVAL),
+        (dict(k=None), pa.PA_EINVAL),
+        (dict(scale=float("nan")), pa.PA_EINVAL),
+        (dict(D=64), pa.PA_EUNSUPPORTED),
+        (dict(G=16), pa.PA_EUNSUPPORTED),
+        (dict(BS=8), pa.PA_EUNSUPPORTED),
+        (dict(ctx_host=np.array([0, 40], dtype=np.int32)), pa.PA_EINVAL),
+        (dict(ws_bytes=64, split=1), pa.PA_EWORKSPACE),
+    ],
+)
+def test_decode_fp8_rejects_bad_arguments(kw, code):
+    lib = pa.load()
+    assert call_decode_fp8(lib, **kw) == code
+    assert lib.pa_last_error().decode().startswith("pa_decode_fp8")
+
+
+def test_decode_fp8_zero_sequences_is_a_no_op():
+    lib = pa.load()
+    assert call_decode_fp8(lib, S=0, q=None, out=None, ks=None) == pa.PA_OK
+
+
 def test_workspace_size_covers_plans():
     for S, P in [(1, 1), (64, 9216), (256, 90000), (1024, 20000)]:
         for G in [1, 4, 8]:

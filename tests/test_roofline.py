@@ -55,3 +55,11 @@ def test_mixed_accounting_on_the_chunked_piggyback_workload():
     assert b["kv"] == 2 * 8 * 128 * 2 * int(lay.context_lens.sum())
     assert b["decode_kv"] == 2 * 8 * 128 * 2 * int(lay.context_lens[4:].sum())
     assert b["q_out"] == 2 * 2304 * 32 * 128 * 2
+
+
+def test_fp8_decode_bytes():
+    b = roofline.decode_fp8_bytes([4096], num_q_heads=32, num_kv_heads=8, head_dim=128)
+    bf = roofline.decode_bytes([4096], num_q_heads=32, num_kv_heads=8, head_dim=128, elem_bytes=2)
+    assert 2 * b["kv"] == bf["kv"]  # one byte per element instead of two
+    assert b["scales"] == 2 * 8 * 4096 * 4  # a float32 scale per K row and per V row
+    assert b["q_out"] == bf["q_out"] and b["tables"] == bf["tables"]

@@ -18,4 +18,6 @@ from .gen import (  # noqa: F401
     new_rows_numpy,
     new_rows_torch,
     pages_of,
+    fp8_values_numpy,
+    fp8_values_torch,
 )

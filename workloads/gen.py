@@ -74,6 +74,9 @@ class Layout:
     # cascade groups (contiguous sequence ranges sharing a prefix)
     group_seq_offsets: Optional[np.ndarray] = None  # int32 [NG+1]
     prefix_lens: Optional[np.ndarray] = None  # int32 [NG]
+    # storage of the K/V pools: None = same as dtype; "fp8" = e4m3fn codes
+    # with one float32 scale per (page, kv-head, slot), q and out in dtype
+    kv_dtype: Optional[str] = None
 
     @property
     def num_seqs(self) -> int:
@@ -362,9 +365,17 @@ def _chunked_piggyback(seed=0):
     )
 
 
+def _llama8b_decode_fp8(seed=0):
+    lay = _llama8b_decode(seed)
+    lay.name = "llama8b_decode_fp8"
+    lay.kv_dtype = "fp8"
+    return lay
+
+
 WORKLOADS = {
     "tiny_f32": _tiny_f32,
     "llama8b_decode": _llama8b_decode,
+    "llama8b_decode_fp8": _llama8b_decode_fp8,
     "longtail_splitkv": _longtail_splitkv,
     "shared_prefix": _shared_prefix,
     "chunked_piggyback": _chunked_piggyback,
@@ -476,3 +487,55 @@ def new_rows_torch(lay: Layout, device, seed: Optional[int] = None):
     gen.manual_seed(int(seed) * 1000003 + 29)
     shape = (lay.num_tokens, lay.num_kv_heads, lay.head_dim)
     return tuple((torch.randn(shape, generator=gen, device=device) * lay.value_std).to(tdt) for _ in range(2))
+
+
+# ----------------------------------------------------------------------------
+# fp8 (e4m3fn) pools.
+# ----------------------------------------------------------------------------
+
+FP8_CODE_STD = 128.0  # spread of the stored codes before the cast (|code| <= 448)
+FP8_NAN_CODE = np.uint8(0x7F)
+
+
+def fp8_values_torch(lay: Layout, device, seed: Optional[int] = None, chunk_pages: int = 4096):
+    """q (bf16) and fp8 K/V pools drawn on ``device``.
+
+    Codes: N(0, 1) * FP8_CODE_STD clamped to +-448 and cast to
+    ``float8_e4m3fn`` by torch (the cast only turns the draw into valid
+    codes); scales: value_std / FP8_CODE_STD * U[0.8, 1.2] per (page,
+    kv-head, slot), float32, so read-back rows spread like the bf16
+    workloads' N(0, value_std^2) values.  Unused pages and the tail rows of
+    each last page hold the NaN code 0x7F and a NaN scale.  Returns q [T, Hq,
+    D] bf16, k_codes, v_codes uint8 [NP, Hkv, BS, D], k_scales, v_scales
+    float32 [NP, Hkv, BS].
+    """
+    import torch
+
+    seed = lay.seed if seed is None else seed
+    H, Hkv, D, BS = lay.num_q_heads, lay.num_kv_heads, lay.head_dim, lay.block_size
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed) * 1000003 + 41)
+    q = (torch.randn((lay.num_tokens, H, D), generator=gen, device=device) * lay.value_std).to(torch.bfloat16)
+    bad = torch.from_numpy(~_valid_rows_mask(lay)).to(device)  # [NP, BS]
+    out = []
+    for _ in range(2):
+        codes = torch.empty((lay.num_pages, Hkv, BS, D), dtype=torch.uint8, device=device)
+        for p0 in range(0, lay.num_pages, chunk_pages):
+            p1 = min(lay.num_pages, p0 + chunk_pages)
+            x = torch.randn((p1 - p0, Hkv, BS, D), generator=gen, device=device) * FP8_CODE_STD
+            codes[p0:p1] = x.clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+        scales = (torch.rand((lay.num_pages, Hkv, BS), generator=gen, device=device) * 0.4 + 0.8) * (
+            lay.value_std / FP8_CODE_STD)
+        codes.masked_fill_(bad[:, None, :, None], int(FP8_NAN_CODE))
+        scales.masked_fill_(bad[:, None, :], float("nan"))
+        out += [codes, scales]
+    return q, out[0], out[1], out[2], out[3]
+
+
+def fp8_values_numpy(lay: Layout, seed: Optional[int] = None):
+    """As :func:`fp8_values_torch`, on the host (q as bf16 bit patterns,
+    codes uint8, scales float32 numpy arrays)."""
+    import torch
+
+    q, kc, ks, vc, vs = fp8_values_torch(lay, torch.device("cpu"), seed)
+    return (q.view(torch.int16).numpy().view(np.uint16), kc.numpy(), ks.numpy(), vc.numpy(), vs.numpy())
