@@ -31,6 +31,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama8b_decode")
+    ap.add_argument("--op", choices=["attention", "append"], default="attention",
+                    help="attention (the call the workload names) or the KV append of its new tokens")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--split-pages", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the oracle sample")
@@ -41,21 +43,27 @@ def parse():
 
 
 KERNEL_SOURCES = ["paged_kv_decode_02_amd/csrc/pa_decode.hip", "paged_kv_decode_02_amd/csrc/pa_common.h"]
+APPEND_SOURCES = ["paged_kv_decode_02_amd/csrc/pa_append.hip", "paged_kv_decode_02_amd/csrc/pa_common.h"]
 
 
-def measured_traffic(workload: str):
+def source_digest(sources) -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in sources:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, sources=KERNEL_SOURCES):
     """HBM bytes per launch of the dominant kernel, from the PMC summary
     committed under profiles/ -- or None when there is none for this
     workload or the kernel source changed since the counters were taken."""
     import glob
-    import hashlib
     import re
 
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
-    digest = h.hexdigest()[:16]
+    digest = source_digest(sources)
     for path in glob.glob(os.path.join(ROOT, "profiles", "*.md")):
         for m in re.finditer(r"<!-- traffic: (.*?) -->", open(path).read()):
             kv = dict(x.split("=", 1) for x in m.group(1).split())
@@ -144,6 +152,63 @@ def cpu_baseline(lay, q, k, v, total_bytes, budget_s, k_scales=None, v_scales=No
     }
 
 
+def bench_append(args):
+    """pa_kv_append alone: every new token of the workload's batch (q_lens
+    rows per segment) written into the pools through the block tables.
+    Bytes: each new K and V row read once and written once, plus cu_q_lens,
+    context_lens and one table entry per token."""
+    import torch
+
+    from paged_kv_decode_02_amd import pa, roofline
+    from workloads import new_rows_torch, values_torch, workload
+
+    lay = workload(args.workload, seed=args.seed)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    _, k, v = values_torch(lay, dev)
+    kn, vn = new_rows_torch(lay, dev)
+    bt = torch.from_numpy(lay.block_tables).to(dev)
+    ctx = torch.from_numpy(lay.context_lens).to(dev)
+    cu = torch.from_numpy(lay.cu_q_lens.astype(np.int32)).to(dev)
+    stream = torch.cuda.current_stream()
+    T = lay.num_tokens
+
+    def step():
+        pa.kv_append(k, v, kn, vn, bt, cu, lay.cu_q_lens, ctx, lay.context_lens, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    pa.profile_enable(args.steps)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kern = float(np.mean(pa.profile_collect(args.steps)))
+    pa.profile_enable(0)
+    rows = 2 * 2 * T * lay.num_kv_heads * lay.head_dim * lay.elem_bytes
+    nbytes = rows + 4 * (lay.num_seqs + 1) + 4 * lay.num_seqs + 4 * T
+    achieved = nbytes / (kern * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "paged KV append GB/s (new K/V rows into the pool)", "value": round(nbytes / (ms * 1e-3) / 1e9, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": lay.dtype, "data": "synthetic",
+        "config": {"workload": args.workload, "op": "append", "new_tokens": int(T), "kv_heads": lay.num_kv_heads,
+                   "head_dim": lay.head_dim, "block_size": 16, "seed": args.seed},
+        "algorithmic_bytes_per_step": int(nbytes),
+        "roofline": {"bound": "hbm", "kernel": "kv_append_kernel", "achieved": round(achieved, 1),
+                     "peak": roofline.HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / roofline.HBM_PEAK_GBS, 4),
+                     "kernel_ms": round(kern, 5),
+                     "traffic": measured_traffic("append:" + args.workload, APPEND_SOURCES)},
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -153,6 +218,9 @@ def main():
         print(f"bench.py measures one GPU only (asked for {args.gpus}); this path does not shard across GPUs.",
               file=sys.stderr)
         sys.exit(2)
+    if args.op == "append":
+        bench_append(args)
+        return
     import torch
 
     from paged_kv_decode_02_amd import pa, roofline

@@ -126,6 +126,33 @@ def test_chunked_piggyback_size(gpu_lib):
         assert torch.equal(g, b), "a row that no new token maps to changed"
 
 
+def test_whole_prefill_write(gpu_lib):
+    # The Llama-shaped batch with every row new (148,663 tokens, 1.2 GB
+    # moved): the rows read back through each table, in order, must be the
+    # new rows bit for bit (the oracle's definition, checked as a property
+    # at this size), and the rows past each sequence's end keep their bits.
+    lay = workload("llama8b_prefill_append")
+    say("case append llama8b_prefill_append full size")
+    _, kp, vp = values_torch(lay, "cuda")
+    kn, vn = new_rows_torch(lay, "cuda")
+    k_before, v_before = kp.clone(), vp.clone()
+    run_append(gpu_lib, lay, kp, vp, kn, vn)
+    rows_page, rows_slot = [], []
+    for s in range(lay.num_seqs):
+        t = np.arange(int(lay.context_lens[s]))
+        rows_page.append(lay.block_tables[s, t // 16])
+        rows_slot.append(t % 16)
+    rp = torch.from_numpy(np.concatenate(rows_page).astype(np.int64)).cuda()
+    rs = torch.from_numpy(np.concatenate(rows_slot).astype(np.int64)).cuda()
+    for got, new, before in ((kp, kn, k_before), (vp, vn, v_before)):
+        back = got.view(torch.int16)[rp, :, rs, :]  # [T, Hkv, D] in token order
+        assert torch.equal(back, new.view(torch.int16)), "a row read back differs from the new row"
+        mask = torch.ones((lay.num_pages, 16), dtype=torch.bool, device="cuda")
+        mask[rp, rs] = False
+        assert torch.equal(got.view(torch.int16).transpose(1, 2)[mask],
+                           before.view(torch.int16).transpose(1, 2)[mask]), "a row no token maps to changed"
+
+
 def test_append_then_mixed_attention(gpu_lib):
     # End to end: the rows of this step's tokens start as NaN in the pools,
     # pa_kv_append writes them, then pa_mixed_chunk attends over the pools;

@@ -372,8 +372,19 @@ def _llama8b_decode_fp8(seed=0):
     return lay
 
 
+def _llama8b_prefill_append(seed=0):
+    """The Llama-shaped batch with every row new this step (a whole prefill
+    written into the cache): the KV-append workload that moves enough bytes
+    to be timed by its bandwidth."""
+    lay = _llama8b_decode(seed)
+    lay.name = "llama8b_prefill_append"
+    lay.q_lens = lay.context_lens.copy()
+    return lay
+
+
 WORKLOADS = {
     "tiny_f32": _tiny_f32,
+    "llama8b_prefill_append": _llama8b_prefill_append,
     "llama8b_decode": _llama8b_decode,
     "llama8b_decode_fp8": _llama8b_decode_fp8,
     "longtail_splitkv": _longtail_splitkv,
