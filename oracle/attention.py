@@ -176,6 +176,47 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale, num_kv_heads, b
     )
 
 
+def decode_window(q, k_pool, v_pool, block_tables, context_lens, window, scale, num_kv_heads, block_size, dtype,
+                  seqs=None):
+    """Decode with a sliding window of ``window`` tokens: the query of a
+    sequence with L rows sees rows ``[max(0, L - window), L)`` only.
+
+    A sliding-window KV group declares its window size in tokens
+    (``sliding_window_tokens``, TokenSpeed deep-dive section 4.1, the
+    attention kinds table); its block table keeps the real blocks at the
+    back and placeholder entries at the front for the blocks that fell out
+    of the window (tokenspeed 딥다이브 section 6-3).  So only table entries
+    from ``(L - window) // block_size`` on are looked up here: a placeholder
+    is never read.
+    """
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    S, Hq, D = q.shape
+    if S != len(ctx):
+        raise ValueError("q must hold one token per sequence")
+    if int(window) < 1:
+        raise ValueError("window must be >= 1")
+    G = Hq // num_kv_heads
+    sc = float(np.float32(scale))
+    out = np.full((S, Hq, D), np.nan, dtype=np.float64)
+    lse = np.full((S, Hq), np.nan, dtype=np.float64)
+    for s in (range(S) if seqs is None else seqs):
+        L = int(ctx[s])
+        if L < 1:
+            raise ValueError(f"sequence {s}: empty context")
+        lo = max(0, L - int(window))
+        t = np.arange(lo, L)
+        pages = np.asarray(block_tables[s])[t // block_size]
+        if pages.min() < 0 or pages.max() >= k_pool.shape[0]:
+            raise IndexError("block table names a page outside the pool")
+        qs = stored_to_f64(q[s], dtype)
+        for g in range(num_kv_heads):
+            K = stored_to_f64(k_pool[pages, g, t % block_size, :], dtype)
+            V = stored_to_f64(v_pool[pages, g, t % block_size, :], dtype)
+            for h in range(g * G, (g + 1) * G):
+                out[s, h], lse[s, h] = attend(qs[h], K, V, sc)
+    return out, lse
+
+
 def check_block_tables(
     block_tables,
     context_lens,

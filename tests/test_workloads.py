@@ -5,7 +5,26 @@ import numpy as np
 import pytest
 
 import oracle
-from workloads import WORKLOADS, pages_of, values_numpy, workload
+from workloads import WORKLOADS, pages_of, values_numpy, window_layout, workload
+
+
+def kept_tables(lay):
+    """For a sliding-window layout: each row's kept entries moved to the
+    front and the lengths cut to match (a valid plain table), after checking
+    that the entries before them are placeholders naming page 0, which no
+    kept entry uses.  Other layouts pass through."""
+    if lay.window is None:
+        return lay.block_tables, lay.context_lens
+    bt = np.full_like(lay.block_tables, -1)
+    ctx = lay.context_lens.copy()
+    for s, L in enumerate(lay.context_lens):
+        f = max(0, int(L) - lay.window) // lay.block_size
+        n = pages_of(L, lay.block_size)
+        assert (lay.block_tables[s, :f] == 0).all()
+        bt[s, : n - f] = lay.block_tables[s, f:n]
+        ctx[s] = L - f * lay.block_size
+        assert (bt[s, : n - f] != 0).all()
+    return bt, ctx
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
@@ -14,7 +33,8 @@ def test_layout_is_valid(name):
     kw = {}
     if lay.group_seq_offsets is not None:
         kw = dict(group_seq_offsets=lay.group_seq_offsets, prefix_lens=lay.prefix_lens)
-    assert oracle.check_block_tables(lay.block_tables, lay.context_lens, lay.num_pages, lay.block_size, **kw) == []
+    bt, ctx = kept_tables(lay)
+    assert oracle.check_block_tables(bt, ctx, lay.num_pages, lay.block_size, **kw) == []
     assert (lay.q_lens >= 1).all() and (lay.q_lens <= lay.context_lens).all()
     for s in range(lay.num_seqs):
         n = pages_of(lay.context_lens[s], lay.block_size)
@@ -62,3 +82,20 @@ def test_values_are_deterministic_and_poisoned():
     assert np.isfinite(q).all()
     c = values_numpy(lay, seed=1)
     assert not np.array_equal(c[0], q)
+
+
+def test_window_layout_keeps_only_the_window_pages():
+    lay = workload("longtail_window4096")
+    assert lay.window == 4096 and lay.num_seqs == 256
+    kept = sum(pages_of(L, 16) - max(0, int(L) - 4096) // 16 for L in lay.context_lens)
+    assert lay.num_pages == 1 + kept  # page 0 is the placeholder target
+    small = window_layout([5, 40, 100, 333], 50, num_q_heads=4, num_kv_heads=2, head_dim=64, dtype="f32", seed=3)
+    bt, ctx = kept_tables(small)
+    assert ctx.tolist() == [5, 40, 100 - 48, 333 - 272]
+    q, k, v = values_numpy(small)
+    assert np.isnan(k[0]).all() and np.isnan(v[0]).all()
+    # the kept rows of every sequence are finite, from the window's first page on
+    for s, L in enumerate(small.context_lens):
+        f = max(0, int(L) - 50) // 16
+        for t in range(f * 16, int(L)):
+            assert np.isfinite(k[small.block_tables[s, t // 16], :, t % 16]).all()

@@ -11,6 +11,7 @@ from .gen import (  # noqa: F401
     bf16_bits_from_f32,
     decode_layout,
     cascade_layout,
+    window_layout,
     mixed_layout,
     workload,
     values_numpy,

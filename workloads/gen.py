@@ -77,6 +77,10 @@ class Layout:
     # storage of the K/V pools: None = same as dtype; "fp8" = e4m3fn codes
     # with one float32 scale per (page, kv-head, slot), q and out in dtype
     kv_dtype: Optional[str] = None
+    # sliding window in tokens (None = full history): sequence s keeps the
+    # pages from (L - window) // block_size on; the entries before them are
+    # placeholders naming page 0, which holds no sequence's rows
+    window: Optional[int] = None
 
     @property
     def num_seqs(self) -> int:
@@ -177,6 +181,56 @@ def decode_layout(
         block_tables=_fill_tables(lists, max(mb, 1)),
         num_pages=int(num_pages),
         seed=seed,
+    )
+
+
+def window_layout(
+    context_lens,
+    window: int,
+    *,
+    num_q_heads: int,
+    num_kv_heads: int,
+    head_dim: int,
+    dtype: str,
+    block_size: int = 16,
+    scale: Optional[float] = None,
+    value_std: float = 0.5,
+    seed: int = 0,
+    name: str = "window",
+) -> Layout:
+    """One query token per sequence over a sliding-window cache: sequence s
+    holds only the pages from (L - window) // block_size on, in a seeded
+    permutation of pages 1..; its table entries before them are placeholders
+    naming page 0, which no sequence stores rows in (it stays NaN)."""
+    ctx = np.asarray(context_lens, dtype=np.int32)
+    firsts = [max(0, int(L) - int(window)) // block_size for L in ctx]
+    need = [pages_of(L, block_size) - f for L, f in zip(ctx, firsts)]
+    num_pages = 1 + int(sum(need))
+    perm = (1 + _rng(seed, 0).permutation(num_pages - 1)).astype(np.int32)
+    mb = max(pages_of(L, block_size) for L in ctx)
+    bt = np.full((len(ctx), mb), -1, dtype=np.int32)
+    at = 0
+    for s, (L, f, n) in enumerate(zip(ctx, firsts, need)):
+        bt[s, :f] = 0
+        bt[s, f : f + n] = perm[at : at + n]
+        at += n
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    return Layout(
+        name=name,
+        dtype=dtype,
+        num_q_heads=num_q_heads,
+        num_kv_heads=num_kv_heads,
+        head_dim=head_dim,
+        block_size=block_size,
+        scale=_scale_f32(scale),
+        value_std=value_std,
+        context_lens=ctx,
+        q_lens=np.ones_like(ctx),
+        block_tables=bt,
+        num_pages=num_pages,
+        seed=seed,
+        window=int(window),
     )
 
 
@@ -382,8 +436,17 @@ def _llama8b_prefill_append(seed=0):
     return lay
 
 
+def _longtail_window4096(seed=0):
+    """The long-tail batch's lengths and heads over a 4096-token sliding
+    window (every sequence attends to at most its last 4096 rows)."""
+    base = _longtail_splitkv(seed)
+    return window_layout(base.context_lens, 4096, num_q_heads=base.num_q_heads, num_kv_heads=base.num_kv_heads,
+                         head_dim=base.head_dim, dtype=base.dtype, seed=seed, name="longtail_window4096")
+
+
 WORKLOADS = {
     "tiny_f32": _tiny_f32,
+    "longtail_window4096": _longtail_window4096,
     "llama8b_prefill_append": _llama8b_prefill_append,
     "llama8b_decode": _llama8b_decode,
     "llama8b_decode_fp8": _llama8b_decode_fp8,
@@ -403,14 +466,16 @@ def workload(name: str, seed: int = 0) -> Layout:
 
 
 def _valid_rows_mask(lay: Layout) -> np.ndarray:
-    """bool [num_pages, block_size]: rows some sequence stores a token in."""
+    """bool [num_pages, block_size]: rows some sequence stores a token in
+    (for a sliding window: the rows of the pages it still keeps)."""
     valid = np.zeros((lay.num_pages, lay.block_size), dtype=bool)
     bs = lay.block_size
     for s in range(lay.num_seqs):
         L = int(lay.context_lens[s])
         n = pages_of(L, bs)
+        first = 0 if lay.window is None else max(0, L - lay.window) // bs
         pg = lay.block_tables[s, :n]
-        valid[pg[: n - 1]] = True
+        valid[pg[first : n - 1]] = True
         last = L - (n - 1) * bs
         valid[pg[n - 1], :last] = True
     return valid
