@@ -91,7 +91,10 @@ def visible_pairs(lay, segs):
     tot = 0
     for s in segs:
         L, n = int(lay.context_lens[s]), int(lay.q_lens[s])
-        tot += n * (L - n) + n * (n + 1) // 2
+        if lay.window is not None:
+            tot += min(L, lay.window)  # one query over its window
+        else:
+            tot += n * (L - n) + n * (n + 1) // 2
     return tot
 
 
@@ -130,6 +133,11 @@ def cpu_baseline(lay, q, k, v, total_bytes, budget_s, k_scales=None, v_scales=No
                 t0 = time.perf_counter()
                 oracle.decode_fp8(qs, kc, ksc, vc, vsc, bt, lay.context_lens[s : s + 1], lay.scale,
                                   lay.num_kv_heads, 16, "bf16")
+            elif lay.window is not None:
+                ks, vs = host(k.index_select(0, idx)), host(v.index_select(0, idx))
+                t0 = time.perf_counter()
+                oracle.decode_window(qs, ks, vs, bt, lay.context_lens[s : s + 1], lay.window, lay.scale,
+                                     lay.num_kv_heads, 16, lay.dtype)
             else:
                 ks, vs = host(k.index_select(0, idx)), host(v.index_select(0, idx))
                 t0 = time.perf_counter()
@@ -269,6 +277,9 @@ def main():
             if fp8:
                 pa.decode_fp8(out, q, k, v, ks, vs, bt, ctx, lay.context_lens, lay.scale, ws,
                               split_pages=args.split_pages, stream=stream)
+            elif lay.window is not None:
+                pa.decode_window(out, q, k, v, bt, ctx, lay.context_lens, lay.scale, lay.window, ws,
+                                 split_pages=args.split_pages, stream=stream)
             else:
                 pa.decode(out, q, k, v, bt, ctx, lay.context_lens, lay.scale, ws, split_pages=args.split_pages,
                           stream=stream)
@@ -343,6 +354,12 @@ def main():
         roof, other = (chunk_roof, dec_roof) if kern_avg[0] >= kern_avg[1] else (dec_roof, chunk_roof)
         extra = {"chunk_gflop": round(flops / 1e9, 3), "other_kernel_roofline": other,
                  "tokens_per_step": int(T)}
+    elif lay.window is not None:
+        # the rows each query sees: the last min(L, window) of its sequence
+        nb = roofline.decode_bytes(np.minimum(lay.context_lens, lay.window), lay.num_q_heads, lay.num_kv_heads, D,
+                                   lay.elem_bytes)
+        roof = hbm_roof("stream_decode_kernel (sliding window)", nb["total"], kern_avg[0],
+                        measured_traffic(args.workload))
     elif fp8:
         nb = roofline.decode_fp8_bytes(lay.context_lens, lay.num_q_heads, lay.num_kv_heads, D)
         roof = hbm_roof("stream_decode_kernel (fp8 pools)", nb["total"], kern_avg[0],
@@ -372,7 +389,8 @@ def main():
             "kv_heads": lay.num_kv_heads,
             "head_dim": int(D),
             "block_size": 16,
-            "kv_tokens": int(lay.context_lens.sum()),
+            "kv_tokens": int(np.minimum(lay.context_lens, lay.window).sum() if lay.window else lay.context_lens.sum()),
+            **({"window": int(lay.window)} if lay.window else {}),
             "seed": args.seed,
             "parallelism": "single GPU",
         },

@@ -115,6 +115,32 @@ int pa_decode(void* out,                      /* device [S, Hq, D] dtype */
               void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Sliding-window decode: pa_decode where the query of a sequence with L rows
+ * sees only rows [max(0, L - window), L).  A sliding-window KV group
+ * declares its window in tokens (TokenSpeed deep-dive section 4.1, the
+ * attention kinds); its block table keeps the real blocks at the back and
+ * placeholder entries at the front for blocks that fell out of the window
+ * (tokenspeed 딥다이브 section 6-3).  Only entries from (L - window) / 16 on
+ * are read, so placeholders may name any page (page 0 by convention) and
+ * are never dereferenced; the rows of the window's first page before
+ * L - window are masked.  Work is planned over the window's pages only.
+ *
+ * window: tokens, >= 1 (PA_EINVAL otherwise); a window >= L is plain decode.
+ * Everything else as pa_decode (same workspace size for the same batch).
+ * ------------------------------------------------------------------------- */
+int pa_decode_window(void* out,                 /* device [S, Hq, D] dtype */
+                     float* lse_out,            /* device [S, Hq] or NULL */
+                     const void* q,             /* device [S, Hq, D] dtype */
+                     const void* k_pool,        /* device [NP, Hkv, BS, D] dtype */
+                     const void* v_pool,        /* device [NP, Hkv, BS, D] dtype */
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, const int32_t* context_lens_host,
+                     int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_ratio, int32_t head_dim,
+                     int32_t block_size, int64_t num_pages, float scale, pa_dtype dtype,
+                     int32_t window,            /* tokens, >= 1 */
+                     int32_t split_pages, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Decode over an fp8 KV cache: pa_decode with K and V stored as OCP e4m3fn
  * codes (one byte each: 4 exponent bits with bias 7, 3 mantissa bits,
  * subnormals, NaN = 0x7f/0xff, largest finite value 448) and one float32

@@ -47,7 +47,7 @@ int decode_call(void* out, float* lse_out, const void* q, const void* k_pool, co
                 int32_t max_blocks, const int32_t* context_lens, const int32_t* context_lens_host, int32_t num_seqs,
                 int32_t num_kv_heads, int32_t gqa_ratio, int32_t head_dim, int32_t block_size, int64_t num_pages,
                 float scale, pa_dtype dtype, int32_t split_pages, void* workspace, size_t workspace_bytes,
-                void* stream, const char* who) {
+                void* stream, int32_t window, const char* who) {
   const std::string w(who);
   if (num_seqs < 0) return fail(PA_EINVAL, w + ": num_seqs < 0");
   if (num_seqs == 0) return PA_OK;
@@ -56,6 +56,7 @@ int decode_call(void* out, float* lse_out, const void* q, const void* k_pool, co
   if (rc) return rc;
   if (kv_fp8 && (!k_scales || !v_scales)) return fail(PA_EINVAL, w + ": null scale pointer");
   if (split_pages < 0) return fail(PA_EINVAL, w + ": split_pages < 0");
+  if (window < 0) return fail(PA_EINVAL, w + ": window < 1");
   const bool built = kv_fp8 ? decode_fp8_supported(head_dim, gqa_ratio) : decode_supported(dtype, head_dim, gqa_ratio);
   if (!built)
     return fail(PA_EUNSUPPORTED, w + ": no kernel for head_dim " + std::to_string(head_dim) + "/gqa_ratio " +
@@ -67,7 +68,10 @@ int decode_call(void* out, float* lse_out, const void* q, const void* k_pool, co
     if (L < 1) return fail(PA_EINVAL, w + ": context_lens[" + std::to_string(s) + "] < 1");
     if (L > static_cast<int64_t>(max_blocks) * block_size)
       return fail(PA_EINVAL, w + ": context_lens[" + std::to_string(s) + "] exceeds the block table");
-    total_pages += (L + block_size - 1) / block_size;
+    // pages the walk covers: from the window's first page on (a sliding
+    // window's earlier entries are placeholders and are never read)
+    const int64_t first = window > 0 && L > window ? (L - window) / block_size : 0;
+    total_pages += (L + block_size - 1) / block_size - first;
   }
   if (total_pages > (int64_t(1) << 31) - 1) return fail(PA_EUNSUPPORTED, w + ": more than 2^31-1 pages");
   // The workspace must hold the largest plan this batch could get, so that
@@ -101,6 +105,7 @@ int decode_call(void* out, float* lse_out, const void* q, const void* k_pool, co
   a.kv_fp8 = kv_fp8;
   a.k_scales = k_scales;
   a.v_scales = v_scales;
+  a.window = window;
   return launch_decode(a);
 }
 
@@ -115,7 +120,20 @@ extern "C" int pa_decode(void* out, float* lse_out, const void* q, const void* k
   clear_error();
   return decode_call(out, lse_out, q, k_pool, v_pool, nullptr, nullptr, false, block_tables, max_blocks, context_lens,
                      context_lens_host, num_seqs, num_kv_heads, gqa_ratio, head_dim, block_size, num_pages, scale,
-                     dtype, split_pages, workspace, workspace_bytes, stream, "pa_decode");
+                     dtype, split_pages, workspace, workspace_bytes, stream, 0, "pa_decode");
+}
+
+extern "C" int pa_decode_window(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,
+                                const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                                const int32_t* context_lens_host, int32_t num_seqs, int32_t num_kv_heads,
+                                int32_t gqa_ratio, int32_t head_dim, int32_t block_size, int64_t num_pages,
+                                float scale, pa_dtype dtype, int32_t window, int32_t split_pages, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  clear_error();
+  if (window < 1) return fail(PA_EINVAL, "pa_decode_window: window < 1");
+  return decode_call(out, lse_out, q, k_pool, v_pool, nullptr, nullptr, false, block_tables, max_blocks, context_lens,
+                     context_lens_host, num_seqs, num_kv_heads, gqa_ratio, head_dim, block_size, num_pages, scale,
+                     dtype, split_pages, workspace, workspace_bytes, stream, window, "pa_decode_window");
 }
 
 extern "C" int pa_decode_fp8(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,
@@ -127,7 +145,7 @@ extern "C" int pa_decode_fp8(void* out, float* lse_out, const void* q, const voi
   clear_error();
   return decode_call(out, lse_out, q, k_pool, v_pool, k_scales, v_scales, true, block_tables, max_blocks,
                      context_lens, context_lens_host, num_seqs, num_kv_heads, gqa_ratio, head_dim, block_size,
-                     num_pages, scale, PA_BF16, split_pages, workspace, workspace_bytes, stream, "pa_decode_fp8");
+                     num_pages, scale, PA_BF16, split_pages, workspace, workspace_bytes, stream, 0, "pa_decode_fp8");
 }
 
 extern "C" size_t pa_prefix_cascade_workspace_size(int32_t max_num_seqs, int32_t num_kv_heads, int32_t gqa_ratio,

@@ -136,6 +136,14 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
+// First page a sequence's walk covers: begin_pages[s] when given (the
+// pages after a shared prefix, or past a prefill chunk), else the page of
+// the first row inside a sliding window of `window` tokens (0 = none).
+__device__ __forceinline__ int walk_begin(const int32_t* __restrict__ begin_pages, int s, int L, int window) {
+  if (begin_pages) return begin_pages[s];
+  return window > 0 && L > window ? (L - window) >> 4 : 0;
+}
+
 // Splits of C pages that sequence s needs over pages [begin, pages).
 __device__ __forceinline__ int nsplit_of(int L, int begin_pages, int max_blocks, int C) {
   const int64_t pg = (static_cast<int64_t>(L) + 15) >> 4;
@@ -156,9 +164,10 @@ struct ItemLoc {
 // sequence; every wave derives the numbering itself from the device copy
 // of the context lengths (one pass over S values, then one over the
 // S/64 values of the lane that holds x), so no plan buffer is needed.
-// `begin_pages` (nullable) gives pages each sequence skips.
+// `begin_pages` (nullable) gives pages each sequence skips; without it a
+// sliding window of `window` tokens (0 = none) decides them.
 __device__ __forceinline__ bool locate_item(const int32_t* __restrict__ ctx, const int32_t* __restrict__ begin_pages,
-                                            int S, int max_blocks, int C, int x, ItemLoc& loc) {
+                                            int window, int S, int max_blocks, int C, int x, ItemLoc& loc) {
   const int lane = lane_id();
   const int per = (S + 63) >> 6;
   int tot = 0;
@@ -168,7 +177,8 @@ __device__ __forceinline__ bool locate_item(const int32_t* __restrict__ ctx, con
   for (int i = 0; i < per; ++i) {
     const int s = lane * per + i;
     const int sc = s < S ? s : S - 1;
-    const int n = nsplit_of(ctx[sc], begin_pages ? begin_pages[sc] : 0, max_blocks, C);
+    const int Lc = ctx[sc];
+    const int n = nsplit_of(Lc, walk_begin(begin_pages, sc, Lc, window), max_blocks, C);
     tot += s < S ? n : 0;
   }
   const int incl = wave_inclusive_scan(tot);
@@ -182,7 +192,11 @@ __device__ __forceinline__ bool locate_item(const int32_t* __restrict__ ctx, con
   for (int r0 = 0; r0 < per; r0 += 64) {
     const int i = r0 + lane;
     const int s = first + i;
-    const int ns = (i < per && s < S) ? nsplit_of(ctx[s], begin_pages ? begin_pages[s] : 0, max_blocks, C) : 0;
+    int ns = 0;
+    if (i < per && s < S) {
+      const int Ls = ctx[s];
+      ns = nsplit_of(Ls, walk_begin(begin_pages, s, Ls, window), max_blocks, C);
+    }
     const int inc2 = wave_inclusive_scan(ns);
     const int ex2 = inc2 - ns;
     const unsigned long long b2 = __ballot(ns > 0 && x >= base + ex2 && x < base + inc2);

@@ -82,6 +82,7 @@ struct Batch {
   int seg_hi;  // one past the last page this wave covers
   int cs;      // flattened index of the sequence's first page
   int qb;      // q buffer holding the sequence's q rows
+  int lo;      // first row the query sees (sliding window; else 0)
   int pid[4];  // physical pages (entries past seg_hi repeat the last one)
 };
 
@@ -159,7 +160,8 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ ctx,
     int max_blocks, int S, int Hkv, int num_pages, float scale_log2, int per, int total_pages,
     int32_t* __restrict__ seq_info, float* __restrict__ part_o, float* __restrict__ part_lse,
-    const int32_t* __restrict__ begin_pages, float* __restrict__ seq_part, const int32_t* __restrict__ q_rows) {
+    const int32_t* __restrict__ begin_pages, float* __restrict__ seq_part, const int32_t* __restrict__ q_rows,
+    int window) {
   using Gm = Geom<TKV, D>;
   constexpr int RD = Gm::RD, NCH = Gm::NCH, TILE = Gm::TILE, NI = Gm::NI, RPI = Gm::RPI, EPC = Gm::EPC;
   constexpr bool FP8 = sizeof(TKV) == 1;
@@ -215,15 +217,18 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
   // Where the run starts: sequence s0 and its first flattened page.
   ItemLoc loc;
   // (Cascade suffix: only pages from begin_pages[s] on are laid end to end.)
-  if (!locate_item(ctx, begin_pages, S, max_blocks, 1, run_a, loc)) return;
+  if (!locate_item(ctx, begin_pages, window, S, max_blocks, 1, run_a, loc)) return;
   const int s0 = __builtin_amdgcn_readfirstlane(loc.s);
-  auto first_page = [&](int s, int P) { return begin_pages ? min(max(begin_pages[s], 0), P) : 0; };
+  auto first_page = [&](int s, int L, int P) { return min(max(walk_begin(begin_pages, s, L, window), 0), P); };
+  // First row a sequence's query sees: 0, or the start of the sliding window.
+  auto first_row = [&](int L) { return window > 0 && L > window ? L - window : 0; };
 
   Batch first;
   first.s = s0;
   first.L = ctx[s0];
   first.P = pages_of_len(first.L, max_blocks);
-  first.B = first_page(s0, first.P);
+  first.B = first_page(s0, first.L, first.P);
+  first.lo = first_row(first.L);
   first.cs = __builtin_amdgcn_readfirstlane(loc.base);
   first.seg_lo = first.B + (run_a - first.cs);
   first.seg_hi = min(first.P, first.B + (run_b - first.cs));
@@ -302,7 +307,7 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
       y.cs = x.cs + (x.P - x.B);
       y.L = ctx[y.s];
       y.P = pages_of_len(y.L, max_blocks);
-      y.B = first_page(y.s, y.P);
+      y.B = first_page(y.s, y.L, y.P);
       // Sequences with nothing after begin_pages (the prefill chunks of a
       // mixed batch) hold no pages of the walk: step over them.  Pages of
       // this run remain, so a sequence that holds some follows.
@@ -310,8 +315,9 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
         y.s += 1;
         y.L = ctx[y.s];
         y.P = pages_of_len(y.L, max_blocks);
-        y.B = first_page(y.s, y.P);
+        y.B = first_page(y.s, y.L, y.P);
       }
+      y.lo = first_row(y.L);
       y.seg_lo = y.B;
       y.seg_hi = min(y.P, y.B + (run_b - y.cs));
       y.pb = y.B;
@@ -347,6 +353,7 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
     // Scores, lane = row: K row chunks and q chunks (one address for the
     // whole wave, a broadcast read) from LDS, CG chunks at a time.
     const int nvalid = min(cur.seg_hi * 16, cur.L) - cur.pb * 16;  // rows of this batch (1..64)
+    const int lo_b = cur.lo - cur.pb * 16;  // rows of this batch before the window (<= 0: none)
     // fp8: this row's K and V scales, read before the next batch's K (and
     // scales) may be issued into the same LDS.
     const float k_row_scale = FP8 ? ks_lds[FP8 ? lane : 0] : 1.0f;
@@ -406,7 +413,7 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
     if (has_next) issue_k(nxt);
 
     // Online softmax; probabilities to LDS.
-    const bool valid = lane < nvalid;
+    const bool valid = lane < nvalid && lane >= lo_b;
     // fp8: the row's K scale multiplies its scores; its V scale is folded
     // into the probability that P.V uses (the normaliser sums the plain
     // probabilities).  Rows past the end select 0 / -inf, never multiply.
@@ -445,10 +452,10 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
     for (int i = 0; i < NI; ++i) vr[i] = v_lds[i * 64 + lane];
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     if (has_next) issue_v(nxt);
-    if (nvalid < 64) {
+    if (nvalid < 64 || lo_b > 0) {
 #pragma unroll
       for (int i = 0; i < NI; ++i)
-        if (i * RPI + grp >= nvalid) vr[i] = make_uint4(0u, 0u, 0u, 0u);
+        if (i * RPI + grp >= nvalid || i * RPI + grp < lo_b) vr[i] = make_uint4(0u, 0u, 0u, 0u);
     }
 
     // P.V: lane (grp, chk) accumulates its NI rows into its EPC columns.
@@ -741,7 +748,8 @@ int launch_typed(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_p
                      static_cast<const TKV*>(a.v_pool), a.k_scales, a.v_scales, a.block_tables, a.context_lens,
                      a.max_blocks, a.num_seqs,
                      a.num_kv_heads, static_cast<int>(a.num_pages), scale_log2, static_cast<int>(per),
-                     static_cast<int>(a.total_pages), seq_info, part_o, part_lse, begin_pages, seq_part, q_rows);
+                     static_cast<int>(a.total_pages), seq_info, part_o, part_lse, begin_pages, seq_part, q_rows,
+                     begin_pages ? 0 : a.window);
   if (a.timed) profile_after(a.stream);
   if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_decode: stream kernel launch failed");
   // Unless one wave covers everything, some sequence may be shared; the

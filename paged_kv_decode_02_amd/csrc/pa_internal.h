@@ -66,6 +66,9 @@ struct DecodeLaunch {
   bool kv_fp8 = false;
   const float* k_scales = nullptr;
   const float* v_scales = nullptr;
+  // sliding window in tokens (0 = full history); total_pages then counts
+  // only the pages from each window's first page on
+  int32_t window = 0;
 };
 
 bool decode_supported(pa_dtype dtype, int32_t head_dim, int32_t gqa);
