@@ -7,8 +7,8 @@ with it: the only code both sides use is the seeded input generator in
 ``workloads``.
 
 Pins (what fixes each function to something other than itself) are listed in
-the headers of ``oracle/attention.py``, ``oracle/kv_append.py`` and
-``oracle/fp8.py``; every
+the headers of ``oracle/attention.py``, ``oracle/kv_append.py``,
+``oracle/fp8.py`` and ``oracle/prefix_groups.py``; every
 function is pinned, none is "parity unpinned".
 """
 
@@ -26,3 +26,4 @@ from .attention import (  # noqa: F401
 )
 from .kv_append import kv_append  # noqa: F401
 from .fp8 import decode_fp8, dequantize, e4m3_to_f64, quantize_rows  # noqa: F401
+from .prefix_groups import detect_prefix_groups  # noqa: F401
