@@ -300,6 +300,33 @@ int pa_check_block_tables(const int32_t* block_tables_host, int32_t max_blocks_p
                           int64_t num_pages, int32_t num_groups, const int32_t* group_seq_offsets_host,
                           const int32_t* prefix_lens_host);
 
+/* ---------------------------------------------------------------------------
+ * Shared-prefix detection for pa_prefix_cascade (host only, no device
+ * access): the greedy search the Tokasaurus page runs before each forward
+ * pass ("dynamic prefix identification").  Shared-prefix blocks are stored
+ * once and named by every table that shares them (SwiftLLM page section
+ * 3.1), so sequences share their first d pages when their first d table
+ * entries are equal.  Each round picks, over a trie of the tables' page ids,
+ * the prefix that saves the most page reads, d * (members - 1) (ties: the
+ * longer prefix, then the one met first when the tables are read in
+ * order), among prefixes of >= min_prefix_pages pages shorter than every
+ * member's context and held by >= min_group (at least 2) sequences not yet
+ * grouped; its sequences become a group.  The rest form a last group with
+ * prefix 0.
+ *
+ * Outputs (host, caller-owned): order_out[num_seqs] -- original sequence
+ * index at each position, group by group (groups in the order found,
+ * members by original index); group_offsets_out[num_seqs + 1] and
+ * prefix_lens_out[num_seqs] -- pa_prefix_cascade's groups over the sequences
+ * taken in that order; *num_groups_out.  Returns PA_OK, or PA_EINVAL for
+ * null pointers, negative sizes or a context length < 1 or beyond the
+ * table.
+ * ------------------------------------------------------------------------- */
+int pa_detect_prefix_groups(const int32_t* block_tables_host, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens_host, int32_t num_seqs, int32_t block_size,
+                            int32_t min_group, int32_t min_prefix_pages, int32_t* order_out,
+                            int32_t* group_offsets_out, int32_t* prefix_lens_out, int32_t* num_groups_out);
+
 /* Message for the last non-OK return on this thread ("" if none). */
 const char* pa_last_error(void);
 

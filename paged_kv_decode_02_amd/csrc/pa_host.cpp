@@ -168,3 +168,164 @@ extern "C" int pa_check_block_tables(const int32_t* bt, int32_t max_blocks, cons
   }
   return PA_OK;
 }
+
+// Shared-prefix detection (the greedy search the Tokasaurus page runs before
+// each forward pass to find shared prefixes among live sequences).  Blocks of
+// a shared prefix are stored once and named by every table sharing it, so two
+// sequences share their first d pages exactly when their first d table
+// entries are equal; a sequence may share at most d pages with d * block_size
+// < its context length.  Each round takes the prefix that saves the most
+// page reads, d * (members - 1) over the sequences not yet grouped (ties: the
+// longer prefix, then the one whose first holder in table order comes
+// first), and makes its remaining holders a group.
+//
+// Instead of a trie of every page, the tables are sorted lexicographically
+// (each up to its own depth limit) and the longest common prefixes of
+// neighbours give the LCP intervals: a run of sorted rows [l, r] whose common
+// prefix is d pages.  Every prefix held by two or more sequences is a trie
+// node whose members are such a run, and among the nodes with the same
+// members the deepest (the interval) saves the most, so only intervals are
+// candidates.  Counts of ungrouped members come from a Fenwick tree over the
+// sorted positions; a candidate's saving only ever decreases, so a max-heap
+// with lazy re-keying finds each round's best without rescanning.
+namespace {
+struct Fenwick {
+  std::vector<int32_t> t;
+  explicit Fenwick(int32_t n) : t(n + 1, 0) {}
+  void add(int32_t i, int32_t v) {
+    for (++i; i < static_cast<int32_t>(t.size()); i += i & -i) t[i] += v;
+  }
+  int32_t prefix(int32_t i) const {  // sum over [0, i)
+    int32_t r = 0;
+    for (; i > 0; i -= i & -i) r += t[i];
+    return r;
+  }
+};
+}  // namespace
+
+extern "C" int pa_detect_prefix_groups(const int32_t* bt, int32_t max_blocks, const int32_t* ctx, int32_t num_seqs,
+                                       int32_t block_size, int32_t min_group, int32_t min_prefix_pages,
+                                       int32_t* order_out, int32_t* group_offsets_out, int32_t* prefix_lens_out,
+                                       int32_t* num_groups_out) {
+  clear_error();
+  if (num_seqs < 0 || max_blocks < 0 || block_size < 1)
+    return fail(PA_EINVAL, "pa_detect_prefix_groups: negative size or block_size < 1");
+  if (!num_groups_out) return fail(PA_EINVAL, "pa_detect_prefix_groups: null num_groups_out");
+  *num_groups_out = 0;
+  if (num_seqs == 0) return PA_OK;
+  if (!bt || !ctx || !order_out || !group_offsets_out || !prefix_lens_out)
+    return fail(PA_EINVAL, "pa_detect_prefix_groups: null pointer argument");
+  const int32_t S = num_seqs;
+  const int32_t mg = std::max(2, min_group);
+  const int32_t mp = std::max(1, min_prefix_pages);
+  std::vector<int32_t> dmax(S);
+  for (int32_t s = 0; s < S; ++s) {
+    const int64_t L = ctx[s];
+    if (L < 1 || L > static_cast<int64_t>(max_blocks) * block_size)
+      return fail(PA_EINVAL, "pa_detect_prefix_groups: context_lens[" + std::to_string(s) + "] out of range");
+    dmax[s] = static_cast<int32_t>((L - 1) / block_size);
+  }
+  auto row = [&](int32_t s) { return bt + static_cast<int64_t>(s) * max_blocks; };
+  // common prefix of two sequences within both depth limits
+  auto lcp = [&](int32_t a, int32_t b) {
+    const int32_t n = std::min(dmax[a], dmax[b]);
+    const int32_t* ra = row(a);
+    const int32_t* rb = row(b);
+    int32_t d = 0;
+    while (d < n && ra[d] == rb[d]) ++d;
+    return d;
+  };
+  std::vector<int32_t> idx(S);
+  for (int32_t s = 0; s < S; ++s) idx[s] = s;
+  std::sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) {
+    const int32_t d = lcp(a, b);
+    const int32_t n = std::min(dmax[a], dmax[b]);
+    if (d < n) return row(a)[d] < row(b)[d];
+    if (dmax[a] != dmax[b]) return dmax[a] < dmax[b];
+    return a < b;
+  });
+  // LCP intervals (depth, sorted range [l, r]) by the usual stack walk over
+  // the neighbours' common prefixes.
+  struct Interval {
+    int32_t depth, l, r, first;  // first: smallest original index in the run
+  };
+  std::vector<Interval> iv;
+  {
+    std::vector<std::pair<int32_t, int32_t>> st;  // (depth, left end)
+    st.emplace_back(0, 0);
+    for (int32_t i = 1; i <= S; ++i) {
+      const int32_t h = i < S ? lcp(idx[i - 1], idx[i]) : 0;
+      int32_t lb = i - 1;
+      while (st.back().first > h) {
+        const auto top = st.back();
+        st.pop_back();
+        iv.push_back(Interval{top.first, top.second, i - 1, 0});
+        lb = top.second;
+      }
+      if (st.back().first < h) st.emplace_back(h, lb);
+    }
+  }
+  for (Interval& x : iv) {
+    x.first = S;
+    for (int32_t p = x.l; p <= x.r; ++p) x.first = std::min(x.first, idx[p]);
+  }
+  Fenwick left(S);  // 1 at each sorted position not yet grouped
+  for (int32_t p = 0; p < S; ++p) left.add(p, 1);
+  auto remaining = [&](const Interval& x) { return left.prefix(x.r + 1) - left.prefix(x.l); };
+  struct Cand {
+    int64_t save;
+    int32_t depth, first, id;
+    bool operator<(const Cand& o) const {
+      if (save != o.save) return save < o.save;
+      if (depth != o.depth) return depth < o.depth;
+      return first > o.first;  // the earlier first holder ranks higher
+    }
+  };
+  auto cand_of = [&](int32_t i) {
+    const int32_t n = remaining(iv[i]);
+    return Cand{static_cast<int64_t>(iv[i].depth) * (n - 1), iv[i].depth, iv[i].first, i};
+  };
+  auto eligible = [&](int32_t i) {
+    const int32_t n = remaining(iv[i]);
+    return n >= mg && iv[i].depth >= mp;
+  };
+  std::vector<Cand> heap;
+  for (int32_t i = 0; i < static_cast<int32_t>(iv.size()); ++i)
+    if (eligible(i)) heap.push_back(cand_of(i));
+  std::make_heap(heap.begin(), heap.end());
+  std::vector<char> assigned(S, 0);
+  int32_t placed = 0, groups = 0;
+  group_offsets_out[0] = 0;
+  while (!heap.empty()) {
+    std::pop_heap(heap.begin(), heap.end());
+    const Cand top = heap.back();
+    heap.pop_back();
+    if (!eligible(top.id)) continue;
+    const Cand now = cand_of(top.id);
+    if (now.save != top.save) {  // stale: members were grouped since it was pushed
+      heap.push_back(now);
+      std::push_heap(heap.begin(), heap.end());
+      continue;
+    }
+    if (now.save <= 0) break;
+    const Interval& x = iv[top.id];
+    const int32_t first = placed;
+    for (int32_t p = x.l; p <= x.r; ++p) {
+      if (assigned[idx[p]]) continue;
+      assigned[idx[p]] = 1;
+      left.add(p, -1);
+      order_out[placed++] = idx[p];
+    }
+    std::sort(order_out + first, order_out + placed);  // members by original index
+    prefix_lens_out[groups] = x.depth * block_size;
+    group_offsets_out[++groups] = placed;
+  }
+  if (placed < S) {
+    for (int32_t s = 0; s < S; ++s)
+      if (!assigned[s]) order_out[placed++] = s;
+    prefix_lens_out[groups] = 0;
+    group_offsets_out[++groups] = placed;
+  }
+  *num_groups_out = groups;
+  return PA_OK;
+}

@@ -38,6 +38,7 @@ EXPORTS = (
     "pa_mixed_chunk",
     "pa_kv_append",
     "pa_check_block_tables",
+    "pa_detect_prefix_groups",
     "pa_last_error",
     "pa_profile_enable",
     "pa_profile_collect",
@@ -92,6 +93,8 @@ def load(path: Optional[str] = None):
     lib.pa_kv_append.restype = ctypes.c_int
     lib.pa_kv_append.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32,
                                  c_i32, c_i64, ctypes.c_int, c_vp]
+    lib.pa_detect_prefix_groups.restype = ctypes.c_int
+    lib.pa_detect_prefix_groups.argtypes = [c_vp, c_i32, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]
     lib.pa_check_block_tables.restype = ctypes.c_int
     lib.pa_check_block_tables.argtypes = [c_vp, c_i32, c_vp, c_i32, c_i32, c_i64, c_i32, c_vp, c_vp]
     lib.pa_last_error.restype = ctypes.c_char_p
@@ -431,3 +434,28 @@ def profile_collect(cap: int = 1 << 16):
     buf = (ctypes.c_float * cap)()
     n = _check(load().pa_profile_collect(buf, cap))
     return [buf[i] for i in range(n)]
+
+
+def detect_prefix_groups(block_tables, context_lens, block_size=16, min_group=2, min_prefix_pages=1):
+    """pa_detect_prefix_groups on host arrays (numpy, or CPU tensors).
+
+    Returns (order [S], group_offsets [NG+1], prefix_lens [NG]) int32 numpy
+    arrays: take sequences in ``order`` (tables, lengths, q rows) to call
+    pa_prefix_cascade with these groups; its output rows then follow
+    ``order`` too.
+    """
+    bt = _host_i32(block_tables, "block_tables")
+    ctx = _host_i32(context_lens, "context_lens")
+    if bt.ndim != 2 or bt.shape[0] != ctx.size:
+        raise ValueError("block_tables must be [S, max_blocks] with one row per context length")
+    S = ctx.size
+    order = np.zeros(S, dtype=np.int32)
+    offs = np.zeros(S + 1, dtype=np.int32)
+    pref = np.zeros(max(S, 1), dtype=np.int32)
+    ng = ctypes.c_int32(0)
+    rc = load().pa_detect_prefix_groups(bt.ctypes.data, bt.shape[1], ctx.ctypes.data, S, int(block_size),
+                                        int(min_group), int(min_prefix_pages), order.ctypes.data, offs.ctypes.data,
+                                        pref.ctypes.data, ctypes.byref(ng))
+    _check(rc)
+    n = ng.value
+    return order, offs[: n + 1].copy(), pref[:n].copy()

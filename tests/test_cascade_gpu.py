@@ -160,3 +160,31 @@ def test_cascade_rejects_bad_groups(gpu_lib):
     lay3 = dataclasses.replace(lay, prefix_lens=bad)
     with pytest.raises(gpu_lib.PAError):
         run_cascade(gpu_lib, lay3, q, k, v)
+
+
+def test_detected_groups_drive_the_cascade(gpu_lib):
+    """End to end: a shared-prefix batch in shuffled order (no group
+    structure given), groups found by pa_detect_prefix_groups, the batch
+    taken in that order through pa_prefix_cascade, the outputs put back;
+    they must match the oracle's plain decode of the shuffled batch."""
+    import dataclasses
+
+    base = cascade_layout(num_groups=5, seqs_per_group=12, prefix_len=256, suffix_lo=1, suffix_hi=200,
+                          num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16", seed=21)
+    perm = np.random.default_rng(8).permutation(base.num_seqs)
+    qh, kh, vh = values_numpy(base)
+    qh = qh[perm]
+    bt, ctx = base.block_tables[perm], base.context_lens[perm]
+    say("case cascade over detected groups, 5 x 12 shuffled")
+    order, offs, pref = gpu_lib.detect_prefix_groups(bt, ctx)
+    assert len(pref) == 5 and (pref == 256).all()
+    lay = dataclasses.replace(base, block_tables=bt[order], context_lens=ctx[order], group_seq_offsets=offs,
+                              prefix_lens=pref)
+    q, k, v = to_device_values(lay, qh[order], kh, vh)
+    out, lse = run_cascade(gpu_lib, lay, q, k, v)
+    back = np.empty_like(order)
+    back[order] = np.arange(len(order))
+    got = out_to_f64(out)[back]
+    ro, rl = oracle.decode(qh, kh, vh, bt, ctx, base.scale, base.num_kv_heads, 16, "bf16")
+    assert_close(lay, got, ro, "cascade over detected groups")
+    assert np.abs(lse.cpu().numpy()[back] - rl).max() < LSE_TOL_MFMA_BF16

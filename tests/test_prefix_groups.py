@@ -1,0 +1,48 @@
+"""pa_detect_prefix_groups (native, host only) against the oracle's greedy
+search: identical groups, order and prefixes."""
+
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_decode_02_amd import pa
+from test_prefix_groups_pins import nested_tables
+from workloads import workload
+
+
+@pytest.mark.parametrize("seed", range(20))
+@pytest.mark.parametrize("mg,mp", [(2, 1), (3, 1), (2, 3), (8, 1)])
+def test_matches_the_oracle_on_nested_layouts(seed, mg, mp):
+    bt, ctx = nested_tables(np.random.default_rng(1000 + seed), S=80)
+    got = pa.detect_prefix_groups(bt, ctx, 16, mg, mp)
+    want = oracle.detect_prefix_groups(bt, ctx, 16, mg, mp)
+    for g, w, name in zip(got, want, ("order", "offsets", "prefix_lens")):
+        assert np.array_equal(g, w), name
+
+
+def test_shuffled_shared_prefix_workload():
+    lay = workload("shared_prefix")
+    perm = np.random.default_rng(4).permutation(lay.num_seqs)
+    bt, ctx = lay.block_tables[perm], lay.context_lens[perm]
+    order, offs, pref = pa.detect_prefix_groups(bt, ctx)
+    want = oracle.detect_prefix_groups(bt, ctx, 16)
+    assert all(np.array_equal(a, b) for a, b in zip((order, offs, pref), want))
+    assert len(pref) == 16 and (pref == 2048).all() and (np.diff(offs) == 64).all()
+    # the reordered batch is a valid cascade grouping
+    assert pa.check_block_tables(bt[order], ctx[order], lay.num_pages, 16, offs, pref) == pa.PA_OK
+
+
+def test_no_sharing_gives_one_prefix_zero_group():
+    bt = np.arange(12, dtype=np.int32).reshape(4, 3)
+    ctx = np.array([40, 33, 17, 48], dtype=np.int32)
+    order, offs, pref = pa.detect_prefix_groups(bt, ctx)
+    assert order.tolist() == [0, 1, 2, 3] and offs.tolist() == [0, 4] and pref.tolist() == [0]
+
+
+def test_bad_arguments():
+    bt = np.zeros((2, 2), dtype=np.int32)
+    with pytest.raises(pa.PAError):
+        pa.detect_prefix_groups(bt, np.array([0, 5], dtype=np.int32))
+    with pytest.raises(pa.PAError):
+        pa.detect_prefix_groups(bt, np.array([33, 5], dtype=np.int32))  # beyond 2 pages
+    assert [x.size for x in pa.detect_prefix_groups(np.zeros((0, 1), np.int32), np.zeros(0, np.int32))] == [0, 1, 0]
