@@ -36,7 +36,11 @@ Pins (tests/test_fp8_pins.py):
   values, and the result equals the (pinned) bf16 attention oracle on those
   values bit for bit; brute force on tiny inputs with Python loops;
 * planted mistakes (scale ignored, K scale used for V, FNUZ bias 8) are each
-  caught.
+  caught;
+* the quantising append (``kv_append_fp8``: quantise each new row, then
+  place codes and scale as ``oracle.kv_append`` places a row) against a
+  brute-force element loop, and its read-back against the new rows within
+  half a code step.
 """
 
 from __future__ import annotations
@@ -158,3 +162,26 @@ def decode_fp8(q, k_codes, k_scales, v_codes, v_scales, block_tables, context_le
             for h in range(g * G, (g + 1) * G):
                 out[s, h], lse[s, h] = attend(qs[h], K, V, sc)
     return out, lse
+
+
+def kv_append_fp8(k_codes, k_scales, v_codes, v_scales, k_new, v_new, block_tables, context_lens, q_lens,
+                  block_size, new_dtype="bf16"):
+    """KV append into an fp8 cache: each new K and V row of each kv-head is
+    quantised on its own (the token-group recipe above, group = the row) and
+    its codes and scale are written where ``oracle.kv_append`` writes a row.
+
+    ``k_new``, ``v_new``: [T, Hkv, D] stored values of ``new_dtype`` (bf16
+    bit patterns or float32), widened exactly to float32 before the
+    quantiser.  Returns new (k_codes, k_scales, v_codes, v_scales).
+    """
+    from .attention import stored_to_f64
+    from .kv_append import kv_append
+
+    kx = stored_to_f64(k_new, new_dtype).astype(np.float32)
+    vx = stored_to_f64(v_new, new_dtype).astype(np.float32)
+    kc_new, ks_new = quantize_rows(kx)
+    vc_new, vs_new = quantize_rows(vx)
+    kc, vc = kv_append(k_codes, v_codes, kc_new, vc_new, block_tables, context_lens, q_lens, block_size)
+    ks, vs = kv_append(np.asarray(k_scales)[..., None], np.asarray(v_scales)[..., None], ks_new[..., None],
+                       vs_new[..., None], block_tables, context_lens, q_lens, block_size)
+    return kc, ks[..., 0], vc, vs[..., 0]

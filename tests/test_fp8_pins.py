@@ -272,3 +272,58 @@ def test_planted_v_scale_swap_is_caught(monkeypatch):
 
     monkeypatch.setattr(f8, "decode_fp8", swapped)
     assert _run_pins(), "no pin noticed the K scale used for V"
+
+
+def test_kv_append_fp8_bruteforce_and_read_back():
+    """Tiny mixed batch: every new row's codes and scale, found by a Python
+    loop over tokens and kv-heads (torch's recipe for the codes), sit at its
+    row of its page; every other row keeps its bits; reading the written
+    rows back is within half a code step of the new values."""
+    from workloads import mixed_layout
+
+    lay = mixed_layout(chunk_prefixes=[0, 7], chunk_len=9, decode_ctx=[1, 16, 17, 40], num_q_heads=4,
+                       num_kv_heads=2, head_dim=16, dtype="bf16", name="append_fp8")
+    rng = np.random.default_rng(2)
+    npg, hkv, bs, d = lay.num_pages, 2, 16, 16
+    kc = rng.integers(0, 126, size=(npg, hkv, bs, d)).astype(np.uint8)
+    vc = rng.integers(0, 126, size=(npg, hkv, bs, d)).astype(np.uint8)
+    ks = rng.uniform(0.1, 1, size=(npg, hkv, bs)).astype(np.float32)
+    vs = rng.uniform(0.1, 1, size=(npg, hkv, bs)).astype(np.float32)
+    T = lay.num_tokens
+    kn = bf16_bits_from_f32((rng.standard_normal((T, hkv, d)) * 3).astype(np.float32))
+    vn = bf16_bits_from_f32((rng.standard_normal((T, hkv, d)) * 0.01).astype(np.float32))
+    got = f8.kv_append_fp8(kc, ks, vc, vs, kn, vn, lay.block_tables, lay.context_lens, lay.q_lens, 16, "bf16")
+    want = [kc.copy(), ks.copy(), vc.copy(), vs.copy()]
+    touched = set()
+    t = 0
+    for s in range(lay.num_seqs):
+        L, n = int(lay.context_lens[s]), int(lay.q_lens[s])
+        for i in range(n):
+            pos = L - n + i
+            p, r = int(lay.block_tables[s, pos // 16]), pos % 16
+            touched.add((p, r))
+            for g in range(hkv):
+                for new, ci, si in ((kn, 0, 1), (vn, 2, 3)):
+                    row = oracle.stored_to_f64(new[t + i, g], "bf16").astype(np.float32)
+                    codes, scale = torch_quantize(row[None, :])
+                    want[ci][p, g, r] = codes[0]
+                    want[si][p, g, r] = scale[0]
+        t += n
+    for a, b in zip(got, want):
+        assert np.array_equal(a, b)
+    # read-back of the written rows: within half a code step of the new value
+    t = 0
+    for s in range(lay.num_seqs):
+        L, n = int(lay.context_lens[s]), int(lay.q_lens[s])
+        for i in range(n):
+            pos = L - n + i
+            p, r = int(lay.block_tables[s, pos // 16]), pos % 16
+            for g in range(hkv):
+                for new, ci, si in ((kn, 0, 1), (vn, 2, 3)):
+                    x = oracle.stored_to_f64(new[t + i, g], "bf16")
+                    sc = float(got[si][p, g, r])
+                    back = f8.dequantize(got[ci][p, g, r][None], got[si][p, g, r][None])[0]
+                    y = np.abs(x) / sc
+                    step = 2.0 ** (np.floor(np.log2(np.maximum(y, 2.0 ** -6))) - 3)
+                    assert np.all(np.abs(back - x) <= (step / 2 + y * 2.0 ** -24) * sc * (1 + 1e-12))
+        t += n
