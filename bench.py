@@ -168,12 +168,16 @@ def bench_append(args):
     import torch
 
     from paged_kv_decode_02_amd import pa, roofline
-    from workloads import new_rows_torch, values_torch, workload
+    from workloads import fp8_values_torch, new_rows_torch, values_torch, workload
 
     lay = workload(args.workload, seed=args.seed)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    _, k, v = values_torch(lay, dev)
+    fp8 = lay.kv_dtype == "fp8"
+    if fp8:
+        _, k, ks, v, vs = fp8_values_torch(lay, dev)
+    else:
+        _, k, v = values_torch(lay, dev)
     kn, vn = new_rows_torch(lay, dev)
     bt = torch.from_numpy(lay.block_tables).to(dev)
     ctx = torch.from_numpy(lay.context_lens).to(dev)
@@ -182,7 +186,10 @@ def bench_append(args):
     T = lay.num_tokens
 
     def step():
-        pa.kv_append(k, v, kn, vn, bt, cu, lay.cu_q_lens, ctx, lay.context_lens, stream=stream)
+        if fp8:
+            pa.kv_append_fp8(k, v, ks, vs, kn, vn, bt, cu, lay.cu_q_lens, ctx, lay.context_lens, stream=stream)
+        else:
+            pa.kv_append(k, v, kn, vn, bt, cu, lay.cu_q_lens, ctx, lay.context_lens, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -200,17 +207,22 @@ def bench_append(args):
     torch.cuda.synchronize()
     kern = float(np.mean(pa.profile_collect(args.steps)))
     pa.profile_enable(0)
-    rows = 2 * 2 * T * lay.num_kv_heads * lay.head_dim * lay.elem_bytes
+    # new K and V rows read once and written once (fp8: codes plus a float32
+    # scale per row written)
+    rows = 2 * T * lay.num_kv_heads * lay.head_dim * lay.elem_bytes
+    rows += 2 * T * lay.num_kv_heads * (lay.head_dim + 4) if fp8 else rows
     nbytes = rows + 4 * (lay.num_seqs + 1) + 4 * lay.num_seqs + 4 * T
     achieved = nbytes / (kern * 1e-3) / 1e9
     print(json.dumps({
         "metric": "paged KV append GB/s (new K/V rows into the pool)", "value": round(nbytes / (ms * 1e-3) / 1e9, 1),
         "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": lay.dtype, "data": "synthetic",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": f"{lay.dtype} rows -> fp8 e4m3fn cache" if fp8 else lay.dtype, "data": "synthetic",
         "config": {"workload": args.workload, "op": "append", "new_tokens": int(T), "kv_heads": lay.num_kv_heads,
                    "head_dim": lay.head_dim, "block_size": 16, "seed": args.seed},
         "algorithmic_bytes_per_step": int(nbytes),
-        "roofline": {"bound": "hbm", "kernel": "kv_append_kernel", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": "kv_append_fp8_kernel" if fp8 else "kv_append_kernel",
+                     "achieved": round(achieved, 1),
                      "peak": roofline.HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / roofline.HBM_PEAK_GBS, 4),
                      "kernel_ms": round(kern, 5),
                      "traffic": measured_traffic("append:" + args.workload, APPEND_SOURCES)},

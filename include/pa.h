@@ -286,6 +286,30 @@ int pa_kv_append(void* k_pool, void* v_pool,        /* device [NP, Hkv, BS, D] d
                  int64_t num_pages, pa_dtype dtype, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * KV append into an fp8 cache: pa_kv_append's placement (segments, rows,
+ * table entries outside the pool not written through), with each new K row
+ * and each new V row of each kv-head quantised on its own by the
+ * token-group FP8 recipe of the tokenspeed 딥다이브 page (section 6-4):
+ *   scale = max(max_d |x_d|, 1e-10) / 448,
+ *   code_d = e4m3fn(clamp(x_d / scale, -448, 448)),
+ * in float32 with correctly rounded division, rounding to the nearest
+ * e4m3fn value (ties to even).  The codes go to the row of k_pool / v_pool
+ * and the scale to the same (page, kv-head, slot) of k_scales / v_scales --
+ * the layout pa_decode_fp8 reads.
+ *
+ *  k_pool, v_pool     [NP, Hkv, 16, D] uint8 codes, updated in place
+ *  k_scales, v_scales [NP, Hkv, 16] float32, updated in place
+ *  k_new, v_new       [T, Hkv, D] new_dtype (PA_BF16 or PA_F32)
+ * head_dim 64 or 128; errors as pa_kv_append (PA_EINVAL also for a NULL
+ * scale pointer).
+ * ------------------------------------------------------------------------- */
+int pa_kv_append_fp8(void* k_pool, void* v_pool, float* k_scales, float* v_scales, const void* k_new,
+                     const void* v_new, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* cu_q_lens, const int32_t* cu_q_lens_host, const int32_t* context_lens,
+                     const int32_t* context_lens_host, int32_t num_segments, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t block_size, int64_t num_pages, pa_dtype new_dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Host-side table check (host copies only, no device access).
  * Every sequence needs ceil(L/block_size) entries in [0, num_pages); a page
  * may appear in more than one table only as a declared shared prefix: for

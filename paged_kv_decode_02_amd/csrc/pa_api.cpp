@@ -368,6 +368,28 @@ extern "C" int pa_mixed_chunk(void* out, float* lse_out, const void* q, const vo
   return launch_mixed(m);
 }
 
+namespace {
+
+// Segments and lengths of a KV append: cu_q_lens[0] = 0, no segment adds a
+// negative count, every context holds its new tokens and fits its table.
+int check_append_segments(const int32_t* cu_q_lens_host, const int32_t* context_lens_host, int32_t num_segments,
+                          int32_t max_blocks, int32_t block_size, const char* who) {
+  const std::string w(who);
+  if (cu_q_lens_host[0] != 0) return fail(PA_EINVAL, w + ": cu_q_lens[0] != 0");
+  for (int32_t s = 0; s < num_segments; ++s) {
+    const int64_t n = static_cast<int64_t>(cu_q_lens_host[s + 1]) - cu_q_lens_host[s];
+    const int64_t L = context_lens_host[s];
+    const std::string at = "[" + std::to_string(s) + "]";
+    if (n < 0) return fail(PA_EINVAL, w + ": cu_q_lens decreases at segment" + at);
+    if (L < n) return fail(PA_EINVAL, w + ": context_lens" + at + " is shorter than its new tokens");
+    if (L > static_cast<int64_t>(max_blocks) * block_size)
+      return fail(PA_EINVAL, w + ": context_lens" + at + " exceeds the block table");
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
 extern "C" int pa_kv_append(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
                             const int32_t* block_tables, int32_t max_blocks, const int32_t* cu_q_lens,
                             const int32_t* cu_q_lens_host, const int32_t* context_lens,
@@ -388,16 +410,9 @@ extern "C" int pa_kv_append(void* k_pool, void* v_pool, const void* k_new, const
     return fail(PA_EUNSUPPORTED, "pa_kv_append: head_dim * element size must be a multiple of 16 bytes, at most " +
                                      std::to_string(kMaxAppendRowBytes));
   if (num_pages > (int64_t(1) << 31) - 1) return fail(PA_EUNSUPPORTED, "pa_kv_append: num_pages above 2^31-1");
-  if (cu_q_lens_host[0] != 0) return fail(PA_EINVAL, "pa_kv_append: cu_q_lens[0] != 0");
-  for (int32_t s = 0; s < num_segments; ++s) {
-    const int64_t n = static_cast<int64_t>(cu_q_lens_host[s + 1]) - cu_q_lens_host[s];
-    const int64_t L = context_lens_host[s];
-    const std::string at = "[" + std::to_string(s) + "]";
-    if (n < 0) return fail(PA_EINVAL, "pa_kv_append: cu_q_lens decreases at segment" + at);
-    if (L < n) return fail(PA_EINVAL, "pa_kv_append: context_lens" + at + " is shorter than its new tokens");
-    if (L > static_cast<int64_t>(max_blocks) * block_size)
-      return fail(PA_EINVAL, "pa_kv_append: context_lens" + at + " exceeds the block table");
-  }
+  if (int rc = check_append_segments(cu_q_lens_host, context_lens_host, num_segments, max_blocks, block_size,
+                                     "pa_kv_append"))
+    return rc;
   const int64_t tokens = cu_q_lens_host[num_segments];
   if (tokens == 0) return PA_OK;
   AppendLaunch a;
@@ -416,4 +431,48 @@ extern "C" int pa_kv_append(void* k_pool, void* v_pool, const void* k_new, const
   a.num_pages = num_pages;
   a.stream = stream;
   return launch_append(a);
+}
+
+extern "C" int pa_kv_append_fp8(void* k_pool, void* v_pool, float* k_scales, float* v_scales, const void* k_new,
+                                const void* v_new, const int32_t* block_tables, int32_t max_blocks,
+                                const int32_t* cu_q_lens, const int32_t* cu_q_lens_host, const int32_t* context_lens,
+                                const int32_t* context_lens_host, int32_t num_segments, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int64_t num_pages, pa_dtype new_dtype,
+                                void* stream) {
+  clear_error();
+  if (num_segments < 0) return fail(PA_EINVAL, "pa_kv_append_fp8: num_segments < 0");
+  if (num_segments == 0) return PA_OK;
+  if (!k_pool || !v_pool || !k_scales || !v_scales || !k_new || !v_new || !block_tables || !cu_q_lens ||
+      !cu_q_lens_host || !context_lens || !context_lens_host)
+    return fail(PA_EINVAL, "pa_kv_append_fp8: null pointer argument");
+  if (max_blocks < 1 || num_kv_heads < 1 || head_dim < 1 || num_pages < 1)
+    return fail(PA_EINVAL, "pa_kv_append_fp8: sizes must be >= 1");
+  if (new_dtype != PA_F32 && new_dtype != PA_BF16) return fail(PA_EUNSUPPORTED, "pa_kv_append_fp8: unknown dtype");
+  if (block_size != kBlockSize) return fail(PA_EUNSUPPORTED, "pa_kv_append_fp8: only block_size 16 is built");
+  if (head_dim != 64 && head_dim != 128) return fail(PA_EUNSUPPORTED, "pa_kv_append_fp8: head_dim must be 64 or 128");
+  if (num_pages > (int64_t(1) << 31) - 1) return fail(PA_EUNSUPPORTED, "pa_kv_append_fp8: num_pages above 2^31-1");
+  if (int rc = check_append_segments(cu_q_lens_host, context_lens_host, num_segments, max_blocks, block_size,
+                                     "pa_kv_append_fp8"))
+    return rc;
+  const int64_t tokens = cu_q_lens_host[num_segments];
+  if (tokens == 0) return PA_OK;
+  AppendFp8Launch a;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.new_dtype = new_dtype;
+  a.block_tables = block_tables;
+  a.max_blocks = max_blocks;
+  a.cu_q_lens = cu_q_lens;
+  a.context_lens = context_lens;
+  a.num_segments = num_segments;
+  a.num_tokens = tokens;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.num_pages = num_pages;
+  a.stream = stream;
+  return launch_append_fp8(a);
 }

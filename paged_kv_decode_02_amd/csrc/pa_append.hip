@@ -91,7 +91,124 @@ __global__ __launch_bounds__(64 * kTokensPerBlock) void kv_append_kernel(
   }
 }
 
+// max over the 16 lanes of a DPP row (each lane gets it)
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  v = fmaxf(v, dpp<kDppXor2>(v));
+  v = fmaxf(v, dpp<kDppRor4>(v));
+  return fmaxf(v, dpp<kDppRor8>(v));
+}
+
+// KV append into an fp8 cache: one wave per new token; its 2 x Hkv rows (K
+// and V of every kv-head) are each quantised on their own -- scale =
+// max(max |x|, 1e-10) / 448, codes = e4m3(clamp(x / scale, -448, 448)), all
+// float32 with correctly rounded division (the token-group FP8 recipe of the
+// tokenspeed deep-dive, section 6-4, with a group = one row) -- and written
+// with their scale to the row's page and slot.  Four rows at a time: lanes
+// 16 r .. 16 r + 15 take row r, lane c of them elements c * EPL .. +EPL.
+template <typename TN, int D>
+__global__ __launch_bounds__(64 * kTokensPerBlock) void kv_append_fp8_kernel(
+    uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool, float* __restrict__ k_scales,
+    float* __restrict__ v_scales, const TN* __restrict__ k_new, const TN* __restrict__ v_new,
+    const int32_t* __restrict__ block_tables, int max_blocks, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ ctx, int S, int T, int Hkv, int num_pages) {
+  constexpr int EPL = D / 16;  // elements per lane: 8 (D = 128) or 4 (D = 64)
+  const int lane = lane_id();
+  const int t = static_cast<int>(blockIdx.x) * kTokensPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (t >= T) return;
+  const int s = __builtin_amdgcn_readfirstlane(segment_of(cu, S, t));
+  const int c0 = cu[s];
+  const int n = cu[s + 1] - c0;
+  const int pos = ctx[s] - n + (t - c0);
+  if (pos < 0 || pos >= static_cast<int64_t>(max_blocks) * kBlockSize) return;
+  const int pid = block_tables[static_cast<int64_t>(s) * max_blocks + (pos / kBlockSize)];
+  if (pid < 0 || pid >= num_pages) return;
+  const int slot = pos % kBlockSize;
+  const int r = lane >> 4;  // row of the four this lane works on
+  const int c = lane & 15;  // its piece of the row
+  for (int r0 = 0; r0 < 2 * Hkv; r0 += 4) {
+    const int ri = r0 + r;  // rows 0 .. Hkv-1: K of kv-head ri; Hkv .. 2 Hkv-1: V
+    const bool live = ri < 2 * Hkv;
+    const int kv = live && ri >= Hkv ? 1 : 0;
+    const int g = live ? ri - kv * Hkv : 0;
+    const TN* nw = kv ? v_new : k_new;
+    const int64_t src = (static_cast<int64_t>(t) * Hkv + g) * D + c * EPL;
+    float x[EPL];
+    if constexpr (sizeof(TN) == 2) {
+      uint32_t w[EPL / 2];
+      if constexpr (EPL == 8) {
+        const uint4 u = *reinterpret_cast<const uint4*>(nw + src);
+        w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
+      } else {
+        const uint2 u = *reinterpret_cast<const uint2*>(nw + src);
+        w[0] = u.x; w[1] = u.y;
+      }
+#pragma unroll
+      for (int e = 0; e < EPL / 2; ++e) {
+        x[2 * e] = bf16_lo(w[e]);
+        x[2 * e + 1] = bf16_hi(w[e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; e += 4) {
+        const float4 f = *reinterpret_cast<const float4*>(nw + src + e);
+        x[e] = f.x; x[e + 1] = f.y; x[e + 2] = f.z; x[e + 3] = f.w;
+      }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    amax = row16_max(amax);
+    const float scale = fmaxf(amax, 1e-10f) / 448.0f;
+    // codes, four per word: v_cvt_pk_fp8_f32 rounds to the nearest e4m3fn
+    // value, ties to even, subnormals included (values are in range after
+    // the clamp)
+    uint32_t code[EPL / 4];
+#pragma unroll
+    for (int e4 = 0; e4 < EPL / 4; ++e4) {
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = fminf(fmaxf(x[4 * e4 + e] / scale, -448.0f), 448.0f);
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], word, true);
+      code[e4] = static_cast<uint32_t>(word);
+    }
+    if (live) {
+      const int64_t row = (static_cast<int64_t>(pid) * Hkv + g) * kBlockSize + slot;
+      uint8_t* dst = (kv ? v_pool : k_pool) + row * D + c * EPL;
+      if constexpr (EPL == 8)
+        *reinterpret_cast<uint2*>(dst) = make_uint2(code[0], code[1]);
+      else
+        *reinterpret_cast<uint32_t*>(dst) = code[0];
+      if (c == 0) (kv ? v_scales : k_scales)[row] = scale;
+    }
+  }
+}
+
 }  // namespace
+
+int launch_append_fp8(const AppendFp8Launch& a) {
+  if (a.num_tokens > 0x7fffffffLL - kTokensPerBlock)
+    return fail(PA_EUNSUPPORTED, "pa_kv_append_fp8: too many tokens");
+  hipStream_t st = static_cast<hipStream_t>(a.stream);
+  const unsigned blocks = static_cast<unsigned>((a.num_tokens + kTokensPerBlock - 1) / kTokensPerBlock);
+  profile_before(a.stream);
+#define PA_APPEND_FP8(TN, D)                                                                                         \
+  hipLaunchKernelGGL((kv_append_fp8_kernel<TN, D>), dim3(blocks), dim3(64 * kTokensPerBlock), 0, st,                  \
+                     static_cast<uint8_t*>(a.k_pool), static_cast<uint8_t*>(a.v_pool), a.k_scales, a.v_scales,      \
+                     static_cast<const TN*>(a.k_new), static_cast<const TN*>(a.v_new), a.block_tables, a.max_blocks, \
+                     a.cu_q_lens, a.context_lens, a.num_segments, static_cast<int>(a.num_tokens), a.num_kv_heads,   \
+                     static_cast<int>(a.num_pages))
+  if (a.new_dtype == PA_BF16 && a.head_dim == 128) PA_APPEND_FP8(uint16_t, 128);
+  else if (a.new_dtype == PA_BF16 && a.head_dim == 64) PA_APPEND_FP8(uint16_t, 64);
+  else if (a.new_dtype == PA_F32 && a.head_dim == 128) PA_APPEND_FP8(float, 128);
+  else if (a.new_dtype == PA_F32 && a.head_dim == 64) PA_APPEND_FP8(float, 64);
+  else return fail(PA_EUNSUPPORTED, "pa_kv_append_fp8: head_dim must be 64 or 128");
+#undef PA_APPEND_FP8
+  profile_after(a.stream);
+  if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_kv_append_fp8: launch failed");
+  return PA_OK;
+}
 
 int launch_append(const AppendLaunch& a) {
   if (a.num_tokens > 0x7fffffffLL - kTokensPerBlock) return fail(PA_EUNSUPPORTED, "pa_kv_append: too many tokens");

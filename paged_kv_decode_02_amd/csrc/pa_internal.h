@@ -187,6 +187,28 @@ struct AppendLaunch {
 };
 int launch_append(const AppendLaunch& a);
 
+// KV append into an fp8 cache (codes + one float32 scale per row).
+struct AppendFp8Launch {
+  void* k_pool;  // [NP, Hkv, 16, D] e4m3fn codes
+  void* v_pool;
+  float* k_scales;  // [NP, Hkv, 16]
+  float* v_scales;
+  const void* k_new;  // [T, Hkv, D] new_dtype
+  const void* v_new;
+  pa_dtype new_dtype;
+  const int32_t* block_tables;
+  int32_t max_blocks;
+  const int32_t* cu_q_lens;     // device [S+1]
+  const int32_t* context_lens;  // device [S]
+  int32_t num_segments;
+  int64_t num_tokens;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int64_t num_pages;
+  void* stream;
+};
+int launch_append_fp8(const AppendFp8Launch& a);
+
 // Profiling hook: bracket the dominant kernel of a call.
 void profile_before(void* stream);
 void profile_after(void* stream);

@@ -37,6 +37,7 @@ EXPORTS = (
     "pa_mixed_chunk_workspace_size",
     "pa_mixed_chunk",
     "pa_kv_append",
+    "pa_kv_append_fp8",
     "pa_check_block_tables",
     "pa_detect_prefix_groups",
     "pa_last_error",
@@ -95,6 +96,9 @@ def load(path: Optional[str] = None):
                                  c_i32, c_i64, ctypes.c_int, c_vp]
     lib.pa_detect_prefix_groups.restype = ctypes.c_int
     lib.pa_detect_prefix_groups.argtypes = [c_vp, c_i32, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]
+    lib.pa_kv_append_fp8.restype = ctypes.c_int
+    lib.pa_kv_append_fp8.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_i32,
+                                     c_i32, c_i32, c_i32, c_i64, ctypes.c_int, c_vp]
     lib.pa_check_block_tables.restype = ctypes.c_int
     lib.pa_check_block_tables.argtypes = [c_vp, c_i32, c_vp, c_i32, c_i32, c_i64, c_i32, c_vp, c_vp]
     lib.pa_last_error.restype = ctypes.c_char_p
@@ -459,3 +463,45 @@ def detect_prefix_groups(block_tables, context_lens, block_size=16, min_group=2,
     _check(rc)
     n = ng.value
     return order, offs[: n + 1].copy(), pref[:n].copy()
+
+
+def kv_append_fp8(k_pool, v_pool, k_scales, v_scales, k_new, v_new, block_tables, cu_q_lens, cu_q_lens_host,
+                  context_lens, context_lens_host, stream=None):
+    """pa_kv_append_fp8 on torch tensors: the new rows quantised into an fp8
+    cache, in place.
+
+    k_pool, v_pool: [NP, Hkv, 16, D] uint8 (or float8_e4m3fn); k_scales,
+    v_scales: [NP, Hkv, 16] float32; k_new, v_new: [T, Hkv, D] bfloat16 or
+    float32; the rest as :func:`kv_append`.
+    """
+    import torch
+
+    NP, Hkv, BS, D = k_pool.shape
+    T = k_new.shape[0]
+    codes = (torch.uint8, torch.float8_e4m3fn)
+    if tuple(v_pool.shape) != tuple(k_pool.shape) or k_pool.dtype not in codes or v_pool.dtype not in codes:
+        raise ValueError("k_pool and v_pool must be [NP, Hkv, BS, D] uint8 / float8_e4m3fn")
+    for t, nm in ((k_scales, "k_scales"), (v_scales, "v_scales")):
+        if tuple(t.shape) != (NP, Hkv, BS) or t.dtype != torch.float32:
+            raise ValueError(f"{nm} must be float32 [NP, Hkv, BS]")
+    if tuple(k_new.shape) != (T, Hkv, D) or tuple(v_new.shape) != (T, Hkv, D) or k_new.dtype != v_new.dtype:
+        raise ValueError("k_new and v_new must be [T, Hkv, D] of one dtype")
+    if k_new.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("new rows must be bfloat16 or float32")
+    cq = _host_i32(cu_q_lens_host, "cu_q_lens_host")
+    ch = _host_i32(context_lens_host, "context_lens_host")
+    S = ch.size
+    if cq.size != S + 1 or cu_q_lens.numel() != S + 1 or context_lens.numel() != S:
+        raise ValueError("cu_q_lens must have one entry more than context_lens")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must have one row per segment")
+    if S and int(cq[-1]) != T:
+        raise ValueError("k_new must have cu_q_lens[-1] rows")
+    rc = load().pa_kv_append_fp8(
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(k_scales, "k_scales", torch.float32),
+        _dev(v_scales, "v_scales", torch.float32), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(cu_q_lens, "cu_q_lens", torch.int32), cq.ctypes.data, _dev(context_lens, "context_lens", torch.int32),
+        ch.ctypes.data, S, Hkv, D, BS, NP, _dtype_code(k_new), _stream_ptr(stream),
+    )
+    return _check(rc)

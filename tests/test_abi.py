@@ -272,3 +272,41 @@ def test_append_with_nothing_to_write_is_a_no_op():
     assert call_append(lib, S=0, k=None, kn=None) == pa.PA_OK
     # segments that add no token: validated, then no launch
     assert call_append(lib, cu_host=np.array([0, 0, 0], dtype=np.int32)) == pa.PA_OK
+
+
+def call_append_fp8(lib, **kw):
+    args = dict(k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, kn=FAKE, vn=FAKE, bt=FAKE, mb=4, cu=FAKE, cu_host=None, ctx=FAKE,
+                ctx_host=None, S=2, Hkv=2, D=128, BS=16, NP=10, dtype=pa.PA_BF16, stream=None)
+    args.update(kw)
+    cu = args["cu_host"] if args["cu_host"] is not None else np.array([0, 5, 6], dtype=np.int32)
+    ch = args["ctx_host"] if args["ctx_host"] is not None else np.array([20, 40], dtype=np.int32)
+    return lib.pa_kv_append_fp8(args["k"], args["v"], args["ks"], args["vs"], args["kn"], args["vn"], args["bt"],
+                                args["mb"], args["cu"], cu.ctypes.data, args["ctx"], ch.ctypes.data, args["S"],
+                                args["Hkv"], args["D"], args["BS"], args["NP"], args["dtype"], args["stream"])
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(ks=None), pa.PA_EINVAL),
+        (dict(vs=None), pa.PA_EINVAL),
+        (dict(kn=None), pa.PA_EINVAL),
+        (dict(cu_host=np.array([1, 5, 6], dtype=np.int32)), pa.PA_EINVAL),
+        (dict(cu_host=np.array([0, 21, 22], dtype=np.int32)), pa.PA_EINVAL),
+        (dict(ctx_host=np.array([20, 65], dtype=np.int32)), pa.PA_EINVAL),
+        (dict(D=96), pa.PA_EUNSUPPORTED),
+        (dict(dtype=7), pa.PA_EUNSUPPORTED),
+        (dict(BS=8), pa.PA_EUNSUPPORTED),
+        (dict(S=-1), pa.PA_EINVAL),
+    ],
+)
+def test_append_fp8_rejects_bad_arguments(kw, code):
+    lib = pa.load()
+    assert call_append_fp8(lib, **kw) == code
+    assert lib.pa_last_error().decode().startswith("pa_kv_append_fp8")
+
+
+def test_append_fp8_with_nothing_to_write_is_a_no_op():
+    lib = pa.load()
+    assert call_append_fp8(lib, S=0, k=None) == pa.PA_OK
+    assert call_append_fp8(lib, cu_host=np.array([0, 0, 0], dtype=np.int32)) == pa.PA_OK

@@ -444,8 +444,17 @@ def _longtail_window4096(seed=0):
                          head_dim=base.head_dim, dtype=base.dtype, seed=seed, name="longtail_window4096")
 
 
+def _llama8b_prefill_append_fp8(seed=0):
+    """The whole-prefill append, quantised into an fp8 cache."""
+    lay = _llama8b_prefill_append(seed)
+    lay.name = "llama8b_prefill_append_fp8"
+    lay.kv_dtype = "fp8"
+    return lay
+
+
 WORKLOADS = {
     "tiny_f32": _tiny_f32,
+    "llama8b_prefill_append_fp8": _llama8b_prefill_append_fp8,
     "longtail_window4096": _longtail_window4096,
     "llama8b_prefill_append": _llama8b_prefill_append,
     "llama8b_decode": _llama8b_decode,
