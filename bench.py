@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--split-pages", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--via-mixed", action="store_true",
+                    help="multi-token batches (every sequence the same q_len > 1) through pa_mixed_chunk "
+                         "instead of pa_decode_multi")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (calibrates HBM traffic counters)")
     return ap.parse_args()
@@ -249,6 +252,12 @@ def main():
     lay = workload(args.workload, seed=args.seed)
     cascade = lay.group_seq_offsets is not None
     mixed = lay.q_lens.max() > 1
+    # every sequence the same number of new tokens (> 1): a multi-token
+    # decode step, through pa_decode_multi unless asked otherwise
+    multi = bool(mixed and (lay.q_lens == lay.q_lens[0]).all() and not args.via_mixed)
+    if multi:
+        mixed = False
+        n_tok = int(lay.q_lens[0])
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] workload {args.workload} seed {args.seed}: drawing inputs on the device", file=sys.stderr,
@@ -274,13 +283,23 @@ def main():
         def step():
             pa.prefix_cascade(out, q, k, v, bt, ctx, lay.context_lens, go, lay.group_seq_offsets, pl,
                               lay.prefix_lens, lay.scale, ws, stream=stream)
-    elif mixed:
+    elif mixed or multi:
         cu = torch.from_numpy(lay.cu_q_lens.astype(np.int32)).to(dev)
-        ws = torch.empty(pa.mixed_chunk_workspace_size(T, S, lay.num_kv_heads, lay.gqa_ratio, D, total_pages),
-                         dtype=torch.uint8, device=dev)
+        mws = torch.empty(pa.mixed_chunk_workspace_size(T, S, lay.num_kv_heads, lay.gqa_ratio, D, total_pages),
+                          dtype=torch.uint8, device=dev)
 
-        def step():
-            pa.mixed_chunk(out, q, k, v, bt, cu, lay.cu_q_lens, ctx, lay.context_lens, lay.scale, ws, stream=stream)
+        def mixed_step():
+            pa.mixed_chunk(out, q, k, v, bt, cu, lay.cu_q_lens, ctx, lay.context_lens, lay.scale, mws,
+                           stream=stream)
+
+        step = mixed_step
+        if multi:
+            ws = torch.empty(pa.decode_multi_workspace_size(S, n_tok, lay.num_kv_heads, lay.gqa_ratio, D, total_pages,
+                                                            args.split_pages), dtype=torch.uint8, device=dev)
+
+            def step():
+                pa.decode_multi(out, q, k, v, bt, ctx, lay.context_lens, lay.scale, n_tok, ws,
+                                split_pages=args.split_pages, stream=stream)
     else:
         ws = torch.empty(pa.decode_workspace_size(S, lay.num_kv_heads, lay.gqa_ratio, D, total_pages,
                                                   args.split_pages), dtype=torch.uint8, device=dev)
@@ -317,7 +336,12 @@ def main():
     # Dominant kernel(s) alone: HIP events the library records around them
     # on the same stream (decode: the stream kernel; cascade: the prefix
     # kernel; mixed: the chunk kernel, then the decode stream kernel).
-    pairs = 2 if mixed else 1
+    has_dec = bool((lay.q_lens == 1).any())
+    pairs = 2 if mixed and has_dec else 1
+    if multi:
+        # folded passes: one stream kernel each
+        fold = max(1, min(n_tok, 16 // lay.gqa_ratio))
+        pairs = -(-n_tok // fold)
     pa.profile_enable(args.steps * pairs)
     for _ in range(args.steps):
         step()
@@ -353,19 +377,32 @@ def main():
                        args.steps)
         extra = {"prefix_gflop": round(flops / 1e9, 3), "decode_same_batch_ms": round(dec_ms, 5),
                  "cascade_speedup_vs_decode": round(dec_ms / ms_per_step, 3)}
+    elif multi:
+        nb = roofline.mixed_bytes(lay.context_lens, lay.q_lens, lay.num_q_heads, lay.num_kv_heads, D,
+                                  lay.elem_bytes)
+        roof = hbm_roof(f"stream_decode_kernel ({n_tok} tokens folded)", nb["total"], float(sum(kern_avg)),
+                        measured_traffic(args.workload))
+        extra = {"tokens_per_step": int(T), "fold_passes": pairs,
+                 "mixed_chunk_same_batch_ms": round(timed(mixed_step, args.steps), 5)}
     elif mixed:
         nb = roofline.mixed_bytes(lay.context_lens, lay.q_lens, lay.num_q_heads, lay.num_kv_heads, D,
                                   lay.elem_bytes)
         flops = roofline.chunk_flops(lay.context_lens, lay.q_lens, lay.num_q_heads, D)
         chunk_roof = mfma_roof("tile_kernel (prefill chunks)", flops, kern_avg[0])
-        dec = lay.q_lens == 1
-        dbytes = roofline.decode_bytes(lay.context_lens[dec], lay.num_q_heads, lay.num_kv_heads, D,
-                                       lay.elem_bytes)["total"]
-        dec_roof = hbm_roof("stream_decode_kernel (decode tokens)", dbytes, kern_avg[1], None)
-        # the dominant kernel is the one that takes longer
-        roof, other = (chunk_roof, dec_roof) if kern_avg[0] >= kern_avg[1] else (dec_roof, chunk_roof)
-        extra = {"chunk_gflop": round(flops / 1e9, 3), "other_kernel_roofline": other,
-                 "tokens_per_step": int(T)}
+        extra = {"chunk_gflop": round(flops / 1e9, 3), "tokens_per_step": int(T)}
+        roof = chunk_roof
+        if has_dec:
+            dec = lay.q_lens == 1
+            dbytes = roofline.decode_bytes(lay.context_lens[dec], lay.num_q_heads, lay.num_kv_heads, D,
+                                           lay.elem_bytes)["total"]
+            dec_roof = hbm_roof("stream_decode_kernel (decode tokens)", dbytes, kern_avg[1], None)
+            # the dominant kernel is the one that takes longer
+            roof, other = (chunk_roof, dec_roof) if kern_avg[0] >= kern_avg[1] else (dec_roof, chunk_roof)
+            extra["other_kernel_roofline"] = other
+        else:
+            # no single-token segments: the chunk kernel is the whole step;
+            # its K/V traffic, for the HBM view of the same launch
+            extra["chunk_kernel_hbm"] = hbm_roof("tile_kernel (prefill chunks)", nb["total"], kern_avg[0], None)
     elif lay.window is not None:
         # the rows each query sees: the last min(L, window) of its sequence
         nb = roofline.decode_bytes(np.minimum(lay.context_lens, lay.window), lay.num_q_heads, lay.num_kv_heads, D,

@@ -171,6 +171,42 @@ int pa_decode_fp8(void* out,                  /* device [S, Hq, D] bf16 */
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Multi-token decode: every sequence brings q_len >= 1 new tokens at once
+ * (T = num_seqs * q_len; token i of sequence s is q / out / lse row
+ * s * q_len + i), causal among them: with L = context_lens[s] rows, the
+ * new tokens counted, token i sits at position L - q_len + i and sees rows
+ * 0 .. L - q_len + i.  The tokens are folded into the query rows a wave
+ * computes from one pass over K and V, next to the gqa_ratio heads: the
+ * fold_sq_factor of the TokenSpeed deep-dive (section 7.2), with a wave's
+ * 16 rows in place of the page's 128-row tile.  fold = min(q_len,
+ * 16 / gqa_ratio) tokens share a pass; ceil(q_len / fold) passes run one
+ * after another on `stream` (unlike the page, q_len need not be a multiple
+ * of the fold: the last pass may hold fewer tokens).  q_len == 1 is
+ * pa_decode exactly.  Results equal pa_mixed_chunk's on a batch of
+ * segments of q_len tokens each.
+ *
+ * workspace: at least pa_decode_multi_workspace_size(...) bytes for the
+ *   largest batch it will serve (max_total_pages = sum of ceil(L / 16));
+ *   256-byte aligned, no initialisation, scratch between calls.
+ * Built for bf16 (head_dim 64, 128) and float32 (head_dim 64), gqa_ratio
+ * 1, 2, 4, 8, 16.  Errors as pa_decode, plus PA_EINVAL for q_len < 1 or a
+ * context length < q_len.
+ * ------------------------------------------------------------------------- */
+size_t pa_decode_multi_workspace_size(int32_t max_num_seqs, int32_t q_len, int32_t num_kv_heads, int32_t gqa_ratio,
+                                      int32_t head_dim, int64_t max_total_pages, int32_t split_pages);
+
+int pa_decode_multi(void* out,                 /* device [S * q_len, Hq, D] dtype */
+                    float* lse_out,            /* device [S * q_len, Hq] or NULL */
+                    const void* q,             /* device [S * q_len, Hq, D] dtype */
+                    const void* k_pool,        /* device [NP, Hkv, BS, D] dtype */
+                    const void* v_pool,        /* device [NP, Hkv, BS, D] dtype */
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, const int32_t* context_lens_host,
+                    int32_t num_seqs, int32_t q_len, int32_t num_kv_heads, int32_t gqa_ratio, int32_t head_dim,
+                    int32_t block_size, int64_t num_pages, float scale, pa_dtype dtype, int32_t split_pages,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Shared-prefix (cascade) decode: one query token per sequence, sequences in
  * groups whose block tables start with the same prefix pages (shared blocks,
  * SwiftLLM page section 3.1); the result equals pa_decode on the same

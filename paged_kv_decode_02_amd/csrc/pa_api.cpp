@@ -41,13 +41,14 @@ extern "C" size_t pa_decode_workspace_size(int32_t max_num_seqs, int32_t num_kv_
 
 namespace {
 
-// pa_decode and pa_decode_fp8: validation, page count, workspace check, launch.
+// pa_decode, pa_decode_window, pa_decode_fp8 and pa_decode_multi:
+// validation, page count, workspace check, launch.
 int decode_call(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,
                 const float* k_scales, const float* v_scales, bool kv_fp8, const int32_t* block_tables,
                 int32_t max_blocks, const int32_t* context_lens, const int32_t* context_lens_host, int32_t num_seqs,
                 int32_t num_kv_heads, int32_t gqa_ratio, int32_t head_dim, int32_t block_size, int64_t num_pages,
                 float scale, pa_dtype dtype, int32_t split_pages, void* workspace, size_t workspace_bytes,
-                void* stream, int32_t window, const char* who) {
+                void* stream, int32_t window, int32_t q_len, const char* who) {
   const std::string w(who);
   if (num_seqs < 0) return fail(PA_EINVAL, w + ": num_seqs < 0");
   if (num_seqs == 0) return PA_OK;
@@ -57,6 +58,7 @@ int decode_call(void* out, float* lse_out, const void* q, const void* k_pool, co
   if (kv_fp8 && (!k_scales || !v_scales)) return fail(PA_EINVAL, w + ": null scale pointer");
   if (split_pages < 0) return fail(PA_EINVAL, w + ": split_pages < 0");
   if (window < 0) return fail(PA_EINVAL, w + ": window < 1");
+  if (q_len < 1) return fail(PA_EINVAL, w + ": q_len < 1");
   const bool built = kv_fp8 ? decode_fp8_supported(head_dim, gqa_ratio) : decode_supported(dtype, head_dim, gqa_ratio);
   if (!built)
     return fail(PA_EUNSUPPORTED, w + ": no kernel for head_dim " + std::to_string(head_dim) + "/gqa_ratio " +
@@ -66,6 +68,7 @@ int decode_call(void* out, float* lse_out, const void* q, const void* k_pool, co
   for (int32_t s = 0; s < num_seqs; ++s) {
     const int64_t L = context_lens_host[s];
     if (L < 1) return fail(PA_EINVAL, w + ": context_lens[" + std::to_string(s) + "] < 1");
+    if (L < q_len) return fail(PA_EINVAL, w + ": context_lens[" + std::to_string(s) + "] < q_len");
     if (L > static_cast<int64_t>(max_blocks) * block_size)
       return fail(PA_EINVAL, w + ": context_lens[" + std::to_string(s) + "] exceeds the block table");
     // pages the walk covers: from the window's first page on (a sliding
@@ -76,8 +79,11 @@ int decode_call(void* out, float* lse_out, const void* q, const void* k_pool, co
   if (total_pages > (int64_t(1) << 31) - 1) return fail(PA_EUNSUPPORTED, w + ": more than 2^31-1 pages");
   // The workspace must hold the largest plan this batch could get, so that
   // a call never depends on the occupancy the device reports.
+  // (multi-token passes keep `rows` query rows per wave; the last pass
+  // walks every page)
+  const int32_t rows = plan_multi_shape(q_len, gqa_ratio).rows;
   const PartialLayout worst = partial_layout(max_waves_per_head(total_pages, num_kv_heads, split_pages), num_seqs,
-                                             num_kv_heads, gqa_ratio, head_dim);
+                                             num_kv_heads, rows, head_dim);
   if (worst.bytes > workspace_bytes)
     return fail(PA_EWORKSPACE, w + ": workspace holds " + std::to_string(workspace_bytes) + " bytes, needs " +
                                    std::to_string(worst.bytes));
@@ -106,7 +112,8 @@ int decode_call(void* out, float* lse_out, const void* q, const void* k_pool, co
   a.k_scales = k_scales;
   a.v_scales = v_scales;
   a.window = window;
-  return launch_decode(a);
+  if (q_len == 1) return launch_decode(a);
+  return launch_decode_multi(a, plan_multi(q_len, gqa_ratio, context_lens_host, num_seqs, block_size));
 }
 
 }  // namespace
@@ -120,7 +127,7 @@ extern "C" int pa_decode(void* out, float* lse_out, const void* q, const void* k
   clear_error();
   return decode_call(out, lse_out, q, k_pool, v_pool, nullptr, nullptr, false, block_tables, max_blocks, context_lens,
                      context_lens_host, num_seqs, num_kv_heads, gqa_ratio, head_dim, block_size, num_pages, scale,
-                     dtype, split_pages, workspace, workspace_bytes, stream, 0, "pa_decode");
+                     dtype, split_pages, workspace, workspace_bytes, stream, 0, 1, "pa_decode");
 }
 
 extern "C" int pa_decode_window(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,
@@ -133,7 +140,7 @@ extern "C" int pa_decode_window(void* out, float* lse_out, const void* q, const 
   if (window < 1) return fail(PA_EINVAL, "pa_decode_window: window < 1");
   return decode_call(out, lse_out, q, k_pool, v_pool, nullptr, nullptr, false, block_tables, max_blocks, context_lens,
                      context_lens_host, num_seqs, num_kv_heads, gqa_ratio, head_dim, block_size, num_pages, scale,
-                     dtype, split_pages, workspace, workspace_bytes, stream, window, "pa_decode_window");
+                     dtype, split_pages, workspace, workspace_bytes, stream, window, 1, "pa_decode_window");
 }
 
 extern "C" int pa_decode_fp8(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,
@@ -145,7 +152,29 @@ extern "C" int pa_decode_fp8(void* out, float* lse_out, const void* q, const voi
   clear_error();
   return decode_call(out, lse_out, q, k_pool, v_pool, k_scales, v_scales, true, block_tables, max_blocks,
                      context_lens, context_lens_host, num_seqs, num_kv_heads, gqa_ratio, head_dim, block_size,
-                     num_pages, scale, PA_BF16, split_pages, workspace, workspace_bytes, stream, 0, "pa_decode_fp8");
+                     num_pages, scale, PA_BF16, split_pages, workspace, workspace_bytes, stream, 0, 1, "pa_decode_fp8");
+}
+
+extern "C" size_t pa_decode_multi_workspace_size(int32_t max_num_seqs, int32_t q_len, int32_t num_kv_heads,
+                                                 int32_t gqa_ratio, int32_t head_dim, int64_t max_total_pages,
+                                                 int32_t split_pages) {
+  if (max_num_seqs < 0 || q_len < 1 || num_kv_heads < 1 || gqa_ratio < 1 || head_dim < 1 || max_total_pages < 0 ||
+      split_pages < 0)
+    return 0;
+  const int64_t waves = max_waves_per_head(max_total_pages, num_kv_heads, split_pages);
+  return partial_layout(waves, max_num_seqs, num_kv_heads, plan_multi_shape(q_len, gqa_ratio).rows, head_dim).bytes;
+}
+
+extern "C" int pa_decode_multi(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                               const int32_t* context_lens_host, int32_t num_seqs, int32_t q_len,
+                               int32_t num_kv_heads, int32_t gqa_ratio, int32_t head_dim, int32_t block_size,
+                               int64_t num_pages, float scale, pa_dtype dtype, int32_t split_pages, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  clear_error();
+  return decode_call(out, lse_out, q, k_pool, v_pool, nullptr, nullptr, false, block_tables, max_blocks, context_lens,
+                     context_lens_host, num_seqs, num_kv_heads, gqa_ratio, head_dim, block_size, num_pages, scale,
+                     dtype, split_pages, workspace, workspace_bytes, stream, 0, q_len, "pa_decode_multi");
 }
 
 extern "C" size_t pa_prefix_cascade_workspace_size(int32_t max_num_seqs, int32_t num_kv_heads, int32_t gqa_ratio,

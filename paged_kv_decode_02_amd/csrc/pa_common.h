@@ -50,6 +50,33 @@ __device__ __forceinline__ void fp8x16_to_bf16x2(const U4& c, uint32_t (&o)[8]) 
   o[7] = fp8x2_to_bf16x2<true>(c.w);
 }
 
+// Vector types for LDS reads and the matrix cores.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const u32x4 LdsU4;
+typedef __attribute__((address_space(3))) i16x4 LdsI16x4;
+
+// ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, lane j of
+// the group passes the address of 4 consecutive 16-bit elements, row j/4 and
+// columns 4(j%4) .. +3 of a 4 x 16 block; lane j receives column j of that
+// block, rows 0..3.  Returned as two packed 32-bit words.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* lds) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsI16x4*)(lds));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// D = A B + C on one 16 x 16 x 32 bf16 tile (v_mfma_f32_16x16x32_bf16).
+// Lane l holds A row l % 16, B column l % 16, each at k = 8 (l / 16) ..
+// +7 (8 bf16 in a u32x4, element 0 in the low half of x), and D/C column
+// l % 16, rows 4 (l / 16) .. +3.
+__device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -165,9 +192,12 @@ struct ItemLoc {
 // of the context lengths (one pass over S values, then one over the
 // S/64 values of the lane that holds x), so no plan buffer is needed.
 // `begin_pages` (nullable) gives pages each sequence skips; without it a
-// sliding window of `window` tokens (0 = none) decides them.
+// sliding window of `window` tokens (0 = none) decides them.  `trim` rows
+// are taken off the end of every context (a multi-token pass that stops
+// before a sequence's last new tokens).
 __device__ __forceinline__ bool locate_item(const int32_t* __restrict__ ctx, const int32_t* __restrict__ begin_pages,
-                                            int window, int S, int max_blocks, int C, int x, ItemLoc& loc) {
+                                            int window, int S, int max_blocks, int C, int x, ItemLoc& loc,
+                                            int trim = 0) {
   const int lane = lane_id();
   const int per = (S + 63) >> 6;
   int tot = 0;
@@ -177,7 +207,7 @@ __device__ __forceinline__ bool locate_item(const int32_t* __restrict__ ctx, con
   for (int i = 0; i < per; ++i) {
     const int s = lane * per + i;
     const int sc = s < S ? s : S - 1;
-    const int Lc = ctx[sc];
+    const int Lc = ctx[sc] - trim;
     const int n = nsplit_of(Lc, walk_begin(begin_pages, sc, Lc, window), max_blocks, C);
     tot += s < S ? n : 0;
   }
@@ -194,7 +224,7 @@ __device__ __forceinline__ bool locate_item(const int32_t* __restrict__ ctx, con
     const int s = first + i;
     int ns = 0;
     if (i < per && s < S) {
-      const int Ls = ctx[s];
+      const int Ls = ctx[s] - trim;
       ns = nsplit_of(Ls, walk_begin(begin_pages, s, Ls, window), max_blocks, C);
     }
     const int inc2 = wave_inclusive_scan(ns);

@@ -25,6 +25,11 @@
 //    cache as the scalar operand of v_dot2_f32_bf16 (bf16) / v_fma (fp32).
 //    The G q-heads sharing a kv-head all use one pass over K and V (the
 //    analog of fold_sq_factor, TokenSpeed deep-dive section 7.2).
+//  * Multi-token decode (n new tokens per sequence, causal among them):
+//    F tokens of a sequence are folded into the wave's query rows next to
+//    the heads (row r = token r / g, head r % g), which is the fold of the
+//    same section with the wave's 16 rows in place of the 128-row tile;
+//    token j of a pass masks the rows after its own position.
 //  * Online softmax per head in the exp2 domain; rows past the end are
 //    masked by select (never by multiplying by zero) so NaN poison in
 //    unused rows cannot leak.
@@ -46,10 +51,6 @@
 
 namespace pa {
 namespace {
-
-// LDS pointer types (DMA destination; opaque q reads).
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) const u32x4 LdsU4;
 
 template <typename T, int D>
 struct Geom {
@@ -153,7 +154,92 @@ __device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return __b
 // T: q and out elements (uint16_t = bf16 bits, or float).  TKV: pool
 // elements, T itself or uint8_t for e4m3fn codes, whose rows come with one
 // float32 scale each in k_scales / v_scales ([page][kv-head][slot]).
-template <typename T, typename TKV, int D, int G>
+// The page walk of one wave's run [run_a, run_b) of a kv-head's flattened
+// pages: the batch the run starts with, and the batch after each batch.
+// `trim` rows are taken off the end of every context (a multi-token pass
+// that stops before a sequence's last new tokens).
+struct Walk {
+  const int32_t* __restrict__ ctx;
+  const int32_t* __restrict__ begin_pages;
+  const int32_t* __restrict__ block_tables;
+  int window, S, max_blocks, num_pages, trim, run_b;
+
+  __device__ int first_page(int s, int L, int P) const {
+    return min(max(walk_begin(begin_pages, s, L, window), 0), P);
+  }
+  // First row a sequence's query sees: 0, or the start of the sliding window.
+  __device__ int first_row(int L) const { return window > 0 && L > window ? L - window : 0; }
+
+  // The run's first batch (qb = 0); false if the run holds no page.
+  __device__ bool start(int run_a, Batch& b) const {
+    ItemLoc loc;
+    // (Cascade suffix: only pages from begin_pages[s] on are laid end to end.)
+    if (!locate_item(ctx, begin_pages, window, S, max_blocks, 1, run_a, loc, trim)) return false;
+    b.s = __builtin_amdgcn_readfirstlane(loc.s);
+    b.L = ctx[b.s] - trim;
+    b.P = pages_of_len(b.L, max_blocks);
+    b.B = first_page(b.s, b.L, b.P);
+    b.lo = first_row(b.L);
+    b.cs = __builtin_amdgcn_readfirstlane(loc.base);
+    b.seg_lo = b.B + (run_a - b.cs);
+    b.seg_hi = min(b.P, b.B + (run_b - b.cs));
+    b.pb = b.seg_lo;
+    b.qb = 0;
+    load_pids(block_tables, max_blocks, num_pages, b);
+    return true;
+  }
+
+  // The batch after x (same sequence, or the next one holding pages of
+  // this run); false if the run ends with x.
+  __device__ bool advance(const Batch& x, Batch& y) const {
+    y = x;
+    if (x.pb + 4 < x.seg_hi) {
+      y.pb = x.pb + 4;
+    } else if (x.cs + (x.P - x.B) < run_b && x.s + 1 < S) {
+      y.s = x.s + 1;
+      y.cs = x.cs + (x.P - x.B);
+      y.L = ctx[y.s] - trim;
+      y.P = pages_of_len(y.L, max_blocks);
+      y.B = first_page(y.s, y.L, y.P);
+      // Sequences with nothing after begin_pages (the prefill chunks of a
+      // mixed batch) hold no pages of the walk: step over them.  Pages of
+      // this run remain, so a sequence that holds some follows.
+      while (y.B >= y.P && y.s + 1 < S) {
+        y.s += 1;
+        y.L = ctx[y.s] - trim;
+        y.P = pages_of_len(y.L, max_blocks);
+        y.B = first_page(y.s, y.L, y.P);
+      }
+      y.lo = first_row(y.L);
+      y.seg_lo = y.B;
+      y.seg_hi = min(y.P, y.B + (run_b - y.cs));
+      y.pb = y.B;
+      y.qb = x.qb ^ 1;
+      if (y.seg_hi <= y.seg_lo) return false;
+    } else {
+      return false;
+    }
+    load_pids(block_tables, max_blocks, num_pages, y);
+    return true;
+  }
+};
+
+// Multi-token pass: tokens tok0 .. tok0+fe-1 of every sequence's n new
+// tokens (q / out rows s*n .. s*n+n-1; token i sits at position
+// L - n + i), folded into the wave's rows: row r = token r >> lg, head
+// r & (g-1).  Rows past fe tokens are idle.
+struct Fold {
+  int n;     // new tokens per sequence
+  int g;     // q-heads per kv-head (a power of two)
+  int lg;    // log2(g)
+  int tok0;  // first token of the pass
+  int fe;    // tokens in the pass
+  int trim;  // n - tok0 - fe: context rows after the pass's last token
+};
+
+// G: query rows per wave: the q-heads of one kv-head, or (MT) a pass's
+// folded (token, head) rows.
+template <typename T, typename TKV, int D, int G, bool MT>
 __global__ __launch_bounds__(64) void stream_decode_kernel(
     T* __restrict__ out, float* __restrict__ lse_out, const T* __restrict__ q, const TKV* __restrict__ k_pool,
     const TKV* __restrict__ v_pool, const float* __restrict__ k_scales, const float* __restrict__ v_scales,
@@ -161,7 +247,7 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
     int max_blocks, int S, int Hkv, int num_pages, float scale_log2, int per, int total_pages,
     int32_t* __restrict__ seq_info, float* __restrict__ part_o, float* __restrict__ part_lse,
     const int32_t* __restrict__ begin_pages, float* __restrict__ seq_part, const int32_t* __restrict__ q_rows,
-    int window) {
+    int window, Fold fold) {
   using Gm = Geom<TKV, D>;
   constexpr int RD = Gm::RD, NCH = Gm::NCH, TILE = Gm::TILE, NI = Gm::NI, RPI = Gm::RPI, EPC = Gm::EPC;
   constexpr bool FP8 = sizeof(TKV) == 1;
@@ -178,6 +264,7 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
   constexpr int QU4 = G * QNCH;              // 16-byte chunks of the G q rows
   constexpr int QPL = (QU4 + 63) / 64;        // of them per lane when loading
   static_assert(NV + NK <= 63, "vmcnt counts at most 63 loads");
+  static_assert(!MT || (!FP8 && (G & (G - 1)) == 0), "folded passes: bf16/f32 pools, power-of-two rows");
   __shared__ uint4 k_lds[64 * NCH];
   __shared__ uint4 v_lds[64 * NCH];
   __shared__ uint4 q_lds[2][QPL * 64];              // two sequences' q rows (current, next)
@@ -190,7 +277,9 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
   const int chk = lane % NCH;  // V layout: 16-byte column chunk of this lane
   const int w = blockIdx.x;
   const int kvh = blockIdx.y;
-  const int Hq = Hkv * G;
+  const int GH = MT ? fold.g : G;  // q-heads per kv-head
+  const int Hq = Hkv * GH;
+  const int trim = MT ? fold.trim : 0;
   const char* kbytes = reinterpret_cast<const char*>(k_pool);
   const char* vbytes = reinterpret_cast<const char*>(v_pool);
 
@@ -215,26 +304,10 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
   const int pslot = (lane % RPI) * NI + lane / RPI;
 
   // Where the run starts: sequence s0 and its first flattened page.
-  ItemLoc loc;
-  // (Cascade suffix: only pages from begin_pages[s] on are laid end to end.)
-  if (!locate_item(ctx, begin_pages, window, S, max_blocks, 1, run_a, loc)) return;
-  const int s0 = __builtin_amdgcn_readfirstlane(loc.s);
-  auto first_page = [&](int s, int L, int P) { return min(max(walk_begin(begin_pages, s, L, window), 0), P); };
-  // First row a sequence's query sees: 0, or the start of the sliding window.
-  auto first_row = [&](int L) { return window > 0 && L > window ? L - window : 0; };
-
+  const Walk walk{ctx, begin_pages, block_tables, window, S, max_blocks, num_pages, trim, run_b};
   Batch first;
-  first.s = s0;
-  first.L = ctx[s0];
-  first.P = pages_of_len(first.L, max_blocks);
-  first.B = first_page(s0, first.L, first.P);
-  first.lo = first_row(first.L);
-  first.cs = __builtin_amdgcn_readfirstlane(loc.base);
-  first.seg_lo = first.B + (run_a - first.cs);
-  first.seg_hi = min(first.P, first.B + (run_b - first.cs));
-  first.pb = first.seg_lo;
-  first.qb = 0;
-  load_pids(block_tables, max_blocks, num_pages, first);
+  if (!walk.start(run_a, first)) return;
+  const int s0 = first.s;
 
   // K and V of a batch go to LDS by DMA, NI loads of 1 KB each: K with the
   // swizzled layout above; V as it is in the pool (instruction i: rows
@@ -276,11 +349,25 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
   // Row of q / out / lse of sequence s (mixed batches: its one token).
   auto qrow = [&](int s) -> int64_t { return q_rows ? q_rows[s] : s; };
   auto load_q = [&](int s, int qb) {
-    const uint4* src = reinterpret_cast<const uint4*>(q + (qrow(s) * Hq + kvh * G) * D);
+    if constexpr (MT) {
+      // row r of the pass: token tok0 + (r >> lg), head r & (g-1); idle
+      // rows (and lanes past the rows) repeat the last active row
+      const int last = (fold.fe << fold.lg) - 1;
 #pragma unroll
-    for (int i = 0; i < QPL; ++i) {
-      const int u = i * 64 + lane;
-      dma16(src + (u < QU4 ? u : QU4 - 1), lds_offset(&q_lds[qb][i * 64]));
+      for (int i = 0; i < QPL; ++i) {
+        const int u = i * 64 + lane;
+        const int r = min(u / QNCH, last);
+        const int64_t row = (static_cast<int64_t>(s) * fold.n + fold.tok0 + (r >> fold.lg)) * Hq + kvh * GH +
+                            (r & (GH - 1));
+        dma16(reinterpret_cast<const uint4*>(q) + row * QNCH + u % QNCH, lds_offset(&q_lds[qb][i * 64]));
+      }
+    } else {
+      const uint4* src = reinterpret_cast<const uint4*>(q + (qrow(s) * Hq + kvh * G) * D);
+#pragma unroll
+      for (int i = 0; i < QPL; ++i) {
+        const int u = i * 64 + lane;
+        dma16(src + (u < QU4 ? u : QU4 - 1), lds_offset(&q_lds[qb][i * 64]));
+      }
     }
   };
 
@@ -296,40 +383,6 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
   };
   reset();
 
-  // The batch after x (same sequence, or the next one holding pages of
-  // this run); false if the run ends with x.
-  auto advance = [&](const Batch& x, Batch& y) -> bool {
-    y = x;
-    if (x.pb + 4 < x.seg_hi) {
-      y.pb = x.pb + 4;
-    } else if (x.cs + (x.P - x.B) < run_b && x.s + 1 < S) {
-      y.s = x.s + 1;
-      y.cs = x.cs + (x.P - x.B);
-      y.L = ctx[y.s];
-      y.P = pages_of_len(y.L, max_blocks);
-      y.B = first_page(y.s, y.L, y.P);
-      // Sequences with nothing after begin_pages (the prefill chunks of a
-      // mixed batch) hold no pages of the walk: step over them.  Pages of
-      // this run remain, so a sequence that holds some follows.
-      while (y.B >= y.P && y.s + 1 < S) {
-        y.s += 1;
-        y.L = ctx[y.s];
-        y.P = pages_of_len(y.L, max_blocks);
-        y.B = first_page(y.s, y.L, y.P);
-      }
-      y.lo = first_row(y.L);
-      y.seg_lo = y.B;
-      y.seg_hi = min(y.P, y.B + (run_b - y.cs));
-      y.pb = y.B;
-      y.qb = x.qb ^ 1;
-      if (y.seg_hi <= y.seg_lo) return false;
-    } else {
-      return false;
-    }
-    load_pids(block_tables, max_blocks, num_pages, y);
-    return true;
-  };
-
   // cur is the batch being computed, nxt the one after it, whose K and V
   // are issued during cur's math (q of a new sequence is loaded right
   // before the K of its first batch).
@@ -339,7 +392,7 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
   issue_v(cur);
 
   while (true) {
-    const bool has_next = advance(cur, nxt);
+    const bool has_next = walk.advance(cur, nxt);
 
     // K of this batch (and its scales, and q, loaded before it) is in LDS
     // once only this batch's V may be outstanding.
@@ -421,10 +474,21 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
     const float vscale = v_row_scale;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float s2 = valid ? sc[h] * kscale : -INFINITY;
+      bool vis = valid;
+      if constexpr (MT) {
+        // token j of the pass sees the rows up to its own position:
+        // those before L - (fe - 1 - j) of the pass's (trimmed) context
+        const int j = h >> fold.lg;
+        const int lim = j < fold.fe ? cur.L - (fold.fe - 1 - j) - cur.pb * 16 : 0;
+        vis = valid && lane < lim;
+      }
+      const float s2 = vis ? sc[h] * kscale : -INFINITY;
       const float mn = fmaxf(m[h], wave_max(s2));
-      const float alpha = fast_exp2(m[h] - mn);
-      const float p = fast_exp2(s2 - mn);
+      // (folded rows can see no row of a batch yet: then exponents are
+      // taken against 0 so that -inf - -inf never occurs)
+      const float mref = MT && mn == -INFINITY ? 0.f : mn;
+      const float alpha = fast_exp2(m[h] - mref);
+      const float p = fast_exp2(s2 - mref);
       // The normaliser sums the float32 probabilities; for bf16 the P.V
       // product uses them rounded to bf16 (unbiased, round to nearest even).
       const uint32_t pbits = BF16 ? bf16_bits_rne(FP8 ? (valid ? p * vscale : 0.f) : p) : __float_as_uint(p);
@@ -554,9 +618,12 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float lt = wave_sum(l[h]);
-        const float inv = 1.0f / lt;
+        // (a folded row can see no row of this wave's part: a partial of
+        // weight 0, zero output, log2-sum-exp -inf)
+        const float inv = MT && lt == 0.f ? 0.f : 1.0f / lt;
         const float lse2 = m[h] + fast_log2(lt);
-        const bool mine = (h % RPI) == grp;  // one row group writes each head
+        const bool act = !MT || (h >> fold.lg) < fold.fe;  // idle folded rows write nothing
+        const bool mine = act && (h % RPI) == grp;  // one row group writes each head
         if (whole && seq_part) {
           // Cascade: the suffix of a sequence one wave covered is still a
           // partial, to be merged with the shared prefix's.
@@ -570,7 +637,9 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
           }
           if (lane == 0) seq_part[static_cast<int64_t>(S) * Hq * D + r] = lse2;
         } else if (whole) {
-          const int64_t row = qrow(s) * Hq + kvh * G + h;
+          const int64_t row = MT ? (static_cast<int64_t>(s) * fold.n + fold.tok0 + (h >> fold.lg)) * Hq + kvh * GH +
+                                       (h & (GH - 1))
+                                 : qrow(s) * Hq + kvh * G + h;
           if (mine) {
             // columns chk*EPC .. +EPC of the output row
             if constexpr (BF16) {
@@ -591,7 +660,7 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
                                 acc[h][4 * j + 3] * inv);
             }
           }
-          if (lse_out && lane == 0) lse_out[row] = lse2 * kLn2;
+          if (lse_out && act && lane == 0) lse_out[row] = lse2 * kLn2;
         } else {
           const int64_t r = ((static_cast<int64_t>(w) * Hkv + kvh) * 2 + slot) * G + h;
           if (mine) {
@@ -610,22 +679,300 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
   }
 }
 
+// The stream kernel for waves that hold 16 query rows (16 q-heads per
+// kv-head, or a multi-token pass's folded (token, head) rows), on the
+// matrix cores.  Same work split, page walk, K/V/q DMA pipeline, partials
+// and merge as stream_decode_kernel; per 64-row batch:
+//  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: the A operand is a K tile
+//    (16 rows, 32 columns) read from the swizzled K buffer, the B operand a
+//    q tile; lane l ends up with query row l % 16 against the batch rows
+//    16 kb + 4 (l / 16) + i (kb, i = 0..3).
+//  * Online softmax per query row: a lane's 16 scores, then the lanes
+//    l ^ 16 and l ^ 32 that hold the same row.  The probabilities stay in
+//    registers as the P^T operand (bf16 pairs, rounded to nearest even);
+//    the normaliser sums the float32 values, as the other decode paths do.
+//  * O^T += V^T P^T: V lands in LDS swizzled like K and is read transposed
+//    (ds_read_b64_tr_b16), its rows in the same order as P^T's; lane l
+//    accumulates row l % 16, columns 16 db + 4 (l / 16) + i.
+// Each wave's matrix work per batch is 32 MFMAs where the vector path
+// needs about 2000 dot2 instructions for 16 rows.
+template <int D, bool MT>
+__global__ __launch_bounds__(64) void stream_mfma_kernel(
+    uint16_t* __restrict__ out, float* __restrict__ lse_out, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool, const float* __restrict__ k_scales,
+    const float* __restrict__ v_scales, const int32_t* __restrict__ block_tables, const int32_t* __restrict__ ctx,
+    int max_blocks, int S, int Hkv, int num_pages, float scale_log2, int per, int total_pages,
+    int32_t* __restrict__ seq_info, float* __restrict__ part_o, float* __restrict__ part_lse,
+    const int32_t* __restrict__ begin_pages, float* __restrict__ seq_part, const int32_t* __restrict__ q_rows,
+    int window, Fold fold) {
+  using Gm = Geom<uint16_t, D>;
+  constexpr int R = 16;  // query rows
+  constexpr int RD = Gm::RD, NCH = Gm::NCH, TILE = Gm::TILE, NI = Gm::NI;
+  constexpr int NK = NI, NV = NI;  // loads of one issue_k / issue_v
+  constexpr int QNCH = NCH;        // 16-byte chunks of one q row
+  constexpr int QPL = R * QNCH / 64;
+  constexpr int KC = D / 32;  // 32-column steps of the scores
+  constexpr int DB = D / 16;  // 16-column blocks of the output
+  constexpr int per_tile = TILE / 1024;
+  static_assert(NV + NK <= 63, "vmcnt counts at most 63 loads");
+  __shared__ uint4 k_lds[64 * NCH];
+  __shared__ uint4 v_lds[64 * NCH];
+  __shared__ uint4 q_lds[2][QPL * 64];  // two sequences' q rows (current, next)
+
+  const int lane = lane_id();
+  const int col = lane & 15;  // query row of this lane (C/D column; B column)
+  const int lg = lane >> 4;   // k group of the operands; row group of C/D
+  const int w = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int GH = MT ? fold.g : R;  // q-heads per kv-head
+  const int Hq = Hkv * GH;
+  const int trim = MT ? fold.trim : 0;
+  const char* kbytes = reinterpret_cast<const char*>(k_pool);
+  const char* vbytes = reinterpret_cast<const char*>(v_pool);
+
+  const int run_a = w * per;
+  const int run_b = min(run_a + per, total_pages);
+  if (run_a >= run_b) return;
+
+  // K and V both land swizzled: instruction i of a page tile fills LDS
+  // slots 64i..64i+63 of its rows, slot -> (row, chunk ^ swz(row)).
+  uint32_t koff[per_tile];
+#pragma unroll
+  for (int r = 0; r < per_tile; ++r) {
+    const int slot = r * 64 + lane;
+    const int row = slot / NCH;
+    const int ch = (slot % NCH) ^ Gm::swz(row);
+    koff[r] = row * (RD * 4) + ch * 16;
+  }
+
+  const Walk walk{ctx, begin_pages, block_tables, window, S, max_blocks, num_pages, trim, run_b};
+  Batch first;
+  if (!walk.start(run_a, first)) return;
+  const int s0 = first.s;
+
+  const uint32_t k_base = lds_offset(k_lds);
+  const uint32_t v_base = lds_offset(v_lds);
+  auto issue_tiles = [&](const char* pool, const Batch& b, uint32_t base) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const char* tile = pool + (static_cast<int64_t>(b.pid[i / per_tile]) * Hkv + kvh) * TILE;
+      dma16(tile + koff[i % per_tile], base + i * 1024);
+    }
+  };
+
+  // Row r of the wave: q-head r of the kv-head, or (MT) token tok0 + (r >>
+  // lg) and head r & (g-1); idle folded rows repeat the last active row.
+  auto qrow = [&](int s) -> int64_t { return q_rows ? q_rows[s] : s; };
+  auto row_index = [&](int s, int r) -> int64_t {
+    if constexpr (MT)
+      return (static_cast<int64_t>(s) * fold.n + fold.tok0 + (r >> fold.lg)) * Hq + kvh * GH + (r & (GH - 1));
+    else
+      return qrow(s) * Hq + kvh * R + r;
+  };
+  auto load_q = [&](int s, int qb) {
+    const int last = MT ? (fold.fe << fold.lg) - 1 : R - 1;
+#pragma unroll
+    for (int i = 0; i < QPL; ++i) {
+      const int u = i * 64 + lane;
+      const int64_t row = row_index(s, min(u / QNCH, last));
+      dma16(reinterpret_cast<const uint4*>(q) + row * QNCH + u % QNCH, lds_offset(&q_lds[qb][i * 64]));
+    }
+  };
+
+  // Row state of this lane's query row (the lanes l ^ 16, l ^ 32, l ^ 48
+  // hold the same m; their l are partial sums over their own batch rows).
+  float m = -INFINITY, lsum = 0.f;
+  f32x4 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Token of this lane's row within the pass (MT): the rows it may see end
+  // fe - 1 - j before the pass's context end.
+  const int tok = MT ? (col >> fold.lg) : 0;
+  const bool active = !MT || tok < fold.fe;
+
+  Batch cur = first, nxt;
+  load_q(cur.s, cur.qb);
+  issue_tiles(kbytes, cur, k_base);
+  issue_tiles(vbytes, cur, v_base);
+
+  while (true) {
+    const bool has_next = walk.advance(cur, nxt);
+    // K (and q, loaded before it) of this batch have landed once only this
+    // batch's V may be outstanding.
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NV) : "memory");
+    lds_order();
+    if (has_next && nxt.s != cur.s) load_q(nxt.s, nxt.qb);
+
+    // S^T = K Q^T.
+    const uint4* qcur = &q_lds[cur.qb][0];
+    f32x4 sc[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const u32x4 qb = *(LdsU4*)(&qcur[col * QNCH + c * 4 + lg]);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int key = kb * 16 + col;
+        const u32x4 a = *(LdsU4*)(&k_lds[key * NCH + ((c * 4 + lg) ^ Gm::swz(key))]);
+        sc[kb] = mfma16x16x32(a, qb, sc[kb]);
+      }
+    }
+    // Every read of this batch's K is done: the next K may land.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (has_next) issue_tiles(kbytes, nxt, k_base);
+
+    // Online softmax of this lane's row over its 16 batch rows.
+    const int nvalid = min(cur.seg_hi * 16, cur.L) - cur.pb * 16;  // rows of this batch (1..64)
+    const int lo_b = cur.lo - cur.pb * 16;  // rows before the window (<= 0: none)
+    // (MT) rows after this token's own position are not seen
+    const int hi_b = !active ? 0 : MT ? min(nvalid, cur.L - (fold.fe - 1 - tok) - cur.pb * 16) : nvalid;
+    float x[4][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = kb * 16 + lg * 4 + i;
+        x[kb][i] = key < hi_b && key >= lo_b ? sc[kb][i] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, x[kb][i]);
+      }
+    mx = max_xor32(max_xor16(mx));
+    const float mn = fmaxf(m, mx);
+    // (a row that has seen nothing yet keeps m = -inf: exponents are then
+    // taken against 0 so that -inf - -inf never occurs)
+    const float mref = mn == -INFINITY ? 0.f : mn;
+    const float alpha = fast_exp2(m - mref);
+    m = mn;
+    lsum *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    u32x4 pb[2];  // P^T operand of keys 32 ks .. 32 ks + 31
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      float p[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[h][i] = fast_exp2(x[2 * ks + h][i] - mref);
+          lsum += p[h][i];
+        }
+      // k slots 8 lg .. 8 lg + 7 = batch rows 32 ks + 4 lg + [0, 4) and
+      // 32 ks + 16 + 4 lg + [0, 4): the order the V^T operand uses.
+      pb[ks] = u32x4{bf16x2_rne(p[0][0], p[0][1]), bf16x2_rne(p[0][2], p[0][3]), bf16x2_rne(p[1][0], p[1][1]),
+                     bf16x2_rne(p[1][2], p[1][3])};
+    }
+
+    // V of this batch: the next K may still be outstanding.
+    if (has_next)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NK) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_order();
+    // Rows past the end (NaN poison in the pool) or before the window are
+    // zeroed in LDS before they are read: p = 0 times NaN would be NaN.
+    if (nvalid < 64 || lo_b > 0) {
+      uint4* vz = v_lds;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int slot = i * 64 + lane;
+        const int row = slot / NCH;
+        if (row >= nvalid || row < lo_b) vz[slot] = make_uint4(0u, 0u, 0u, 0u);
+      }
+      lds_order();
+    }
+    // O^T += V^T P^T: the V^T operand (columns 16 db + col, rows as in
+    // P^T) from two transposed reads of 4 rows each.
+    const char* vb = reinterpret_cast<const char*>(v_lds);
+    const int tr_r = col >> 2, tr_c = col & 3;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        u32x2 part[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int row = ks * 32 + e * 16 + lg * 4 + tr_r;
+          const int ch = (db * 2 + (tr_c >> 1)) ^ Gm::swz(row);
+          part[e] = lds_read_tr16(vb + row * (RD * 4) + ch * 16 + (tr_c & 1) * 8);
+        }
+        o[db] = mfma16x16x32(u32x4{part[0].x, part[0].y, part[1].x, part[1].y}, pb[ks], o[db]);
+      }
+    }
+    // Every read of this batch's V is done: the next V may land.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (has_next) issue_tiles(vbytes, nxt, v_base);
+
+    if (cur.pb + 4 >= cur.seg_hi) {
+      // End of this wave's part of sequence cur.s: normalise, write the
+      // output (whole sequence), a cascade partial, or a partial.
+      const int s = cur.s;
+      const bool whole = cur.seg_lo == cur.B && cur.seg_hi == cur.P;
+      const int slot = (s == s0) ? 0 : 1;
+      if (cur.seg_lo == cur.B && kvh == 0 && lane == 0) {
+        seq_info[4 * s + 0] = w;
+        seq_info[4 * s + 1] = (cur.cs + (cur.P - cur.B) - 1) / per;  // last wave on the sequence
+        seq_info[4 * s + 2] = slot;
+        seq_info[4 * s + 3] = 0;
+      }
+      const float lt = add_xor32(add_xor16(lsum));
+      // (a folded row can see no row of this wave's part: a partial of
+      // weight 0, zero output, log2-sum-exp -inf)
+      const float inv = lt == 0.f ? 0.f : 1.0f / lt;
+      const float lse2 = m + fast_log2(lt);
+      if (whole && seq_part) {
+        // seq_part: outputs [S][Hq][D], then log2-sum-exp [S][Hq].
+        const int64_t r = static_cast<int64_t>(s) * Hq + kvh * R + col;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          *reinterpret_cast<float4*>(seq_part + r * D + db * 16 + lg * 4) =
+              make_float4(o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
+        if (lg == 0) seq_part[static_cast<int64_t>(S) * Hq * D + r] = lse2;
+      } else if (whole) {
+        if (active) {
+          const int64_t row = row_index(s, col);
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            *reinterpret_cast<uint2*>(out + row * D + db * 16 + lg * 4) =
+                make_uint2(bf16x2_rne(o[db][0] * inv, o[db][1] * inv), bf16x2_rne(o[db][2] * inv, o[db][3] * inv));
+          if (lse_out && lg == 0) lse_out[row] = lse2 * kLn2;
+        }
+      } else {
+        const int64_t r = ((static_cast<int64_t>(w) * Hkv + kvh) * 2 + slot) * R + col;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          *reinterpret_cast<float4*>(part_o + r * D + db * 16 + lg * 4) =
+              make_float4(o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
+        if (lg == 0) part_lse[r] = lse2;
+      }
+      m = -INFINITY;
+      lsum = 0.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (!has_next) break;
+    cur = nxt;
+  }
+}
+
 // Merge the partials of one (sequence, kv-head): the waves w0..w1 that
 // shared the sequence each left (o_w, lse_w) per head; out = sum_w a_w o_w /
 // sum_w a_w with a_w = 2^(lse_w - max lse), lse = max + log2(sum a_w).  Lane
 // j holds wave j's weights; lane d holds output columns; four waves'
 // partial rows are loaded together.
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool MT>
 __global__ __launch_bounds__(64) void merge_kernel(T* __restrict__ out, float* __restrict__ lse_out, int Hkv, int W,
                                                    const int32_t* __restrict__ seq_info,
                                                    const float* __restrict__ part_o,
                                                    const float* __restrict__ part_lse,
-                                                   const int32_t* __restrict__ q_rows) {
+                                                   const int32_t* __restrict__ q_rows, Fold fold) {
   constexpr int EPL = D / 64;  // output elements per lane
   const int lane = lane_id();
   const int s = blockIdx.x;
   const int kvh = blockIdx.y;
-  const int Hq = Hkv * G;
+  const int GH = MT ? fold.g : G;  // q-heads per kv-head
+  const int Hq = Hkv * GH;
   const int w0 = seq_info[4 * s + 0];
   const int w1 = seq_info[4 * s + 1];
   const int slot0 = seq_info[4 * s + 2];
@@ -678,9 +1025,12 @@ __global__ __launch_bounds__(64) void merge_kernel(T* __restrict__ out, float* _
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
+    if (MT && (h >> fold.lg) >= fold.fe) continue;  // idle folded row
     const float ws = wave_sum(wsum[h]);
     const float inv = 1.0f / ws;
-    const int64_t row = (q_rows ? q_rows[s] : s) * static_cast<int64_t>(Hq) + kvh * G + h;
+    const int64_t row = MT ? (static_cast<int64_t>(s) * fold.n + fold.tok0 + (h >> fold.lg)) * Hq + kvh * GH +
+                                 (h & (GH - 1))
+                           : (q_rows ? q_rows[s] : s) * static_cast<int64_t>(Hq) + kvh * G + h;
     if constexpr (sizeof(T) == 2) {
       if constexpr (EPL == 2) {
         reinterpret_cast<uint32_t*>(out)[row * (D / 2) + lane] =
@@ -711,11 +1061,17 @@ int resident_waves(KernelFn fn, std::atomic<int>* cache) {
   return v;
 }
 
-template <typename T, typename TKV, int D, int G>
+template <typename T, typename TKV, int D, int G, bool MT = false>
 int launch_typed(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_part, const int32_t* q_rows, bool merge,
-                 StreamPlan* plan) {
+                 StreamPlan* plan, const Fold& fold = Fold{1, G, 0, 0, 1, 0}) {
   static std::atomic<int> occ_cache[64];
-  auto kern = stream_decode_kernel<T, TKV, D, G>;
+  // Waves of 16 bf16 query rows run on the matrix cores.
+  auto kern = [] {
+    if constexpr (G == 16 && sizeof(T) == 2 && sizeof(TKV) == 2)
+      return stream_mfma_kernel<D, MT>;
+    else
+      return stream_decode_kernel<T, TKV, D, G, MT>;
+  }();
   int64_t per = a.split_pages;
   if (per <= 0) {
     // Fill the GPU once: as many waves as can be resident, spread over the
@@ -727,7 +1083,9 @@ int launch_typed(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_p
   }
   const int64_t W = std::max<int64_t>(1, (a.total_pages + per - 1) / per);
   if (W > 0x7fffffff) return fail(PA_EUNSUPPORTED, "pa_decode: too many waves");
-  const PartialLayout pl = partial_layout(W, a.num_seqs, a.num_kv_heads, a.gqa, a.head_dim);
+  // partial rows per wave: the kernel's query rows (folded passes hold
+  // more rows than q-heads per kv-head)
+  const PartialLayout pl = partial_layout(W, a.num_seqs, a.num_kv_heads, G, a.head_dim);
   if (pl.bytes > a.workspace_bytes)
     return fail(PA_EWORKSPACE, "pa_decode: workspace holds " + std::to_string(a.workspace_bytes) +
                                    " bytes, this batch needs " + std::to_string(pl.bytes));
@@ -749,15 +1107,15 @@ int launch_typed(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_p
                      a.max_blocks, a.num_seqs,
                      a.num_kv_heads, static_cast<int>(a.num_pages), scale_log2, static_cast<int>(per),
                      static_cast<int>(a.total_pages), seq_info, part_o, part_lse, begin_pages, seq_part, q_rows,
-                     begin_pages ? 0 : a.window);
+                     begin_pages ? 0 : a.window, fold);
   if (a.timed) profile_after(a.stream);
   if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_decode: stream kernel launch failed");
   // Unless one wave covers everything, some sequence may be shared; the
   // merge kernel skips the sequences one wave covered.
   if (merge && W > 1) {
-    hipLaunchKernelGGL((merge_kernel<T, D, G>), dim3(a.num_seqs, a.num_kv_heads), dim3(64), 0, st,
+    hipLaunchKernelGGL((merge_kernel<T, D, G, MT>), dim3(a.num_seqs, a.num_kv_heads), dim3(64), 0, st,
                        static_cast<T*>(a.out), a.lse_out, a.num_kv_heads, static_cast<int>(W), seq_info, part_o,
-                       part_lse, q_rows);
+                       part_lse, q_rows, fold);
     if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_decode: merge kernel launch failed");
   }
   return PA_OK;
@@ -776,6 +1134,18 @@ int launch_g(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_part,
       break;
   }
   return fail(PA_EUNSUPPORTED, "pa_decode: gqa_ratio not built");
+}
+
+// Folded multi-token passes: rows = query rows per wave (a power of two).
+template <typename T, int D>
+int launch_fold_rows(const DecodeLaunch& a, int rows, const Fold& f) {
+  switch (rows) {
+    case 2: return launch_typed<T, T, D, 2, true>(a, nullptr, nullptr, nullptr, true, nullptr, f);
+    case 4: return launch_typed<T, T, D, 4, true>(a, nullptr, nullptr, nullptr, true, nullptr, f);
+    case 8: return launch_typed<T, T, D, 8, true>(a, nullptr, nullptr, nullptr, true, nullptr, f);
+    case 16: return launch_typed<T, T, D, 16, true>(a, nullptr, nullptr, nullptr, true, nullptr, f);
+  }
+  return fail(PA_EUNSUPPORTED, "pa_decode_multi: fold rows not built");
 }
 
 // Profiling ring (thread-local).
@@ -825,6 +1195,35 @@ int launch_stream(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_
 }
 
 int launch_decode(const DecodeLaunch& a) { return launch_stream(a, nullptr, nullptr, nullptr, true, nullptr); }
+
+int launch_decode_multi(const DecodeLaunch& a, const MultiPlan& p) {
+  if (p.q_len == 1) return launch_decode(a);
+  if (a.kv_fp8 || a.window != 0) return fail(PA_EUNSUPPORTED, "pa_decode_multi: bf16/f32 pools, no window");
+  if (static_cast<int>(p.pass_pages.size()) != p.passes) return fail(PA_EINVAL, "pa_decode_multi: bad plan");
+  Fold f;
+  f.n = p.q_len;
+  f.g = a.gqa;
+  f.lg = __builtin_ctz(static_cast<unsigned>(a.gqa));
+  // Passes run one after another on the stream and reuse the workspace.
+  for (int pass = 0; pass < p.passes; ++pass) {
+    f.tok0 = pass * p.fold;
+    f.fe = std::min(p.fold, p.q_len - f.tok0);
+    f.trim = p.q_len - f.tok0 - f.fe;
+    DecodeLaunch b = a;
+    b.total_pages = p.pass_pages[pass];
+    int rc = PA_EUNSUPPORTED;
+    if (a.dtype == PA_BF16 && a.head_dim == 128)
+      rc = launch_fold_rows<uint16_t, 128>(b, p.rows, f);
+    else if (a.dtype == PA_BF16 && a.head_dim == 64)
+      rc = launch_fold_rows<uint16_t, 64>(b, p.rows, f);
+    else if (a.dtype == PA_F32 && a.head_dim == 64)
+      rc = launch_fold_rows<float, 64>(b, p.rows, f);
+    else
+      return fail(PA_EUNSUPPORTED, "pa_decode_multi: shape not built");
+    if (rc) return rc;
+  }
+  return PA_OK;
+}
 
 void profile_before(void* stream) {
   if (g_prof.ev.empty() || g_prof.next + 2 > g_prof.ev.size()) return;

@@ -40,6 +40,37 @@ int64_t max_waves_per_head(int64_t total_pages, int32_t num_kv_heads, int32_t sp
   return std::max<int64_t>(1, std::min(by_gpu, by_pages));
 }
 
+MultiPlan plan_multi_shape(int32_t q_len, int32_t gqa) {
+  MultiPlan p;
+  p.q_len = std::max(1, q_len);
+  if (p.q_len == 1) {
+    p.rows = gqa;  // plain decode
+    return p;
+  }
+  // The fold factor of the TokenSpeed deep-dive (section 7.2) against the
+  // wave's 16 rows; the page's divisibility condition is dropped: a pass
+  // addresses its q rows token by token, so the last pass may hold fewer.
+  p.fold = std::max(1, std::min(p.q_len, kMaxFoldRows / std::max(1, gqa)));
+  int32_t rows = 2;
+  while (rows < gqa * p.fold) rows <<= 1;
+  p.rows = rows;
+  p.passes = (p.q_len + p.fold - 1) / p.fold;
+  return p;
+}
+
+MultiPlan plan_multi(int32_t q_len, int32_t gqa, const int32_t* context_lens_host, int32_t num_seqs,
+                     int32_t block_size) {
+  MultiPlan p = plan_multi_shape(q_len, gqa);
+  for (int32_t pass = 0; pass < p.passes; ++pass) {
+    const int64_t trim = p.q_len - std::min<int64_t>(p.q_len, static_cast<int64_t>(pass + 1) * p.fold);
+    int64_t pages = 0;
+    for (int32_t s = 0; s < num_seqs; ++s)
+      pages += (static_cast<int64_t>(context_lens_host[s]) - trim + block_size - 1) / block_size;
+    p.pass_pages.push_back(pages);
+  }
+  return p;
+}
+
 CascadeLayout cascade_layout(int64_t num_seqs, int32_t num_kv_heads, int32_t gqa, int32_t head_dim, int32_t nks,
                              int64_t stream_bytes) {
   CascadeLayout l;

@@ -71,6 +71,24 @@ struct DecodeLaunch {
   int32_t window = 0;
 };
 
+// Multi-token decode: q_len new tokens per sequence, causal among them.
+// `fold` tokens of every sequence share one pass over its pages, their
+// (token, head) rows folded into the wave's query rows (`rows`, the power
+// of two >= gqa * fold); passes = ceil(q_len / fold), pass p covering
+// tokens p*fold .. and walking each context up to its last token.
+constexpr int kMaxFoldRows = 16;  // query rows one wave holds
+struct MultiPlan {
+  int32_t q_len = 1;
+  int32_t fold = 1;
+  int32_t rows = 1;
+  int32_t passes = 1;
+  std::vector<int64_t> pass_pages;  // pages each pass walks (from the host copy of the lengths)
+};
+// fold, rows and passes only (no lengths): what sizes the workspace.
+MultiPlan plan_multi_shape(int32_t q_len, int32_t gqa);
+MultiPlan plan_multi(int32_t q_len, int32_t gqa, const int32_t* context_lens_host, int32_t num_seqs,
+                     int32_t block_size);
+int launch_decode_multi(const DecodeLaunch& a, const MultiPlan& p);
 bool decode_supported(pa_dtype dtype, int32_t head_dim, int32_t gqa);
 bool decode_fp8_supported(int32_t head_dim, int32_t gqa);
 int launch_decode(const DecodeLaunch& a);

@@ -39,32 +39,9 @@
 namespace pa {
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
 constexpr int kRows = kPrefixRowsPerBlock;  // query rows per workgroup: 4 row groups of 32
 constexpr int kKeyTile = 64;                  // keys per LDS tile (4 pages); each wave takes 32 of them
 constexpr int kPidWindow = 256;               // page ids per LDS window (64 tiles)
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 LdsI16x4;
-typedef __attribute__((address_space(3))) const u32x4 LdsU4;
-
-// ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, lane j of
-// the group passes the address of 4 consecutive 16-bit elements, row j/4 and
-// columns 4(j%4) .. +3 of a 4 x 16 block; lane j receives column j of that
-// block, rows 0..3.  Returned as two packed 32-bit words.
-__device__ __forceinline__ u32x2 lds_read_tr16(const void* lds) {
-  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsI16x4*)(lds));
-  return __builtin_bit_cast(u32x2, r);
-}
-
-__device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
-                                                 0, 0);
-}
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

@@ -32,6 +32,8 @@ EXPORTS = (
     "pa_decode",
     "pa_decode_fp8",
     "pa_decode_window",
+    "pa_decode_multi_workspace_size",
+    "pa_decode_multi",
     "pa_prefix_cascade_workspace_size",
     "pa_prefix_cascade",
     "pa_mixed_chunk_workspace_size",
@@ -77,6 +79,11 @@ def load(path: Optional[str] = None):
     lib.pa_decode_window.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32,
                                      c_i32, c_i32, c_i64, ctypes.c_float, ctypes.c_int, c_i32, c_i32, c_vp, c_sz,
                                      c_vp]
+    lib.pa_decode_multi_workspace_size.restype = c_sz
+    lib.pa_decode_multi_workspace_size.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32, c_i64, c_i32]
+    lib.pa_decode_multi.restype = ctypes.c_int
+    lib.pa_decode_multi.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
+                                    c_i32, c_i32, c_i64, ctypes.c_float, ctypes.c_int, c_i32, c_vp, c_sz, c_vp]
     lib.pa_decode_fp8.restype = ctypes.c_int
     lib.pa_decode_fp8.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32,
                                   c_i32, c_i32, c_i32, c_i64, ctypes.c_float, c_i32, c_vp, c_sz, c_vp]
@@ -191,6 +198,54 @@ def decode_window(out, q, k_pool, v_pool, block_tables, context_lens, context_le
         _dev(context_lens, "context_lens", torch.int32),
         ch.ctypes.data,
         S, Hkv, Hq // Hkv, D, BS, NP, float(scale), _dtype_code(q), int(window), int(split_pages),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream_ptr(stream),
+    )
+    return _check(rc)
+
+
+def decode_multi_workspace_size(max_num_seqs, q_len, num_kv_heads, gqa_ratio, head_dim, max_total_pages,
+                                split_pages=0) -> int:
+    return int(load().pa_decode_multi_workspace_size(max_num_seqs, q_len, num_kv_heads, gqa_ratio, head_dim,
+                                                     max_total_pages, split_pages))
+
+
+def decode_multi(out, q, k_pool, v_pool, block_tables, context_lens, context_lens_host, scale, q_len, workspace,
+                 lse_out=None, split_pages=0, stream=None):
+    """pa_decode_multi on torch tensors: ``q_len`` new tokens per sequence,
+    q / out ``[S * q_len, Hq, D]`` (token i of sequence s at row
+    s * q_len + i), causal among the new tokens."""
+    import torch
+
+    T, Hq, D = q.shape
+    NP, Hkv, BS, D2 = k_pool.shape
+    q_len = int(q_len)
+    if q_len < 1 or T % q_len:
+        raise ValueError("q rows must be num_seqs * q_len")
+    S = T // q_len
+    if tuple(out.shape) != (T, Hq, D) or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if tuple(v_pool.shape) != tuple(k_pool.shape) or k_pool.dtype != q.dtype or v_pool.dtype != q.dtype:
+        raise ValueError("k_pool and v_pool must match each other and q's dtype")
+    if D2 != D or Hq % Hkv:
+        raise ValueError("head_dim mismatch or q heads not a multiple of kv heads")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_tables / context_lens must have one row per sequence")
+    ch = _host_i32(context_lens_host, "context_lens_host")
+    if ch.size != S:
+        raise ValueError("context_lens_host must have one entry per sequence")
+    if lse_out is not None and tuple(lse_out.shape) != (T, Hq):
+        raise ValueError("lse_out must be [S * q_len, Hq]")
+    rc = load().pa_decode_multi(
+        _dev(out, "out"),
+        _dev(lse_out, "lse_out", torch.float32) if lse_out is not None else None,
+        _dev(q, "q"),
+        _dev(k_pool, "k_pool"),
+        _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32),
+        ch.ctypes.data,
+        S, q_len, Hkv, Hq // Hkv, D, BS, NP, float(scale), _dtype_code(q), int(split_pages),
         _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream_ptr(stream),
     )
     return _check(rc)

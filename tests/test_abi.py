@@ -310,3 +310,60 @@ def test_append_fp8_with_nothing_to_write_is_a_no_op():
     lib = pa.load()
     assert call_append_fp8(lib, S=0, k=None) == pa.PA_OK
     assert call_append_fp8(lib, cu_host=np.array([0, 0, 0], dtype=np.int32)) == pa.PA_OK
+
+
+def call_decode_multi(lib, **kw):
+    args = dict(out=FAKE, lse=None, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, mb=4, ctx=FAKE, ctx_host=None, S=2, n=4, Hkv=2,
+                G=4, D=128, BS=16, NP=10, scale=0.1, dtype=pa.PA_BF16, split=0, ws=ctypes.c_void_p(0x100000),
+                ws_bytes=1 << 20, stream=None)
+    args.update(kw)
+    ch = args["ctx_host"]
+    if ch is None:
+        ch = np.array([20, 40], dtype=np.int32)
+    return lib.pa_decode_multi(args["out"], args["lse"], args["q"], args["k"], args["v"], args["bt"], args["mb"],
+                               args["ctx"], ch.ctypes.data, args["S"], args["n"], args["Hkv"], args["G"], args["D"],
+                               args["BS"], args["NP"], args["scale"], args["dtype"], args["split"], args["ws"],
+                               args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(q=None), pa.PA_EINVAL),
+        (dict(n=0), pa.PA_EINVAL),
+        (dict(n=-2), pa.PA_EINVAL),
+        (dict(ctx_host=np.array([3, 40], dtype=np.int32)), pa.PA_EINVAL),  # shorter than q_len
+        (dict(ctx_host=np.array([20, 65], dtype=np.int32)), pa.PA_EINVAL),
+        (dict(scale=float("nan")), pa.PA_EINVAL),
+        (dict(split=-1), pa.PA_EINVAL),
+        (dict(G=3), pa.PA_EUNSUPPORTED),
+        (dict(D=96), pa.PA_EUNSUPPORTED),
+        (dict(dtype=pa.PA_F32, D=128), pa.PA_EUNSUPPORTED),
+        (dict(ws=ctypes.c_void_p(0x100010)), pa.PA_EINVAL),
+        (dict(ws_bytes=64, split=1), pa.PA_EWORKSPACE),
+    ],
+)
+def test_decode_multi_rejects_bad_arguments(kw, code):
+    lib = pa.load()
+    assert call_decode_multi(lib, **kw) == code
+    assert lib.pa_last_error().decode().startswith("pa_decode_multi")
+
+
+def test_decode_multi_zero_sequences_is_a_no_op():
+    lib = pa.load()
+    assert call_decode_multi(lib, S=0, q=None, out=None) == pa.PA_OK
+
+
+def test_decode_multi_workspace_follows_the_fold():
+    """q_len 1 sizes like plain decode; folded passes keep rows = the power
+    of two >= gqa * min(q_len, 16 / gqa) partial rows per wave."""
+    for S, P, G in [(1, 1, 4), (64, 9216, 4), (256, 9000, 8), (16, 500, 1), (8, 300, 16)]:
+        assert pa.decode_multi_workspace_size(S, 1, 8, G, 128, P, 0) == pa.decode_workspace_size(S, 8, G, 128, P, 0)
+        for n in (2, 3, 4, 7):
+            fold = max(1, min(n, 16 // G))
+            rows = 2
+            while rows < G * fold:
+                rows *= 2
+            want = pa.decode_workspace_size(S, 8, rows, 128, P, 3)
+            assert pa.decode_multi_workspace_size(S, n, 8, G, 128, P, 3) == want
+    assert pa.decode_multi_workspace_size(4, 0, 8, 4, 128, 10, 0) == 0

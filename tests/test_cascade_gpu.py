@@ -65,6 +65,7 @@ def oracle_cascade(lay, qh, kh, vh, seqs=None):
         (2, 16, 80, 100, 64, 8),     # G = 8, prefix not a multiple of 64 keys
         (1, 33, 2048, 600, 32, 8),   # long prefix, several key splits
         (3, 4, 0, 90, 32, 8),        # no prefix at all
+        (2, 12, 96, 70, 128, 8),     # G = 16: suffixes on the matrix-core stream kernel
     ],
 )
 def test_cascade_small(gpu_lib, groups, per_group, prefix, suf_hi, hq, hkv):

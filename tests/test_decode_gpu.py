@@ -78,7 +78,8 @@ def test_longtail_sampled(gpu_lib):
 
 
 @pytest.mark.parametrize("dtype,d,hq,hkv", [("bf16", 128, 8, 8), ("bf16", 128, 16, 8), ("bf16", 128, 128, 8),
-                                            ("bf16", 64, 8, 2), ("bf16", 64, 32, 4), ("f32", 64, 4, 4),
+                                            ("bf16", 64, 8, 2), ("bf16", 64, 32, 4), ("bf16", 64, 32, 2),
+                                            ("f32", 64, 4, 4),
                                             ("f32", 64, 16, 2)])
 def test_shapes_and_ragged_lengths(gpu_lib, dtype, d, hq, hkv):
     ctx = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 200, 511, 512, 513, 1000, 2049]

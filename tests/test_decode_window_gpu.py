@@ -42,7 +42,8 @@ def oracle_window(lay, q, k, v, seqs=None):
 CTX = [1, 15, 16, 17, 40, 63, 64, 65, 100, 257, 1000, 2049]
 
 
-@pytest.mark.parametrize("dtype,d,hq,hkv", [("bf16", 128, 32, 8), ("bf16", 128, 64, 8), ("bf16", 64, 8, 2),
+@pytest.mark.parametrize("dtype,d,hq,hkv", [("bf16", 128, 32, 8), ("bf16", 128, 64, 8), ("bf16", 128, 128, 8),
+                                            ("bf16", 64, 8, 2),
                                             ("f32", 64, 8, 2)])
 @pytest.mark.parametrize("window", [1, 15, 16, 17, 100, 1000])
 def test_ragged_windows(gpu_lib, dtype, d, hq, hkv, window):

@@ -452,8 +452,18 @@ def _llama8b_prefill_append_fp8(seed=0):
     return lay
 
 
+def _llama8b_multitoken4(seed=0):
+    """The Llama-shaped batch decoding 4 tokens per sequence at once (a
+    speculative-decoding step): 64 segments of q_len 4, causal among the 4."""
+    base = _llama8b_decode(seed)
+    prefixes = [int(L) - 4 for L in base.context_lens]
+    return mixed_layout(chunk_prefixes=prefixes, chunk_len=4, decode_ctx=[], num_q_heads=32, num_kv_heads=8,
+                        head_dim=128, seed=seed, name="llama8b_multitoken4")
+
+
 WORKLOADS = {
     "tiny_f32": _tiny_f32,
+    "llama8b_multitoken4": _llama8b_multitoken4,
     "llama8b_prefill_append_fp8": _llama8b_prefill_append_fp8,
     "longtail_window4096": _longtail_window4096,
     "llama8b_prefill_append": _llama8b_prefill_append,
