@@ -36,7 +36,7 @@ extern "C" size_t pa_decode_workspace_size(int32_t max_num_seqs, int32_t num_kv_
       split_pages < 0)
     return 0;
   const int64_t waves = max_waves_per_head(max_total_pages, num_kv_heads, split_pages);
-  return partial_layout(waves, max_num_seqs, num_kv_heads, gqa_ratio, head_dim).bytes;
+  return partial_layout(waves, max_num_seqs, num_kv_heads, stream_rows(gqa_ratio), head_dim).bytes;
 }
 
 namespace {
@@ -181,7 +181,7 @@ extern "C" size_t pa_prefix_cascade_workspace_size(int32_t max_num_seqs, int32_t
                                                    int32_t head_dim, int64_t max_total_pages) {
   if (max_num_seqs < 0 || num_kv_heads < 1 || gqa_ratio < 1 || head_dim < 1 || max_total_pages < 0) return 0;
   const int64_t waves = max_waves_per_head(max_total_pages, num_kv_heads, 0);
-  const size_t stream = partial_layout(waves, max_num_seqs, num_kv_heads, gqa_ratio, head_dim).bytes;
+  const size_t stream = partial_layout(waves, max_num_seqs, num_kv_heads, stream_rows(gqa_ratio), head_dim).bytes;
   return cascade_layout(max_num_seqs, num_kv_heads, gqa_ratio, head_dim, kMaxPrefixSplits, stream).bytes;
 }
 
@@ -247,7 +247,7 @@ extern "C" int pa_prefix_cascade(void* out, float* lse_out, const void* q, const
     nks = 1;
   }
   const int64_t waves = max_waves_per_head(suffix_pages, num_kv_heads, 0);
-  const size_t stream_bytes = partial_layout(waves, num_seqs, num_kv_heads, gqa_ratio, head_dim).bytes;
+  const size_t stream_bytes = partial_layout(waves, num_seqs, num_kv_heads, stream_rows(gqa_ratio), head_dim).bytes;
   const CascadeLayout lay = cascade_layout(num_seqs, num_kv_heads, gqa_ratio, head_dim, nks, stream_bytes);
   if (lay.bytes > workspace_bytes)
     return fail(PA_EWORKSPACE, "pa_prefix_cascade: workspace holds " + std::to_string(workspace_bytes) +
@@ -294,7 +294,8 @@ extern "C" size_t pa_mixed_chunk_workspace_size(int32_t max_num_tokens, int32_t 
       max_total_pages < 0)
     return 0;
   const int64_t waves = max_waves_per_head(max_total_pages, num_kv_heads, 0);
-  const size_t stream = partial_layout(waves, max_num_segments, num_kv_heads, gqa_ratio, head_dim).bytes;
+  const size_t stream =
+      partial_layout(waves, max_num_segments, num_kv_heads, stream_rows(gqa_ratio), head_dim).bytes;
   return mixed_layout(max_num_segments, max_num_tokens, num_kv_heads, gqa_ratio, head_dim, kMaxChunkSplits, stream)
       .bytes;
 }
@@ -355,7 +356,8 @@ extern "C" int pa_mixed_chunk(void* out, float* lse_out, const void* q, const vo
     if (plan.records > INT32_MAX) return fail(PA_EUNSUPPORTED, "pa_mixed_chunk: too many chunk tokens");
   }
   const int64_t waves = max_waves_per_head(decode_pages, num_kv_heads, 0);
-  const size_t stream_bytes = partial_layout(waves, num_segments, num_kv_heads, gqa_ratio, head_dim).bytes;
+  const size_t stream_bytes =
+      partial_layout(waves, num_segments, num_kv_heads, stream_rows(gqa_ratio), head_dim).bytes;
   // (Partial records per kv-head: sum over chunks of tokens x splits.)
   const MixedLayout lay = mixed_layout(num_segments, plan.records / num_kv_heads, num_kv_heads, gqa_ratio, head_dim,
                                        1, stream_bytes);

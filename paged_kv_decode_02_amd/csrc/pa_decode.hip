@@ -224,10 +224,12 @@ struct Walk {
   }
 };
 
-// Multi-token pass: tokens tok0 .. tok0+fe-1 of every sequence's n new
-// tokens (q / out rows s*n .. s*n+n-1; token i sits at position
-// L - n + i), folded into the wave's rows: row r = token r >> lg, head
-// r & (g-1).  Rows past fe tokens are idle.
+// Which query rows a wave holds.  Multi-token pass: tokens tok0 ..
+// tok0+fe-1 of every sequence's n new tokens (q / out rows s*n .. s*n+n-1;
+// token i sits at position L - n + i), folded into the wave's rows: row r
+// = token r >> lg, head r & (g-1).  One token per sequence: n = fe = 1,
+// tok0 = 0, and row r is q-head r of the kv-head.  Rows of tokens past fe
+// (past g heads) are idle.
 struct Fold {
   int n;     // new tokens per sequence
   int g;     // q-heads per kv-head (a power of two)
@@ -724,7 +726,7 @@ __global__ __launch_bounds__(64) void stream_mfma_kernel(
   const int lg = lane >> 4;   // k group of the operands; row group of C/D
   const int w = blockIdx.x;
   const int kvh = blockIdx.y;
-  const int GH = MT ? fold.g : R;  // q-heads per kv-head
+  const int GH = fold.g;  // q-heads per kv-head (8 or 16; fewer when tokens are folded)
   const int Hq = Hkv * GH;
   const int trim = MT ? fold.trim : 0;
   const char* kbytes = reinterpret_cast<const char*>(k_pool);
@@ -761,16 +763,16 @@ __global__ __launch_bounds__(64) void stream_mfma_kernel(
   };
 
   // Row r of the wave: q-head r of the kv-head, or (MT) token tok0 + (r >>
-  // lg) and head r & (g-1); idle folded rows repeat the last active row.
+  // lg) and head r & (g-1); idle rows repeat the last active row.
   auto qrow = [&](int s) -> int64_t { return q_rows ? q_rows[s] : s; };
   auto row_index = [&](int s, int r) -> int64_t {
     if constexpr (MT)
       return (static_cast<int64_t>(s) * fold.n + fold.tok0 + (r >> fold.lg)) * Hq + kvh * GH + (r & (GH - 1));
     else
-      return qrow(s) * Hq + kvh * R + r;
+      return qrow(s) * Hq + kvh * GH + r;
   };
   auto load_q = [&](int s, int qb) {
-    const int last = MT ? (fold.fe << fold.lg) - 1 : R - 1;
+    const int last = (fold.fe << fold.lg) - 1;
 #pragma unroll
     for (int i = 0; i < QPL; ++i) {
       const int u = i * 64 + lane;
@@ -786,9 +788,9 @@ __global__ __launch_bounds__(64) void stream_mfma_kernel(
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   // Token of this lane's row within the pass (MT): the rows it may see end
-  // fe - 1 - j before the pass's context end.
-  const int tok = MT ? (col >> fold.lg) : 0;
-  const bool active = !MT || tok < fold.fe;
+  // fe - 1 - j before the pass's context end.  Idle rows see nothing.
+  const int tok = col >> fold.lg;
+  const bool active = tok < fold.fe;
 
   Batch cur = first, nxt;
   load_q(cur.s, cur.qb);
@@ -923,12 +925,14 @@ __global__ __launch_bounds__(64) void stream_mfma_kernel(
       const float lse2 = m + fast_log2(lt);
       if (whole && seq_part) {
         // seq_part: outputs [S][Hq][D], then log2-sum-exp [S][Hq].
-        const int64_t r = static_cast<int64_t>(s) * Hq + kvh * R + col;
+        if (active) {
+          const int64_t r = static_cast<int64_t>(s) * Hq + kvh * GH + col;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-          *reinterpret_cast<float4*>(seq_part + r * D + db * 16 + lg * 4) =
-              make_float4(o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
-        if (lg == 0) seq_part[static_cast<int64_t>(S) * Hq * D + r] = lse2;
+          for (int db = 0; db < DB; ++db)
+            *reinterpret_cast<float4*>(seq_part + r * D + db * 16 + lg * 4) =
+                make_float4(o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
+          if (lg == 0) seq_part[static_cast<int64_t>(S) * Hq * D + r] = lse2;
+        }
       } else if (whole) {
         if (active) {
           const int64_t row = row_index(s, col);
@@ -971,7 +975,7 @@ __global__ __launch_bounds__(64) void merge_kernel(T* __restrict__ out, float* _
   const int lane = lane_id();
   const int s = blockIdx.x;
   const int kvh = blockIdx.y;
-  const int GH = MT ? fold.g : G;  // q-heads per kv-head
+  const int GH = fold.g;  // q-heads per kv-head
   const int Hq = Hkv * GH;
   const int w0 = seq_info[4 * s + 0];
   const int w1 = seq_info[4 * s + 1];
@@ -1025,12 +1029,12 @@ __global__ __launch_bounds__(64) void merge_kernel(T* __restrict__ out, float* _
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    if (MT && (h >> fold.lg) >= fold.fe) continue;  // idle folded row
+    if ((h >> fold.lg) >= fold.fe) continue;  // idle row
     const float ws = wave_sum(wsum[h]);
     const float inv = 1.0f / ws;
     const int64_t row = MT ? (static_cast<int64_t>(s) * fold.n + fold.tok0 + (h >> fold.lg)) * Hq + kvh * GH +
                                  (h & (GH - 1))
-                           : (q_rows ? q_rows[s] : s) * static_cast<int64_t>(Hq) + kvh * G + h;
+                           : (q_rows ? q_rows[s] : s) * static_cast<int64_t>(Hq) + kvh * GH + h;
     if constexpr (sizeof(T) == 2) {
       if constexpr (EPL == 2) {
         reinterpret_cast<uint32_t*>(out)[row * (D / 2) + lane] =
@@ -1063,7 +1067,7 @@ int resident_waves(KernelFn fn, std::atomic<int>* cache) {
 
 template <typename T, typename TKV, int D, int G, bool MT = false>
 int launch_typed(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_part, const int32_t* q_rows, bool merge,
-                 StreamPlan* plan, const Fold& fold = Fold{1, G, 0, 0, 1, 0}) {
+                 StreamPlan* plan, const Fold* multi = nullptr) {
   static std::atomic<int> occ_cache[64];
   // Waves of 16 bf16 query rows run on the matrix cores.
   auto kern = [] {
@@ -1092,8 +1096,11 @@ int launch_typed(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_p
   if (plan) {
     plan->waves = W;
     plan->per = static_cast<int32_t>(per);
+    plan->rows = G;
     plan->layout = pl;
   }
+  // One token per sequence: row r is q-head r (rows past gqa_ratio idle).
+  const Fold fold = multi ? *multi : Fold{1, a.gqa, __builtin_ctz(static_cast<unsigned>(a.gqa)), 0, 1, 0};
   char* ws = static_cast<char*>(a.workspace);
   int32_t* seq_info = reinterpret_cast<int32_t*>(ws + pl.info_offset);
   float* part_lse = reinterpret_cast<float*>(ws + pl.lse_offset);
@@ -1128,7 +1135,13 @@ int launch_g(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_part,
     case 1: return launch_typed<T, TKV, D, 1>(a, begin_pages, seq_part, q_rows, merge, plan);
     case 2: return launch_typed<T, TKV, D, 2>(a, begin_pages, seq_part, q_rows, merge, plan);
     case 4: return launch_typed<T, TKV, D, 4>(a, begin_pages, seq_part, q_rows, merge, plan);
-    case 8: return launch_typed<T, TKV, D, 8>(a, begin_pages, seq_part, q_rows, merge, plan);
+    case 8:
+      // bf16 pools: the matrix-core kernel, half its 16 rows idle, streams
+      // faster than the vector kernel's 8 rows
+      if constexpr (sizeof(T) == 2 && sizeof(TKV) == 2)
+        return launch_typed<T, TKV, D, 16>(a, begin_pages, seq_part, q_rows, merge, plan);
+      else
+        return launch_typed<T, TKV, D, 8>(a, begin_pages, seq_part, q_rows, merge, plan);
     case 16:
       if constexpr (sizeof(TKV) > 1) return launch_typed<T, TKV, D, 16>(a, begin_pages, seq_part, q_rows, merge, plan);
       break;
@@ -1136,14 +1149,19 @@ int launch_g(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_part,
   return fail(PA_EUNSUPPORTED, "pa_decode: gqa_ratio not built");
 }
 
-// Folded multi-token passes: rows = query rows per wave (a power of two).
+// Folded multi-token passes: rows = query rows per wave (a power of two);
+// bf16 passes of 8 or 16 rows run on the matrix-core kernel's 16 rows.
 template <typename T, int D>
 int launch_fold_rows(const DecodeLaunch& a, int rows, const Fold& f) {
   switch (rows) {
-    case 2: return launch_typed<T, T, D, 2, true>(a, nullptr, nullptr, nullptr, true, nullptr, f);
-    case 4: return launch_typed<T, T, D, 4, true>(a, nullptr, nullptr, nullptr, true, nullptr, f);
-    case 8: return launch_typed<T, T, D, 8, true>(a, nullptr, nullptr, nullptr, true, nullptr, f);
-    case 16: return launch_typed<T, T, D, 16, true>(a, nullptr, nullptr, nullptr, true, nullptr, f);
+    case 2: return launch_typed<T, T, D, 2, true>(a, nullptr, nullptr, nullptr, true, nullptr, &f);
+    case 4: return launch_typed<T, T, D, 4, true>(a, nullptr, nullptr, nullptr, true, nullptr, &f);
+    case 8:
+      if constexpr (sizeof(T) == 2)
+        return launch_typed<T, T, D, 16, true>(a, nullptr, nullptr, nullptr, true, nullptr, &f);
+      else
+        return launch_typed<T, T, D, 8, true>(a, nullptr, nullptr, nullptr, true, nullptr, &f);
+    case 16: return launch_typed<T, T, D, 16, true>(a, nullptr, nullptr, nullptr, true, nullptr, &f);
   }
   return fail(PA_EUNSUPPORTED, "pa_decode_multi: fold rows not built");
 }

@@ -544,12 +544,14 @@ __global__ __launch_bounds__(64) void chunk_merge_kernel(uint16_t* __restrict__ 
 // group (from begin_pages: the prefix length) and its suffix, which is one
 // partial (seq_part) when a single wave covered it and one partial per wave
 // otherwise.
+// (The stream kernel's partials hold PR rows per (wave, kv-head, slot):
+// G, or 16 where its waves run on the matrix cores.)
 template <typename T, int D, int G>
 __global__ __launch_bounds__(64) void cascade_merge_kernel(
     T* __restrict__ out, float* __restrict__ lse_out, int S, int Hkv, int W, int nks, int kps,
     const int32_t* __restrict__ begin_pages, const float* __restrict__ pre_o, const float* __restrict__ pre_lse,
     const float* __restrict__ seq_part, const int32_t* __restrict__ seq_info, const float* __restrict__ part_o,
-    const float* __restrict__ part_lse) {
+    const float* __restrict__ part_lse, int PR) {
   constexpr int EPL = D / 64;
   const int lane = lane_id();
   const int s = blockIdx.x;
@@ -568,13 +570,13 @@ __global__ __launch_bounds__(64) void cascade_merge_kernel(
     if (j < np) return pre_lse[((static_cast<int64_t>(s) * Hkv + kvh) * nks + j) * G + h];
     const int k = j - np;
     if (!shared) return seq_part[static_cast<int64_t>(S) * Hq * D + static_cast<int64_t>(s) * Hq + kvh * G + h];
-    return part_lse[((static_cast<int64_t>(w0 + k) * Hkv + kvh) * 2 + (k == 0 ? slot0 : 0)) * G + h];
+    return part_lse[((static_cast<int64_t>(w0 + k) * Hkv + kvh) * 2 + (k == 0 ? slot0 : 0)) * PR + h];
   };
   auto o_at = [&](int j, int h) -> const float* {
     if (j < np) return pre_o + (((static_cast<int64_t>(s) * Hkv + kvh) * nks + j) * G + h) * D;
     const int k = j - np;
     if (!shared) return seq_part + (static_cast<int64_t>(s) * Hq + kvh * G + h) * D;
-    return part_o + (((static_cast<int64_t>(w0 + k) * Hkv + kvh) * 2 + (k == 0 ? slot0 : 0)) * G + h) * D;
+    return part_o + (((static_cast<int64_t>(w0 + k) * Hkv + kvh) * 2 + (k == 0 ? slot0 : 0)) * PR + h) * D;
   };
 #pragma unroll 1
   for (int h = 0; h < G; ++h) {
@@ -647,7 +649,7 @@ int launch_cascade_g(const CascadeLaunch& c) {
                      static_cast<int>(plan.waves), c.nks, c.kps, begin_pages, pre_o, pre_lse, seq_part,
                      reinterpret_cast<const int32_t*>(sws + plan.layout.info_offset),
                      reinterpret_cast<const float*>(sws + plan.layout.o_offset),
-                     reinterpret_cast<const float*>(sws + plan.layout.lse_offset));
+                     reinterpret_cast<const float*>(sws + plan.layout.lse_offset), plan.rows);
   if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_prefix_cascade: merge kernel launch failed");
   return PA_OK;
 }
@@ -663,8 +665,8 @@ int launch_mixed_g(const MixedLaunch& mx) {
   float* pre_lse = reinterpret_cast<float*>(ws + L.pre_lse_offset);
   char* sws = ws + L.stream_offset;
   // The stream kernel's per-sequence records start its workspace.
-  int32_t* seq_info = reinterpret_cast<int32_t*>(sws + partial_layout(1, a.num_seqs, a.num_kv_heads, a.gqa,
-                                                                      a.head_dim).info_offset);
+  int32_t* seq_info = reinterpret_cast<int32_t*>(sws + partial_layout(1, a.num_seqs, a.num_kv_heads,
+                                                                      stream_rows(a.gqa), a.head_dim).info_offset);
   const float scale_log2 = a.scale * kLog2e;
   const ChunkPlan& plan = *mx.plan;
   auto chunk_list = [&](int b0) {
