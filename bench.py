@@ -363,6 +363,10 @@ def main():
                 "frac": round(tflops / roofline.MFMA_BF16_PEAK_TFLOPS, 4), "kernel_ms": round(ms, 5),
                 "traffic": None}
 
+    def stream_kernel(rows):
+        # waves of 8 or more bf16 query rows run on the matrix-core kernel
+        return "stream_mfma_kernel" if lay.dtype == "bf16" and not fp8 and rows >= 8 else "stream_decode_kernel"
+
     extra = {}
     if cascade:
         nb = roofline.cascade_bytes(lay.context_lens, lay.group_seq_offsets, lay.prefix_lens, lay.num_q_heads,
@@ -380,7 +384,10 @@ def main():
     elif multi:
         nb = roofline.mixed_bytes(lay.context_lens, lay.q_lens, lay.num_q_heads, lay.num_kv_heads, D,
                                   lay.elem_bytes)
-        roof = hbm_roof(f"stream_decode_kernel ({n_tok} tokens folded)", nb["total"], float(sum(kern_avg)),
+        rows = 2
+        while rows < lay.gqa_ratio * fold:
+            rows *= 2
+        roof = hbm_roof(f"{stream_kernel(rows)} ({n_tok} tokens folded)", nb["total"], float(sum(kern_avg)),
                         measured_traffic(args.workload))
         extra = {"tokens_per_step": int(T), "fold_passes": pairs,
                  "mixed_chunk_same_batch_ms": round(timed(mixed_step, args.steps), 5)}
@@ -395,7 +402,7 @@ def main():
             dec = lay.q_lens == 1
             dbytes = roofline.decode_bytes(lay.context_lens[dec], lay.num_q_heads, lay.num_kv_heads, D,
                                            lay.elem_bytes)["total"]
-            dec_roof = hbm_roof("stream_decode_kernel (decode tokens)", dbytes, kern_avg[1], None)
+            dec_roof = hbm_roof(f"{stream_kernel(lay.gqa_ratio)} (decode tokens)", dbytes, kern_avg[1], None)
             # the dominant kernel is the one that takes longer
             roof, other = (chunk_roof, dec_roof) if kern_avg[0] >= kern_avg[1] else (dec_roof, chunk_roof)
             extra["other_kernel_roofline"] = other
@@ -407,7 +414,7 @@ def main():
         # the rows each query sees: the last min(L, window) of its sequence
         nb = roofline.decode_bytes(np.minimum(lay.context_lens, lay.window), lay.num_q_heads, lay.num_kv_heads, D,
                                    lay.elem_bytes)
-        roof = hbm_roof("stream_decode_kernel (sliding window)", nb["total"], kern_avg[0],
+        roof = hbm_roof(f"{stream_kernel(lay.gqa_ratio)} (sliding window)", nb["total"], kern_avg[0],
                         measured_traffic(args.workload))
     elif fp8:
         nb = roofline.decode_fp8_bytes(lay.context_lens, lay.num_q_heads, lay.num_kv_heads, D)
@@ -415,7 +422,7 @@ def main():
                         measured_traffic(args.workload))
     else:
         nb = roofline.decode_bytes(lay.context_lens, lay.num_q_heads, lay.num_kv_heads, D, lay.elem_bytes)
-        roof = hbm_roof("stream_decode_kernel", nb["total"], kern_avg[0], measured_traffic(args.workload))
+        roof = hbm_roof(stream_kernel(lay.gqa_ratio), nb["total"], kern_avg[0], measured_traffic(args.workload))
     gbs = nb["total"] / (ms_per_step * 1e-3) / 1e9
     result = {
         "metric": "paged decode attn KV GB/s (% of HBM peak) + decode tokens/s, Llama-8B shape",

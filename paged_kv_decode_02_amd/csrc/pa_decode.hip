@@ -942,7 +942,7 @@ __global__ __launch_bounds__(64) void stream_mfma_kernel(
                 make_uint2(bf16x2_rne(o[db][0] * inv, o[db][1] * inv), bf16x2_rne(o[db][2] * inv, o[db][3] * inv));
           if (lse_out && lg == 0) lse_out[row] = lse2 * kLn2;
         }
-      } else {
+      } else if (active) {  // (idle rows leave no partial; the merge skips them)
         const int64_t r = ((static_cast<int64_t>(w) * Hkv + kvh) * 2 + slot) * R + col;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -965,7 +965,9 @@ __global__ __launch_bounds__(64) void stream_mfma_kernel(
 // sum_w a_w with a_w = 2^(lse_w - max lse), lse = max + log2(sum a_w).  Lane
 // j holds wave j's weights; lane d holds output columns; four waves'
 // partial rows are loaded together.
-template <typename T, int D, int G, bool MT>
+// G: partial rows per (wave, kv-head, slot); NA <= G: the rows merged
+// (the active ones: rows past NA were never written).
+template <typename T, int D, int G, int NA, bool MT>
 __global__ __launch_bounds__(64) void merge_kernel(T* __restrict__ out, float* __restrict__ lse_out, int Hkv, int W,
                                                    const int32_t* __restrict__ seq_info,
                                                    const float* __restrict__ part_o,
@@ -987,27 +989,27 @@ __global__ __launch_bounds__(64) void merge_kernel(T* __restrict__ out, float* _
     const int slot = j == 0 ? slot0 : 0;
     return ((static_cast<int64_t>(w0 + j) * Hkv + kvh) * 2 + slot) * G + h;
   };
-  float M[G];
+  float M[NA];
 #pragma unroll
-  for (int h = 0; h < G; ++h) M[h] = -INFINITY;
+  for (int h = 0; h < NA; ++h) M[h] = -INFINITY;
   for (int j = lane; j < n; j += 64) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) M[h] = fmaxf(M[h], part_lse[prow(j, h)]);
+    for (int h = 0; h < NA; ++h) M[h] = fmaxf(M[h], part_lse[prow(j, h)]);
   }
 #pragma unroll
-  for (int h = 0; h < G; ++h) M[h] = wave_max(M[h]);
-  float acc[G][EPL], wsum[G];
+  for (int h = 0; h < NA; ++h) M[h] = wave_max(M[h]);
+  float acc[NA][EPL], wsum[NA];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
+  for (int h = 0; h < NA; ++h) {
     wsum[h] = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
   for (int j0 = 0; j0 < n; j0 += 64) {
     const int j = j0 + lane;
-    float wt[G];
+    float wt[NA];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+    for (int h = 0; h < NA; ++h) {
       wt[h] = j < n ? fast_exp2(part_lse[prow(min(j, n - 1), h)] - M[h]) : 0.f;
       wsum[h] += wt[h];
     }
@@ -1017,7 +1019,7 @@ __global__ __launch_bounds__(64) void merge_kernel(T* __restrict__ out, float* _
       for (int u = 0; u < 4; ++u) {
         const int jx = min(jj + u, cnt - 1);
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
+        for (int h = 0; h < NA; ++h) {
           const float* src = part_o + prow(j0 + jx, h) * D + lane * EPL;
           const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt[h]), jx));
           const float a = (jj + u < cnt) ? wj : 0.f;
@@ -1028,8 +1030,8 @@ __global__ __launch_bounds__(64) void merge_kernel(T* __restrict__ out, float* _
     }
   }
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    if ((h >> fold.lg) >= fold.fe) continue;  // idle row
+  for (int h = 0; h < NA; ++h) {
+    if ((h >> fold.lg) >= fold.fe) continue;  // idle row of a folded pass
     const float ws = wave_sum(wsum[h]);
     const float inv = 1.0f / ws;
     const int64_t row = MT ? (static_cast<int64_t>(s) * fold.n + fold.tok0 + (h >> fold.lg)) * Hq + kvh * GH +
@@ -1120,9 +1122,14 @@ int launch_typed(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_p
   // Unless one wave covers everything, some sequence may be shared; the
   // merge kernel skips the sequences one wave covered.
   if (merge && W > 1) {
-    hipLaunchKernelGGL((merge_kernel<T, D, G, MT>), dim3(a.num_seqs, a.num_kv_heads), dim3(64), 0, st,
-                       static_cast<T*>(a.out), a.lse_out, a.num_kv_heads, static_cast<int>(W), seq_info, part_o,
-                       part_lse, q_rows, fold);
+    // Rows merged: all of a folded pass's (idle ones are skipped at the
+    // write), else the q-heads (8 of the matrix-core kernel's 16 rows when
+    // gqa_ratio is 8).
+    auto mk = merge_kernel<T, D, G, G, MT>;
+    if constexpr (G == 16 && !MT)
+      if (a.gqa == 8) mk = merge_kernel<T, D, G, 8, MT>;
+    hipLaunchKernelGGL(mk, dim3(a.num_seqs, a.num_kv_heads), dim3(64), 0, st, static_cast<T*>(a.out), a.lse_out,
+                       a.num_kv_heads, static_cast<int>(W), seq_info, part_o, part_lse, q_rows, fold);
     if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_decode: merge kernel launch failed");
   }
   return PA_OK;
