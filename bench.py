@@ -451,7 +451,8 @@ def main():
             "parallelism": "single GPU",
         },
         "hbm_frac": round(gbs / roofline.HBM_PEAK_GBS, 4),
-        "decode_tokens_per_s_32_layers": round(int((lay.q_lens == 1).sum()) /
+        # (a multi-token decode step decodes every one of its tokens)
+        "decode_tokens_per_s_32_layers": round(int(T if multi else (lay.q_lens == 1).sum()) /
                                                (roofline.LLAMA8B_LAYERS * ms_per_step * 1e-3), 1),
         "algorithmic_bytes_per_step": nb["total"],
         "wall_s": round(wall, 3),
