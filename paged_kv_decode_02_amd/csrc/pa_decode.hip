@@ -965,8 +965,9 @@ __global__ __launch_bounds__(64) void stream_mfma_kernel(
 // sum_w a_w with a_w = 2^(lse_w - max lse), lse = max + log2(sum a_w).  Lane
 // j holds wave j's weights; lane d holds output columns; four waves'
 // partial rows are loaded together.
-// G: partial rows per (wave, kv-head, slot); NA <= G: the rows merged
-// (the active ones: rows past NA were never written).
+// G: partial rows per (wave, kv-head, slot).  A workgroup merges NA of
+// them, rows NA * blockIdx.z .. +NA-1 (the grid covers only rows that can
+// be active: rows past gqa_ratio of a 16-row wave were never written).
 template <typename T, int D, int G, int NA, bool MT>
 __global__ __launch_bounds__(64) void merge_kernel(T* __restrict__ out, float* __restrict__ lse_out, int Hkv, int W,
                                                    const int32_t* __restrict__ seq_info,
@@ -984,10 +985,11 @@ __global__ __launch_bounds__(64) void merge_kernel(T* __restrict__ out, float* _
   const int slot0 = seq_info[4 * s + 2];
   if (w1 <= w0 || w0 < 0 || w1 >= W || slot0 < 0 || slot0 > 1) return;
   const int n = w1 - w0 + 1;
-  // Partial row of (wave w0 + j, head h).
+  const int r0 = NA * blockIdx.z;  // first row of this workgroup
+  // Partial row of (wave w0 + j, row r0 + h).
   auto prow = [&](int j, int h) -> int64_t {
     const int slot = j == 0 ? slot0 : 0;
-    return ((static_cast<int64_t>(w0 + j) * Hkv + kvh) * 2 + slot) * G + h;
+    return ((static_cast<int64_t>(w0 + j) * Hkv + kvh) * 2 + slot) * G + r0 + h;
   };
   float M[NA];
 #pragma unroll
@@ -1031,12 +1033,13 @@ __global__ __launch_bounds__(64) void merge_kernel(T* __restrict__ out, float* _
   }
 #pragma unroll
   for (int h = 0; h < NA; ++h) {
-    if ((h >> fold.lg) >= fold.fe) continue;  // idle row of a folded pass
+    const int r = r0 + h;  // row of the wave
+    if ((r >> fold.lg) >= fold.fe) continue;  // idle row of a folded pass
     const float ws = wave_sum(wsum[h]);
     const float inv = 1.0f / ws;
-    const int64_t row = MT ? (static_cast<int64_t>(s) * fold.n + fold.tok0 + (h >> fold.lg)) * Hq + kvh * GH +
-                                 (h & (GH - 1))
-                           : (q_rows ? q_rows[s] : s) * static_cast<int64_t>(Hq) + kvh * GH + h;
+    const int64_t row = MT ? (static_cast<int64_t>(s) * fold.n + fold.tok0 + (r >> fold.lg)) * Hq + kvh * GH +
+                                 (r & (GH - 1))
+                           : (q_rows ? q_rows[s] : s) * static_cast<int64_t>(Hq) + kvh * GH + r;
     if constexpr (sizeof(T) == 2) {
       if constexpr (EPL == 2) {
         reinterpret_cast<uint32_t*>(out)[row * (D / 2) + lane] =
@@ -1124,12 +1127,12 @@ int launch_typed(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_p
   if (merge && W > 1) {
     // Rows merged: all of a folded pass's (idle ones are skipped at the
     // write), else the q-heads (8 of the matrix-core kernel's 16 rows when
-    // gqa_ratio is 8).
-    auto mk = merge_kernel<T, D, G, G, MT>;
-    if constexpr (G == 16 && !MT)
-      if (a.gqa == 8) mk = merge_kernel<T, D, G, 8, MT>;
-    hipLaunchKernelGGL(mk, dim3(a.num_seqs, a.num_kv_heads), dim3(64), 0, st, static_cast<T*>(a.out), a.lse_out,
-                       a.num_kv_heads, static_cast<int>(W), seq_info, part_o, part_lse, q_rows, fold);
+    // gqa_ratio is 8); up to 4 rows per workgroup.
+    constexpr int NA = G < 4 ? G : 4;
+    const int rows = MT ? G : std::min(G, a.gqa);
+    hipLaunchKernelGGL((merge_kernel<T, D, G, NA, MT>), dim3(a.num_seqs, a.num_kv_heads, rows / NA), dim3(64), 0, st,
+                       static_cast<T*>(a.out), a.lse_out, a.num_kv_heads, static_cast<int>(W), seq_info, part_o,
+                       part_lse, q_rows, fold);
     if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_decode: merge kernel launch failed");
   }
   return PA_OK;
