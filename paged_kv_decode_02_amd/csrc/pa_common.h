@@ -68,6 +68,17 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* lds) {
   return __builtin_bit_cast(u32x2, r);
 }
 
+// ds_read_b64_tr_b8 (gfx950): within each group of 16 lanes, lane j of
+// the group passes the address of 8 consecutive bytes, row j/2 and columns
+// 8(j%2) .. +7 of an 8 x 16 block of bytes; lane j receives column j of
+// that block, rows 0..7 (row k in byte k).
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 LdsI32x2;
+__device__ __forceinline__ u32x2 lds_read_tr8(const void* lds) {
+  const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LdsI32x2*)(lds));
+  return __builtin_bit_cast(u32x2, r);
+}
+
 // D = A B + C on one 16 x 16 x 32 bf16 tile (v_mfma_f32_16x16x32_bf16).
 // Lane l holds A row l % 16, B column l % 16, each at k = 8 (l / 16) ..
 // +7 (8 bf16 in a u32x4, element 0 in the low half of x), and D/C column

@@ -698,28 +698,41 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
 //    accumulates row l % 16, columns 16 db + 4 (l / 16) + i.
 // Each wave's matrix work per batch is 32 MFMAs where the vector path
 // needs about 2000 dot2 instructions for 16 rows.
-template <int D, bool MT>
+// fp8 pools (TKV = uint8_t, e4m3fn codes with a float32 scale per row):
+// K operands come from 8-byte reads of the codes widened to bf16 pairs
+// (exact), V^T operands from ds_read_b64_tr_b8 (lane j of a 16-lane group
+// passes row j/2, bytes 8 (j % 2) .. +7 of an 8 x 16-byte block and
+// receives column j, rows 0..7), widened the same way; the K scale of a row
+// multiplies its scores, its V scale the probability P^T carries (the
+// normaliser sums the plain probabilities), as in the vector fp8 path.
+template <typename TKV, int D, bool MT>
 __global__ __launch_bounds__(64) void stream_mfma_kernel(
     uint16_t* __restrict__ out, float* __restrict__ lse_out, const uint16_t* __restrict__ q,
-    const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool, const float* __restrict__ k_scales,
+    const TKV* __restrict__ k_pool, const TKV* __restrict__ v_pool, const float* __restrict__ k_scales,
     const float* __restrict__ v_scales, const int32_t* __restrict__ block_tables, const int32_t* __restrict__ ctx,
     int max_blocks, int S, int Hkv, int num_pages, float scale_log2, int per, int total_pages,
     int32_t* __restrict__ seq_info, float* __restrict__ part_o, float* __restrict__ part_lse,
     const int32_t* __restrict__ begin_pages, float* __restrict__ seq_part, const int32_t* __restrict__ q_rows,
     int window, Fold fold) {
-  using Gm = Geom<uint16_t, D>;
+  using Gm = Geom<TKV, D>;
+  constexpr bool FP8 = sizeof(TKV) == 1;
   constexpr int R = 16;  // query rows
   constexpr int RD = Gm::RD, NCH = Gm::NCH, TILE = Gm::TILE, NI = Gm::NI;
-  constexpr int NK = NI, NV = NI;  // loads of one issue_k / issue_v
-  constexpr int QNCH = NCH;        // 16-byte chunks of one q row
+  constexpr int NK = NI + (FP8 ? 2 : 0), NV = NI;  // loads of one issue_k (+ the K and V scales) / issue_v
+  constexpr int QNCH = D / 8;                      // 16-byte chunks of one bf16 q row
   constexpr int QPL = R * QNCH / 64;
   constexpr int KC = D / 32;  // 32-column steps of the scores
   constexpr int DB = D / 16;  // 16-column blocks of the output
   constexpr int per_tile = TILE / 1024;
   static_assert(NV + NK <= 63, "vmcnt counts at most 63 loads");
+  static_assert(!FP8 || !MT, "folded passes read bf16 or float32 pools");
   __shared__ uint4 k_lds[64 * NCH];
   __shared__ uint4 v_lds[64 * NCH];
   __shared__ uint4 q_lds[2][QPL * 64];  // two sequences' q rows (current, next)
+  // fp8: the scales of the batch's K and V rows, two batches' worth (the
+  // next batch's land while this one's are still read)
+  __shared__ float4 ks_lds[2][FP8 ? 16 : 1];
+  __shared__ float4 vs_lds[2][FP8 ? 16 : 1];
 
   const int lane = lane_id();
   const int col = lane & 15;  // query row of this lane (C/D column; B column)
@@ -761,6 +774,20 @@ __global__ __launch_bounds__(64) void stream_mfma_kernel(
       dma16(tile + koff[i % per_tile], base + i * 1024);
     }
   };
+  // fp8: lane r fetches the scales of batch row r (page r / 16, slot r % 16)
+  // into scale buffer sb, with the batch's K.
+  auto issue_k = [&](const Batch& b, int sb) {
+    issue_tiles(kbytes, b, k_base);
+    if constexpr (FP8) {
+      // (values first: a select over the array itself would keep the batch
+      // in scratch memory)
+      const int p0 = b.pid[0], p1 = b.pid[1], p2 = b.pid[2], p3 = b.pid[3];
+      const int pl = lane < 32 ? (lane < 16 ? p0 : p1) : (lane < 48 ? p2 : p3);
+      const int64_t at = (static_cast<int64_t>(pl) * Hkv + kvh) * 16 + (lane & 15);
+      dma4(k_scales + at, lds_offset(&ks_lds[sb][0]));
+      dma4(v_scales + at, lds_offset(&vs_lds[sb][0]));
+    }
+  };
 
   // Row r of the wave: q-head r of the kv-head, or (MT) token tok0 + (r >>
   // lg) and head r & (g-1); idle rows repeat the last active row.
@@ -793,14 +820,15 @@ __global__ __launch_bounds__(64) void stream_mfma_kernel(
   const bool active = tok < fold.fe;
 
   Batch cur = first, nxt;
+  int sb = 0;  // scale buffer of the current batch (fp8)
   load_q(cur.s, cur.qb);
-  issue_tiles(kbytes, cur, k_base);
+  issue_k(cur, sb);
   issue_tiles(vbytes, cur, v_base);
 
   while (true) {
     const bool has_next = walk.advance(cur, nxt);
-    // K (and q, loaded before it) of this batch have landed once only this
-    // batch's V may be outstanding.
+    // K (and q, loaded before it, and the fp8 scales) of this batch have
+    // landed once only this batch's V may be outstanding.
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NV) : "memory");
     lds_order();
     if (has_next && nxt.s != cur.s) load_q(nxt.s, nxt.qb);
@@ -816,13 +844,23 @@ __global__ __launch_bounds__(64) void stream_mfma_kernel(
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const int key = kb * 16 + col;
-        const u32x4 a = *(LdsU4*)(&k_lds[key * NCH + ((c * 4 + lg) ^ Gm::swz(key))]);
+        u32x4 a;
+        if constexpr (FP8) {
+          // codes 32 c + 8 lg .. +7 of the row: half of a swizzled chunk
+          const int ch = (2 * c + (lg >> 1)) ^ Gm::swz(key);
+          const u32x2 w8 = *(__attribute__((address_space(3))) const u32x2*)(
+              reinterpret_cast<const char*>(k_lds) + key * (RD * 4) + ch * 16 + (lg & 1) * 8);
+          a = u32x4{fp8x2_to_bf16x2<false>(w8.x), fp8x2_to_bf16x2<true>(w8.x), fp8x2_to_bf16x2<false>(w8.y),
+                    fp8x2_to_bf16x2<true>(w8.y)};
+        } else {
+          a = *(LdsU4*)(&k_lds[key * NCH + ((c * 4 + lg) ^ Gm::swz(key))]);
+        }
         sc[kb] = mfma16x16x32(a, qb, sc[kb]);
       }
     }
     // Every read of this batch's K is done: the next K may land.
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (has_next) issue_tiles(kbytes, nxt, k_base);
+    if (has_next) issue_k(nxt, sb ^ 1);
 
     // Online softmax of this lane's row over its 16 batch rows.
     const int nvalid = min(cur.seg_hi * 16, cur.L) - cur.pb * 16;  // rows of this batch (1..64)
@@ -832,13 +870,17 @@ __global__ __launch_bounds__(64) void stream_mfma_kernel(
     float x[4][4];
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 4; ++kb) {
+      // fp8: the K scales of this lane's 4 rows of the block
+      const float4 ksc = FP8 ? ks_lds[sb][FP8 ? kb * 4 + lg : 0] : make_float4(1.f, 1.f, 1.f, 1.f);
+      const float kq[4] = {ksc.x, ksc.y, ksc.z, ksc.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = kb * 16 + lg * 4 + i;
-        x[kb][i] = key < hi_b && key >= lo_b ? sc[kb][i] * scale_log2 : -INFINITY;
+        x[kb][i] = key < hi_b && key >= lo_b ? sc[kb][i] * (FP8 ? kq[i] * scale_log2 : scale_log2) : -INFINITY;
         mx = fmaxf(mx, x[kb][i]);
       }
+    }
     mx = max_xor32(max_xor16(mx));
     const float mn = fmaxf(m, mx);
     // (a row that has seen nothing yet keeps m = -inf: exponents are then
@@ -854,12 +896,18 @@ __global__ __launch_bounds__(64) void stream_mfma_kernel(
     for (int ks = 0; ks < 2; ++ks) {
       float p[2][4];
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h) {
+        const float4 vsc = FP8 ? vs_lds[sb][FP8 ? (2 * ks + h) * 4 + lg : 0] : make_float4(1.f, 1.f, 1.f, 1.f);
+        const float vq[4] = {vsc.x, vsc.y, vsc.z, vsc.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           p[h][i] = fast_exp2(x[2 * ks + h][i] - mref);
           lsum += p[h][i];
+          // fp8: P^T carries p times the row's V scale (0 for rows not
+          // seen, whose scale may be NaN)
+          if constexpr (FP8) p[h][i] = x[2 * ks + h][i] == -INFINITY ? 0.f : p[h][i] * vq[i];
         }
+      }
       // k slots 8 lg .. 8 lg + 7 = batch rows 32 ks + 4 lg + [0, 4) and
       // 32 ks + 16 + 4 lg + [0, 4): the order the V^T operand uses.
       pb[ks] = u32x4{bf16x2_rne(p[0][0], p[0][1]), bf16x2_rne(p[0][2], p[0][3]), bf16x2_rne(p[1][0], p[1][1]),
@@ -892,14 +940,26 @@ __global__ __launch_bounds__(64) void stream_mfma_kernel(
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        u32x2 part[2];
+        u32x4 a;
+        if constexpr (FP8) {
+          // one transposed read of 8 rows: lanes 2r, 2r+1 name row r of
+          // the block, the batch rows in P^T's order
+          const int r8 = col >> 1;
+          const int row = ks * 32 + (r8 >> 2) * 16 + lg * 4 + (r8 & 3);
+          const u32x2 w8 = lds_read_tr8(vb + row * (RD * 4) + (db ^ Gm::swz(row)) * 16 + (col & 1) * 8);
+          a = u32x4{fp8x2_to_bf16x2<false>(w8.x), fp8x2_to_bf16x2<true>(w8.x), fp8x2_to_bf16x2<false>(w8.y),
+                    fp8x2_to_bf16x2<true>(w8.y)};
+        } else {
+          u32x2 part[2];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int row = ks * 32 + e * 16 + lg * 4 + tr_r;
-          const int ch = (db * 2 + (tr_c >> 1)) ^ Gm::swz(row);
-          part[e] = lds_read_tr16(vb + row * (RD * 4) + ch * 16 + (tr_c & 1) * 8);
+          for (int e = 0; e < 2; ++e) {
+            const int row = ks * 32 + e * 16 + lg * 4 + tr_r;
+            const int ch = (db * 2 + (tr_c >> 1)) ^ Gm::swz(row);
+            part[e] = lds_read_tr16(vb + row * (RD * 4) + ch * 16 + (tr_c & 1) * 8);
+          }
+          a = u32x4{part[0].x, part[0].y, part[1].x, part[1].y};
         }
-        o[db] = mfma16x16x32(u32x4{part[0].x, part[0].y, part[1].x, part[1].y}, pb[ks], o[db]);
+        o[db] = mfma16x16x32(a, pb[ks], o[db]);
       }
     }
     // Every read of this batch's V is done: the next V may land.
@@ -957,6 +1017,7 @@ __global__ __launch_bounds__(64) void stream_mfma_kernel(
     }
     if (!has_next) break;
     cur = nxt;
+    sb ^= 1;
   }
 }
 
@@ -1034,7 +1095,7 @@ __global__ __launch_bounds__(64) void merge_kernel(T* __restrict__ out, float* _
 #pragma unroll
   for (int h = 0; h < NA; ++h) {
     const int r = r0 + h;  // row of the wave
-    if ((r >> fold.lg) >= fold.fe) continue;  // idle row of a folded pass
+    if ((r >> fold.lg) >= fold.fe) continue;  // idle row (past gqa_ratio, or a folded pass's tokens)
     const float ws = wave_sum(wsum[h]);
     const float inv = 1.0f / ws;
     const int64_t row = MT ? (static_cast<int64_t>(s) * fold.n + fold.tok0 + (r >> fold.lg)) * Hq + kvh * GH +
@@ -1076,8 +1137,8 @@ int launch_typed(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_p
   static std::atomic<int> occ_cache[64];
   // Waves of 16 bf16 query rows run on the matrix cores.
   auto kern = [] {
-    if constexpr (G == 16 && sizeof(T) == 2 && sizeof(TKV) == 2)
-      return stream_mfma_kernel<D, MT>;
+    if constexpr (G == 16 && sizeof(T) == 2)
+      return stream_mfma_kernel<TKV, D, MT>;
     else
       return stream_decode_kernel<T, TKV, D, G, MT>;
   }();
@@ -1125,12 +1186,13 @@ int launch_typed(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_p
   // Unless one wave covers everything, some sequence may be shared; the
   // merge kernel skips the sequences one wave covered.
   if (merge && W > 1) {
-    // Rows merged: all of a folded pass's (idle ones are skipped at the
-    // write), else the q-heads (8 of the matrix-core kernel's 16 rows when
-    // gqa_ratio is 8); up to 4 rows per workgroup.
+    // Rows merged: all of a folded pass's, else the q-heads (gqa_ratio of
+    // the matrix-core kernel's 16 rows); up to 4 rows per workgroup (idle
+    // rows in the last group are skipped at the write).
     constexpr int NA = G < 4 ? G : 4;
     const int rows = MT ? G : std::min(G, a.gqa);
-    hipLaunchKernelGGL((merge_kernel<T, D, G, NA, MT>), dim3(a.num_seqs, a.num_kv_heads, rows / NA), dim3(64), 0, st,
+    hipLaunchKernelGGL((merge_kernel<T, D, G, NA, MT>), dim3(a.num_seqs, a.num_kv_heads, (rows + NA - 1) / NA),
+                       dim3(64), 0, st,
                        static_cast<T*>(a.out), a.lse_out, a.num_kv_heads, static_cast<int>(W), seq_info, part_o,
                        part_lse, q_rows, fold);
     if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_decode: merge kernel launch failed");
@@ -1144,31 +1206,35 @@ int launch_g(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_part,
   switch (a.gqa) {
     case 1: return launch_typed<T, TKV, D, 1>(a, begin_pages, seq_part, q_rows, merge, plan);
     case 2: return launch_typed<T, TKV, D, 2>(a, begin_pages, seq_part, q_rows, merge, plan);
-    case 4: return launch_typed<T, TKV, D, 4>(a, begin_pages, seq_part, q_rows, merge, plan);
+    case 4:
     case 8:
-      // bf16 pools: the matrix-core kernel, half its 16 rows idle, streams
-      // faster than the vector kernel's 8 rows
-      if constexpr (sizeof(T) == 2 && sizeof(TKV) == 2)
+      // bf16 q (bf16 or fp8 pools): the matrix-core kernel, with 12 or 8
+      // of its 16 rows idle, streams faster than the vector kernel's 4 or
+      // 8 rows (for 1 or 2 rows the two are even)
+      if constexpr (sizeof(T) == 2)
         return launch_typed<T, TKV, D, 16>(a, begin_pages, seq_part, q_rows, merge, plan);
+      else if (a.gqa == 4)
+        return launch_typed<T, TKV, D, 4>(a, begin_pages, seq_part, q_rows, merge, plan);
       else
         return launch_typed<T, TKV, D, 8>(a, begin_pages, seq_part, q_rows, merge, plan);
     case 16:
-      if constexpr (sizeof(TKV) > 1) return launch_typed<T, TKV, D, 16>(a, begin_pages, seq_part, q_rows, merge, plan);
-      break;
+      return launch_typed<T, TKV, D, 16>(a, begin_pages, seq_part, q_rows, merge, plan);
   }
   return fail(PA_EUNSUPPORTED, "pa_decode: gqa_ratio not built");
 }
 
 // Folded multi-token passes: rows = query rows per wave (a power of two);
-// bf16 passes of 8 or 16 rows run on the matrix-core kernel's 16 rows.
+// bf16 passes of 4 to 16 rows run on the matrix-core kernel's 16 rows.
 template <typename T, int D>
 int launch_fold_rows(const DecodeLaunch& a, int rows, const Fold& f) {
   switch (rows) {
     case 2: return launch_typed<T, T, D, 2, true>(a, nullptr, nullptr, nullptr, true, nullptr, &f);
-    case 4: return launch_typed<T, T, D, 4, true>(a, nullptr, nullptr, nullptr, true, nullptr, &f);
+    case 4:
     case 8:
       if constexpr (sizeof(T) == 2)
         return launch_typed<T, T, D, 16, true>(a, nullptr, nullptr, nullptr, true, nullptr, &f);
+      else if (rows == 4)
+        return launch_typed<T, T, D, 4, true>(a, nullptr, nullptr, nullptr, true, nullptr, &f);
       else
         return launch_typed<T, T, D, 8, true>(a, nullptr, nullptr, nullptr, true, nullptr, &f);
     case 16: return launch_typed<T, T, D, 16, true>(a, nullptr, nullptr, nullptr, true, nullptr, &f);
@@ -1197,7 +1263,7 @@ int device_cu_count() {
 }
 
 bool decode_fp8_supported(int32_t head_dim, int32_t gqa) {
-  return head_dim == 128 && (gqa == 1 || gqa == 2 || gqa == 4 || gqa == 8);
+  return head_dim == 128 && (gqa == 1 || gqa == 2 || gqa == 4 || gqa == 8 || gqa == 16);
 }
 
 bool decode_supported(pa_dtype dtype, int32_t head_dim, int32_t gqa) {

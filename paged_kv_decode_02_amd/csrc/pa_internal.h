@@ -33,10 +33,10 @@ struct PartialLayout {
 };
 PartialLayout partial_layout(int64_t waves, int64_t num_seqs, int32_t num_kv_heads, int32_t gqa, int32_t head_dim);
 // Query rows per wave (and partial rows per wave and kv-head) of the
-// stream kernel for `rows` rows of work: 8 or more run on the matrix-core
-// kernel's 16 rows (bf16; other element types use fewer, so sizing by this
-// is enough for every type).
-inline int32_t stream_rows(int32_t rows) { return rows >= 8 ? 16 : rows; }
+// stream kernel for `rows` rows of work: 4 or more run on the matrix-core
+// kernel's 16 rows (bf16 q; float32 uses fewer, so sizing by this is
+// enough for every type).
+inline int32_t stream_rows(int32_t rows) { return rows >= 4 ? 16 : rows; }
 
 // Waves per kv-head the decode planner may use for a batch of total_pages
 // pages: split_pages > 0 fixes the run length, 0 lets the launcher size runs

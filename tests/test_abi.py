@@ -117,7 +117,7 @@ def call_decode_fp8(lib, **kw):
         (dict(k=None), pa.PA_EINVAL),
         (dict(scale=float("nan")), pa.PA_EINVAL),
         (dict(D=64), pa.PA_EUNSUPPORTED),
-        (dict(G=16), pa.PA_EUNSUPPORTED),
+        (dict(G=32), pa.PA_EUNSUPPORTED),
         (dict(BS=8), pa.PA_EUNSUPPORTED),
         (dict(ctx_host=np.array([0, 40], dtype=np.int32)), pa.PA_EINVAL),
         (dict(ws_bytes=64, split=1), pa.PA_EWORKSPACE),

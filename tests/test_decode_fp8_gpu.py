@@ -52,7 +52,7 @@ def fp8_layout(ctx, hq, hkv, seed):
     return lay
 
 
-@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (32, 8), (64, 8), (8, 2)])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (32, 8), (64, 8), (128, 8), (8, 2), (32, 2)])
 def test_shapes_and_ragged_lengths(gpu_lib, hq, hkv):
     ctx = [1, 15, 16, 17, 63, 64, 65, 200, 1000, 2049]
     lay = fp8_layout(ctx, hq, hkv, seed=hq + hkv)
@@ -79,7 +79,8 @@ def test_llama8b_fp8_full(gpu_lib):
     assert torch.isfinite(out.float()).all()
 
 
-def test_needle_gather_is_bit_exact(gpu_lib):
+@pytest.mark.parametrize("hq", [32, 64, 128])
+def test_needle_gather_is_bit_exact(gpu_lib, hq):
     """One row per (sequence, kv-head) scores ~2500 above every other (code
     448, scale 1, against q = 64 on one column), so its weight is exactly 1
     and the output is that V row read back: code value times its scale.
@@ -88,7 +89,9 @@ def test_needle_gather_is_bit_exact(gpu_lib):
     scales at first/last rows, page boundaries and random rows."""
     rng = np.random.default_rng(3)
     ctx = [1, 16, 17, 64, 65, 100, 255, 256, 257, 1000, 4096, 3000]
-    lay = fp8_layout(ctx, 32, 8, seed=5)
+    lay = fp8_layout(ctx, hq, 8, seed=5)
+    G = hq // 8
+    say(f"case fp8 needle hq={hq}")
     q0, kc0, ks0, vc, vs = fp8_values_numpy(lay)
     valid = np.isfinite(vs)
     # V scales with 8 significant bits (exact in bf16)
@@ -96,8 +99,8 @@ def test_needle_gather_is_bit_exact(gpu_lib):
     for trial in range(3):
         kc = np.where(valid[..., None], np.uint8(0), kc0).astype(np.uint8)
         ks = np.where(valid, np.float32(1.0), ks0).astype(np.float32)
-        qf = np.zeros((lay.num_seqs, 32, 128), dtype=np.float32)
-        want = np.zeros((lay.num_seqs, 32, 128), dtype=np.uint16)
+        qf = np.zeros((lay.num_seqs, hq, 128), dtype=np.float32)
+        want = np.zeros((lay.num_seqs, hq, 128), dtype=np.uint16)
         for s, L in enumerate(ctx):
             for g in range(8):
                 if trial == 0:
@@ -109,9 +112,9 @@ def test_needle_gather_is_bit_exact(gpu_lib):
                 j = (s * 8 + g) % 128
                 p = lay.block_tables[s, t // 16]
                 kc[p, g, t % 16, j] = 0x7E
-                qf[s, g * 4:(g + 1) * 4, j] = 64.0
+                qf[s, g * G:(g + 1) * G, j] = 64.0
                 row = of8.dequantize(vc[p, g, t % 16], vs[p, g, t % 16])
-                want[s, g * 4:(g + 1) * 4] = bf16_bits_from_f32(row.astype(np.float32))
+                want[s, g * G:(g + 1) * G] = bf16_bits_from_f32(row.astype(np.float32))
         q = bf16_bits_from_f32(qf)
         ro, _ = oracle_fp8(lay, q, kc, ks, vc, vs)
         ref = bf16_bits_from_f32(ro.astype(np.float32))
@@ -121,7 +124,8 @@ def test_needle_gather_is_bit_exact(gpu_lib):
         assert np.array_equal(got, ref), f"trial {trial}: gather mismatch against the oracle"
 
 
-def test_power_of_two_scales_match_bf16_decode(gpu_lib):
+@pytest.mark.parametrize("hq", [32, 64, 128])
+def test_power_of_two_scales_match_bf16_decode(gpu_lib, hq):
     """With power-of-two scales every read-back value is a bf16 value and
     every scaling is exact, so pa_decode_fp8 computes the same products as
     pa_decode on the read-back bf16 pools (whose parity is tested against
@@ -131,7 +135,7 @@ def test_power_of_two_scales_match_bf16_decode(gpu_lib):
     tolerance, so a mis-applied scale cannot hide in it."""
     rng = np.random.default_rng(8)
     ctx = [5, 33, 100, 640, 1500]
-    lay = fp8_layout(ctx, 32, 8, seed=12)
+    lay = fp8_layout(ctx, hq, 8, seed=12)
     q, kc, _, vc, _ = fp8_values_numpy(lay)
     shape = kc.shape[:3]
     valid = np.isfinite(fp8_values_numpy(lay)[2])
@@ -147,7 +151,7 @@ def test_power_of_two_scales_match_bf16_decode(gpu_lib):
     out16 = torch.empty_like(qd)
     lse16 = torch.empty_like(lse8)
     total_pages = int(sum((int(L) + 15) // 16 for L in ctx))
-    ws = torch.empty(gpu_lib.decode_workspace_size(len(ctx), 8, 4, 128, total_pages, 2), dtype=torch.uint8,
+    ws = torch.empty(gpu_lib.decode_workspace_size(len(ctx), 8, hq // 8, 128, total_pages, 2), dtype=torch.uint8,
                      device="cuda")
     gpu_lib.decode(out16, qd, kbd, vbd, bt, ctxd, lay.context_lens, lay.scale, ws, lse_out=lse16, split_pages=2)
     torch.cuda.synchronize()
