@@ -364,8 +364,9 @@ def main():
                 "traffic": None}
 
     def stream_kernel(rows):
-        # waves of 8 or more bf16 query rows run on the matrix-core kernel
-        return "stream_mfma_kernel" if lay.dtype == "bf16" and not fp8 and rows >= 8 else "stream_decode_kernel"
+        # waves of 4 or more bf16 query rows (bf16 or fp8 pools) run on the
+        # matrix-core kernel
+        return "stream_mfma_kernel" if lay.dtype == "bf16" and rows >= 4 else "stream_decode_kernel"
 
     extra = {}
     if cascade:
@@ -418,7 +419,7 @@ def main():
                         measured_traffic(args.workload))
     elif fp8:
         nb = roofline.decode_fp8_bytes(lay.context_lens, lay.num_q_heads, lay.num_kv_heads, D)
-        roof = hbm_roof("stream_decode_kernel (fp8 pools)", nb["total"], kern_avg[0],
+        roof = hbm_roof(f"{stream_kernel(lay.gqa_ratio)} (fp8 pools)", nb["total"], kern_avg[0],
                         measured_traffic(args.workload))
     else:
         nb = roofline.decode_bytes(lay.context_lens, lay.num_q_heads, lay.num_kv_heads, D, lay.elem_bytes)
