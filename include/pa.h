@@ -76,7 +76,10 @@ enum {
 };
 
 /* Supported shapes: block_size 16; head_dim 64 or 128 (bf16) and 64
- * (float32); gqa_ratio 1, 2, 4, 8 or 16 for decode. */
+ * (float32); gqa_ratio 1, 2, 4, 8 or 16 for decode.  With bf16 q and 4 or
+ * more q-heads per kv-head a wave's 16 query rows run on the matrix cores
+ * (16 x 16 x 32 bf16 MFMA tiles); otherwise on the vector ALUs.  Results
+ * are the same attention either way, within the stated tolerances. */
 
 /* ---------------------------------------------------------------------------
  * Decode: one query token per sequence (T = num_seqs).
@@ -154,7 +157,7 @@ int pa_decode_window(void* out,                 /* device [S, Hq, D] dtype */
  *
  *  k_pool, v_pool   [NP, Hkv, 16, D] uint8 codes (device)
  *  k_scales, v_scales [NP, Hkv, 16] float32 (device)
- * Built for head_dim 128 and gqa_ratio 1, 2, 4, 8.  Errors as pa_decode;
+ * Built for head_dim 128 and gqa_ratio 1, 2, 4, 8, 16.  Errors as pa_decode;
  * PA_EINVAL also for a NULL scale pointer.
  * ------------------------------------------------------------------------- */
 int pa_decode_fp8(void* out,                  /* device [S, Hq, D] bf16 */
