@@ -23,7 +23,9 @@ Readings (the page leaves these open):
 * the division, the clamp and the scale are float32 (the quantiser's tensors
   are float32); the conversion rounds to nearest, ties to even;
 * attention over an fp8 cache is the attention of ``oracle/attention.py``
-  over the read-back (dequantised) K and V rows, computed in float64.
+  over the read-back (dequantised) K and V rows, computed in float64; with
+  several new tokens per sequence (``decode_multi_fp8``) token i sees the
+  rows up to its own position, as in a prefill chunk.
 
 Pins (tests/test_fp8_pins.py):
 * the code table against torch's own ``float8_e4m3fn`` conversion (a library
@@ -37,6 +39,10 @@ Pins (tests/test_fp8_pins.py):
   values bit for bit; brute force on tiny inputs with Python loops;
 * planted mistakes (scale ignored, K scale used for V, FNUZ bias 8) are each
   caught;
+* multi-token decode: q_len 1 equals ``decode_fp8``; with power-of-two
+  scales it equals the pinned chunk oracle (``oracle.mixed_chunk``) on the
+  read-back bf16 values bit for bit; brute force with Python loops; a causal
+  edge one row off and tokens read in the wrong order are caught;
 * the quantising append (``kv_append_fp8``: quantise each new row, then
   place codes and scale as ``oracle.kv_append`` places a row) against a
   brute-force element loop, and its read-back against the new rows within
@@ -161,6 +167,50 @@ def decode_fp8(q, k_codes, k_scales, v_codes, v_scales, block_tables, context_le
             V = _gather_fp8(v_codes, v_scales, block_tables[s], g, L, block_size)
             for h in range(g * G, (g + 1) * G):
                 out[s, h], lse[s, h] = attend(qs[h], K, V, sc)
+    return out, lse
+
+
+def _visible(L: int, q_len: int, i: int) -> int:
+    """Rows new token i of a sequence with L rows (the last q_len new) sees:
+    rows 0 .. L - q_len + i, its own position included."""
+    return L - q_len + i + 1
+
+
+def decode_multi_fp8(q, k_codes, k_scales, v_codes, v_scales, block_tables, context_lens, q_len, scale,
+                     num_kv_heads, block_size, q_dtype="bf16", seqs=None):
+    """q_len new tokens per sequence over an fp8 cache, causal among them
+    (the chunk reading of the attention oracle: token i of a sequence with L
+    rows sees rows up to its own position L - q_len + i).
+
+    ``q`` [S * q_len, Hq, D] stored values, token i of sequence s at row
+    s * q_len + i; pools and scales as :func:`decode_fp8`.  Returns out and
+    lse of the same leading shape in float64; sequences not in ``seqs`` stay
+    NaN.
+    """
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    n = int(q_len)
+    T, Hq, D = q.shape
+    if n < 1 or T != n * len(ctx):
+        raise ValueError("q must hold q_len tokens per sequence")
+    if Hq % num_kv_heads:
+        raise ValueError("q heads must be a multiple of kv heads")
+    G = Hq // num_kv_heads
+    sc = float(np.float32(scale))
+    out = np.full((T, Hq, D), np.nan, dtype=np.float64)
+    lse = np.full((T, Hq), np.nan, dtype=np.float64)
+    for s in (range(len(ctx)) if seqs is None else seqs):
+        L = int(ctx[s])
+        if L < n:
+            raise ValueError(f"sequence {s}: fewer rows than new tokens")
+        for g in range(num_kv_heads):
+            K = _gather_fp8(k_codes, k_scales, block_tables[s], g, L, block_size)
+            V = _gather_fp8(v_codes, v_scales, block_tables[s], g, L, block_size)
+            for i in range(n):
+                row = s * n + i
+                qs = stored_to_f64(q[row], q_dtype)
+                vis = _visible(L, n, i)
+                for h in range(g * G, (g + 1) * G):
+                    out[row, h], lse[row, h] = attend(qs[h], K[:vis], V[:vis], sc)
     return out, lse
 
 

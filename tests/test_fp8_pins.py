@@ -207,8 +207,67 @@ def pin_bruteforce():
     return fails
 
 
+def multi_q(rng, ctx, q_len, hq, d):
+    return bf16_bits_from_f32(rng.standard_normal((len(ctx) * q_len, hq, d)).astype(np.float32))
+
+
+def pin_multi_token_reductions():
+    """q_len 1 is decode_fp8 bit for bit; with power-of-two scales the
+    result equals the (pinned) chunk oracle over the read-back bf16 values,
+    each sequence a segment of q_len tokens, bit for bit."""
+    rng = np.random.default_rng(21)
+    fails = []
+    ctx = [3, 16, 17, 40, 70]
+    lay, q1, kc, ks, vc, vs = fp8_cache(rng, ctx, hkv=2, d=16, block_size=16, pow2_scales=True)
+    a = f8.decode_multi_fp8(q1, kc, ks, vc, vs, lay.block_tables, lay.context_lens, 1, 0.25, 2, 16)
+    b = f8.decode_fp8(q1, kc, ks, vc, vs, lay.block_tables, lay.context_lens, 0.25, 2, 16)
+    if not (np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])):
+        fails.append("q_len 1 differs from decode_fp8")
+    kb = bf16_bits_from_f32(np.nan_to_num(f8.dequantize(kc, ks)).astype(np.float32))
+    vb = bf16_bits_from_f32(np.nan_to_num(f8.dequantize(vc, vs)).astype(np.float32))
+    for n in (2, 3):
+        q = multi_q(rng, ctx, n, 4, 16)
+        out, lse = f8.decode_multi_fp8(q, kc, ks, vc, vs, lay.block_tables, lay.context_lens, n, 0.25, 2, 16)
+        ro, rl = oracle.mixed_chunk(q, kb, vb, lay.block_tables, lay.context_lens, [n] * len(ctx), 0.25, 2, 16,
+                                    "bf16")
+        if not (np.array_equal(out, ro) and np.array_equal(lse, rl)):
+            fails.append(f"q_len {n}: differs from the chunk oracle on read-back values")
+    return fails
+
+
+def pin_multi_token_bruteforce():
+    """Tiny inputs, Python loops: token i sees rows 0 .. L - q_len + i."""
+    rng = np.random.default_rng(9)
+    ctx = [2, 17, 20]
+    hkv, d, bs, n = 1, 4, 16, 2
+    lay, _, kc, ks, vc, vs = fp8_cache(rng, ctx, hkv=hkv, d=d, block_size=bs, pow2_scales=False)
+    q = multi_q(rng, ctx, n, 2, d)
+    out, lse = f8.decode_multi_fp8(q, kc, ks, vc, vs, lay.block_tables, lay.context_lens, n, 0.5, hkv, bs)
+    cv = torch_code_values()
+    qf = oracle.stored_to_f64(q, "bf16")
+    sc = float(np.float32(0.5))
+    fails = []
+    for s, L in enumerate(ctx):
+        for i in range(n):
+            for h in range(2):
+                xs, vrows = [], []
+                for t in range(L - n + i + 1):
+                    p, r = int(lay.block_tables[s, t // bs]), t % bs
+                    k = [cv[kc[p, 0, r, j]] * float(ks[p, 0, r]) for j in range(d)]
+                    vrows.append([cv[vc[p, 0, r, j]] * float(vs[p, 0, r]) for j in range(d)])
+                    xs.append(sc * sum(qf[s * n + i, h, j] * k[j] for j in range(d)))
+                m = max(xs)
+                w = [math.exp(x - m) for x in xs]
+                z = sum(w)
+                o = [sum(w[t] * vrows[t][j] for t in range(len(w))) / z for j in range(d)]
+                if np.max(np.abs(np.array(o) - out[s * n + i, h])) > 1e-12 or \
+                        abs(m + math.log(z) - lse[s * n + i, h]) > 1e-12:
+                    fails.append(f"seq {s} token {i} head {h} differs from brute force")
+    return fails
+
+
 ALL_PINS = [pin_code_table, pin_closed_forms, pin_quantizer_vs_torch, pin_quantizer_properties,
-            pin_attention_vs_bf16_oracle, pin_bruteforce]
+            pin_attention_vs_bf16_oracle, pin_bruteforce, pin_multi_token_reductions, pin_multi_token_bruteforce]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
@@ -327,3 +386,11 @@ def test_kv_append_fp8_bruteforce_and_read_back():
                     step = 2.0 ** (np.floor(np.log2(np.maximum(y, 2.0 ** -6))) - 3)
                     assert np.all(np.abs(back - x) <= (step / 2 + y * 2.0 ** -24) * sc * (1 + 1e-12))
         t += n
+
+
+@pytest.mark.parametrize("name,bad", [("sees one row more", lambda L, n, i: L - n + i + 2),
+                                      ("sees one row less", lambda L, n, i: L - n + i),
+                                      ("tokens reversed", lambda L, n, i: L - i)])
+def test_planted_multi_token_mistake_is_caught(monkeypatch, name, bad):
+    monkeypatch.setattr(f8, "_visible", bad)
+    assert _run_pins(), f"no pin noticed: {name}"
