@@ -134,8 +134,8 @@ def cpu_baseline(lay, q, k, v, total_bytes, budget_s, k_scales=None, v_scales=No
                 kc, vc = k.index_select(0, idx).cpu().numpy(), v.index_select(0, idx).cpu().numpy()
                 ksc, vsc = k_scales.index_select(0, idx).cpu().numpy(), v_scales.index_select(0, idx).cpu().numpy()
                 t0 = time.perf_counter()
-                oracle.decode_fp8(qs, kc, ksc, vc, vsc, bt, lay.context_lens[s : s + 1], lay.scale,
-                                  lay.num_kv_heads, 16, "bf16")
+                oracle.decode_multi_fp8(qs, kc, ksc, vc, vsc, bt, lay.context_lens[s : s + 1], int(lay.q_lens[s]),
+                                        lay.scale, lay.num_kv_heads, 16, "bf16")
             elif lay.window is not None:
                 ks, vs = host(k.index_select(0, idx)), host(v.index_select(0, idx))
                 t0 = time.perf_counter()
@@ -298,8 +298,12 @@ def main():
                                                             args.split_pages), dtype=torch.uint8, device=dev)
 
             def step():
-                pa.decode_multi(out, q, k, v, bt, ctx, lay.context_lens, lay.scale, n_tok, ws,
-                                split_pages=args.split_pages, stream=stream)
+                if fp8:
+                    pa.decode_multi_fp8(out, q, k, v, ks, vs, bt, ctx, lay.context_lens, lay.scale, n_tok, ws,
+                                        split_pages=args.split_pages, stream=stream)
+                else:
+                    pa.decode_multi(out, q, k, v, bt, ctx, lay.context_lens, lay.scale, n_tok, ws,
+                                    split_pages=args.split_pages, stream=stream)
     else:
         ws = torch.empty(pa.decode_workspace_size(S, lay.num_kv_heads, lay.gqa_ratio, D, total_pages,
                                                   args.split_pages), dtype=torch.uint8, device=dev)
@@ -383,15 +387,19 @@ def main():
         extra = {"prefix_gflop": round(flops / 1e9, 3), "decode_same_batch_ms": round(dec_ms, 5),
                  "cascade_speedup_vs_decode": round(dec_ms / ms_per_step, 3)}
     elif multi:
-        nb = roofline.mixed_bytes(lay.context_lens, lay.q_lens, lay.num_q_heads, lay.num_kv_heads, D,
-                                  lay.elem_bytes)
+        if fp8:
+            nb = roofline.decode_fp8_bytes(lay.context_lens, lay.num_q_heads, lay.num_kv_heads, D, q_len=n_tok)
+        else:
+            nb = roofline.mixed_bytes(lay.context_lens, lay.q_lens, lay.num_q_heads, lay.num_kv_heads, D,
+                                      lay.elem_bytes)
         rows = 2
         while rows < lay.gqa_ratio * fold:
             rows *= 2
         roof = hbm_roof(f"{stream_kernel(rows)} ({n_tok} tokens folded)", nb["total"], float(sum(kern_avg)),
                         measured_traffic(args.workload))
-        extra = {"tokens_per_step": int(T), "fold_passes": pairs,
-                 "mixed_chunk_same_batch_ms": round(timed(mixed_step, args.steps), 5)}
+        extra = {"tokens_per_step": int(T), "fold_passes": pairs}
+        if not fp8:  # (the chunk path reads bf16 / float32 pools only)
+            extra["mixed_chunk_same_batch_ms"] = round(timed(mixed_step, args.steps), 5)
     elif mixed:
         nb = roofline.mixed_bytes(lay.context_lens, lay.q_lens, lay.num_q_heads, lay.num_kv_heads, D,
                                   lay.elem_bytes)

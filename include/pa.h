@@ -210,6 +210,29 @@ int pa_decode_multi(void* out,                 /* device [S * q_len, Hq, D] dtyp
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Multi-token decode over an fp8 cache: pa_decode_multi's tokens, rows and
+ * causal limits (token i of a sequence with L rows sees rows 0 ..
+ * L - q_len + i) over pa_decode_fp8's pools (e4m3fn codes with one float32
+ * scale per (page, kv-head, slot) for K and one for V, tokenspeed 딥다이브
+ * section 6-4); q and out bf16.  Every folded pass runs on the matrix cores.
+ * Workspace: pa_decode_multi_workspace_size.  Built for head_dim 128 and
+ * gqa_ratio 1, 2, 4, 8, 16.  Errors as pa_decode_multi, plus PA_EINVAL for
+ * a NULL scale pointer.  q_len == 1 is pa_decode_fp8 exactly.
+ * ------------------------------------------------------------------------- */
+int pa_decode_multi_fp8(void* out,                 /* device [S * q_len, Hq, D] bf16 */
+                        float* lse_out,            /* device [S * q_len, Hq] or NULL */
+                        const void* q,             /* device [S * q_len, Hq, D] bf16 */
+                        const void* k_pool,        /* device [NP, Hkv, BS, D] e4m3fn codes */
+                        const void* v_pool,        /* device [NP, Hkv, BS, D] e4m3fn codes */
+                        const float* k_scales,     /* device [NP, Hkv, BS] */
+                        const float* v_scales,     /* device [NP, Hkv, BS] */
+                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                        const int32_t* context_lens, const int32_t* context_lens_host,
+                        int32_t num_seqs, int32_t q_len, int32_t num_kv_heads, int32_t gqa_ratio,
+                        int32_t head_dim, int32_t block_size, int64_t num_pages, float scale,
+                        int32_t split_pages, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Shared-prefix (cascade) decode: one query token per sequence, sequences in
  * groups whose block tables start with the same prefix pages (shared blocks,
  * SwiftLLM page section 3.1); the result equals pa_decode on the same

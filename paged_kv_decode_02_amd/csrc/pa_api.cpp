@@ -81,7 +81,7 @@ int decode_call(void* out, float* lse_out, const void* q, const void* k_pool, co
   // a call never depends on the occupancy the device reports.
   // (multi-token passes keep `rows` query rows per wave; the last pass
   // walks every page)
-  const int32_t rows = plan_multi_shape(q_len, gqa_ratio).rows;
+  const int32_t rows = multi_ws_rows(q_len, gqa_ratio);
   const PartialLayout worst = partial_layout(max_waves_per_head(total_pages, num_kv_heads, split_pages), num_seqs,
                                              num_kv_heads, rows, head_dim);
   if (worst.bytes > workspace_bytes)
@@ -162,7 +162,7 @@ extern "C" size_t pa_decode_multi_workspace_size(int32_t max_num_seqs, int32_t q
       split_pages < 0)
     return 0;
   const int64_t waves = max_waves_per_head(max_total_pages, num_kv_heads, split_pages);
-  return partial_layout(waves, max_num_seqs, num_kv_heads, plan_multi_shape(q_len, gqa_ratio).rows, head_dim).bytes;
+  return partial_layout(waves, max_num_seqs, num_kv_heads, multi_ws_rows(q_len, gqa_ratio), head_dim).bytes;
 }
 
 extern "C" int pa_decode_multi(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,
@@ -175,6 +175,19 @@ extern "C" int pa_decode_multi(void* out, float* lse_out, const void* q, const v
   return decode_call(out, lse_out, q, k_pool, v_pool, nullptr, nullptr, false, block_tables, max_blocks, context_lens,
                      context_lens_host, num_seqs, num_kv_heads, gqa_ratio, head_dim, block_size, num_pages, scale,
                      dtype, split_pages, workspace, workspace_bytes, stream, 0, q_len, "pa_decode_multi");
+}
+
+extern "C" int pa_decode_multi_fp8(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,
+                                   const float* k_scales, const float* v_scales, const int32_t* block_tables,
+                                   int32_t max_blocks, const int32_t* context_lens, const int32_t* context_lens_host,
+                                   int32_t num_seqs, int32_t q_len, int32_t num_kv_heads, int32_t gqa_ratio,
+                                   int32_t head_dim, int32_t block_size, int64_t num_pages, float scale,
+                                   int32_t split_pages, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  return decode_call(out, lse_out, q, k_pool, v_pool, k_scales, v_scales, true, block_tables, max_blocks,
+                     context_lens, context_lens_host, num_seqs, num_kv_heads, gqa_ratio, head_dim, block_size,
+                     num_pages, scale, PA_BF16, split_pages, workspace, workspace_bytes, stream, 0, q_len,
+                     "pa_decode_multi_fp8");
 }
 
 extern "C" size_t pa_prefix_cascade_workspace_size(int32_t max_num_seqs, int32_t num_kv_heads, int32_t gqa_ratio,

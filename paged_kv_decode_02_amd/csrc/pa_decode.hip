@@ -725,7 +725,6 @@ __global__ __launch_bounds__(64) void stream_mfma_kernel(
   constexpr int DB = D / 16;  // 16-column blocks of the output
   constexpr int per_tile = TILE / 1024;
   static_assert(NV + NK <= 63, "vmcnt counts at most 63 loads");
-  static_assert(!FP8 || !MT, "folded passes read bf16 or float32 pools");
   __shared__ uint4 k_lds[64 * NCH];
   __shared__ uint4 v_lds[64 * NCH];
   __shared__ uint4 q_lds[2][QPL * 64];  // two sequences' q rows (current, next)
@@ -1223,23 +1222,28 @@ int launch_g(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_part,
   return fail(PA_EUNSUPPORTED, "pa_decode: gqa_ratio not built");
 }
 
-// Folded multi-token passes: rows = query rows per wave (a power of two);
-// bf16 passes of 4 to 16 rows run on the matrix-core kernel's 16 rows.
-template <typename T, int D>
+// Folded multi-token passes: rows = query rows of work per wave (a power
+// of two).  bf16 passes of 4 to 16 rows, and every pass over fp8 pools, run
+// on the matrix-core kernel's 16 rows; the rest on the vector kernel.
+template <typename T, typename TKV, int D>
 int launch_fold_rows(const DecodeLaunch& a, int rows, const Fold& f) {
-  switch (rows) {
-    case 2: return launch_typed<T, T, D, 2, true>(a, nullptr, nullptr, nullptr, true, nullptr, &f);
-    case 4:
-    case 8:
-      if constexpr (sizeof(T) == 2)
-        return launch_typed<T, T, D, 16, true>(a, nullptr, nullptr, nullptr, true, nullptr, &f);
-      else if (rows == 4)
-        return launch_typed<T, T, D, 4, true>(a, nullptr, nullptr, nullptr, true, nullptr, &f);
-      else
-        return launch_typed<T, T, D, 8, true>(a, nullptr, nullptr, nullptr, true, nullptr, &f);
-    case 16: return launch_typed<T, T, D, 16, true>(a, nullptr, nullptr, nullptr, true, nullptr, &f);
+  if constexpr (sizeof(TKV) == 1) {
+    return launch_typed<T, TKV, D, 16, true>(a, nullptr, nullptr, nullptr, true, nullptr, &f);
+  } else {
+    switch (rows) {
+      case 2: return launch_typed<T, TKV, D, 2, true>(a, nullptr, nullptr, nullptr, true, nullptr, &f);
+      case 4:
+      case 8:
+        if constexpr (sizeof(T) == 2)
+          return launch_typed<T, TKV, D, 16, true>(a, nullptr, nullptr, nullptr, true, nullptr, &f);
+        else if (rows == 4)
+          return launch_typed<T, TKV, D, 4, true>(a, nullptr, nullptr, nullptr, true, nullptr, &f);
+        else
+          return launch_typed<T, TKV, D, 8, true>(a, nullptr, nullptr, nullptr, true, nullptr, &f);
+      case 16: return launch_typed<T, TKV, D, 16, true>(a, nullptr, nullptr, nullptr, true, nullptr, &f);
+    }
+    return fail(PA_EUNSUPPORTED, "pa_decode_multi: fold rows not built");
   }
-  return fail(PA_EUNSUPPORTED, "pa_decode_multi: fold rows not built");
 }
 
 // Profiling ring (thread-local).
@@ -1292,7 +1296,7 @@ int launch_decode(const DecodeLaunch& a) { return launch_stream(a, nullptr, null
 
 int launch_decode_multi(const DecodeLaunch& a, const MultiPlan& p) {
   if (p.q_len == 1) return launch_decode(a);
-  if (a.kv_fp8 || a.window != 0) return fail(PA_EUNSUPPORTED, "pa_decode_multi: bf16/f32 pools, no window");
+  if (a.window != 0) return fail(PA_EUNSUPPORTED, "pa_decode_multi: no sliding window");
   if (static_cast<int>(p.pass_pages.size()) != p.passes) return fail(PA_EINVAL, "pa_decode_multi: bad plan");
   Fold f;
   f.n = p.q_len;
@@ -1306,12 +1310,16 @@ int launch_decode_multi(const DecodeLaunch& a, const MultiPlan& p) {
     DecodeLaunch b = a;
     b.total_pages = p.pass_pages[pass];
     int rc = PA_EUNSUPPORTED;
-    if (a.dtype == PA_BF16 && a.head_dim == 128)
-      rc = launch_fold_rows<uint16_t, 128>(b, p.rows, f);
+    if (a.kv_fp8 && a.dtype == PA_BF16 && a.head_dim == 128)
+      rc = launch_fold_rows<uint16_t, uint8_t, 128>(b, p.rows, f);
+    else if (a.kv_fp8)
+      return fail(PA_EUNSUPPORTED, "pa_decode_multi_fp8: shape not built");
+    else if (a.dtype == PA_BF16 && a.head_dim == 128)
+      rc = launch_fold_rows<uint16_t, uint16_t, 128>(b, p.rows, f);
     else if (a.dtype == PA_BF16 && a.head_dim == 64)
-      rc = launch_fold_rows<uint16_t, 64>(b, p.rows, f);
+      rc = launch_fold_rows<uint16_t, uint16_t, 64>(b, p.rows, f);
     else if (a.dtype == PA_F32 && a.head_dim == 64)
-      rc = launch_fold_rows<float, 64>(b, p.rows, f);
+      rc = launch_fold_rows<float, float, 64>(b, p.rows, f);
     else
       return fail(PA_EUNSUPPORTED, "pa_decode_multi: shape not built");
     if (rc) return rc;

@@ -44,7 +44,7 @@ MultiPlan plan_multi_shape(int32_t q_len, int32_t gqa) {
   MultiPlan p;
   p.q_len = std::max(1, q_len);
   if (p.q_len == 1) {
-    p.rows = stream_rows(gqa);  // plain decode
+    p.rows = gqa;  // plain decode
     return p;
   }
   // The fold factor of the TokenSpeed deep-dive (section 7.2) against the
@@ -53,7 +53,7 @@ MultiPlan plan_multi_shape(int32_t q_len, int32_t gqa) {
   p.fold = std::max(1, std::min(p.q_len, kMaxFoldRows / std::max(1, gqa)));
   int32_t rows = 2;
   while (rows < gqa * p.fold) rows <<= 1;
-  p.rows = stream_rows(rows);
+  p.rows = rows;
   p.passes = (p.q_len + p.fold - 1) / p.fold;
   return p;
 }

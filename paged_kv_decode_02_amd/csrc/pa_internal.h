@@ -80,7 +80,8 @@ struct DecodeLaunch {
 // `fold` tokens of every sequence share one pass over its pages, their
 // (token, head) rows folded into the wave's query rows (`rows`, the power
 // of two >= gqa * fold); passes = ceil(q_len / fold), pass p covering
-// tokens p*fold .. and walking each context up to its last token.
+// tokens p*fold .. and walking each context up to its last token.  The
+// workspace is sized for multi_ws_rows partial rows per wave.
 constexpr int kMaxFoldRows = 16;  // query rows one wave holds
 struct MultiPlan {
   int32_t q_len = 1;
@@ -94,6 +95,10 @@ MultiPlan plan_multi_shape(int32_t q_len, int32_t gqa);
 MultiPlan plan_multi(int32_t q_len, int32_t gqa, const int32_t* context_lens_host, int32_t num_seqs,
                      int32_t block_size);
 int launch_decode_multi(const DecodeLaunch& a, const MultiPlan& p);
+// Partial rows per wave a multi-token call's workspace holds: the stream
+// kernel's for one token; 16 for folded passes (every fp8 pass, and bf16
+// passes of 4 or more rows, run on the matrix-core kernel's 16 rows).
+inline int32_t multi_ws_rows(int32_t q_len, int32_t gqa) { return q_len > 1 ? 16 : stream_rows(gqa); }
 bool decode_supported(pa_dtype dtype, int32_t head_dim, int32_t gqa);
 bool decode_fp8_supported(int32_t head_dim, int32_t gqa);
 int launch_decode(const DecodeLaunch& a);

@@ -34,6 +34,7 @@ EXPORTS = (
     "pa_decode_window",
     "pa_decode_multi_workspace_size",
     "pa_decode_multi",
+    "pa_decode_multi_fp8",
     "pa_prefix_cascade_workspace_size",
     "pa_prefix_cascade",
     "pa_mixed_chunk_workspace_size",
@@ -84,6 +85,10 @@ def load(path: Optional[str] = None):
     lib.pa_decode_multi.restype = ctypes.c_int
     lib.pa_decode_multi.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                                     c_i32, c_i32, c_i64, ctypes.c_float, ctypes.c_int, c_i32, c_vp, c_sz, c_vp]
+    lib.pa_decode_multi_fp8.restype = ctypes.c_int
+    lib.pa_decode_multi_fp8.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32,
+                                        c_i32, c_i32, c_i32, c_i32, c_i32, c_i64, ctypes.c_float, c_i32, c_vp, c_sz,
+                                        c_vp]
     lib.pa_decode_fp8.restype = ctypes.c_int
     lib.pa_decode_fp8.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32,
                                   c_i32, c_i32, c_i32, c_i64, ctypes.c_float, c_i32, c_vp, c_sz, c_vp]
@@ -293,6 +298,54 @@ def decode_fp8(out, q, k_pool, v_pool, k_scales, v_scales, block_tables, context
         _dev(context_lens, "context_lens", torch.int32),
         ch.ctypes.data,
         S, Hkv, Hq // Hkv, D, BS, NP, float(scale), int(split_pages),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream_ptr(stream),
+    )
+    return _check(rc)
+
+
+def decode_multi_fp8(out, q, k_pool, v_pool, k_scales, v_scales, block_tables, context_lens, context_lens_host,
+                     scale, q_len, workspace, lse_out=None, split_pages=0, stream=None):
+    """pa_decode_multi_fp8 on torch tensors: :func:`decode_multi`'s tokens
+    (q / out ``[S * q_len, Hq, D]`` bfloat16) over :func:`decode_fp8`'s
+    pools and scales."""
+    import torch
+
+    T, Hq, D = q.shape
+    NP, Hkv, BS, D2 = k_pool.shape
+    q_len = int(q_len)
+    if q_len < 1 or T % q_len:
+        raise ValueError("q rows must be num_seqs * q_len")
+    S = T // q_len
+    if q.dtype != torch.bfloat16 or tuple(out.shape) != (T, Hq, D) or out.dtype != torch.bfloat16:
+        raise ValueError("q and out must be bfloat16 [S * q_len, Hq, D]")
+    codes = (torch.uint8, torch.float8_e4m3fn)
+    if tuple(v_pool.shape) != tuple(k_pool.shape) or k_pool.dtype not in codes or v_pool.dtype not in codes:
+        raise ValueError("k_pool and v_pool must be [NP, Hkv, BS, D] uint8 / float8_e4m3fn")
+    for t, nm in ((k_scales, "k_scales"), (v_scales, "v_scales")):
+        if tuple(t.shape) != (NP, Hkv, BS) or t.dtype != torch.float32:
+            raise ValueError(f"{nm} must be float32 [NP, Hkv, BS]")
+    if D2 != D or Hq % Hkv:
+        raise ValueError("head_dim mismatch or q heads not a multiple of kv heads")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_tables / context_lens must have one row per sequence")
+    ch = _host_i32(context_lens_host, "context_lens_host")
+    if ch.size != S:
+        raise ValueError("context_lens_host must have one entry per sequence")
+    if lse_out is not None and tuple(lse_out.shape) != (T, Hq):
+        raise ValueError("lse_out must be [S * q_len, Hq]")
+    rc = load().pa_decode_multi_fp8(
+        _dev(out, "out"),
+        _dev(lse_out, "lse_out", torch.float32) if lse_out is not None else None,
+        _dev(q, "q"),
+        _dev(k_pool, "k_pool"),
+        _dev(v_pool, "v_pool"),
+        _dev(k_scales, "k_scales", torch.float32),
+        _dev(v_scales, "v_scales", torch.float32),
+        _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32),
+        ch.ctypes.data,
+        S, q_len, Hkv, Hq // Hkv, D, BS, NP, float(scale), int(split_pages),
         _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream_ptr(stream),
     )
     return _check(rc)

@@ -33,16 +33,18 @@ def decode_bytes(context_lens, num_q_heads, num_kv_heads, head_dim, elem_bytes, 
     return {"kv": kv, "q_out": qo, "tables": tables, "total": kv + qo + tables}
 
 
-def decode_fp8_bytes(context_lens, num_q_heads, num_kv_heads, head_dim, q_elem_bytes=2, block_size=16) -> dict:
+def decode_fp8_bytes(context_lens, num_q_heads, num_kv_heads, head_dim, q_elem_bytes=2, block_size=16,
+                     q_len=1) -> dict:
     """Decode over an fp8 cache: one byte per K and V element plus one
     float32 scale per K row and per V row (per token and kv-head); q and out
-    in their own (bf16) width; table entries as for :func:`decode_bytes`."""
+    of q_len tokens per sequence in their own (bf16) width; table entries as
+    for :func:`decode_bytes`."""
     ctx = np.asarray(context_lens, dtype=np.int64)
     S = ctx.size
     tokens = int(ctx.sum())
     kv = kv_cache_bytes(1, num_kv_heads, head_dim, tokens, 1)
     scales = 2 * num_kv_heads * tokens * 4
-    qo = 2 * S * num_q_heads * head_dim * q_elem_bytes
+    qo = 2 * S * int(q_len) * num_q_heads * head_dim * q_elem_bytes
     tables = 4 * int(((ctx + block_size - 1) // block_size).sum()) + 4 * S
     return {"kv": kv, "scales": scales, "q_out": qo, "tables": tables, "total": kv + scales + qo + tables}
 

@@ -355,15 +355,48 @@ def test_decode_multi_zero_sequences_is_a_no_op():
 
 
 def test_decode_multi_workspace_follows_the_fold():
-    """q_len 1 sizes like plain decode; folded passes keep rows = the power
-    of two >= gqa * min(q_len, 16 / gqa) partial rows per wave."""
+    """q_len 1 sizes like plain decode; folded passes keep 16 partial rows
+    per wave (the matrix-core kernel's; smaller passes fit inside)."""
     for S, P, G in [(1, 1, 4), (64, 9216, 4), (256, 9000, 8), (16, 500, 1), (8, 300, 16)]:
         assert pa.decode_multi_workspace_size(S, 1, 8, G, 128, P, 0) == pa.decode_workspace_size(S, 8, G, 128, P, 0)
         for n in (2, 3, 4, 7):
-            fold = max(1, min(n, 16 // G))
-            rows = 2
-            while rows < G * fold:
-                rows *= 2
-            want = pa.decode_workspace_size(S, 8, rows, 128, P, 3)
+            want = pa.decode_workspace_size(S, 8, 16, 128, P, 3)
             assert pa.decode_multi_workspace_size(S, n, 8, G, 128, P, 3) == want
     assert pa.decode_multi_workspace_size(4, 0, 8, 4, 128, 10, 0) == 0
+
+
+def call_decode_multi_fp8(lib, **kw):
+    args = dict(out=FAKE, lse=None, q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, bt=FAKE, mb=4, ctx=FAKE, ctx_host=None,
+                S=2, n=3, Hkv=2, G=4, D=128, BS=16, NP=10, scale=0.1, split=0, ws=ctypes.c_void_p(0x100000),
+                ws_bytes=1 << 20, stream=None)
+    args.update(kw)
+    ch = args["ctx_host"]
+    if ch is None:
+        ch = np.array([20, 40], dtype=np.int32)
+    return lib.pa_decode_multi_fp8(args["out"], args["lse"], args["q"], args["k"], args["v"], args["ks"], args["vs"],
+                                   args["bt"], args["mb"], args["ctx"], ch.ctypes.data, args["S"], args["n"],
+                                   args["Hkv"], args["G"], args["D"], args["BS"], args["NP"], args["scale"],
+                                   args["split"], args["ws"], args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(ks=None), pa.PA_EINVAL),
+        (dict(vs=None), pa.PA_EINVAL),
+        (dict(n=0), pa.PA_EINVAL),
+        (dict(ctx_host=np.array([2, 40], dtype=np.int32)), pa.PA_EINVAL),  # shorter than q_len
+        (dict(D=64), pa.PA_EUNSUPPORTED),
+        (dict(G=32), pa.PA_EUNSUPPORTED),
+        (dict(ws_bytes=64, split=1), pa.PA_EWORKSPACE),
+    ],
+)
+def test_decode_multi_fp8_rejects_bad_arguments(kw, code):
+    lib = pa.load()
+    assert call_decode_multi_fp8(lib, **kw) == code
+    assert lib.pa_last_error().decode().startswith("pa_decode_multi_fp8")
+
+
+def test_decode_multi_fp8_zero_sequences_is_a_no_op():
+    lib = pa.load()
+    assert call_decode_multi_fp8(lib, S=0, q=None, out=None, ks=None) == pa.PA_OK

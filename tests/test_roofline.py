@@ -63,3 +63,10 @@ def test_fp8_decode_bytes():
     assert 2 * b["kv"] == bf["kv"]  # one byte per element instead of two
     assert b["scales"] == 2 * 8 * 4096 * 4  # a float32 scale per K row and per V row
     assert b["q_out"] == bf["q_out"] and b["tables"] == bf["tables"]
+
+
+def test_fp8_bytes_count_every_new_token():
+    one = roofline.decode_fp8_bytes([100, 2000], 32, 8, 128)
+    four = roofline.decode_fp8_bytes([100, 2000], 32, 8, 128, q_len=4)
+    assert four["q_out"] == 4 * one["q_out"]
+    assert four["total"] - one["total"] == 3 * one["q_out"]

@@ -461,8 +461,17 @@ def _llama8b_multitoken4(seed=0):
                         head_dim=128, seed=seed, name="llama8b_multitoken4")
 
 
+def _llama8b_multitoken4_fp8(seed=0):
+    """The 4-token decode step over an fp8 (e4m3fn) cache."""
+    lay = _llama8b_multitoken4(seed)
+    lay.name = "llama8b_multitoken4_fp8"
+    lay.kv_dtype = "fp8"
+    return lay
+
+
 WORKLOADS = {
     "tiny_f32": _tiny_f32,
+    "llama8b_multitoken4_fp8": _llama8b_multitoken4_fp8,
     "llama8b_multitoken4": _llama8b_multitoken4,
     "llama8b_prefill_append_fp8": _llama8b_prefill_append_fp8,
     "longtail_window4096": _longtail_window4096,
