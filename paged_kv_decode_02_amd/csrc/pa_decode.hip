@@ -1115,9 +1115,10 @@ __global__ __launch_bounds__(64) void merge_kernel(T* __restrict__ out, float* _
   }
 }
 
-// Resident waves of one kernel on the current device (cached per device).
+// Resident waves of one kernel on the current device (cached per device),
+// at most max_per_cu per compute unit.
 template <typename KernelFn>
-int resident_waves(KernelFn fn, std::atomic<int>* cache) {
+int resident_waves(KernelFn fn, std::atomic<int>* cache, int max_per_cu) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   int v = cache[dev].load(std::memory_order_relaxed);
@@ -1125,7 +1126,7 @@ int resident_waves(KernelFn fn, std::atomic<int>* cache) {
   int cus = 0, blocks = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, 64, 0) != hipSuccess) return 0;
-  v = std::max(1, cus * blocks);
+  v = std::max(1, cus * std::min(blocks, max_per_cu));
   cache[dev].store(v, std::memory_order_relaxed);
   return v;
 }
@@ -1135,17 +1136,23 @@ int launch_typed(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_p
                  StreamPlan* plan, const Fold* multi = nullptr) {
   static std::atomic<int> occ_cache[64];
   // Waves of 16 bf16 query rows run on the matrix cores.
+  constexpr bool kMfma = G == 16 && sizeof(T) == 2;
   auto kern = [] {
-    if constexpr (G == 16 && sizeof(T) == 2)
+    if constexpr (kMfma)
       return stream_mfma_kernel<TKV, D, MT>;
     else
       return stream_decode_kernel<T, TKV, D, G, MT>;
   }();
+  // The matrix-core kernel streams best at 4 waves per CU: its fp8 form
+  // fits 6, which made shorter runs and more shared-sequence partials and
+  // ran 8 % slower (61.9 against 56.7 us on the Llama-shaped fp8 batch);
+  // 3 or 2 were slower still.
+  constexpr int kWavesPerCu = kMfma ? 4 : 64;
   int64_t per = a.split_pages;
   if (per <= 0) {
     // Fill the GPU once: as many waves as can be resident, spread over the
     // kv-heads, each streaming the same number of pages.
-    const int res = resident_waves(kern, occ_cache);
+    const int res = resident_waves(kern, occ_cache, kWavesPerCu);
     if (res <= 0) return fail(PA_EHIP, "pa_decode: occupancy query failed");
     const int64_t per_head = std::max<int64_t>(1, std::min<int64_t>(res, kMaxResidentWaves) / a.num_kv_heads);
     per = std::max<int64_t>(kMinPagesPerWave, (a.total_pages + per_head - 1) / per_head);
