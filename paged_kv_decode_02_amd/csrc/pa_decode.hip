@@ -1,4 +1,4 @@
-// Paged decode attention for gfx950 (MI355X): stream-K split-KV kernel and
+// Paged decode attention for gfx950 (MI355X): stream-K split-KV kernels and
 // log-sum-exp merge.
 //
 // Work split.  For each kv-head, the pages of all sequences are laid end to
@@ -13,16 +13,20 @@
 // reduction the TokenSpeed deep-dive describes (sections 7 and 7.1), with
 // the splits placed by byte count instead of a fixed split count.
 //
-// Inside a wave: batches of 4 pages (64 rows) of one sequence.
-//  * K: the 4 (page, kv-head) tiles go straight from HBM into LDS with
-//    16-byte global_load_lds (1 KB contiguous per instruction), XOR-swizzled
-//    so that the transposed read (lane t takes row t) is conflict-free; the
-//    next batch's K is fetched while this batch finishes softmax and P.V.
-//  * V: 1 KB contiguous per instruction into registers: lane (grp, chk)
-//    holds 16-byte chunk chk of rows grp, grp+RPI, ...; the next batch's V
-//    is fetched while the next batch's scores are computed.
-//  * Scores: lane = row; q is wave-uniform and read through the scalar
-//    cache as the scalar operand of v_dot2_f32_bf16 (bf16) / v_fma (fp32).
+// Inside a wave: batches of 4 pages (64 rows) of one sequence; the next
+// batch's K and V travel while this one is computed.
+//  * K and V: the 4 (page, kv-head) tiles go straight from HBM into LDS with
+//    16-byte global_load_lds (1 KB contiguous per instruction), K XOR-
+//    swizzled so that a read of one row per lane is bank-conflict free; q by
+//    DMA into a double buffer when a new sequence starts.
+//  * Two kernels share this walk and pipeline and differ in the math.
+//    stream_decode_kernel (1 or 2 q-heads per kv-head, and float32): lane =
+//    row, the K row against q broadcast from LDS on v_dot2_f32_bf16 (fp32:
+//    v_fma); V rows copied to registers; P.V with the probabilities through
+//    LDS, rounded to bf16 (nearest even) and paired across rows for
+//    v_dot2_f32_bf16 while the normaliser and the log-sum-exp use the
+//    float32 values.  stream_mfma_kernel (4 to 16 bf16 query rows per wave):
+//    the same batch on 16 x 16 x 32 MFMA tiles (described below).
 //    The G q-heads sharing a kv-head all use one pass over K and V (the
 //    analog of fold_sq_factor, TokenSpeed deep-dive section 7.2).
 //  * Multi-token decode (n new tokens per sequence, causal among them):
@@ -30,13 +34,9 @@
 //    the heads (row r = token r / g, head r % g), which is the fold of the
 //    same section with the wave's 16 rows in place of the 128-row tile;
 //    token j of a pass masks the rows after its own position.
-//  * Online softmax per head in the exp2 domain; rows past the end are
+//  * Online softmax per query row in the exp2 domain; rows past the end are
 //    masked by select (never by multiplying by zero) so NaN poison in
 //    unused rows cannot leak.
-//  * P.V: probabilities go through LDS; for bf16 they are rounded to bf16
-//    (round to nearest even) and paired across rows for v_dot2_f32_bf16,
-//    while the normaliser and the log-sum-exp use the float32 values;
-//    fp32 uses v_fma.
 // The page walk follows the block table of the PagedAttention cache
 // (SwiftLLM page, section 3.1); physical page ids are clamped into the pool.
 #include <hip/hip_runtime.h>
