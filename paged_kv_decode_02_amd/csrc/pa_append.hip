@@ -160,17 +160,41 @@ __global__ __launch_bounds__(64 * kTokensPerBlock) void kv_append_fp8_kernel(
     for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
     amax = row16_max(amax);
     const float scale = fmaxf(amax, 1e-10f) / 448.0f;
+    // x / scale, correctly rounded, by a product and a rare fallback: with
+    // the correctly rounded reciprocal, q = x * (1 / scale) lies within 2
+    // float32 ulps of the quotient, so it falls on the same side of every
+    // rounding midpoint of the e4m3 grid unless it lies within a few ulps of
+    // one (a normal value whose 20 mantissa bits below the 3 kept ones are
+    // near 0x80000) or is below 2^-6 (the subnormal grid); only those
+    // elements take the division.
+    const float rcp = 1.0f / scale;
+    float y[EPL];
+    bool slow[EPL];
+    bool any = false;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      y[e] = x[e] * rcp;
+      const uint32_t b = __float_as_uint(y[e]) & 0x7fffffffu;
+      const int d = static_cast<int>(b & 0xfffffu) - 0x80000;
+      slow[e] = b < 0x3c800000u || (d >= -4 && d <= 4);
+      any = any || slow[e];
+    }
+    if (__ballot(any) != 0ull) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e)
+        if (slow[e]) y[e] = x[e] / scale;
+    }
     // codes, four per word: v_cvt_pk_fp8_f32 rounds to the nearest e4m3fn
     // value, ties to even, subnormals included (values are in range after
     // the clamp)
     uint32_t code[EPL / 4];
 #pragma unroll
     for (int e4 = 0; e4 < EPL / 4; ++e4) {
-      float y[4];
+      float z[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] = fminf(fmaxf(x[4 * e4 + e] / scale, -448.0f), 448.0f);
-      int word = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-      word = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], word, true);
+      for (int e = 0; e < 4; ++e) z[e] = fminf(fmaxf(y[4 * e4 + e], -448.0f), 448.0f);
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(z[0], z[1], 0, false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(z[2], z[3], word, true);
       code[e4] = static_cast<uint32_t>(word);
     }
     if (live) {
