@@ -393,12 +393,12 @@ int pa_check_block_tables(const int32_t* block_tables_host, int32_t max_blocks_p
  * once and named by every table that shares them (SwiftLLM page section
  * 3.1), so sequences share their first d pages when their first d table
  * entries are equal.  Each round picks, over a trie of the tables' page ids,
- * the prefix that saves the most page reads, d * (members - 1) (ties: the
- * longer prefix, then the one met first when the tables are read in
- * order), among prefixes of >= min_prefix_pages pages shorter than every
- * member's context and held by >= min_group (at least 2) sequences not yet
- * grouped; its sequences become a group.  The rest form a last group with
- * prefix 0.
+ * the longest prefix (the page's rule) among prefixes of >= min_prefix_pages
+ * pages, shorter than every member's context and held by >= min_group (at
+ * least 2) sequences not yet grouped (ties: the prefix with more such
+ * sequences, then the one met first when the tables are read in order);
+ * those sequences become a group.  The rest form a last group with prefix
+ * 0.
  *
  * Outputs (host, caller-owned): order_out[num_seqs] -- original sequence
  * index at each position, group by group (groups in the order found,

@@ -19,26 +19,28 @@ Readings (the page gives no more than that sentence):
   the sequences whose first d entries are that path; a sequence reaches
   depth d only if d * block_size < its context length (a cascade prefix
   must be shorter than every member's context);
-* "longest shared prefix" is weighed by the work it saves: a group of n
-  sequences sharing d pages saves d * (n - 1) page reads; each round takes
-  the node with the largest saving (ties: the deeper node, then the node
-  created first when the tables are inserted sequence by sequence), makes
-  its remaining sequences a group with prefix d * block_size, and removes
-  them from every node; rounds stop when no node has at least
-  ``min_group`` remaining sequences and ``min_pages`` pages of depth, or
-  saves nothing;
+* "the longest shared prefix" is taken literally: each round takes the
+  deepest node that still holds at least ``min_group`` (at least 2)
+  sequences not yet grouped and is at least ``min_pages`` pages deep (ties:
+  the node with more such sequences, then the node created first when the
+  tables are inserted sequence by sequence, i.e. table order), makes those
+  sequences a group with prefix d * block_size, and removes them from every
+  node; rounds stop when no node qualifies;
 * the sequences left over form one last group with prefix 0;
 * the output orders sequences group by group (groups in the order they were
   found, members by their original index), which is the contiguous layout
   ``pa_prefix_cascade`` takes.
 
 Pins (tests/test_prefix_groups_pins.py): the known groups of a shuffled
-shared-prefix batch are recovered; a second implementation that groups by
-page-id tuples at every depth (no trie) agrees on random nested layouts;
-every group's members share their first prefix pages and are longer than
-the prefix; savings never increase from one group to the next; planted
-mistakes (prefix allowed to reach the context length, ties broken the
-other way, members not removed) are each caught.
+shared-prefix batch are recovered; a hand-worked nested batch (two
+sequences sharing 100 pages inside 26 sharing 10) gives the deep pair
+first, where ranking by pages saved would take all 26 at 10 pages; a second
+implementation that groups by page-id tuples at every depth (no trie)
+agrees on random nested layouts; every group's members share their first
+prefix pages and are longer than the prefix; prefix depths never increase
+from one group to the next; planted mistakes (prefix allowed to reach the
+context length, ranking by pages saved, ties broken the other way, members
+not removed) are each caught.
 """
 
 from __future__ import annotations
@@ -51,9 +53,10 @@ def _max_depth(L: int, block_size: int) -> int:
     return max(0, (int(L) - 1) // block_size)
 
 
-def _rank(save: int, depth: int, node: int):
-    """Order of candidates: more pages saved, then deeper, then created first."""
-    return (save, depth, -node)
+def _rank(depth: int, count: int, node: int):
+    """Order of candidates: deeper, then more ungrouped members, then created
+    first (table order)."""
+    return (depth, count, -node)
 
 
 def _remove(count, path):
@@ -98,11 +101,10 @@ def detect_prefix_groups(block_tables, context_lens, block_size: int, min_group:
         for n in range(1, len(depth)):
             if count[n] < max(2, min_group) or depth[n] < min_pages:
                 continue
-            save = depth[n] * (count[n] - 1)
-            key = _rank(save, depth[n], n)
+            key = _rank(depth[n], count[n], n)
             if best_key is None or key > best_key:
                 best, best_key = n, key
-        if best < 0 or best_key[0] <= 0:
+        if best < 0:
             break
         group = [s for s in members[best] if not assigned[s]]
         if not group:  # a node's count always equals its unassigned members

@@ -13,6 +13,7 @@ import shutil
 import subprocess
 import sys
 import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -47,8 +48,8 @@ def build(verbose: bool = False, defines: tuple = (), out: str = LIB) -> str:
     -D options (tuning constants such as PA_TAIL_PERMILLE=150)."""
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC] + [f"-D{d}" for d in defines]
     with tempfile.TemporaryDirectory(prefix="pa_build_") as tmp:
-        objs = []
-        for src in SOURCES:
+
+        def compile_one(src):
             obj = os.path.join(tmp, src + ".o")
             lang = ["-x", "hip"] if src.endswith(".hip") else []
             cmd = [hipcc(), *HIPCC_FLAGS, *inc, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
@@ -63,7 +64,11 @@ def build(verbose: bool = False, defines: tuple = (), out: str = LIB) -> str:
                 raise RuntimeError(f"compiling {src} failed:\n{msg}")
             if msg.strip() and verbose:
                 print(msg)
-            objs.append(obj)
+            return obj
+
+        # one compiler process per source, at most four at a time
+        with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as pool:
+            objs = list(pool.map(compile_one, SOURCES))
         tmp_lib = os.path.join(tmp, "libpa.so")
         cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp_lib]
         r = subprocess.run(cmd, capture_output=True, text=True)

@@ -205,20 +205,21 @@ extern "C" int pa_check_block_tables(const int32_t* bt, int32_t max_blocks, cons
 // a shared prefix are stored once and named by every table sharing it, so two
 // sequences share their first d pages exactly when their first d table
 // entries are equal; a sequence may share at most d pages with d * block_size
-// < its context length.  Each round takes the prefix that saves the most
-// page reads, d * (members - 1) over the sequences not yet grouped (ties: the
-// longer prefix, then the one whose first holder in table order comes
-// first), and makes its remaining holders a group.
+// < its context length.  Each round takes the longest prefix still held by
+// at least min_group sequences not yet grouped (ties: the prefix with more
+// such holders, then the one whose first holder in table order comes first),
+// and makes those holders a group.
 //
 // Instead of a trie of every page, the tables are sorted lexicographically
 // (each up to its own depth limit) and the longest common prefixes of
 // neighbours give the LCP intervals: a run of sorted rows [l, r] whose common
 // prefix is d pages.  Every prefix held by two or more sequences is a trie
 // node whose members are such a run, and among the nodes with the same
-// members the deepest (the interval) saves the most, so only intervals are
+// members the deepest (the interval) ranks first, so only intervals are
 // candidates.  Counts of ungrouped members come from a Fenwick tree over the
-// sorted positions; a candidate's saving only ever decreases, so a max-heap
-// with lazy re-keying finds each round's best without rescanning.
+// sorted positions; a candidate's depth is fixed and its count only ever
+// decreases, so a max-heap with lazy re-keying finds each round's best
+// without rescanning.
 namespace {
 struct Fenwick {
   std::vector<int32_t> t;
@@ -304,18 +305,14 @@ extern "C" int pa_detect_prefix_groups(const int32_t* bt, int32_t max_blocks, co
   for (int32_t p = 0; p < S; ++p) left.add(p, 1);
   auto remaining = [&](const Interval& x) { return left.prefix(x.r + 1) - left.prefix(x.l); };
   struct Cand {
-    int64_t save;
-    int32_t depth, first, id;
+    int32_t depth, count, first, id;
     bool operator<(const Cand& o) const {
-      if (save != o.save) return save < o.save;
       if (depth != o.depth) return depth < o.depth;
+      if (count != o.count) return count < o.count;
       return first > o.first;  // the earlier first holder ranks higher
     }
   };
-  auto cand_of = [&](int32_t i) {
-    const int32_t n = remaining(iv[i]);
-    return Cand{static_cast<int64_t>(iv[i].depth) * (n - 1), iv[i].depth, iv[i].first, i};
-  };
+  auto cand_of = [&](int32_t i) { return Cand{iv[i].depth, remaining(iv[i]), iv[i].first, i}; };
   auto eligible = [&](int32_t i) {
     const int32_t n = remaining(iv[i]);
     return n >= mg && iv[i].depth >= mp;
@@ -333,12 +330,11 @@ extern "C" int pa_detect_prefix_groups(const int32_t* bt, int32_t max_blocks, co
     heap.pop_back();
     if (!eligible(top.id)) continue;
     const Cand now = cand_of(top.id);
-    if (now.save != top.save) {  // stale: members were grouped since it was pushed
+    if (now.count != top.count) {  // stale: members were grouped since it was pushed
       heap.push_back(now);
       std::push_heap(heap.begin(), heap.end());
       continue;
     }
-    if (now.save <= 0) break;
     const Interval& x = iv[top.id];
     const int32_t first = placed;
     for (int32_t p = x.l; p <= x.r; ++p) {

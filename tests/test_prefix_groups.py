@@ -46,3 +46,21 @@ def test_bad_arguments():
     with pytest.raises(pa.PAError):
         pa.detect_prefix_groups(bt, np.array([33, 5], dtype=np.int32))  # beyond 2 pages
     assert [x.size for x in pa.detect_prefix_groups(np.zeros((0, 1), np.int32), np.zeros(0, np.int32))] == [0, 1, 0]
+
+
+def test_longest_prefix_first_where_savings_would_differ():
+    """Two sequences share 100 pages inside 26 that share 10: the pair's
+    longer prefix is taken first (ranking by pages saved would take all 26)."""
+    bs = 16
+    common = list(range(1, 11))
+    deep = common + list(range(11, 101))
+    rows = [(deep if s < 2 else common) + [1000 + s] for s in range(26)]
+    bt = np.full((26, max(len(r) for r in rows)), -1, dtype=np.int32)
+    for s, r in enumerate(rows):
+        bt[s, : len(r)] = r
+    ctx = np.array([len(r) * bs - 3 for r in rows], dtype=np.int32)
+    got = pa.detect_prefix_groups(bt, ctx, bs)
+    want = oracle.detect_prefix_groups(bt, ctx, bs)
+    for g, w in zip(got, want):
+        assert np.array_equal(g, w)
+    assert got[1].tolist() == [0, 2, 26] and got[2].tolist() == [1600, 160]

@@ -59,8 +59,9 @@ def nested_tables(rng, S=40, block_size=16):
 def tuple_route(bt, ctx, block_size, min_group=2, min_pages=1):
     """The same greedy rounds without a trie: at every depth d the remaining
     sequences that reach d are bucketed by their first d page ids; the
-    candidate that saves the most (d * (n - 1)) wins, ties to the deeper one,
-    then to the one whose first holder (over all sequences) comes first."""
+    deepest bucket with enough members wins, ties to the one with more
+    members, then to the one whose first holder (over all sequences) comes
+    first."""
     S = len(ctx)
     dmax = [max(0, (int(L) - 1) // block_size) for L in ctx]
     first_holder = {}
@@ -80,10 +81,10 @@ def tuple_route(bt, ctx, block_size, min_group=2, min_pages=1):
             for key, mem in buckets.items():
                 if len(mem) < max(2, min_group):
                     continue
-                cand = (d * (len(mem) - 1), d, -first_holder[key])
+                cand = (d, len(mem), -first_holder[key])
                 if best is None or cand > best[0]:
                     best = (cand, mem, d)
-        if best is None or best[0][0] <= 0:
+        if best is None:
             break
         _, mem, d = best
         assigned.update(mem)
@@ -120,6 +121,45 @@ def pin_known_groups():
     return fails
 
 
+def pin_longest_first():
+    """Worked by hand: sequences 0 and 1 share 100 pages; all 26 sequences
+    share the first 10 of them.  The longest shared prefix is the pair's:
+    group {0, 1} at 100 pages first, then the other 24 at 10 pages.  (Ranked
+    by pages saved, d * (n - 1), the 26 at 10 pages would win: 250 > 99.)"""
+    bs = 16
+    common = list(range(1, 11))
+    deep = common + list(range(11, 101))
+    rows, nxt = [], 1000
+    for s in range(26):
+        pages = (deep if s < 2 else common) + [nxt]
+        nxt += 1
+        rows.append(pages)
+    mb = max(len(r) for r in rows)
+    bt = np.full((26, mb), -1, dtype=np.int32)
+    for s, r in enumerate(rows):
+        bt[s, : len(r)] = r
+    ctx = np.array([len(r) * bs - 3 for r in rows], dtype=np.int32)
+    order, offs, pref = oracle.detect_prefix_groups(bt, ctx, bs)
+    fails = []
+    if order.tolist() != list(range(26)):
+        fails.append(f"order {order.tolist()}")
+    if offs.tolist() != [0, 2, 26]:
+        fails.append(f"offsets {offs.tolist()}")
+    if pref.tolist() != [100 * bs, 10 * bs]:
+        fails.append(f"prefix lengths {pref.tolist()}")
+    # min_group 3: the pair no longer qualifies, all 26 share 10 pages
+    order, offs, pref = oracle.detect_prefix_groups(bt, ctx, bs, 3)
+    if offs.tolist() != [0, 26] or pref.tolist() != [10 * bs]:
+        fails.append(f"min_group 3: offsets {offs.tolist()} prefixes {pref.tolist()}")
+    # ties: equal depth, more members first; equal members, table order
+    bt2 = np.array([[7, 1], [5, 2], [5, 3], [7, 4], [5, 6], [9, 8], [9, 10]], dtype=np.int32)
+    ctx2 = np.full(7, 2 * bs, dtype=np.int32)
+    order, offs, pref = oracle.detect_prefix_groups(bt2, ctx2, bs)
+    if order.tolist() != [1, 2, 4, 0, 3, 5, 6] or offs.tolist() != [0, 3, 5, 7] or pref.tolist() != [bs] * 3:
+        fails.append(f"ties: {order.tolist()} {offs.tolist()} {pref.tolist()}")
+    return fails
+
+
 def pin_tuple_route():
     fails = []
     for seed in range(12):
@@ -141,7 +181,7 @@ def pin_invariants():
         order, offs, pref = oracle.detect_prefix_groups(bt, ctx, 16)
         if sorted(order.tolist()) != list(range(len(ctx))):
             fails.append(f"seed {seed}: order is not a permutation")
-        saves = []
+        depths = []
         for g in range(len(pref)):
             mem = order[offs[g] : offs[g + 1]]
             P = int(pref[g]) // 16
@@ -150,9 +190,9 @@ def pin_invariants():
             if not (ctx[mem] > pref[g]).all():
                 fails.append(f"seed {seed} group {g}: prefix not shorter than a member")
             if P:
-                saves.append(P * (len(mem) - 1))
-        if any(b > a for a, b in zip(saves, saves[1:])):
-            fails.append(f"seed {seed}: savings increase from one group to the next")
+                depths.append(P)
+        if any(b > a for a, b in zip(depths, depths[1:])):
+            fails.append(f"seed {seed}: prefix depths increase from one group to the next")
         if (pref[:-1] == 0).any():
             fails.append(f"seed {seed}: a prefix-0 group before the last")
     # the output is a valid cascade grouping for the table checker
@@ -169,7 +209,7 @@ def pin_invariants():
     return fails
 
 
-ALL_PINS = [pin_known_groups, pin_tuple_route, pin_invariants]
+ALL_PINS = [pin_known_groups, pin_longest_first, pin_tuple_route, pin_invariants]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
@@ -180,8 +220,9 @@ def test_pin(pin):
 
 PLANTED = {
     "prefix may reach the context length": ("_max_depth", lambda L, bs: max(0, int(L) // bs)),
-    "ties to the shallower node": ("_rank", lambda save, depth, node: (save, -depth, -node)),
-    "ties to the later node": ("_rank", lambda save, depth, node: (save, depth, node)),
+    "ranked by pages saved": ("_rank", lambda depth, count, node: (depth * (count - 1), depth, -node)),
+    "ties to fewer members": ("_rank", lambda depth, count, node: (depth, -count, -node)),
+    "ties to the later node": ("_rank", lambda depth, count, node: (depth, count, node)),
     "members not removed": ("_remove", lambda count, path: None),
 }
 
