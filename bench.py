@@ -4,11 +4,16 @@
 
 A step is one library call over the whole batch (pa_decode for decode
 batches, pa_prefix_cascade for shared-prefix groups, pa_mixed_chunk for
-prefill chunks + decode tokens), with inputs resident in HBM.  Prints ONE
-JSON line: value = algorithmic bytes per step / measured step time (GB/s),
-plus decode tokens/s for a 32-layer model (attention only), a roofline object
-for the dominant kernel timed with HIP events on its own stream, and the fp64
-CPU oracle timed on a bounded sample of the same workload.
+prefill chunks + decode tokens), with inputs resident in HBM.  Each timed
+step follows a 1 GiB fill of a scratch buffer on the same stream (outside
+the step's own event pair), so no input is still in the last-level cache.
+Prints ONE JSON line: value = algorithmic bytes per step / median cold step
+time (GB/s), with the minimum and a warm-cache (back-to-back) figure under
+"timing"; decode tokens/s for a 32-layer model (attention only); a roofline
+object for the dominant kernel timed with HIP events on its own stream; and
+the fp64 CPU oracle timed on a bounded sample of the same workload over the
+host cores (oracle.parallel).  Profile runs pass --no-cpu-baseline, so that
+no worker process is started under the profiler.
 """
 
 from __future__ import annotations
@@ -102,17 +107,15 @@ def visible_pairs(lay, segs):
 
 
 def cpu_baseline(lay, q, k, v, total_bytes, budget_s, k_scales=None, v_scales=None):
-    """Time the fp64 oracle, single-threaded, on whole segments of the same
-    batch (random order) until about budget_s seconds of CPU work are spent,
-    then scale to the whole batch by the (token, key) pairs attended and
-    report the batch's algorithmic bytes over that time."""
+    """Time the fp64 oracle, as it stands, on the host cores: whole sequences
+    of the same batch in random order, split into (sequence, kv-head) units
+    over the oracle's worker processes (one BLAS thread each), fed until
+    about budget_s seconds of wall time have passed; the wall time of that
+    sample is scaled to the whole batch by the (token, key) pairs attended,
+    and the batch's algorithmic bytes over that time are reported."""
     import torch
 
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
-    import oracle
+    from oracle import parallel
 
     def host(t):
         if t.dtype == torch.bfloat16:
@@ -120,46 +123,44 @@ def cpu_baseline(lay, q, k, v, total_bytes, budget_s, k_scales=None, v_scales=No
         return t.float().cpu().numpy()
 
     cu = lay.cu_q_lens
-    order = np.random.default_rng(123).permutation(lay.num_seqs)
-    done, spent = [], 0.0
-    limit = threadpool_limits(1) if threadpool_limits else None
-    try:
-        while spent < budget_s and len(done) < lay.num_seqs:
-            s = int(order[len(done)])
-            n = (int(lay.context_lens[s]) + 15) // 16
-            idx = torch.from_numpy(lay.block_tables[s, :n].astype(np.int64)).to(k.device)
-            qs = host(q[int(cu[s]) : int(cu[s + 1])])
-            bt = np.arange(n, dtype=np.int32)[None, :]  # the gathered pages, relabelled 0..n-1
-            if k_scales is not None:
-                kc, vc = k.index_select(0, idx).cpu().numpy(), v.index_select(0, idx).cpu().numpy()
-                ksc, vsc = k_scales.index_select(0, idx).cpu().numpy(), v_scales.index_select(0, idx).cpu().numpy()
-                t0 = time.perf_counter()
-                oracle.decode_multi_fp8(qs, kc, ksc, vc, vsc, bt, lay.context_lens[s : s + 1], int(lay.q_lens[s]),
-                                        lay.scale, lay.num_kv_heads, 16, "bf16")
-            elif lay.window is not None:
-                ks, vs = host(k.index_select(0, idx)), host(v.index_select(0, idx))
-                t0 = time.perf_counter()
-                oracle.decode_window(qs, ks, vs, bt, lay.context_lens[s : s + 1], lay.window, lay.scale,
-                                     lay.num_kv_heads, 16, lay.dtype)
-            else:
-                ks, vs = host(k.index_select(0, idx)), host(v.index_select(0, idx))
-                t0 = time.perf_counter()
-                oracle.paged_attention(qs, ks, vs, bt, lay.context_lens[s : s + 1], lay.q_lens[s : s + 1],
-                                       lay.scale, lay.num_kv_heads, 16, lay.dtype)
-            spent += time.perf_counter() - t0
-            done.append(s)
-    finally:
-        if limit is not None:
-            limit.unregister()
+    fp8 = k_scales is not None
+    W = lay.window
+    order = [int(x) for x in np.random.default_rng(123).permutation(lay.num_seqs)]
+    fed = []
+    t0 = time.perf_counter()
+
+    def seqs():
+        for s in order:
+            if time.perf_counter() - t0 > budget_s:
+                return
+            fed.append(s)
+            yield s
+
+    def fetch(s):
+        L = int(lay.context_lens[s])
+        first = (L - W) // 16 if W is not None and L > W else 0
+        idx = torch.from_numpy(lay.block_tables[s, first:(L + 15) // 16].astype(np.int64)).to(k.device)
+        qs = host(q[int(cu[s]) : int(cu[s + 1])])
+        if fp8:
+            return (qs, k.index_select(0, idx).cpu().numpy(), v.index_select(0, idx).cpu().numpy(),
+                    k_scales.index_select(0, idx).cpu().numpy(), v_scales.index_select(0, idx).cpu().numpy())
+        return qs, host(k.index_select(0, idx)), host(v.index_select(0, idx))
+
+    done = [s for s, _, _ in parallel.batch_attention(fetch, seqs(), lay.context_lens, lay.q_lens,
+                                                          lay.num_kv_heads, lay.scale, lay.dtype, window=W,
+                                                          fp8_kv=fp8)]
+    spent = time.perf_counter() - t0
     frac = visible_pairs(lay, done) / visible_pairs(lay, range(lay.num_seqs))
     est = spent / frac
+    cores = max(1, parallel.pool_size())
     return {
         "value": round(total_bytes / est / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
-        "sample": f"{len(done)} of {lay.num_seqs} segments ({100 * frac:.1f}% of the batch's (token, key) pairs), "
-                  f"{spent:.1f} s, fp64 numpy, BLAS limited to 1 thread; whole-batch time scaled by pairs",
+        "sample": f"{len(done)} of {lay.num_seqs} sequences ({100 * frac:.1f}% of the batch's (token, key) pairs) "
+                  f"in {spent:.1f} s wall on {cores} worker processes (fp64 numpy, one BLAS thread each, units of "
+                  f"(sequence, kv-head)), pages copied from the device per sequence; whole-batch time scaled by pairs",
     }
 
 
@@ -244,6 +245,12 @@ def main():
     if args.op == "append":
         bench_append(args)
         return
+    if not args.no_cpu_baseline:
+        # the oracle's worker processes start before this process touches
+        # the GPU (they are fresh interpreters that never do)
+        from oracle import parallel
+
+        parallel.start_pool()
     import torch
 
     from paged_kv_decode_02_amd import pa, roofline
@@ -320,6 +327,7 @@ def main():
                           stream=stream)
 
     def timed(fn, n):
+        """Warm-cache mean: n steps back to back between two events."""
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record(stream)
@@ -329,16 +337,38 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
+    # Cold cache: before each timed step a fill kernel writes a 1 GiB buffer
+    # on the same stream, outside the step's event pair, which evicts the
+    # step's inputs from the 256 MB last-level cache (MALL) and the L2s.
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def cold(fn, n, pairs=0):
+        """Per-step times (ms) of n steps, each after a cache flush and
+        timed by its own event pair; with pairs > 0 the library's events
+        around its dominant kernel(s) are collected as well."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        if pairs:
+            pa.profile_enable(n * pairs)
+        torch.cuda.synchronize()
+        for a, b in ev:
+            flush.zero_()
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        kern = None
+        if pairs:
+            kern = np.array(pa.profile_collect(n * pairs)).reshape(n, pairs)
+            pa.profile_enable(0)
+        return np.array([a.elapsed_time(b) for a, b in ev]), kern
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
-    t0 = time.perf_counter()
-    ms_per_step = timed(step, args.steps)
-    wall = time.perf_counter() - t0
 
-    # Dominant kernel(s) alone: HIP events the library records around them
-    # on the same stream (decode: the stream kernel; cascade: the prefix
+    # Dominant kernel(s) of a step: HIP events the library records around
+    # them on the same stream (decode: the stream kernel; cascade: the prefix
     # kernel; mixed: the chunk kernel, then the decode stream kernel).
     has_dec = bool((lay.q_lens == 1).any())
     pairs = 2 if mixed and has_dec else 1
@@ -346,13 +376,13 @@ def main():
         # folded passes: one stream kernel each
         fold = max(1, min(n_tok, 16 // lay.gqa_ratio))
         pairs = -(-n_tok // fold)
-    pa.profile_enable(args.steps * pairs)
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    kern_ms = np.array(pa.profile_collect(args.steps * pairs)).reshape(args.steps, pairs)
-    pa.profile_enable(0)
+    t0 = time.perf_counter()
+    step_ms, kern_ms = cold(step, args.steps, pairs)
+    wall = time.perf_counter() - t0
+    ms_per_step = float(np.median(step_ms))
+    ms_min = float(step_ms.min())
     kern_avg = [float(x) for x in kern_ms.mean(axis=0)]
+    warm_ms = timed(step, args.steps)
 
     def hbm_roof(kernel, nbytes, ms, traffic):
         achieved = nbytes / (ms * 1e-3) / 1e9
@@ -382,8 +412,8 @@ def main():
         dws = torch.empty(pa.decode_workspace_size(S, lay.num_kv_heads, lay.gqa_ratio, D, total_pages, 0),
                           dtype=torch.uint8, device=dev)
         dout = torch.empty_like(q)
-        dec_ms = timed(lambda: pa.decode(dout, q, k, v, bt, ctx, lay.context_lens, lay.scale, dws, stream=stream),
-                       args.steps)
+        dec_ms = float(np.median(cold(lambda: pa.decode(dout, q, k, v, bt, ctx, lay.context_lens, lay.scale, dws,
+                                                        stream=stream), args.steps)[0]))
         extra = {"prefix_gflop": round(flops / 1e9, 3), "decode_same_batch_ms": round(dec_ms, 5),
                  "cascade_speedup_vs_decode": round(dec_ms / ms_per_step, 3)}
     elif multi:
@@ -399,7 +429,7 @@ def main():
                         measured_traffic(args.workload))
         extra = {"tokens_per_step": int(T), "fold_passes": pairs}
         if not fp8:  # (the chunk path reads bf16 / float32 pools only)
-            extra["mixed_chunk_same_batch_ms"] = round(timed(mixed_step, args.steps), 5)
+            extra["mixed_chunk_same_batch_ms"] = round(float(np.median(cold(mixed_step, args.steps)[0])), 5)
     elif mixed:
         nb = roofline.mixed_bytes(lay.context_lens, lay.q_lens, lay.num_q_heads, lay.num_kv_heads, D,
                                   lay.elem_bytes)
@@ -460,6 +490,12 @@ def main():
             "parallelism": "single GPU",
         },
         "hbm_frac": round(gbs / roofline.HBM_PEAK_GBS, 4),
+        "timing": {"cache": "cold: 1 GiB fill before each step, outside its event pair",
+                   "median_ms": round(ms_per_step, 5), "min_ms": round(ms_min, 5),
+                   "mean_ms": round(float(step_ms.mean()), 5),
+                   "min_step_GBps": round(nb["total"] / (ms_min * 1e-3) / 1e9, 1),
+                   "warm_cache_mean_ms": round(warm_ms, 5),
+                   "warm_cache_GBps": round(nb["total"] / (warm_ms * 1e-3) / 1e9, 1)},
         # (a multi-token decode step decodes every one of its tokens)
         "decode_tokens_per_s_32_layers": round(int(T if multi else (lay.q_lens == 1).sum()) /
                                                (roofline.LLAMA8B_LAYERS * ms_per_step * 1e-3), 1),

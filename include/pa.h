@@ -3,8 +3,9 @@
  *
  * C ABI of libpa.so.  Every pointer is a raw address; the header says for
  * each one whether it is device memory (HBM) or host memory.  No call
- * allocates memory: the caller owns q, the pools, the tables, the outputs
- * and the workspace.  Kernels are launched asynchronously on the HIP stream
+ * allocates memory (the measurement hook pa_profile_enable at the end
+ * aside): the caller owns q, the pools, the tables, the outputs and the
+ * workspace.  Kernels are launched asynchronously on the HIP stream
  * passed as `stream` (a hipStream_t, NULL = the default stream); device
  * buffers must stay alive until the stream reaches the call.  Host arrays
  * (the `*_host` twins) are read synchronously before the call returns, so
@@ -52,8 +53,9 @@
  * the same values; if they do not, results are undefined but every access
  * still stays inside the buffers passed.
  *
- * Thread safety: calls are reentrant.  Two calls that share a workspace
- * must be ordered on one stream.
+ * Thread safety: calls are reentrant (pa_profile_enable / _collect aside:
+ * they keep per-thread state).  Two calls that share a workspace must be
+ * ordered on one stream.
  */
 #ifndef PA_H
 #define PA_H
@@ -272,8 +274,8 @@ int pa_prefix_cascade(void* out,                       /* device [S, Hq, D] */
 
 /* ---------------------------------------------------------------------------
  * Mixed batch: prefill chunks and decode tokens in one call (decode tokens
- * of many sequences piggybacked on prefill chunks: SOSP tutorial page,
- * section 3.3 "SARATHI"; prefill admitted in bounded chunks, each attending
+ * of many sequences piggybacked on prefill chunks: SwiftLLM page, section
+ * 3.3, SARATHI-style piggybacking; prefill admitted in bounded chunks, each attending
  * to the cached prefix plus itself: TokenSpeed deep-dive section 5.1, with
  * the per-segment lengths passed as device + host copies and no defaults,
  * section 8.2).
@@ -417,7 +419,10 @@ int pa_detect_prefix_groups(const int32_t* block_tables_host, int32_t max_blocks
 const char* pa_last_error(void);
 
 /* ---------------------------------------------------------------------------
- * Profiling hook (measurement only; changes no result).
+ * Profiling hook (measurement only; changes no result).  A test and
+ * benchmark hook, not part of the hot path: pa_profile_enable allocates
+ * HIP events and both calls keep thread-local state, so they are neither
+ * allocation-free nor reentrant.
  * pa_profile_enable(n) creates n pairs of HIP timing events on this thread;
  * every later call records one pair around each of its dominant kernels on
  * its stream: the stream kernel of pa_decode; the prefix kernel of

@@ -7,8 +7,8 @@
 // whole group: the group's queries against the prefix keys form one dense
 // product.  Attention over prefix + suffix is then the log-sum-exp merge of
 // attention over each part.  Three launches on the caller's stream:
-//  1. tile_kernel<G, false> (MFMA): per (group, row chunk, key split,
-//     kv-head) a workgroup of 8 waves takes up to 256 query rows --
+//  1. tile_kernel<G, false> (MFMA): per (group, row block, key split,
+//     kv-head) a workgroup of 8 waves takes up to 128 query rows --
 //     (member, q-head) pairs of the kv-head, folded into one tile dimension
 //     the way TokenSpeed's fold_sq_factor folds query tokens (TokenSpeed
 //     deep-dive section 7.2) -- against one split of the prefix keys,
@@ -16,17 +16,19 @@
 //     v_mfma_f32_16x16x32_bf16, online softmax in between.  Writes one
 //     partial (o, log2-sum-exp) per (member, head, split) and each member's
 //     first suffix page.
-//  2. stream_decode_kernel over the suffix pages only.
+//  2. The stream kernel (stream_mfma_kernel for 4 or more q-heads per
+//     kv-head, stream_decode_kernel otherwise) over the suffix pages only.
 //  3. cascade_merge_kernel: per (sequence, kv-head), the prefix splits and
 //     the suffix partial(s) merged by log-sum-exp.
 //
-// Mixed batch (SARATHI-style piggybacking, SOSP tutorial page section 3.3;
-// chunked prefill, TokenSpeed deep-dive section 5.1): prefill chunks (n > 1
-// new tokens, causal inside the chunk) and decode tokens in one call.
-//  1. tile_kernel<G, true>: per (chunk, row chunk, key split, kv-head) the
+// Mixed batch (SARATHI-style piggybacking of decode tokens on prefill
+// chunks, SwiftLLM page section 3.3; chunked prefill, TokenSpeed deep-dive
+// section 5.1): prefill chunks (n > 1 new tokens, causal inside the chunk)
+// and decode tokens in one call.
+//  1. tile_kernel<G, true>: per (chunk, row block, key split, kv-head) the
 //     chunk's (token, q-head) rows against its own keys, causal mask by
 //     select; marks the chunks as "no decode pages" for step 2.
-//  2. stream_decode_kernel (+ its merge) over the decode segments.
+//  2. The stream kernel (+ its merge) over the decode segments.
 //  3. chunk_merge_kernel: per (chunk token, kv-head), the key splits.
 #include <hip/hip_runtime.h>
 
@@ -220,19 +222,19 @@ __global__ __launch_bounds__(512) void tile_kernel(
   const char* kbytes = reinterpret_cast<const char*>(k_pool);
   const char* vbytes = reinterpret_cast<const char*>(v_pool);
 
-  // O^T accumulators, and the row sums of P (as bf16, the values P.V
-  // uses) from one more MFMA per row block against an all-ones A operand:
-  // every element of osum[rb] is the sum over this wave's keys of its row.
+  // O^T accumulators, and the float32 row sums of P over this lane's keys
+  // (the lanes l ^ 16, l ^ 32, l ^ 48 hold the rest of the row's keys; the
+  // sums are reduced over them at the end).  As in the decode kernels, the
+  // normaliser sums the float32 probabilities while P.V takes them rounded
+  // to bf16.
   f32x4 o[8][2];
-  f32x4 osum[2];
+  float lsum[2] = {0.f, 0.f};
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    osum[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < 8; ++db) o[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   float m[2] = {-INFINITY, -INFINITY};
-  const u32x4 ones = u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0 pairs
 
   // K or V of tile t (keys k_lo + 64 t ..) -> an LDS buffer, by DMA: slot
   // (i*8 + wave)*64 + lane of a buffer holds key slot/16, chunk
@@ -393,7 +395,7 @@ __global__ __launch_bounds__(512) void tile_kernel(
         // m = -inf (nothing visible yet): o and the sums are 0, any factor will do
         const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m[rb] - mn);
         m[rb] = mn;
-        osum[rb] *= alpha;
+        lsum[rb] *= alpha;
 #pragma unroll
         for (int db = 0; db < 8; ++db) o[db][rb] *= alpha;
       }
@@ -408,7 +410,10 @@ __global__ __launch_bounds__(512) void tile_kernel(
       for (int kb = 0; kb < 2; ++kb) {
         float p[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(s[kb][rb][i], scale_log2, nref));
+        for (int i = 0; i < 4; ++i) {
+          p[i] = fast_exp2(fmaf(s[kb][rb][i], scale_log2, nref));
+          lsum[rb] += p[i];
+        }
         pw[kb][0] = bf16x2_rne(p[0], p[1]);
         pw[kb][1] = bf16x2_rne(p[2], p[3]);
       }
@@ -417,8 +422,7 @@ __global__ __launch_bounds__(512) void tile_kernel(
       pb[rb] = u32x4{pw[0][0], pw[0][1], pw[1][0], pw[1][1]};
     }
     // O^T += V^T P^T; the V^T operand (d = 16 db + col, keys as above) comes
-    // from two transposed reads of 4 keys each; the row sums come from the
-    // all-ones operand.
+    // from two transposed reads of 4 keys each.
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       u32x2 part[2];
@@ -432,8 +436,6 @@ __global__ __launch_bounds__(512) void tile_kernel(
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) o[db][rb] = mfma16x16x32(a, pb[rb], o[db][rb]);
     }
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) osum[rb] = mfma16x16x32(ones, pb[rb], osum[rb]);
     return t + 1 < nt;
   };
   for (int t = 0;; t += 4) {
@@ -449,6 +451,10 @@ __global__ __launch_bounds__(512) void tile_kernel(
   // for row block kh into its own.  Record (rg, kh): o as [8 db][64 lanes]
   // f32x4 in K buffer rg at 8 KB * kh; m and the row sum per lane in V
   // buffer 0 at 128 floats * (2 rg + kh).
+  // (the row sums over all of this wave's keys: its lanes l, l ^ 16, l ^ 32
+  // and l ^ 48 hold the same row)
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) lsum[rb] = add_xor32(add_xor16(lsum[rb]));
   __syncthreads();
   uint4* kbuf = rg == 0 ? k_lds0 : rg == 1 ? k_lds1 : rg == 2 ? k_lds2 : k_lds3;
   float* xm = reinterpret_cast<float*>(v_lds0);
@@ -459,7 +465,7 @@ __global__ __launch_bounds__(512) void tile_kernel(
 #pragma unroll
     for (int db = 0; db < 8; ++db) xo[db * 64 + lane] = kh ? o[db][0] : o[db][1];
     xm[(2 * rg + kh) * 128 + lane] = kh ? m[0] : m[1];
-    xm[(2 * rg + kh) * 128 + 64 + lane] = kh ? osum[0][0] : osum[1][0];
+    xm[(2 * rg + kh) * 128 + 64 + lane] = kh ? lsum[0] : lsum[1];
   }
   __syncthreads();
   const int rb = kh;
@@ -467,7 +473,7 @@ __global__ __launch_bounds__(512) void tile_kernel(
 #pragma unroll
   for (int db = 0; db < 8; ++db) om[db] = kh ? o[db][1] : o[db][0];
   const float mm = kh ? m[1] : m[0];
-  const float lm = kh ? osum[1][0] : osum[0][0];
+  const float lm = kh ? lsum[1] : lsum[0];
   const f32x4* po = reinterpret_cast<const f32x4*>(kbuf) + (1 - kh) * 512;
   const float* pm = xm + (2 * rg + 1 - kh) * 128;
   const float m2 = pm[lane];

@@ -24,3 +24,25 @@ def gpu_lib():
 
     pa.load()  # raises if the built library is missing
     return pa
+
+
+def pytest_collection_finish(session):
+    """Start the oracle's worker processes (spawned interpreters that never
+    touch a GPU) before any test initialises the GPU, when GPU tests will
+    run on a machine that has one.  (Counting devices does not initialise
+    the runtime.)"""
+    if not any(item.get_closest_marker("gpu") for item in session.items):
+        return
+    import torch
+
+    if torch.cuda.device_count() > 0:
+        from oracle import parallel
+
+        n = parallel.start_pool()
+        print(f"[conftest] oracle worker processes: {n}", file=sys.stderr, flush=True)
+
+
+def pytest_unconfigure(config):
+    from oracle import parallel
+
+    parallel.stop_pool()

@@ -87,11 +87,56 @@ def out_to_f64(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
-# Log-sum-exp bound where MFMA tiles attend (shared prefixes, prefill
-# chunks): their P.V contraction takes P rounded to bf16 on the bf16 MFMA,
-# and the normaliser is summed from the same rounded P (so the weights of
-# every output row sum to one).  Rounding to nearest even moves each p by at
-# most 2^-9 of itself, so the sum, and exp(lse), by at most 2^-9 relative:
-# lse within 2^-9 ~ 1.95e-3.  (The decode kernels sum the float32 p and
-# meet 1e-3.)
-LSE_TOL_MFMA_BF16 = 2.0e-3
+# Log-sum-exp bar for every kernel, 1e-3 absolute (natural log).  Every
+# kernel forms lse = m + ln(sum_t p_t) from float32 probabilities p_t =
+# 2^(x_t - m) (scores x_t in the log2 domain): no kernel sums the bf16-rounded
+# p that P.V uses (rounding to nearest even moves a bf16 value by up to 2^-8
+# of itself, so such a sum could be off by ln(1 + 2^-8) ~ 3.9e-3).  What is
+# left, for contexts up to 32768 rows:
+#  * each score is a float32 sum of D = 128 exact bf16 products:
+#    |dx| <= 128 * 2^-24 * scale * sum_d |q_d k_d| -- 2e-5 for these inputs;
+#  * each p carries the exp2 instruction's error (about 1 ulp, 2^-23 relative)
+#    and every lazy or online rescale one more rounding;
+#  * a lane adds at most L / 64 = 512 values, then a tree of 6 levels:
+#    (512 + 6) * 2^-24 ~ 3e-5 relative on the sum;
+#  * merges of partials add a float32 exp2 / log2 each (~1e-7).
+# The sum of these stays below 1e-4, so 1e-3 holds with a wide margin.
+LSE_TOL = 1.0e-3
+
+
+def oracle_full(lay: Layout, q_dev, k_dev, v_dev, seqs=None, k_scales=None, v_scales=None):
+    """The fp64 oracle over every token of the given sequences (default: the
+    whole batch), computed unit by unit -- (sequence, kv-head) -- on the
+    oracle's worker processes when they run (``oracle.parallel``), else in
+    this process.  Each sequence's pages are copied from the device in table
+    order (from the window's first page on for windowed layouts), so device-
+    drawn pools of several GB never need a host copy.  fp8 pools: pass the
+    scale tensors.  Returns out [T, Hq, D] and lse [T, Hq] in float64 (NaN
+    for tokens of sequences not asked for)."""
+    from oracle import parallel
+
+    cu = lay.cu_q_lens
+    T, Hq, D = q_dev.shape
+    fp8 = k_scales is not None
+    W = lay.window
+
+    def fetch(s):
+        L = int(lay.context_lens[s])
+        first = (L - W) // 16 if W is not None and L > W else 0
+        idx = torch.from_numpy(lay.block_tables[s, first:(L + 15) // 16].astype(np.int64)).to(k_dev.device)
+        if fp8:
+            kc = k_dev.index_select(0, idx).cpu().numpy()
+            vc = v_dev.index_select(0, idx).cpu().numpy()
+            return (to_host_values(lay, q_dev[int(cu[s]):int(cu[s + 1])]), kc, vc,
+                    k_scales.index_select(0, idx).cpu().numpy(), v_scales.index_select(0, idx).cpu().numpy())
+        return (to_host_values(lay, q_dev[int(cu[s]):int(cu[s + 1])]), to_host_values(lay, k_dev.index_select(0, idx)),
+                to_host_values(lay, v_dev.index_select(0, idx)))
+
+    out = np.full((T, Hq, D), np.nan)
+    lse = np.full((T, Hq), np.nan)
+    todo = range(lay.num_seqs) if seqs is None else seqs
+    for s, o, l in parallel.batch_attention(fetch, todo, lay.context_lens, lay.q_lens, lay.num_kv_heads, lay.scale,
+                                            lay.dtype, window=W, fp8_kv=fp8):
+        out[int(cu[s]):int(cu[s + 1])] = o
+        lse[int(cu[s]):int(cu[s + 1])] = l
+    return out, lse

@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import (LSE_TOL_MFMA_BF16, assert_close, device_inputs, oracle_subset, out_to_f64, to_device_values,
+from gpu_util import (LSE_TOL, assert_close, device_inputs, oracle_full, out_to_f64, to_device_values,
                       to_host_values)
 from workloads import bf16_bits_from_f32, cascade_layout, values_numpy, workload
 
@@ -76,7 +76,7 @@ def test_cascade_small(gpu_lib, groups, per_group, prefix, suf_hi, hq, hkv):
     out, lse = run_cascade(gpu_lib, lay, q, k, v)
     ro, rl = oracle_cascade(lay, qh, kh, vh)
     assert_close(lay, out_to_f64(out), ro, "cascade")
-    assert np.abs(lse.cpu().numpy() - rl).max() < LSE_TOL_MFMA_BF16
+    assert np.abs(lse.cpu().numpy() - rl).max() < LSE_TOL
     dout, dlse = run_decode(gpu_lib, lay, q, k, v)
     assert_close(lay, out_to_f64(out), out_to_f64(dout).astype(np.float64), "cascade vs decode")
 
@@ -88,21 +88,24 @@ def test_cascade_mixed_prefix_lengths(gpu_lib):
     out, lse = run_cascade(gpu_lib, lay, q, k, v)
     ro, rl = oracle_cascade(lay, qh, kh, vh)
     assert_close(lay, out_to_f64(out), ro, "cascade mixed prefixes")
-    assert np.abs(lse.cpu().numpy() - rl).max() < LSE_TOL_MFMA_BF16
+    assert np.abs(lse.cpu().numpy() - rl).max() < LSE_TOL
 
 
 def test_shared_prefix_workload(gpu_lib):
+    """The shared-prefix batch (16 groups x 64 sequences, 2048-token
+    prefixes) in the launch configuration the benchmark times: every
+    sequence against the oracle, and against pa_decode."""
     lay = workload("shared_prefix")
-    say("case shared_prefix seed 0 (full, sampled oracle)")
-    (q, k, v), (qh, kh, vh) = device_inputs(lay)
+    say("case shared_prefix seed 0 (every sequence)")
+    (q, k, v), _ = device_inputs(lay, host_values=False)
     out, lse = run_cascade(gpu_lib, lay, q, k, v)
-    seqs = sorted({0, 1, 63, 64, 500, 777, 1023, int(np.argmax(lay.context_lens)), int(np.argmin(lay.context_lens))})
-    ro, rl = oracle_cascade(lay, qh, kh, vh, seqs)
-    assert_close(lay, out_to_f64(out)[seqs], ro[seqs], "shared_prefix sampled")
-    assert np.abs(lse.cpu().numpy()[seqs] - rl[seqs]).max() < LSE_TOL_MFMA_BF16
+    assert torch.isfinite(out.float()).all()
+    ro, rl = oracle_full(lay, q, k, v)
+    err, rel = assert_close(lay, out_to_f64(out), ro, "shared_prefix, every sequence")
+    say(f"  max-abs {err:.2e} rel-L2 {rel:.2e}")
+    assert np.abs(lse.cpu().numpy() - rl).max() < LSE_TOL
     dout, _ = run_decode(gpu_lib, lay, q, k, v)
     assert_close(lay, out_to_f64(out), out_to_f64(dout), "shared_prefix: cascade vs decode, all sequences")
-    assert torch.isfinite(out.float()).all()
 
 
 def test_cascade_needle_in_prefix_and_suffix(gpu_lib):
@@ -188,4 +191,4 @@ def test_detected_groups_drive_the_cascade(gpu_lib):
     got = out_to_f64(out)[back]
     ro, rl = oracle.decode(qh, kh, vh, bt, ctx, base.scale, base.num_kv_heads, 16, "bf16")
     assert_close(lay, got, ro, "cascade over detected groups")
-    assert np.abs(lse.cpu().numpy()[back] - rl).max() < LSE_TOL_MFMA_BF16
+    assert np.abs(lse.cpu().numpy()[back] - rl).max() < LSE_TOL

@@ -79,7 +79,9 @@ def test_llama8b_fp8_full(gpu_lib):
     assert torch.isfinite(out.float()).all()
 
 
-@pytest.mark.parametrize("hq", [32, 64, 128])
+# 8 and 16 q-heads (1 and 2 per kv-head) run on the vector stream kernel,
+# 32 to 128 on the matrix-core kernel
+@pytest.mark.parametrize("hq", [8, 16, 32, 64, 128])
 def test_needle_gather_is_bit_exact(gpu_lib, hq):
     """One row per (sequence, kv-head) scores ~2500 above every other (code
     448, scale 1, against q = 64 on one column), so its weight is exactly 1
