@@ -120,6 +120,38 @@ int pa_decode(void* out,                      /* device [S, Hq, D] dtype */
               void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Decode without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, kernels, plan and results as pa_decode
+ * (bit for bit), minus the workspace: the scratch lives in a file-scope
+ * device array of PA_NOALLOC_SCRATCH_BYTES bytes, one copy per GPU, held
+ * until the process ends.  The call allocates nothing (its first call on a
+ * device looks the array's address up; nothing is allocated then either).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (other streams, other host threads) race; calls ordered on one stream
+ * are safe.  The scratch needs no clearing between calls.
+ * Returns as pa_decode; PA_EWORKSPACE when the batch's plan needs more than
+ * PA_NOALLOC_SCRATCH_BYTES (many sequences shared by many waves: a smaller
+ * split_pages needs more), checked before anything is launched; PA_EHIP if
+ * there is no current device.
+ * ------------------------------------------------------------------------- */
+#define PA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+int pa_decode_noalloc(void* out,                   /* device [S, Hq, D] dtype */
+                      float* lse_out,              /* device [S, Hq] or NULL */
+                      const void* q,               /* device [S, Hq, D] dtype */
+                      const void* k_pool,          /* device [NP, Hkv, BS, D] dtype */
+                      const void* v_pool,          /* device [NP, Hkv, BS, D] dtype */
+                      const int32_t* block_tables, /* device [S, max_blocks_per_seq] */
+                      int32_t max_blocks_per_seq,
+                      const int32_t* context_lens,      /* device [S] */
+                      const int32_t* context_lens_host, /* host [S], same values */
+                      int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_ratio, int32_t head_dim,
+                      int32_t block_size, int64_t num_pages, float scale, pa_dtype dtype,
+                      int32_t split_pages, /* pages per split; 0 = automatic */
+                      void* stream);
+
+/* ---------------------------------------------------------------------------
  * Sliding-window decode: pa_decode where the query of a sequence with L rows
  * sees only rows [max(0, L - window), L).  A sliding-window KV group
  * declares its window in tokens (TokenSpeed deep-dive section 4.1, the

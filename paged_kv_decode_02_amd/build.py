@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpa.so")
-SOURCES = ["pa_host.cpp", "pa_api.cpp", "pa_decode.hip", "pa_tiles.hip", "pa_append.hip"]
+SOURCES = ["pa_host.cpp", "pa_api.cpp", "pa_decode.hip", "pa_tiles.hip", "pa_append.hip", "pa_noalloc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -67,7 +67,7 @@ def build(verbose: bool = False, defines: tuple = (), out: str = LIB) -> str:
             return obj
 
         # one compiler process per source, at most four at a time
-        with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as pool:
+        with ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as pool:
             objs = list(pool.map(compile_one, SOURCES))
         tmp_lib = os.path.join(tmp, "libpa.so")
         cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp_lib]

@@ -39,16 +39,15 @@ extern "C" size_t pa_decode_workspace_size(int32_t max_num_seqs, int32_t num_kv_
   return partial_layout(waves, max_num_seqs, num_kv_heads, stream_rows(gqa_ratio), head_dim).bytes;
 }
 
-namespace {
-
-// pa_decode, pa_decode_window, pa_decode_fp8 and pa_decode_multi:
-// validation, page count, workspace check, launch.
-int decode_call(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,
-                const float* k_scales, const float* v_scales, bool kv_fp8, const int32_t* block_tables,
-                int32_t max_blocks, const int32_t* context_lens, const int32_t* context_lens_host, int32_t num_seqs,
-                int32_t num_kv_heads, int32_t gqa_ratio, int32_t head_dim, int32_t block_size, int64_t num_pages,
-                float scale, pa_dtype dtype, int32_t split_pages, void* workspace, size_t workspace_bytes,
-                void* stream, int32_t window, int32_t q_len, const char* who) {
+// pa_decode, pa_decode_window, pa_decode_fp8, pa_decode_multi and
+// pa_decode_noalloc: validation, page count, workspace check, launch.
+int pa::decode_call(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,
+                    const float* k_scales, const float* v_scales, bool kv_fp8, const int32_t* block_tables,
+                    int32_t max_blocks, const int32_t* context_lens, const int32_t* context_lens_host,
+                    int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_ratio, int32_t head_dim, int32_t block_size,
+                    int64_t num_pages, float scale, pa_dtype dtype, int32_t split_pages, void* workspace,
+                    size_t workspace_bytes, void* stream, int32_t window, int32_t q_len, const char* who,
+                    bool plan_sized) {
   const std::string w(who);
   if (num_seqs < 0) return fail(PA_EINVAL, w + ": num_seqs < 0");
   if (num_seqs == 0) return PA_OK;
@@ -81,10 +80,12 @@ int decode_call(void* out, float* lse_out, const void* q, const void* k_pool, co
   // a call never depends on the occupancy the device reports.
   // (multi-token passes keep `rows` query rows per wave; the last pass
   // walks every page)
+  // (plan_sized: a fixed scratch buffer is checked against the plan the
+  // launcher actually makes instead, before anything is launched)
   const int32_t rows = multi_ws_rows(q_len, gqa_ratio);
   const PartialLayout worst = partial_layout(max_waves_per_head(total_pages, num_kv_heads, split_pages), num_seqs,
                                              num_kv_heads, rows, head_dim);
-  if (worst.bytes > workspace_bytes)
+  if (!plan_sized && worst.bytes > workspace_bytes)
     return fail(PA_EWORKSPACE, w + ": workspace holds " + std::to_string(workspace_bytes) + " bytes, needs " +
                                    std::to_string(worst.bytes));
   DecodeLaunch a;
@@ -115,8 +116,6 @@ int decode_call(void* out, float* lse_out, const void* q, const void* k_pool, co
   if (q_len == 1) return launch_decode(a);
   return launch_decode_multi(a, plan_multi(q_len, gqa_ratio, context_lens_host, num_seqs, block_size));
 }
-
-}  // namespace
 
 extern "C" int pa_decode(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,
                          const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,

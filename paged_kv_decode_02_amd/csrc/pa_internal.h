@@ -100,6 +100,15 @@ int launch_decode_multi(const DecodeLaunch& a, const MultiPlan& p);
 // passes of 4 or more rows, run on the matrix-core kernel's 16 rows).
 inline int32_t multi_ws_rows(int32_t q_len, int32_t gqa) { return q_len > 1 ? 16 : stream_rows(gqa); }
 bool decode_supported(pa_dtype dtype, int32_t head_dim, int32_t gqa);
+// Validation, planning and launch shared by the decode entry points.  With
+// plan_sized the workspace is checked against the plan actually made (a
+// fixed-size scratch buffer) instead of the largest plan the batch could get.
+int decode_call(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,
+                const float* k_scales, const float* v_scales, bool kv_fp8, const int32_t* block_tables,
+                int32_t max_blocks, const int32_t* context_lens, const int32_t* context_lens_host, int32_t num_seqs,
+                int32_t num_kv_heads, int32_t gqa_ratio, int32_t head_dim, int32_t block_size, int64_t num_pages,
+                float scale, pa_dtype dtype, int32_t split_pages, void* workspace, size_t workspace_bytes,
+                void* stream, int32_t window, int32_t q_len, const char* who, bool plan_sized = false);
 bool decode_fp8_supported(int32_t head_dim, int32_t gqa);
 int launch_decode(const DecodeLaunch& a);
 

@@ -30,6 +30,7 @@ PA_EHIP = -4
 EXPORTS = (
     "pa_decode_workspace_size",
     "pa_decode",
+    "pa_decode_noalloc",
     "pa_decode_fp8",
     "pa_decode_window",
     "pa_decode_multi_workspace_size",
@@ -77,6 +78,9 @@ def load(path: Optional[str] = None):
     lib.pa_decode.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                               c_i32, c_i64, ctypes.c_float, ctypes.c_int, c_i32, c_vp, c_sz, c_vp]
     lib.pa_decode_window.restype = ctypes.c_int
+    lib.pa_decode_noalloc.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32,
+                                      c_i32, c_i32, c_i64, ctypes.c_float, c_i32, c_i32, c_vp]
+    lib.pa_decode_noalloc.restype = c_i32
     lib.pa_decode_window.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32,
                                      c_i32, c_i32, c_i64, ctypes.c_float, ctypes.c_int, c_i32, c_i32, c_vp, c_sz,
                                      c_vp]
@@ -388,6 +392,43 @@ def decode(out, q, k_pool, v_pool, block_tables, context_lens, context_lens_host
         ch.ctypes.data,
         S, Hkv, Hq // Hkv, D, BS, NP, float(scale), _dtype_code(q), int(split_pages),
         _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream_ptr(stream),
+    )
+    return _check(rc)
+
+
+def decode_noalloc(out, q, k_pool, v_pool, block_tables, context_lens, context_lens_host, scale, lse_out=None,
+                   split_pages=0, stream=None):
+    """pa_decode_noalloc on torch tensors: pa_decode's arguments without a
+    workspace (the library's fixed per-GPU scratch is used; calls that
+    overlap on one GPU race)."""
+    import torch
+
+    S, Hq, D = q.shape
+    NP, Hkv, BS, D2 = k_pool.shape
+    if tuple(out.shape) != (S, Hq, D) or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if tuple(v_pool.shape) != tuple(k_pool.shape) or k_pool.dtype != q.dtype or v_pool.dtype != q.dtype:
+        raise ValueError("k_pool and v_pool must match each other and q's dtype")
+    if D2 != D or Hq % Hkv:
+        raise ValueError("head_dim mismatch or q heads not a multiple of kv heads")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_tables / context_lens must have one row per sequence")
+    ch = _host_i32(context_lens_host, "context_lens_host")
+    if ch.size != S:
+        raise ValueError("context_lens_host must have one entry per sequence")
+    if lse_out is not None and tuple(lse_out.shape) != (S, Hq):
+        raise ValueError("lse_out must be [S, Hq]")
+    rc = load().pa_decode_noalloc(
+        _dev(out, "out"),
+        _dev(lse_out, "lse_out", torch.float32) if lse_out is not None else None,
+        _dev(q, "q"),
+        _dev(k_pool, "k_pool"),
+        _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32),
+        ch.ctypes.data,
+        S, Hkv, Hq // Hkv, D, BS, NP, float(scale), _dtype_code(q), int(split_pages), _stream_ptr(stream),
     )
     return _check(rc)
 

@@ -400,3 +400,17 @@ def test_decode_multi_fp8_rejects_bad_arguments(kw, code):
 def test_decode_multi_fp8_zero_sequences_is_a_no_op():
     lib = pa.load()
     assert call_decode_multi_fp8(lib, S=0, q=None, out=None, ks=None) == pa.PA_OK
+
+
+def test_noalloc_without_a_device_returns_an_error():
+    """Without a GPU (this check runs on the CPU), pa_decode_noalloc looks up
+    its scratch on the current device first and fails cleanly."""
+    import torch
+
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible")
+    lib = pa.load()
+    ctx = (ctypes.c_int32 * 2)(17, 40)
+    rc = lib.pa_decode_noalloc(FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, FAKE, ctx, 2, 2, 4, 128, 16, 10, 0.1,
+                               pa.PA_BF16, 0, None)
+    assert rc == pa.PA_EHIP and "device" in pa.last_error()
