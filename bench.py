@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--split-pages", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush", choices=["read", "fill", "none"], default="read",
+                    help="before each timed step: read a 1 GiB buffer (default), fill it, or nothing")
     ap.add_argument("--via-mixed", action="store_true",
                     help="multi-token batches (every sequence the same q_len > 1) through pa_mixed_chunk "
                          "instead of pa_decode_multi")
@@ -337,10 +339,20 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
-    # Cold cache: before each timed step a fill kernel writes a 1 GiB buffer
-    # on the same stream, outside the step's event pair, which evicts the
-    # step's inputs from the 256 MB last-level cache (MALL) and the L2s.
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    # Cold cache: before each timed step 1 GiB passes through the caches on
+    # the same stream, outside the step's event pair, which evicts the step's
+    # inputs from the 256 MB last-level cache (MALL) and the L2s.  The
+    # default sweep reads the buffer (a sum): a fill would leave up to 256 MB
+    # of dirty lines whose write-back to HBM then lands inside the timed
+    # step (measured: 186 against 116 us on the Llama-shaped batch).
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    flush_out = torch.empty((), dtype=torch.float32, device=dev)
+
+    def flush():
+        if args.flush == "read":
+            torch.sum(flush_buf, dim=0, out=flush_out)
+        elif args.flush == "fill":
+            flush_buf.zero_()
 
     def cold(fn, n, pairs=0):
         """Per-step times (ms) of n steps, each after a cache flush and
@@ -351,7 +363,7 @@ def main():
             pa.profile_enable(n * pairs)
         torch.cuda.synchronize()
         for a, b in ev:
-            flush.zero_()
+            flush()
             a.record(stream)
             fn()
             b.record(stream)
@@ -490,7 +502,9 @@ def main():
             "parallelism": "single GPU",
         },
         "hbm_frac": round(gbs / roofline.HBM_PEAK_GBS, 4),
-        "timing": {"cache": "cold: 1 GiB fill before each step, outside its event pair",
+        "timing": {"cache": {"read": "cold: a 1 GiB read sweep before each step, outside its event pair",
+                             "fill": "cold: a 1 GiB fill before each step, outside its event pair",
+                             "none": "warm: no flush between steps"}[args.flush],
                    "median_ms": round(ms_per_step, 5), "min_ms": round(ms_min, 5),
                    "mean_ms": round(float(step_ms.mean()), 5),
                    "min_step_GBps": round(nb["total"] / (ms_min * 1e-3) / 1e9, 1),
