@@ -370,7 +370,9 @@ def main():
         torch.cuda.synchronize()
         kern = None
         if pairs:
-            kern = np.array(pa.profile_collect(n * pairs)).reshape(n, pairs)
+            # (as many pairs per step as the library recorded: a mixed batch
+            # with chunks and decode tokens in one launch records one)
+            kern = np.array(pa.profile_collect(n * pairs)).reshape(n, -1)
             pa.profile_enable(0)
         return np.array([a.elapsed_time(b) for a, b in ev]), kern
 
@@ -449,7 +451,14 @@ def main():
         chunk_roof = mfma_roof("tile_kernel (prefill chunks)", flops, kern_avg[0])
         extra = {"chunk_gflop": round(flops / 1e9, 3), "tokens_per_step": int(T)}
         roof = chunk_roof
-        if has_dec:
+        if has_dec and len(kern_avg) == 1:
+            # chunks and decode tokens in one launch (mixed_kernel): its HBM
+            # view (all K/V bytes of the step) and its matrix view (the chunk
+            # flops) over the same kernel time
+            roof = hbm_roof("mixed_kernel (prefill chunks + decode tokens, one launch)", nb["total"], kern_avg[0],
+                            None)
+            extra["mixed_kernel_mfma"] = mfma_roof("mixed_kernel (chunk flops)", flops, kern_avg[0])
+        elif has_dec:
             dec = lay.q_lens == 1
             dbytes = roofline.decode_bytes(lay.context_lens[dec], lay.num_q_heads, lay.num_kv_heads, D,
                                            lay.elem_bytes)["total"]

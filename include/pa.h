@@ -320,7 +320,11 @@ int pa_prefix_cascade(void* out,                       /* device [S, Hq, D] */
  * inside the chunk; q_len = 1 is a decode token and sees every row.
  * Chunks (q_len > 1) run as MFMA tiles of (token, q-head) rows against the
  * segment's keys, split along the keys and merged by log-sum-exp; decode
- * tokens run through pa_decode's kernels, so their rows equal pa_decode's.
+ * tokens run on pa_decode's stream wave.  With 4 or more q-heads per
+ * kv-head, a batch holding both runs them in one launch (chunk workgroups
+ * and decode workgroups side by side, the decode split planned for that
+ * launch), so its decode rows equal pa_decode's within the stated
+ * tolerances; a batch without chunks takes pa_decode's plan, bit for bit.
  * Chunks are built for bf16, head_dim 128, gqa_ratio 1, 2, 4, 8, 16; a
  * batch without chunks takes every pa_decode shape.
  * Returns as pa_decode, plus PA_EINVAL for cu_q_lens[0] != 0, a segment

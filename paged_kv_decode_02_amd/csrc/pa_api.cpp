@@ -243,13 +243,17 @@ extern "C" int pa_prefix_cascade(void* out, float* lse_out, const void* q, const
     }
   }
   if (suffix_pages > (int64_t(1) << 31) - 1) return fail(PA_EUNSUPPORTED, "pa_prefix_cascade: too many pages");
-  // Prefix plan: one workgroup per CU holds 128 KB of LDS, so aim at about
-  // 256 workgroups (row blocks x key splits), each a 64-key multiple of the
-  // prefix; key splits only when the row blocks alone leave CUs idle.
+  // Prefix plan: two tile workgroups fit on a CU (66 KB of LDS each), so aim
+  // at about two per CU (row blocks x key splits), each split a 64-key
+  // multiple of the prefix; key splits only when the row blocks alone leave
+  // workgroup slots idle.
   const int32_t row_chunks =
       static_cast<int32_t>(std::max<int64_t>(1, (max_rows + kPrefixRowsPerBlock - 1) / kPrefixRowsPerBlock));
   const int64_t units = static_cast<int64_t>(num_groups) * row_chunks * num_kv_heads;
-  int32_t nks = static_cast<int32_t>(std::min<int64_t>(kMaxPrefixSplits, std::max<int64_t>(1, (256 + units - 1) / units)));
+  const int cus = device_cu_count();
+  const int64_t slots = static_cast<int64_t>(kTileWorkgroupsPerCU) * (cus > 0 ? cus : 256);
+  int32_t nks =
+      static_cast<int32_t>(std::min<int64_t>(kMaxPrefixSplits, std::max<int64_t>(1, (slots + units - 1) / units)));
   int32_t kps = 64;
   if (max_prefix > 0) {
     kps = (max_prefix + nks - 1) / nks;

@@ -17,6 +17,10 @@ constexpr int kMinPagesPerWave = 4;       // automatic runs are at least one 4-p
 constexpr int kMaxResidentWaves = 16384;  // bound on waves resident on one GPU (sizes workspace)
 constexpr int kMaxPrefixSplits = 8;       // key splits of a shared prefix (sizes workspace)
 constexpr int kPrefixRowsPerBlock = 128;  // query rows one MFMA tile workgroup takes
+#ifndef PA_TILE_WG_PER_CU
+#define PA_TILE_WG_PER_CU 2
+#endif
+constexpr int kTileWorkgroupsPerCU = PA_TILE_WG_PER_CU;  // MFMA tile workgroups resident per CU
 constexpr size_t kAlign = 256;
 
 // Error reporting: thread-local message + code.
@@ -127,6 +131,10 @@ struct StreamPlan {
 int launch_stream(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_part, const int32_t* q_rows,
                   bool merge, StreamPlan* plan);
 
+// The merge of a matrix-core stream launch (16 partial rows per wave,
+// bf16, head_dim 128) over `waves` runs per kv-head; q_rows as launch_stream.
+int launch_stream_merge(const DecodeLaunch& a, const int32_t* q_rows, int64_t waves);
+
 // Prefill chunks of a mixed batch, passed by value to the MFMA tile kernel.
 constexpr int32_t kMaxChunkSplits = 8;  // key splits of one chunk (sizes workspace)
 constexpr int32_t kMinChunkSplitKeys = 1024;
@@ -147,7 +155,7 @@ struct ChunkList {
 // total tiles / (CUs * kChunkWorkgroupsPerCU) tiles of 64 keys, and no
 // fewer than kMinChunkSplitKeys keys; at most kMaxChunkSplits splits.
 #ifndef PA_CHUNK_WG_PER_CU
-#define PA_CHUNK_WG_PER_CU 2
+#define PA_CHUNK_WG_PER_CU 3
 #endif
 constexpr int kChunkWorkgroupsPerCU = PA_CHUNK_WG_PER_CU;
 struct ChunkPlan {

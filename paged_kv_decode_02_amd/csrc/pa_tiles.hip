@@ -37,12 +37,12 @@
 
 #include "pa_common.h"
 #include "pa_internal.h"
+#include "pa_stream.h"
 
 namespace pa {
 namespace {
 
-constexpr int kRows = kPrefixRowsPerBlock;  // query rows per workgroup: 4 row groups of 32
-constexpr int kKeyTile = 64;                  // keys per LDS tile (4 pages); each wave takes 32 of them
+constexpr int kRows = kPrefixRowsPerBlock;  // query rows per workgroup: 4 waves of 32
 constexpr int kPidWindow = 256;               // page ids per LDS window (64 tiles)
 
 template <int N>
@@ -64,13 +64,14 @@ __device__ __forceinline__ void lds_barrier() {
 // k = 8*(l/16) .. +8; B (32 x 16): lane l holds column l%16, the same k;
 // C (16 x 16): lane l holds column l%16, rows 4*(l/16) .. +4.
 //
-// One workgroup = 8 waves = up to 128 query rows of one kv-head against the
-// keys [k_lo, k_hi) of one block-table row, in tiles of 64 keys that stream
-// through four LDS buffers (three tiles in flight while one is used).  Wave
-// (row group rg, key half kh) takes query rows 32 rg .. +32 against keys
-// 32 kh .. +32 of every tile, so two waves share each SIMD and every K/V byte
-// in LDS is read by four waves; at the end the two key halves of a row group
-// are merged through LDS.
+// One workgroup = 4 waves = up to 128 query rows of one kv-head against the
+// keys [k_lo, k_hi) of one block-table row, in tiles of 64 keys (4 pages)
+// that stream through two LDS buffer pairs (tile t + 1 lands while tile t is
+// used).  Wave w takes query rows 32 w .. +32 against all 64 keys of every
+// tile, so every K/V byte in LDS is read by the four waves.  The workgroup
+// needs 66 KB of LDS and about 200 VGPRs per wave, so two workgroups share a
+// CU; their barriers are independent, and the matrix work of one overlaps the
+// softmax of the other on the same SIMD.
 //  PREFIX: unit = a group; rows are (member, q-head) pairs; keys are the
 //          shared prefix, read through the first member's table; every row
 //          sees every key.
@@ -82,115 +83,123 @@ __device__ __forceinline__ void lds_barrier() {
 // i % 8), so they fetch the same K/V tiles through the same L2.
 // Output: one partial (normalised o, log2-sum-exp) per (row, key split);
 // a row that sees no key of the split gets o = 0, lse = -inf.
+constexpr int kTileThreads = 256;
+
+template <int KT, int NB>
+struct TileLds {
+  uint4 k[NB][KT * 16];         // [key][16 chunks of 16 bytes], chunk XOR-swizzled by tswz(key % 16)
+  uint4 v[NB][KT * 16];         // the same layout
+  int32_t pid[2][kPidWindow];   // page ids of the key range, two windows of 256 pages
+};
+
+// Chunk swizzle of a K/V row in LDS: global chunk c of row r sits at LDS
+// chunk c ^ (r % 16), so that the K operand read (16 lanes, 16 consecutive
+// rows, one 16-byte chunk each) touches 16 distinct chunk slots.  (A swizzle
+// that also spreads the transposed V reads, whose 4 rows x 2 chunks share 4
+// slots here, measured no faster.)
+__device__ __forceinline__ int tswz(int r) { return r & 15; }
+
+// What one tile workgroup computes.
+struct TileWork {
+  int seg;          // block-table row the keys are read through
+  int kvh;          // kv-head
+  int n_rows;       // query rows of the unit
+  int row_base;     // first row of this workgroup
+  int k_lo, k_hi;   // key range
+  int L, n_tok;     // CHUNK: the segment's rows and query tokens
+  int q_base;       // q row of the unit's first token (chunk) or member (prefix)
+  int64_t rec_base; // partial record of the unit's first row
+  int nsplit, ks;   // key splits of the unit, and this one
+};
+
+// Workgroup slot -> its work; false if the slot has none.  Slot j of XCD x
+// holds row block j % RC of item (j / RC) * 8 + x.  Chunks: items are
+// numbered chunk by chunk in launch order (the chunks with the longest
+// splits first), each chunk's (kv-head, split) pairs together; prefix
+// groups: (group, kv-head, split) in order.  Prefix groups also record each
+// member's first suffix page (by the first row block of split 0, kv-head 0).
 template <int G, bool CHUNK>
-__global__ __launch_bounds__(512) void tile_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool,
-    const int32_t* __restrict__ block_tables, int max_blocks, const int32_t* __restrict__ ctx,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ group_off, const int32_t* __restrict__ prefix_lens,
-    ChunkList chunks, int S, int RC, int nks, int kps, int Hkv, int n_items, int num_pages, float scale_log2,
-    int32_t* __restrict__ begin_pages, int32_t* __restrict__ seq_info, float* __restrict__ pre_o,
-    float* __restrict__ pre_lse) {
-  constexpr int D = 128;
-  constexpr int TILE = 16 * D * 2;  // bytes of one (page, kv-head) tile
-  // Four buffers each of K and V: [key][16 chunks of 16 bytes], the chunk
-  // index XOR-swizzled by key % 16 so that column reads spread over the
-  // banks.  The tiles arrive by DMA (dma16), waited for explicitly.
-  // (Four arrays each, named statically in a loop unrolled by four.)
-  __shared__ uint4 k_lds0[kKeyTile * 16], k_lds1[kKeyTile * 16], k_lds2[kKeyTile * 16], k_lds3[kKeyTile * 16];
-  __shared__ uint4 v_lds0[kKeyTile * 16], v_lds1[kKeyTile * 16], v_lds2[kKeyTile * 16], v_lds3[kKeyTile * 16];
-  // Page ids of the key range, in windows of kPidWindow pages (64 tiles),
-  // two windows resident: reading an id from LDS is one short broadcast
-  // read, where a scalar load from the table would put a cache round trip
-  // in front of every tile's DMA.
-  __shared__ int32_t pid_lds[2][kPidWindow];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // (wave-uniform: scalar from here on)
-  const int rg = wv & 3;   // row group
-  const int kh = wv >> 2;  // key half
-  const int Hq = Hkv * G;
-
-  // Per-sequence set-up for the launches that follow (mixed batches: each
-  // chunk's "no decode pages" mark and the "not shared" record the decode
-  // merge reads).
-  if constexpr (CHUNK) {
-    if (blockIdx.x == 0) {
-      for (int s = tid; s < S; s += 512) {
-        const bool chunk = cu_q[s + 1] - cu_q[s] > 1;
-        const int64_t pg = (static_cast<int64_t>(ctx[s]) + 15) >> 4;
-        begin_pages[s] = chunk ? static_cast<int>(pg < max_blocks ? pg : max_blocks) : 0;
-        if (chunk) {
-          seq_info[4 * s + 0] = 0;
-          seq_info[4 * s + 1] = 0;
-          seq_info[4 * s + 2] = 0;
-          seq_info[4 * s + 3] = 0;
-        }
-      }
-    }
-  }
-
-  // Workgroup -> (item w, row block rc): slot j of XCD x holds row block
-  // j % RC of item (j / RC) * 8 + x.
-  const int xcd = blockIdx.x & 7;
-  const int slot = blockIdx.x >> 3;
+__device__ __forceinline__ bool tile_work(int b, int RC, int n_items, int Hkv, int nks, int kps,
+                                          const ChunkList& chunks, const int32_t* __restrict__ ctx,
+                                          const int32_t* __restrict__ cu_q, const int32_t* __restrict__ group_off,
+                                          const int32_t* __restrict__ prefix_lens, int32_t* __restrict__ begin_pages,
+                                          TileWork& tw) {
+  const int xcd = b & 7;
+  const int slot = b >> 3;
   const int w = (slot / RC) * 8 + xcd;
   const int rc = slot % RC;
-  if (w >= n_items) return;
-  // Item w -> (unit u, kv-head, key split ks of nsplit, kpsplit keys each).
-  // Chunks: items are numbered chunk by chunk in launch order (the chunks
-  // with the longest splits first), each chunk's (kv-head, split) pairs
-  // together; prefix groups: (group, kv-head, split) in order.
-  int u, kvh, ks, nsplit, kpsplit;
+  if (w >= n_items) return false;
+  int u;
   if constexpr (CHUNK) {
     int j = 0;
     while (chunks.item_end[j] <= w) ++j;  // w < n_items = item_end[n - 1]
     u = chunks.ord[j];
     const int local = w - (j > 0 ? chunks.item_end[j - 1] : 0);
-    nsplit = chunks.nks[u];
-    kpsplit = chunks.kps[u];
-    ks = local % nsplit;
-    kvh = local / nsplit;
-  } else {
-    nsplit = nks;
-    kpsplit = kps;
-    ks = w % nks;
-    kvh = (w / nks) % Hkv;
-    u = w / (nks * Hkv);
-  }
-
-  // rec_base: partial record (token or member, kv-head, split) of the
-  // unit's first row.
-  int seg, n_rows, k_lo, k_hi, L = 0, n_tok = 1, q_base;
-  int64_t rec_base;
-  if constexpr (CHUNK) {
-    seg = chunks.seg[u];
-    n_tok = cu_q[seg + 1] - cu_q[seg];
-    L = ctx[seg];
-    n_rows = n_tok * G;
-    q_base = cu_q[seg];
-    rec_base = chunks.rec[u];
-    const int r_end = min(n_rows, (rc + 1) * kRows);
+    tw.nsplit = chunks.nks[u];
+    const int kpsplit = chunks.kps[u];
+    tw.ks = local % tw.nsplit;
+    tw.kvh = local / tw.nsplit;
+    tw.seg = chunks.seg[u];
+    tw.n_tok = cu_q[tw.seg + 1] - cu_q[tw.seg];
+    tw.L = ctx[tw.seg];
+    tw.n_rows = tw.n_tok * G;
+    tw.q_base = cu_q[tw.seg];
+    tw.rec_base = chunks.rec[u];
+    const int r_end = min(tw.n_rows, (rc + 1) * kRows);
     const int i_max = (r_end - 1) / G;
-    const int k_end = min(L, L - n_tok + i_max + 1);
-    k_lo = ks * kpsplit;
-    k_hi = min(k_end, k_lo + kpsplit);
+    const int k_end = min(tw.L, tw.L - tw.n_tok + i_max + 1);
+    tw.k_lo = tw.ks * kpsplit;
+    tw.k_hi = min(k_end, tw.k_lo + kpsplit);
   } else {
+    tw.nsplit = nks;
+    tw.ks = w % nks;
+    tw.kvh = (w / nks) % Hkv;
+    u = w / (nks * Hkv);
     const int off0 = group_off[u];
     const int n_g = group_off[u + 1] - off0;
     const int P = prefix_lens[u];  // prefix tokens (whole pages)
-    if (kvh == 0 && rc == 0 && ks == 0)
-      for (int i = tid; i < n_g; i += 512) begin_pages[off0 + i] = P / 16;
-    seg = off0;
-    n_rows = n_g * G;
-    q_base = off0;
-    rec_base = static_cast<int64_t>(off0) * Hkv * nks;
-    k_lo = ks * kps;
-    k_hi = min(P, k_lo + kps);
+    if (tw.kvh == 0 && rc == 0 && tw.ks == 0)
+      for (int i = threadIdx.x; i < n_g; i += kTileThreads) begin_pages[off0 + i] = P / 16;
+    tw.seg = off0;
+    tw.n_rows = n_g * G;
+    tw.q_base = off0;
+    tw.rec_base = static_cast<int64_t>(off0) * Hkv * nks;
+    tw.k_lo = tw.ks * kps;
+    tw.k_hi = min(P, tw.k_lo + kps);
+    tw.L = 0;
+    tw.n_tok = 1;
   }
-  if (k_lo >= k_hi || rc * kRows >= n_rows) return;  // uniform over the workgroup
+  tw.row_base = rc * kRows;
+  return tw.k_lo < tw.k_hi && tw.row_base < tw.n_rows;
+}
 
-  const int row0 = rc * kRows + rg * 32;  // first of this wave's 32 query rows
+// KT keys per tile (32 or 64: 2 or 4 pages), NB buffers (NB - 1 tiles in
+// flight while one is used).
+template <int G, bool CHUNK, int KT, int NB>
+__device__ __forceinline__ void tile_body(const TileWork& tw, TileLds<KT, NB>& lds, const uint16_t* __restrict__ q,
+                                          const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool,
+                                          const int32_t* __restrict__ block_tables, int max_blocks, int Hkv,
+                                          int num_pages, float scale_log2, float* __restrict__ pre_o,
+                                          float* __restrict__ pre_lse) {
+  constexpr int D = 128;
+  constexpr int TILE = 16 * D * 2;      // bytes of one (page, kv-head) tile
+  constexpr int NKB = KT / 16;          // 16-key blocks of a tile
+  constexpr int NKS = KT / 32;          // 32-key steps of P.V
+  constexpr int LPW = KT / 16;          // 1 KB loads per wave per tile, each of K and V
+  constexpr int TPW = kPidWindow * 16 / KT;  // tiles per page-id window
+  static_assert(KT == 32 || KT == 64, "tiles of 2 or 4 pages");
+  static_assert(NB >= 2 && NB <= 4 && TPW > NB, "buffer count");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // (wave-uniform: scalar from here on)
+  const int Hq = Hkv * G;
+  // (the work is uniform over the workgroup: keep it in scalar registers,
+  // so that the page bases of the DMAs are scalar)
+  auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+  const int kvh = uni(tw.kvh), n_rows = uni(tw.n_rows), L = uni(tw.L), n_tok = uni(tw.n_tok);
+  const int k_lo = uni(tw.k_lo), k_hi = uni(tw.k_hi), seg = uni(tw.seg), q_base = uni(tw.q_base);
+
+  const int row0 = uni(tw.row_base) + wv * 32;  // first of this wave's 32 query rows
   const int col = lane & 15;
   const int lg = lane >> 4;
   // Q^T operand (B of S^T = K Q^T): row r = row0 + 16 rb + col, d = 32 c + 8 lg.
@@ -228,170 +237,162 @@ __global__ __launch_bounds__(512) void tile_kernel(
   // normaliser sums the float32 probabilities while P.V takes them rounded
   // to bf16.
   f32x4 o[8][2];
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) o[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float lsum[2] = {0.f, 0.f};
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-    for (int db = 0; db < 8; ++db) o[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
   float m[2] = {-INFINITY, -INFINITY};
 
-  // K or V of tile t (keys k_lo + 64 t ..) -> an LDS buffer, by DMA: slot
-  // (i*8 + wave)*64 + lane of a buffer holds key slot/16, chunk
-  // (slot%16) ^ (key%16).  Keys past the tile's end (past the split or the
+  // K or V of tile t (keys k_lo + KT t ..) -> an LDS buffer, by DMA: the
+  // tile's KT / 4 loads of 1 KB (4 keys each) are spread over the 4 waves;
+  // load g covers page g / 4, keys 4 (g % 4) .. +3, and lane (lg, col) of it
+  // writes LDS chunk col of key 4 (g % 4) + lg, which holds global chunk
+  // col ^ tswz(key).  Keys past the tile's end (past the split or the
   // sequence) load the last valid key's row: finite values whose
   // probability is 0.
-  const int nt = (k_hi - k_lo + kKeyTile - 1) / kKeyTile;
-  // Lane offsets of a whole tile's DMA inside its page tile: slot
-  // (i*8 + wave)*64 + lane -> key row % 16 and the swizzled chunk.
-  uint32_t dma_off[2];
+  const int nt = (k_hi - k_lo + KT - 1) / KT;
+  uint32_t dma_off[LPW];  // inside a page tile, for this wave's loads
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int sl = (i * 8 + wv) * 64 + lane;
-    const int key = sl >> 4;
-    dma_off[i] = (key & 15) * (D * 2) + ((sl & 15) ^ (key & 15)) * 16;
+  for (int i = 0; i < LPW; ++i) {
+    const int g = wv * LPW + i;
+    const int key = 4 * (g & 3) + lg;
+    dma_off[i] = key * (D * 2) + ((col ^ tswz(key)) * 16);
   }
   // Window w of page ids: pages k_lo/16 + 256 w .. +256 of the table row
-  // (entries past the row read its last entry), one dword DMA per wave
-  // from waves 0..3.
+  // (entries past the row read its last entry), one dword DMA per lane.
   const int pg0 = k_lo / 16;
   auto issue_pids = [&](int w) {
-    if (wv < 4) {
-      const int p = min(pg0 + w * kPidWindow + wv * 64 + lane, max_blocks - 1);
-      dma4(bt + p, lds_offset(&pid_lds[w & 1][wv * 64]));
-    }
+    const int p = min(pg0 + w * kPidWindow + wv * 64 + lane, max_blocks - 1);
+    dma4(bt + p, lds_offset(&lds.pid[w & 1][wv * 64]));
   };
-  // Two DMA loads per wave: this wave's share of tile t of the pool at
-  // `pool` into buffer `dst`.  Page ids come from the LDS window (uniform).
   auto issue_half = [&](int t, const char* pool, uint4* dst) {
-    const int kt = k_lo + t * kKeyTile;
-    const int nk = min(kKeyTile, k_hi - kt);
-    const int npg = (nk + 15) / 16;
-    const int32_t* pw = &pid_lds[(t / (kPidWindow / 4)) & 1][(t * 4) % kPidWindow];
-    int pid[4];
+    const int kt = k_lo + t * KT;
+    const int nk = min(KT, k_hi - kt);
+    const int32_t* pw = &lds.pid[(t / TPW) & 1][(t * NKB) % kPidWindow];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      pid[j] = __builtin_amdgcn_readfirstlane(min(max(pw[min(j, npg - 1)], 0), num_pages - 1));
-    if (nk == kKeyTile) {
-      // Whole tile: DMA instruction i of this wave covers keys
-      // 4 (8 i + wave) .. +4, all in page 2 i + wave / 4; the page's tile
-      // base is scalar, the lane's row and chunk a fixed offset.
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int64_t tb = (static_cast<int64_t>(pid[2 * i + wv / 4]) * Hkv + kvh) * TILE;
-        dma16_sbase(pool + tb, dma_off[i], lds_offset(&dst[(i * 8 + wv) * 64]));
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int sl = (i * 8 + wv) * 64 + lane;
-        const int key = sl >> 4;
-        const int ch = (sl & 15) ^ (key & 15);
+    for (int i = 0; i < LPW; ++i) {
+      const int g = wv * LPW + i;
+      const int page = g >> 2;
+      uint4* d = dst + g * 64;
+      if (nk >= 16 * page + 4 * (g & 3) + 4) {
+        // all 4 keys of the load exist: the page's tile base is scalar, the
+        // lane's row and chunk a fixed offset
+        const int pid = __builtin_amdgcn_readfirstlane(min(max(pw[page], 0), num_pages - 1));
+        dma16_sbase(pool + (static_cast<int64_t>(pid) * Hkv + kvh) * TILE, dma_off[i], lds_offset(d));
+      } else {
+        const int key = 16 * page + 4 * (g & 3) + lg;
         const int kc = min(key, nk - 1);
-        const int64_t off = (static_cast<int64_t>(pid[kc >> 4]) * Hkv + kvh) * TILE + (kc & 15) * (D * 2) + ch * 16;
-        dma16(pool + off, lds_offset(&dst[(i * 8 + wv) * 64]));
+        const int pid = min(max(pw[kc >> 4], 0), num_pages - 1);
+        const int64_t off =
+            (static_cast<int64_t>(pid) * Hkv + kvh) * TILE + (kc & 15) * (D * 2) + ((col ^ tswz(key & 15)) * 16);
+        dma16(pool + off, lds_offset(d));
       }
     }
   };
-  // Per-lane byte offsets of the transposed V reads inside a buffer: lane
-  // (group lg, j) reads row key0 + j/4, columns d0 + 4(j%4) .. +3, with
-  // key0 = 32 kh + 4 lg (+16) and d0 = 16 db.
+  auto issue_tile = [&](int t, int b) {
+    issue_half(t, kbytes, lds.k[b]);
+    issue_half(t, vbytes, lds.v[b]);
+  };
+  // Per-lane row and chunk of the transposed V reads: lane (group lg, j)
+  // reads row key0 + j/4, columns d0 + 4(j%4) .. +3, with key0 = 32 ks + 4 lg
+  // (+16) and d0 = 16 db.
   const int tr_r = col >> 2;
   const int tr_c = col & 3;
 
-  // Tile t's K and V into buffers kw, vw.
-  auto issue_tile = [&](int t, uint4* kw, uint4* vw) {
-    issue_half(t, kbytes, kw);
-    issue_half(t, vbytes, vw);
-  };
-
-  // The first page-id window, then tiles 0..2 in flight before the first
-  // is used.
+  // The first page-id window (and the second, if the range needs it), then
+  // tiles 0 .. NB - 2 in flight before the loop.
   issue_pids(0);
   wait_vmcnt<0>();
   lds_barrier();
-  if (nt > kPidWindow / 4) issue_pids(1);
-  issue_tile(0, k_lds0, v_lds0);
-  if (nt > 1) issue_tile(1, k_lds1, v_lds1);
-  if (nt > 2) issue_tile(2, k_lds2, v_lds2);
-
-  // One tile: wait for its DMA (each wave issued 4 loads per tile; tiles
-  // t+1 and t+2 may stay in flight), start tile t+3 into the buffer freed by
-  // tile t-1, compute.  Returns whether another tile follows.
-  auto tile = [&](int t, const uint4* kb_lds, const uint4* vb_lds4, uint4* k_next, uint4* v_next) -> bool {
-    const int kt = k_lo + t * kKeyTile;
-    const int nk = min(kKeyTile, k_hi - kt);  // keys of this tile that exist
-    const int ahead = min(2, nt - 1 - t);
-    if (ahead >= 2)
-      wait_vmcnt<8>();
-    else if (ahead == 1)
-      wait_vmcnt<4>();
-    else
-      wait_vmcnt<0>();
-    // Every wave's part of this tile has landed, and every wave is done
-    // with the buffer tile t-1 used.
-    lds_barrier();
-    if (t + 3 < nt) issue_tile(t + 3, k_next, v_next);
-    // Page-id window w + 1 into the buffer window w - 1 used: its last
-    // tile's DMA went out three tiles before window w began.  (Its loads,
-    // issued after this tile's, are waited for by the tile waits that
-    // follow, long before the first of its ids is read.)
-    if (t % (kPidWindow / 4) == 0 && t > 0 && (t / (kPidWindow / 4) + 1) * (kPidWindow / 4) < nt)
-      issue_pids(t / (kPidWindow / 4) + 1);
-    const char* vb_lds = reinterpret_cast<const char*>(vb_lds4);
-
-    // S^T = K Q^T: s[kb][rb] holds keys 32 kh + 16 kb + 4 lg + i, query
-    // row 16 rb + col.
-    f32x4 s[2][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = kh * 32 + kb * 16 + col;
+  for (int t = 0; t < NB - 1; ++t)
+    if (t < nt) issue_tile(t, t);
+  if (nt > TPW) issue_pids(1);
+
+  int buf = 0;  // buffer of tile t
+  for (int t = 0; t < nt; ++t) {
+    const int kt = k_lo + t * KT;
+    const int nk = min(KT, k_hi - kt);  // keys of this tile that exist
+    // This wave's loads of tile t have landed once only the loads of the
+    // tiles after it (at most NB - 2, 2 LPW loads each, plus any page-id
+    // load issued after them) remain; after the barrier every wave's have,
+    // and every wave is done with tile t - 1, whose buffer takes tile
+    // t + NB - 1.
+    const int ahead = min(NB - 2, nt - 1 - t);
+    if constexpr (NB >= 4) {
+      if (ahead >= 2) wait_vmcnt<4 * LPW>();
+      else if (ahead == 1) wait_vmcnt<2 * LPW>();
+      else wait_vmcnt<0>();
+    } else if constexpr (NB == 3) {
+      if (ahead >= 1) wait_vmcnt<2 * LPW>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();
+    const int tn = t + NB - 1;
+    if (tn < nt) {
+      const int bn = buf == 0 ? NB - 1 : buf - 1;  // (tn % NB: the buffer tile t - 1 used)
+      issue_tile(tn, bn);
+      // The first tile of page-id window W has just been issued: load
+      // window W + 1 into the buffer window W - 1 used (every tile of it was
+      // issued before this iteration's barrier).
+      if (tn % TPW == 0 && tn > 0 && tn + TPW < nt) issue_pids(tn / TPW + 1);
+    }
+    const uint4* kb_lds = lds.k[buf];
+    const char* vb_lds = reinterpret_cast<const char*>(lds.v[buf]);
+    buf = buf + 1 == NB ? 0 : buf + 1;
+
+    // S^T = K Q^T: s[kb][rb] holds keys 16 kb + 4 lg + i, query row
+    // 16 rb + col.  Each K operand serves both row blocks.
+    f32x4 s[NKB][2];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int key = kb * 16 + col;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) s[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int cc = c * 4 + lg;
-        const u32x4 a = *(LdsU4*)(&kb_lds[key * 16 + (cc ^ (key & 15))]);
+        const u32x4 a = *(LdsU4*)(&kb_lds[key * 16 + (cc ^ tswz(col))]);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) s[kb][rb] = mfma16x16x32(a, qb[rb][c], s[kb][rb]);
       }
     }
-    // Online softmax per query row (column of S^T); the 32 keys of a row in
-    // this wave's half are spread over this lane's 8 values and the lanes
-    // l^16, l^32, l^48.  Keys are masked (by select) only in tiles that need
-    // it: the last, partial tile of a split, and chunk tiles that cross the
-    // causal diagonal of this wave's rows.
-    const bool need_mask = nk < kh * 32 + 32 || (CHUNK && kt + kh * 32 + 31 > vis_lo);
+    // Keys are masked (by select) only in tiles that need it: the last,
+    // partial tile of a split, and chunk tiles that cross the causal
+    // diagonal of this wave's rows.
+    const bool need_mask = nk < KT || (CHUNK && kt + KT - 1 > vis_lo);
     if (need_mask) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int key = kh * 32 + kb * 16 + lg * 4 + i;
+            const int key = kb * 16 + lg * 4 + i;
             const bool ok = key < nk && (!CHUNK || kt + key <= vis[rb]);
             s[kb][rb][i] = ok ? s[kb][rb][i] : -INFINITY;
           }
     }
-    float mx[2];
+    // Online softmax per query row (column of S^T): the row's KT keys are
+    // spread over this lane's 4 NKB values and the lanes l^16, l^32, l^48.
+    u32x4 pb[NKS][2];  // P^T operand [32-key step ks][row block rb]
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       float x = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) x = fmaxf(x, s[kb][rb][i]);
-      mx[rb] = max_xor32(max_xor16(x)) * scale_log2;  // scale > 0 keeps the order
-    }
-    // Lazy rescaling: probabilities are taken against the running reference
-    // m, which moves (and o, the row sums are rescaled) only when a row's
-    // maximum exceeds it by more than 2^8 -- so p <= 256, and the rescale, a
-    // wave-wide branch, is rare after the first tiles.
-    if (__ballot(mx[0] > m[0] + 8.f || mx[1] > m[1] + 8.f) != 0ull) {
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const float mn = fmaxf(m[rb], mx[rb]);
+      const float mx = max_xor32(max_xor16(x)) * scale_log2;  // scale > 0 keeps the order
+      // Lazy rescaling: probabilities are taken against the running
+      // reference m, which moves (and o, the row sums are rescaled) only
+      // when a row's maximum exceeds it by more than 2^8 -- so p <= 256, and
+      // the rescale, a wave-wide branch, is rare after the first tiles.
+      if (__ballot(mx > m[rb] + 8.f) != 0ull) {
+        const float mn = fmaxf(m[rb], mx);
         // m = -inf (nothing visible yet): o and the sums are 0, any factor will do
         const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m[rb] - mn);
         m[rb] = mn;
@@ -399,102 +400,89 @@ __global__ __launch_bounds__(512) void tile_kernel(
 #pragma unroll
         for (int db = 0; db < 8; ++db) o[db][rb] *= alpha;
       }
-    }
-    u32x4 pb[2];  // P^T operand per row block
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
       // A row with no visible key so far keeps m = -inf: its p are all 0.
       const float nref = m[rb] == -INFINITY ? 0.f : -m[rb];
-      uint32_t pw[2][2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float p[4];
+      for (int ks = 0; ks < NKS; ++ks) {
+        uint32_t pw[2][2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[i] = fast_exp2(fmaf(s[kb][rb][i], scale_log2, nref));
-          lsum[rb] += p[i];
+        for (int e = 0; e < 2; ++e) {
+          float p[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            p[i] = fast_exp2(fmaf(s[2 * ks + e][rb][i], scale_log2, nref));
+            lsum[rb] += p[i];
+          }
+          pw[e][0] = bf16x2_rne(p[0], p[1]);
+          pw[e][1] = bf16x2_rne(p[2], p[3]);
         }
-        pw[kb][0] = bf16x2_rne(p[0], p[1]);
-        pw[kb][1] = bf16x2_rne(p[2], p[3]);
+        // k slots 8 lg .. 8 lg + 7 = keys 32 ks + 4 lg + [0, 4) and
+        // 32 ks + 16 + 4 lg + [0, 4): the same order the V^T operand uses.
+        pb[ks][rb] = u32x4{pw[0][0], pw[0][1], pw[1][0], pw[1][1]};
       }
-      // k slots 8 lg .. 8 lg + 7 = keys 32 kh + 4 lg + [0, 4) and
-      // 32 kh + 16 + 4 lg + [0, 4): the same order the V^T operand uses.
-      pb[rb] = u32x4{pw[0][0], pw[0][1], pw[1][0], pw[1][1]};
     }
     // O^T += V^T P^T; the V^T operand (d = 16 db + col, keys as above) comes
-    // from two transposed reads of 4 keys each.
+    // from two transposed reads of 4 keys each and serves both row blocks.
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      u32x2 part[2];
+    for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int row = kh * 32 + e * 16 + lg * 4 + tr_r;
-        const int ch = (db * 2 + (tr_c >> 1)) ^ (row & 15);
-        part[e] = lds_read_tr16(vb_lds + row * (D * 2) + ch * 16 + (tr_c & 1) * 8);
+      for (int db = 0; db < 8; ++db) {
+        u32x2 part[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int row = ks * 32 + e * 16 + lg * 4 + tr_r;
+          const int ch = (db * 2 + (tr_c >> 1)) ^ tswz(row & 15);
+          part[e] = lds_read_tr16(vb_lds + row * (D * 2) + ch * 16 + (tr_c & 1) * 8);
+        }
+        const u32x4 a = u32x4{part[0].x, part[0].y, part[1].x, part[1].y};
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) o[db][rb] = mfma16x16x32(a, pb[ks][rb], o[db][rb]);
       }
-      const u32x4 a = u32x4{part[0].x, part[0].y, part[1].x, part[1].y};
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) o[db][rb] = mfma16x16x32(a, pb[rb], o[db][rb]);
     }
-    return t + 1 < nt;
-  };
-  for (int t = 0;; t += 4) {
-    if (!tile(t, k_lds0, v_lds0, k_lds3, v_lds3)) break;
-    if (!tile(t + 1, k_lds1, v_lds1, k_lds0, v_lds0)) break;
-    if (!tile(t + 2, k_lds2, v_lds2, k_lds1, v_lds1)) break;
-    if (!tile(t + 3, k_lds3, v_lds3, k_lds2, v_lds2)) break;
   }
 
-  // Merge the two key halves of each row group through LDS (the buffers are
-  // free once every wave is past its last tile): wave (rg, kh) hands its
-  // state for row block 1 - kh to its partner and merges the partner's state
-  // for row block kh into its own.  Record (rg, kh): o as [8 db][64 lanes]
-  // f32x4 in K buffer rg at 8 KB * kh; m and the row sum per lane in V
-  // buffer 0 at 128 floats * (2 rg + kh).
-  // (the row sums over all of this wave's keys: its lanes l, l ^ 16, l ^ 32
-  // and l ^ 48 hold the same row)
+  // Normalise and write this wave's rows: the row sums over all the keys of
+  // the split (lanes l, l ^ 16, l ^ 32, l ^ 48 hold the same row).
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) lsum[rb] = add_xor32(add_xor16(lsum[rb]));
-  __syncthreads();
-  uint4* kbuf = rg == 0 ? k_lds0 : rg == 1 ? k_lds1 : rg == 2 ? k_lds2 : k_lds3;
-  float* xm = reinterpret_cast<float*>(v_lds0);
-  // (Row block selected by value, not by a run-time index, so that o stays
-  // in registers.)
-  {
-    f32x4* xo = reinterpret_cast<f32x4*>(kbuf) + kh * 512;
+  for (int rb = 0; rb < 2; ++rb) {
+    const float lt = add_xor32(add_xor16(lsum[rb]));
+    const int r = row0 + rb * 16 + col;
+    if (r < n_rows) {
+      const int64_t pr = (tw.rec_base + (static_cast<int64_t>(r / G) * Hkv + kvh) * tw.nsplit + tw.ks) * G + r % G;
+      const bool any = lt > 0.f;
+      const float inv = any ? 1.0f / lt : 0.f;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) xo[db * 64 + lane] = kh ? o[db][0] : o[db][1];
-    xm[(2 * rg + kh) * 128 + lane] = kh ? m[0] : m[1];
-    xm[(2 * rg + kh) * 128 + 64 + lane] = kh ? lsum[0] : lsum[1];
-  }
-  __syncthreads();
-  const int rb = kh;
-  f32x4 om[8];
-#pragma unroll
-  for (int db = 0; db < 8; ++db) om[db] = kh ? o[db][1] : o[db][0];
-  const float mm = kh ? m[1] : m[0];
-  const float lm = kh ? lsum[1] : lsum[0];
-  const f32x4* po = reinterpret_cast<const f32x4*>(kbuf) + (1 - kh) * 512;
-  const float* pm = xm + (2 * rg + 1 - kh) * 128;
-  const float m2 = pm[lane];
-  const float l2 = pm[64 + lane];
-  const float mn = fmaxf(mm, m2);
-  // A half that saw no visible key keeps m = -inf and o = l = 0.
-  const float a1 = mm == -INFINITY ? 0.f : fast_exp2(mm - mn);
-  const float a2 = m2 == -INFINITY ? 0.f : fast_exp2(m2 - mn);
-  const float lt = lm * a1 + l2 * a2;
-  const int r = row0 + rb * 16 + col;
-  if (r < n_rows) {
-    const int64_t pr = (rec_base + (static_cast<int64_t>(r / G) * Hkv + kvh) * nsplit + ks) * G + r % G;
-    const bool any = lt > 0.f;
-    const float inv = any ? 1.0f / lt : 0.f;
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const f32x4 v = (om[db] * a1 + po[db * 64 + lane] * a2) * inv;
-      *reinterpret_cast<f32x4*>(pre_o + pr * D + db * 16 + lg * 4) = v;
+      for (int db = 0; db < 8; ++db)
+        *reinterpret_cast<f32x4*>(pre_o + pr * D + db * 16 + lg * 4) = o[db][rb] * inv;
+      if (lg == 0) pre_lse[pr] = any ? m[rb] + fast_log2(lt) : -INFINITY;
     }
-    if (lg == 0) pre_lse[pr] = any ? mn + fast_log2(lt) : -INFINITY;
   }
+}
+
+// Tile shape of the launches: PA_TILE_KEYS keys per tile, PA_TILE_BUFS buffers.
+#ifndef PA_TILE_KEYS
+#define PA_TILE_KEYS 64
+#endif
+#ifndef PA_TILE_BUFS
+#define PA_TILE_BUFS 2
+#endif
+constexpr int kTK = PA_TILE_KEYS;
+constexpr int kTB = PA_TILE_BUFS;
+
+template <int G, bool CHUNK>
+__global__ __launch_bounds__(kTileThreads, kTileWorkgroupsPerCU) void tile_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool,
+    const int32_t* __restrict__ block_tables, int max_blocks, const int32_t* __restrict__ ctx,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ group_off, const int32_t* __restrict__ prefix_lens,
+    ChunkList chunks, int RC, int nks, int kps, int Hkv, int n_items, int num_pages, float scale_log2,
+    int32_t* __restrict__ begin_pages, float* __restrict__ pre_o, float* __restrict__ pre_lse) {
+  __shared__ TileLds<kTK, kTB> lds;
+  TileWork tw;
+  if (!tile_work<G, CHUNK>(blockIdx.x, RC, n_items, Hkv, nks, kps, chunks, ctx, cu_q, group_off, prefix_lens,
+                           begin_pages, tw))
+    return;  // uniform over the workgroup
+  tile_body<G, CHUNK, kTK, kTB>(tw, lds, q, k_pool, v_pool, block_tables, max_blocks, Hkv, num_pages, scale_log2, pre_o,
+                      pre_lse);
 }
 
 // Merge the key splits of one chunk token (all G heads of a kv-head) and
@@ -633,11 +621,11 @@ int launch_cascade_g(const CascadeLaunch& c) {
   none.n = 0;
   const int n_items = c.num_groups * a.num_kv_heads * c.nks;
   const unsigned blocks = static_cast<unsigned>((n_items + 7) / 8 * 8 * c.row_chunks);
-  hipLaunchKernelGGL((tile_kernel<G, false>), dim3(blocks), dim3(512), 0, st, static_cast<const uint16_t*>(a.q),
+  hipLaunchKernelGGL((tile_kernel<G, false>), dim3(blocks), dim3(kTileThreads), 0, st, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k_pool), static_cast<const uint16_t*>(a.v_pool),
                      a.block_tables, a.max_blocks, a.context_lens, nullptr, c.group_offsets, c.prefix_lens, none,
-                     a.num_seqs, c.row_chunks, c.nks, c.kps, a.num_kv_heads, n_items, static_cast<int>(a.num_pages),
-                     scale_log2, begin_pages, nullptr, pre_o, pre_lse);
+                     c.row_chunks, c.nks, c.kps, a.num_kv_heads, n_items, static_cast<int>(a.num_pages), scale_log2,
+                     begin_pages, pre_o, pre_lse);
   profile_after(a.stream);
   if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_prefix_cascade: prefix kernel launch failed");
   // Suffix: the stream decode kernel over the pages after each prefix.
@@ -660,19 +648,99 @@ int launch_cascade_g(const CascadeLaunch& c) {
   return PA_OK;
 }
 
+// Decode runs of the one-launch mixed kernel: the runs of a plain decode
+// launch (4 matrix-core stream waves per CU) times PA_MIXED_RUNS_PER_WAVE.
+#ifndef PA_MIXED_RUNS_PER_WAVE
+#define PA_MIXED_RUNS_PER_WAVE 2
+#endif
+// Decode workgroups per chunk workgroup in the dispatch order.
+#ifndef PA_MIXED_DECODE_PER_CHUNK
+#define PA_MIXED_DECODE_PER_CHUNK 7
+#endif
+// Keys per tile of the mixed kernel's chunk workgroups (two buffers).
+#ifndef PA_MIXED_TILE_KEYS
+#define PA_MIXED_TILE_KEYS 32
+#endif
+constexpr int kMixRatio = PA_MIXED_DECODE_PER_CHUNK;
+constexpr int kMixTK = PA_MIXED_TILE_KEYS;
+
+// Prefill chunks and decode tokens in one launch (SwiftLLM page, section
+// 3.3: decode tokens piggybacked on a prefill chunk, so that the chunk's
+// matrix work and the decode's HBM streaming run at the same time).  A
+// workgroup of 4 waves is either a chunk workgroup (tile_body with tiles of
+// kMixTK keys: 128 (token, q-head) rows against one key split of one
+// kv-head) or a decode workgroup whose first wave streams one decode run
+// (stream_mfma_body; the other waves end at once).  Each takes 40 KB of LDS
+// or less, so a CU holds one chunk workgroup next to three decode waves, or
+// four decode waves.  Along each XCD's dispatch order one chunk workgroup
+// comes before every kMixRatio decode workgroups while both remain.  Decode
+// segments find their pages themselves (a walk over the segments with one
+// query token); the merges of both run as launches after this one.
+struct MixedGrid {
+  int ncw;   // chunk workgroups (a multiple of 8, as tile_work numbers them)
+  int ndw;   // decode workgroups (a multiple of 8): one run each
+  int runs;  // decode runs: runs per kv-head x kv-heads
+  int W;     // decode runs per kv-head
+};
+
+template <int G>
+__global__ __launch_bounds__(kTileThreads, 2) void mixed_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool,
+    const int32_t* __restrict__ block_tables, int max_blocks, const int32_t* __restrict__ ctx,
+    const int32_t* __restrict__ cu_q, ChunkList chunks, int RC, int Hkv, int n_items, int num_pages,
+    float scale_log2, float* __restrict__ pre_o, float* __restrict__ pre_lse, uint16_t* __restrict__ out,
+    float* __restrict__ lse_out, int S, int per, int total_pages, int32_t* __restrict__ seq_info,
+    float* __restrict__ part_o, float* __restrict__ part_lse, MixedGrid grid) {
+  using WaveLds = StreamMfmaLds<uint16_t, 128>;
+  using ChunkLds = TileLds<kMixTK, 2>;
+  constexpr size_t kBytes = sizeof(ChunkLds) > sizeof(WaveLds) ? sizeof(ChunkLds) : sizeof(WaveLds);
+  __shared__ __align__(16) unsigned char raw[kBytes];
+  // Workgroup -> kind and index along XCD x's dispatch order: cycles of one
+  // chunk workgroup and kMixRatio decode workgroups while both kinds
+  // remain, then the remaining decode workgroups, then the remaining chunk
+  // workgroups.
+  const int x = blockIdx.x & 7;
+  const int j = blockIdx.x >> 3;
+  const int nc = grid.ncw >> 3, nd = grid.ndw >> 3;
+  const int full = nc < nd / kMixRatio ? nc : nd / kMixRatio;
+  bool chunk;
+  int idx;
+  if (j < (1 + kMixRatio) * full) {
+    const int k = j / (1 + kMixRatio), r = j % (1 + kMixRatio);
+    chunk = r == 0;
+    idx = chunk ? k : k * kMixRatio + r - 1;
+  } else {
+    const int j2 = j - (1 + kMixRatio) * full;
+    const int left_d = nd - kMixRatio * full;
+    chunk = j2 >= left_d;
+    idx = chunk ? full + j2 - left_d : kMixRatio * full + j2;
+  }
+  if (chunk) {
+    TileWork tw;
+    if (!tile_work<G, true>(idx * 8 + x, RC, n_items, Hkv, 0, 0, chunks, ctx, cu_q, nullptr, nullptr, nullptr, tw))
+      return;  // uniform over the workgroup
+    tile_body<G, true, kMixTK, 2>(tw, *reinterpret_cast<ChunkLds*>(raw), q, k_pool, v_pool, block_tables, max_blocks,
+                                  Hkv, num_pages, scale_log2, pre_o, pre_lse);
+  } else {
+    const int r = idx * 8 + x;
+    if (threadIdx.x >= 64 || r >= grid.runs) return;
+    const Fold fold{1, G, __builtin_ctz(G), 0, 1, 0};
+    stream_mfma_body<uint16_t, 128, false>(*reinterpret_cast<WaveLds*>(raw), r % grid.W, r / grid.W, out, lse_out, q,
+                                           k_pool, v_pool, nullptr, nullptr, block_tables, ctx, max_blocks, S, Hkv,
+                                           num_pages, scale_log2, per, total_pages, seq_info, part_o, part_lse,
+                                           nullptr, nullptr, cu_q, 0, fold);
+  }
+}
+
 template <int G>
 int launch_mixed_g(const MixedLaunch& mx) {
   const DecodeLaunch& a = mx.base;
   hipStream_t st = static_cast<hipStream_t>(a.stream);
   char* ws = static_cast<char*>(mx.workspace);
   const MixedLayout& L = mx.layout;
-  int32_t* begin_pages = reinterpret_cast<int32_t*>(ws + L.begin_offset);
   float* pre_o = reinterpret_cast<float*>(ws + L.pre_o_offset);
   float* pre_lse = reinterpret_cast<float*>(ws + L.pre_lse_offset);
   char* sws = ws + L.stream_offset;
-  // The stream kernel's per-sequence records start its workspace.
-  int32_t* seq_info = reinterpret_cast<int32_t*>(sws + partial_layout(1, a.num_seqs, a.num_kv_heads,
-                                                                      stream_rows(a.gqa), a.head_dim).info_offset);
   const float scale_log2 = a.scale * kLog2e;
   const ChunkPlan& plan = *mx.plan;
   auto chunk_list = [&](int b0) {
@@ -697,29 +765,70 @@ int launch_mixed_g(const MixedLaunch& mx) {
     }
     return cl;
   };
-  if (mx.num_chunks > 0) {
+  // One launch for chunks and decode tokens when the decode tokens run on
+  // the matrix-core stream wave (4 or more q-heads per kv-head) and the
+  // chunks fit one chunk list; otherwise the chunk tiles, then the decode
+  // stream, one after the other.
+  const bool one = G >= 4 && mx.decode_pages > 0 && mx.num_chunks <= kMaxChunkSegments;
+  if (one) {
+    const ChunkList cl = chunk_list(0);
+    const int n_items = cl.item_end[cl.n - 1];
+    const int ncw = (n_items + 7) / 8 * 8 * mx.row_chunks;
+    const int cus = device_cu_count();
+    const int64_t target = static_cast<int64_t>(4) * PA_MIXED_RUNS_PER_WAVE * (cus > 0 ? cus : 256);
+    const int64_t per_head = std::max<int64_t>(1, std::min<int64_t>(target, kMaxResidentWaves) / a.num_kv_heads);
+    const int64_t per = std::max<int64_t>(kMinPagesPerWave, (mx.decode_pages + per_head - 1) / per_head);
+    const int64_t W = std::max<int64_t>(1, (mx.decode_pages + per - 1) / per);
+    const PartialLayout pl = partial_layout(W, a.num_seqs, a.num_kv_heads, 16, 128);
+    if (pl.bytes > mx.workspace_bytes - L.stream_offset)
+      return fail(PA_EWORKSPACE, "pa_mixed_chunk: workspace too small for the decode plan");
+    MixedGrid grid;
+    grid.W = static_cast<int>(W);
+    grid.runs = static_cast<int>(W * a.num_kv_heads);
+    grid.ndw = (grid.runs + 7) / 8 * 8;  // one run per workgroup
+    grid.ncw = ncw;
     profile_before(a.stream);
-    for (int b0 = 0; b0 < mx.num_chunks; b0 += kMaxChunkSegments) {
-      const ChunkList cl = chunk_list(b0);
-      const int n_items = cl.item_end[cl.n - 1];
-      const unsigned blocks = static_cast<unsigned>((n_items + 7) / 8 * 8 * mx.row_chunks);
-      hipLaunchKernelGGL((tile_kernel<G, true>), dim3(blocks), dim3(512), 0, st, static_cast<const uint16_t*>(a.q),
-                         static_cast<const uint16_t*>(a.k_pool), static_cast<const uint16_t*>(a.v_pool),
-                         a.block_tables, a.max_blocks, a.context_lens, mx.cu_q_lens, nullptr, nullptr, cl,
-                         a.num_seqs, mx.row_chunks, 0, 0, a.num_kv_heads, n_items,
-                         static_cast<int>(a.num_pages), scale_log2, begin_pages, seq_info, pre_o, pre_lse);
-      if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_mixed_chunk: chunk kernel launch failed");
-    }
+    hipLaunchKernelGGL((mixed_kernel<G>), dim3(static_cast<unsigned>(grid.ncw + grid.ndw)), dim3(kTileThreads), 0,
+                       st, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
+                       static_cast<const uint16_t*>(a.v_pool), a.block_tables, a.max_blocks, a.context_lens,
+                       mx.cu_q_lens, cl, mx.row_chunks, a.num_kv_heads, n_items, static_cast<int>(a.num_pages),
+                       scale_log2, pre_o, pre_lse, static_cast<uint16_t*>(a.out), a.lse_out, a.num_seqs,
+                       static_cast<int>(per), static_cast<int>(mx.decode_pages),
+                       reinterpret_cast<int32_t*>(sws + pl.info_offset), reinterpret_cast<float*>(sws + pl.o_offset),
+                       reinterpret_cast<float*>(sws + pl.lse_offset), grid);
     profile_after(a.stream);
-  }
-  if (mx.decode_pages > 0) {
+    if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_mixed_chunk: mixed kernel launch failed");
     DecodeLaunch dec = a;
     dec.workspace = sws;
     dec.workspace_bytes = mx.workspace_bytes - L.stream_offset;
     dec.total_pages = mx.decode_pages;
-    const int rc = launch_stream(dec, mx.num_chunks > 0 ? begin_pages : nullptr, nullptr, mx.cu_q_lens,
-                                 /*merge=*/true, nullptr);
+    const int rc = launch_stream_merge(dec, mx.cu_q_lens, W);
     if (rc) return rc;
+  } else {
+    if (mx.num_chunks > 0) {
+      profile_before(a.stream);
+      for (int b0 = 0; b0 < mx.num_chunks; b0 += kMaxChunkSegments) {
+        const ChunkList cl = chunk_list(b0);
+        const int n_items = cl.item_end[cl.n - 1];
+        const unsigned blocks = static_cast<unsigned>((n_items + 7) / 8 * 8 * mx.row_chunks);
+        hipLaunchKernelGGL((tile_kernel<G, true>), dim3(blocks), dim3(kTileThreads), 0, st,
+                           static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
+                           static_cast<const uint16_t*>(a.v_pool), a.block_tables, a.max_blocks, a.context_lens,
+                           mx.cu_q_lens, nullptr, nullptr, cl, mx.row_chunks, 0, 0, a.num_kv_heads, n_items,
+                           static_cast<int>(a.num_pages), scale_log2, nullptr, pre_o, pre_lse);
+        if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_mixed_chunk: chunk kernel launch failed");
+      }
+      profile_after(a.stream);
+    }
+    if (mx.decode_pages > 0) {
+      DecodeLaunch dec = a;
+      dec.workspace = sws;
+      dec.workspace_bytes = mx.workspace_bytes - L.stream_offset;
+      dec.total_pages = mx.decode_pages;
+      // (the walk skips the chunks' segments: q_rows is the batch's cu_q_lens)
+      const int rc = launch_stream(dec, nullptr, nullptr, mx.cu_q_lens, /*merge=*/true, nullptr);
+      if (rc) return rc;
+    }
   }
   for (int b0 = 0; b0 < mx.num_chunks; b0 += kMaxChunkSegments) {
     const ChunkList cl = chunk_list(b0);

@@ -104,9 +104,10 @@ def test_mixed_many_chunks(gpu_lib):
 def test_chunked_piggyback_workload(gpu_lib):
     """The full mixed batch: 4 chunks of 512 tokens after prefixes of 0, 1024,
     4096 and 8192 rows, plus 256 decode tokens, in the launch configuration
-    the benchmark times.  Every token against the oracle; the decode rows
-    also bit for bit against pa_decode on the decode segments alone (same
-    kernels, same plan)."""
+    the benchmark times (chunks and decode tokens in one launch).  Every
+    token against the oracle; the decode rows also against pa_decode on the
+    decode segments alone (the one-launch kernel plans its own decode runs,
+    so the split points and the rounding may differ)."""
     lay = workload("chunked_piggyback")
     say("case chunked_piggyback seed 0 (every token)")
     (q, k, v), _ = device_inputs(lay, host_values=False)
@@ -123,8 +124,8 @@ def test_chunked_piggyback_workload(gpu_lib):
     rows = torch.tensor([int(cu[s]) for s in decs], device="cuda")
     bt = torch.from_numpy(lay.block_tables[decs]).cuda()
     dout, dlse = run_decode(gpu_lib, q[rows].contiguous(), k, v, bt, lay.context_lens[decs].copy(), lay.scale, 8)
-    assert torch.equal(out[rows].view(torch.int16), dout.view(torch.int16))
-    assert torch.equal(lse[rows], dlse)
+    assert_close(lay, out_to_f64(out[rows]), out_to_f64(dout), "chunked_piggyback decode rows vs pa_decode")
+    assert (lse[rows] - dlse).abs().max().item() < LSE_TOL
 
 
 def test_mixed_causal_needle(gpu_lib):
