@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--via-mixed", action="store_true",
                     help="multi-token batches (every sequence the same q_len > 1) through pa_mixed_chunk "
                          "instead of pa_decode_multi")
+    ap.add_argument("--hbm-probe", action="store_true",
+                    help="only run the HBM load-path probe (random 4 KB tiles of two pools, LDS DMA against "
+                         "loads into registers, a sweep of waves per CU)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (calibrates HBM traffic counters)")
     return ap.parse_args()
@@ -94,6 +97,39 @@ def copy_probe(nbytes: int) -> None:
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": nbytes, "copies": 3}), flush=True)
+
+
+def hbm_probe() -> None:
+    """The decode kernels' access pattern without their math: every tile of
+    two pools of 150,000 random 4 KB tiles (614 MB each) read once per launch
+    in a random order, 2 or 4 tiles of each pool per batch, the next batch
+    in flight while one is consumed, by LDS DMA (mode 0) or by loads into
+    registers (mode 1), at 1 to 16 waves per CU.  One JSON line per point."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_decode_02_amd", "libpa_probe.so"))
+    lib.hbm_probe_run.restype = ctypes.c_float
+    lib.hbm_probe_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    n = 150_000
+    torch.manual_seed(0)
+    kp = torch.randint(0, 255, (n * 4096,), dtype=torch.uint8, device="cuda")
+    vp = torch.randint(0, 255, (n * 4096,), dtype=torch.uint8, device="cuda")
+    ids = torch.randperm(n, device="cuda").to(torch.int32)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    st = torch.cuda.current_stream().cuda_stream
+    nbytes = 2 * n * 4096
+    for mode in (0, 1):
+        for tpb in (2, 4):
+            for wpc in (1, 2, 3, 4, 5, 6, 8, 12, 16):
+                ms = lib.hbm_probe_run(mode, tpb, kp.data_ptr(), vp.data_ptr(), ids.data_ptr(), n, wpc * cus, 5, st)
+                if ms <= 0:
+                    raise RuntimeError(f"hbm probe failed ({ms})")
+                print(json.dumps({"probe": "hbm", "load_path": ["lds_dma", "registers"][mode], "tiles_per_batch": tpb,
+                                  "waves_per_cu": wpc, "bytes": nbytes, "ms": round(ms, 5),
+                                  "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def visible_pairs(lay, segs):
@@ -239,6 +275,9 @@ def main():
     args = parse()
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.hbm_probe:
+        hbm_probe()
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); this path does not shard across GPUs.",

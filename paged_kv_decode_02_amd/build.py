@@ -79,5 +79,25 @@ def build(verbose: bool = False, defines: tuple = (), out: str = LIB) -> str:
     return out
 
 
+PROBE_SRC = os.path.join(HERE, "probe", "hbm_probe.hip")
+PROBE_LIB = os.path.join(HERE, "libpa_probe.so")
+
+
+def build_probe(out: str = PROBE_LIB) -> str:
+    """The HBM load-path probe (a measurement aid that bench.py --hbm-probe
+    runs; not part of libpa)."""
+    with tempfile.TemporaryDirectory(prefix="pa_probe_") as tmp:
+        tmp_lib = os.path.join(tmp, "libpa_probe.so")
+        cmd = [hipcc(), *HIPCC_FLAGS, "-shared", PROBE_SRC, "-o", tmp_lib]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            noise = "is not a recognized feature for this target"
+            msg = "\n".join(x for x in (r.stdout + r.stderr).splitlines() if noise not in x)
+            raise RuntimeError(f"compiling the HBM probe failed:\n{msg}")
+        shutil.move(tmp_lib, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_probe())

@@ -174,17 +174,22 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
-// First page a sequence's walk covers: begin_pages[s] when given (the
-// pages after a shared prefix); else, in a mixed batch (cu_q = its
-// cumulative query counts), past the end for a segment of more than one
-// query token (a prefill chunk, which the tile kernel attends) and 0 for a
-// decode token; else the page of the first row inside a sliding window of
-// `window` tokens (0 = none).
-__device__ __forceinline__ int walk_begin(const int32_t* __restrict__ begin_pages, const int32_t* __restrict__ cu_q,
-                                          int s, int L, int window) {
-  if (begin_pages) return begin_pages[s];
+// Which pages at the start of each sequence a stream walk skips (all
+// fields optional; the first that is given decides).
+struct PageSkip {
+  const int32_t* begin_pages = nullptr;  // per sequence: the first page to walk (cascade: after the prefix)
+  int window = 0;                        // sliding window in tokens (0 = none)
+};
+
+// First page a sequence's walk covers: begin_pages[s] when given; else, in
+// a mixed batch (cu_q = its cumulative query counts), past the end for a
+// segment of more than one query token (a prefill chunk, which the tile
+// kernel attends) and 0 for a decode token; else the page of the first row
+// inside a sliding window (0 without one).
+__device__ __forceinline__ int walk_begin(const PageSkip& k, const int32_t* __restrict__ cu_q, int s, int L) {
+  if (k.begin_pages) return k.begin_pages[s];
   if (cu_q) return cu_q[s + 1] - cu_q[s] > 1 ? (L + 15) >> 4 : 0;
-  return window > 0 && L > window ? (L - window) >> 4 : 0;
+  return k.window > 0 && L > k.window ? (L - k.window) >> 4 : 0;
 }
 
 // Splits of C pages that sequence s needs over pages [begin, pages).
@@ -207,13 +212,12 @@ struct ItemLoc {
 // sequence; every wave derives the numbering itself from the device copy
 // of the context lengths (one pass over S values, then one over the
 // S/64 values of the lane that holds x), so no plan buffer is needed.
-// `begin_pages` (nullable) gives pages each sequence skips; without it the
-// segments of a mixed batch (cu_q, nullable) or a sliding window of `window`
-// tokens (0 = none) decide them (walk_begin).  `trim` rows
+// `skip` and `cu_q` (nullable) decide the pages each sequence skips
+// (walk_begin).  `trim` rows
 // are taken off the end of every context (a multi-token pass that stops
 // before a sequence's last new tokens).
-__device__ __forceinline__ bool locate_item(const int32_t* __restrict__ ctx, const int32_t* __restrict__ begin_pages,
-                                            const int32_t* __restrict__ cu_q, int window, int S, int max_blocks, int C, int x, ItemLoc& loc,
+__device__ __forceinline__ bool locate_item(const int32_t* __restrict__ ctx, const PageSkip& skip,
+                                            const int32_t* __restrict__ cu_q, int S, int max_blocks, int C, int x, ItemLoc& loc,
                                             int trim = 0) {
   const int lane = lane_id();
   const int per = (S + 63) >> 6;
@@ -225,7 +229,7 @@ __device__ __forceinline__ bool locate_item(const int32_t* __restrict__ ctx, con
     const int s = lane * per + i;
     const int sc = s < S ? s : S - 1;
     const int Lc = ctx[sc] - trim;
-    const int n = nsplit_of(Lc, walk_begin(begin_pages, cu_q, sc, Lc, window), max_blocks, C);
+    const int n = nsplit_of(Lc, walk_begin(skip, cu_q, sc, Lc), max_blocks, C);
     tot += s < S ? n : 0;
   }
   const int incl = wave_inclusive_scan(tot);
@@ -242,7 +246,7 @@ __device__ __forceinline__ bool locate_item(const int32_t* __restrict__ ctx, con
     int ns = 0;
     if (i < per && s < S) {
       const int Ls = ctx[s] - trim;
-      ns = nsplit_of(Ls, walk_begin(begin_pages, cu_q, s, Ls, window), max_blocks, C);
+      ns = nsplit_of(Ls, walk_begin(skip, cu_q, s, Ls), max_blocks, C);
     }
     const int inc2 = wave_inclusive_scan(ns);
     const int ex2 = inc2 - ns;

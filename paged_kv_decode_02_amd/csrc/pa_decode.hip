@@ -96,8 +96,7 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ ctx,
     int max_blocks, int S, int Hkv, int num_pages, float scale_log2, int per, int total_pages,
     int32_t* __restrict__ seq_info, float* __restrict__ part_o, float* __restrict__ part_lse,
-    const int32_t* __restrict__ begin_pages, float* __restrict__ seq_part, const int32_t* __restrict__ q_rows,
-    int window, Fold fold) {
+    PageSkip skip, float* __restrict__ seq_part, const int32_t* __restrict__ q_rows, Fold fold) {
   using Gm = Geom<TKV, D>;
   constexpr int RD = Gm::RD, NCH = Gm::NCH, TILE = Gm::TILE, NI = Gm::NI, RPI = Gm::RPI, EPC = Gm::EPC;
   constexpr bool FP8 = sizeof(TKV) == 1;
@@ -154,7 +153,7 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
   const int pslot = (lane % RPI) * NI + lane / RPI;
 
   // Where the run starts: sequence s0 and its first flattened page.
-  const Walk walk{ctx, begin_pages, q_rows, block_tables, window, S, max_blocks, num_pages, trim, run_b};
+  const Walk walk{ctx, skip, q_rows, block_tables, S, max_blocks, num_pages, trim, run_b};
   Batch first;
   if (!walk.start(run_a, first)) return;
   const int s0 = first.s;
@@ -539,12 +538,11 @@ __global__ __launch_bounds__(64) void stream_mfma_kernel(
     const float* __restrict__ v_scales, const int32_t* __restrict__ block_tables, const int32_t* __restrict__ ctx,
     int max_blocks, int S, int Hkv, int num_pages, float scale_log2, int per, int total_pages,
     int32_t* __restrict__ seq_info, float* __restrict__ part_o, float* __restrict__ part_lse,
-    const int32_t* __restrict__ begin_pages, float* __restrict__ seq_part, const int32_t* __restrict__ q_rows,
-    int window, Fold fold) {
+    PageSkip skip, float* __restrict__ seq_part, const int32_t* __restrict__ q_rows, Fold fold) {
   __shared__ StreamMfmaLds<TKV, D> lds;
   stream_mfma_body<TKV, D, MT>(lds, blockIdx.x, blockIdx.y, out, lse_out, q, k_pool, v_pool, k_scales, v_scales,
                                block_tables, ctx, max_blocks, S, Hkv, num_pages, scale_log2, per, total_pages,
-                               seq_info, part_o, part_lse, begin_pages, seq_part, q_rows, window, fold);
+                               seq_info, part_o, part_lse, skip, seq_part, q_rows, fold);
 }
 
 // Merge the partials of one (sequence, kv-head): the waves w0..w1 that
@@ -709,14 +707,16 @@ int launch_typed(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_p
   float* part_o = reinterpret_cast<float*>(ws + pl.o_offset);
   hipStream_t st = static_cast<hipStream_t>(a.stream);
   const float scale_log2 = a.scale * kLog2e;
+  PageSkip skip;
+  skip.begin_pages = begin_pages;
+  skip.window = begin_pages ? 0 : a.window;
   if (a.timed) profile_before(a.stream);
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(W), a.num_kv_heads), dim3(64), 0, st, static_cast<T*>(a.out),
                      a.lse_out, static_cast<const T*>(a.q), static_cast<const TKV*>(a.k_pool),
                      static_cast<const TKV*>(a.v_pool), a.k_scales, a.v_scales, a.block_tables, a.context_lens,
                      a.max_blocks, a.num_seqs,
                      a.num_kv_heads, static_cast<int>(a.num_pages), scale_log2, static_cast<int>(per),
-                     static_cast<int>(a.total_pages), seq_info, part_o, part_lse, begin_pages, seq_part, q_rows,
-                     begin_pages ? 0 : a.window, fold);
+                     static_cast<int>(a.total_pages), seq_info, part_o, part_lse, skip, seq_part, q_rows, fold);
   if (a.timed) profile_after(a.stream);
   if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_decode: stream kernel launch failed");
   // Unless one wave covers everything, some sequence may be shared; the

@@ -82,22 +82,22 @@ __device__ __forceinline__ void lds_order() {
 // that stops before a sequence's last new tokens).
 struct Walk {
   const int32_t* __restrict__ ctx;
-  const int32_t* __restrict__ begin_pages;
+  PageSkip skip;
   const int32_t* __restrict__ cu_q;  // mixed batch: cumulative query counts (chunks hold no pages of the walk)
   const int32_t* __restrict__ block_tables;
-  int window, S, max_blocks, num_pages, trim, run_b;
+  int S, max_blocks, num_pages, trim, run_b;
 
   __device__ int first_page(int s, int L, int P) const {
-    return min(max(walk_begin(begin_pages, cu_q, s, L, window), 0), P);
+    return min(max(walk_begin(skip, cu_q, s, L), 0), P);
   }
   // First row a sequence's query sees: 0, or the start of the sliding window.
-  __device__ int first_row(int L) const { return window > 0 && L > window ? L - window : 0; }
+  __device__ int first_row(int L) const { return skip.window > 0 && L > skip.window ? L - skip.window : 0; }
 
   // The run's first batch (qb = 0); false if the run holds no page.
   __device__ bool start(int run_a, Batch& b) const {
     ItemLoc loc;
-    // (Cascade suffix: only pages from begin_pages[s] on are laid end to end.)
-    if (!locate_item(ctx, begin_pages, cu_q, window, S, max_blocks, 1, run_a, loc, trim)) return false;
+    // (Cascade suffix: only the pages after each prefix are laid end to end.)
+    if (!locate_item(ctx, skip, cu_q, S, max_blocks, 1, run_a, loc, trim)) return false;
     b.s = __builtin_amdgcn_readfirstlane(loc.s);
     b.L = ctx[b.s] - trim;
     b.P = pages_of_len(b.L, max_blocks);
@@ -223,8 +223,7 @@ __device__ __forceinline__ void stream_mfma_body(
     const float* __restrict__ v_scales, const int32_t* __restrict__ block_tables, const int32_t* __restrict__ ctx,
     int max_blocks, int S, int Hkv, int num_pages, float scale_log2, int per, int total_pages,
     int32_t* __restrict__ seq_info, float* __restrict__ part_o, float* __restrict__ part_lse,
-    const int32_t* __restrict__ begin_pages, float* __restrict__ seq_part, const int32_t* __restrict__ q_rows,
-    int window, Fold fold) {
+    PageSkip skip, float* __restrict__ seq_part, const int32_t* __restrict__ q_rows, Fold fold) {
   using Gm = Geom<TKV, D>;
   constexpr bool FP8 = sizeof(TKV) == 1;
   constexpr int R = 16;  // query rows
@@ -266,7 +265,7 @@ __device__ __forceinline__ void stream_mfma_body(
     koff[r] = row * (RD * 4) + ch * 16;
   }
 
-  const Walk walk{ctx, begin_pages, q_rows, block_tables, window, S, max_blocks, num_pages, trim, run_b};
+  const Walk walk{ctx, skip, q_rows, block_tables, S, max_blocks, num_pages, trim, run_b};
   Batch first;
   if (!walk.start(run_a, first)) return;
   const int s0 = first.s;

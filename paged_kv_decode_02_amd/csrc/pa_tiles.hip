@@ -605,49 +605,6 @@ __global__ __launch_bounds__(64) void cascade_merge_kernel(
   }
 }
 
-template <int G>
-int launch_cascade_g(const CascadeLaunch& c) {
-  const DecodeLaunch& a = c.base;
-  hipStream_t st = static_cast<hipStream_t>(a.stream);
-  char* ws = static_cast<char*>(c.workspace);
-  const CascadeLayout& L = c.layout;
-  int32_t* begin_pages = reinterpret_cast<int32_t*>(ws + L.begin_offset);
-  float* seq_part = reinterpret_cast<float*>(ws + L.seq_part_offset);
-  float* pre_o = reinterpret_cast<float*>(ws + L.pre_o_offset);
-  float* pre_lse = reinterpret_cast<float*>(ws + L.pre_lse_offset);
-  const float scale_log2 = a.scale * kLog2e;
-  profile_before(a.stream);
-  ChunkList none;
-  none.n = 0;
-  const int n_items = c.num_groups * a.num_kv_heads * c.nks;
-  const unsigned blocks = static_cast<unsigned>((n_items + 7) / 8 * 8 * c.row_chunks);
-  hipLaunchKernelGGL((tile_kernel<G, false>), dim3(blocks), dim3(kTileThreads), 0, st, static_cast<const uint16_t*>(a.q),
-                     static_cast<const uint16_t*>(a.k_pool), static_cast<const uint16_t*>(a.v_pool),
-                     a.block_tables, a.max_blocks, a.context_lens, nullptr, c.group_offsets, c.prefix_lens, none,
-                     c.row_chunks, c.nks, c.kps, a.num_kv_heads, n_items, static_cast<int>(a.num_pages), scale_log2,
-                     begin_pages, pre_o, pre_lse);
-  profile_after(a.stream);
-  if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_prefix_cascade: prefix kernel launch failed");
-  // Suffix: the stream decode kernel over the pages after each prefix.
-  DecodeLaunch sfx = a;
-  sfx.workspace = ws + L.stream_offset;
-  sfx.workspace_bytes = c.workspace_bytes - L.stream_offset;
-  sfx.total_pages = c.suffix_pages;
-  sfx.timed = false;
-  StreamPlan plan;
-  int rc = launch_stream(sfx, begin_pages, seq_part, nullptr, /*merge=*/false, &plan);
-  if (rc) return rc;
-  char* sws = static_cast<char*>(sfx.workspace);
-  hipLaunchKernelGGL((cascade_merge_kernel<uint16_t, 128, G>), dim3(a.num_seqs, a.num_kv_heads), dim3(64), 0, st,
-                     static_cast<uint16_t*>(a.out), a.lse_out, a.num_seqs, a.num_kv_heads,
-                     static_cast<int>(plan.waves), c.nks, c.kps, begin_pages, pre_o, pre_lse, seq_part,
-                     reinterpret_cast<const int32_t*>(sws + plan.layout.info_offset),
-                     reinterpret_cast<const float*>(sws + plan.layout.o_offset),
-                     reinterpret_cast<const float*>(sws + plan.layout.lse_offset), plan.rows);
-  if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_prefix_cascade: merge kernel launch failed");
-  return PA_OK;
-}
-
 // Decode runs of the one-launch mixed kernel: the runs of a plain decode
 // launch (4 matrix-core stream waves per CU) times PA_MIXED_RUNS_PER_WAVE.
 #ifndef PA_MIXED_RUNS_PER_WAVE
@@ -664,33 +621,42 @@ int launch_cascade_g(const CascadeLaunch& c) {
 constexpr int kMixRatio = PA_MIXED_DECODE_PER_CHUNK;
 constexpr int kMixTK = PA_MIXED_TILE_KEYS;
 
-// Prefill chunks and decode tokens in one launch (SwiftLLM page, section
-// 3.3: decode tokens piggybacked on a prefill chunk, so that the chunk's
-// matrix work and the decode's HBM streaming run at the same time).  A
-// workgroup of 4 waves is either a chunk workgroup (tile_body with tiles of
-// kMixTK keys: 128 (token, q-head) rows against one key split of one
-// kv-head) or a decode workgroup whose first wave streams one decode run
+// Prefill chunks and decode tokens of a mixed batch in one launch (SwiftLLM
+// page, section 3.3: decode tokens piggybacked on a prefill chunk, so that
+// the chunk's matrix work and the decode's HBM streaming run at the same
+// time).  A workgroup of 4 waves is either a chunk workgroup (tile_body with
+// tiles of kMixTK keys: 128 (token, q-head) rows against one key split of
+// one kv-head) or a decode workgroup whose first wave streams one decode run
 // (stream_mfma_body; the other waves end at once).  Each takes 40 KB of LDS
-// or less, so a CU holds one chunk workgroup next to three decode waves, or
-// four decode waves.  Along each XCD's dispatch order one chunk workgroup
-// comes before every kMixRatio decode workgroups while both remain.  Decode
-// segments find their pages themselves (a walk over the segments with one
-// query token); the merges of both run as launches after this one.
-struct MixedGrid {
+// or less.  Along each XCD's dispatch order one chunk workgroup comes before
+// every kMixRatio decode workgroups while both kinds remain.  Decode segments
+// find their pages themselves (a walk over the segments with one query
+// token, cu_q); the merges of both run as launches after this one.
+// (The same pairing for a cascade's prefix tiles and suffix stream measured
+// slower than the two launches: 313 against 304 us on the shared-prefix
+// batch, whose prefix work is small next to its suffix stream.)
+struct PairGrid {
   int ncw;   // chunk workgroups (a multiple of 8, as tile_work numbers them)
   int ndw;   // decode workgroups (a multiple of 8): one run each
   int runs;  // decode runs: runs per kv-head x kv-heads
   int W;     // decode runs per kv-head
 };
 
+// Chunk-side arguments.
+struct PairTiles {
+  int RC, n_items;
+  const int32_t* cu_q;  // the batch's cumulative query counts
+  float* pre_o;
+  float* pre_lse;
+};
+
 template <int G>
 __global__ __launch_bounds__(kTileThreads, 2) void mixed_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool,
-    const int32_t* __restrict__ block_tables, int max_blocks, const int32_t* __restrict__ ctx,
-    const int32_t* __restrict__ cu_q, ChunkList chunks, int RC, int Hkv, int n_items, int num_pages,
-    float scale_log2, float* __restrict__ pre_o, float* __restrict__ pre_lse, uint16_t* __restrict__ out,
+    const int32_t* __restrict__ block_tables, int max_blocks, const int32_t* __restrict__ ctx, ChunkList chunks,
+    PairTiles tiles, int Hkv, int num_pages, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse_out, int S, int per, int total_pages, int32_t* __restrict__ seq_info,
-    float* __restrict__ part_o, float* __restrict__ part_lse, MixedGrid grid) {
+    float* __restrict__ part_o, float* __restrict__ part_lse, PairGrid grid) {
   using WaveLds = StreamMfmaLds<uint16_t, 128>;
   using ChunkLds = TileLds<kMixTK, 2>;
   constexpr size_t kBytes = sizeof(ChunkLds) > sizeof(WaveLds) ? sizeof(ChunkLds) : sizeof(WaveLds);
@@ -717,10 +683,11 @@ __global__ __launch_bounds__(kTileThreads, 2) void mixed_kernel(
   }
   if (chunk) {
     TileWork tw;
-    if (!tile_work<G, true>(idx * 8 + x, RC, n_items, Hkv, 0, 0, chunks, ctx, cu_q, nullptr, nullptr, nullptr, tw))
+    if (!tile_work<G, true>(idx * 8 + x, tiles.RC, tiles.n_items, Hkv, 0, 0, chunks, ctx, tiles.cu_q, nullptr,
+                            nullptr, nullptr, tw))
       return;  // uniform over the workgroup
     tile_body<G, true, kMixTK, 2>(tw, *reinterpret_cast<ChunkLds*>(raw), q, k_pool, v_pool, block_tables, max_blocks,
-                                  Hkv, num_pages, scale_log2, pre_o, pre_lse);
+                                  Hkv, num_pages, scale_log2, tiles.pre_o, tiles.pre_lse);
   } else {
     const int r = idx * 8 + x;
     if (threadIdx.x >= 64 || r >= grid.runs) return;
@@ -728,8 +695,65 @@ __global__ __launch_bounds__(kTileThreads, 2) void mixed_kernel(
     stream_mfma_body<uint16_t, 128, false>(*reinterpret_cast<WaveLds*>(raw), r % grid.W, r / grid.W, out, lse_out, q,
                                            k_pool, v_pool, nullptr, nullptr, block_tables, ctx, max_blocks, S, Hkv,
                                            num_pages, scale_log2, per, total_pages, seq_info, part_o, part_lse,
-                                           nullptr, nullptr, cu_q, 0, fold);
+                                           PageSkip{}, nullptr, tiles.cu_q, fold);
   }
+}
+
+// Decode runs of a mixed launch over `pages` pages per kv-head.
+struct PairPlan {
+  int64_t per, W;
+};
+PairPlan pair_plan(int64_t pages, int32_t num_kv_heads) {
+  const int cus = device_cu_count();
+  const int64_t target = static_cast<int64_t>(4) * PA_MIXED_RUNS_PER_WAVE * (cus > 0 ? cus : 256);
+  const int64_t per_head = std::max<int64_t>(1, std::min<int64_t>(target, kMaxResidentWaves) / num_kv_heads);
+  PairPlan p;
+  p.per = std::max<int64_t>(kMinPagesPerWave, (pages + per_head - 1) / per_head);
+  p.W = std::max<int64_t>(1, (pages + p.per - 1) / p.per);
+  return p;
+}
+
+template <int G>
+int launch_cascade_g(const CascadeLaunch& c) {
+  const DecodeLaunch& a = c.base;
+  hipStream_t st = static_cast<hipStream_t>(a.stream);
+  char* ws = static_cast<char*>(c.workspace);
+  const CascadeLayout& L = c.layout;
+  int32_t* begin_pages = reinterpret_cast<int32_t*>(ws + L.begin_offset);
+  float* seq_part = reinterpret_cast<float*>(ws + L.seq_part_offset);
+  float* pre_o = reinterpret_cast<float*>(ws + L.pre_o_offset);
+  float* pre_lse = reinterpret_cast<float*>(ws + L.pre_lse_offset);
+  const float scale_log2 = a.scale * kLog2e;
+  ChunkList none;
+  none.n = 0;
+  const int n_items = c.num_groups * a.num_kv_heads * c.nks;
+  profile_before(a.stream);
+  const unsigned blocks = static_cast<unsigned>((n_items + 7) / 8 * 8 * c.row_chunks);
+  hipLaunchKernelGGL((tile_kernel<G, false>), dim3(blocks), dim3(kTileThreads), 0, st, static_cast<const uint16_t*>(a.q),
+                     static_cast<const uint16_t*>(a.k_pool), static_cast<const uint16_t*>(a.v_pool),
+                     a.block_tables, a.max_blocks, a.context_lens, nullptr, c.group_offsets, c.prefix_lens, none,
+                     c.row_chunks, c.nks, c.kps, a.num_kv_heads, n_items, static_cast<int>(a.num_pages), scale_log2,
+                     begin_pages, pre_o, pre_lse);
+  profile_after(a.stream);
+  if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_prefix_cascade: prefix kernel launch failed");
+  // Suffix: the stream decode kernel over the pages after each prefix.
+  DecodeLaunch sfx = a;
+  sfx.workspace = ws + L.stream_offset;
+  sfx.workspace_bytes = c.workspace_bytes - L.stream_offset;
+  sfx.total_pages = c.suffix_pages;
+  sfx.timed = false;
+  StreamPlan plan;
+  int rc = launch_stream(sfx, begin_pages, seq_part, nullptr, /*merge=*/false, &plan);
+  if (rc) return rc;
+  char* sws = static_cast<char*>(sfx.workspace);
+  hipLaunchKernelGGL((cascade_merge_kernel<uint16_t, 128, G>), dim3(a.num_seqs, a.num_kv_heads), dim3(64), 0, st,
+                     static_cast<uint16_t*>(a.out), a.lse_out, a.num_seqs, a.num_kv_heads,
+                     static_cast<int>(plan.waves), c.nks, c.kps, begin_pages, pre_o, pre_lse, seq_part,
+                     reinterpret_cast<const int32_t*>(sws + plan.layout.info_offset),
+                     reinterpret_cast<const float*>(sws + plan.layout.o_offset),
+                     reinterpret_cast<const float*>(sws + plan.layout.lse_offset), plan.rows);
+  if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_prefix_cascade: merge kernel launch failed");
+  return PA_OK;
 }
 
 template <int G>
@@ -773,27 +797,27 @@ int launch_mixed_g(const MixedLaunch& mx) {
   if (one) {
     const ChunkList cl = chunk_list(0);
     const int n_items = cl.item_end[cl.n - 1];
-    const int ncw = (n_items + 7) / 8 * 8 * mx.row_chunks;
-    const int cus = device_cu_count();
-    const int64_t target = static_cast<int64_t>(4) * PA_MIXED_RUNS_PER_WAVE * (cus > 0 ? cus : 256);
-    const int64_t per_head = std::max<int64_t>(1, std::min<int64_t>(target, kMaxResidentWaves) / a.num_kv_heads);
-    const int64_t per = std::max<int64_t>(kMinPagesPerWave, (mx.decode_pages + per_head - 1) / per_head);
-    const int64_t W = std::max<int64_t>(1, (mx.decode_pages + per - 1) / per);
-    const PartialLayout pl = partial_layout(W, a.num_seqs, a.num_kv_heads, 16, 128);
+    const PairPlan pp = pair_plan(mx.decode_pages, a.num_kv_heads);
+    const PartialLayout pl = partial_layout(pp.W, a.num_seqs, a.num_kv_heads, 16, 128);
     if (pl.bytes > mx.workspace_bytes - L.stream_offset)
       return fail(PA_EWORKSPACE, "pa_mixed_chunk: workspace too small for the decode plan");
-    MixedGrid grid;
-    grid.W = static_cast<int>(W);
-    grid.runs = static_cast<int>(W * a.num_kv_heads);
+    PairGrid grid;
+    grid.W = static_cast<int>(pp.W);
+    grid.runs = static_cast<int>(pp.W * a.num_kv_heads);
     grid.ndw = (grid.runs + 7) / 8 * 8;  // one run per workgroup
-    grid.ncw = ncw;
+    grid.ncw = (n_items + 7) / 8 * 8 * mx.row_chunks;
+    PairTiles tiles{};
+    tiles.RC = mx.row_chunks;
+    tiles.n_items = n_items;
+    tiles.cu_q = mx.cu_q_lens;
+    tiles.pre_o = pre_o;
+    tiles.pre_lse = pre_lse;
     profile_before(a.stream);
-    hipLaunchKernelGGL((mixed_kernel<G>), dim3(static_cast<unsigned>(grid.ncw + grid.ndw)), dim3(kTileThreads), 0,
-                       st, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
-                       static_cast<const uint16_t*>(a.v_pool), a.block_tables, a.max_blocks, a.context_lens,
-                       mx.cu_q_lens, cl, mx.row_chunks, a.num_kv_heads, n_items, static_cast<int>(a.num_pages),
-                       scale_log2, pre_o, pre_lse, static_cast<uint16_t*>(a.out), a.lse_out, a.num_seqs,
-                       static_cast<int>(per), static_cast<int>(mx.decode_pages),
+    hipLaunchKernelGGL((mixed_kernel<G>), dim3(static_cast<unsigned>(grid.ncw + grid.ndw)), dim3(kTileThreads),
+                       0, st, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
+                       static_cast<const uint16_t*>(a.v_pool), a.block_tables, a.max_blocks, a.context_lens, cl, tiles,
+                       a.num_kv_heads, static_cast<int>(a.num_pages), scale_log2, static_cast<uint16_t*>(a.out),
+                       a.lse_out, a.num_seqs, static_cast<int>(pp.per), static_cast<int>(mx.decode_pages),
                        reinterpret_cast<int32_t*>(sws + pl.info_offset), reinterpret_cast<float*>(sws + pl.o_offset),
                        reinterpret_cast<float*>(sws + pl.lse_offset), grid);
     profile_after(a.stream);
@@ -802,7 +826,7 @@ int launch_mixed_g(const MixedLaunch& mx) {
     dec.workspace = sws;
     dec.workspace_bytes = mx.workspace_bytes - L.stream_offset;
     dec.total_pages = mx.decode_pages;
-    const int rc = launch_stream_merge(dec, mx.cu_q_lens, W);
+    const int rc = launch_stream_merge(dec, mx.cu_q_lens, pp.W);
     if (rc) return rc;
   } else {
     if (mx.num_chunks > 0) {
