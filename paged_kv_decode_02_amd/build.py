@@ -79,6 +79,28 @@ def build(verbose: bool = False, defines: tuple = (), out: str = LIB) -> str:
     return out
 
 
+HOST_SOURCES = ["pa_host.cpp", "pa_api.cpp", "pa_host_stub.cpp"]
+
+
+def build_host_sanitized(out: str) -> str:
+    """The host code alone (validation, planning, prefix detection; the
+    launches replaced by stand-ins that report no device), compiled by g++
+    with AddressSanitizer and UndefinedBehaviorSanitizer: a CPU-only library
+    with libpa's C ABI for the ABI and host-planner tests.  Load it with the
+    ASan runtime preloaded (tests/test_host_sanitized.py does)."""
+    gxx = shutil.which("g++")
+    if not gxx:
+        raise RuntimeError("g++ not found")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-Wall", "-Wextra", "-Werror",
+           "-Wno-unused-parameter", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           *[os.path.join(CSRC, f) for f in HOST_SOURCES], "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitizer build of the host code failed:\n{r.stdout}{r.stderr}")
+    return out
+
+
 PROBE_SRC = os.path.join(HERE, "probe", "hbm_probe.hip")
 PROBE_LIB = os.path.join(HERE, "libpa_probe.so")
 

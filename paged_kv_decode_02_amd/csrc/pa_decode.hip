@@ -803,18 +803,6 @@ int device_cu_count() {
   return v;
 }
 
-bool decode_fp8_supported(int32_t head_dim, int32_t gqa) {
-  return head_dim == 128 && (gqa == 1 || gqa == 2 || gqa == 4 || gqa == 8 || gqa == 16);
-}
-
-bool decode_supported(pa_dtype dtype, int32_t head_dim, int32_t gqa) {
-  const bool g_ok = gqa == 1 || gqa == 2 || gqa == 4 || gqa == 8 || gqa == 16;
-  if (!g_ok) return false;
-  if (dtype == PA_BF16) return head_dim == 64 || head_dim == 128;
-  if (dtype == PA_F32) return head_dim == 64;
-  return false;
-}
-
 int launch_stream(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_part, const int32_t* q_rows, bool merge,
                   StreamPlan* plan) {
   if (a.kv_fp8) {

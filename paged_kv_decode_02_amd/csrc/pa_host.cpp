@@ -33,6 +33,25 @@ PartialLayout partial_layout(int64_t waves, int64_t num_seqs, int32_t num_kv_hea
   return l;
 }
 
+// Shapes the kernels are built for.
+bool decode_fp8_supported(int32_t head_dim, int32_t gqa) {
+  return head_dim == 128 && (gqa == 1 || gqa == 2 || gqa == 4 || gqa == 8 || gqa == 16);
+}
+
+bool decode_supported(pa_dtype dtype, int32_t head_dim, int32_t gqa) {
+  const bool g_ok = gqa == 1 || gqa == 2 || gqa == 4 || gqa == 8 || gqa == 16;
+  if (!g_ok) return false;
+  if (dtype == PA_BF16) return head_dim == 64 || head_dim == 128;
+  if (dtype == PA_F32) return head_dim == 64;
+  return false;
+}
+
+bool cascade_supported(pa_dtype dtype, int32_t head_dim, int32_t gqa) {
+  return dtype == PA_BF16 && head_dim == 128 && (gqa == 1 || gqa == 2 || gqa == 4 || gqa == 8 || gqa == 16);
+}
+
+bool mixed_supported(pa_dtype dtype, int32_t head_dim, int32_t gqa) { return cascade_supported(dtype, head_dim, gqa); }
+
 int64_t max_waves_per_head(int64_t total_pages, int32_t num_kv_heads, int32_t split_pages) {
   if (split_pages > 0) return (total_pages + split_pages - 1) / split_pages;
   const int64_t by_gpu = (kMaxResidentWaves + num_kv_heads - 1) / num_kv_heads;

@@ -866,8 +866,6 @@ int launch_mixed_g(const MixedLaunch& mx) {
 
 }  // namespace
 
-bool mixed_supported(pa_dtype dtype, int32_t head_dim, int32_t gqa) { return cascade_supported(dtype, head_dim, gqa); }
-
 int launch_mixed(const MixedLaunch& m) {
   if (m.num_chunks == 0) {
     DecodeLaunch dec = m.base;
@@ -884,10 +882,6 @@ int launch_mixed(const MixedLaunch& m) {
     case 16: return launch_mixed_g<16>(m);
   }
   return fail(PA_EUNSUPPORTED, "pa_mixed_chunk: gqa_ratio not built");
-}
-
-bool cascade_supported(pa_dtype dtype, int32_t head_dim, int32_t gqa) {
-  return dtype == PA_BF16 && head_dim == 128 && (gqa == 1 || gqa == 2 || gqa == 4 || gqa == 8 || gqa == 16);
 }
 
 int launch_cascade(const CascadeLaunch& c) {

@@ -16,7 +16,9 @@ from typing import Optional
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libpa.so")
+# PA_LIB names another build of the same C ABI (the host-only sanitizer
+# build in the CPU tests); by default the in-tree libpa.so.
+LIB_PATH = os.environ.get("PA_LIB") or os.path.join(HERE, "libpa.so")
 
 PA_F32 = 0
 PA_BF16 = 1
