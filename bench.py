@@ -55,8 +55,11 @@ def parse():
     return ap.parse_args()
 
 
-KERNEL_SOURCES = ["paged_kv_decode_02_amd/csrc/pa_decode.hip", "paged_kv_decode_02_amd/csrc/pa_common.h"]
+KERNEL_SOURCES = ["paged_kv_decode_02_amd/csrc/pa_decode.hip", "paged_kv_decode_02_amd/csrc/pa_stream.h",
+                  "paged_kv_decode_02_amd/csrc/pa_common.h"]
 APPEND_SOURCES = ["paged_kv_decode_02_amd/csrc/pa_append.hip", "paged_kv_decode_02_amd/csrc/pa_common.h"]
+TILE_SOURCES = ["paged_kv_decode_02_amd/csrc/pa_tiles.hip", "paged_kv_decode_02_amd/csrc/pa_stream.h",
+                "paged_kv_decode_02_amd/csrc/pa_common.h"]
 
 
 def source_digest(sources) -> str:
@@ -443,12 +446,12 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / roofline.HBM_PEAK_GBS, 4), "kernel_ms": round(ms, 5),
                 "traffic": traffic}
 
-    def mfma_roof(kernel, flops, ms):
+    def mfma_roof(kernel, flops, ms, traffic=None):
         tflops = flops / (ms * 1e-3) / 1e12
         return {"bound": "mfma", "kernel": kernel, "achieved": round(tflops, 1),
                 "peak": roofline.MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tflops / roofline.MFMA_BF16_PEAK_TFLOPS, 4), "kernel_ms": round(ms, 5),
-                "traffic": None}
+                "traffic": traffic}
 
     def stream_kernel(rows):
         # waves of 4 or more bf16 query rows (bf16 or fp8 pools) run on the
@@ -460,7 +463,8 @@ def main():
         nb = roofline.cascade_bytes(lay.context_lens, lay.group_seq_offsets, lay.prefix_lens, lay.num_q_heads,
                                     lay.num_kv_heads, D, lay.elem_bytes)
         flops = roofline.prefix_flops(lay.group_seq_offsets, lay.prefix_lens, lay.num_q_heads, D)
-        roof = mfma_roof("tile_kernel (shared prefix)", flops, kern_avg[0])
+        roof = mfma_roof("tile_kernel (shared prefix)", flops, kern_avg[0],
+                         measured_traffic("tile:" + args.workload, TILE_SOURCES))
         # the same batch through plain decode, for the cascade's speed-up
         dws = torch.empty(pa.decode_workspace_size(S, lay.num_kv_heads, lay.gqa_ratio, D, total_pages, 0),
                           dtype=torch.uint8, device=dev)
@@ -494,9 +498,10 @@ def main():
             # chunks and decode tokens in one launch (mixed_kernel): its HBM
             # view (all K/V bytes of the step) and its matrix view (the chunk
             # flops) over the same kernel time
+            traffic = measured_traffic("mixed:" + args.workload, TILE_SOURCES)
             roof = hbm_roof("mixed_kernel (prefill chunks + decode tokens, one launch)", nb["total"], kern_avg[0],
-                            None)
-            extra["mixed_kernel_mfma"] = mfma_roof("mixed_kernel (chunk flops)", flops, kern_avg[0])
+                            traffic)
+            extra["mixed_kernel_mfma"] = mfma_roof("mixed_kernel (chunk flops)", flops, kern_avg[0], traffic)
         elif has_dec:
             dec = lay.q_lens == 1
             dbytes = roofline.decode_bytes(lay.context_lens[dec], lay.num_q_heads, lay.num_kv_heads, D,
