@@ -8,7 +8,7 @@
 // product.  Attention over prefix + suffix is then the log-sum-exp merge of
 // attention over each part.  Three launches on the caller's stream:
 //  1. tile_kernel<G, false> (MFMA): per (group, row block, key split,
-//     kv-head) a workgroup of 8 waves takes up to 128 query rows --
+//     kv-head) a workgroup of 4 waves takes up to 128 query rows --
 //     (member, q-head) pairs of the kv-head, folded into one tile dimension
 //     the way TokenSpeed's fold_sq_factor folds query tokens (TokenSpeed
 //     deep-dive section 7.2) -- against one split of the prefix keys,
@@ -24,12 +24,17 @@
 // Mixed batch (SARATHI-style piggybacking of decode tokens on prefill
 // chunks, SwiftLLM page section 3.3; chunked prefill, TokenSpeed deep-dive
 // section 5.1): prefill chunks (n > 1 new tokens, causal inside the chunk)
-// and decode tokens in one call.
-//  1. tile_kernel<G, true>: per (chunk, row block, key split, kv-head) the
-//     chunk's (token, q-head) rows against its own keys, causal mask by
-//     select; marks the chunks as "no decode pages" for step 2.
-//  2. The stream kernel (+ its merge) over the decode segments.
-//  3. chunk_merge_kernel: per (chunk token, kv-head), the key splits.
+// and decode tokens in one call.  With 4 or more q-heads per kv-head and
+// decode tokens present, one launch:
+//  1. mixed_kernel<G>: chunk workgroups (the tile body on one (chunk, row
+//     block, key split, kv-head), causal mask by select) and decode
+//     workgroups (the matrix-core stream wave on one run of decode pages)
+//     interleaved along each XCD's dispatch order, so the matrix-bound and
+//     the HBM-bound work share the CUs for the whole launch.
+//  2. The decode merge, then chunk_merge_kernel: per (chunk token, kv-head),
+//     the key splits.
+// Otherwise tile_kernel<G, true> for the chunks, then the stream kernel
+// (+ its merge) over the decode segments, then chunk_merge_kernel.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -290,9 +295,26 @@ __device__ __forceinline__ void tile_body(const TileWork& tw, TileLds<KT, NB>& l
       }
     }
   };
+  // A whole tile: all of this wave's loads fall in one page (loads 4 wv ..
+  // of 64 keys, or 2 wv .. of 32, cover keys 16 page ..), so its id is read
+  // from LDS once for the K and the V loads.  (Read per load, behind each
+  // DMA's memory clobber, it cost an LDS round trip per load.)
+  static_assert(4 % LPW == 0, "a wave's loads of a tile stay in one page");
   auto issue_tile = [&](int t, int b) {
-    issue_half(t, kbytes, lds.k[b]);
-    issue_half(t, vbytes, lds.v[b]);
+    if (k_hi - (k_lo + t * KT) >= KT) {
+      const int32_t* pw = &lds.pid[(t / TPW) & 1][(t * NKB) % kPidWindow];
+      const int pid = min(max(__builtin_amdgcn_readfirstlane(pw[(wv * LPW) >> 2]), 0), num_pages - 1);
+      const int64_t base = (static_cast<int64_t>(pid) * Hkv + kvh) * TILE;
+#pragma unroll
+      for (int i = 0; i < LPW; ++i)
+        dma16_sbase(kbytes + base, dma_off[i], lds_offset(lds.k[b] + (wv * LPW + i) * 64));
+#pragma unroll
+      for (int i = 0; i < LPW; ++i)
+        dma16_sbase(vbytes + base, dma_off[i], lds_offset(lds.v[b] + (wv * LPW + i) * 64));
+    } else {
+      issue_half(t, kbytes, lds.k[b]);
+      issue_half(t, vbytes, lds.v[b]);
+    }
   };
   // Per-lane row and chunk of the transposed V reads: lane (group lg, j)
   // reads row key0 + j/4, columns d0 + 4(j%4) .. +3, with key0 = 32 ks + 4 lg
