@@ -594,36 +594,50 @@ __global__ __launch_bounds__(64) void cascade_merge_kernel(
     if (!shared) return seq_part + (static_cast<int64_t>(s) * Hq + kvh * G + h) * D;
     return part_o + (((static_cast<int64_t>(w0 + k) * Hkv + kvh) * 2 + (k == 0 ? slot0 : 0)) * PR + h) * D;
   };
-#pragma unroll 1
-  for (int h = 0; h < G; ++h) {
-    float M = -INFINITY;
-    for (int j = lane; j < n; j += 64) M = fmaxf(M, lse_at(j, h));
-    M = wave_max(M);
-    float acc[EPL];
+  // All G heads at once: their log-sum-exp loads, then their output loads,
+  // go out together (one head after another put two dependent load round
+  // trips per head on each workgroup's path).
+  float M[G];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-    float wsum = 0.f;
-    for (int j = 0; j < n; ++j) {
-      const float a = fast_exp2(lse_at(j, h) - M);
-      wsum += a;
+  for (int h = 0; h < G; ++h) {
+    M[h] = -INFINITY;
+    for (int j = lane; j < n; j += 64) M[h] = fmaxf(M[h], lse_at(j, h));
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) M[h] = wave_max(M[h]);
+  float acc[G][EPL];
+  float wsum[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    wsum[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
+  for (int j = 0; j < n; ++j) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float a = fast_exp2(lse_at(j, h) - M[h]);
+      wsum[h] += a;
       const float* src = o_at(j, h) + lane * EPL;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(a, src[e], acc[e]);
+      for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(a, src[e], acc[h][e]);
     }
-    const float inv = 1.0f / wsum;
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float inv = 1.0f / wsum[h];
     const int64_t row = static_cast<int64_t>(s) * Hq + kvh * G + h;
     if constexpr (sizeof(T) == 2) {
       if constexpr (EPL == 2) {
-        reinterpret_cast<uint32_t*>(out)[row * (D / 2) + lane] =
-            bf16x2_rne(acc[0] * inv, acc[1] * inv);
+        reinterpret_cast<uint32_t*>(out)[row * (D / 2) + lane] = bf16x2_rne(acc[h][0] * inv, acc[h][1] * inv);
       } else {
-        reinterpret_cast<uint16_t*>(out)[row * D + lane] = static_cast<uint16_t>(bf16_bits_rne(acc[0] * inv));
+        reinterpret_cast<uint16_t*>(out)[row * D + lane] = static_cast<uint16_t>(bf16_bits_rne(acc[h][0] * inv));
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) reinterpret_cast<float*>(out)[row * D + lane * EPL + e] = acc[e] * inv;
+      for (int e = 0; e < EPL; ++e) reinterpret_cast<float*>(out)[row * D + lane * EPL + e] = acc[h][e] * inv;
     }
-    if (lse_out && lane == 0) lse_out[row] = (M + fast_log2(wsum)) * kLn2;
+    if (lse_out && lane == 0) lse_out[row] = (M[h] + fast_log2(wsum[h])) * kLn2;
   }
 }
 
