@@ -19,6 +19,7 @@ from .attention import (  # noqa: F401
     lse_merge,
     paged_attention,
     decode,
+    decode_multi_window,
     decode_window,
     prefix_cascade,
     mixed_chunk,

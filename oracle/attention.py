@@ -217,6 +217,54 @@ def decode_window(q, k_pool, v_pool, block_tables, context_lens, window, scale, 
     return out, lse
 
 
+def decode_multi_window(q, k_pool, v_pool, block_tables, context_lens, q_len, window, scale, num_kv_heads,
+                        block_size, dtype, seqs=None):
+    """Multi-token decode over a sliding-window cache: sequence s brings its
+    last ``q_len`` rows as new tokens; token i sits at position
+    ``p = L - q_len + i`` and sees the rows ``[max(0, p + 1 - window), p]``:
+    the causal rule of a multi-token step (each token sees the rows up to its
+    own position; TokenSpeed deep-dive section 7.2 folds such tokens into
+    one tile) with each token's own window of ``window`` tokens (TokenSpeed
+    deep-dive section 4.1, ``sliding_window_tokens``).
+
+    Token i of sequence s is row ``s * q_len + i`` of ``q`` / ``out``.
+    Table entries before the earliest token's window,
+    ``(L - q_len + 1 - window) // block_size``, may be placeholders
+    (tokenspeed 딥다이브 section 6-3) and are never looked up.
+    """
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    n = int(q_len)
+    W = int(window)
+    T, Hq, D = q.shape
+    if n < 1 or T != len(ctx) * n:
+        raise ValueError("q must hold q_len tokens per sequence")
+    if W < 1:
+        raise ValueError("window must be >= 1")
+    G = Hq // num_kv_heads
+    sc = float(np.float32(scale))
+    out = np.full((T, Hq, D), np.nan, dtype=np.float64)
+    lse = np.full((T, Hq), np.nan, dtype=np.float64)
+    for s in (range(len(ctx)) if seqs is None else seqs):
+        L = int(ctx[s])
+        if L < n:
+            raise ValueError(f"sequence {s}: context shorter than q_len")
+        lo0 = max(0, L - n + 1 - W)  # the earliest row any of the tokens sees
+        t = np.arange(lo0, L)
+        pages = np.asarray(block_tables[s])[t // block_size]
+        if pages.min() < 0 or pages.max() >= k_pool.shape[0]:
+            raise IndexError("block table names a page outside the pool")
+        qs = stored_to_f64(q[s * n : (s + 1) * n], dtype)  # [n, Hq, D]
+        for g in range(num_kv_heads):
+            K = stored_to_f64(k_pool[pages, g, t % block_size, :], dtype)
+            V = stored_to_f64(v_pool[pages, g, t % block_size, :], dtype)
+            for i in range(n):
+                p = L - n + i
+                a, b = max(0, p + 1 - W) - lo0, p + 1 - lo0  # rows [a, b) of K, V
+                for h in range(g * G, (g + 1) * G):
+                    out[s * n + i, h], lse[s * n + i, h] = attend(qs[i, h], K[a:b], V[a:b], sc)
+    return out, lse
+
+
 def check_block_tables(
     block_tables,
     context_lens,

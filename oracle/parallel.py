@@ -9,7 +9,7 @@ kv-head's G q-heads (and all of the sequence's query tokens) over that
 sequence's rows, which is independent of every other unit (q-head h reads
 kv-head h // G only).  Each unit is computed by the oracle's own functions
 (``attention.paged_attention``, ``attention.decode_window``,
-``fp8.decode_multi_fp8``) on a one-kv-head copy of the sequence's pages with
+``attention.decode_multi_window``, ``fp8.decode_multi_fp8``) on a one-kv-head copy of the sequence's pages with
 its table relabelled 0..n-1 -- a page relabelling, which the oracle's pins
 show leaves the result bit-identical.  Nothing here computes attention
 itself.
@@ -88,11 +88,16 @@ def _unit(task):
     P = task["k"].shape[0]
     bt = np.arange(P, dtype=np.int32)[None, :]
     if kind == "window":
-        # entries before the window's first page are never read; name page 0
+        # entries before the (earliest token's) window's first page are
+        # never read; name page 0
         first = task["first_page"]
         bt = np.concatenate([np.zeros(first, np.int32), np.arange(P, dtype=np.int32)])[None, :]
-        out, lse = attention.decode_window(task["q"], task["k"], task["v"], bt, np.array([L]), task["window"],
-                                           task["scale"], 1, 16, task["dtype"])
+        if n == 1:
+            out, lse = attention.decode_window(task["q"], task["k"], task["v"], bt, np.array([L]), task["window"],
+                                               task["scale"], 1, 16, task["dtype"])
+        else:
+            out, lse = attention.decode_multi_window(task["q"], task["k"], task["v"], bt, np.array([L]), n,
+                                                     task["window"], task["scale"], 1, 16, task["dtype"])
     elif kind == "fp8":
         out, lse = fp8.decode_multi_fp8(task["q"], task["k"], task["ks"], task["v"], task["vs"], bt, np.array([L]),
                                         n, task["scale"], 1, 16, task["dtype"])
@@ -135,7 +140,8 @@ def batch_attention(fetch: Callable, seqs, context_lens, q_lens, num_kv_heads: i
     ``(q [n, Hq, D], k [P, Hkv, 16, D], v [P, Hkv, 16, D])`` -- plus
     ``(k_scales [P, Hkv, 16], v_scales [P, Hkv, 16])`` when ``fp8_kv`` --
     where the P pages are the ones its table names, in table order (from
-    the window's first page on when ``window`` is given), and n =
+    the first page of the earliest token's window on when ``window`` is
+    given), and n =
     ``q_lens[s]`` tokens.  Yields (s, out [n, Hq, D], lse [n, Hq]) in
     float64 as sequences complete.
     """
@@ -155,8 +161,8 @@ def batch_attention(fetch: Callable, seqs, context_lens, q_lens, num_kv_heads: i
                      "dtype": dtype, "q": np.ascontiguousarray(q[:, g * G:(g + 1) * G]),
                      "k": np.ascontiguousarray(k[:, g:g + 1]), "v": np.ascontiguousarray(v[:, g:g + 1])}
                 if window is not None:
-                    t.update(kind="window", window=int(window),
-                             first_page=(L - int(window)) // 16 if L > int(window) else 0)
+                    lo = L - int(ql[s]) + 1 - int(window)  # the earliest row a token sees
+                    t.update(kind="window", window=int(window), first_page=lo // 16 if lo > 0 else 0)
                 if fp8_kv:
                     t.update(kind="fp8", ks=np.ascontiguousarray(got[3][:, g:g + 1]),
                              vs=np.ascontiguousarray(got[4][:, g:g + 1]))

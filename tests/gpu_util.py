@@ -122,7 +122,8 @@ def oracle_full(lay: Layout, q_dev, k_dev, v_dev, seqs=None, k_scales=None, v_sc
 
     def fetch(s):
         L = int(lay.context_lens[s])
-        first = (L - W) // 16 if W is not None and L > W else 0
+        lo = L - int(lay.q_lens[s]) + 1 - W if W is not None else 0  # the earliest row a token sees
+        first = lo // 16 if lo > 0 else 0
         idx = torch.from_numpy(lay.block_tables[s, first:(L + 15) // 16].astype(np.int64)).to(k_dev.device)
         if fp8:
             kc = k_dev.index_select(0, idx).cpu().numpy()

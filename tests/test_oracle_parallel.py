@@ -17,7 +17,8 @@ def host_fetch(lay, q, k, v, ks=None, vs=None):
     def fetch(s):
         L = int(lay.context_lens[s])
         W = lay.window
-        first = (L - W) // 16 if W is not None and L > W else 0
+        lo = L - int(lay.q_lens[s]) + 1 - W if W is not None else 0  # the earliest row a token sees
+        first = lo // 16 if lo > 0 else 0
         pages = lay.block_tables[s, first:(L + 15) // 16]
         got = (q[cu[s]:cu[s + 1]], k[pages], v[pages])
         return got + (ks[pages], vs[pages]) if ks is not None else got
@@ -71,6 +72,16 @@ def test_window_bit_identical(pool):
     lay = window_layout([10, 100, 257], 40, num_q_heads=8, num_kv_heads=2, head_dim=64, dtype="f32", seed=2)
     q, k, v = values_numpy(lay)
     want = oracle.decode_window(q, k, v, lay.block_tables, lay.context_lens, 40, lay.scale, 2, 16, "f32")
+    got = run_all(lay, host_fetch(lay, q, k, v), window=40)
+    for g, w in zip(got, want):
+        assert np.array_equal(g, w)
+
+
+def test_multi_token_window_bit_identical(pool):
+    lay = window_layout([4, 37, 100, 257], 40, num_q_heads=8, num_kv_heads=2, head_dim=64, dtype="f32", seed=4,
+                        q_len=4)
+    q, k, v = values_numpy(lay)
+    want = oracle.decode_multi_window(q, k, v, lay.block_tables, lay.context_lens, 4, 40, lay.scale, 2, 16, "f32")
     got = run_all(lay, host_fetch(lay, q, k, v), window=40)
     for g, w in zip(got, want):
         assert np.array_equal(g, w)

@@ -18,7 +18,7 @@ def kept_tables(lay):
     bt = np.full_like(lay.block_tables, -1)
     ctx = lay.context_lens.copy()
     for s, L in enumerate(lay.context_lens):
-        f = max(0, int(L) - lay.window) // lay.block_size
+        f = max(0, int(L) - int(lay.q_lens[s]) + 1 - lay.window) // lay.block_size  # the earliest token's window
         n = pages_of(L, lay.block_size)
         assert (lay.block_tables[s, :f] == 0).all()
         bt[s, : n - f] = lay.block_tables[s, f:n]

@@ -78,7 +78,8 @@ class Layout:
     # with one float32 scale per (page, kv-head, slot), q and out in dtype
     kv_dtype: Optional[str] = None
     # sliding window in tokens (None = full history): sequence s keeps the
-    # pages from (L - window) // block_size on; the entries before them are
+    # pages from (L - q_len + 1 - window) // block_size on (the earliest
+    # new token's window); the entries before them are
     # placeholders naming page 0, which holds no sequence's rows
     window: Optional[int] = None
 
@@ -197,13 +198,18 @@ def window_layout(
     value_std: float = 0.5,
     seed: int = 0,
     name: str = "window",
+    q_len: int = 1,
 ) -> Layout:
-    """One query token per sequence over a sliding-window cache: sequence s
-    holds only the pages from (L - window) // block_size on, in a seeded
-    permutation of pages 1..; its table entries before them are placeholders
-    naming page 0, which no sequence stores rows in (it stays NaN)."""
+    """q_len query tokens per sequence (the last q_len rows of its context;
+    one for decode) over a sliding-window cache: sequence s holds only the
+    pages from (L - q_len + 1 - window) // block_size on (the earliest
+    token's window), in a seeded permutation of pages 1..; its table entries
+    before them are placeholders naming page 0, which no sequence stores
+    rows in (it stays NaN)."""
     ctx = np.asarray(context_lens, dtype=np.int32)
-    firsts = [max(0, int(L) - int(window)) // block_size for L in ctx]
+    if int(q_len) < 1 or (ctx < int(q_len)).any():
+        raise ValueError("need 1 <= q_len <= every context length")
+    firsts = [max(0, int(L) - int(q_len) + 1 - int(window)) // block_size for L in ctx]
     need = [pages_of(L, block_size) - f for L, f in zip(ctx, firsts)]
     num_pages = 1 + int(sum(need))
     perm = (1 + _rng(seed, 0).permutation(num_pages - 1)).astype(np.int32)
@@ -226,7 +232,7 @@ def window_layout(
         scale=_scale_f32(scale),
         value_std=value_std,
         context_lens=ctx,
-        q_lens=np.ones_like(ctx),
+        q_lens=np.full_like(ctx, int(q_len)),
         block_tables=bt,
         num_pages=num_pages,
         seed=seed,
@@ -444,6 +450,15 @@ def _longtail_window4096(seed=0):
                          head_dim=base.head_dim, dtype=base.dtype, seed=seed, name="longtail_window4096")
 
 
+def _llama8b_multitoken4_window1024(seed=0):
+    """The 4-token decode step of the Llama-shaped batch over a 1024-token
+    sliding window: token i of a sequence with L rows sees the rows
+    [L - 4 + i + 1 - 1024, L - 4 + i]."""
+    base = _llama8b_decode(seed)
+    return window_layout(base.context_lens, 1024, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16",
+                         seed=seed, name="llama8b_multitoken4_window1024", q_len=4)
+
+
 def _llama8b_prefill_append_fp8(seed=0):
     """The whole-prefill append, quantised into an fp8 cache."""
     lay = _llama8b_prefill_append(seed)
@@ -475,6 +490,7 @@ WORKLOADS = {
     "llama8b_multitoken4": _llama8b_multitoken4,
     "llama8b_prefill_append_fp8": _llama8b_prefill_append_fp8,
     "longtail_window4096": _longtail_window4096,
+    "llama8b_multitoken4_window1024": _llama8b_multitoken4_window1024,
     "llama8b_prefill_append": _llama8b_prefill_append,
     "llama8b_decode": _llama8b_decode,
     "llama8b_decode_fp8": _llama8b_decode_fp8,
@@ -501,7 +517,7 @@ def _valid_rows_mask(lay: Layout) -> np.ndarray:
     for s in range(lay.num_seqs):
         L = int(lay.context_lens[s])
         n = pages_of(L, bs)
-        first = 0 if lay.window is None else max(0, L - lay.window) // bs
+        first = 0 if lay.window is None else max(0, L - int(lay.q_lens[s]) + 1 - lay.window) // bs
         pg = lay.block_tables[s, :n]
         valid[pg[first : n - 1]] = True
         last = L - (n - 1) * bs
