@@ -141,7 +141,7 @@ def visible_pairs(lay, segs):
     for s in segs:
         L, n = int(lay.context_lens[s]), int(lay.q_lens[s])
         if lay.window is not None:
-            tot += min(L, lay.window)  # one query over its window
+            tot += sum(min(L - n + i + 1, lay.window) for i in range(n))  # each token over its own window
         else:
             tot += n * (L - n) + n * (n + 1) // 2
     return tot
@@ -179,7 +179,8 @@ def cpu_baseline(lay, q, k, v, total_bytes, budget_s, k_scales=None, v_scales=No
 
     def fetch(s):
         L = int(lay.context_lens[s])
-        first = (L - W) // 16 if W is not None and L > W else 0
+        lo = L - int(lay.q_lens[s]) + 1 - W if W is not None else 0  # the earliest row a token sees
+        first = lo // 16 if lo > 0 else 0
         idx = torch.from_numpy(lay.block_tables[s, first:(L + 15) // 16].astype(np.int64)).to(k.device)
         qs = host(q[int(cu[s]) : int(cu[s + 1])])
         if fp8:
@@ -352,6 +353,9 @@ def main():
                 if fp8:
                     pa.decode_multi_fp8(out, q, k, v, ks, vs, bt, ctx, lay.context_lens, lay.scale, n_tok, ws,
                                         split_pages=args.split_pages, stream=stream)
+                elif lay.window is not None:
+                    pa.decode_multi_window(out, q, k, v, bt, ctx, lay.context_lens, lay.scale, n_tok, lay.window,
+                                           ws, split_pages=args.split_pages, stream=stream)
                 else:
                     pa.decode_multi(out, q, k, v, bt, ctx, lay.context_lens, lay.scale, n_tok, ws,
                                     split_pages=args.split_pages, stream=stream)
@@ -476,16 +480,21 @@ def main():
     elif multi:
         if fp8:
             nb = roofline.decode_fp8_bytes(lay.context_lens, lay.num_q_heads, lay.num_kv_heads, D, q_len=n_tok)
+        elif lay.window is not None:
+            # the rows any of a sequence's tokens sees: its last window + n - 1
+            nb = roofline.mixed_bytes(np.minimum(lay.context_lens, lay.window + n_tok - 1), lay.q_lens,
+                                      lay.num_q_heads, lay.num_kv_heads, D, lay.elem_bytes)
         else:
             nb = roofline.mixed_bytes(lay.context_lens, lay.q_lens, lay.num_q_heads, lay.num_kv_heads, D,
                                       lay.elem_bytes)
         rows = 2
         while rows < lay.gqa_ratio * fold:
             rows *= 2
-        roof = hbm_roof(f"{stream_kernel(rows)} ({n_tok} tokens folded)", nb["total"], float(sum(kern_avg)),
-                        measured_traffic(args.workload))
+        label = f"{stream_kernel(rows)} ({n_tok} tokens folded" + (
+            f", {lay.window}-token window)" if lay.window is not None else ")")
+        roof = hbm_roof(label, nb["total"], float(sum(kern_avg)), measured_traffic(args.workload))
         extra = {"tokens_per_step": int(T), "fold_passes": pairs}
-        if not fp8:  # (the chunk path reads bf16 / float32 pools only)
+        if not fp8 and lay.window is None:  # (the chunk path reads bf16 / float32 pools, no window)
             extra["mixed_chunk_same_batch_ms"] = round(float(np.median(cold(mixed_step, args.steps)[0])), 5)
     elif mixed:
         nb = roofline.mixed_bytes(lay.context_lens, lay.q_lens, lay.num_q_heads, lay.num_kv_heads, D,

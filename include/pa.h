@@ -244,6 +244,31 @@ int pa_decode_multi(void* out,                 /* device [S * q_len, Hq, D] dtyp
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Multi-token decode over a sliding-window cache: pa_decode_multi's tokens
+ * and fold, each token with its own window of `window` tokens (TokenSpeed
+ * deep-dive section 4.1, sliding_window_tokens): with L = context_lens[s],
+ * token i sits at position p = L - q_len + i and sees rows
+ * max(0, p + 1 - window) .. p.  Table entries before the first page of the
+ * earliest token's window, (L - q_len + 1 - window) / block_size, may be
+ * placeholders (tokenspeed 딥다이브 section 6-3): they are never read.
+ * Workspace: pa_decode_multi_workspace_size.  Built as pa_decode_multi.
+ * Errors as pa_decode_multi, plus PA_EINVAL for window < 1.  q_len == 1 is
+ * pa_decode_window exactly; a window of at least every context length is
+ * pa_decode_multi exactly.
+ * ------------------------------------------------------------------------- */
+int pa_decode_multi_window(void* out,                 /* device [S * q_len, Hq, D] dtype */
+                           float* lse_out,            /* device [S * q_len, Hq] or NULL */
+                           const void* q,             /* device [S * q_len, Hq, D] dtype */
+                           const void* k_pool,        /* device [NP, Hkv, BS, D] dtype */
+                           const void* v_pool,        /* device [NP, Hkv, BS, D] dtype */
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, const int32_t* context_lens_host,
+                           int32_t num_seqs, int32_t q_len, int32_t window, int32_t num_kv_heads,
+                           int32_t gqa_ratio, int32_t head_dim, int32_t block_size, int64_t num_pages, float scale,
+                           pa_dtype dtype, int32_t split_pages, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* ---------------------------------------------------------------------------
  * Multi-token decode over an fp8 cache: pa_decode_multi's tokens, rows and
  * causal limits (token i of a sequence with L rows sees rows 0 ..
  * L - q_len + i) over pa_decode_fp8's pools (e4m3fn codes with one float32

@@ -70,9 +70,11 @@ int pa::decode_call(void* out, float* lse_out, const void* q, const void* k_pool
     if (L < q_len) return fail(PA_EINVAL, w + ": context_lens[" + std::to_string(s) + "] < q_len");
     if (L > static_cast<int64_t>(max_blocks) * block_size)
       return fail(PA_EINVAL, w + ": context_lens[" + std::to_string(s) + "] exceeds the block table");
-    // pages the walk covers: from the window's first page on (a sliding
-    // window's earlier entries are placeholders and are never read)
-    const int64_t first = window > 0 && L > window ? (L - window) / block_size : 0;
+    // pages the walk covers: from the first page of the earliest token's
+    // window on (a sliding window's earlier entries are placeholders and
+    // are never read)
+    const int64_t reach = window > 0 ? static_cast<int64_t>(window) + q_len - 1 : 0;
+    const int64_t first = reach > 0 && L > reach ? (L - reach) / block_size : 0;
     total_pages += (L + block_size - 1) / block_size - first;
   }
   if (total_pages > (int64_t(1) << 31) - 1) return fail(PA_EUNSUPPORTED, w + ": more than 2^31-1 pages");
@@ -114,7 +116,7 @@ int pa::decode_call(void* out, float* lse_out, const void* q, const void* k_pool
   a.v_scales = v_scales;
   a.window = window;
   if (q_len == 1) return launch_decode(a);
-  return launch_decode_multi(a, plan_multi(q_len, gqa_ratio, context_lens_host, num_seqs, block_size));
+  return launch_decode_multi(a, plan_multi(q_len, gqa_ratio, context_lens_host, num_seqs, block_size, window));
 }
 
 extern "C" int pa_decode(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,
@@ -174,6 +176,20 @@ extern "C" int pa_decode_multi(void* out, float* lse_out, const void* q, const v
   return decode_call(out, lse_out, q, k_pool, v_pool, nullptr, nullptr, false, block_tables, max_blocks, context_lens,
                      context_lens_host, num_seqs, num_kv_heads, gqa_ratio, head_dim, block_size, num_pages, scale,
                      dtype, split_pages, workspace, workspace_bytes, stream, 0, q_len, "pa_decode_multi");
+}
+
+extern "C" int pa_decode_multi_window(void* out, float* lse_out, const void* q, const void* k_pool,
+                                      const void* v_pool, const int32_t* block_tables, int32_t max_blocks,
+                                      const int32_t* context_lens, const int32_t* context_lens_host, int32_t num_seqs,
+                                      int32_t q_len, int32_t window, int32_t num_kv_heads, int32_t gqa_ratio,
+                                      int32_t head_dim, int32_t block_size, int64_t num_pages, float scale,
+                                      pa_dtype dtype, int32_t split_pages, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  clear_error();
+  if (window < 1) return fail(PA_EINVAL, "pa_decode_multi_window: window < 1");
+  return decode_call(out, lse_out, q, k_pool, v_pool, nullptr, nullptr, false, block_tables, max_blocks, context_lens,
+                     context_lens_host, num_seqs, num_kv_heads, gqa_ratio, head_dim, block_size, num_pages, scale,
+                     dtype, split_pages, workspace, workspace_bytes, stream, window, q_len, "pa_decode_multi_window");
 }
 
 extern "C" int pa_decode_multi_fp8(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,

@@ -329,7 +329,8 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
         // those before L - (fe - 1 - j) of the pass's (trimmed) context
         const int j = h >> fold.lg;
         const int lim = j < fold.fe ? cur.L - (fold.fe - 1 - j) - cur.pb * 16 : 0;
-        vis = valid && lane < lim;
+        // (with a window: only the win rows up to the token's own position)
+        vis = valid && lane < lim && (fold.win == 0 || lane >= lim - fold.win);
       }
       const float s2 = vis ? sc[h] * kscale : -INFINITY;
       const float mn = fmaxf(m[h], wave_max(s2));
@@ -839,12 +840,12 @@ int launch_stream_merge(const DecodeLaunch& a, const int32_t* q_rows, int64_t wa
 
 int launch_decode_multi(const DecodeLaunch& a, const MultiPlan& p) {
   if (p.q_len == 1) return launch_decode(a);
-  if (a.window != 0) return fail(PA_EUNSUPPORTED, "pa_decode_multi: no sliding window");
   if (static_cast<int>(p.pass_pages.size()) != p.passes) return fail(PA_EINVAL, "pa_decode_multi: bad plan");
   Fold f;
   f.n = p.q_len;
   f.g = a.gqa;
   f.lg = __builtin_ctz(static_cast<unsigned>(a.gqa));
+  f.win = a.window;
   // Passes run one after another on the stream and reuse the workspace.
   for (int pass = 0; pass < p.passes; ++pass) {
     f.tok0 = pass * p.fold;
@@ -852,6 +853,9 @@ int launch_decode_multi(const DecodeLaunch& a, const MultiPlan& p) {
     f.trim = p.q_len - f.tok0 - f.fe;
     DecodeLaunch b = a;
     b.total_pages = p.pass_pages[pass];
+    // a window: the pass's walk covers its earliest token's window (the
+    // last window + fe - 1 rows of its context); each row masks its own
+    b.window = a.window > 0 ? a.window + f.fe - 1 : 0;
     int rc = PA_EUNSUPPORTED;
     if (a.kv_fp8 && a.dtype == PA_BF16 && a.head_dim == 128)
       rc = launch_fold_rows<uint16_t, uint8_t, 128>(b, p.rows, f);

@@ -78,13 +78,21 @@ MultiPlan plan_multi_shape(int32_t q_len, int32_t gqa) {
 }
 
 MultiPlan plan_multi(int32_t q_len, int32_t gqa, const int32_t* context_lens_host, int32_t num_seqs,
-                     int32_t block_size) {
+                     int32_t block_size, int32_t window) {
   MultiPlan p = plan_multi_shape(q_len, gqa);
   for (int32_t pass = 0; pass < p.passes; ++pass) {
-    const int64_t trim = p.q_len - std::min<int64_t>(p.q_len, static_cast<int64_t>(pass + 1) * p.fold);
+    const int64_t tok0 = static_cast<int64_t>(pass) * p.fold;
+    const int64_t fe = std::min<int64_t>(p.fold, p.q_len - tok0);  // tokens of the pass
+    const int64_t trim = p.q_len - tok0 - fe;
+    // with a window, the pass walks from its earliest token's window on:
+    // the last window + fe - 1 rows of its context
+    const int64_t walk = window > 0 ? window + fe - 1 : 0;
     int64_t pages = 0;
-    for (int32_t s = 0; s < num_seqs; ++s)
-      pages += (static_cast<int64_t>(context_lens_host[s]) - trim + block_size - 1) / block_size;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+      const int64_t L = static_cast<int64_t>(context_lens_host[s]) - trim;
+      const int64_t first = walk > 0 && L > walk ? (L - walk) / block_size : 0;
+      pages += (L + block_size - 1) / block_size - first;
+    }
     p.pass_pages.push_back(pages);
   }
   return p;

@@ -97,7 +97,7 @@ struct MultiPlan {
 // fold, rows and passes only (no lengths): what sizes the workspace.
 MultiPlan plan_multi_shape(int32_t q_len, int32_t gqa);
 MultiPlan plan_multi(int32_t q_len, int32_t gqa, const int32_t* context_lens_host, int32_t num_seqs,
-                     int32_t block_size);
+                     int32_t block_size, int32_t window = 0);
 int launch_decode_multi(const DecodeLaunch& a, const MultiPlan& p);
 // Partial rows per wave a multi-token call's workspace holds: the stream
 // kernel's for one token; 16 for folded passes (every fp8 pass, and bf16

@@ -160,6 +160,9 @@ struct Fold {
   int tok0;  // first token of the pass
   int fe;    // tokens in the pass
   int trim;  // n - tok0 - fe: context rows after the pass's last token
+  int win = 0;  // sliding window in tokens (0: none): token j of the pass sees
+                // only the win rows up to its own position; the walk then
+                // starts at the pass's earliest token's window
 };
 
 // LDS of one matrix-core stream wave: the batch's K and V (64 rows,
@@ -371,7 +374,10 @@ __device__ __forceinline__ void stream_mfma_body(
     const int nvalid = min(cur.seg_hi * 16, cur.L) - cur.pb * 16;  // rows of this batch (1..64)
     const int lo_b = cur.lo - cur.pb * 16;  // rows before the window (<= 0: none)
     // (MT) rows after this token's own position are not seen
-    const int hi_b = !active ? 0 : MT ? min(nvalid, cur.L - (fold.fe - 1 - tok) - cur.pb * 16) : nvalid;
+    const int hi_t = cur.L - (fold.fe - 1 - tok) - cur.pb * 16;  // (MT) one past this row's token position
+    const int hi_b = !active ? 0 : MT ? min(nvalid, hi_t) : nvalid;
+    // (MT with a window) the row's own window starts win rows before its end
+    const int lo_r = MT && fold.win > 0 ? max(lo_b, hi_t - fold.win) : lo_b;
     float x[4][4];
     float mx = -INFINITY;
 #pragma unroll
@@ -382,7 +388,7 @@ __device__ __forceinline__ void stream_mfma_body(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = kb * 16 + lg * 4 + i;
-        x[kb][i] = key < hi_b && key >= lo_b ? sc[kb][i] * (FP8 ? kq[i] * scale_log2 : scale_log2) : -INFINITY;
+        x[kb][i] = key < hi_b && key >= lo_r ? sc[kb][i] * (FP8 ? kq[i] * scale_log2 : scale_log2) : -INFINITY;
         mx = fmaxf(mx, x[kb][i]);
       }
     }

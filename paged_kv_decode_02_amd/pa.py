@@ -37,6 +37,7 @@ EXPORTS = (
     "pa_decode_window",
     "pa_decode_multi_workspace_size",
     "pa_decode_multi",
+    "pa_decode_multi_window",
     "pa_decode_multi_fp8",
     "pa_prefix_cascade_workspace_size",
     "pa_prefix_cascade",
@@ -91,6 +92,10 @@ def load(path: Optional[str] = None):
     lib.pa_decode_multi.restype = ctypes.c_int
     lib.pa_decode_multi.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                                     c_i32, c_i32, c_i64, ctypes.c_float, ctypes.c_int, c_i32, c_vp, c_sz, c_vp]
+    lib.pa_decode_multi_window.restype = ctypes.c_int
+    lib.pa_decode_multi_window.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32,
+                                           c_i32, c_i32, c_i32, c_i32, c_i32, c_i64, ctypes.c_float, ctypes.c_int,
+                                           c_i32, c_vp, c_sz, c_vp]
     lib.pa_decode_multi_fp8.restype = ctypes.c_int
     lib.pa_decode_multi_fp8.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32,
                                         c_i32, c_i32, c_i32, c_i32, c_i32, c_i64, ctypes.c_float, c_i32, c_vp, c_sz,
@@ -225,6 +230,20 @@ def decode_multi(out, q, k_pool, v_pool, block_tables, context_lens, context_len
     """pa_decode_multi on torch tensors: ``q_len`` new tokens per sequence,
     q / out ``[S * q_len, Hq, D]`` (token i of sequence s at row
     s * q_len + i), causal among the new tokens."""
+    return _decode_multi(None, out, q, k_pool, v_pool, block_tables, context_lens, context_lens_host, scale, q_len,
+                         workspace, lse_out, split_pages, stream)
+
+
+def decode_multi_window(out, q, k_pool, v_pool, block_tables, context_lens, context_lens_host, scale, q_len, window,
+                        workspace, lse_out=None, split_pages=0, stream=None):
+    """pa_decode_multi_window on torch tensors: pa_decode_multi's tokens,
+    each seeing only the ``window`` rows up to its own position."""
+    return _decode_multi(int(window), out, q, k_pool, v_pool, block_tables, context_lens, context_lens_host, scale,
+                         q_len, workspace, lse_out, split_pages, stream)
+
+
+def _decode_multi(window, out, q, k_pool, v_pool, block_tables, context_lens, context_lens_host, scale, q_len,
+                  workspace, lse_out, split_pages, stream):
     import torch
 
     T, Hq, D = q.shape
@@ -246,7 +265,7 @@ def decode_multi(out, q, k_pool, v_pool, block_tables, context_lens, context_len
         raise ValueError("context_lens_host must have one entry per sequence")
     if lse_out is not None and tuple(lse_out.shape) != (T, Hq):
         raise ValueError("lse_out must be [S * q_len, Hq]")
-    rc = load().pa_decode_multi(
+    head = (
         _dev(out, "out"),
         _dev(lse_out, "lse_out", torch.float32) if lse_out is not None else None,
         _dev(q, "q"),
@@ -256,9 +275,14 @@ def decode_multi(out, q, k_pool, v_pool, block_tables, context_lens, context_len
         block_tables.shape[1],
         _dev(context_lens, "context_lens", torch.int32),
         ch.ctypes.data,
-        S, q_len, Hkv, Hq // Hkv, D, BS, NP, float(scale), _dtype_code(q), int(split_pages),
-        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream_ptr(stream),
+        S, q_len,
     )
+    tail = (Hkv, Hq // Hkv, D, BS, NP, float(scale), _dtype_code(q), int(split_pages),
+            _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream_ptr(stream))
+    if window is None:
+        rc = load().pa_decode_multi(*head, *tail)
+    else:
+        rc = load().pa_decode_multi_window(*head, int(window), *tail)
     return _check(rc)
 
 

@@ -354,6 +354,45 @@ def test_decode_multi_zero_sequences_is_a_no_op():
     assert call_decode_multi(lib, S=0, q=None, out=None) == pa.PA_OK
 
 
+def call_decode_multi_window(lib, window=8, **kw):
+    args = dict(out=FAKE, lse=None, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, mb=4, ctx=FAKE, ctx_host=None, S=2, n=4, Hkv=2,
+                G=4, D=128, BS=16, NP=10, scale=0.1, dtype=pa.PA_BF16, split=0, ws=ctypes.c_void_p(0x100000),
+                ws_bytes=1 << 20, stream=None)
+    args.update(kw)
+    ch = args["ctx_host"]
+    if ch is None:
+        ch = np.array([20, 40], dtype=np.int32)
+    return lib.pa_decode_multi_window(args["out"], args["lse"], args["q"], args["k"], args["v"], args["bt"],
+                                      args["mb"], args["ctx"], ch.ctypes.data, args["S"], args["n"], window,
+                                      args["Hkv"], args["G"], args["D"], args["BS"], args["NP"], args["scale"],
+                                      args["dtype"], args["split"], args["ws"], args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(window=0), pa.PA_EINVAL),
+        (dict(window=-5), pa.PA_EINVAL),
+        (dict(q=None), pa.PA_EINVAL),
+        (dict(n=0), pa.PA_EINVAL),
+        (dict(ctx_host=np.array([3, 40], dtype=np.int32)), pa.PA_EINVAL),  # shorter than q_len
+        (dict(ctx_host=np.array([20, 65], dtype=np.int32)), pa.PA_EINVAL),
+        (dict(G=3), pa.PA_EUNSUPPORTED),
+        (dict(ws=ctypes.c_void_p(0x100010)), pa.PA_EINVAL),
+        (dict(ws_bytes=64, split=1), pa.PA_EWORKSPACE),
+    ],
+)
+def test_decode_multi_window_rejects_bad_arguments(kw, code):
+    lib = pa.load()
+    assert call_decode_multi_window(lib, **kw) == code
+    assert lib.pa_last_error().decode().startswith("pa_decode_multi_window")
+
+
+def test_decode_multi_window_zero_sequences_is_a_no_op():
+    lib = pa.load()
+    assert call_decode_multi_window(lib, S=0, q=None, out=None) == pa.PA_OK
+
+
 def test_decode_multi_workspace_follows_the_fold():
     """q_len 1 sizes like plain decode; folded passes keep 16 partial rows
     per wave (the matrix-core kernel's; smaller passes fit inside)."""
