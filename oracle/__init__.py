@@ -26,5 +26,13 @@ from .attention import (  # noqa: F401
     check_block_tables,
 )
 from .kv_append import kv_append  # noqa: F401
-from .fp8 import decode_fp8, decode_multi_fp8, dequantize, e4m3_to_f64, kv_append_fp8, quantize_rows  # noqa: F401
+from .fp8 import (  # noqa: F401
+    decode_fp8,
+    decode_multi_fp8,
+    dequantize,
+    e4m3_to_f64,
+    kv_append_fp8,
+    prefix_cascade_fp8,
+    quantize_rows,
+)
 from .prefix_groups import detect_prefix_groups  # noqa: F401

@@ -43,6 +43,11 @@ Pins (tests/test_fp8_pins.py):
   scales it equals the pinned chunk oracle (``oracle.mixed_chunk``) on the
   read-back bf16 values bit for bit; brute force with Python loops; a causal
   edge one row off and tokens read in the wrong order are caught;
+* shared-prefix decode (``prefix_cascade_fp8``: the group check, then
+  ``decode_fp8``): equal to the log-sum-exp merge of the fp8 attention over
+  the prefix rows alone and over the suffix rows alone; a broken group is
+  rejected; dropping the suffix, skipping the check and counting the prefix
+  twice are each caught;
 * the quantising append (``kv_append_fp8``: quantise each new row, then
   place codes and scale as ``oracle.kv_append`` places a row) against a
   brute-force element loop, and its read-back against the new rows within
@@ -55,7 +60,7 @@ import math
 
 import numpy as np
 
-from .attention import attend, stored_to_f64
+from .attention import attend, check_block_tables, stored_to_f64
 
 E4M3_MAX = 448.0
 E4M3_BIAS = 7
@@ -168,6 +173,23 @@ def decode_fp8(q, k_codes, k_scales, v_codes, v_scales, block_tables, context_le
             for h in range(g * G, (g + 1) * G):
                 out[s, h], lse[s, h] = attend(qs[h], K, V, sc)
     return out, lse
+
+
+def prefix_cascade_fp8(q, k_codes, k_scales, v_codes, v_scales, block_tables, context_lens, scale, num_kv_heads,
+                       block_size, group_seq_offsets, prefix_lens, q_dtype="bf16", seqs=None):
+    """Shared-prefix (cascade) decode over an fp8 cache: as
+    :func:`attention.prefix_cascade` -- defined as plain decode over each
+    member's whole table, the prefix blocks shared by the group (Tokasaurus
+    page, "dynamic prefix identification"; SwiftLLM page section 3.1) -- with
+    the K and V rows read back from e4m3fn codes and their scales
+    (tokenspeed 딥다이브 section 6-4), i.e. :func:`decode_fp8`.  The group
+    structure is checked first."""
+    probs = check_block_tables(block_tables, context_lens, k_codes.shape[0], block_size, group_seq_offsets,
+                               prefix_lens)
+    if probs:
+        raise ValueError("; ".join(probs[:5]))
+    return decode_fp8(q, k_codes, k_scales, v_codes, v_scales, block_tables, context_lens, scale, num_kv_heads,
+                      block_size, q_dtype, seqs)
 
 
 def _visible(L: int, q_len: int, i: int) -> int:

@@ -394,3 +394,94 @@ def test_kv_append_fp8_bruteforce_and_read_back():
 def test_planted_multi_token_mistake_is_caught(monkeypatch, name, bad):
     monkeypatch.setattr(f8, "_visible", bad)
     assert _run_pins(), f"no pin noticed: {name}"
+
+
+# ---------------------------------------------------------------------------
+# shared-prefix (cascade) decode over an fp8 cache
+# ---------------------------------------------------------------------------
+
+
+def _cascade_case(seed=11):
+    from workloads import cascade_layout, fp8_values_numpy
+
+    lay = cascade_layout(num_groups=3, seqs_per_group=3, prefix_len=48, suffix_lo=1, suffix_hi=40, num_q_heads=8,
+                         num_kv_heads=2, head_dim=32, seed=seed, prefix_lens=[48, 16, 64])
+    lay.kv_dtype = "fp8"
+    return lay, fp8_values_numpy(lay)
+
+
+def pin_cascade_is_prefix_merge_suffix():
+    """Attention over prefix + suffix equals the log-sum-exp merge of the
+    fp8 attention over the shared prefix rows alone (table cut at the
+    prefix) and over each member's suffix rows alone (table shifted past the
+    prefix, which ends on a page boundary), within fp64 rounding."""
+    lay, (q, kc, ks, vc, vs) = _cascade_case()
+    out, lse = oracle.prefix_cascade_fp8(q, kc, ks, vc, vs, lay.block_tables, lay.context_lens, lay.scale,
+                                         lay.num_kv_heads, 16, lay.group_seq_offsets, lay.prefix_lens)
+    per_seq_prefix = np.repeat(lay.prefix_lens, np.diff(lay.group_seq_offsets))
+    fails = []
+    for s in range(lay.num_seqs):
+        P, L = int(per_seq_prefix[s]), int(lay.context_lens[s])
+        parts = []
+        if P > 0:
+            po, pl = f8.decode_fp8(q[s:s + 1], kc, ks, vc, vs, lay.block_tables[s:s + 1], np.array([P]), lay.scale,
+                                   lay.num_kv_heads, 16)
+            parts.append((po[0], pl[0]))
+        bt = np.full_like(lay.block_tables[s:s + 1], -1)
+        n = (L + 15) // 16 - P // 16
+        bt[0, :n] = lay.block_tables[s, P // 16:(L + 15) // 16]
+        so, sl = f8.decode_fp8(q[s:s + 1], kc, ks, vc, vs, bt, np.array([L - P]), lay.scale, lay.num_kv_heads, 16)
+        parts.append((so[0], sl[0]))
+        for h in range(lay.num_q_heads):
+            mo, ml = oracle.lse_merge([(o[h], l[h]) for o, l in parts])
+            if not (np.max(np.abs(mo - out[s, h])) <= 1e-12 and abs(ml - lse[s, h]) <= 1e-12):
+                fails.append(f"seq {s} head {h}: cascade != prefix (+) suffix")
+    return fails
+
+
+def pin_cascade_checks_groups():
+    """A member whose prefix entries differ from its group's is rejected."""
+    lay, (q, kc, ks, vc, vs) = _cascade_case(seed=12)
+    bt = lay.block_tables.copy()
+    bt[1, 0] = bt[lay.group_seq_offsets[1], 0]  # member 1 of group 0 names group 1's first prefix page
+    try:
+        oracle.prefix_cascade_fp8(q, kc, ks, vc, vs, bt, lay.context_lens, lay.scale, lay.num_kv_heads, 16,
+                                  lay.group_seq_offsets, lay.prefix_lens)
+    except ValueError:
+        return []
+    return ["an unshared prefix was accepted"]
+
+
+CASCADE_PINS = [pin_cascade_is_prefix_merge_suffix, pin_cascade_checks_groups]
+
+
+@pytest.mark.parametrize("pin", CASCADE_PINS, ids=lambda p: p.__name__)
+def test_cascade_pin(pin):
+    fails = pin()
+    assert not fails, fails[:5]
+
+
+def _cascade_prefix_only(q, kc, ks, vc, vs, bt, ctx, scale, hkv, bs, go, pl, q_dtype="bf16", seqs=None):
+    per = np.repeat(np.asarray(pl), np.diff(np.asarray(go)))
+    return f8.decode_fp8(q, kc, ks, vc, vs, bt, np.maximum(per, 1), scale, hkv, bs, q_dtype, seqs)
+
+
+def _cascade_no_check(q, kc, ks, vc, vs, bt, ctx, scale, hkv, bs, go, pl, q_dtype="bf16", seqs=None):
+    return f8.decode_fp8(q, kc, ks, vc, vs, bt, ctx, scale, hkv, bs, q_dtype, seqs)
+
+
+def _cascade_prefix_twice(q, kc, ks, vc, vs, bt, ctx, scale, hkv, bs, go, pl, q_dtype="bf16", seqs=None):
+    per = np.repeat(np.asarray(pl), np.diff(np.asarray(go)))
+    out, lse = f8.decode_fp8(q, kc, ks, vc, vs, bt, ctx, scale, hkv, bs, q_dtype, seqs)
+    po, plse = f8.decode_fp8(q, kc, ks, vc, vs, bt, np.maximum(per, 1), scale, hkv, bs, q_dtype, seqs)
+    m = np.maximum(lse, plse)
+    a, b = np.exp(lse - m), np.exp(plse - m)
+    return (a[..., None] * out + b[..., None] * po) / (a + b)[..., None], m + np.log(a + b)
+
+
+@pytest.mark.parametrize("name,bad", [("prefix rows only", _cascade_prefix_only),
+                                      ("group structure unchecked", _cascade_no_check),
+                                      ("prefix counted twice", _cascade_prefix_twice)])
+def test_planted_cascade_mistake_is_caught(monkeypatch, name, bad):
+    monkeypatch.setattr(oracle, "prefix_cascade_fp8", bad)
+    assert any(p() for p in CASCADE_PINS), f"no pin noticed: {name}"
