@@ -332,9 +332,14 @@ def main():
         ws = torch.empty(pa.prefix_cascade_workspace_size(S, lay.num_kv_heads, lay.gqa_ratio, D, total_pages),
                          dtype=torch.uint8, device=dev)
 
-        def step():
-            pa.prefix_cascade(out, q, k, v, bt, ctx, lay.context_lens, go, lay.group_seq_offsets, pl,
-                              lay.prefix_lens, lay.scale, ws, stream=stream)
+        if fp8:
+            def step():
+                pa.prefix_cascade_fp8(out, q, k, v, ks, vs, bt, ctx, lay.context_lens, go, lay.group_seq_offsets, pl,
+                                      lay.prefix_lens, lay.scale, ws, stream=stream)
+        else:
+            def step():
+                pa.prefix_cascade(out, q, k, v, bt, ctx, lay.context_lens, go, lay.group_seq_offsets, pl,
+                                  lay.prefix_lens, lay.scale, ws, stream=stream)
     elif mixed or multi:
         cu = torch.from_numpy(lay.cu_q_lens.astype(np.int32)).to(dev)
         mws = torch.empty(pa.mixed_chunk_workspace_size(T, S, lay.num_kv_heads, lay.gqa_ratio, D, total_pages),
@@ -465,16 +470,21 @@ def main():
     extra = {}
     if cascade:
         nb = roofline.cascade_bytes(lay.context_lens, lay.group_seq_offsets, lay.prefix_lens, lay.num_q_heads,
-                                    lay.num_kv_heads, D, lay.elem_bytes)
+                                    lay.num_kv_heads, D, 2 if fp8 else lay.elem_bytes, kv_fp8=fp8)
         flops = roofline.prefix_flops(lay.group_seq_offsets, lay.prefix_lens, lay.num_q_heads, D)
-        roof = mfma_roof("tile_kernel (shared prefix)", flops, kern_avg[0],
-                         measured_traffic("tile:" + args.workload, TILE_SOURCES))
+        roof = mfma_roof("tile_kernel (shared prefix, fp8 pools)" if fp8 else "tile_kernel (shared prefix)", flops,
+                         kern_avg[0], measured_traffic("tile:" + args.workload, TILE_SOURCES))
         # the same batch through plain decode, for the cascade's speed-up
         dws = torch.empty(pa.decode_workspace_size(S, lay.num_kv_heads, lay.gqa_ratio, D, total_pages, 0),
                           dtype=torch.uint8, device=dev)
         dout = torch.empty_like(q)
-        dec_ms = float(np.median(cold(lambda: pa.decode(dout, q, k, v, bt, ctx, lay.context_lens, lay.scale, dws,
-                                                        stream=stream), args.steps)[0]))
+        if fp8:
+            def dec_step():
+                pa.decode_fp8(dout, q, k, v, ks, vs, bt, ctx, lay.context_lens, lay.scale, dws, stream=stream)
+        else:
+            def dec_step():
+                pa.decode(dout, q, k, v, bt, ctx, lay.context_lens, lay.scale, dws, stream=stream)
+        dec_ms = float(np.median(cold(dec_step, args.steps)[0]))
         extra = {"prefix_gflop": round(flops / 1e9, 3), "decode_same_batch_ms": round(dec_ms, 5),
                  "cascade_speedup_vs_decode": round(dec_ms / ms_per_step, 3)}
     elif multi:

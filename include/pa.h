@@ -330,6 +330,34 @@ int pa_prefix_cascade(void* out,                       /* device [S, Hq, D] */
                       void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Shared-prefix (cascade) decode over an fp8 cache: pa_prefix_cascade's
+ * groups, prefixes and result (decode over each member's whole table) over
+ * pa_decode_fp8's pools -- e4m3fn codes with one float32 scale per (page,
+ * kv-head, slot) for K and one for V (tokenspeed 딥다이브 section 6-4); q and
+ * out bf16.  The prefix tiles read the codes, widen them exactly to bf16 for
+ * the matrix cores, and apply each key's K scale to its scores and its V
+ * scale to the probability P.V takes; the suffix runs on the fp8 stream
+ * kernel.  Workspace: pa_prefix_cascade_workspace_size.  Built for
+ * head_dim 128, gqa_ratio 1, 2, 4, 8, 16.  Errors as pa_prefix_cascade, plus
+ * PA_EINVAL for a NULL scale pointer.
+ * ------------------------------------------------------------------------- */
+int pa_prefix_cascade_fp8(void* out,                       /* device [S, Hq, D] bf16 */
+                          float* lse_out,                  /* device [S, Hq] or NULL */
+                          const void* q,                   /* device [S, Hq, D] bf16 */
+                          const void* k_pool, const void* v_pool, /* device [NP, Hkv, BS, D] e4m3fn codes */
+                          const float* k_scales, const float* v_scales, /* device [NP, Hkv, BS] */
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens,      /* device [S] */
+                          const int32_t* context_lens_host, /* host [S] */
+                          int32_t num_seqs, int32_t num_groups,
+                          const int32_t* group_seq_offsets,      /* device [G+1] */
+                          const int32_t* group_seq_offsets_host, /* host [G+1] */
+                          const int32_t* prefix_lens,            /* device [G] */
+                          const int32_t* prefix_lens_host,       /* host [G] */
+                          int32_t num_kv_heads, int32_t gqa_ratio, int32_t head_dim, int32_t block_size,
+                          int64_t num_pages, float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Mixed batch: prefill chunks and decode tokens in one call (decode tokens
  * of many sequences piggybacked on prefill chunks: SwiftLLM page, section
  * 3.3, SARATHI-style piggybacking; prefill admitted in bounded chunks, each attending

@@ -213,52 +213,54 @@ extern "C" size_t pa_prefix_cascade_workspace_size(int32_t max_num_seqs, int32_t
   return cascade_layout(max_num_seqs, num_kv_heads, gqa_ratio, head_dim, kMaxPrefixSplits, stream).bytes;
 }
 
-extern "C" int pa_prefix_cascade(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,
-                                 const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
-                                 const int32_t* context_lens_host, int32_t num_seqs, int32_t num_groups,
-                                 const int32_t* group_seq_offsets, const int32_t* group_seq_offsets_host,
-                                 const int32_t* prefix_lens, const int32_t* prefix_lens_host, int32_t num_kv_heads,
-                                 int32_t gqa_ratio, int32_t head_dim, int32_t block_size, int64_t num_pages,
-                                 float scale, pa_dtype dtype, void* workspace, size_t workspace_bytes,
-                                 void* stream) {
-  clear_error();
-  if (num_seqs < 0 || num_groups < 0) return fail(PA_EINVAL, "pa_prefix_cascade: negative count");
+namespace {
+
+// pa_prefix_cascade and pa_prefix_cascade_fp8: validation, plans, launch.
+int cascade_call(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,
+                 const float* k_scales, const float* v_scales, bool kv_fp8, const int32_t* block_tables,
+                 int32_t max_blocks, const int32_t* context_lens, const int32_t* context_lens_host, int32_t num_seqs,
+                 int32_t num_groups, const int32_t* group_seq_offsets, const int32_t* group_seq_offsets_host,
+                 const int32_t* prefix_lens, const int32_t* prefix_lens_host, int32_t num_kv_heads, int32_t gqa_ratio,
+                 int32_t head_dim, int32_t block_size, int64_t num_pages, float scale, pa_dtype dtype,
+                 void* workspace, size_t workspace_bytes, void* stream, const char* who) {
+  const std::string w(who);
+  if (num_seqs < 0 || num_groups < 0) return fail(PA_EINVAL, w + ": negative count");
   if (num_seqs == 0) return PA_OK;
   int rc = check_common(out, q, k_pool, v_pool, block_tables, max_blocks, context_lens, context_lens_host,
-                        num_kv_heads, gqa_ratio, head_dim, block_size, num_pages, scale, dtype, workspace,
-                        "pa_prefix_cascade");
+                        num_kv_heads, gqa_ratio, head_dim, block_size, num_pages, scale, dtype, workspace, who);
   if (rc) return rc;
+  if (kv_fp8 && (!k_scales || !v_scales)) return fail(PA_EINVAL, w + ": null scale pointer");
   if (num_groups < 1 || !group_seq_offsets || !group_seq_offsets_host || !prefix_lens || !prefix_lens_host)
-    return fail(PA_EINVAL, "pa_prefix_cascade: groups must be given (device and host copies)");
+    return fail(PA_EINVAL, w + ": groups must be given (device and host copies)");
   if (!cascade_supported(dtype, head_dim, gqa_ratio))
-    return fail(PA_EUNSUPPORTED, "pa_prefix_cascade: built for bf16, head_dim 128, gqa_ratio 1/2/4/8/16");
+    return fail(PA_EUNSUPPORTED, w + ": built for bf16 q, head_dim 128, gqa_ratio 1/2/4/8/16");
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
-    return fail(PA_EINVAL, "pa_prefix_cascade: workspace not 256B aligned");
+    return fail(PA_EINVAL, w + ": workspace not 256B aligned");
   if (group_seq_offsets_host[0] != 0 || group_seq_offsets_host[num_groups] != num_seqs)
-    return fail(PA_EINVAL, "pa_prefix_cascade: groups must cover sequences 0 .. num_seqs-1 in order");
+    return fail(PA_EINVAL, w + ": groups must cover sequences 0 .. num_seqs-1 in order");
   int64_t suffix_pages = 0;
   int64_t max_rows = 0;
   int32_t max_prefix = 0;
   for (int32_t g = 0; g < num_groups; ++g) {
     const int32_t a = group_seq_offsets_host[g], b = group_seq_offsets_host[g + 1];
-    if (b < a) return fail(PA_EINVAL, "pa_prefix_cascade: group offsets decrease");
+    if (b < a) return fail(PA_EINVAL, w + ": group offsets decrease");
     const int32_t P = prefix_lens_host[g];
     if (P < 0 || P % block_size)
-      return fail(PA_EINVAL, "pa_prefix_cascade: prefix_lens[" + std::to_string(g) + "] not a whole number of pages");
+      return fail(PA_EINVAL, w + ": prefix_lens[" + std::to_string(g) + "] not a whole number of pages");
     max_prefix = std::max(max_prefix, P);
     max_rows = std::max<int64_t>(max_rows, static_cast<int64_t>(b - a) * gqa_ratio);
     for (int32_t s = a; s < b; ++s) {
       const int64_t L = context_lens_host[s];
-      if (L < 1) return fail(PA_EINVAL, "pa_prefix_cascade: context_lens[" + std::to_string(s) + "] < 1");
+      if (L < 1) return fail(PA_EINVAL, w + ": context_lens[" + std::to_string(s) + "] < 1");
       if (L > static_cast<int64_t>(max_blocks) * block_size)
-        return fail(PA_EINVAL, "pa_prefix_cascade: context_lens[" + std::to_string(s) + "] exceeds the block table");
+        return fail(PA_EINVAL, w + ": context_lens[" + std::to_string(s) + "] exceeds the block table");
       if (P >= L)
-        return fail(PA_EINVAL, "pa_prefix_cascade: prefix of group " + std::to_string(g) +
+        return fail(PA_EINVAL, w + ": prefix of group " + std::to_string(g) +
                                    " is not shorter than sequence " + std::to_string(s));
       suffix_pages += (L + block_size - 1) / block_size - P / block_size;
     }
   }
-  if (suffix_pages > (int64_t(1) << 31) - 1) return fail(PA_EUNSUPPORTED, "pa_prefix_cascade: too many pages");
+  if (suffix_pages > (int64_t(1) << 31) - 1) return fail(PA_EUNSUPPORTED, w + ": too many pages");
   // Prefix plan: two tile workgroups fit on a CU (66 KB of LDS each), so aim
   // at about two per CU (row blocks x key splits), each split a 64-key
   // multiple of the prefix; key splits only when the row blocks alone leave
@@ -267,7 +269,7 @@ extern "C" int pa_prefix_cascade(void* out, float* lse_out, const void* q, const
       static_cast<int32_t>(std::max<int64_t>(1, (max_rows + kPrefixRowsPerBlock - 1) / kPrefixRowsPerBlock));
   const int64_t units = static_cast<int64_t>(num_groups) * row_chunks * num_kv_heads;
   const int cus = device_cu_count();
-  const int64_t slots = static_cast<int64_t>(kTileWorkgroupsPerCU) * (cus > 0 ? cus : 256);
+  const int64_t slots = static_cast<int64_t>(kv_fp8 ? kTileFp8WorkgroupsPerCU : kTileWorkgroupsPerCU) * (cus > 0 ? cus : 256);
   int32_t nks =
       static_cast<int32_t>(std::min<int64_t>(kMaxPrefixSplits, std::max<int64_t>(1, (slots + units - 1) / units)));
   int32_t kps = 64;
@@ -282,7 +284,7 @@ extern "C" int pa_prefix_cascade(void* out, float* lse_out, const void* q, const
   const size_t stream_bytes = partial_layout(waves, num_seqs, num_kv_heads, stream_rows(gqa_ratio), head_dim).bytes;
   const CascadeLayout lay = cascade_layout(num_seqs, num_kv_heads, gqa_ratio, head_dim, nks, stream_bytes);
   if (lay.bytes > workspace_bytes)
-    return fail(PA_EWORKSPACE, "pa_prefix_cascade: workspace holds " + std::to_string(workspace_bytes) +
+    return fail(PA_EWORKSPACE, w + ": workspace holds " + std::to_string(workspace_bytes) +
                                    " bytes, needs " + std::to_string(lay.bytes));
   CascadeLaunch c;
   DecodeLaunch& a = c.base;
@@ -306,6 +308,9 @@ extern "C" int pa_prefix_cascade(void* out, float* lse_out, const void* q, const
   a.workspace = nullptr;
   a.workspace_bytes = 0;
   a.stream = stream;
+  a.kv_fp8 = kv_fp8;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
   c.group_offsets = group_seq_offsets;
   c.prefix_lens = prefix_lens;
   c.num_groups = num_groups;
@@ -317,6 +322,40 @@ extern "C" int pa_prefix_cascade(void* out, float* lse_out, const void* q, const
   c.workspace = workspace;
   c.workspace_bytes = workspace_bytes;
   return launch_cascade(c);
+}
+
+}  // namespace
+
+extern "C" int pa_prefix_cascade(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                                 const int32_t* context_lens_host, int32_t num_seqs, int32_t num_groups,
+                                 const int32_t* group_seq_offsets, const int32_t* group_seq_offsets_host,
+                                 const int32_t* prefix_lens, const int32_t* prefix_lens_host, int32_t num_kv_heads,
+                                 int32_t gqa_ratio, int32_t head_dim, int32_t block_size, int64_t num_pages,
+                                 float scale, pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  clear_error();
+  return cascade_call(out, lse_out, q, k_pool, v_pool, nullptr, nullptr, false, block_tables, max_blocks,
+                      context_lens, context_lens_host, num_seqs, num_groups, group_seq_offsets,
+                      group_seq_offsets_host, prefix_lens, prefix_lens_host, num_kv_heads, gqa_ratio, head_dim,
+                      block_size, num_pages, scale, dtype, workspace, workspace_bytes, stream, "pa_prefix_cascade");
+}
+
+extern "C" int pa_prefix_cascade_fp8(void* out, float* lse_out, const void* q, const void* k_pool,
+                                     const void* v_pool, const float* k_scales, const float* v_scales,
+                                     const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                                     const int32_t* context_lens_host, int32_t num_seqs, int32_t num_groups,
+                                     const int32_t* group_seq_offsets, const int32_t* group_seq_offsets_host,
+                                     const int32_t* prefix_lens, const int32_t* prefix_lens_host,
+                                     int32_t num_kv_heads, int32_t gqa_ratio, int32_t head_dim, int32_t block_size,
+                                     int64_t num_pages, float scale, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  clear_error();
+  return cascade_call(out, lse_out, q, k_pool, v_pool, k_scales, v_scales, true, block_tables, max_blocks,
+                      context_lens, context_lens_host, num_seqs, num_groups, group_seq_offsets,
+                      group_seq_offsets_host, prefix_lens, prefix_lens_host, num_kv_heads, gqa_ratio, head_dim,
+                      block_size, num_pages, scale, PA_BF16, workspace, workspace_bytes, stream,
+                      "pa_prefix_cascade_fp8");
 }
 
 extern "C" size_t pa_mixed_chunk_workspace_size(int32_t max_num_tokens, int32_t max_num_segments,

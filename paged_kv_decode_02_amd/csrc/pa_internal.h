@@ -21,6 +21,10 @@ constexpr int kPrefixRowsPerBlock = 128;  // query rows one MFMA tile workgroup 
 #define PA_TILE_WG_PER_CU 2
 #endif
 constexpr int kTileWorkgroupsPerCU = PA_TILE_WG_PER_CU;  // MFMA tile workgroups resident per CU
+#ifndef PA_TILE_FP8_WG_PER_CU
+#define PA_TILE_FP8_WG_PER_CU 2
+#endif
+constexpr int kTileFp8WorkgroupsPerCU = PA_TILE_FP8_WG_PER_CU;  // the same over fp8 pools (half the LDS)
 constexpr size_t kAlign = 256;
 
 // Error reporting: thread-local message + code.

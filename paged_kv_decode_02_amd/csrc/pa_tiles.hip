@@ -90,11 +90,21 @@ __device__ __forceinline__ void lds_barrier() {
 // a row that sees no key of the split gets o = 0, lse = -inf.
 constexpr int kTileThreads = 256;
 
-template <int KT, int NB>
+template <int KT, int NB, bool FP8 = false>
 struct TileLds {
   uint4 k[NB][KT * 16];         // [key][16 chunks of 16 bytes], chunk XOR-swizzled by tswz(key % 16)
   uint4 v[NB][KT * 16];         // the same layout
   int32_t pid[2][kPidWindow];   // page ids of the key range, two windows of 256 pages
+};
+// fp8 pools (e4m3fn codes, one float32 scale per (page, kv-head, slot)):
+// rows of 128 codes, and each key's K and V scale.
+template <int KT, int NB>
+struct TileLds<KT, NB, true> {
+  uint4 k[NB][KT * 8];          // [key][8 chunks of 16 codes], chunk XOR-swizzled by fswz(key)
+  uint4 v[NB][KT * 8];          // the same layout
+  float ks[NB][KT];             // K scale of each key of the tile
+  float vs[NB][KT];             // V scale of each key of the tile
+  int32_t pid[2][kPidWindow];
 };
 
 // Chunk swizzle of a K/V row in LDS: global chunk c of row r sits at LDS
@@ -103,6 +113,10 @@ struct TileLds {
 // that also spreads the transposed V reads, whose 4 rows x 2 chunks share 4
 // slots here, measured no faster.)
 __device__ __forceinline__ int tswz(int r) { return r & 15; }
+// Rows of 128 bytes (fp8 codes): rows r and r + 8 would sit on the same
+// banks of the 64-bank LDS; (r / 2) mod 8 spreads the 16 rows a K operand
+// read touches over distinct chunk slots (the fp8 stream wave's layout).
+__device__ __forceinline__ int fswz(int r) { return (r >> 1) & 7; }
 
 // What one tile workgroup computes.
 struct TileWork {
@@ -179,20 +193,34 @@ __device__ __forceinline__ bool tile_work(int b, int RC, int n_items, int Hkv, i
 }
 
 // KT keys per tile (32 or 64: 2 or 4 pages), NB buffers (NB - 1 tiles in
-// flight while one is used).
-template <int G, bool CHUNK, int KT, int NB>
-__device__ __forceinline__ void tile_body(const TileWork& tw, TileLds<KT, NB>& lds, const uint16_t* __restrict__ q,
-                                          const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool,
-                                          const int32_t* __restrict__ block_tables, int max_blocks, int Hkv,
-                                          int num_pages, float scale_log2, float* __restrict__ pre_o,
-                                          float* __restrict__ pre_lse) {
+// flight while one is used).  FP8: the pools hold e4m3fn codes with one
+// float32 scale per (page, kv-head, slot) (k_scales, v_scales); K operands
+// are read as codes and widened to bf16 pairs (exact), the V^T operand by
+// the transposed 8-bit read; each key's K scale multiplies its scores, its V
+// scale the probability P^T carries (the normaliser sums the plain
+// probabilities), as in the fp8 stream wave.
+template <int G, bool CHUNK, int KT, int NB, bool FP8 = false>
+__device__ __forceinline__ void tile_body(const TileWork& tw, TileLds<KT, NB, FP8>& lds,
+                                          const uint16_t* __restrict__ q, const void* __restrict__ k_pool,
+                                          const void* __restrict__ v_pool, const int32_t* __restrict__ block_tables,
+                                          int max_blocks, int Hkv, int num_pages, float scale_log2,
+                                          float* __restrict__ pre_o, float* __restrict__ pre_lse,
+                                          const float* __restrict__ k_scales = nullptr,
+                                          const float* __restrict__ v_scales = nullptr) {
   constexpr int D = 128;
-  constexpr int TILE = 16 * D * 2;      // bytes of one (page, kv-head) tile
-  constexpr int NKB = KT / 16;          // 16-key blocks of a tile
-  constexpr int NKS = KT / 32;          // 32-key steps of P.V
-  constexpr int LPW = KT / 16;          // 1 KB loads per wave per tile, each of K and V
+  constexpr int ROWB = FP8 ? D : 2 * D;  // bytes of one K/V row
+  constexpr int NCHR = ROWB / 16;        // 16-byte chunks of a row
+  constexpr int TILE = 16 * ROWB;        // bytes of one (page, kv-head) tile
+  constexpr int KPL = 64 / NCHR;         // keys one 1 KB load covers (4, fp8 8)
+  constexpr int LPP = 16 / KPL;          // 1 KB loads per page (4, fp8 2)
+  constexpr int NKB = KT / 16;           // 16-key blocks of a tile
+  constexpr int NKS = KT / 32;           // 32-key steps of P.V
+  constexpr int LPW = KT / KPL / 4;      // 1 KB loads per wave per tile, each of K and V
   constexpr int TPW = kPidWindow * 16 / KT;  // tiles per page-id window
   static_assert(KT == 32 || KT == 64, "tiles of 2 or 4 pages");
+  static_assert(!FP8 || KT == 64, "fp8 tiles of 64 keys (one 4-byte scale DMA per lane covers a tile)");
+  static_assert(LPW >= 1 && LPP % LPW == 0, "a wave's loads of a whole tile stay in one page");
+  auto swzf = [](int r) { return FP8 ? fswz(r) : tswz(r); };
   static_assert(NB >= 2 && NB <= 4 && TPW > NB, "buffer count");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -261,8 +289,8 @@ __device__ __forceinline__ void tile_body(const TileWork& tw, TileLds<KT, NB>& l
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int g = wv * LPW + i;
-    const int key = 4 * (g & 3) + lg;
-    dma_off[i] = key * (D * 2) + ((col ^ tswz(key)) * 16);
+    const int key = KPL * (g % LPP) + lane / NCHR;
+    dma_off[i] = key * ROWB + (((lane % NCHR) ^ swzf(key)) * 16);
   }
   // Window w of page ids: pages k_lo/16 + 256 w .. +256 of the table row
   // (entries past the row read its last entry), one dword DMA per lane.
@@ -278,32 +306,47 @@ __device__ __forceinline__ void tile_body(const TileWork& tw, TileLds<KT, NB>& l
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int g = wv * LPW + i;
-      const int page = g >> 2;
+      const int page = g / LPP;
       uint4* d = dst + g * 64;
-      if (nk >= 16 * page + 4 * (g & 3) + 4) {
-        // all 4 keys of the load exist: the page's tile base is scalar, the
-        // lane's row and chunk a fixed offset
+      if (nk >= 16 * page + KPL * (g % LPP) + KPL) {
+        // all KPL keys of the load exist: the page's tile base is scalar,
+        // the lane's row and chunk a fixed offset
         const int pid = __builtin_amdgcn_readfirstlane(min(max(pw[page], 0), num_pages - 1));
         dma16_sbase(pool + (static_cast<int64_t>(pid) * Hkv + kvh) * TILE, dma_off[i], lds_offset(d));
       } else {
-        const int key = 16 * page + 4 * (g & 3) + lg;
+        const int key = 16 * page + KPL * (g % LPP) + lane / NCHR;
         const int kc = min(key, nk - 1);
         const int pid = min(max(pw[kc >> 4], 0), num_pages - 1);
-        const int64_t off =
-            (static_cast<int64_t>(pid) * Hkv + kvh) * TILE + (kc & 15) * (D * 2) + ((col ^ tswz(key & 15)) * 16);
+        const int64_t off = (static_cast<int64_t>(pid) * Hkv + kvh) * TILE + (kc & 15) * ROWB +
+                            (((lane % NCHR) ^ swzf(key & 15)) * 16);
         dma16(pool + off, lds_offset(d));
       }
     }
   };
-  // A whole tile: all of this wave's loads fall in one page (loads 4 wv ..
-  // of 64 keys, or 2 wv .. of 32, cover keys 16 page ..), so its id is read
-  // from LDS once for the K and the V loads.  (Read per load, behind each
-  // DMA's memory clobber, it cost an LDS round trip per load.)
-  static_assert(4 % LPW == 0, "a wave's loads of a tile stay in one page");
+  // fp8: the K (wave 0) and V (wave 1) scales of tile t's keys, one dword
+  // per lane (lane j: key j; keys past the tile's end take the last valid
+  // key's scale, finite).
+  auto issue_scales = [&](int t, int b) {
+    if constexpr (FP8) {
+      if (wv < 2) {
+        const int kt = k_lo + t * KT;
+        const int nk = min(KT, k_hi - kt);
+        const int32_t* pw = &lds.pid[(t / TPW) & 1][(t * NKB) % kPidWindow];
+        const int j = min(lane, nk - 1);
+        const int pid = min(max(pw[j >> 4], 0), num_pages - 1);
+        const int64_t at = (static_cast<int64_t>(pid) * Hkv + kvh) * 16 + (j & 15);
+        dma4((wv == 0 ? k_scales : v_scales) + at, lds_offset(wv == 0 ? &lds.ks[b][0] : &lds.vs[b][0]));
+      }
+    }
+  };
+  // A whole tile: all of this wave's loads fall in one page (loads
+  // LPW wv .. cover keys 16 page ..), so its id is read from LDS once for
+  // the K and the V loads.  (Read per load, behind each DMA's memory
+  // clobber, it cost an LDS round trip per load.)
   auto issue_tile = [&](int t, int b) {
     if (k_hi - (k_lo + t * KT) >= KT) {
       const int32_t* pw = &lds.pid[(t / TPW) & 1][(t * NKB) % kPidWindow];
-      const int pid = min(max(__builtin_amdgcn_readfirstlane(pw[(wv * LPW) >> 2]), 0), num_pages - 1);
+      const int pid = min(max(__builtin_amdgcn_readfirstlane(pw[(wv * LPW) / LPP]), 0), num_pages - 1);
       const int64_t base = (static_cast<int64_t>(pid) * Hkv + kvh) * TILE;
 #pragma unroll
       for (int i = 0; i < LPW; ++i)
@@ -315,6 +358,7 @@ __device__ __forceinline__ void tile_body(const TileWork& tw, TileLds<KT, NB>& l
       issue_half(t, kbytes, lds.k[b]);
       issue_half(t, vbytes, lds.v[b]);
     }
+    issue_scales(t, b);
   };
   // Per-lane row and chunk of the transposed V reads: lane (group lg, j)
   // reads row key0 + j/4, columns d0 + 4(j%4) .. +3, with key0 = 32 ks + 4 lg
@@ -364,6 +408,7 @@ __device__ __forceinline__ void tile_body(const TileWork& tw, TileLds<KT, NB>& l
     }
     const uint4* kb_lds = lds.k[buf];
     const char* vb_lds = reinterpret_cast<const char*>(lds.v[buf]);
+    const int sbuf = buf;  // (fp8: the scale buffers of tile t)
     buf = buf + 1 == NB ? 0 : buf + 1;
 
     // S^T = K Q^T: s[kb][rb] holds keys 16 kb + 4 lg + i, query row
@@ -376,10 +421,32 @@ __device__ __forceinline__ void tile_body(const TileWork& tw, TileLds<KT, NB>& l
       for (int rb = 0; rb < 2; ++rb) s[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int cc = c * 4 + lg;
-        const u32x4 a = *(LdsU4*)(&kb_lds[key * 16 + (cc ^ tswz(col))]);
+        u32x4 a;
+        if constexpr (FP8) {
+          // codes 32 c + 8 lg .. +7 of the key: half of swizzled chunk 2 c + lg / 2
+          const int ch = (2 * c + (lg >> 1)) ^ fswz(key);
+          const u32x2 w8 = *(__attribute__((address_space(3))) const u32x2*)(
+              reinterpret_cast<const char*>(kb_lds) + key * ROWB + ch * 16 + (lg & 1) * 8);
+          a = u32x4{fp8x2_to_bf16x2<false>(w8.x), fp8x2_to_bf16x2<true>(w8.x), fp8x2_to_bf16x2<false>(w8.y),
+                    fp8x2_to_bf16x2<true>(w8.y)};
+        } else {
+          const int cc = c * 4 + lg;
+          a = *(LdsU4*)(&kb_lds[key * 16 + (cc ^ tswz(col))]);
+        }
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) s[kb][rb] = mfma16x16x32(a, qb[rb][c], s[kb][rb]);
+      }
+    }
+    if constexpr (FP8) {
+      // each key's K scale on its scores (keys 16 kb + 4 lg + i)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const f32x4 k4 = *(__attribute__((address_space(3))) const f32x4*)(&lds.ks[sbuf][kb * 16 + 4 * lg]);
+        const float kq[4] = {k4[0], k4[1], k4[2], k4[3]};
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[kb][rb][i] *= kq[i];
       }
     }
     // Keys are masked (by select) only in tiles that need it: the last,
@@ -435,6 +502,16 @@ __device__ __forceinline__ void tile_body(const TileWork& tw, TileLds<KT, NB>& l
             p[i] = fast_exp2(fmaf(s[2 * ks + e][rb][i], scale_log2, nref));
             lsum[rb] += p[i];
           }
+          if constexpr (FP8) {
+            // P^T carries p times the key's V scale (keys 32 ks + 16 e + 4 lg + i;
+            // a masked key's p is 0 and its scale finite)
+            const f32x4 v4 =
+                *(__attribute__((address_space(3))) const f32x4*)(&lds.vs[sbuf][(2 * ks + e) * 16 + 4 * lg]);
+            p[0] *= v4[0];
+            p[1] *= v4[1];
+            p[2] *= v4[2];
+            p[3] *= v4[3];
+          }
           pw[e][0] = bf16x2_rne(p[0], p[1]);
           pw[e][1] = bf16x2_rne(p[2], p[3]);
         }
@@ -449,14 +526,25 @@ __device__ __forceinline__ void tile_body(const TileWork& tw, TileLds<KT, NB>& l
     for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        u32x2 part[2];
+        u32x4 a;
+        if constexpr (FP8) {
+          // one transposed read of 8 rows: lanes 2 r, 2 r + 1 name row r of
+          // the block, the keys in P^T's order
+          const int r8 = col >> 1;
+          const int row = ks * 32 + (r8 >> 2) * 16 + lg * 4 + (r8 & 3);
+          const u32x2 w8 = lds_read_tr8(vb_lds + row * ROWB + (db ^ fswz(row)) * 16 + (col & 1) * 8);
+          a = u32x4{fp8x2_to_bf16x2<false>(w8.x), fp8x2_to_bf16x2<true>(w8.x), fp8x2_to_bf16x2<false>(w8.y),
+                    fp8x2_to_bf16x2<true>(w8.y)};
+        } else {
+          u32x2 part[2];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int row = ks * 32 + e * 16 + lg * 4 + tr_r;
-          const int ch = (db * 2 + (tr_c >> 1)) ^ tswz(row & 15);
-          part[e] = lds_read_tr16(vb_lds + row * (D * 2) + ch * 16 + (tr_c & 1) * 8);
+          for (int e = 0; e < 2; ++e) {
+            const int row = ks * 32 + e * 16 + lg * 4 + tr_r;
+            const int ch = (db * 2 + (tr_c >> 1)) ^ tswz(row & 15);
+            part[e] = lds_read_tr16(vb_lds + row * (D * 2) + ch * 16 + (tr_c & 1) * 8);
+          }
+          a = u32x4{part[0].x, part[0].y, part[1].x, part[1].y};
         }
-        const u32x4 a = u32x4{part[0].x, part[0].y, part[1].x, part[1].y};
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) o[db][rb] = mfma16x16x32(a, pb[ks][rb], o[db][rb]);
       }
@@ -491,20 +579,24 @@ __device__ __forceinline__ void tile_body(const TileWork& tw, TileLds<KT, NB>& l
 constexpr int kTK = PA_TILE_KEYS;
 constexpr int kTB = PA_TILE_BUFS;
 
-template <int G, bool CHUNK>
-__global__ __launch_bounds__(kTileThreads, kTileWorkgroupsPerCU) void tile_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool,
+// FP8: pools of e4m3fn codes with their row scales (built for the shared
+// prefix, whose tiles hold 64 keys).
+template <int G, bool CHUNK, bool FP8 = false>
+__global__ __launch_bounds__(kTileThreads, FP8 ? kTileFp8WorkgroupsPerCU : kTileWorkgroupsPerCU) void tile_kernel(
+    const uint16_t* __restrict__ q, const void* __restrict__ k_pool, const void* __restrict__ v_pool,
     const int32_t* __restrict__ block_tables, int max_blocks, const int32_t* __restrict__ ctx,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ group_off, const int32_t* __restrict__ prefix_lens,
     ChunkList chunks, int RC, int nks, int kps, int Hkv, int n_items, int num_pages, float scale_log2,
-    int32_t* __restrict__ begin_pages, float* __restrict__ pre_o, float* __restrict__ pre_lse) {
-  __shared__ TileLds<kTK, kTB> lds;
+    int32_t* __restrict__ begin_pages, float* __restrict__ pre_o, float* __restrict__ pre_lse,
+    const float* __restrict__ k_scales, const float* __restrict__ v_scales) {
+  static_assert(!(FP8 && CHUNK), "fp8 tiles are built for the shared prefix");
+  __shared__ TileLds<kTK, kTB, FP8> lds;
   TileWork tw;
   if (!tile_work<G, CHUNK>(blockIdx.x, RC, n_items, Hkv, nks, kps, chunks, ctx, cu_q, group_off, prefix_lens,
                            begin_pages, tw))
     return;  // uniform over the workgroup
-  tile_body<G, CHUNK, kTK, kTB>(tw, lds, q, k_pool, v_pool, block_tables, max_blocks, Hkv, num_pages, scale_log2, pre_o,
-                      pre_lse);
+  tile_body<G, CHUNK, kTK, kTB, FP8>(tw, lds, q, k_pool, v_pool, block_tables, max_blocks, Hkv, num_pages, scale_log2,
+                                     pre_o, pre_lse, k_scales, v_scales);
 }
 
 // Merge the key splits of one chunk token (all G heads of a kv-head) and
@@ -765,11 +857,18 @@ int launch_cascade_g(const CascadeLaunch& c) {
   const int n_items = c.num_groups * a.num_kv_heads * c.nks;
   profile_before(a.stream);
   const unsigned blocks = static_cast<unsigned>((n_items + 7) / 8 * 8 * c.row_chunks);
-  hipLaunchKernelGGL((tile_kernel<G, false>), dim3(blocks), dim3(kTileThreads), 0, st, static_cast<const uint16_t*>(a.q),
-                     static_cast<const uint16_t*>(a.k_pool), static_cast<const uint16_t*>(a.v_pool),
-                     a.block_tables, a.max_blocks, a.context_lens, nullptr, c.group_offsets, c.prefix_lens, none,
-                     c.row_chunks, c.nks, c.kps, a.num_kv_heads, n_items, static_cast<int>(a.num_pages), scale_log2,
-                     begin_pages, pre_o, pre_lse);
+  if (a.kv_fp8)
+    hipLaunchKernelGGL((tile_kernel<G, false, true>), dim3(blocks), dim3(kTileThreads), 0, st,
+                       static_cast<const uint16_t*>(a.q), a.k_pool, a.v_pool, a.block_tables, a.max_blocks,
+                       a.context_lens, nullptr, c.group_offsets, c.prefix_lens, none, c.row_chunks, c.nks, c.kps,
+                       a.num_kv_heads, n_items, static_cast<int>(a.num_pages), scale_log2, begin_pages, pre_o,
+                       pre_lse, a.k_scales, a.v_scales);
+  else
+    hipLaunchKernelGGL((tile_kernel<G, false, false>), dim3(blocks), dim3(kTileThreads), 0, st,
+                       static_cast<const uint16_t*>(a.q), a.k_pool, a.v_pool, a.block_tables, a.max_blocks,
+                       a.context_lens, nullptr, c.group_offsets, c.prefix_lens, none, c.row_chunks, c.nks, c.kps,
+                       a.num_kv_heads, n_items, static_cast<int>(a.num_pages), scale_log2, begin_pages, pre_o,
+                       pre_lse, nullptr, nullptr);
   profile_after(a.stream);
   if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_prefix_cascade: prefix kernel launch failed");
   // Suffix: the stream decode kernel over the pages after each prefix.
@@ -875,7 +974,7 @@ int launch_mixed_g(const MixedLaunch& mx) {
                            static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
                            static_cast<const uint16_t*>(a.v_pool), a.block_tables, a.max_blocks, a.context_lens,
                            mx.cu_q_lens, nullptr, nullptr, cl, mx.row_chunks, 0, 0, a.num_kv_heads, n_items,
-                           static_cast<int>(a.num_pages), scale_log2, nullptr, pre_o, pre_lse);
+                           static_cast<int>(a.num_pages), scale_log2, nullptr, pre_o, pre_lse, nullptr, nullptr);
         if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_mixed_chunk: chunk kernel launch failed");
       }
       profile_after(a.stream);

@@ -41,6 +41,7 @@ EXPORTS = (
     "pa_decode_multi_fp8",
     "pa_prefix_cascade_workspace_size",
     "pa_prefix_cascade",
+    "pa_prefix_cascade_fp8",
     "pa_mixed_chunk_workspace_size",
     "pa_mixed_chunk",
     "pa_kv_append",
@@ -109,6 +110,10 @@ def load(path: Optional[str] = None):
     lib.pa_prefix_cascade.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_vp, c_vp,
                                       c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i64, ctypes.c_float, ctypes.c_int,
                                       c_vp, c_sz, c_vp]
+    lib.pa_prefix_cascade_fp8.restype = ctypes.c_int
+    lib.pa_prefix_cascade_fp8.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32,
+                                          c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i64,
+                                          ctypes.c_float, c_vp, c_sz, c_vp]
     lib.pa_mixed_chunk_workspace_size.restype = c_sz
     lib.pa_mixed_chunk_workspace_size.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32, c_i64]
     lib.pa_mixed_chunk.restype = ctypes.c_int
@@ -499,6 +504,50 @@ def prefix_cascade(out, q, k_pool, v_pool, block_tables, context_lens, context_l
         _dev(group_seq_offsets, "group_seq_offsets", torch.int32), goh.ctypes.data,
         _dev(prefix_lens, "prefix_lens", torch.int32), plh.ctypes.data,
         Hkv, Hq // Hkv, D, BS, NP, float(scale), _dtype_code(q),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream_ptr(stream),
+    )
+    return _check(rc)
+
+
+def prefix_cascade_fp8(out, q, k_pool, v_pool, k_scales, v_scales, block_tables, context_lens, context_lens_host,
+                       group_seq_offsets, group_seq_offsets_host, prefix_lens, prefix_lens_host, scale, workspace,
+                       lse_out=None, stream=None):
+    """pa_prefix_cascade_fp8 on torch tensors: the groups of
+    :func:`prefix_cascade`, the pools and scales of :func:`decode_fp8`."""
+    import torch
+
+    S, Hq, D = q.shape
+    NP, Hkv, BS, D2 = k_pool.shape
+    if q.dtype != torch.bfloat16 or tuple(out.shape) != (S, Hq, D) or out.dtype != torch.bfloat16:
+        raise ValueError("q and out must be bfloat16 [S, Hq, D]")
+    codes = (torch.uint8, torch.float8_e4m3fn)
+    if tuple(v_pool.shape) != tuple(k_pool.shape) or k_pool.dtype not in codes or v_pool.dtype not in codes:
+        raise ValueError("k_pool and v_pool must be [NP, Hkv, BS, D] uint8 / float8_e4m3fn")
+    for t, nm in ((k_scales, "k_scales"), (v_scales, "v_scales")):
+        if tuple(t.shape) != (NP, Hkv, BS) or t.dtype != torch.float32:
+            raise ValueError(f"{nm} must be float32 [NP, Hkv, BS]")
+    if D2 != D or Hq % Hkv:
+        raise ValueError("head_dim mismatch or q heads not a multiple of kv heads")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_tables / context_lens must have one row per sequence")
+    ch = _host_i32(context_lens_host, "context_lens_host")
+    goh = _host_i32(group_seq_offsets_host, "group_seq_offsets_host")
+    plh = _host_i32(prefix_lens_host, "prefix_lens_host")
+    NG = plh.size
+    if ch.size != S or goh.size != NG + 1 or group_seq_offsets.numel() != NG + 1 or prefix_lens.numel() != NG:
+        raise ValueError("group arrays must be [NG+1] offsets and [NG] prefix lengths")
+    if lse_out is not None and tuple(lse_out.shape) != (S, Hq):
+        raise ValueError("lse_out must be [S, Hq]")
+    rc = load().pa_prefix_cascade_fp8(
+        _dev(out, "out"),
+        _dev(lse_out, "lse_out", torch.float32) if lse_out is not None else None,
+        _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(k_scales, "k_scales", torch.float32), _dev(v_scales, "v_scales", torch.float32),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), ch.ctypes.data, S, NG,
+        _dev(group_seq_offsets, "group_seq_offsets", torch.int32), goh.ctypes.data,
+        _dev(prefix_lens, "prefix_lens", torch.int32), plh.ctypes.data,
+        Hkv, Hq // Hkv, D, BS, NP, float(scale),
         _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream_ptr(stream),
     )
     return _check(rc)

@@ -55,21 +55,28 @@ def decode_flops(context_lens, num_q_heads, head_dim) -> int:
 
 
 def cascade_bytes(context_lens, group_seq_offsets, prefix_lens, num_q_heads, num_kv_heads, head_dim, elem_bytes,
-                  block_size=16) -> dict:
+                  block_size=16, kv_fp8=False) -> dict:
     """Shared-prefix decode: each group's prefix K/V read once, every
-    member's suffix once, plus q, out and table entries."""
+    member's suffix once, plus q, out and table entries.  With kv_fp8 the
+    K/V elements are one-byte codes and each K and V row (token, kv-head)
+    adds a float32 scale; q and out keep elem_bytes."""
     ctx = np.asarray(context_lens, dtype=np.int64)
     offs = np.asarray(group_seq_offsets, dtype=np.int64)
     pl = np.asarray(prefix_lens, dtype=np.int64)
     per_seq_prefix = np.repeat(pl, np.diff(offs))
     prefix_tokens = int(pl.sum())
     suffix_tokens = int((ctx - per_seq_prefix).sum())
-    kv = kv_cache_bytes(1, num_kv_heads, head_dim, prefix_tokens + suffix_tokens, elem_bytes)
+
+    def kv_of(tokens):
+        if kv_fp8:
+            return kv_cache_bytes(1, num_kv_heads, head_dim, tokens, 1) + 2 * num_kv_heads * tokens * 4
+        return kv_cache_bytes(1, num_kv_heads, head_dim, tokens, elem_bytes)
+
+    kv = kv_of(prefix_tokens + suffix_tokens)
     S = ctx.size
     qo = 2 * S * num_q_heads * head_dim * elem_bytes
     tables = 4 * int(((ctx + block_size - 1) // block_size).sum()) + 4 * S
-    return {"kv": kv, "q_out": qo, "tables": tables, "total": kv + qo + tables,
-            "prefix_kv": kv_cache_bytes(1, num_kv_heads, head_dim, prefix_tokens, elem_bytes)}
+    return {"kv": kv, "q_out": qo, "tables": tables, "total": kv + qo + tables, "prefix_kv": kv_of(prefix_tokens)}
 
 
 def prefix_flops(group_seq_offsets, prefix_lens, num_q_heads, head_dim) -> int:

@@ -453,3 +453,70 @@ def test_noalloc_without_a_device_returns_an_error():
     rc = lib.pa_decode_noalloc(FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, FAKE, ctx, 2, 2, 4, 128, 16, 10, 0.1,
                                pa.PA_BF16, 0, None)
     assert rc == pa.PA_EHIP and "device" in pa.last_error()
+
+
+def call_cascade(lib, fp8=False, **kw):
+    """Two groups of two sequences (context 40 and 50 / 30 and 60), a 16-row
+    prefix each, on fake device pointers that validation never reaches."""
+    args = dict(out=FAKE, lse=None, q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, bt=FAKE, mb=4, ctx=FAKE,
+                ctx_host=np.array([40, 50, 30, 60], dtype=np.int32), S=4, ngroups=2, go=FAKE,
+                go_host=np.array([0, 2, 4], dtype=np.int32), pl=FAKE, pl_host=np.array([16, 16], dtype=np.int32),
+                Hkv=2, G=4, D=128, BS=16, NP=10, scale=0.1, dtype=pa.PA_BF16, ws=ctypes.c_void_p(0x100000),
+                ws_bytes=1 << 24, stream=None)
+    args.update(kw)
+    head = (args["out"], args["lse"], args["q"], args["k"], args["v"])
+    if fp8:
+        head += (args["ks"], args["vs"])
+    tail = (args["bt"], args["mb"], args["ctx"], args["ctx_host"].ctypes.data, args["S"], args["ngroups"], args["go"],
+            args["go_host"].ctypes.data, args["pl"], args["pl_host"].ctypes.data, args["Hkv"], args["G"], args["D"],
+            args["BS"], args["NP"], args["scale"])
+    if fp8:
+        return lib.pa_prefix_cascade_fp8(*head, *tail, args["ws"], args["ws_bytes"], args["stream"])
+    return lib.pa_prefix_cascade(*head, *tail, args["dtype"], args["ws"], args["ws_bytes"], args["stream"])
+
+
+CASCADE_BAD = [
+    (dict(q=None), pa.PA_EINVAL),
+    (dict(S=-1), pa.PA_EINVAL),
+    (dict(ngroups=0), pa.PA_EINVAL),
+    (dict(go=None), pa.PA_EINVAL),
+    (dict(D=64), pa.PA_EUNSUPPORTED),
+    (dict(G=3), pa.PA_EUNSUPPORTED),
+    (dict(ws=ctypes.c_void_p(0x100010)), pa.PA_EINVAL),  # misaligned
+    (dict(go_host=np.array([0, 2, 3], dtype=np.int32)), pa.PA_EINVAL),  # groups end before num_seqs
+    (dict(go_host=np.array([0, 3, 2], dtype=np.int32), ngroups=2), pa.PA_EINVAL),  # offsets decrease
+    (dict(pl_host=np.array([16, 20], dtype=np.int32)), pa.PA_EINVAL),  # not whole pages
+    (dict(pl_host=np.array([48, 16], dtype=np.int32)), pa.PA_EINVAL),  # prefix not shorter than a member
+    (dict(ctx_host=np.array([40, 50, 0, 60], dtype=np.int32)), pa.PA_EINVAL),
+    (dict(ctx_host=np.array([40, 50, 30, 65], dtype=np.int32)), pa.PA_EINVAL),  # beyond 4 pages
+    (dict(ws_bytes=64), pa.PA_EWORKSPACE),
+]
+
+
+@pytest.mark.parametrize("kw,code", CASCADE_BAD + [(dict(dtype=pa.PA_F32), pa.PA_EUNSUPPORTED)])
+def test_prefix_cascade_rejects_bad_arguments(kw, code):
+    lib = pa.load()
+    assert call_cascade(lib, **kw) == code
+    assert lib.pa_last_error().decode().startswith("pa_prefix_cascade")
+
+
+@pytest.mark.parametrize("kw,code", CASCADE_BAD + [(dict(ks=None), pa.PA_EINVAL), (dict(vs=None), pa.PA_EINVAL)])
+def test_prefix_cascade_fp8_rejects_bad_arguments(kw, code):
+    lib = pa.load()
+    assert call_cascade(lib, fp8=True, **kw) == code
+    assert lib.pa_last_error().decode().startswith("pa_prefix_cascade_fp8")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_prefix_cascade_zero_sequences_is_a_no_op(fp8):
+    lib = pa.load()
+    assert call_cascade(lib, fp8=fp8, S=0, q=None, out=None, ks=None) == pa.PA_OK
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_prefix_cascade_valid_arguments_reach_the_launch(fp8):
+    """Arguments that pass every check reach the kernel launch, which the
+    host-only build answers with its no-device error."""
+    lib = pa.load()
+    rc = call_cascade(lib, fp8=fp8)
+    assert rc not in (pa.PA_OK, pa.PA_EINVAL, pa.PA_EWORKSPACE, pa.PA_EUNSUPPORTED), lib.pa_last_error().decode()

@@ -450,6 +450,14 @@ def _longtail_window4096(seed=0):
                          head_dim=base.head_dim, dtype=base.dtype, seed=seed, name="longtail_window4096")
 
 
+def _shared_prefix_fp8(seed=0):
+    """The shared-prefix batch over an fp8 (e4m3fn) cache."""
+    lay = _shared_prefix(seed)
+    lay.name = "shared_prefix_fp8"
+    lay.kv_dtype = "fp8"
+    return lay
+
+
 def _llama8b_multitoken4_window1024(seed=0):
     """The 4-token decode step of the Llama-shaped batch over a 1024-token
     sliding window: token i of a sequence with L rows sees the rows
@@ -491,6 +499,7 @@ WORKLOADS = {
     "llama8b_prefill_append_fp8": _llama8b_prefill_append_fp8,
     "longtail_window4096": _longtail_window4096,
     "llama8b_multitoken4_window1024": _llama8b_multitoken4_window1024,
+    "shared_prefix_fp8": _shared_prefix_fp8,
     "llama8b_prefill_append": _llama8b_prefill_append,
     "llama8b_decode": _llama8b_decode,
     "llama8b_decode_fp8": _llama8b_decode_fp8,
