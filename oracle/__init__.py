@@ -32,6 +32,7 @@ from .fp8 import (  # noqa: F401
     dequantize,
     e4m3_to_f64,
     kv_append_fp8,
+    mixed_chunk_fp8,
     prefix_cascade_fp8,
     quantize_rows,
 )

@@ -43,6 +43,12 @@ Pins (tests/test_fp8_pins.py):
   scales it equals the pinned chunk oracle (``oracle.mixed_chunk``) on the
   read-back bf16 values bit for bit; brute force with Python loops; a causal
   edge one row off and tokens read in the wrong order are caught;
+* a mixed batch (``mixed_chunk_fp8``: prefill chunks and decode tokens,
+  q_lens per segment): all-ones q_lens equal ``decode_fp8`` and a uniform
+  q_len equals ``decode_multi_fp8`` bit for bit; with power-of-two scales a
+  ragged batch equals the pinned chunk oracle on the read-back bf16 values
+  bit for bit; brute force with Python loops; the causal mistakes above and
+  segments read at the wrong offsets in q are caught;
 * shared-prefix decode (``prefix_cascade_fp8``: the group check, then
   ``decode_fp8``): equal to the log-sum-exp merge of the fp8 attention over
   the prefix rows alone and over the suffix rows alone; a broken group is
@@ -229,6 +235,58 @@ def decode_multi_fp8(q, k_codes, k_scales, v_codes, v_scales, block_tables, cont
             V = _gather_fp8(v_codes, v_scales, block_tables[s], g, L, block_size)
             for i in range(n):
                 row = s * n + i
+                qs = stored_to_f64(q[row], q_dtype)
+                vis = _visible(L, n, i)
+                for h in range(g * G, (g + 1) * G):
+                    out[row, h], lse[row, h] = attend(qs[h], K[:vis], V[:vis], sc)
+    return out, lse
+
+
+def _segment_starts(q_lens) -> np.ndarray:
+    """First row in q of each segment: the segments' tokens are stored one
+    segment after another, so segment s starts at q_lens[0] + .. + q_lens[s-1]."""
+    ql = np.asarray(q_lens, dtype=np.int64)
+    starts = np.zeros(ql.size + 1, dtype=np.int64)
+    np.cumsum(ql, out=starts[1:])
+    return starts
+
+
+def mixed_chunk_fp8(q, k_codes, k_scales, v_codes, v_scales, block_tables, context_lens, q_lens, scale,
+                    num_kv_heads, block_size, q_dtype="bf16", seqs=None):
+    """Prefill chunks and decode tokens in one batch over an fp8 cache: the
+    piggybacked batch of the SwiftLLM page (section 3.3) with K and V rows
+    read back from e4m3fn codes and their scales (tokenspeed 딥다이브 section
+    6-4).  Segment s has q_lens[s] new tokens, its last rows; token i of a
+    segment with L rows and n new tokens sees rows 0 .. L - n + i (a decode
+    token, n = 1, sees all L).
+
+    ``q`` [sum(q_lens), Hq, D] stored values of ``q_dtype``, segment after
+    segment; pools and scales as :func:`decode_fp8`.  Returns out and lse of
+    q's leading shape in float64; segments not in ``seqs`` stay NaN.
+    """
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    ql = np.asarray(q_lens, dtype=np.int64)
+    T, Hq, D = q.shape
+    if ql.size != ctx.size or (ql < 1).any():
+        raise ValueError("one q_len >= 1 per segment")
+    starts = _segment_starts(ql)
+    if T != int(ql.sum()):
+        raise ValueError("q must hold sum(q_lens) tokens")
+    if Hq % num_kv_heads:
+        raise ValueError("q heads must be a multiple of kv heads")
+    G = Hq // num_kv_heads
+    sc = float(np.float32(scale))
+    out = np.full((T, Hq, D), np.nan, dtype=np.float64)
+    lse = np.full((T, Hq), np.nan, dtype=np.float64)
+    for s in (range(ctx.size) if seqs is None else seqs):
+        L, n = int(ctx[s]), int(ql[s])
+        if L < n:
+            raise ValueError(f"segment {s}: fewer rows than new tokens")
+        for g in range(num_kv_heads):
+            K = _gather_fp8(k_codes, k_scales, block_tables[s], g, L, block_size)
+            V = _gather_fp8(v_codes, v_scales, block_tables[s], g, L, block_size)
+            for i in range(n):
+                row = int(starts[s]) + i
                 qs = stored_to_f64(q[row], q_dtype)
                 vis = _visible(L, n, i)
                 for h in range(g * G, (g + 1) * G):

@@ -266,8 +266,73 @@ def pin_multi_token_bruteforce():
     return fails
 
 
+def pin_mixed_reductions():
+    """A mixed batch (q_lens per segment): all ones is decode_fp8 and a
+    uniform q_len is decode_multi_fp8, bit for bit; with power-of-two scales
+    a ragged batch (decode tokens and chunks of 3 to 16 tokens) equals the
+    (pinned) chunk oracle over the read-back bf16 values, bit for bit."""
+    rng = np.random.default_rng(31)
+    fails = []
+    ctx = [3, 16, 17, 40, 70]
+    lay, q1, kc, ks, vc, vs = fp8_cache(rng, ctx, hkv=2, d=16, block_size=16, pow2_scales=True)
+    bt, cl = lay.block_tables, lay.context_lens
+    a = f8.mixed_chunk_fp8(q1, kc, ks, vc, vs, bt, cl, [1] * len(ctx), 0.25, 2, 16)
+    b = f8.decode_fp8(q1, kc, ks, vc, vs, bt, cl, 0.25, 2, 16)
+    if not (np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])):
+        fails.append("all-ones q_lens differ from decode_fp8")
+    q3 = multi_q(rng, ctx, 3, 4, 16)
+    a = f8.mixed_chunk_fp8(q3, kc, ks, vc, vs, bt, cl, [3] * len(ctx), 0.25, 2, 16)
+    b = f8.decode_multi_fp8(q3, kc, ks, vc, vs, bt, cl, 3, 0.25, 2, 16)
+    if not (np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])):
+        fails.append("a uniform q_len differs from decode_multi_fp8")
+    kb = bf16_bits_from_f32(np.nan_to_num(f8.dequantize(kc, ks)).astype(np.float32))
+    vb = bf16_bits_from_f32(np.nan_to_num(f8.dequantize(vc, vs)).astype(np.float32))
+    ql = [1, 3, 1, 16, 5]
+    q = bf16_bits_from_f32(rng.standard_normal((sum(ql), 4, 16)).astype(np.float32))
+    out, lse = f8.mixed_chunk_fp8(q, kc, ks, vc, vs, bt, cl, ql, 0.25, 2, 16)
+    ro, rl = oracle.mixed_chunk(q, kb, vb, bt, cl, ql, 0.25, 2, 16, "bf16")
+    if not (np.array_equal(out, ro) and np.array_equal(lse, rl)):
+        fails.append("ragged q_lens: differs from the chunk oracle on read-back values")
+    return fails
+
+
+def pin_mixed_bruteforce():
+    """Tiny ragged batch, Python loops: segment s's tokens follow those of
+    the segments before it in q; token i sees rows 0 .. L - n + i."""
+    rng = np.random.default_rng(12)
+    ctx, ql = [2, 17, 20], [2, 1, 3]
+    hkv, d, bs = 1, 4, 16
+    lay, _, kc, ks, vc, vs = fp8_cache(rng, ctx, hkv=hkv, d=d, block_size=bs, pow2_scales=False)
+    q = bf16_bits_from_f32(rng.standard_normal((sum(ql), 2, d)).astype(np.float32))
+    out, lse = f8.mixed_chunk_fp8(q, kc, ks, vc, vs, lay.block_tables, lay.context_lens, ql, 0.5, hkv, bs)
+    cv = torch_code_values()
+    qf = oracle.stored_to_f64(q, "bf16")
+    sc = float(np.float32(0.5))
+    fails = []
+    row = 0
+    for s, L in enumerate(ctx):
+        n = ql[s]
+        for i in range(n):
+            for h in range(2):
+                xs, vrows = [], []
+                for t in range(L - n + i + 1):
+                    p, r = int(lay.block_tables[s, t // bs]), t % bs
+                    k = [cv[kc[p, 0, r, j]] * float(ks[p, 0, r]) for j in range(d)]
+                    vrows.append([cv[vc[p, 0, r, j]] * float(vs[p, 0, r]) for j in range(d)])
+                    xs.append(sc * sum(qf[row, h, j] * k[j] for j in range(d)))
+                m = max(xs)
+                w = [math.exp(x - m) for x in xs]
+                z = sum(w)
+                o = [sum(w[t] * vrows[t][j] for t in range(len(w))) / z for j in range(d)]
+                if np.max(np.abs(np.array(o) - out[row, h])) > 1e-12 or abs(m + math.log(z) - lse[row, h]) > 1e-12:
+                    fails.append(f"segment {s} token {i} head {h} differs from brute force")
+            row += 1
+    return fails
+
+
 ALL_PINS = [pin_code_table, pin_closed_forms, pin_quantizer_vs_torch, pin_quantizer_properties,
-            pin_attention_vs_bf16_oracle, pin_bruteforce, pin_multi_token_reductions, pin_multi_token_bruteforce]
+            pin_attention_vs_bf16_oracle, pin_bruteforce, pin_multi_token_reductions, pin_multi_token_bruteforce,
+            pin_mixed_reductions, pin_mixed_bruteforce]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
@@ -313,7 +378,16 @@ PLANTED = {
 
 
 def _run_pins():
-    return [p.__name__ for p in ALL_PINS if p()]
+    """Names of the pins that fail (a pin that raises counts as failing)."""
+    failed = []
+    for p in ALL_PINS:
+        try:
+            bad = p()
+        except (IndexError, ValueError) as e:
+            bad = [f"raised {e!r}"]
+        if bad:
+            failed.append(p.__name__)
+    return failed
 
 
 @pytest.mark.parametrize("name", sorted(PLANTED))
@@ -394,6 +468,14 @@ def test_kv_append_fp8_bruteforce_and_read_back():
 def test_planted_multi_token_mistake_is_caught(monkeypatch, name, bad):
     monkeypatch.setattr(f8, "_visible", bad)
     assert _run_pins(), f"no pin noticed: {name}"
+
+
+def test_planted_segment_offsets_are_caught(monkeypatch):
+    """Segments read from q at the offsets the q_lens would have in ascending
+    order (every row index stays in range, so a pin must notice the values)."""
+    monkeypatch.setattr(f8, "_segment_starts",
+                        lambda ql: np.concatenate([[0], np.cumsum(np.sort(np.asarray(ql, dtype=np.int64)))]))
+    assert _run_pins(), "no pin noticed segments read at the wrong offsets"
 
 
 # ---------------------------------------------------------------------------
