@@ -346,8 +346,12 @@ def main():
                           dtype=torch.uint8, device=dev)
 
         def mixed_step():
-            pa.mixed_chunk(out, q, k, v, bt, cu, lay.cu_q_lens, ctx, lay.context_lens, lay.scale, mws,
-                           stream=stream)
+            if fp8:
+                pa.mixed_chunk_fp8(out, q, k, v, ks, vs, bt, cu, lay.cu_q_lens, ctx, lay.context_lens, lay.scale, mws,
+                                   stream=stream)
+            else:
+                pa.mixed_chunk(out, q, k, v, bt, cu, lay.cu_q_lens, ctx, lay.context_lens, lay.scale, mws,
+                               stream=stream)
 
         step = mixed_step
         if multi:
@@ -504,13 +508,14 @@ def main():
             f", {lay.window}-token window)" if lay.window is not None else ")")
         roof = hbm_roof(label, nb["total"], float(sum(kern_avg)), measured_traffic(args.workload))
         extra = {"tokens_per_step": int(T), "fold_passes": pairs}
-        if not fp8 and lay.window is None:  # (the chunk path reads bf16 / float32 pools, no window)
+        if lay.window is None:  # (the chunk path takes no window)
             extra["mixed_chunk_same_batch_ms"] = round(float(np.median(cold(mixed_step, args.steps)[0])), 5)
     elif mixed:
         nb = roofline.mixed_bytes(lay.context_lens, lay.q_lens, lay.num_q_heads, lay.num_kv_heads, D,
-                                  lay.elem_bytes)
+                                  2 if fp8 else lay.elem_bytes, kv_fp8=fp8)
         flops = roofline.chunk_flops(lay.context_lens, lay.q_lens, lay.num_q_heads, D)
-        chunk_roof = mfma_roof("tile_kernel (prefill chunks)", flops, kern_avg[0])
+        pools = " (fp8 pools)" if fp8 else ""
+        chunk_roof = mfma_roof("tile_kernel (prefill chunks)" + pools, flops, kern_avg[0])
         extra = {"chunk_gflop": round(flops / 1e9, 3), "tokens_per_step": int(T)}
         roof = chunk_roof
         if has_dec and len(kern_avg) == 1:
@@ -518,21 +523,26 @@ def main():
             # view (all K/V bytes of the step) and its matrix view (the chunk
             # flops) over the same kernel time
             traffic = measured_traffic("mixed:" + args.workload, TILE_SOURCES)
-            roof = hbm_roof("mixed_kernel (prefill chunks + decode tokens, one launch)", nb["total"], kern_avg[0],
-                            traffic)
-            extra["mixed_kernel_mfma"] = mfma_roof("mixed_kernel (chunk flops)", flops, kern_avg[0], traffic)
+            roof = hbm_roof("mixed_kernel (prefill chunks + decode tokens, one launch)" + pools, nb["total"],
+                            kern_avg[0], traffic)
+            extra["mixed_kernel_mfma"] = mfma_roof("mixed_kernel (chunk flops)" + pools, flops, kern_avg[0], traffic)
         elif has_dec:
             dec = lay.q_lens == 1
-            dbytes = roofline.decode_bytes(lay.context_lens[dec], lay.num_q_heads, lay.num_kv_heads, D,
-                                           lay.elem_bytes)["total"]
-            dec_roof = hbm_roof(f"{stream_kernel(lay.gqa_ratio)} (decode tokens)", dbytes, kern_avg[1], None)
+            if fp8:
+                dbytes = roofline.decode_fp8_bytes(lay.context_lens[dec], lay.num_q_heads, lay.num_kv_heads,
+                                                   D)["total"]
+            else:
+                dbytes = roofline.decode_bytes(lay.context_lens[dec], lay.num_q_heads, lay.num_kv_heads, D,
+                                               lay.elem_bytes)["total"]
+            dec_roof = hbm_roof(f"{stream_kernel(lay.gqa_ratio)} (decode tokens)" + pools, dbytes, kern_avg[1], None)
             # the dominant kernel is the one that takes longer
             roof, other = (chunk_roof, dec_roof) if kern_avg[0] >= kern_avg[1] else (dec_roof, chunk_roof)
             extra["other_kernel_roofline"] = other
         else:
             # no single-token segments: the chunk kernel is the whole step;
             # its K/V traffic, for the HBM view of the same launch
-            extra["chunk_kernel_hbm"] = hbm_roof("tile_kernel (prefill chunks)", nb["total"], kern_avg[0], None)
+            extra["chunk_kernel_hbm"] = hbm_roof("tile_kernel (prefill chunks)" + pools, nb["total"], kern_avg[0],
+                                                 None)
     elif lay.window is not None:
         # the rows each query sees: the last min(L, window) of its sequence
         nb = roofline.decode_bytes(np.minimum(lay.context_lens, lay.window), lay.num_q_heads, lay.num_kv_heads, D,

@@ -401,6 +401,34 @@ int pa_mixed_chunk(void* out,                      /* device [T, Hq, D] dtype */
                    size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Mixed batch over an fp8 cache: pa_mixed_chunk's segments, causal rule and
+ * result over pa_decode_fp8's pools -- e4m3fn codes with one float32 scale
+ * per (page, kv-head, slot) for K and one for V (tokenspeed 딥다이브 section
+ * 6-4); q and out bf16.  The chunk tiles read 64-key code tiles, widen them
+ * exactly to bf16 for the matrix cores and apply each key's K scale to its
+ * scores and its V scale to the probability P.V takes; decode tokens run on
+ * the fp8 stream wave, in the same launch as the chunks with 4 or more
+ * q-heads per kv-head.  A batch without chunks takes pa_decode_fp8's plan.
+ * Workspace: pa_mixed_chunk_workspace_size.  Built for head_dim 128,
+ * gqa_ratio 1, 2, 4, 8, 16.  Errors as pa_mixed_chunk, plus PA_EINVAL for a
+ * NULL scale pointer.
+ * ------------------------------------------------------------------------- */
+int pa_mixed_chunk_fp8(void* out,                      /* device [T, Hq, D] bf16 */
+                       float* lse_out,                 /* device [T, Hq] or NULL */
+                       const void* q,                  /* device [T, Hq, D] bf16 */
+                       const void* k_pool, const void* v_pool, /* device [NP, Hkv, BS, D] e4m3fn codes */
+                       const float* k_scales, const float* v_scales, /* device [NP, Hkv, BS] */
+                       const int32_t* block_tables,    /* device [S, max_blocks_per_seq] */
+                       int32_t max_blocks_per_seq,
+                       const int32_t* cu_q_lens,       /* device [S+1] */
+                       const int32_t* cu_q_lens_host,  /* host [S+1], same values */
+                       const int32_t* context_lens,    /* device [S] */
+                       const int32_t* context_lens_host, /* host [S], same values */
+                       int32_t num_segments, int32_t num_kv_heads, int32_t gqa_ratio, int32_t head_dim,
+                       int32_t block_size, int64_t num_pages, float scale, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* ---------------------------------------------------------------------------
  * KV append: write this step's new K/V rows into the paged cache, the step
  * that runs before attention each decode or prefill step.  The block table
  * names where a sequence's rows live, its blocks being handed out as the

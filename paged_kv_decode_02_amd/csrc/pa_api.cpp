@@ -371,23 +371,24 @@ extern "C" size_t pa_mixed_chunk_workspace_size(int32_t max_num_tokens, int32_t 
       .bytes;
 }
 
-extern "C" int pa_mixed_chunk(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,
-                              const int32_t* block_tables, int32_t max_blocks, const int32_t* cu_q_lens,
-                              const int32_t* cu_q_lens_host, const int32_t* context_lens,
-                              const int32_t* context_lens_host, int32_t num_segments, int32_t num_kv_heads,
-                              int32_t gqa_ratio, int32_t head_dim, int32_t block_size, int64_t num_pages, float scale,
-                              pa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  clear_error();
-  if (num_segments < 0) return fail(PA_EINVAL, "pa_mixed_chunk: num_segments < 0");
+namespace {
+
+int mixed_call(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,
+               const float* k_scales, const float* v_scales, bool kv_fp8, const int32_t* block_tables,
+               int32_t max_blocks, const int32_t* cu_q_lens, const int32_t* cu_q_lens_host,
+               const int32_t* context_lens, const int32_t* context_lens_host, int32_t num_segments,
+               int32_t num_kv_heads, int32_t gqa_ratio, int32_t head_dim, int32_t block_size, int64_t num_pages,
+               float scale, pa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream, const char* who) {
+  const std::string w(who);
+  if (num_segments < 0) return fail(PA_EINVAL, w + ": num_segments < 0");
   if (num_segments == 0) return PA_OK;
   int rc = check_common(out, q, k_pool, v_pool, block_tables, max_blocks, context_lens, context_lens_host,
-                        num_kv_heads, gqa_ratio, head_dim, block_size, num_pages, scale, dtype, workspace,
-                        "pa_mixed_chunk");
+                        num_kv_heads, gqa_ratio, head_dim, block_size, num_pages, scale, dtype, workspace, who);
   if (rc) return rc;
-  if (!cu_q_lens || !cu_q_lens_host) return fail(PA_EINVAL, "pa_mixed_chunk: cu_q_lens must be given (device and host)");
-  if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
-    return fail(PA_EINVAL, "pa_mixed_chunk: workspace not 256B aligned");
-  if (cu_q_lens_host[0] != 0) return fail(PA_EINVAL, "pa_mixed_chunk: cu_q_lens[0] != 0");
+  if (kv_fp8 && (!k_scales || !v_scales)) return fail(PA_EINVAL, w + ": null scale pointer");
+  if (!cu_q_lens || !cu_q_lens_host) return fail(PA_EINVAL, w + ": cu_q_lens must be given (device and host)");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return fail(PA_EINVAL, w + ": workspace not 256B aligned");
+  if (cu_q_lens_host[0] != 0) return fail(PA_EINVAL, w + ": cu_q_lens[0] != 0");
   std::vector<int32_t> chunk_seg, chunk_tok{0}, chunk_n, chunk_keys;
   int64_t decode_pages = 0;
   int64_t max_rows = 0;
@@ -395,10 +396,10 @@ extern "C" int pa_mixed_chunk(void* out, float* lse_out, const void* q, const vo
     const int64_t n = static_cast<int64_t>(cu_q_lens_host[s + 1]) - cu_q_lens_host[s];
     const int64_t L = context_lens_host[s];
     const std::string at = "[" + std::to_string(s) + "]";
-    if (n < 1) return fail(PA_EINVAL, "pa_mixed_chunk: segment" + at + " has no query token");
-    if (L < n) return fail(PA_EINVAL, "pa_mixed_chunk: context_lens" + at + " is shorter than its query tokens");
+    if (n < 1) return fail(PA_EINVAL, w + ": segment" + at + " has no query token");
+    if (L < n) return fail(PA_EINVAL, w + ": context_lens" + at + " is shorter than its query tokens");
     if (L > static_cast<int64_t>(max_blocks) * block_size)
-      return fail(PA_EINVAL, "pa_mixed_chunk: context_lens" + at + " exceeds the block table");
+      return fail(PA_EINVAL, w + ": context_lens" + at + " exceeds the block table");
     if (n == 1) {
       decode_pages += (L + block_size - 1) / block_size;
     } else {
@@ -409,11 +410,14 @@ extern "C" int pa_mixed_chunk(void* out, float* lse_out, const void* q, const vo
       max_rows = std::max(max_rows, n * gqa_ratio);
     }
   }
-  if (decode_pages > (int64_t(1) << 31) - 1) return fail(PA_EUNSUPPORTED, "pa_mixed_chunk: too many pages");
+  if (decode_pages > (int64_t(1) << 31) - 1) return fail(PA_EUNSUPPORTED, w + ": too many pages");
   const int32_t num_chunks = static_cast<int32_t>(chunk_seg.size());
-  if (num_chunks > 0 ? !mixed_supported(dtype, head_dim, gqa_ratio) : !decode_supported(dtype, head_dim, gqa_ratio))
-    return fail(PA_EUNSUPPORTED, "pa_mixed_chunk: prefill chunks are built for bf16, head_dim 128, gqa_ratio "
-                                 "1/2/4/8/16");
+  // (over an fp8 cache every shape the chunk tiles take is one the fp8
+  // stream kernel takes too)
+  const bool built = num_chunks > 0 || kv_fp8 ? mixed_supported(dtype, head_dim, gqa_ratio)
+                                              : decode_supported(dtype, head_dim, gqa_ratio);
+  if (!built)
+    return fail(PA_EUNSUPPORTED, w + ": prefill chunks are built for bf16, head_dim 128, gqa_ratio 1/2/4/8/16");
   // Chunk plan: row blocks of kPrefixRowsPerBlock (token, q-head) rows,
   // each chunk's keys cut into splits of about equal work per workgroup.
   const int32_t row_chunks =
@@ -424,7 +428,7 @@ extern "C" int pa_mixed_chunk(void* out, float* lse_out, const void* q, const vo
     // query fail, the launch below reports the device error.)
     const int cus = device_cu_count();
     plan = plan_chunks(chunk_n, chunk_keys, gqa_ratio, num_kv_heads, cus > 0 ? cus : 256);
-    if (plan.records > INT32_MAX) return fail(PA_EUNSUPPORTED, "pa_mixed_chunk: too many chunk tokens");
+    if (plan.records > INT32_MAX) return fail(PA_EUNSUPPORTED, w + ": too many chunk tokens");
   }
   const int64_t waves = max_waves_per_head(decode_pages, num_kv_heads, 0);
   const size_t stream_bytes =
@@ -433,8 +437,8 @@ extern "C" int pa_mixed_chunk(void* out, float* lse_out, const void* q, const vo
   const MixedLayout lay = mixed_layout(num_segments, plan.records / num_kv_heads, num_kv_heads, gqa_ratio, head_dim,
                                        1, stream_bytes);
   if (lay.bytes > workspace_bytes)
-    return fail(PA_EWORKSPACE, "pa_mixed_chunk: workspace holds " + std::to_string(workspace_bytes) +
-                                   " bytes, needs " + std::to_string(lay.bytes));
+    return fail(PA_EWORKSPACE, w + ": workspace holds " + std::to_string(workspace_bytes) + " bytes, needs " +
+                                   std::to_string(lay.bytes));
   MixedLaunch m;
   DecodeLaunch& a = m.base;
   a.out = out;
@@ -457,6 +461,9 @@ extern "C" int pa_mixed_chunk(void* out, float* lse_out, const void* q, const vo
   a.workspace = nullptr;
   a.workspace_bytes = 0;
   a.stream = stream;
+  a.kv_fp8 = kv_fp8;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
   m.cu_q_lens = cu_q_lens;
   m.chunk_seg = chunk_seg.data();
   m.chunk_tok = chunk_tok.data();
@@ -468,6 +475,33 @@ extern "C" int pa_mixed_chunk(void* out, float* lse_out, const void* q, const vo
   m.workspace = workspace;
   m.workspace_bytes = workspace_bytes;
   return launch_mixed(m);
+}
+
+}  // namespace
+
+extern "C" int pa_mixed_chunk(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, int32_t max_blocks, const int32_t* cu_q_lens,
+                              const int32_t* cu_q_lens_host, const int32_t* context_lens,
+                              const int32_t* context_lens_host, int32_t num_segments, int32_t num_kv_heads,
+                              int32_t gqa_ratio, int32_t head_dim, int32_t block_size, int64_t num_pages, float scale,
+                              pa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  return mixed_call(out, lse_out, q, k_pool, v_pool, nullptr, nullptr, false, block_tables, max_blocks, cu_q_lens,
+                    cu_q_lens_host, context_lens, context_lens_host, num_segments, num_kv_heads, gqa_ratio, head_dim,
+                    block_size, num_pages, scale, dtype, workspace, workspace_bytes, stream, "pa_mixed_chunk");
+}
+
+extern "C" int pa_mixed_chunk_fp8(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,
+                                  const float* k_scales, const float* v_scales, const int32_t* block_tables,
+                                  int32_t max_blocks, const int32_t* cu_q_lens, const int32_t* cu_q_lens_host,
+                                  const int32_t* context_lens, const int32_t* context_lens_host, int32_t num_segments,
+                                  int32_t num_kv_heads, int32_t gqa_ratio, int32_t head_dim, int32_t block_size,
+                                  int64_t num_pages, float scale, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  clear_error();
+  return mixed_call(out, lse_out, q, k_pool, v_pool, k_scales, v_scales, true, block_tables, max_blocks, cu_q_lens,
+                    cu_q_lens_host, context_lens, context_lens_host, num_segments, num_kv_heads, gqa_ratio, head_dim,
+                    block_size, num_pages, scale, PA_BF16, workspace, workspace_bytes, stream, "pa_mixed_chunk_fp8");
 }
 
 namespace {

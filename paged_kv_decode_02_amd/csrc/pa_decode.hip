@@ -821,7 +821,7 @@ int launch_stream(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_
 int launch_decode(const DecodeLaunch& a) { return launch_stream(a, nullptr, nullptr, nullptr, true, nullptr); }
 
 int launch_stream_merge(const DecodeLaunch& a, const int32_t* q_rows, int64_t waves) {
-  if (!(a.dtype == PA_BF16 && a.head_dim == 128 && !a.kv_fp8 && (a.gqa == 4 || a.gqa == 8 || a.gqa == 16)))
+  if (!(a.dtype == PA_BF16 && a.head_dim == 128 && (a.gqa == 4 || a.gqa == 8 || a.gqa == 16)))
     return fail(PA_EUNSUPPORTED, "stream merge: shape not built");
   if (waves <= 1) return PA_OK;
   const PartialLayout pl = partial_layout(waves, a.num_seqs, a.num_kv_heads, 16, a.head_dim);

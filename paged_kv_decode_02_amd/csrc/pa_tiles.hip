@@ -6,8 +6,10 @@
 // identification") describes attending to the shared prefix once for the
 // whole group: the group's queries against the prefix keys form one dense
 // product.  Attention over prefix + suffix is then the log-sum-exp merge of
-// attention over each part.  Three launches on the caller's stream:
-//  1. tile_kernel<G, false> (MFMA): per (group, row block, key split,
+// attention over each part.  Over bf16 pools or fp8 ones (e4m3fn codes
+// widened exactly to bf16 in the tile, each key's K scale on its scores and
+// V scale on its probabilities), three launches on the caller's stream:
+//  1. tile_kernel<G, false, FP8> (MFMA): per (group, row block, key split,
 //     kv-head) a workgroup of 4 waves takes up to 128 query rows --
 //     (member, q-head) pairs of the kv-head, folded into one tile dimension
 //     the way TokenSpeed's fold_sq_factor folds query tokens (TokenSpeed
@@ -24,21 +26,24 @@
 // Mixed batch (SARATHI-style piggybacking of decode tokens on prefill
 // chunks, SwiftLLM page section 3.3; chunked prefill, TokenSpeed deep-dive
 // section 5.1): prefill chunks (n > 1 new tokens, causal inside the chunk)
-// and decode tokens in one call.  With 4 or more q-heads per kv-head and
-// decode tokens present, one launch:
-//  1. mixed_kernel<G>: chunk workgroups (the tile body on one (chunk, row
-//     block, key split, kv-head), causal mask by select) and decode
-//     workgroups (the matrix-core stream wave on one run of decode pages)
-//     interleaved along each XCD's dispatch order, so the matrix-bound and
-//     the HBM-bound work share the CUs for the whole launch.
+// and decode tokens in one call, over bf16 pools or fp8 ones (e4m3fn codes
+// and per-row scales, read as the prefix tiles read them).  With 4 or more
+// q-heads per kv-head and decode tokens present, one launch:
+//  1. mixed_kernel<G, FP8>: chunk workgroups (the tile body on one (chunk,
+//     row block, key split, kv-head), causal mask by select) and decode
+//     workgroups (two matrix-core stream waves, one run of decode pages
+//     each) interleaved along each XCD's dispatch order, so the
+//     matrix-bound and the HBM-bound work share the CUs for the whole
+//     launch.
 //  2. The decode merge, then chunk_merge_kernel: per (chunk token, kv-head),
 //     the key splits.
-// Otherwise tile_kernel<G, true> for the chunks, then the stream kernel
+// Otherwise tile_kernel<G, true, FP8> for the chunks, then the stream kernel
 // (+ its merge) over the decode segments, then chunk_merge_kernel.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <string>
+#include <type_traits>
 
 #include "pa_common.h"
 #include "pa_internal.h"
@@ -74,9 +79,10 @@ __device__ __forceinline__ void lds_barrier() {
 // that stream through two LDS buffer pairs (tile t + 1 lands while tile t is
 // used).  Wave w takes query rows 32 w .. +32 against all 64 keys of every
 // tile, so every K/V byte in LDS is read by the four waves.  The workgroup
-// needs 66 KB of LDS and about 200 VGPRs per wave, so two workgroups share a
-// CU; their barriers are independent, and the matrix work of one overlaps the
-// softmax of the other on the same SIMD.
+// needs 66 KB of LDS (35 KB over fp8 pools) and about 240 VGPRs per wave
+// (220 for fp8), so two workgroups share a CU; their barriers are
+// independent, and the matrix work of one overlaps the softmax of the other
+// on the same SIMD.
 //  PREFIX: unit = a group; rows are (member, q-head) pairs; keys are the
 //          shared prefix, read through the first member's table; every row
 //          sees every key.
@@ -589,7 +595,6 @@ __global__ __launch_bounds__(kTileThreads, FP8 ? kTileFp8WorkgroupsPerCU : kTile
     ChunkList chunks, int RC, int nks, int kps, int Hkv, int n_items, int num_pages, float scale_log2,
     int32_t* __restrict__ begin_pages, float* __restrict__ pre_o, float* __restrict__ pre_lse,
     const float* __restrict__ k_scales, const float* __restrict__ v_scales) {
-  static_assert(!(FP8 && CHUNK), "fp8 tiles are built for the shared prefix");
   __shared__ TileLds<kTK, kTB, FP8> lds;
   TileWork tw;
   if (!tile_work<G, CHUNK>(blockIdx.x, RC, n_items, Hkv, nks, kps, chunks, ctx, cu_q, group_off, prefix_lens,
@@ -734,30 +739,51 @@ __global__ __launch_bounds__(64) void cascade_merge_kernel(
 }
 
 // Decode runs of the one-launch mixed kernel: the runs of a plain decode
-// launch (4 matrix-core stream waves per CU) times PA_MIXED_RUNS_PER_WAVE.
+// launch (4 matrix-core stream waves per CU) times PA_MIXED_RUNS_PER_WAVE
+// (bf16 pools) or PA_MIXED_RUNS_PER_WAVE_FP8.
 #ifndef PA_MIXED_RUNS_PER_WAVE
 #define PA_MIXED_RUNS_PER_WAVE 2
 #endif
-// Decode workgroups per chunk workgroup in the dispatch order.
+#ifndef PA_MIXED_RUNS_PER_WAVE_FP8
+#define PA_MIXED_RUNS_PER_WAVE_FP8 3
+#endif
+// Decode workgroups per chunk workgroup in the dispatch order (bf16, fp8
+// pools: an fp8 decode run streams half the bytes of a bf16 one).
 #ifndef PA_MIXED_DECODE_PER_CHUNK
-#define PA_MIXED_DECODE_PER_CHUNK 7
+#define PA_MIXED_DECODE_PER_CHUNK 3
+#endif
+#ifndef PA_MIXED_DECODE_PER_CHUNK_FP8
+#define PA_MIXED_DECODE_PER_CHUNK_FP8 5
 #endif
 // Keys per tile of the mixed kernel's chunk workgroups (two buffers).
 #ifndef PA_MIXED_TILE_KEYS
 #define PA_MIXED_TILE_KEYS 32
 #endif
-constexpr int kMixRatio = PA_MIXED_DECODE_PER_CHUNK;
+// Build switch: 0 runs every mixed batch as the chunk launch(es), then the
+// decode stream (for measuring the one-launch kernel against them).
+#ifndef PA_MIXED_ONE_LAUNCH
+#define PA_MIXED_ONE_LAUNCH 1
+#endif
+// Stream waves (runs) per decode workgroup, each with its own LDS.
+#ifndef PA_MIXED_DECODE_WAVES
+#define PA_MIXED_DECODE_WAVES 2
+#endif
+constexpr int kMixDecodeWaves = PA_MIXED_DECODE_WAVES;
+static_assert(kMixDecodeWaves >= 1 && kMixDecodeWaves <= 4, "decode waves per workgroup");
 constexpr int kMixTK = PA_MIXED_TILE_KEYS;
 
 // Prefill chunks and decode tokens of a mixed batch in one launch (SwiftLLM
 // page, section 3.3: decode tokens piggybacked on a prefill chunk, so that
 // the chunk's matrix work and the decode's HBM streaming run at the same
 // time).  A workgroup of 4 waves is either a chunk workgroup (tile_body with
-// tiles of kMixTK keys: 128 (token, q-head) rows against one key split of
-// one kv-head) or a decode workgroup whose first wave streams one decode run
-// (stream_mfma_body; the other waves end at once).  Each takes 40 KB of LDS
-// or less.  Along each XCD's dispatch order one chunk workgroup comes before
-// every kMixRatio decode workgroups while both kinds remain.  Decode segments
+// tiles of kMixTK keys, 64 over fp8 pools: 128 (token, q-head) rows against
+// one key split of one kv-head) or a decode workgroup whose first
+// kMixDecodeWaves waves each stream one decode run with LDS of their own
+// (stream_mfma_body; the other waves end at once): 80 KB (bf16) or 50 KB
+// (fp8), so that two decode workgroups on a CU -- the chunk body's registers
+// let two workgroups share one -- stream with four waves, as a plain decode
+// launch does.  Along each XCD's dispatch order one chunk workgroup comes
+// before every `ratio` decode workgroups while both kinds remain.  Decode segments
 // find their pages themselves (a walk over the segments with one query
 // token, cu_q); the merges of both run as launches after this one.
 // (The same pairing for a cascade's prefix tiles and suffix stream measured
@@ -765,7 +791,7 @@ constexpr int kMixTK = PA_MIXED_TILE_KEYS;
 // batch, whose prefix work is small next to its suffix stream.)
 struct PairGrid {
   int ncw;   // chunk workgroups (a multiple of 8, as tile_work numbers them)
-  int ndw;   // decode workgroups (a multiple of 8): one run each
+  int ndw;   // decode workgroups (a multiple of 8): kMixDecodeWaves runs each
   int runs;  // decode runs: runs per kv-head x kv-heads
   int W;     // decode runs per kv-head
 };
@@ -778,52 +804,62 @@ struct PairTiles {
   float* pre_lse;
 };
 
-template <int G>
+template <int G, bool FP8>
 __global__ __launch_bounds__(kTileThreads, 2) void mixed_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool,
+    const uint16_t* __restrict__ q, const void* __restrict__ k_pool, const void* __restrict__ v_pool,
+    const float* __restrict__ k_scales, const float* __restrict__ v_scales,
     const int32_t* __restrict__ block_tables, int max_blocks, const int32_t* __restrict__ ctx, ChunkList chunks,
     PairTiles tiles, int Hkv, int num_pages, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse_out, int S, int per, int total_pages, int32_t* __restrict__ seq_info,
     float* __restrict__ part_o, float* __restrict__ part_lse, PairGrid grid) {
-  using WaveLds = StreamMfmaLds<uint16_t, 128>;
-  using ChunkLds = TileLds<kMixTK, 2>;
-  constexpr size_t kBytes = sizeof(ChunkLds) > sizeof(WaveLds) ? sizeof(ChunkLds) : sizeof(WaveLds);
+  // fp8 pools: code tiles of 64 keys (35 KB with their scales), the fp8
+  // stream wave (25 KB)
+  using TKV = typename std::conditional<FP8, uint8_t, uint16_t>::type;
+  constexpr int CKT = FP8 ? 64 : kMixTK;
+  using WaveLds = StreamMfmaLds<TKV, 128>;
+  using ChunkLds = TileLds<CKT, 2, FP8>;
+  constexpr size_t kWaveBytes = kMixDecodeWaves * sizeof(WaveLds);
+  constexpr size_t kBytes = sizeof(ChunkLds) > kWaveBytes ? sizeof(ChunkLds) : kWaveBytes;
   __shared__ __align__(16) unsigned char raw[kBytes];
   // Workgroup -> kind and index along XCD x's dispatch order: cycles of one
-  // chunk workgroup and kMixRatio decode workgroups while both kinds
+  // chunk workgroup and `ratio` decode workgroups while both kinds
   // remain, then the remaining decode workgroups, then the remaining chunk
   // workgroups.
   const int x = blockIdx.x & 7;
   const int j = blockIdx.x >> 3;
   const int nc = grid.ncw >> 3, nd = grid.ndw >> 3;
-  const int full = nc < nd / kMixRatio ? nc : nd / kMixRatio;
+  constexpr int ratio = FP8 ? PA_MIXED_DECODE_PER_CHUNK_FP8 : PA_MIXED_DECODE_PER_CHUNK;
+  const int full = nc < nd / ratio ? nc : nd / ratio;
   bool chunk;
   int idx;
-  if (j < (1 + kMixRatio) * full) {
-    const int k = j / (1 + kMixRatio), r = j % (1 + kMixRatio);
+  if (j < (1 + ratio) * full) {
+    const int k = j / (1 + ratio), r = j % (1 + ratio);
     chunk = r == 0;
-    idx = chunk ? k : k * kMixRatio + r - 1;
+    idx = chunk ? k : k * ratio + r - 1;
   } else {
-    const int j2 = j - (1 + kMixRatio) * full;
-    const int left_d = nd - kMixRatio * full;
+    const int j2 = j - (1 + ratio) * full;
+    const int left_d = nd - ratio * full;
     chunk = j2 >= left_d;
-    idx = chunk ? full + j2 - left_d : kMixRatio * full + j2;
+    idx = chunk ? full + j2 - left_d : ratio * full + j2;
   }
   if (chunk) {
     TileWork tw;
     if (!tile_work<G, true>(idx * 8 + x, tiles.RC, tiles.n_items, Hkv, 0, 0, chunks, ctx, tiles.cu_q, nullptr,
                             nullptr, nullptr, tw))
       return;  // uniform over the workgroup
-    tile_body<G, true, kMixTK, 2>(tw, *reinterpret_cast<ChunkLds*>(raw), q, k_pool, v_pool, block_tables, max_blocks,
-                                  Hkv, num_pages, scale_log2, tiles.pre_o, tiles.pre_lse);
+    tile_body<G, true, CKT, 2, FP8>(tw, *reinterpret_cast<ChunkLds*>(raw), q, k_pool, v_pool, block_tables,
+                                    max_blocks, Hkv, num_pages, scale_log2, tiles.pre_o, tiles.pre_lse, k_scales,
+                                    v_scales);
   } else {
-    const int r = idx * 8 + x;
-    if (threadIdx.x >= 64 || r >= grid.runs) return;
+    const int wv = threadIdx.x >> 6;
+    const int r = (idx * 8 + x) * kMixDecodeWaves + wv;
+    if (wv >= kMixDecodeWaves || r >= grid.runs) return;
     const Fold fold{1, G, __builtin_ctz(G), 0, 1, 0};
-    stream_mfma_body<uint16_t, 128, false>(*reinterpret_cast<WaveLds*>(raw), r % grid.W, r / grid.W, out, lse_out, q,
-                                           k_pool, v_pool, nullptr, nullptr, block_tables, ctx, max_blocks, S, Hkv,
-                                           num_pages, scale_log2, per, total_pages, seq_info, part_o, part_lse,
-                                           PageSkip{}, nullptr, tiles.cu_q, fold);
+    stream_mfma_body<TKV, 128, false>(*reinterpret_cast<WaveLds*>(raw + wv * sizeof(WaveLds)), r % grid.W, r / grid.W,
+                                      out, lse_out, q,
+                                      static_cast<const TKV*>(k_pool), static_cast<const TKV*>(v_pool), k_scales,
+                                      v_scales, block_tables, ctx, max_blocks, S, Hkv, num_pages, scale_log2, per,
+                                      total_pages, seq_info, part_o, part_lse, PageSkip{}, nullptr, tiles.cu_q, fold);
   }
 }
 
@@ -831,9 +867,10 @@ __global__ __launch_bounds__(kTileThreads, 2) void mixed_kernel(
 struct PairPlan {
   int64_t per, W;
 };
-PairPlan pair_plan(int64_t pages, int32_t num_kv_heads) {
+PairPlan pair_plan(int64_t pages, int32_t num_kv_heads, bool kv_fp8) {
   const int cus = device_cu_count();
-  const int64_t target = static_cast<int64_t>(4) * PA_MIXED_RUNS_PER_WAVE * (cus > 0 ? cus : 256);
+  const int64_t target = static_cast<int64_t>(4) * (kv_fp8 ? PA_MIXED_RUNS_PER_WAVE_FP8 : PA_MIXED_RUNS_PER_WAVE) *
+                         (cus > 0 ? cus : 256);
   const int64_t per_head = std::max<int64_t>(1, std::min<int64_t>(target, kMaxResidentWaves) / num_kv_heads);
   PairPlan p;
   p.per = std::max<int64_t>(kMinPagesPerWave, (pages + per_head - 1) / per_head);
@@ -928,18 +965,18 @@ int launch_mixed_g(const MixedLaunch& mx) {
   // the matrix-core stream wave (4 or more q-heads per kv-head) and the
   // chunks fit one chunk list; otherwise the chunk tiles, then the decode
   // stream, one after the other.
-  const bool one = G >= 4 && mx.decode_pages > 0 && mx.num_chunks <= kMaxChunkSegments;
+  const bool one = PA_MIXED_ONE_LAUNCH && G >= 4 && mx.decode_pages > 0 && mx.num_chunks <= kMaxChunkSegments;
   if (one) {
     const ChunkList cl = chunk_list(0);
     const int n_items = cl.item_end[cl.n - 1];
-    const PairPlan pp = pair_plan(mx.decode_pages, a.num_kv_heads);
+    const PairPlan pp = pair_plan(mx.decode_pages, a.num_kv_heads, a.kv_fp8);
     const PartialLayout pl = partial_layout(pp.W, a.num_seqs, a.num_kv_heads, 16, 128);
     if (pl.bytes > mx.workspace_bytes - L.stream_offset)
       return fail(PA_EWORKSPACE, "pa_mixed_chunk: workspace too small for the decode plan");
     PairGrid grid;
     grid.W = static_cast<int>(pp.W);
     grid.runs = static_cast<int>(pp.W * a.num_kv_heads);
-    grid.ndw = (grid.runs + 7) / 8 * 8;  // one run per workgroup
+    grid.ndw = ((grid.runs + kMixDecodeWaves - 1) / kMixDecodeWaves + 7) / 8 * 8;  // kMixDecodeWaves runs each
     grid.ncw = (n_items + 7) / 8 * 8 * mx.row_chunks;
     PairTiles tiles{};
     tiles.RC = mx.row_chunks;
@@ -948,13 +985,20 @@ int launch_mixed_g(const MixedLaunch& mx) {
     tiles.pre_o = pre_o;
     tiles.pre_lse = pre_lse;
     profile_before(a.stream);
-    hipLaunchKernelGGL((mixed_kernel<G>), dim3(static_cast<unsigned>(grid.ncw + grid.ndw)), dim3(kTileThreads),
-                       0, st, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
-                       static_cast<const uint16_t*>(a.v_pool), a.block_tables, a.max_blocks, a.context_lens, cl, tiles,
-                       a.num_kv_heads, static_cast<int>(a.num_pages), scale_log2, static_cast<uint16_t*>(a.out),
-                       a.lse_out, a.num_seqs, static_cast<int>(pp.per), static_cast<int>(mx.decode_pages),
-                       reinterpret_cast<int32_t*>(sws + pl.info_offset), reinterpret_cast<float*>(sws + pl.o_offset),
-                       reinterpret_cast<float*>(sws + pl.lse_offset), grid);
+    const unsigned blocks = static_cast<unsigned>(grid.ncw + grid.ndw);
+    auto launch = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kTileThreads), 0, st, static_cast<const uint16_t*>(a.q),
+                         a.k_pool, a.v_pool, a.k_scales, a.v_scales, a.block_tables, a.max_blocks, a.context_lens, cl,
+                         tiles, a.num_kv_heads, static_cast<int>(a.num_pages), scale_log2,
+                         static_cast<uint16_t*>(a.out), a.lse_out, a.num_seqs, static_cast<int>(pp.per),
+                         static_cast<int>(mx.decode_pages), reinterpret_cast<int32_t*>(sws + pl.info_offset),
+                         reinterpret_cast<float*>(sws + pl.o_offset), reinterpret_cast<float*>(sws + pl.lse_offset),
+                         grid);
+    };
+    if (a.kv_fp8)
+      launch(mixed_kernel<G, true>);
+    else
+      launch(mixed_kernel<G, false>);
     profile_after(a.stream);
     if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_mixed_chunk: mixed kernel launch failed");
     DecodeLaunch dec = a;
@@ -970,11 +1014,17 @@ int launch_mixed_g(const MixedLaunch& mx) {
         const ChunkList cl = chunk_list(b0);
         const int n_items = cl.item_end[cl.n - 1];
         const unsigned blocks = static_cast<unsigned>((n_items + 7) / 8 * 8 * mx.row_chunks);
-        hipLaunchKernelGGL((tile_kernel<G, true>), dim3(blocks), dim3(kTileThreads), 0, st,
-                           static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
-                           static_cast<const uint16_t*>(a.v_pool), a.block_tables, a.max_blocks, a.context_lens,
-                           mx.cu_q_lens, nullptr, nullptr, cl, mx.row_chunks, 0, 0, a.num_kv_heads, n_items,
-                           static_cast<int>(a.num_pages), scale_log2, nullptr, pre_o, pre_lse, nullptr, nullptr);
+        auto launch = [&](auto kernel) {
+          hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kTileThreads), 0, st, static_cast<const uint16_t*>(a.q),
+                             a.k_pool, a.v_pool, a.block_tables, a.max_blocks, a.context_lens, mx.cu_q_lens, nullptr,
+                             nullptr, cl, mx.row_chunks, 0, 0, a.num_kv_heads, n_items,
+                             static_cast<int>(a.num_pages), scale_log2, nullptr, pre_o, pre_lse, a.k_scales,
+                             a.v_scales);
+        };
+        if (a.kv_fp8)
+          launch(tile_kernel<G, true, true>);
+        else
+          launch(tile_kernel<G, true, false>);
         if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_mixed_chunk: chunk kernel launch failed");
       }
       profile_after(a.stream);

@@ -44,6 +44,7 @@ EXPORTS = (
     "pa_prefix_cascade_fp8",
     "pa_mixed_chunk_workspace_size",
     "pa_mixed_chunk",
+    "pa_mixed_chunk_fp8",
     "pa_kv_append",
     "pa_kv_append_fp8",
     "pa_check_block_tables",
@@ -119,6 +120,9 @@ def load(path: Optional[str] = None):
     lib.pa_mixed_chunk.restype = ctypes.c_int
     lib.pa_mixed_chunk.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32,
                                    c_i32, c_i32, c_i32, c_i64, ctypes.c_float, ctypes.c_int, c_vp, c_sz, c_vp]
+    lib.pa_mixed_chunk_fp8.restype = ctypes.c_int
+    lib.pa_mixed_chunk_fp8.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp,
+                                       c_i32, c_i32, c_i32, c_i32, c_i32, c_i64, ctypes.c_float, c_vp, c_sz, c_vp]
     lib.pa_kv_append.restype = ctypes.c_int
     lib.pa_kv_append.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32,
                                  c_i32, c_i64, ctypes.c_int, c_vp]
@@ -596,6 +600,49 @@ def mixed_chunk(out, q, k_pool, v_pool, block_tables, cu_q_lens, cu_q_lens_host,
         _dev(cu_q_lens, "cu_q_lens", torch.int32), cq.ctypes.data,
         _dev(context_lens, "context_lens", torch.int32), ch.ctypes.data,
         S, Hkv, Hq // Hkv, D, BS, NP, float(scale), _dtype_code(q),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream_ptr(stream),
+    )
+    return _check(rc)
+
+
+def mixed_chunk_fp8(out, q, k_pool, v_pool, k_scales, v_scales, block_tables, cu_q_lens, cu_q_lens_host,
+                    context_lens, context_lens_host, scale, workspace, lse_out=None, stream=None):
+    """pa_mixed_chunk_fp8 on torch tensors: the segments of
+    :func:`mixed_chunk`, the pools and scales of :func:`decode_fp8`."""
+    import torch
+
+    T, Hq, D = q.shape
+    NP, Hkv, BS, D2 = k_pool.shape
+    if q.dtype != torch.bfloat16 or tuple(out.shape) != (T, Hq, D) or out.dtype != torch.bfloat16:
+        raise ValueError("q and out must be bfloat16 [T, Hq, D]")
+    codes = (torch.uint8, torch.float8_e4m3fn)
+    if tuple(v_pool.shape) != tuple(k_pool.shape) or k_pool.dtype not in codes or v_pool.dtype not in codes:
+        raise ValueError("k_pool and v_pool must be [NP, Hkv, BS, D] uint8 / float8_e4m3fn")
+    for t, nm in ((k_scales, "k_scales"), (v_scales, "v_scales")):
+        if tuple(t.shape) != (NP, Hkv, BS) or t.dtype != torch.float32:
+            raise ValueError(f"{nm} must be float32 [NP, Hkv, BS]")
+    if D2 != D or Hq % Hkv:
+        raise ValueError("head_dim mismatch or q heads not a multiple of kv heads")
+    cq = _host_i32(cu_q_lens_host, "cu_q_lens_host")
+    ch = _host_i32(context_lens_host, "context_lens_host")
+    S = ch.size
+    if cq.size != S + 1 or cu_q_lens.numel() != S + 1 or context_lens.numel() != S:
+        raise ValueError("cu_q_lens must have one entry more than context_lens")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must have one row per segment")
+    if S and int(cq[-1]) != T:
+        raise ValueError("q must have cu_q_lens[-1] rows")
+    if lse_out is not None and tuple(lse_out.shape) != (T, Hq):
+        raise ValueError("lse_out must be [T, Hq]")
+    rc = load().pa_mixed_chunk_fp8(
+        _dev(out, "out"),
+        _dev(lse_out, "lse_out", torch.float32) if lse_out is not None else None,
+        _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(k_scales, "k_scales", torch.float32), _dev(v_scales, "v_scales", torch.float32),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(cu_q_lens, "cu_q_lens", torch.int32), cq.ctypes.data,
+        _dev(context_lens, "context_lens", torch.int32), ch.ctypes.data,
+        S, Hkv, Hq // Hkv, D, BS, NP, float(scale),
         _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream_ptr(stream),
     )
     return _check(rc)

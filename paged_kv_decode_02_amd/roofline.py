@@ -86,18 +86,26 @@ def prefix_flops(group_seq_offsets, prefix_lens, num_q_heads, head_dim) -> int:
     return int(4 * head_dim * num_q_heads * (np.diff(offs) * pl).sum())
 
 
-def mixed_bytes(context_lens, q_lens, num_q_heads, num_kv_heads, head_dim, elem_bytes, block_size=16) -> dict:
+def mixed_bytes(context_lens, q_lens, num_q_heads, num_kv_heads, head_dim, elem_bytes, block_size=16,
+                kv_fp8=False) -> dict:
     """Mixed batch: every segment's visible K/V read once per kv-head (a
     chunk's rows once for all its tokens), plus q and out for every token
-    and the table entries walked."""
+    and the table entries walked.  With kv_fp8 the K/V elements are one-byte
+    codes and each K and V row (token, kv-head) adds a float32 scale; q and
+    out keep elem_bytes."""
     ctx = np.asarray(context_lens, dtype=np.int64)
     ql = np.asarray(q_lens, dtype=np.int64)
-    kv = kv_cache_bytes(1, num_kv_heads, head_dim, int(ctx.sum()), elem_bytes)
+
+    def kv_of(tokens):
+        if kv_fp8:
+            return kv_cache_bytes(1, num_kv_heads, head_dim, tokens, 1) + 2 * num_kv_heads * tokens * 4
+        return kv_cache_bytes(1, num_kv_heads, head_dim, tokens, elem_bytes)
+
+    kv = kv_of(int(ctx.sum()))
     qo = 2 * int(ql.sum()) * num_q_heads * head_dim * elem_bytes
     tables = 4 * int(((ctx + block_size - 1) // block_size).sum()) + 4 * (2 * ctx.size + 1)
     dec = ql == 1
-    return {"kv": kv, "q_out": qo, "tables": tables, "total": kv + qo + tables,
-            "decode_kv": kv_cache_bytes(1, num_kv_heads, head_dim, int(ctx[dec].sum()), elem_bytes)}
+    return {"kv": kv, "q_out": qo, "tables": tables, "total": kv + qo + tables, "decode_kv": kv_of(int(ctx[dec].sum()))}
 
 
 def chunk_flops(context_lens, q_lens, num_q_heads, head_dim) -> int:

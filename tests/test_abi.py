@@ -223,6 +223,56 @@ def test_mixed_zero_segments_is_a_no_op():
     assert call_mixed(lib, S=0, q=None, out=None) == pa.PA_OK
 
 
+def call_mixed_fp8(lib, **kw):
+    args = dict(out=FAKE, lse=None, q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, bt=FAKE, mb=4, cu=FAKE, cu_host=None,
+                ctx=FAKE, ctx_host=None, S=2, Hkv=2, G=4, D=128, BS=16, NP=10, scale=0.1,
+                ws=ctypes.c_void_p(0x100000), ws_bytes=1 << 20, stream=None)
+    args.update(kw)
+    cu = args["cu_host"] if args["cu_host"] is not None else np.array([0, 5, 6], dtype=np.int32)
+    ch = args["ctx_host"] if args["ctx_host"] is not None else np.array([20, 40], dtype=np.int32)
+    return lib.pa_mixed_chunk_fp8(args["out"], args["lse"], args["q"], args["k"], args["v"], args["ks"], args["vs"],
+                                  args["bt"], args["mb"], args["cu"], cu.ctypes.data, args["ctx"], ch.ctypes.data,
+                                  args["S"], args["Hkv"], args["G"], args["D"], args["BS"], args["NP"], args["scale"],
+                                  args["ws"], args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(ks=None), pa.PA_EINVAL),
+        (dict(vs=None), pa.PA_EINVAL),
+        (dict(q=None), pa.PA_EINVAL),
+        (dict(cu=None), pa.PA_EINVAL),
+        (dict(cu_host=np.array([1, 5, 6], dtype=np.int32)), pa.PA_EINVAL),
+        (dict(cu_host=np.array([0, 5, 5], dtype=np.int32)), pa.PA_EINVAL),
+        (dict(cu_host=np.array([0, 21, 22], dtype=np.int32)), pa.PA_EINVAL),
+        (dict(ctx_host=np.array([20, 65], dtype=np.int32)), pa.PA_EINVAL),
+        (dict(ws=ctypes.c_void_p(0x100010)), pa.PA_EINVAL),
+        (dict(ws_bytes=64), pa.PA_EWORKSPACE),
+        (dict(D=64), pa.PA_EUNSUPPORTED),
+        (dict(D=64, cu_host=np.array([0, 1, 2], dtype=np.int32)), pa.PA_EUNSUPPORTED),  # decode tokens only
+        (dict(G=3), pa.PA_EUNSUPPORTED),
+        (dict(S=-1), pa.PA_EINVAL),
+    ],
+)
+def test_mixed_fp8_rejects_bad_arguments(kw, code):
+    lib = pa.load()
+    assert call_mixed_fp8(lib, **kw) == code
+    assert lib.pa_last_error().decode().startswith("pa_mixed_chunk_fp8")
+
+
+def test_mixed_fp8_zero_segments_is_a_no_op():
+    lib = pa.load()
+    assert call_mixed_fp8(lib, S=0, q=None, out=None, ks=None) == pa.PA_OK
+
+
+@pytest.mark.parametrize("cu_host", [np.array([0, 5, 6], dtype=np.int32), np.array([0, 1, 2], dtype=np.int32)])
+def test_mixed_fp8_valid_arguments_reach_the_launch(cu_host):
+    lib = pa.load()
+    rc = call_mixed_fp8(lib, cu_host=cu_host)
+    assert rc not in (pa.PA_OK, pa.PA_EINVAL, pa.PA_EWORKSPACE, pa.PA_EUNSUPPORTED), lib.pa_last_error().decode()
+
+
 def test_mixed_workspace_size_covers_chunk_partials():
     # 2,048 chunk tokens + 256 decode segments, Llama-8B heads.
     ws = pa.mixed_chunk_workspace_size(2304, 260, 8, 4, 128, 80000)

@@ -26,8 +26,9 @@ def to_device(q, kc, ks, vc, vs):
             torch.from_numpy(ks).to(d), torch.from_numpy(vc).to(d), torch.from_numpy(vs).to(d))
 
 
-def want_bits_to_f32(bits):
-    return (bits.astype(np.uint32) << 16).view(np.float32)
+def bits_to_f32(bits):
+    """bf16 bit patterns -> their float32 values."""
+    return (np.asarray(bits).astype(np.uint32) << 16).view(np.float32)
 
 
 def run_cascade_fp8(pa, lay, q, kc, ks, vc, vs):
@@ -151,11 +152,14 @@ def test_cascade_fp8_needle_in_prefix_and_suffix(gpu_lib):
     qq = bf16_bits_from_f32(qf)
     out, _ = run_cascade_fp8(gpu_lib, lay, *to_device(qq, kc, ks, vc, vs))
     want_bits = bf16_bits_from_f32(want.astype(np.float32))
-    assert np.array_equal(want_bits_to_f32(want_bits).astype(np.float64), want)  # the rows are exact in bf16
+    assert np.array_equal(bits_to_f32(want_bits).astype(np.float64), want)  # the rows are exact in bf16
     ro, _ = oracle_cascade_fp8(lay, qq, kc, ks, vc, vs)
-    assert np.array_equal(bf16_bits_from_f32(ro.astype(np.float32)), want_bits), "the oracle misses the planted rows"
+    # (compared as values: a zero of the row may come back as -0 where the
+    # fp64 oracle adds negative terms far below bf16's range, or as +0)
+    assert np.array_equal(bits_to_f32(bf16_bits_from_f32(ro.astype(np.float32))), bits_to_f32(want_bits)), \
+        "the oracle misses the planted rows"
     got = out.view(torch.int16).cpu().numpy().view(np.uint16)
-    assert np.array_equal(got, want_bits), "the kernel does not return the planted rows' bits"
+    assert np.array_equal(bits_to_f32(got), bits_to_f32(want_bits)), "the kernel does not return the planted rows"
 
 
 def test_shared_prefix_fp8_workload(gpu_lib):

@@ -70,3 +70,26 @@ def test_fp8_bytes_count_every_new_token():
     four = roofline.decode_fp8_bytes([100, 2000], 32, 8, 128, q_len=4)
     assert four["q_out"] == 4 * one["q_out"]
     assert four["total"] - one["total"] == 3 * one["q_out"]
+
+
+def test_fp8_cascade_and_mixed_bytes():
+    """Over an fp8 cache the cascade and mixed byte counts take one byte per
+    K/V element plus a float32 scale per K row and per V row, in the same
+    places the bf16 counts take two bytes per element."""
+    from workloads import workload
+
+    lay = workload("shared_prefix")
+    b = roofline.cascade_bytes(lay.context_lens, lay.group_seq_offsets, lay.prefix_lens, 32, 8, 128, 2)
+    f = roofline.cascade_bytes(lay.context_lens, lay.group_seq_offsets, lay.prefix_lens, 32, 8, 128, 2, kv_fp8=True)
+    tokens = b["kv"] // (2 * 8 * 128 * 2)  # K/V rows read: each prefix once, every suffix
+    assert f["kv"] == 2 * 8 * 128 * tokens + 2 * 8 * tokens * 4
+    assert f["prefix_kv"] == 16 * 2048 * (2 * 8 * 128 + 2 * 8 * 4)
+    assert f["q_out"] == b["q_out"] and f["tables"] == b["tables"]
+    lay = workload("chunked_piggyback")
+    b = roofline.mixed_bytes(lay.context_lens, lay.q_lens, 32, 8, 128, 2)
+    f = roofline.mixed_bytes(lay.context_lens, lay.q_lens, 32, 8, 128, 2, kv_fp8=True)
+    n = int(lay.context_lens.sum())
+    assert f["kv"] == 2 * 8 * 128 * n + 2 * 8 * n * 4
+    assert f["decode_kv"] == roofline.decode_fp8_bytes(lay.context_lens[4:], 32, 8, 128)["kv"] + \
+        roofline.decode_fp8_bytes(lay.context_lens[4:], 32, 8, 128)["scales"]
+    assert f["q_out"] == b["q_out"] and f["tables"] == b["tables"]

@@ -492,8 +492,18 @@ def _llama8b_multitoken4_fp8(seed=0):
     return lay
 
 
+def _chunked_piggyback_fp8(seed=0):
+    """The mixed batch (4 prefill chunks + 256 decode tokens) over an fp8
+    (e4m3fn) cache."""
+    lay = _chunked_piggyback(seed)
+    lay.name = "chunked_piggyback_fp8"
+    lay.kv_dtype = "fp8"
+    return lay
+
+
 WORKLOADS = {
     "tiny_f32": _tiny_f32,
+    "chunked_piggyback_fp8": _chunked_piggyback_fp8,
     "llama8b_multitoken4_fp8": _llama8b_multitoken4_fp8,
     "llama8b_multitoken4": _llama8b_multitoken4,
     "llama8b_prefill_append_fp8": _llama8b_prefill_append_fp8,
