@@ -542,11 +542,14 @@ const char* pa_last_error(void);
  * allocation-free nor reentrant.
  * pa_profile_enable(n) creates n pairs of HIP timing events on this thread;
  * every later call records one pair around each of its dominant kernels on
- * its stream: the stream kernel of pa_decode; the prefix kernel of
- * pa_prefix_cascade; for pa_mixed_chunk, the chunk kernel(s) (if the batch
- * has chunks) and then the decode stream kernel (if it has decode tokens).  pa_profile_collect() waits for those
- * events, writes up to `cap` durations in milliseconds to `ms_out`, returns
- * how many it wrote and rewinds the ring.  pa_profile_enable(0) frees the
+ * its stream: the stream kernel of the decode entry points (one pair per
+ * pass of a multi-token call); the prefix kernel of pa_prefix_cascade and
+ * pa_prefix_cascade_fp8; for pa_mixed_chunk and pa_mixed_chunk_fp8, the
+ * one-launch mixed kernel, or, when the batch runs as separate launches,
+ * the chunk kernel(s) (if it has chunks) and then the decode stream kernel
+ * (if it has decode tokens).  pa_profile_collect() waits for those events,
+ * writes up to `cap` durations in milliseconds to `ms_out`, returns how
+ * many it wrote and rewinds the ring.  pa_profile_enable(0) frees the
  * events and stops recording.  Returns a negative code on error.
  * ------------------------------------------------------------------------- */
 int pa_profile_enable(int32_t num_pairs);
