@@ -86,6 +86,7 @@ def fp8_cascade(groups, per_group, prefix, suf_hi, hq, hkv, seed, prefix_lens=No
         (1, 33, 2048, 600, 32, 8),   # long prefix, several key splits
         (3, 4, 0, 90, 32, 8),        # no prefix at all
         (2, 12, 96, 70, 128, 8),     # G = 16
+        (3, 10, 48, 60, 16, 8),      # G = 2 (suffix on the vector kernel)
     ],
 )
 def test_cascade_fp8_small(gpu_lib, groups, per_group, prefix, suf_hi, hq, hkv):

@@ -66,6 +66,7 @@ def oracle_cascade(lay, qh, kh, vh, seqs=None):
         (1, 33, 2048, 600, 32, 8),   # long prefix, several key splits
         (3, 4, 0, 90, 32, 8),        # no prefix at all
         (2, 12, 96, 70, 128, 8),     # G = 16: suffixes on the matrix-core stream kernel
+        (3, 10, 48, 60, 16, 8),      # G = 2: suffixes on the vector stream kernel
     ],
 )
 def test_cascade_small(gpu_lib, groups, per_group, prefix, suf_hi, hq, hkv):
