@@ -755,9 +755,10 @@ __global__ __launch_bounds__(64) void cascade_merge_kernel(
 #ifndef PA_MIXED_DECODE_PER_CHUNK_FP8
 #define PA_MIXED_DECODE_PER_CHUNK_FP8 5
 #endif
-// Keys per tile of the mixed kernel's chunk workgroups (two buffers).
+// Keys per tile of the mixed kernel's chunk workgroups (two buffers; 64
+// keys, 66 KB, fit inside a decode workgroup's 80 KB of LDS).
 #ifndef PA_MIXED_TILE_KEYS
-#define PA_MIXED_TILE_KEYS 32
+#define PA_MIXED_TILE_KEYS 64
 #endif
 // Build switch: 0 runs every mixed batch as the chunk launch(es), then the
 // decode stream (for measuring the one-launch kernel against them).
@@ -787,8 +788,11 @@ constexpr int kMixTK = PA_MIXED_TILE_KEYS;
 // find their pages themselves (a walk over the segments with one query
 // token, cu_q); the merges of both run as launches after this one.
 // (The same pairing for a cascade's prefix tiles and suffix stream measured
-// slower than the two launches: 313 against 304 us on the shared-prefix
-// batch, whose prefix work is small next to its suffix stream.)
+// slower than the separate launches on the shared-prefix batch, whose prefix
+// work is small next to its suffix stream: 313 against 304 us with one
+// stream wave per suffix workgroup; 320 us for the kernel alone against a
+// 299 us step with two, one suffix workgroup per CU and each member's first
+// suffix page written by a set-up kernel beforehand.)
 struct PairGrid {
   int ncw;   // chunk workgroups (a multiple of 8, as tile_work numbers them)
   int ndw;   // decode workgroups (a multiple of 8): kMixDecodeWaves runs each
