@@ -247,25 +247,7 @@ __device__ __forceinline__ void tile_body(const TileWork& tw, TileLds<KT, NB, FP
   // CHUNK: last key every row of this wave sees (uniform).
   const int vis_lo = CHUNK ? L - n_tok + min(row0, n_rows - 1) / G : 0x7fffffff;
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int r = row0 + rb * 16 + col;
-    vis[rb] = CHUNK ? L - n_tok + min(r, n_rows - 1) / G : 0x7fffffff;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      if (r < n_rows) {
-        const int64_t qi = (static_cast<int64_t>(q_base + r / G) * Hq + kvh * G + r % G) * D + c * 32 + lg * 8;
-        qb[rb][c] = *reinterpret_cast<const u32x4*>(q + qi);
-      } else {
-        qb[rb][c] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  }
-  // Wait for the q rows here, before any tile DMA is in flight: the
-  // compiler does not see the (inline-assembly) DMAs, and left to itself it
-  // would wait for q -- with vmcnt(0), draining the tile pipeline -- at the
-  // first MFMA of every tile.
-  asm volatile("" ::"v"(qb[0][0]), "v"(qb[0][1]), "v"(qb[0][2]), "v"(qb[0][3]), "v"(qb[1][0]), "v"(qb[1][1]),
-               "v"(qb[1][2]), "v"(qb[1][3]));
+  for (int rb = 0; rb < 2; ++rb) vis[rb] = CHUNK ? L - n_tok + min(row0 + rb * 16 + col, n_rows - 1) / G : 0x7fffffff;
   const int32_t* bt = block_tables + static_cast<int64_t>(seg) * max_blocks;
   const char* kbytes = reinterpret_cast<const char*>(k_pool);
   const char* vbytes = reinterpret_cast<const char*>(v_pool);
@@ -372,9 +354,186 @@ __device__ __forceinline__ void tile_body(const TileWork& tw, TileLds<KT, NB, FP
   const int tr_r = col >> 2;
   const int tr_c = col & 3;
 
-  // The first page-id window (and the second, if the range needs it), then
-  // tiles 0 .. NB - 2 in flight before the loop.
+  // S^T = K Q^T over the K tile in kb_lds: s[kb][rb] holds keys
+  // 16 kb + 4 lg + i, query row 16 rb + col.  Each K operand serves both row
+  // blocks.
+  auto scores = [&](const uint4* kb_lds, f32x4 (&s)[NKB][2]) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int key = kb * 16 + col;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) s[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        u32x4 a;
+        if constexpr (FP8) {
+          // codes 32 c + 8 lg .. +7 of the key: half of swizzled chunk 2 c + lg / 2
+          const int ch = (2 * c + (lg >> 1)) ^ fswz(key);
+          const u32x2 w8 = *(__attribute__((address_space(3))) const u32x2*)(
+              reinterpret_cast<const char*>(kb_lds) + key * ROWB + ch * 16 + (lg & 1) * 8);
+          a = u32x4{fp8x2_to_bf16x2<false>(w8.x), fp8x2_to_bf16x2<true>(w8.x), fp8x2_to_bf16x2<false>(w8.y),
+                    fp8x2_to_bf16x2<true>(w8.y)};
+        } else {
+          const int cc = c * 4 + lg;
+          a = *(LdsU4*)(&kb_lds[key * 16 + (cc ^ tswz(col))]);
+        }
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) s[kb][rb] = mfma16x16x32(a, qb[rb][c], s[kb][rb]);
+      }
+    }
+  };
+  // fp8: each key's K scale (scale buffer sb) on its scores.
+  auto scale_scores = [&](int sb, f32x4 (&s)[NKB][2]) {
+    if constexpr (FP8) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const f32x4 k4 = *(__attribute__((address_space(3))) const f32x4*)(&lds.ks[sb][kb * 16 + 4 * lg]);
+        const float kq[4] = {k4[0], k4[1], k4[2], k4[3]};
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[kb][rb][i] *= kq[i];
+      }
+    }
+  };
+  // Keys are masked (by select) only in tiles that need it: the last,
+  // partial tile of a split, and chunk tiles that cross the causal
+  // diagonal of this wave's rows.
+  auto mask_scores = [&](int kt, int nk, f32x4 (&s)[NKB][2]) {
+    const bool need_mask = nk < KT || (CHUNK && kt + KT - 1 > vis_lo);
+    if (need_mask) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kb * 16 + lg * 4 + i;
+            const bool ok = key < nk && (!CHUNK || kt + key <= vis[rb]);
+            s[kb][rb][i] = ok ? s[kb][rb][i] : -INFINITY;
+          }
+    }
+  };
+  // Online softmax per query row (column of S^T): the row's KT keys are
+  // spread over this lane's 4 NKB values and the lanes l^16, l^32, l^48.
+  // First the row maxima and the reference m.  Lazy rescaling:
+  // probabilities are taken against the running reference m, which moves
+  // (and o, the row sums are rescaled) only when a row's maximum exceeds it
+  // by more than 2^8 -- so p <= 256, and the rescale, a wave-wide branch, is
+  // rare after the first tiles.
+  auto rescale = [&](const f32x4 (&s)[NKB][2]) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      float x = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x = fmaxf(x, s[kb][rb][i]);
+      const float mx = max_xor32(max_xor16(x)) * scale_log2;  // scale > 0 keeps the order
+      if (__ballot(mx > m[rb] + 8.f) != 0ull) {
+        const float mn = fmaxf(m[rb], mx);
+        // m = -inf (nothing visible yet): o and the sums are 0, any factor will do
+        const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m[rb] - mn);
+        m[rb] = mn;
+        lsum[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) o[db][rb] *= alpha;
+      }
+    }
+  };
+  // Then the probabilities against m, rounded to bf16 into the P^T operand
+  // (scale buffer sb: fp8 V scales), and their float32 row sums.
+  auto probs = [&](const f32x4 (&s)[NKB][2], int sb, u32x4 (&pb)[NKS][2]) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      // A row with no visible key so far keeps m = -inf: its p are all 0.
+      const float nref = m[rb] == -INFINITY ? 0.f : -m[rb];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        uint32_t pw[2][2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          float p[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            p[i] = fast_exp2(fmaf(s[2 * ks + e][rb][i], scale_log2, nref));
+            lsum[rb] += p[i];
+          }
+          if constexpr (FP8) {
+            // P^T carries p times the key's V scale (keys 32 ks + 16 e + 4 lg + i;
+            // a masked key's p is 0 and its scale finite)
+            const f32x4 v4 =
+                *(__attribute__((address_space(3))) const f32x4*)(&lds.vs[sb][(2 * ks + e) * 16 + 4 * lg]);
+            p[0] *= v4[0];
+            p[1] *= v4[1];
+            p[2] *= v4[2];
+            p[3] *= v4[3];
+          }
+          pw[e][0] = bf16x2_rne(p[0], p[1]);
+          pw[e][1] = bf16x2_rne(p[2], p[3]);
+        }
+        // k slots 8 lg .. 8 lg + 7 = keys 32 ks + 4 lg + [0, 4) and
+        // 32 ks + 16 + 4 lg + [0, 4): the same order the V^T operand uses.
+        pb[ks][rb] = u32x4{pw[0][0], pw[0][1], pw[1][0], pw[1][1]};
+      }
+    }
+  };
+  // O^T += V^T P^T over the V tile in vb_lds; the V^T operand (d = 16 db +
+  // col, keys as above) comes from two transposed reads of 4 keys each and
+  // serves both row blocks.
+  auto accumulate = [&](const char* vb_lds, const u32x4 (&pb)[NKS][2]) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        u32x4 a;
+        if constexpr (FP8) {
+          // one transposed read of 8 rows: lanes 2 r, 2 r + 1 name row r of
+          // the block, the keys in P^T's order
+          const int r8 = col >> 1;
+          const int row = ks * 32 + (r8 >> 2) * 16 + lg * 4 + (r8 & 3);
+          const u32x2 w8 = lds_read_tr8(vb_lds + row * ROWB + (db ^ fswz(row)) * 16 + (col & 1) * 8);
+          a = u32x4{fp8x2_to_bf16x2<false>(w8.x), fp8x2_to_bf16x2<true>(w8.x), fp8x2_to_bf16x2<false>(w8.y),
+                    fp8x2_to_bf16x2<true>(w8.y)};
+        } else {
+          u32x2 part[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int row = ks * 32 + e * 16 + lg * 4 + tr_r;
+            const int ch = (db * 2 + (tr_c >> 1)) ^ tswz(row & 15);
+            part[e] = lds_read_tr16(vb_lds + row * (D * 2) + ch * 16 + (tr_c & 1) * 8);
+          }
+          a = u32x4{part[0].x, part[0].y, part[1].x, part[1].y};
+        }
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) o[db][rb] = mfma16x16x32(a, pb[ks][rb], o[db][rb]);
+      }
+    }
+  };
+
+  // The q rows and the first page-id window in one round trip, then (the
+  // second window, if the range needs it, and) tiles 0 .. NB - 2 in flight
+  // before the loop.
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int r = row0 + rb * 16 + col;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (r < n_rows) {
+        const int64_t qi = (static_cast<int64_t>(q_base + r / G) * Hq + kvh * G + r % G) * D + c * 32 + lg * 8;
+        qb[rb][c] = *reinterpret_cast<const u32x4*>(q + qi);
+      } else {
+        qb[rb][c] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
   issue_pids(0);
+  // Wait for the q rows here, before any tile DMA is in flight: the
+  // compiler does not see the (inline-assembly) DMAs, and left to itself it
+  // would wait for q -- with vmcnt(0), draining the tile pipeline -- at the
+  // first MFMA of every tile.
+  asm volatile("" ::"v"(qb[0][0]), "v"(qb[0][1]), "v"(qb[0][2]), "v"(qb[0][3]), "v"(qb[1][0]), "v"(qb[1][1]),
+               "v"(qb[1][2]), "v"(qb[1][3]));
   wait_vmcnt<0>();
   lds_barrier();
 #pragma unroll
@@ -412,149 +571,16 @@ __device__ __forceinline__ void tile_body(const TileWork& tw, TileLds<KT, NB, FP
       // issued before this iteration's barrier).
       if (tn % TPW == 0 && tn > 0 && tn + TPW < nt) issue_pids(tn / TPW + 1);
     }
-    const uint4* kb_lds = lds.k[buf];
-    const char* vb_lds = reinterpret_cast<const char*>(lds.v[buf]);
     const int sbuf = buf;  // (fp8: the scale buffers of tile t)
-    buf = buf + 1 == NB ? 0 : buf + 1;
-
-    // S^T = K Q^T: s[kb][rb] holds keys 16 kb + 4 lg + i, query row
-    // 16 rb + col.  Each K operand serves both row blocks.
     f32x4 s[NKB][2];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const int key = kb * 16 + col;
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) s[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        u32x4 a;
-        if constexpr (FP8) {
-          // codes 32 c + 8 lg .. +7 of the key: half of swizzled chunk 2 c + lg / 2
-          const int ch = (2 * c + (lg >> 1)) ^ fswz(key);
-          const u32x2 w8 = *(__attribute__((address_space(3))) const u32x2*)(
-              reinterpret_cast<const char*>(kb_lds) + key * ROWB + ch * 16 + (lg & 1) * 8);
-          a = u32x4{fp8x2_to_bf16x2<false>(w8.x), fp8x2_to_bf16x2<true>(w8.x), fp8x2_to_bf16x2<false>(w8.y),
-                    fp8x2_to_bf16x2<true>(w8.y)};
-        } else {
-          const int cc = c * 4 + lg;
-          a = *(LdsU4*)(&kb_lds[key * 16 + (cc ^ tswz(col))]);
-        }
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) s[kb][rb] = mfma16x16x32(a, qb[rb][c], s[kb][rb]);
-      }
-    }
-    if constexpr (FP8) {
-      // each key's K scale on its scores (keys 16 kb + 4 lg + i)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const f32x4 k4 = *(__attribute__((address_space(3))) const f32x4*)(&lds.ks[sbuf][kb * 16 + 4 * lg]);
-        const float kq[4] = {k4[0], k4[1], k4[2], k4[3]};
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) s[kb][rb][i] *= kq[i];
-      }
-    }
-    // Keys are masked (by select) only in tiles that need it: the last,
-    // partial tile of a split, and chunk tiles that cross the causal
-    // diagonal of this wave's rows.
-    const bool need_mask = nk < KT || (CHUNK && kt + KT - 1 > vis_lo);
-    if (need_mask) {
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = kb * 16 + lg * 4 + i;
-            const bool ok = key < nk && (!CHUNK || kt + key <= vis[rb]);
-            s[kb][rb][i] = ok ? s[kb][rb][i] : -INFINITY;
-          }
-    }
-    // Online softmax per query row (column of S^T): the row's KT keys are
-    // spread over this lane's 4 NKB values and the lanes l^16, l^32, l^48.
+    scores(lds.k[buf], s);
+    scale_scores(sbuf, s);
+    mask_scores(kt, nk, s);
+    rescale(s);
     u32x4 pb[NKS][2];  // P^T operand [32-key step ks][row block rb]
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      float x = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x = fmaxf(x, s[kb][rb][i]);
-      const float mx = max_xor32(max_xor16(x)) * scale_log2;  // scale > 0 keeps the order
-      // Lazy rescaling: probabilities are taken against the running
-      // reference m, which moves (and o, the row sums are rescaled) only
-      // when a row's maximum exceeds it by more than 2^8 -- so p <= 256, and
-      // the rescale, a wave-wide branch, is rare after the first tiles.
-      if (__ballot(mx > m[rb] + 8.f) != 0ull) {
-        const float mn = fmaxf(m[rb], mx);
-        // m = -inf (nothing visible yet): o and the sums are 0, any factor will do
-        const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m[rb] - mn);
-        m[rb] = mn;
-        lsum[rb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < 8; ++db) o[db][rb] *= alpha;
-      }
-      // A row with no visible key so far keeps m = -inf: its p are all 0.
-      const float nref = m[rb] == -INFINITY ? 0.f : -m[rb];
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        uint32_t pw[2][2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          float p[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            p[i] = fast_exp2(fmaf(s[2 * ks + e][rb][i], scale_log2, nref));
-            lsum[rb] += p[i];
-          }
-          if constexpr (FP8) {
-            // P^T carries p times the key's V scale (keys 32 ks + 16 e + 4 lg + i;
-            // a masked key's p is 0 and its scale finite)
-            const f32x4 v4 =
-                *(__attribute__((address_space(3))) const f32x4*)(&lds.vs[sbuf][(2 * ks + e) * 16 + 4 * lg]);
-            p[0] *= v4[0];
-            p[1] *= v4[1];
-            p[2] *= v4[2];
-            p[3] *= v4[3];
-          }
-          pw[e][0] = bf16x2_rne(p[0], p[1]);
-          pw[e][1] = bf16x2_rne(p[2], p[3]);
-        }
-        // k slots 8 lg .. 8 lg + 7 = keys 32 ks + 4 lg + [0, 4) and
-        // 32 ks + 16 + 4 lg + [0, 4): the same order the V^T operand uses.
-        pb[ks][rb] = u32x4{pw[0][0], pw[0][1], pw[1][0], pw[1][1]};
-      }
-    }
-    // O^T += V^T P^T; the V^T operand (d = 16 db + col, keys as above) comes
-    // from two transposed reads of 4 keys each and serves both row blocks.
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        u32x4 a;
-        if constexpr (FP8) {
-          // one transposed read of 8 rows: lanes 2 r, 2 r + 1 name row r of
-          // the block, the keys in P^T's order
-          const int r8 = col >> 1;
-          const int row = ks * 32 + (r8 >> 2) * 16 + lg * 4 + (r8 & 3);
-          const u32x2 w8 = lds_read_tr8(vb_lds + row * ROWB + (db ^ fswz(row)) * 16 + (col & 1) * 8);
-          a = u32x4{fp8x2_to_bf16x2<false>(w8.x), fp8x2_to_bf16x2<true>(w8.x), fp8x2_to_bf16x2<false>(w8.y),
-                    fp8x2_to_bf16x2<true>(w8.y)};
-        } else {
-          u32x2 part[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int row = ks * 32 + e * 16 + lg * 4 + tr_r;
-            const int ch = (db * 2 + (tr_c >> 1)) ^ tswz(row & 15);
-            part[e] = lds_read_tr16(vb_lds + row * (D * 2) + ch * 16 + (tr_c & 1) * 8);
-          }
-          a = u32x4{part[0].x, part[0].y, part[1].x, part[1].y};
-        }
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) o[db][rb] = mfma16x16x32(a, pb[ks][rb], o[db][rb]);
-      }
-    }
+    probs(s, sbuf, pb);
+    accumulate(reinterpret_cast<const char*>(lds.v[buf]), pb);
+    buf = buf + 1 == NB ? 0 : buf + 1;
   }
 
   // Normalise and write this wave's rows: the row sums over all the keys of
