@@ -264,4 +264,68 @@ __device__ __forceinline__ bool locate_item(const int32_t* __restrict__ ctx, con
   return false;
 }
 
+// Log-sum-exp merge of n partials (a normalised o row of D floats and its
+// log2-sum-exp) for the G heads of one kv-head, this lane's EPL = D / 64
+// elements of each row.  lse_at(j, h) and row_at(j, h) name partial j of
+// head h.  Partials are taken J at a time, their sums and rows loaded
+// together (one round trip per J partials, all heads at once), with a
+// running maximum M: a partial with lse = -inf weighs 0, and with all n
+// partials in one step the result is that of a max pass followed by a sum
+// pass.
+// Partials per step of merge_partials for G rows of D elements.
+constexpr int merge_step(int G, int D) { return G * (D / 64) >= 32 ? 1 : 32 / (G * (D / 64)); }
+template <int G, int D, typename LseAt, typename RowAt>
+__device__ __forceinline__ void merge_partials(int n, int lane, LseAt lse_at, RowAt row_at, float (&M)[G],
+                                               float (&wsum)[G], float (&acc)[G][D / 64]) {
+  constexpr int EPL = D / 64;
+  constexpr int J = merge_step(G, D);
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    M[h] = -INFINITY;
+    wsum[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
+  for (int j0 = 0; j0 < n; j0 += J) {
+    float l[J][G];
+    float v[J][G][EPL];
+#pragma unroll
+    for (int jj = 0; jj < J; ++jj) {
+      const int j = j0 + jj;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        if (j < n) {
+          l[jj][h] = lse_at(j, h);
+          const float* src = row_at(j, h) + lane * EPL;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) v[jj][h][e] = src[e];
+        } else {
+          l[jj][h] = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) v[jj][h][e] = 0.f;
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mn = M[h];
+#pragma unroll
+      for (int jj = 0; jj < J; ++jj) mn = fmaxf(mn, l[jj][h]);
+      if (mn == -INFINITY) continue;  // nothing but empty partials so far
+      const float alpha = fast_exp2(M[h] - mn);  // M = -inf: 0
+      wsum[h] *= alpha;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+#pragma unroll
+      for (int jj = 0; jj < J; ++jj) {
+        const float a = fast_exp2(l[jj][h] - mn);  // -inf (no visible key) -> 0
+        wsum[h] += a;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(a, v[jj][h][e], acc[h][e]);
+      }
+      M[h] = mn;
+    }
+  }
+}
+
 }  // namespace pa

@@ -658,24 +658,19 @@ __global__ __launch_bounds__(64) void chunk_merge_kernel(uint16_t* __restrict__ 
   const int nks = chunks.nks[u];
   const int kps = chunks.kps[u];
   const int nsp = min(nks, (k_end + kps - 1) / kps);
-#pragma unroll 1
+  // Split j of head h: record p0 + G j + h (the G heads of a split are
+  // consecutive records).
+  const int64_t p0 = (chunks.rec[u] + (static_cast<int64_t>(i) * Hkv + kvh) * nks) * G;
+  auto lse_at = [&](int j, int h) -> float { return pre_lse[p0 + static_cast<int64_t>(j) * G + h]; };
+  auto row_at = [&](int j, int h) -> const float* { return pre_o + (p0 + static_cast<int64_t>(j) * G + h) * D; };
+  float M[G], wsum[G], acc[G][2];
+  merge_partials<G, D>(nsp, lane, lse_at, row_at, M, wsum, acc);
+#pragma unroll
   for (int h = 0; h < G; ++h) {
-    const int64_t p0 = (chunks.rec[u] + (static_cast<int64_t>(i) * Hkv + kvh) * nks) * G + h;
-    float M = -INFINITY;
-    for (int j = lane; j < nsp; j += 64) M = fmaxf(M, pre_lse[p0 + static_cast<int64_t>(j) * G]);
-    M = wave_max(M);
-    float acc0 = 0.f, acc1 = 0.f, wsum = 0.f;
-    for (int j = 0; j < nsp; ++j) {
-      const int64_t pr = p0 + static_cast<int64_t>(j) * G;
-      const float a = fast_exp2(pre_lse[pr] - M);  // -inf (no visible key) -> 0
-      wsum += a;
-      acc0 = fmaf(a, pre_o[pr * D + 2 * lane], acc0);
-      acc1 = fmaf(a, pre_o[pr * D + 2 * lane + 1], acc1);
-    }
-    const float inv = 1.0f / wsum;
+    const float inv = 1.0f / wsum[h];
     const int64_t row = static_cast<int64_t>(cu_q[s] + i) * Hq + kvh * G + h;
-    reinterpret_cast<uint32_t*>(out)[row * (D / 2) + lane] = bf16x2_rne(acc0 * inv, acc1 * inv);
-    if (lse_out && lane == 0) lse_out[row] = (M + fast_log2(wsum)) * kLn2;
+    reinterpret_cast<uint32_t*>(out)[row * (D / 2) + lane] = bf16x2_rne(acc[h][0] * inv, acc[h][1] * inv);
+    if (lse_out && lane == 0) lse_out[row] = (M[h] + fast_log2(wsum[h])) * kLn2;
   }
 }
 
@@ -717,35 +712,8 @@ __global__ __launch_bounds__(64) void cascade_merge_kernel(
     if (!shared) return seq_part + (static_cast<int64_t>(s) * Hq + kvh * G + h) * D;
     return part_o + (((static_cast<int64_t>(w0 + k) * Hkv + kvh) * 2 + (k == 0 ? slot0 : 0)) * PR + h) * D;
   };
-  // All G heads at once: their log-sum-exp loads, then their output loads,
-  // go out together (one head after another put two dependent load round
-  // trips per head on each workgroup's path).
-  float M[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    M[h] = -INFINITY;
-    for (int j = lane; j < n; j += 64) M[h] = fmaxf(M[h], lse_at(j, h));
-  }
-#pragma unroll
-  for (int h = 0; h < G; ++h) M[h] = wave_max(M[h]);
-  float acc[G][EPL];
-  float wsum[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    wsum[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
-  }
-  for (int j = 0; j < n; ++j) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float a = fast_exp2(lse_at(j, h) - M[h]);
-      wsum[h] += a;
-      const float* src = o_at(j, h) + lane * EPL;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(a, src[e], acc[h][e]);
-    }
-  }
+  float M[G], wsum[G], acc[G][EPL];
+  merge_partials<G, D>(n, lane, lse_at, o_at, M, wsum, acc);
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const float inv = 1.0f / wsum[h];
