@@ -109,7 +109,9 @@ def hbm_probe() -> None:
     two pools of 150,000 random 4 KB tiles (614 MB each) read once per launch
     in a random order, 2 or 4 tiles of each pool per batch, the next batch
     in flight while one is consumed, by LDS DMA (mode 0) or by loads into
-    registers (mode 1), at 1 to 16 waves per CU.  One JSON line per point."""
+    registers (mode 1), at 1 to 16 waves per CU; then the same number of
+    reads over a few distinct tiles (L2- and MALL-resident).  One JSON line
+    per point."""
     import ctypes
 
     import torch
@@ -135,6 +137,18 @@ def hbm_probe() -> None:
                 print(json.dumps({"probe": "hbm", "load_path": ["lds_dma", "registers"][mode], "tiles_per_batch": tpb,
                                   "waves_per_cu": wpc, "bytes": nbytes, "ms": round(ms, 5),
                                   "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)}), flush=True)
+    # The same reads over ids that name only `distinct` tiles of each pool:
+    # 256 (1 MB per pool) stay in the L2s, 2,048 (8 MB) spill to the MALL,
+    # 16,384 (64 MB) live in the MALL.
+    for distinct in (256, 2048, 16384):
+        ids_d = (torch.randperm(n, device="cuda") % distinct).to(torch.int32)
+        for mode in (0, 1):
+            ms = lib.hbm_probe_run(mode, 2, kp.data_ptr(), vp.data_ptr(), ids_d.data_ptr(), n, 4 * cus, 5, st)
+            if ms <= 0:
+                raise RuntimeError(f"hbm probe failed ({ms})")
+            print(json.dumps({"probe": "reuse", "distinct_tiles": distinct, "load_path": ["lds_dma", "registers"][mode],
+                              "tiles_per_batch": 2, "waves_per_cu": 4, "bytes": nbytes, "ms": round(ms, 5),
+                              "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def visible_pairs(lay, segs):

@@ -580,61 +580,51 @@ __global__ __launch_bounds__(64) void merge_kernel(T* __restrict__ out, float* _
     const int slot = j == 0 ? slot0 : 0;
     return ((static_cast<int64_t>(w0 + j) * Hkv + kvh) * 2 + slot) * G + r0 + h;
   };
-  float M[NA], acc[NA][EPL], wsum[NA];
-  if (n <= merge_step(NA, D)) {
-    // The usual case (a sequence shared by a few waves): every partial's
-    // sum and row in one round trip.
-    merge_partials<NA, D>(
-        n, lane, [&](int j, int h) { return part_lse[prow(j, h)]; },
-        [&](int j, int h) { return part_o + prow(j, h) * D; }, M, wsum, acc);
-  } else {
-    // Many partials: their sums over the lanes, then the rows.
+  float M[NA];
 #pragma unroll
-    for (int h = 0; h < NA; ++h) M[h] = -INFINITY;
-    for (int j = lane; j < n; j += 64) {
+  for (int h = 0; h < NA; ++h) M[h] = -INFINITY;
+  for (int j = lane; j < n; j += 64) {
 #pragma unroll
-      for (int h = 0; h < NA; ++h) M[h] = fmaxf(M[h], part_lse[prow(j, h)]);
-    }
+    for (int h = 0; h < NA; ++h) M[h] = fmaxf(M[h], part_lse[prow(j, h)]);
+  }
 #pragma unroll
-    for (int h = 0; h < NA; ++h) M[h] = wave_max(M[h]);
+  for (int h = 0; h < NA; ++h) M[h] = wave_max(M[h]);
+  float acc[NA][EPL], wsum[NA];
+#pragma unroll
+  for (int h = 0; h < NA; ++h) {
+    wsum[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
+  for (int j0 = 0; j0 < n; j0 += 64) {
+    const int j = j0 + lane;
+    float wt[NA];
 #pragma unroll
     for (int h = 0; h < NA; ++h) {
-      wsum[h] = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+      wt[h] = j < n ? fast_exp2(part_lse[prow(min(j, n - 1), h)] - M[h]) : 0.f;
+      wsum[h] += wt[h];
     }
-    for (int j0 = 0; j0 < n; j0 += 64) {
-      const int j = j0 + lane;
-      float wt[NA];
+    const int cnt = min(64, n - j0);
+    for (int jj = 0; jj < cnt; jj += 4) {
 #pragma unroll
-      for (int h = 0; h < NA; ++h) {
-        wt[h] = j < n ? fast_exp2(part_lse[prow(min(j, n - 1), h)] - M[h]) : 0.f;
-        wsum[h] += wt[h];
-      }
-      const int cnt = min(64, n - j0);
-      for (int jj = 0; jj < cnt; jj += 4) {
+      for (int u = 0; u < 4; ++u) {
+        const int jx = min(jj + u, cnt - 1);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int jx = min(jj + u, cnt - 1);
+        for (int h = 0; h < NA; ++h) {
+          const float* src = part_o + prow(j0 + jx, h) * D + lane * EPL;
+          const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt[h]), jx));
+          const float a = (jj + u < cnt) ? wj : 0.f;
 #pragma unroll
-          for (int h = 0; h < NA; ++h) {
-            const float* src = part_o + prow(j0 + jx, h) * D + lane * EPL;
-            const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt[h]), jx));
-            const float a = (jj + u < cnt) ? wj : 0.f;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(a, src[e], acc[h][e]);
-          }
+          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(a, src[e], acc[h][e]);
         }
       }
     }
-#pragma unroll
-    for (int h = 0; h < NA; ++h) wsum[h] = wave_sum(wsum[h]);
   }
 #pragma unroll
   for (int h = 0; h < NA; ++h) {
     const int r = r0 + h;  // row of the wave
     if ((r >> fold.lg) >= fold.fe) continue;  // idle row (past gqa_ratio, or a folded pass's tokens)
-    const float ws = wsum[h];
+    const float ws = wave_sum(wsum[h]);
     const float inv = 1.0f / ws;
     const int64_t row = MT ? (static_cast<int64_t>(s) * fold.n + fold.tok0 + (r >> fold.lg)) * Hq + kvh * GH +
                                  (r & (GH - 1))
