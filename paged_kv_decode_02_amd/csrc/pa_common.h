@@ -264,28 +264,39 @@ __device__ __forceinline__ bool locate_item(const int32_t* __restrict__ ctx, con
   return false;
 }
 
-// Log-sum-exp merge of n partials (a normalised o row of D floats and its
+// Log-sum-exp merge of n partials (a normalised o row of D elements and its
 // log2-sum-exp) for the G heads of one kv-head, this lane's EPL = D / 64
-// elements of each row.  lse_at(j, h) and row_at(j, h) name partial j of
-// head h.  Partials are taken J at a time, their sums and rows loaded
-// together (one round trip per J partials, all heads at once), with a
-// running maximum M: a partial with lse = -inf weighs 0, and with all n
-// partials in one step the result is that of a max pass followed by a sum
-// pass.
-// Partials per step of merge_partials for G rows of D elements.
-constexpr int merge_step(int G, int D) { return G * (D / 64) >= 32 ? 1 : 32 / (G * (D / 64)); }
-template <int G, int D, typename LseAt, typename RowAt>
-__device__ __forceinline__ void merge_partials(int n, int lane, LseAt lse_at, RowAt row_at, float (&M)[G],
-                                               float (&wsum)[G], float (&acc)[G][D / 64]) {
-  constexpr int EPL = D / 64;
-  constexpr int J = merge_step(G, D);
+// elements of each row.  lse_at(j, h) gives partial j's log2-sum-exp for
+// head h, load_row(j, h, v) this lane's EPL elements of its row.  Partials
+// are taken J at a time, their sums and rows loaded together (one round
+// trip per J partials, all heads at once), with a running maximum M: a
+// partial with lse = -inf weighs 0, and with all n partials in one step
+// the result is that of a max pass followed by a sum pass.  The state (M,
+// wsum, acc) carries over, so partials of different kinds can be merged by
+// successive calls; merge_init sets it up.
+template <int G, int D>
+__device__ __forceinline__ void merge_init(float (&M)[G], float (&wsum)[G], float (&acc)[G][D / 64]) {
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     M[h] = -INFINITY;
     wsum[h] = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+    for (int e = 0; e < D / 64; ++e) acc[h][e] = 0.f;
   }
+}
+// Elements 2 lane, 2 lane + 1 of a bf16 row, widened to float32 (exact).
+__device__ __forceinline__ void load_bf16_pair(const uint16_t* row, int lane, float (&v)[2]) {
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(row + 2 * lane);
+  v[0] = bf16_lo(w);
+  v[1] = bf16_hi(w);
+}
+// Partials per step of merge_partials for G rows of D elements.
+constexpr int merge_step(int G, int D) { return G * (D / 64) >= 32 ? 1 : 32 / (G * (D / 64)); }
+template <int G, int D, typename LseAt, typename LoadRow>
+__device__ __forceinline__ void merge_partials(int n, LseAt lse_at, LoadRow load_row, float (&M)[G], float (&wsum)[G],
+                                               float (&acc)[G][D / 64]) {
+  constexpr int EPL = D / 64;
+  constexpr int J = merge_step(G, D);
   for (int j0 = 0; j0 < n; j0 += J) {
     float l[J][G];
     float v[J][G][EPL];
@@ -296,9 +307,7 @@ __device__ __forceinline__ void merge_partials(int n, int lane, LseAt lse_at, Ro
       for (int h = 0; h < G; ++h) {
         if (j < n) {
           l[jj][h] = lse_at(j, h);
-          const float* src = row_at(j, h) + lane * EPL;
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) v[jj][h][e] = src[e];
+          load_row(j, h, v[jj][h]);
         } else {
           l[jj][h] = -INFINITY;
 #pragma unroll

@@ -477,13 +477,15 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
         if (whole && seq_part) {
           // Cascade: the suffix of a sequence one wave covered is still a
           // partial, to be merged with the shared prefix's.
-          // seq_part: outputs [S][Hq][D], then log2-sum-exp [S][Hq].
+          // seq_part: bf16 rows [S][Hq][D] (rounded to nearest even), then
+          // from float S Hq D on, the log2-sum-exp [S][Hq] as float32.
           const int64_t r = static_cast<int64_t>(s) * Hq + kvh * G + h;
           if (mine) {
-            float4* dst = reinterpret_cast<float4*>(seq_part + r * D + chk * EPC);
+            uint2* dst = reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(seq_part) + r * D + chk * EPC);
 #pragma unroll
             for (int e = 0; e < EPC; e += 4)
-              dst[e / 4] = make_float4(acc[h][e] * inv, acc[h][e + 1] * inv, acc[h][e + 2] * inv, acc[h][e + 3] * inv);
+              dst[e / 4] = make_uint2(bf16x2_rne(acc[h][e] * inv, acc[h][e + 1] * inv),
+                                      bf16x2_rne(acc[h][e + 2] * inv, acc[h][e + 3] * inv));
           }
           if (lane == 0) seq_part[static_cast<int64_t>(S) * Hq * D + r] = lse2;
         } else if (whole) {

@@ -104,6 +104,7 @@ CascadeLayout cascade_layout(int64_t num_seqs, int32_t num_kv_heads, int32_t gqa
   const size_t rows = static_cast<size_t>(num_seqs) * num_kv_heads * gqa;  // (sequence, q-head)
   l.begin_offset = 0;
   l.seq_part_offset = align_up(static_cast<size_t>(num_seqs) * sizeof(int32_t));
+  // (seq_part and pre_o hold bf16 rows in float-sized slots: room to spare)
   l.pre_o_offset = l.seq_part_offset + align_up(rows * (head_dim + 1) * sizeof(float));
   l.pre_lse_offset = l.pre_o_offset + align_up(rows * nks * head_dim * sizeof(float));
   l.stream_offset = l.pre_lse_offset + align_up(rows * nks * sizeof(float));

@@ -123,6 +123,7 @@ int launch_decode(const DecodeLaunch& a);
 // The stream kernel alone (plus, if `merge`, its merge kernel).  With
 // begin_pages (device, per sequence) only pages from there on are walked;
 // with seq_part, sequences one wave covers are written there as partials
+// (bf16 rows [S][Hq][D], then float32 log2-sum-exps from float S Hq D on)
 // instead of to `out`.  The plan actually used comes back in *plan.
 struct StreamPlan {
   int64_t waves;

@@ -495,13 +495,15 @@ __device__ __forceinline__ void stream_mfma_body(
       const float inv = lt == 0.f ? 0.f : 1.0f / lt;
       const float lse2 = m + fast_log2(lt);
       if (whole && seq_part) {
-        // seq_part: outputs [S][Hq][D], then log2-sum-exp [S][Hq].
+        // seq_part: bf16 rows [S][Hq][D] (rounded to nearest even), then
+        // from float S Hq D on, the log2-sum-exp [S][Hq] as float32.
         if (active) {
           const int64_t r = static_cast<int64_t>(s) * Hq + kvh * GH + col;
+          uint16_t* row = reinterpret_cast<uint16_t*>(seq_part) + r * D + lg * 4;
 #pragma unroll
           for (int db = 0; db < DB; ++db)
-            *reinterpret_cast<float4*>(seq_part + r * D + db * 16 + lg * 4) =
-                make_float4(o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
+            *reinterpret_cast<uint2*>(row + db * 16) =
+                make_uint2(bf16x2_rne(o[db][0] * inv, o[db][1] * inv), bf16x2_rne(o[db][2] * inv, o[db][3] * inv));
           if (lg == 0) seq_part[static_cast<int64_t>(S) * Hq * D + r] = lse2;
         }
       } else if (whole) {

@@ -593,9 +593,12 @@ __device__ __forceinline__ void tile_body(const TileWork& tw, TileLds<KT, NB, FP
       const int64_t pr = (tw.rec_base + (static_cast<int64_t>(r / G) * Hkv + kvh) * tw.nsplit + tw.ks) * G + r % G;
       const bool any = lt > 0.f;
       const float inv = any ? 1.0f / lt : 0.f;
+      // (the row as bf16, rounded to nearest even: 256 bytes per partial)
+      uint16_t* row = reinterpret_cast<uint16_t*>(pre_o) + pr * D + lg * 4;
 #pragma unroll
       for (int db = 0; db < 8; ++db)
-        *reinterpret_cast<f32x4*>(pre_o + pr * D + db * 16 + lg * 4) = o[db][rb] * inv;
+        *reinterpret_cast<uint2*>(row + db * 16) =
+            make_uint2(bf16x2_rne(o[db][rb][0] * inv, o[db][rb][1] * inv), bf16x2_rne(o[db][rb][2] * inv, o[db][rb][3] * inv));
       if (lg == 0) pre_lse[pr] = any ? m[rb] + fast_log2(lt) : -INFINITY;
     }
   }
@@ -662,9 +665,12 @@ __global__ __launch_bounds__(64) void chunk_merge_kernel(uint16_t* __restrict__ 
   // consecutive records).
   const int64_t p0 = (chunks.rec[u] + (static_cast<int64_t>(i) * Hkv + kvh) * nks) * G;
   auto lse_at = [&](int j, int h) -> float { return pre_lse[p0 + static_cast<int64_t>(j) * G + h]; };
-  auto row_at = [&](int j, int h) -> const float* { return pre_o + (p0 + static_cast<int64_t>(j) * G + h) * D; };
+  auto load_row = [&](int j, int h, float (&v)[2]) {
+    load_bf16_pair(reinterpret_cast<const uint16_t*>(pre_o) + (p0 + static_cast<int64_t>(j) * G + h) * D, lane, v);
+  };
   float M[G], wsum[G], acc[G][2];
-  merge_partials<G, D>(nsp, lane, lse_at, row_at, M, wsum, acc);
+  merge_init<G, D>(M, wsum, acc);
+  merge_partials<G, D>(nsp, lse_at, load_row, M, wsum, acc);
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const float inv = 1.0f / wsum[h];
@@ -698,22 +704,40 @@ __global__ __launch_bounds__(64) void cascade_merge_kernel(
   const bool shared = w1 > w0;
   if (shared && (w0 < 0 || w1 >= W || slot0 < 0 || slot0 > 1)) return;
   const int ns = shared ? (w1 - w0 + 1) : 1;
-  const int n = np + ns;
-  // Partial j: prefix split j < np, else suffix part j - np.
-  auto lse_at = [&](int j, int h) -> float {
-    if (j < np) return pre_lse[((static_cast<int64_t>(s) * Hkv + kvh) * nks + j) * G + h];
-    const int k = j - np;
-    if (!shared) return seq_part[static_cast<int64_t>(S) * Hq * D + static_cast<int64_t>(s) * Hq + kvh * G + h];
-    return part_lse[((static_cast<int64_t>(w0 + k) * Hkv + kvh) * 2 + (k == 0 ? slot0 : 0)) * PR + h];
-  };
-  auto o_at = [&](int j, int h) -> const float* {
-    if (j < np) return pre_o + (((static_cast<int64_t>(s) * Hkv + kvh) * nks + j) * G + h) * D;
-    const int k = j - np;
-    if (!shared) return seq_part + (static_cast<int64_t>(s) * Hq + kvh * G + h) * D;
-    return part_o + (((static_cast<int64_t>(w0 + k) * Hkv + kvh) * 2 + (k == 0 ? slot0 : 0)) * PR + h) * D;
-  };
+  // The prefix splits (bf16 rows), then the suffix: one whole-sequence
+  // partial (seq_part, a bf16 row) or one per wave that shared the sequence
+  // (float32 rows), merged in that order, each kind in a pass of its own.
+  static_assert(EPL == 2, "rows of 128 elements");
   float M[G], wsum[G], acc[G][EPL];
-  merge_partials<G, D>(n, lane, lse_at, o_at, M, wsum, acc);
+  merge_init<G, D>(M, wsum, acc);
+  const int64_t pre0 = (static_cast<int64_t>(s) * Hkv + kvh) * nks * G;  // split 0, head 0
+  merge_partials<G, D>(
+      np, [&](int j, int h) { return pre_lse[pre0 + static_cast<int64_t>(j) * G + h]; },
+      [&](int j, int h, float (&v)[EPL]) {
+        load_bf16_pair(reinterpret_cast<const uint16_t*>(pre_o) + (pre0 + static_cast<int64_t>(j) * G + h) * D, lane, v);
+      },
+      M, wsum, acc);
+  if (!shared) {
+    const int64_t r0 = static_cast<int64_t>(s) * Hq + kvh * G;
+    merge_partials<G, D>(
+        1, [&](int, int h) { return seq_part[static_cast<int64_t>(S) * Hq * D + r0 + h]; },
+        [&](int, int h, float (&v)[EPL]) {
+          load_bf16_pair(reinterpret_cast<const uint16_t*>(seq_part) + (r0 + h) * D, lane, v);
+        },
+        M, wsum, acc);
+  } else {
+    auto rec = [&](int k, int h) -> int64_t {
+      return ((static_cast<int64_t>(w0 + k) * Hkv + kvh) * 2 + (k == 0 ? slot0 : 0)) * PR + h;
+    };
+    merge_partials<G, D>(
+        ns, [&](int k, int h) { return part_lse[rec(k, h)]; },
+        [&](int k, int h, float (&v)[EPL]) {
+          const float* src = part_o + rec(k, h) * D + lane * EPL;
+          v[0] = src[0];
+          v[1] = src[1];
+        },
+        M, wsum, acc);
+  }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const float inv = 1.0f / wsum[h];
