@@ -427,7 +427,9 @@ int mixed_call(void* out, float* lse_out, const void* q, const void* k_pool, con
     // (The CU count only shapes the splits, never the results; should the
     // query fail, the launch below reports the device error.)
     const int cus = device_cu_count();
-    plan = plan_chunks(chunk_n, chunk_keys, gqa_ratio, num_kv_heads, cus > 0 ? cus : 256);
+    const int32_t wg_per_cu = mixed_one_launch(gqa_ratio, decode_pages, num_chunks) ? kMixedChunkWorkgroupsPerCU
+                                                                                    : kChunkWorkgroupsPerCU;
+    plan = plan_chunks(chunk_n, chunk_keys, gqa_ratio, num_kv_heads, cus > 0 ? cus : 256, wg_per_cu);
     if (plan.records > INT32_MAX) return fail(PA_EUNSUPPORTED, w + ": too many chunk tokens");
   }
   const int64_t waves = max_waves_per_head(decode_pages, num_kv_heads, 0);

@@ -125,7 +125,7 @@ MixedLayout mixed_layout(int64_t num_seqs, int64_t chunk_tokens, int32_t num_kv_
 }
 
 ChunkPlan plan_chunks(const std::vector<int32_t>& n_tok, const std::vector<int32_t>& keys, int32_t gqa,
-                      int32_t num_kv_heads, int32_t cus) {
+                      int32_t num_kv_heads, int32_t cus, int32_t wg_per_cu) {
   const size_t n = n_tok.size();
   // Tiles of 64 keys the chunks' row blocks stream in all: the last token
   // of a row block bounds the keys it sees (causal inside the chunk).
@@ -140,7 +140,7 @@ ChunkPlan plan_chunks(const std::vector<int32_t>& n_tok, const std::vector<int32
     }
   }
   total *= num_kv_heads;
-  const int64_t slots = static_cast<int64_t>(std::max(cus, 1)) * kChunkWorkgroupsPerCU;
+  const int64_t slots = static_cast<int64_t>(std::max(cus, 1)) * std::max(wg_per_cu, 1);
   const int64_t per_wg = std::max<int64_t>(kMinChunkSplitKeys / 64, (total + slots - 1) / slots);
   ChunkPlan p;
   p.nks.resize(n);

@@ -163,13 +163,33 @@ struct ChunkList {
 #define PA_CHUNK_WG_PER_CU 3
 #endif
 constexpr int kChunkWorkgroupsPerCU = PA_CHUNK_WG_PER_CU;
+// In the one-launch mixed kernel the chunk workgroups share the CUs with
+// the decode waves: fewer, longer chunk workgroups (one per CU's worth of
+// splits) measured faster there (chunked_piggyback 862-864 against 868-876
+// us at 3, fp8 629-631 against 640-646 us; 2, 5 and 8 slower), while chunks
+// launched on their own keep 3.
+#ifndef PA_MIXED_CHUNK_WG_PER_CU
+#define PA_MIXED_CHUNK_WG_PER_CU 1
+#endif
+constexpr int kMixedChunkWorkgroupsPerCU = PA_MIXED_CHUNK_WG_PER_CU;
+// The mixed batch runs as one launch (mixed_kernel) when built so, with 4
+// or more q-heads per kv-head, decode tokens present and at most
+// kMaxChunkSegments chunks; otherwise the chunk tiles and the decode stream
+// run one after the other.
+#ifndef PA_MIXED_ONE_LAUNCH
+#define PA_MIXED_ONE_LAUNCH 1
+#endif
+inline bool mixed_one_launch(int32_t gqa, int64_t decode_pages, int32_t num_chunks) {
+  return PA_MIXED_ONE_LAUNCH && gqa >= 4 && decode_pages > 0 && num_chunks <= kMaxChunkSegments;
+}
 struct ChunkPlan {
   std::vector<int32_t> nks, kps, rec;
   std::vector<int32_t> tiles;  // tiles of 64 keys per work item (launch order: most first)
   int64_t records = 0;         // partial records (token, kv-head, split) of all chunks
 };
 ChunkPlan plan_chunks(const std::vector<int32_t>& n_tok, const std::vector<int32_t>& keys, int32_t gqa,
-                      int32_t num_kv_heads, int32_t cus);
+                      int32_t num_kv_heads, int32_t cus,
+                      int32_t wg_per_cu);
 // Compute units of the current device (0 if the query fails).
 int device_cu_count();
 
