@@ -94,7 +94,7 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
     T* __restrict__ out, float* __restrict__ lse_out, const T* __restrict__ q, const TKV* __restrict__ k_pool,
     const TKV* __restrict__ v_pool, const float* __restrict__ k_scales, const float* __restrict__ v_scales,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ ctx,
-    int max_blocks, int S, int Hkv, int num_pages, float scale_log2, int per, int total_pages,
+    int max_blocks, int S, int Hkv, int num_pages, float scale_log2, int per, int lead, int total_pages,
     int32_t* __restrict__ seq_info, float* __restrict__ part_o, float* __restrict__ part_lse,
     PageSkip skip, float* __restrict__ seq_part, const int32_t* __restrict__ q_rows, Fold fold) {
   using Gm = Geom<TKV, D>;
@@ -132,8 +132,8 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
   const char* kbytes = reinterpret_cast<const char*>(k_pool);
   const char* vbytes = reinterpret_cast<const char*>(v_pool);
 
-  const int run_a = w * per;
-  const int run_b = min(run_a + per, total_pages);
+  const int run_a = run_begin(w, per, lead);
+  const int run_b = min(run_begin(w + 1, per, lead), total_pages);
   if (run_a >= run_b) return;
 
   // Per-lane offsets inside a page tile.  K: instruction i of a tile fills
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(64) void stream_decode_kernel(
       const int slot = (s == s0) ? 0 : 1;
       if (cur.seg_lo == cur.B && kvh == 0 && lane == 0) {
         seq_info[4 * s + 0] = w;
-        seq_info[4 * s + 1] = (cur.cs + (cur.P - cur.B) - 1) / per;  // last wave on the sequence
+        seq_info[4 * s + 1] = run_wave(cur.cs + (cur.P - cur.B) - 1, per, lead);  // last wave on the sequence
         seq_info[4 * s + 2] = slot;
         seq_info[4 * s + 3] = 0;
       }
@@ -539,13 +539,13 @@ __global__ __launch_bounds__(64) void stream_mfma_kernel(
     uint16_t* __restrict__ out, float* __restrict__ lse_out, const uint16_t* __restrict__ q,
     const TKV* __restrict__ k_pool, const TKV* __restrict__ v_pool, const float* __restrict__ k_scales,
     const float* __restrict__ v_scales, const int32_t* __restrict__ block_tables, const int32_t* __restrict__ ctx,
-    int max_blocks, int S, int Hkv, int num_pages, float scale_log2, int per, int total_pages,
+    int max_blocks, int S, int Hkv, int num_pages, float scale_log2, int per, int lead, int total_pages,
     int32_t* __restrict__ seq_info, float* __restrict__ part_o, float* __restrict__ part_lse,
     PageSkip skip, float* __restrict__ seq_part, const int32_t* __restrict__ q_rows, Fold fold) {
   __shared__ StreamMfmaLds<TKV, D> lds;
   stream_mfma_body<TKV, D, MT>(lds, blockIdx.x, blockIdx.y, out, lse_out, q, k_pool, v_pool, k_scales, v_scales,
-                               block_tables, ctx, max_blocks, S, Hkv, num_pages, scale_log2, per, total_pages,
-                               seq_info, part_o, part_lse, skip, seq_part, q_rows, fold);
+                               block_tables, ctx, max_blocks, S, Hkv, num_pages, scale_log2, per, lead,
+                               total_pages, seq_info, part_o, part_lse, skip, seq_part, q_rows, fold);
 }
 
 // Merge the partials of one (sequence, kv-head): the waves w0..w1 that
@@ -689,7 +689,14 @@ int launch_typed(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_p
     per = std::max<int64_t>(kMinPagesPerWave, (a.total_pages + per_head - 1) / per_head);
   }
   const int64_t W = std::max<int64_t>(1, (a.total_pages + per - 1) / per);
-  if (W > 0x7fffffff) return fail(PA_EUNSUPPORTED, "pa_decode: too many waves");
+  if (W > 0x7ffffffe) return fail(PA_EUNSUPPORTED, "pa_decode: too many waves");
+  // Automatic plans of the matrix-core kernel over bf16 pools shift pages
+  // from the odd waves of each pair to the even ones (the XCD balance of
+  // run_lead); the grid then holds an even number of waves per kv-head (a
+  // last, empty one if W is odd), so that wave parity is workgroup parity
+  // for every kv-head.  Splits the caller fixes stay equal.
+  const int32_t lead = (a.split_pages <= 0 && kMfma && sizeof(TKV) == 2) ? run_lead(per) : 0;
+  const int64_t Wg = lead > 0 ? (W + 1) / 2 * 2 : W;
   // partial rows per wave: the kernel's query rows (folded passes hold
   // more rows than q-heads per kv-head)
   const PartialLayout pl = partial_layout(W, a.num_seqs, a.num_kv_heads, G, a.head_dim);
@@ -714,11 +721,11 @@ int launch_typed(const DecodeLaunch& a, const int32_t* begin_pages, float* seq_p
   skip.begin_pages = begin_pages;
   skip.window = begin_pages ? 0 : a.window;
   if (a.timed) profile_before(a.stream);
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(W), a.num_kv_heads), dim3(64), 0, st, static_cast<T*>(a.out),
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(Wg), a.num_kv_heads), dim3(64), 0, st, static_cast<T*>(a.out),
                      a.lse_out, static_cast<const T*>(a.q), static_cast<const TKV*>(a.k_pool),
                      static_cast<const TKV*>(a.v_pool), a.k_scales, a.v_scales, a.block_tables, a.context_lens,
                      a.max_blocks, a.num_seqs,
-                     a.num_kv_heads, static_cast<int>(a.num_pages), scale_log2, static_cast<int>(per),
+                     a.num_kv_heads, static_cast<int>(a.num_pages), scale_log2, static_cast<int>(per), lead,
                      static_cast<int>(a.total_pages), seq_info, part_o, part_lse, skip, seq_part, q_rows, fold);
   if (a.timed) profile_after(a.stream);
   if (hipGetLastError() != hipSuccess) return fail(PA_EHIP, "pa_decode: stream kernel launch failed");

@@ -46,6 +46,17 @@ struct Batch {
   int pid[4];  // physical pages (entries past seg_hi repeat the last one)
 };
 
+// Runs of a kv-head's flattened pages: waves 2j and 2j + 1 share 2 per
+// pages, the even one taking per + lead of them (lead = 0: equal runs).
+// With an even number of waves per kv-head in the grid's x extent, a
+// wave's parity is that of its workgroup index, and so of its XCD.
+__device__ __forceinline__ int run_begin(int w, int per, int lead) { return w * per + ((w & 1) ? lead : 0); }
+// The wave whose run holds flattened page `page`.
+__device__ __forceinline__ int run_wave(int page, int per, int lead) {
+  const int j = page / (2 * per);
+  return 2 * j + (page - 2 * j * per >= per + lead ? 1 : 0);
+}
+
 __device__ __forceinline__ int pages_of_len(int L, int max_blocks) {
   const int64_t pg = (static_cast<int64_t>(L) + 15) >> 4;
   return static_cast<int>(pg < max_blocks ? (pg > 0 ? pg : 0) : max_blocks);
@@ -224,7 +235,7 @@ __device__ __forceinline__ void stream_mfma_body(
     StreamMfmaLds<TKV, D>& lds, int w, int kvh, uint16_t* __restrict__ out, float* __restrict__ lse_out, const uint16_t* __restrict__ q,
     const TKV* __restrict__ k_pool, const TKV* __restrict__ v_pool, const float* __restrict__ k_scales,
     const float* __restrict__ v_scales, const int32_t* __restrict__ block_tables, const int32_t* __restrict__ ctx,
-    int max_blocks, int S, int Hkv, int num_pages, float scale_log2, int per, int total_pages,
+    int max_blocks, int S, int Hkv, int num_pages, float scale_log2, int per, int lead, int total_pages,
     int32_t* __restrict__ seq_info, float* __restrict__ part_o, float* __restrict__ part_lse,
     PageSkip skip, float* __restrict__ seq_part, const int32_t* __restrict__ q_rows, Fold fold) {
   using Gm = Geom<TKV, D>;
@@ -253,8 +264,8 @@ __device__ __forceinline__ void stream_mfma_body(
   const char* kbytes = reinterpret_cast<const char*>(k_pool);
   const char* vbytes = reinterpret_cast<const char*>(v_pool);
 
-  const int run_a = w * per;
-  const int run_b = min(run_a + per, total_pages);
+  const int run_a = run_begin(w, per, lead);
+  const int run_b = min(run_begin(w + 1, per, lead), total_pages);
   if (run_a >= run_b) return;
 
   // K and V both land swizzled: instruction i of a page tile fills LDS
@@ -485,7 +496,7 @@ __device__ __forceinline__ void stream_mfma_body(
       const int slot = (s == s0) ? 0 : 1;
       if (cur.seg_lo == cur.B && kvh == 0 && lane == 0) {
         seq_info[4 * s + 0] = w;
-        seq_info[4 * s + 1] = (cur.cs + (cur.P - cur.B) - 1) / per;  // last wave on the sequence
+        seq_info[4 * s + 1] = run_wave(cur.cs + (cur.P - cur.B) - 1, per, lead);  // last wave on the sequence
         seq_info[4 * s + 2] = slot;
         seq_info[4 * s + 3] = 0;
       }

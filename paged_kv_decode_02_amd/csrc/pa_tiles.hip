@@ -883,7 +883,7 @@ __global__ __launch_bounds__(kTileThreads, 2) void mixed_kernel(
                                       out, lse_out, q,
                                       static_cast<const TKV*>(k_pool), static_cast<const TKV*>(v_pool), k_scales,
                                       v_scales, block_tables, ctx, max_blocks, S, Hkv, num_pages, scale_log2, per,
-                                      total_pages, seq_info, part_o, part_lse, PageSkip{}, nullptr, tiles.cu_q, fold);
+                                      /*lead=*/0, total_pages, seq_info, part_o, part_lse, PageSkip{}, nullptr, tiles.cu_q, fold);
   }
 }
 
