@@ -75,6 +75,28 @@ def test_longtail_full(gpu_lib):
     assert np.abs(lse.cpu().numpy() - rl).max() < LSE_TOL
 
 
+@pytest.mark.parametrize("total_pages", [1290, 1300, 2611, 5000])
+def test_automatic_plan_paired_runs(gpu_lib, total_pages):
+    """Automatic plans of the matrix-core kernel over bf16 pools pair the
+    runs (the even wave of each pair takes a few pages more than the odd
+    one) and add one empty wave when the run count is odd; with 8 kv-heads
+    on 256 CUs these totals give runs of 11 to 40 pages and both parities
+    of the run count.  Every sequence still matches the oracle."""
+    rng = np.random.default_rng(total_pages)
+    n = 24
+    cuts = np.sort(rng.choice(np.arange(1, total_pages), n - 1, replace=False))
+    pages = np.diff(np.concatenate([[0], cuts, [total_pages]]))
+    ctx = [int(16 * p - rng.integers(0, 16)) for p in pages]  # ragged last page, same page count
+    lay = decode_layout(ctx, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16", pool_factor=1.2, seed=7,
+                        value_std=0.5)
+    say(f"case paired runs: {total_pages} pages over {n} sequences")
+    (q, k, v), (qh, kh, vh) = device_inputs(lay)
+    ro, rl = oracle_decode(lay, qh, kh, vh)
+    out, lse = run_decode(gpu_lib, lay, q, k, v)
+    assert_close(lay, out_to_f64(out), ro, f"paired runs, {total_pages} pages")
+    assert np.abs(lse.cpu().numpy() - rl).max() < 1e-3
+
+
 @pytest.mark.parametrize("dtype,d,hq,hkv", [("bf16", 128, 8, 8), ("bf16", 128, 16, 8), ("bf16", 128, 128, 8),
                                             ("bf16", 64, 8, 2), ("bf16", 64, 32, 4), ("bf16", 64, 32, 2),
                                             ("f32", 64, 4, 4),
