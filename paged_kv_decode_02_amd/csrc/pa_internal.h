@@ -28,13 +28,15 @@ constexpr int kTileFp8WorkgroupsPerCU = PA_TILE_FP8_WG_PER_CU;  // the same over
 constexpr size_t kAlign = 256;
 // Automatic plans of the matrix-core stream over bf16 pools: the even wave
 // of each pair (2j, 2j + 1) takes this many thousandths of `per` pages
-// more, the odd one as many fewer.  Under a full streaming load the waves
-// on the odd XCDs of an MI355X (workgroup i runs on XCD i mod 8) stream
-// 4-9 % slower than those on the even ones (per-wave timelines of the
-// Llama-shaped, long-tail and cascade-suffix batches), so equal runs leave
-// the even XCDs idle at the end.  Leads of 35 and 60 took 1-1.5 % off the
-// Llama-shaped and long-tail kernels; over fp8 pools (half the bytes per
-// page) they were 2-3 % slower, so those keep equal runs.
+// more, the odd one as many fewer.  Under a full streaming load the XCDs
+// of an MI355X (workgroup i runs on XCD i mod 8) do not stream equally
+// fast: in most per-wave timelines of the Llama-shaped, long-tail and
+// cascade-suffix batches the odd XCDs were 4-9 % slower, so equal runs
+// left the even XCDs idle at the end (other runs split the XCDs into other
+// halves; there the lead only moves work inside equally fast pairs).
+// Leads of 35 and 60 took 1-1.5 % off the Llama-shaped and long-tail
+// kernels; over fp8 pools (half the bytes per page) they were 2-3 %
+// slower, so those keep equal runs.
 #ifndef PA_RUN_LEAD_PERMILLE
 #define PA_RUN_LEAD_PERMILLE 50
 #endif
